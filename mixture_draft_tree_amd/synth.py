@@ -1,0 +1,248 @@
+"""Seeded synthetic workloads for the mixture draft tree path.
+
+This module only draws random inputs. It holds none of the method's arithmetic
+(no softmax, no scoring, no tree logic), so both the fp64 oracle tests and the
+GPU path may use it as a common source of inputs.
+
+The workloads stand in for real drafter logits. The Multi-Future Drafting pages
+measure on drafter outputs over public task suites with trained checkpoints;
+none of that is used here. What is kept from the pages is the shape of the
+problem: a block of 16 slots with 15 drafted positions (MFD-Qwen3.5-4B model
+card, "Model"), K = 8 modes and a budget of B = 256 (same card, "Results"), and
+modes that each draft one coherent future (project page, "How it works", step 2).
+
+Five named workloads:
+
+  tiny      K=2,  L=4,  V=16,     B=8     fp32, brute-forceable
+  product   K=1,  L=15, V=32000,  B=64    bf16, two injected futures at equal mass
+  single    K=8,  L=15, V=151936, B=256   bf16, one tree
+  batched   64 trees of the `single` shape, T alternating 0 / 1
+  stress    K=16, L=15, V=248320, B=1024  bf16, heavy exact ties
+
+Every draw comes from a torch.Generator seeded from (workload id, tree index,
+base seed), on the device the caller names, so a given (device, seed) always
+yields the same tensors.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    wid: int
+    K: int
+    L: int
+    V: int
+    B: int
+    N: int
+    dtype: torch.dtype
+    sigma: float          # std of the drafter noise
+    boost: float          # added to each mode's future tokens
+    target_boost: float   # added to the chosen future in the target rows
+    temperatures: tuple   # per-tree temperature pattern (cycled)
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 2, 4, 16, 8, 1, torch.float32, 2.0, 4.0, 5.0, (0.0,)),
+    "product": Workload("product", 2, 1, 15, 32000, 64, 1, torch.bfloat16, 2.0, 0.0, 10.0, (0.0,)),
+    "single": Workload("single", 3, 8, 15, 151936, 256, 1, torch.bfloat16, 3.0, 8.0, 10.0, (0.0, 1.0)),
+    "batched": Workload("batched", 4, 8, 15, 151936, 256, 64, torch.bfloat16, 3.0, 8.0, 10.0, (0.0, 1.0)),
+    "stress": Workload("stress", 5, 16, 15, 248320, 1024, 1, torch.bfloat16, 3.0, 8.0, 10.0, (1.0,)),
+}
+
+
+def tree_seed(wid: int, tree_index: int, base_seed: int) -> int:
+    """Mix (workload id, tree index, base seed) into one 63-bit seed (splitmix64 steps)."""
+    mask = (1 << 64) - 1
+    z = 0
+    for part in (wid, tree_index, base_seed):
+        z = (z + 0x9E3779B97F4A7C15 + (part & mask)) & mask
+        z ^= z >> 30
+        z = (z * 0xBF58476D1CE4E5B9) & mask
+        z ^= z >> 27
+        z = (z * 0x94D049BB133111EB) & mask
+        z ^= z >> 31
+    return z & ((1 << 63) - 1)
+
+
+def _gen(device, seed: int) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def _randint(g, high, size, device):
+    return torch.randint(0, high, size, generator=g, device=device)
+
+
+def _distinct_other(g, avoid: int, V: int, device) -> int:
+    """A token drawn uniformly from [0, V) \\ {avoid}."""
+    t = int(_randint(g, V - 1, (1,), device).item())
+    return t + 1 if t >= avoid else t
+
+
+@dataclasses.dataclass
+class DraftBatch:
+    """Drafter-side inputs for N trees."""
+    workload: Workload
+    logits: torch.Tensor        # [N, K, L, V] in workload.dtype
+    futures: torch.Tensor       # [N, F, L] int64: the injected futures (F = K, or 2 for `product`)
+    chosen_mode: torch.Tensor   # [N] int64: index into F of the future the target follows
+    anchor: torch.Tensor        # [N] int32: committed token at the root
+    pos_base: torch.Tensor      # [N] int64: position id of the root
+    temperature: torch.Tensor   # [N] float32
+    seed: torch.Tensor          # [N] uint64 stored as int64 (two's complement)
+    tree_seeds: list            # python ints, one per tree
+
+
+def _tiny_tree(w, g, device):
+    K, L, V = w.K, w.L, w.V
+    x = torch.randn((K, L, V), generator=g, device=device, dtype=torch.float32) * w.sigma
+    A = _randint(g, V, (L,), device)
+    Bf = A.clone()
+    pos = torch.randperm(L, generator=g, device=device)[:2]
+    for p in pos.tolist():
+        Bf[p] = _distinct_other(g, int(A[p]), V, device)
+    fut = torch.stack([A, Bf])  # mode 0 follows A, mode 1 follows B
+    ar = torch.arange(L, device=device)
+    for k in range(K):
+        x[k, ar, fut[k]] += w.boost
+    return x, fut
+
+
+def _zipf_bump(g, L, V, device, n=20, height=6.0, s=1.1):
+    """Per position, `n` random tokens get height * r^-s for r = 1..n."""
+    bump = torch.zeros((L, V), device=device, dtype=torch.float32)
+    r = torch.arange(1, n + 1, device=device, dtype=torch.float32)
+    vals = height * r.pow(-s)
+    for i in range(L):
+        toks = torch.randperm(V, generator=g, device=device)[:n]
+        bump[i, toks] = vals
+    return bump
+
+
+# Offsets (in units of 1/2) for the three disagreeing positions of the
+# `product` workload: A gets c + d/2, B gets c - d/2.  They sum to zero, so A
+# and B carry equal total mass, and no other signed subset sums to zero.
+PRODUCT_DELTAS = (1.0, 0.5, -1.5)
+PRODUCT_SPLIT_POSITIONS = (1, 2, 3)   # 0-based drafted positions 2..4
+
+
+def _product_tree(w, g, device):
+    L, V = w.L, w.V
+    x = torch.randn((1, L, V), generator=g, device=device, dtype=torch.float32) * w.sigma
+    x[0] += _zipf_bump(g, L, V, device)
+    A = _randint(g, V, (L,), device)
+    Bf = A.clone()
+    for p in PRODUCT_SPLIT_POSITIONS:
+        Bf[p] = _distinct_other(g, int(A[p]), V, device)
+    # c: a multiple of 0.25, at least 4 above every row maximum (exact in bf16 below 32).
+    rowmax = float(x.max().item())
+    c = math.ceil((rowmax + 4.0) * 4.0) / 4.0
+    assert c + 1.0 < 32.0
+    ar = torch.arange(L, device=device)
+    x[0, ar, A] = c
+    for p, d in zip(PRODUCT_SPLIT_POSITIONS, PRODUCT_DELTAS):
+        x[0, p, A[p]] = c + d / 2.0
+        x[0, p, Bf[p]] = c - d / 2.0
+    return x, torch.stack([A, Bf])  # futures reported as [2, L] for this workload
+
+
+def _mode_futures(w, g, device):
+    """Each mode's future: a shared prefix of length U{0..7}, then m_k ~ U{1..7}
+    positions after it resampled (one coherent future per mode)."""
+    K, L, V = w.K, w.L, w.V
+    base = _randint(g, V, (L,), device)
+    p = int(_randint(g, 8, (1,), device).item())
+    fut = base.unsqueeze(0).repeat(K, 1)
+    for k in range(K):
+        m = int(_randint(g, 7, (1,), device).item()) + 1
+        m = min(m, L - p)
+        pos = p + torch.randperm(L - p, generator=g, device=device)[:m]
+        for q in pos.tolist():
+            fut[k, q] = _distinct_other(g, int(base[q]), V, device)
+    return fut
+
+
+def _mixture_tree(w, g, device, ties: bool):
+    K, L, V = w.K, w.L, w.V
+    x = torch.randn((K, L, V), generator=g, device=device, dtype=torch.float32) * w.sigma
+    fut = _mode_futures(w, g, device)
+    ar = torch.arange(L, device=device)
+    for k in range(K):
+        x[k, ar, fut[k]] += w.boost
+    if ties:
+        # In 10% of (mode, position) rows a second token gets the bit-identical
+        # (after bf16 rounding) value of the boosted future token.
+        xb = x.to(torch.bfloat16)
+        pick = torch.rand((K, L), generator=g, device=device) < 0.10
+        for k, i in pick.nonzero().tolist():
+            other = _distinct_other(g, int(fut[k, i]), V, device)
+            xb[k, i, other] = xb[k, i, fut[k, i]]
+        return xb, fut
+    return x, fut
+
+
+def draft_batch(name: str, base_seed: int = 0, device="cpu", N: Optional[int] = None) -> DraftBatch:
+    """Drafter logits and per-tree metadata for workload `name`."""
+    w = WORKLOADS[name]
+    N = w.N if N is None else N
+    logits = torch.empty((N, w.K, w.L, w.V), dtype=w.dtype, device=device)
+    futs, chosen, anchors, seeds = [], [], [], []
+    for n in range(N):
+        s = tree_seed(w.wid, n, base_seed)
+        seeds.append(s)
+        g = _gen(device, s)
+        if name == "tiny":
+            x, fut = _tiny_tree(w, g, device)
+        elif name == "product":
+            x, fut = _product_tree(w, g, device)
+        else:
+            x, fut = _mixture_tree(w, g, device, ties=(name == "stress"))
+        logits[n] = x.to(w.dtype)
+        futs.append(fut)
+        chosen.append(int(_randint(g, fut.shape[0], (1,), device).item()))
+        anchors.append(int(_randint(g, w.V, (1,), device).item()))
+    temps = torch.tensor([w.temperatures[n % len(w.temperatures)] for n in range(N)], dtype=torch.float32)
+    seed_t = torch.tensor([(s ^ 0x5DEECE66D) & ((1 << 63) - 1) for s in seeds], dtype=torch.int64)
+    return DraftBatch(
+        workload=w, logits=logits, futures=torch.stack(futs),
+        chosen_mode=torch.tensor(chosen, dtype=torch.int64),
+        anchor=torch.tensor(anchors, dtype=torch.int32),
+        pos_base=torch.tensor([1000 + 17 * n for n in range(N)], dtype=torch.int64),
+        temperature=temps, seed=seed_t, tree_seeds=seeds)
+
+
+def target_logits(batch: DraftBatch, depth: torch.Tensor, n_nodes: torch.Tensor,
+                  device="cpu", base_seed: int = 0) -> torch.Tensor:
+    """Target per-node logits [N, B+1, V].
+
+    Rows are N(0,1).  The target follows one future F (the chosen mode's): every
+    tree node at depth d < L gets `target_boost` on F[d], so from the root the
+    target's preferred continuation is F token by token.  `depth` / `n_nodes`
+    describe the tree the rows belong to (node i of tree n has depth depth[n, i]).
+    """
+    w = batch.workload
+    N = batch.logits.shape[0]
+    Bp1 = w.B + 1
+    out = torch.empty((N, Bp1, w.V), dtype=w.dtype, device=device)
+    depth = depth.to("cpu")
+    n_nodes = n_nodes.to("cpu")
+    for n in range(N):
+        g = _gen(device, tree_seed(w.wid + 100, n, base_seed))
+        r = torch.randn((Bp1, w.V), generator=g, device=device, dtype=torch.float32)
+        F = batch.futures[n, int(batch.chosen_mode[n])].to(device)
+        nn_ = int(n_nodes[n])
+        d = depth[n, :nn_].to(torch.int64)
+        rows = torch.nonzero(d < w.L).flatten()
+        if rows.numel():
+            r[rows.to(device), F[d[rows].to(device)]] += w.target_boost
+        out[n] = r.to(w.dtype)
+    return out

@@ -1,0 +1,475 @@
+"""CPU pins for the fp64 oracle: each check ties the oracle to something other
+than itself (library routines, closed forms, brute force, and properties the
+Multi-Future Drafting pages fix)."""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mixture_draft_tree_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _facts():
+    with open(os.path.join(GOLDEN, "pages_facts.json")) as f:
+        return json.load(f)
+
+
+def _rand_logits(rng, K, L, V, scale=2.0, ints=False):
+    if ints:
+        return rng.integers(-3, 4, size=(K, L, V)).astype(np.float64)
+    return rng.normal(0.0, scale, size=(K, L, V))
+
+
+# ---------------------------------------------------------------- log-softmax
+
+def test_lse_matches_torch_logsumexp():
+    rng = np.random.default_rng(1)
+    x = rng.normal(0, 3, size=(3, 5, 1000))
+    ref = torch.logsumexp(torch.from_numpy(x), dim=-1).numpy()
+    assert np.max(np.abs(O.lse_rows(x) - ref)) < 1e-12
+    # log-probabilities against torch.log_softmax in float64
+    lp = x - O.lse_rows(x)[..., None]
+    ref_lp = torch.log_softmax(torch.from_numpy(x), dim=-1).numpy()
+    assert np.max(np.abs(lp - ref_lp)) < 1e-12
+
+
+def test_lse_closed_forms():
+    V = 777
+    row = np.full(V, 2.5)
+    assert abs(O.lse_rows(row) - (2.5 + math.log(V))) < 1e-13
+    r2 = np.array([1.0, -np.inf, 3.0, -np.inf])
+    assert abs(O.lse_rows(r2) - math.log(math.e ** 1 + math.e ** 3)) < 1e-13
+    assert O.lse_rows(np.full(5, -np.inf)) == -np.inf
+    # shift invariance of log-probabilities
+    rng = np.random.default_rng(2)
+    x = rng.normal(size=(4, 300))
+    lp1 = x - O.lse_rows(x)[:, None]
+    lp2 = (x + 7.25) - O.lse_rows(x + 7.25)[:, None]
+    assert np.max(np.abs(lp1 - lp2)) < 1e-12
+
+
+def test_prefix_norms_closed_form():
+    lse = np.array([[1.0, 2.0, 3.5], [0.25, 0.5, 0.75]])
+    n = O.prefix_norms(lse)
+    assert np.array_equal(n, np.array([[0, 1, 3, 6.5], [0, 0.25, 0.75, 1.5]]))
+
+
+# ---------------------------------------------------------------- rank order
+
+@pytest.mark.parametrize("ints", [False, True])
+def test_rank_order_against_python_sort(ints):
+    rng = np.random.default_rng(3)
+    for _ in range(20):
+        V = int(rng.integers(1, 60))
+        row = rng.integers(-2, 3, size=V).astype(float) if ints else rng.normal(size=V)
+        k = int(rng.integers(1, V + 1))
+        ref = sorted(range(V), key=lambda v: (-row[v], v))[:k]
+        assert list(O.rank_order(row, k)) == ref
+
+
+# ---------------------------------------------------------------- selection
+
+def _check_same_selection(a, b):
+    assert a.n_select == b.n_select
+    assert a.selected == b.selected
+    for t in a.selected:
+        assert a.S[t] == b.S[t]
+        assert a.mu[t] == b.mu[t]
+    assert a.cutoff == b.cutoff
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_heap_equals_bruteforce_tiny_workload(seed):
+    """The merged heap gives exactly the B best prefixes by best-mode score
+    (model card summary; project page 'In one minute')."""
+    b = synth.draft_batch("tiny", base_seed=seed)
+    x = b.logits[0].double().numpy()
+    for B in (1, 3, 8, 20):
+        h = O.mixture_select_heap(x, B)
+        bf = O.mixture_select_bruteforce(x, B)
+        _check_same_selection(h, bf)
+        if h.n_select == B and len(bf.order) > B and bf.S[bf.order[B]] < bf.cutoff:
+            assert np.array_equal(h.per_mode_kept, bf.per_mode_kept)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_heap_equals_bruteforce_with_ties_and_neginf(seed):
+    rng = np.random.default_rng(100 + seed)
+    K, L, V = int(rng.integers(1, 4)), int(rng.integers(1, 4)), int(rng.integers(2, 7))
+    x = _rand_logits(rng, K, L, V, ints=True)
+    if seed % 2:
+        x[rng.random(x.shape) < 0.2] = -np.inf
+    for B in (1, 4, 10, 25):
+        h = O.mixture_select_heap(x, B)
+        bf = O.mixture_select_bruteforce(x, B)
+        _check_same_selection(h, bf)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_k1_is_product_ddtree(seed):
+    """With one mode the mixture tree is the product-ranked tree (project page
+    'In one minute', drafter (a); 'Abstract')."""
+    rng = np.random.default_rng(200 + seed)
+    L, V = 4, 9
+    x = _rand_logits(rng, 1, L, V, ints=(seed % 2 == 1))
+    for B in (1, 5, 17, 40):
+        h = O.mixture_select_heap(x, B)
+        dd = O.ddtree_product_select(x[0], B)
+        bf = O.mixture_select_bruteforce(x, B)
+        assert h.selected == dd == bf.selected
+
+
+def _margin_positive(sel):
+    """The (B+1)-th prefix scores strictly below the cut-off.  The heap lists the
+    prefixes within its band below the cut-off, so none listed means none there."""
+    return len(sel.order) == sel.n_select or sel.S[sel.order[sel.n_select]] < sel.cutoff
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_union_identity_and_keep_counts(seed):
+    """The tree equals the union of the per-mode keeps at the common cut-off,
+    and the per-mode keeps add up to at least the tree size (37 >= 15 in the
+    pages' example) -- project page 'In one minute' and step 3."""
+    rng = np.random.default_rng(300 + seed)
+    K, L, V, B = 4, 5, 40, 30
+    x = _rand_logits(rng, K, L, V)
+    sel = O.mixture_select_heap(x, B, band=1e-9)
+    per_mode, union = O.union_at_cutoff(x, sel.cutoff, k=min(B, V))
+    assert set(sel.selected) <= union
+    assert _margin_positive(sel)
+    assert union == set(sel.selected)
+    assert [len(p) for p in per_mode] == list(sel.per_mode_kept)
+    assert sum(sel.per_mode_kept) >= sel.n_select
+    facts = _facts()["in_one_minute"]
+    assert facts["per_mode_keeps_total"] >= facts["tree_nodes"]
+
+
+def test_nested_and_prefix_closed():
+    rng = np.random.default_rng(4)
+    x = _rand_logits(rng, 3, 4, 12)
+    prev = []
+    full = O.mixture_select_heap(x, 40)
+    for B in range(1, 40):
+        s = O.mixture_select_heap(x, B)
+        assert s.selected == full.selected[:B]
+        assert set(prev) <= set(s.selected)
+        for t in s.selected:
+            assert len(t) == 1 or t[:-1] in set(s.selected)
+        prev = s.selected
+
+
+def test_mode_permutation_and_duplication():
+    rng = np.random.default_rng(5)
+    x = _rand_logits(rng, 4, 4, 20)
+    B = 25
+    a = O.mixture_select_heap(x, B)
+    perm = np.array([2, 0, 3, 1])
+    b = O.mixture_select_heap(x[perm], B)
+    assert _margin_positive(a)
+    assert set(a.selected) == set(b.selected)
+    for t in a.selected:
+        assert a.S[t] == b.S[t]
+        assert perm[b.mu[t]] == a.mu[t]
+    # a duplicated mode changes nothing; the lower copy is the best mode
+    one = O.mixture_select_heap(x[:1], B)
+    dup = O.mixture_select_heap(np.concatenate([x[:1], x[:1]]), B)
+    assert one.selected == dup.selected
+    assert all(dup.mu[t] == 0 and dup.S[t] == one.S[t] for t in dup.selected)
+
+
+def test_shift_invariance():
+    rng = np.random.default_rng(6)
+    x = _rand_logits(rng, 3, 4, 15)
+    shift = rng.integers(-4, 5, size=(3, 4, 1)) * 0.5
+    a = O.mixture_select_heap(x, 30)
+    b = O.mixture_select_heap(x + shift, 30)
+    assert a.selected == b.selected
+    assert max(abs(a.S[t] - b.S[t]) for t in a.selected) < 1e-12
+
+
+def test_budget_edges():
+    rng = np.random.default_rng(7)
+    x = _rand_logits(rng, 2, 3, 4)
+    z = O.mixture_select_heap(x, 0)
+    assert z.n_select == 0 and z.cutoff == math.inf
+    allp = O.mixture_select_heap(x, 10 ** 4)  # more than every prefix (4 + 16 + 64)
+    assert allp.n_select == 84
+    assert allp.selected == O.mixture_select_bruteforce(x, 10 ** 4).selected
+    # -inf everywhere except one token per row: the tree is one chain
+    y = np.full((2, 3, 4), -np.inf)
+    y[:, :, 1] = 0.0
+    c = O.mixture_select_heap(y, 10)
+    assert c.selected == [(1,), (1, 1), (1, 1, 1)]
+
+
+# ---------------------------------------------------------------- chimeras
+
+def test_product_workload_chimeras():
+    """Two futures disagreeing in m = 3 positions at equal mass force at least
+    2^(m-1) - 1 = 3 chimeras into a product-ranked tree (paper-tracker abstract;
+    project page TL;DR and 'Abstract')."""
+    b = synth.draft_batch("product")
+    x = b.logits[0].double().numpy()
+    A, Bf = b.futures[0, 0].tolist(), b.futures[0, 1].tolist()
+    sel = O.mixture_select_heap(x, 64)
+    tree = set(sel.selected)
+    d = max(synth.PRODUCT_SPLIT_POSITIONS) + 1
+    assert tuple(A[:d]) in tree and tuple(Bf[:d]) in tree
+    chims = O.chimera_nodes(sel.selected, A, Bf)
+    m = len(synth.PRODUCT_SPLIT_POSITIONS)
+    bound = _facts()["chimera_lower_bound"]["values"][str(m)]
+    assert bound == 2 ** (m - 1) - 1
+    full_len = [c for c in chims if len(c) == d]
+    assert len(full_len) >= bound
+    # exactly the splices whose signed offsets sum above zero
+    want = set()
+    for signs in range(2 ** m):
+        off = 0.0
+        t = list(A[:d])
+        for j, (p, dl) in enumerate(zip(synth.PRODUCT_SPLIT_POSITIONS, synth.PRODUCT_DELTAS)):
+            if signs >> j & 1:
+                off += dl / 2
+            else:
+                off -= dl / 2
+                t[p] = Bf[p]
+        if off > 0:
+            want.add(tuple(t))
+    assert len(want) == bound
+    assert want <= tree
+
+
+@pytest.mark.parametrize("m", [2, 3, 4, 5])
+def test_chimera_count_random_splices(m):
+    """Pairing argument: each splice c and its complement sum to s(A) + s(B), so
+    exactly 2^(m-1) - 1 splices score above the two futures; all of them are in
+    any product tree that holds both futures."""
+    rng = np.random.default_rng(400 + m)
+    L, V = 6, 30
+    x = rng.normal(0, 1, size=(1, L, V))
+    A = rng.integers(0, V, size=L)
+    Bf = A.copy()
+    pos = np.sort(rng.choice(L, size=m, replace=False))
+    for p in pos:
+        Bf[p] = (A[p] + 1 + rng.integers(0, V - 1)) % V
+    while True:  # dyadic offsets, zero sum, no other signed subset sum zero
+        dl = rng.integers(-8, 9, size=m).astype(float) / 4
+        dl[-1] = -dl[:-1].sum()
+        sums = [sum(dl[j] * (1 if s >> j & 1 else -1) for j in range(m)) for s in range(2 ** m)]
+        if all(abs(v) > 1e-9 for v in sums[1:-1]) and np.all(dl != 0):
+            break
+    c = 10.0
+    x[0, np.arange(L), A] = c
+    for j, p in enumerate(pos):
+        x[0, p, A[p]] = c + dl[j] / 2
+        x[0, p, Bf[p]] = c - dl[j] / 2
+    d = int(pos[-1]) + 1
+    budget = 4
+    while True:
+        sel = O.mixture_select_heap(x, budget)
+        tree = set(sel.selected)
+        if tuple(A[:d]) in tree and tuple(Bf[:d]) in tree:
+            break
+        budget *= 2
+    above = [t for t in O.chimera_nodes(sel.selected, A, Bf) if len(t) == d
+             and sel.S[t] > sel.S[tuple(A[:d])]]
+    assert len(above) == 2 ** (m - 1) - 1
+
+
+def test_mixture_contrast_no_chimeras():
+    """One future per mode: the mixture tree keeps both futures without
+    splicing them (project page Figure 2: 6 nodes on A, 9 on B, no chimera)."""
+    rng = np.random.default_rng(8)
+    L, V = 6, 40
+    x = rng.normal(0, 1, size=(2, L, V))
+    A = rng.integers(0, V, size=L)
+    Bf = A.copy()
+    for p in (1, 3, 4):
+        Bf[p] = (A[p] + 7) % V
+    x[0, np.arange(L), A] += 8.0
+    x[1, np.arange(L), Bf] += 8.0
+    sel = O.mixture_select_heap(x, 2 * L)
+    assert tuple(A) in set(sel.selected) and tuple(Bf) in set(sel.selected)
+    assert O.chimera_nodes(sel.selected, A, Bf) == []
+    # the product tree of the averaged distribution does splice them
+    prod = O.mixture_select_heap(np.log(0.5 * np.exp(x[0]) + 0.5 * np.exp(x[1]))[None], 2 * L)
+    assert len(O.chimera_nodes(prod.selected, A, Bf)) > 0
+
+
+# ---------------------------------------------------------------- layout & mask
+
+def test_canonical_layout_and_mask():
+    rng = np.random.default_rng(9)
+    x = _rand_logits(rng, 3, 4, 10)
+    B = 40
+    sel = O.mixture_select_heap(x, B)
+    tr = O.canonical_tree(sel, anchor=5, B=B)
+    n = tr["n_nodes"]
+    par, dep, tok = tr["parent"], tr["depth"], tr["node_token"]
+    assert n == B + 1
+    for i in range(1, n):
+        assert 0 <= par[i] < i
+        assert dep[i] == dep[par[i]] + 1
+        assert tr["prefixes"][i][:-1] == tr["prefixes"][par[i]]
+        if i > 1 and dep[i] == dep[i - 1]:
+            assert (par[i - 1], tok[i - 1]) < (par[i], tok[i])
+    dense, pos = O.tree_mask(par, dep, n, 123, B + 1)
+    # closure of the parent relation by repeated boolean products
+    P = np.zeros((B + 1, B + 1), dtype=np.int64)
+    for i in range(1, n):
+        P[i, par[i]] = 1
+    C = np.eye(B + 1, dtype=np.int64)
+    C[n:, n:] = 0
+    step = C.copy()
+    for _ in range(x.shape[1] + 1):
+        step = ((step @ P) > 0).astype(np.int64)
+        C = ((C + step) > 0).astype(np.int64)
+    assert np.array_equal(C.astype(bool), dense)
+    assert np.array_equal(dense.sum(1)[:n], dep[:n] + 1)
+    sub = np.zeros(n, dtype=np.int64)
+    for i in range(n - 1, -1, -1):
+        sub[i] += 1
+        if i > 0:
+            sub[par[i]] += sub[i]
+    assert np.array_equal(dense.sum(0)[:n], sub)
+    assert np.array_equal(pos[:n], 123 + dep[:n]) and np.all(pos[n:] == -1)
+    words = O.pack_mask_words(dense)
+    unpacked = np.array([[(int(words[r, c // 64]) >> (c % 64)) & 1 for c in range(B + 1)] for r in range(B + 1)])
+    assert np.array_equal(unpacked.astype(bool), dense)
+
+
+# ---------------------------------------------------------------- RNG
+
+def test_philox_matches_numpy():
+    rng = np.random.default_rng(10)
+    for _ in range(20):
+        key = [int(v) for v in rng.integers(0, 2 ** 63, size=2)]
+        ctr = [int(v) for v in rng.integers(1, 2 ** 63, size=4)]
+        ours = [int(np.asarray(w)) for w in O.philox4x64_10(ctr, key)]
+        npc = np.array(ctr, dtype=np.uint64)
+        npc[0] -= np.uint64(1)  # numpy bumps the counter before each block
+        g = np.random.Philox(key=np.array(key, dtype=np.uint64), counter=npc)
+        assert ours == [int(v) for v in g.random_raw(4)]
+
+
+def test_gumbel_moments():
+    g = O.gumbel_noise(seed=12345, depth=3, V=400000)
+    assert np.all(np.isfinite(g))
+    assert abs(g.mean() - 0.5772156649) < 0.01
+    assert abs(g.var() - math.pi ** 2 / 6) < 0.03
+    g2 = O.gumbel_noise(seed=12345, depth=4, V=10)
+    assert not np.array_equal(g[:10], g2)
+    assert np.array_equal(O.gumbel_noise(seed=12345, depth=3, V=10), g[:10])
+
+
+# ---------------------------------------------------------------- walk
+
+def _tiny_tree_and_target(seed):
+    b = synth.draft_batch("tiny", base_seed=seed)
+    w = b.workload
+    x = b.logits[0].double().numpy()
+    sel = O.mixture_select_heap(x, w.B)
+    tr = O.canonical_tree(sel, int(b.anchor[0]), w.B)
+    dep = torch.from_numpy(tr["depth"]).unsqueeze(0)
+    R = synth.target_logits(b, dep, torch.tensor([tr["n_nodes"]]), base_seed=seed)[0].double().numpy()
+    return b, tr, R
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_walk_greedy_closed_form(seed):
+    """At T = 0 with the target boosting one future, the walk accepts the longest
+    prefix of that future present in the tree, plus a bonus token."""
+    b, tr, R = _tiny_tree_and_target(seed)
+    L = b.workload.L
+    F = b.futures[0, int(b.chosen_mode[0])].tolist()
+    tau, toks, path, steps = O.verify_walk(tr["node_token"], tr["parent"], tr["depth"], tr["n_nodes"], R, 0.0, 0, L)
+    prefixes = set(tr["prefixes"])
+    j = 0
+    while j < L and tuple(F[: j + 1]) in prefixes:
+        j += 1
+    dominated = all(int(np.argmax(R[p])) == F[tr["depth"][p]] for p in path[:tau] if tr["depth"][p] < L)
+    if dominated:
+        assert tau == j + 1
+        assert toks[: tau - 1].tolist() == F[: tau - 1]
+    assert 1 <= tau <= L + 1
+    assert toks[tau - 1] == int(np.argmax(R[path[tau - 1]]))
+    assert np.all(toks[tau:] == -1) and np.all(path[tau:] == -1)
+
+
+def test_walk_figure2_tau_convention():
+    """A walk that accepts 6 drafted tokens reports tau = 7 (project page Figure 2)."""
+    f = _facts()["figure2_walk"]
+    L = 15
+    n = f["nodes"]
+    # chain of 9 nodes plus 6 leaves hanging off the root: 15 drafted nodes
+    parent = [-1] + list(range(0, 9)) + [0] * (n - 9)
+    token = [0] + [10 + i for i in range(9)] + [50 + i for i in range(n - 9)]
+    depth = [0] + list(range(1, 10)) + [1] * (n - 9)
+    V = 64
+    R = np.zeros((n + 1, V))
+    for u in range(f["accepted_drafted"] + 1):
+        nxt = 10 + u if u < f["accepted_drafted"] else 63
+        R[u, nxt] = 5.0
+    tau, toks, path, _ = O.verify_walk(token, parent, depth, n + 1, R, 0.0, 0, L)
+    assert tau == f["tau"] and tau - 1 == f["accepted_drafted"]
+    assert toks[tau - 1] == 63
+
+
+def test_walk_sampling_is_exact_chi2():
+    """At T > 0 the first step is a sample of softmax(R[0] / T): lossless
+    verification keeps the target's own distribution (model card summary)."""
+    from scipy.stats import chisquare
+    rng = np.random.default_rng(11)
+    V, T = 16, 0.8
+    row = rng.normal(0, 1.5, size=V)
+    parent, token, depth = [-1], [0], [0]
+    R = row[None]
+    n_seeds = 20000
+    counts = np.zeros(V)
+    for s in range(n_seeds):
+        g = O.gumbel_noise(s, 0, V)
+        counts[int(np.argmax(row / T + g))] += 1
+    p = np.exp(row / T - O.lse_rows(row / T))
+    stat, pval = chisquare(counts, p * n_seeds)
+    assert pval > 1e-4
+    tau, toks, _, _ = O.verify_walk(token, parent, depth, 1, R, T, 7, 15)
+    assert tau == 1 and toks[0] == int(np.argmax(row / T + O.gumbel_noise(7, 0, V)))
+
+
+def test_walk_expected_accepted_equals_covered_mass():
+    """Expected accepted tokens = probability mass the tree covers (project page
+    'Abstract'), checked by Monte Carlo over seeds."""
+    rng = np.random.default_rng(12)
+    K, L, V, B = 2, 4, 6, 12
+    x = rng.normal(0, 1, size=(K, L, V))
+    sel = O.mixture_select_heap(x, B)
+    tr = O.canonical_tree(sel, 0, B)
+    R = rng.normal(0, 1, size=(B + 1, V))
+    T = 1.0
+    mass = O.covered_mass(tr["node_token"], tr["parent"], tr["n_nodes"], R, T)
+    acc = []
+    for s in range(4000):
+        tau, *_ = O.verify_walk(tr["node_token"], tr["parent"], tr["depth"], tr["n_nodes"], R, T, s, L)
+        acc.append(tau - 1)
+    acc = np.array(acc, dtype=float)
+    se = acc.std() / math.sqrt(len(acc))
+    assert abs(acc.mean() - mass) < 5 * se + 1e-3
+
+
+def test_band_criterion():
+    rng = np.random.default_rng(13)
+    x = _rand_logits(rng, 2, 3, 8)
+    sel = O.mixture_select_heap(x, 10, band=1e-4)
+    assert O.band_is_exact(x, sel)
+    # an exact cross-mode tie at the cut-off is not decidable by raw sums
+    y = np.zeros((2, 1, 4))
+    y[0, 0] = [1.0, 0.0, -1.0, -2.0]
+    y[1, 0] = [0.0, 1.0, -2.0, -1.0]
+    s2 = O.mixture_select_heap(y, 1, band=1e-4)
+    assert s2.selected == [(0,)] and not O.band_is_exact(y, s2)
