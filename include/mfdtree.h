@@ -1,0 +1,229 @@
+/*
+ * libmfdtree -- the mixture draft tree (Multi-Future Drafting) hot path on
+ * MI355X (gfx950), behind a plain C ABI.
+ *
+ * What the calls compute, in the order a decoding round runs them:
+ *
+ *   mfd_logsoftmax_topk    per (tree, mode, position) row of drafter logits:
+ *                          the log-normaliser and the k best tokens.
+ *   mfd_mixture_threshold  the common cut-off: the B-th best best-mode score
+ *                          over all prefixes, counting each prefix once.
+ *   mfd_tree_build         the prefixes that reach the cut-off, merged into
+ *                          one deduplicated tree with ties broken, laid out.
+ *   mfd_tree_mask          ancestor mask and position ids for verification.
+ *   mfd_verify_walk        the verification walk over the target's per-node
+ *                          logits: accepted length tau and the bonus token.
+ *
+ * Sources: the model card "MFD drafter for Qwen3.5-4B (1.42M prompts)"
+ * (summary paragraph: K modes draft in one pass, the tree keeps the B
+ * prefixes with the highest best-mode log-probability, the target verifies
+ * it in one pass, standard tree verification keeps decoding lossless;
+ * "Model": block of 16, 15 drafted positions; "Usage": tree_budget = B,
+ * block_size - 1 = L, temperature = T) and the project page "Multi-Future
+ * Drafting: Mixture Block Drafters for Tree-Verified Speculative Decoding"
+ * ("In one minute": the B-th best score is the common cut-off, each mode
+ * keeps the prefixes that reach it, shared prefixes are built once; "How it
+ * works" step 1: a prefix's probability under a mode is the product of that
+ * mode's per-position probabilities; step 3: best-mode scoring, the union of
+ * the per-mode trees, one verification pass; Figure 2: one distribution per
+ * position per mode, tau counts the bonus token).
+ *
+ * Conventions for every call
+ *   - Pointers named as device pointers are device memory on the current HIP
+ *     device, contiguous, row-major, caller-owned.  The library allocates
+ *     nothing and keeps no state between calls; calls on different streams
+ *     are independent when their workspaces differ.
+ *   - Every call is asynchronous on `stream` (0 = the null stream).
+ *   - A return value other than MFD_OK means nothing was launched; a
+ *     thread-local message is available from mfd_last_error().
+ *   - Data-dependent problems are reported per tree in an optional device
+ *     array `status` [N] (int32, bit flags OR-ed in; the caller zeroes it):
+ *       MFD_TREE_NONFINITE        a NaN or +inf drafter logit in the tree
+ *       MFD_TREE_CAPACITY         the tree exceeded a working capacity (see
+ *                                 mfd_tree_build); that tree's outputs are
+ *                                 not valid
+ *       MFD_TREE_BAD_TEMPERATURE  temperature < 0 or not finite
+ *   - Shapes: N trees, K modes, L drafted positions, V vocabulary, B budget
+ *     (drafted nodes; the root is extra, so trees have B+1 rows), k = number
+ *     of ranked candidates kept per row (use k = min(B, V)).
+ *   - Scores are natural-log probabilities in fp64.
+ *
+ * Limits: 1 <= K <= 32, 1 <= L <= 32, 1 <= V < 2^20, 0 <= B <= 16383,
+ *         1 <= k <= min(V, 2048); the tree calls also need K*k <= 16384.
+ */
+#ifndef MFDTREE_H
+#define MFDTREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mfd_status {
+  MFD_OK = 0,
+  MFD_ERR_INVALID_ARG = 1, /* a size, pointer or flag is out of range */
+  MFD_ERR_DTYPE = 2,       /* unsupported element type */
+  MFD_ERR_WORKSPACE = 3,   /* workspace missing or smaller than mfd_workspace_size */
+  MFD_ERR_DEVICE = 4       /* the HIP runtime refused a launch or query */
+} mfd_status;
+
+typedef enum mfd_dtype { MFD_BF16 = 0, MFD_F32 = 1 } mfd_dtype;
+
+typedef enum mfd_op {
+  MFD_OP_LOGSOFTMAX_TOPK = 0,
+  MFD_OP_MIXTURE_THRESHOLD = 1,
+  MFD_OP_TREE_BUILD = 2,
+  MFD_OP_TREE_MASK = 3,
+  MFD_OP_VERIFY_WALK = 4
+} mfd_op;
+
+#define MFD_TREE_NONFINITE 1
+#define MFD_TREE_CAPACITY 2
+#define MFD_TREE_BAD_TEMPERATURE 4
+
+/* Message for the last failed call on this host thread ("" if none). */
+const char* mfd_last_error(void);
+
+/* Library version string. */
+const char* mfd_version(void);
+
+/* Bytes of device workspace the call `op` needs for these shapes (0 if none).
+ * Arguments a call does not use are ignored.  Returns MFD_ERR_INVALID_ARG for
+ * shapes outside the limits. */
+mfd_status mfd_workspace_size(mfd_op op, int N, int K, int L, int V, int B, size_t* bytes);
+
+/*
+ * Per-(mode, position) log-softmax and top-k ("In one minute" and Figure 2:
+ * each mode gives one distribution per position; step 3: the best-first
+ * searches take each position's candidates from most to least probable).
+ *
+ *   logits    device [N, K, L, V], bf16 (MFD_BF16) or fp32 (MFD_F32), read once.
+ *             Row r = (n, K, L) flattened; must be aligned to the element size.
+ *   lse       device [N, K, L] fp64 out: log sum_v exp(logits[r, v]); -inf for
+ *             a row of only -inf.
+ *   topk_id   device [N, K, L, k] int32 out: token ids by logit descending,
+ *             equal logits by id ascending (-0.0 and +0.0 are equal).
+ *   topk_raw  device [N, K, L, k] fp32 out: the logit of each listed token,
+ *             exactly (bf16 widened to fp32).
+ *   topk_logp device [N, K, L, k] fp32 out or NULL: topk_raw - lse rounded to fp32.
+ *   status    device [N] int32 or NULL: MFD_TREE_NONFINITE is OR-ed in for a
+ *             tree with a NaN or +inf logit (its outputs are then unspecified).
+ *   ws        unused (may be NULL; mfd_workspace_size reports 0).
+ */
+mfd_status mfd_logsoftmax_topk(const void* logits, mfd_dtype dtype, int N, int K, int L, int V, int k,
+                               double* lse, int32_t* topk_id, float* topk_raw, float* topk_logp,
+                               int32_t* status, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The common cut-off ("In one minute": the B-th best score over all modes is
+ * one cut-off shared by every mode; step 3: every prefix is scored by its best
+ * mode).  A prefix t = (t_1..t_d), 1 <= d <= L, scores
+ *     s_k(t) = (sum_{i<=d} raw_k(i, t_i)) - (sum_{i<=d} lse[k, i])
+ * under mode k (both sums fp64, accumulated from i = 1 upward), and
+ * S(t) = max_k s_k(t).  A mode scores only prefixes whose every token is among
+ * its k listed candidates at that position (with k = min(B, V) this changes
+ * nothing among the B best); -inf candidates never count.  Prefixes are
+ * counted once however many modes reach them.
+ *
+ *   inputs    outputs of mfd_logsoftmax_topk for the same N, K, L, k.
+ *   cutoff    device [N] fp64 out: S of the n_select-th best prefix
+ *             (+inf when n_select is 0).
+ *   n_select  device [N] int32 out: min(B, number of prefixes with finite S).
+ *   per_mode_kept device [N, K] int32 out or NULL: number of prefixes with
+ *             s_k >= cutoff under each mode ("each mode keeps the prefixes of
+ *             its block that reach it").
+ *   status    device [N] int32 or NULL: MFD_TREE_CAPACITY when a level of the
+ *             search needs more than the working capacity.
+ *   ws        device workspace of at least mfd_workspace_size(MFD_OP_MIXTURE_THRESHOLD).
+ */
+mfd_status mfd_mixture_threshold(const int32_t* topk_id, const float* topk_raw, const double* lse,
+                                 int N, int K, int L, int k, int B,
+                                 double* cutoff, int32_t* n_select, int32_t* per_mode_kept,
+                                 int32_t* status, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The tree ("In one minute": every node is pulled from the modes that keep it,
+ * shared prefixes are built once; step 3: the B best prefixes over all modes
+ * form one tree, the union of the per-mode trees).  Selects, among prefixes
+ * with S >= cutoff, the first n_select in the order (S descending, best mode
+ * ascending, token ids lexicographically ascending with a proper prefix first);
+ * the best mode of a prefix is the lowest mode attaining S.  The selection is
+ * prefix-closed.  Layout: row 0 is the root (anchor token, depth 0, parent -1,
+ * score 0, best mode -1); rows 1..n_select are the selected prefixes sorted by
+ * (depth, token sequence), so parent[i] < i and siblings are in token order.
+ * Rows n_nodes..B are -1 (score -inf).
+ *
+ *   cutoff, n_select  device [N], normally from mfd_mixture_threshold.  Any
+ *             cutoff at or below the true n_select-th score gives the same tree.
+ *   anchor_token      device [N] int32: the committed token at the root.
+ *   node_token, parent, depth, best_mode  device [N, B+1] int32 out.
+ *   score     device [N, B+1] fp64 out: S of each node.
+ *   n_nodes   device [N] int32 out: n_select + 1.
+ *   status    device [N] int32 or NULL: MFD_TREE_CAPACITY if the prefixes
+ *             reaching the cut-off (or the ties at it) exceed the working
+ *             capacity; that tree's rows are then not valid.
+ *   ws        device workspace of at least mfd_workspace_size(MFD_OP_TREE_BUILD).
+ */
+mfd_status mfd_tree_build(const int32_t* topk_id, const float* topk_raw, const double* lse,
+                          const double* cutoff, const int32_t* n_select, const int32_t* anchor_token,
+                          int N, int K, int L, int k, int B,
+                          int32_t* node_token, int32_t* parent, int32_t* depth, double* score,
+                          int32_t* best_mode, int32_t* n_nodes, int32_t* status,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Tree-verification inputs (model card summary: the target checks the whole
+ * tree in one pass with standard tree verification).  Row i of the mask has
+ * bit j set iff node j is node i or one of its ancestors (the root included).
+ *
+ *   parent, depth  device [N, Bp1] int32, n_nodes device [N] int32 (from mfd_tree_build).
+ *   pos_base  device [N] int64: position id of the root.
+ *   mask_words device [N, Bp1, W] uint64 out, W = ceil(Bp1 / 64); column j is
+ *             bit (j % 64) of word j / 64.  Rows and columns >= n_nodes are 0.
+ *   position_ids device [N, Bp1] int64 out: pos_base + depth; -1 for rows >= n_nodes.
+ *   dense_mask device [N, Bp1, Bp1] uint8 out or NULL: the same mask, one byte per entry.
+ */
+mfd_status mfd_tree_mask(const int32_t* parent, const int32_t* depth, const int32_t* n_nodes,
+                         const int64_t* pos_base, int N, int Bp1,
+                         uint64_t* mask_words, int64_t* position_ids, uint8_t* dense_mask,
+                         hipStream_t stream);
+
+/*
+ * Verification walk (model card summary and project page Figure 2: the target
+ * keeps the future it takes; accepted drafted tokens plus one bonus token).
+ * From the root u = 0: the target's token at u is t* = argmax_v R[u, v] at
+ * T = 0 (equal logits to the lower id), or at T > 0 the Gumbel-max sample
+ *     t* = argmax_v ( fp64(R[u, v]) / fp64(T) + g_v ),  g_v = -log(-log(U_v)),
+ *     U_v = ((w_v >> 12) + 1/2) * 2^-52,
+ *     w_v = lane (v mod 4) of Philox4x64-10(counter = (v div 4, depth(u), 0, 0),
+ *                                           key = (seed[n], 0))
+ * (Salmon et al., "Parallel random numbers: as easy as 1, 2, 3", SC'11).
+ * If u has a child with token t*, the walk moves there and repeats; else it
+ * stops with tau = depth(u) + 1.
+ *
+ *   target_logits device [N, Bp1, V] bf16 or fp32: the target's logits at each
+ *             node (only the rows on the walked path are read).
+ *   node_token, parent, depth, n_nodes  the tree (from mfd_tree_build).
+ *   temperature device [N] fp32; seed device [N] uint64.
+ *   tau       device [N] int32 out (1..L+1; 0 with MFD_TREE_BAD_TEMPERATURE).
+ *   out_tokens device [N, L+1] int32 out: accepted drafted tokens then the
+ *             bonus token; -1 after.
+ *   path_nodes device [N, L+1] int32 out: rows visited, root first; -1 after.
+ *   status    device [N] int32 or NULL: MFD_TREE_BAD_TEMPERATURE.
+ *   ws        unused (may be NULL; mfd_workspace_size reports 0).
+ */
+mfd_status mfd_verify_walk(const void* target_logits, mfd_dtype dtype, int N, int Bp1, int V, int L,
+                           const int32_t* node_token, const int32_t* parent, const int32_t* depth,
+                           const int32_t* n_nodes, const float* temperature, const uint64_t* seed,
+                           int32_t* tau, int32_t* out_tokens, int32_t* path_nodes, int32_t* status,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MFDTREE_H */

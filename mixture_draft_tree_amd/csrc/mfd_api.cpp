@@ -1,0 +1,207 @@
+// C ABI of libmfdtree: argument checks, workspace sizes, error text, launches.
+// Every check happens before any HIP call, so a rejected call launches nothing
+// and touches no device state.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/mfdtree.h"
+#include "mfd_launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mfd_status fail(mfd_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+mfd_status ok() {
+  g_err[0] = 0;
+  return MFD_OK;
+}
+
+mfd_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(MFD_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kMaxK = 32, kMaxL = 32, kMaxV = (1 << 20) - 1, kMaxB = 16383, kMaxTopk = 2048, kMaxKk = 16384;
+
+mfd_status check_dims(int N, int K, int L, int V) {
+  if (N < 0) return fail(MFD_ERR_INVALID_ARG, "N must be >= 0 (got %d)", N);
+  if (K < 1 || K > kMaxK) return fail(MFD_ERR_INVALID_ARG, "K must be in [1, %d] (got %d)", kMaxK, K);
+  if (L < 1 || L > kMaxL) return fail(MFD_ERR_INVALID_ARG, "L must be in [1, %d] (got %d)", kMaxL, L);
+  if (V < 1 || V > kMaxV) return fail(MFD_ERR_INVALID_ARG, "V must be in [1, %d] (got %d)", kMaxV, V);
+  return MFD_OK;
+}
+
+mfd_status check_tree_dims(int N, int K, int L, int k, int B) {
+  if (N < 0) return fail(MFD_ERR_INVALID_ARG, "N must be >= 0 (got %d)", N);
+  if (K < 1 || K > kMaxK) return fail(MFD_ERR_INVALID_ARG, "K must be in [1, %d] (got %d)", kMaxK, K);
+  if (L < 1 || L > kMaxL) return fail(MFD_ERR_INVALID_ARG, "L must be in [1, %d] (got %d)", kMaxL, L);
+  if (B < 0 || B > kMaxB) return fail(MFD_ERR_INVALID_ARG, "B must be in [0, %d] (got %d)", kMaxB, B);
+  if (k < 1 || k > kMaxTopk) return fail(MFD_ERR_INVALID_ARG, "k must be in [1, %d] (got %d)", kMaxTopk, k);
+  if ((long long)K * k > kMaxKk) return fail(MFD_ERR_INVALID_ARG, "K*k must be <= %d (got %lld)", kMaxKk, (long long)K * k);
+  return MFD_OK;
+}
+
+#define REQUIRE_PTR(p)                                                        \
+  do {                                                                        \
+    if ((p) == nullptr) return fail(MFD_ERR_INVALID_ARG, "%s is NULL", #p); \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* mfd_last_error(void) { return g_err; }
+
+const char* mfd_version(void) { return "libmfdtree 0.1 (gfx950)"; }
+
+mfd_status mfd_workspace_size(mfd_op op, int N, int K, int L, int V, int B, size_t* bytes) {
+  REQUIRE_PTR(bytes);
+  *bytes = 0;
+  switch (op) {
+    case MFD_OP_LOGSOFTMAX_TOPK:
+    case MFD_OP_TREE_MASK:
+    case MFD_OP_VERIFY_WALK:
+      if (N < 0) return fail(MFD_ERR_INVALID_ARG, "N must be >= 0 (got %d)", N);
+      return ok();
+    case MFD_OP_MIXTURE_THRESHOLD:
+    case MFD_OP_TREE_BUILD: {
+      mfd_status s = check_dims(N, K, L, V);
+      if (s != MFD_OK) return s;
+      if (B < 0 || B > kMaxB) return fail(MFD_ERR_INVALID_ARG, "B must be in [0, %d] (got %d)", kMaxB, B);
+      const int k = B < V ? (B < 1 ? 1 : B) : V;
+      s = check_tree_dims(N, K, L, k, B);
+      if (s != MFD_OK) return s;
+      *bytes = (size_t)N * mfd::tree_caps(K, L, k, B).ws_bytes_per_tree;
+      return ok();
+    }
+  }
+  return fail(MFD_ERR_INVALID_ARG, "unknown op %d", (int)op);
+}
+
+mfd_status mfd_logsoftmax_topk(const void* logits, mfd_dtype dtype, int N, int K, int L, int V, int k, double* lse,
+                               int32_t* topk_id, float* topk_raw, float* topk_logp, int32_t* status, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  mfd_status s = check_dims(N, K, L, V);
+  if (s != MFD_OK) return s;
+  if (dtype != MFD_BF16 && dtype != MFD_F32) return fail(MFD_ERR_DTYPE, "dtype must be MFD_BF16 or MFD_F32");
+  if (k < 1 || k > kMaxTopk || k > V) return fail(MFD_ERR_INVALID_ARG, "k must be in [1, min(V, %d)] (got %d)", kMaxTopk, k);
+  if (N == 0) return ok();
+  REQUIRE_PTR(logits);
+  REQUIRE_PTR(lse);
+  REQUIRE_PTR(topk_id);
+  REQUIRE_PTR(topk_raw);
+  const size_t esz = dtype == MFD_BF16 ? 2 : 4;
+  if (reinterpret_cast<uintptr_t>(logits) % esz) return fail(MFD_ERR_INVALID_ARG, "logits not aligned to its element size");
+  const long long rows = (long long)N * K * L;
+  if (rows > 0x7FFFFFFFLL) return fail(MFD_ERR_INVALID_ARG, "too many rows (%lld)", rows);
+  return from_hip(mfd::launch_logsoftmax_topk(logits, dtype == MFD_BF16, (int)rows, K * L, V, k, lse, topk_id, topk_raw,
+                                              topk_logp, status, stream),
+                  "mfd_logsoftmax_topk launch");
+}
+
+mfd_status mfd_mixture_threshold(const int32_t* topk_id, const float* topk_raw, const double* lse, int N, int K, int L,
+                                 int k, int B, double* cutoff, int32_t* n_select, int32_t* per_mode_kept,
+                                 int32_t* status, void* ws, size_t ws_bytes, hipStream_t stream) {
+  mfd_status s = check_tree_dims(N, K, L, k, B);
+  if (s != MFD_OK) return s;
+  if (N == 0) return ok();
+  REQUIRE_PTR(topk_id);
+  REQUIRE_PTR(topk_raw);
+  REQUIRE_PTR(lse);
+  REQUIRE_PTR(cutoff);
+  REQUIRE_PTR(n_select);
+  const size_t need = (size_t)N * mfd::tree_caps(K, L, k, B).ws_bytes_per_tree;
+  if (ws == nullptr || ws_bytes < need)
+    return fail(MFD_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws == nullptr ? (size_t)0 : ws_bytes);
+  return from_hip(mfd::launch_mixture_threshold(topk_id, topk_raw, lse, N, K, L, k, B, cutoff, n_select, per_mode_kept,
+                                                status, ws, stream),
+                  "mfd_mixture_threshold launch");
+}
+
+mfd_status mfd_tree_build(const int32_t* topk_id, const float* topk_raw, const double* lse, const double* cutoff,
+                          const int32_t* n_select, const int32_t* anchor_token, int N, int K, int L, int k, int B,
+                          int32_t* node_token, int32_t* parent, int32_t* depth, double* score, int32_t* best_mode,
+                          int32_t* n_nodes, int32_t* status, void* ws, size_t ws_bytes, hipStream_t stream) {
+  mfd_status s = check_tree_dims(N, K, L, k, B);
+  if (s != MFD_OK) return s;
+  if (N == 0) return ok();
+  REQUIRE_PTR(topk_id);
+  REQUIRE_PTR(topk_raw);
+  REQUIRE_PTR(lse);
+  REQUIRE_PTR(cutoff);
+  REQUIRE_PTR(n_select);
+  REQUIRE_PTR(anchor_token);
+  REQUIRE_PTR(node_token);
+  REQUIRE_PTR(parent);
+  REQUIRE_PTR(depth);
+  REQUIRE_PTR(score);
+  REQUIRE_PTR(best_mode);
+  REQUIRE_PTR(n_nodes);
+  const size_t need = (size_t)N * mfd::tree_caps(K, L, k, B).ws_bytes_per_tree;
+  if (ws == nullptr || ws_bytes < need)
+    return fail(MFD_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws == nullptr ? (size_t)0 : ws_bytes);
+  return from_hip(mfd::launch_tree_build(topk_id, topk_raw, lse, cutoff, n_select, anchor_token, N, K, L, k, B,
+                                         node_token, parent, depth, score, best_mode, n_nodes, status, ws, stream),
+                  "mfd_tree_build launch");
+}
+
+mfd_status mfd_tree_mask(const int32_t* parent, const int32_t* depth, const int32_t* n_nodes, const int64_t* pos_base,
+                         int N, int Bp1, uint64_t* mask_words, int64_t* position_ids, uint8_t* dense_mask,
+                         hipStream_t stream) {
+  if (N < 0) return fail(MFD_ERR_INVALID_ARG, "N must be >= 0 (got %d)", N);
+  if (Bp1 < 1 || Bp1 > kMaxB + 1) return fail(MFD_ERR_INVALID_ARG, "Bp1 must be in [1, %d] (got %d)", kMaxB + 1, Bp1);
+  if (N == 0) return ok();
+  REQUIRE_PTR(parent);
+  REQUIRE_PTR(depth);
+  REQUIRE_PTR(n_nodes);
+  REQUIRE_PTR(pos_base);
+  REQUIRE_PTR(mask_words);
+  REQUIRE_PTR(position_ids);
+  return from_hip(
+      mfd::launch_tree_mask(parent, depth, n_nodes, pos_base, N, Bp1, mask_words, position_ids, dense_mask, stream),
+      "mfd_tree_mask launch");
+}
+
+mfd_status mfd_verify_walk(const void* target_logits, mfd_dtype dtype, int N, int Bp1, int V, int L,
+                           const int32_t* node_token, const int32_t* parent, const int32_t* depth,
+                           const int32_t* n_nodes, const float* temperature, const uint64_t* seed, int32_t* tau,
+                           int32_t* out_tokens, int32_t* path_nodes, int32_t* status, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (N < 0) return fail(MFD_ERR_INVALID_ARG, "N must be >= 0 (got %d)", N);
+  if (Bp1 < 1 || Bp1 > kMaxB + 1) return fail(MFD_ERR_INVALID_ARG, "Bp1 must be in [1, %d] (got %d)", kMaxB + 1, Bp1);
+  if (V < 1 || V > kMaxV) return fail(MFD_ERR_INVALID_ARG, "V must be in [1, %d] (got %d)", kMaxV, V);
+  if (L < 1 || L > kMaxL) return fail(MFD_ERR_INVALID_ARG, "L must be in [1, %d] (got %d)", kMaxL, L);
+  if (dtype != MFD_BF16 && dtype != MFD_F32) return fail(MFD_ERR_DTYPE, "dtype must be MFD_BF16 or MFD_F32");
+  if (N == 0) return ok();
+  REQUIRE_PTR(target_logits);
+  REQUIRE_PTR(node_token);
+  REQUIRE_PTR(parent);
+  REQUIRE_PTR(depth);
+  REQUIRE_PTR(n_nodes);
+  REQUIRE_PTR(temperature);
+  REQUIRE_PTR(seed);
+  REQUIRE_PTR(tau);
+  REQUIRE_PTR(out_tokens);
+  REQUIRE_PTR(path_nodes);
+  const size_t esz = dtype == MFD_BF16 ? 2 : 4;
+  if (reinterpret_cast<uintptr_t>(target_logits) % esz)
+    return fail(MFD_ERR_INVALID_ARG, "target_logits not aligned to its element size");
+  return from_hip(mfd::launch_verify_walk(target_logits, dtype == MFD_BF16, N, Bp1, V, L, node_token, parent, depth,
+                                          n_nodes, temperature, seed, tau, out_tokens, path_nodes, status, stream),
+                  "mfd_verify_walk launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,235 @@
+// Device helpers shared by the gfx950 kernels of libmfdtree.
+//
+// Everything here is wave64-native: scans and ballots work on 64 lanes, and
+// block-level helpers take the block size as a template argument so loops
+// and LDS sizes are compile-time.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mfd {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+__device__ __forceinline__ int wave_id() { return (int)(threadIdx.x >> 6); }
+__device__ __forceinline__ uint64_t lanemask_lt() { return (1ull << lane_id()) - 1ull; }
+
+// Orders LDS traffic between lanes of one wavefront (no block barrier).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---------------------------------------------------------------- ordered keys
+// Unsigned keys that order like the floating-point values (larger value ->
+// larger key).  -0.0 is folded onto +0.0 so equal values give equal keys.
+
+__device__ __forceinline__ uint32_t bf16_key(uint32_t b) {
+  b &= 0xFFFFu;
+  if (b == 0x8000u) b = 0;
+  return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+}
+__device__ __forceinline__ uint32_t bf16_from_key(uint32_t k) {
+  return (k & 0x8000u) ? (k & 0x7FFFu) : (~k & 0xFFFFu);
+}
+__device__ __forceinline__ uint32_t f32_key(uint32_t u) {
+  if (u == 0x80000000u) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ uint32_t f32_from_key(uint32_t k) {
+  return (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+}
+__device__ __forceinline__ uint64_t f64_key(double d) {
+  uint64_t u = (uint64_t)__double_as_longlong(d);
+  if (u == 0x8000000000000000ull) u = 0;
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+__device__ __forceinline__ double f64_from_key(uint64_t k) {
+  uint64_t u = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
+  return __longlong_as_double((long long)u);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float((b & 0xFFFFu) << 16); }
+
+// ---------------------------------------------------------------- scans
+
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
+
+// Exclusive scan over the block; `total` receives the block sum.  `smem` needs
+// NT/64 ints.  Contains barriers: every thread of the block must call it.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* smem, int* total) {
+  constexpr int NW = NT / kWave;
+  const int lane = lane_id(), wid = wave_id();
+  int x = wave_inclusive_scan(v);
+  if (lane == kWave - 1) smem[wid] = x;
+  __syncthreads();
+  if (wid == 0) {
+    int w = (lane < NW) ? smem[lane] : 0;
+    w = wave_inclusive_scan(w);
+    if (lane < NW) smem[lane] = w;
+  }
+  __syncthreads();
+  int prefix = (wid > 0 ? smem[wid - 1] : 0) + x - v;
+  *total = smem[NW - 1];
+  __syncthreads();
+  return prefix;
+}
+
+template <int NT>
+__device__ __forceinline__ int block_sum(int v, int* smem) {
+  int total;
+  block_exclusive_scan<NT>(v, smem, &total);
+  return total;
+}
+
+// ---------------------------------------------------------------- bitonic sort
+// Sorts a[0..n) ascending in LDS; n must be a power of two.  Barriers inside.
+template <int NT>
+__device__ void block_bitonic_sort(uint64_t* a, int n) {
+  for (int size = 2; size <= n; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int t = threadIdx.x; t < (n >> 1); t += NT) {
+        const int i = 2 * t - (t & (stride - 1));
+        const int j = i + stride;
+        const bool up = (i & size) == 0;
+        const uint64_t x = a[i], y = a[j];
+        if ((x > y) == up) {
+          a[i] = y;
+          a[j] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__host__ __device__ __forceinline__ int next_pow2(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+// ---------------------------------------------------------------- radix select
+// Wave 0 of the block: given a 256-bin histogram, find the digit holding the
+// `remaining`-th largest element and how many lie strictly above that digit.
+__device__ __forceinline__ void wave_pick_digit(const uint32_t* hist, int remaining, int* out_digit,
+                                                int* out_above) {
+  const int lane = lane_id();
+  int c[4];
+  int sum = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    c[j] = (int)hist[255 - 4 * lane - j];
+    sum += c[j];
+  }
+  const int incl = wave_inclusive_scan(sum);
+  const int excl = incl - sum;
+  if (excl < remaining && remaining <= incl) {
+    int cum = excl;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (cum + c[j] >= remaining) {
+        *out_digit = 255 - 4 * lane - j;
+        *out_above = cum;
+        break;
+      }
+      cum += c[j];
+    }
+  }
+}
+
+// The rank-th largest (rank >= 1) 64-bit key among the items i in [0, n) for
+// which get(i, &key) returns true.  The caller guarantees at least `rank`
+// such items.  `hist` needs 256 uint32, `sh` 2 ints.  Barriers inside.
+template <int NT, int BITS, typename Get>
+__device__ uint64_t block_kth_largest(int n, int rank, Get get, uint32_t* hist, int* sh) {
+  uint64_t prefix = 0;
+  int remaining = rank;
+  for (int shift = BITS - 8; shift >= 0; shift -= 8) {
+    for (int i = threadIdx.x; i < 256; i += NT) hist[i] = 0;
+    __syncthreads();
+    const uint64_t hi_mask = (shift + 8 >= 64) ? 0ull : (~0ull << (shift + 8));
+    for (int i = threadIdx.x; i < n; i += NT) {
+      uint64_t key;
+      if (get(i, &key) && ((key & hi_mask) == (prefix & hi_mask)))
+        atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+      int digit = 0, above = 0;
+      wave_pick_digit(hist, remaining, &digit, &above);
+      // exactly one lane found it; spread with a max-reduce
+      int d = digit, a = above;
+#pragma unroll
+      for (int o = kWave / 2; o > 0; o >>= 1) {
+        d = max(d, __shfl_xor(d, o, kWave));
+        a = max(a, __shfl_xor(a, o, kWave));
+      }
+      if (threadIdx.x == 0) {
+        sh[0] = d;
+        sh[1] = a;
+      }
+    }
+    __syncthreads();
+    prefix |= (uint64_t)sh[0] << shift;
+    remaining -= sh[1];
+    __syncthreads();
+  }
+  return prefix;
+}
+
+// ---------------------------------------------------------------- Philox4x64-10
+// Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3",
+// SC'11: two 64x64->128 multiplies per round, key bumped by Weyl constants.
+struct Philox4 {
+  uint64_t v[4];
+};
+
+__device__ __forceinline__ Philox4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3, uint64_t k0,
+                                                 uint64_t k1) {
+  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t lo0 = M0 * c0, hi0 = __umul64hi(M0, c0);
+    const uint64_t lo1 = M1 * c2, hi1 = __umul64hi(M1, c2);
+    const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+    k0 += W0;
+    k1 += W1;
+  }
+  Philox4 out;
+  out.v[0] = c0;
+  out.v[1] = c1;
+  out.v[2] = c2;
+  out.v[3] = c3;
+  return out;
+}
+
+// Standard Gumbel noise from one 64-bit word: U = ((w >> 12) + 1/2) 2^-52.
+__device__ __forceinline__ double gumbel_from_word(uint64_t w) {
+  const double u = ((double)(w >> 12) + 0.5) * 0x1.0p-52;
+  return -log(-log(u));
+}
+
+}  // namespace mfd

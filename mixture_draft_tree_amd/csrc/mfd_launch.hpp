@@ -1,0 +1,47 @@
+// Host-side launchers of the libmfdtree kernels (one per C-ABI call).  The
+// C-ABI layer validates arguments, then calls these; they only size LDS and
+// grids and launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/mfdtree.h"
+
+namespace mfd {
+
+hipError_t launch_logsoftmax_topk(const void* logits, bool bf16, int rows, int rows_per_tree, long long V, int k,
+                                  double* lse, int32_t* topk_id, float* topk_raw, float* topk_logp,
+                                  int32_t* status, hipStream_t stream);
+
+// Working capacities of the tree search for one tree (shared by the threshold
+// and build calls, and by the workspace query).
+struct TreeCaps {
+  int sort_cap;   // children of one level that fit the LDS sort (power of two)
+  int ent_cap;    // per-mode entries over all levels
+  int node_cap;   // unique prefixes over all levels
+  size_t ws_bytes_per_tree;
+  size_t lds_bytes;
+};
+TreeCaps tree_caps(int K, int L, int k, int B);
+
+hipError_t launch_mixture_threshold(const int32_t* topk_id, const float* topk_raw, const double* lse, int N, int K,
+                                    int L, int k, int B, double* cutoff, int32_t* n_select, int32_t* per_mode_kept,
+                                    int32_t* status, void* ws, hipStream_t stream);
+
+hipError_t launch_tree_build(const int32_t* topk_id, const float* topk_raw, const double* lse, const double* cutoff,
+                             const int32_t* n_select, const int32_t* anchor, int N, int K, int L, int k, int B,
+                             int32_t* node_token, int32_t* parent, int32_t* depth, double* score,
+                             int32_t* best_mode, int32_t* n_nodes, int32_t* status, void* ws, hipStream_t stream);
+
+hipError_t launch_tree_mask(const int32_t* parent, const int32_t* depth, const int32_t* n_nodes,
+                            const int64_t* pos_base, int N, int Bp1, uint64_t* mask_words, int64_t* position_ids,
+                            uint8_t* dense_mask, hipStream_t stream);
+
+hipError_t launch_verify_walk(const void* target, bool bf16, int N, int Bp1, long long V, int L,
+                              const int32_t* node_token, const int32_t* parent, const int32_t* depth,
+                              const int32_t* n_nodes, const float* temperature, const uint64_t* seed, int32_t* tau,
+                              int32_t* out_tokens, int32_t* path_nodes, int32_t* status, hipStream_t stream);
+
+}  // namespace mfd

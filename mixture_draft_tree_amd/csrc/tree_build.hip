@@ -1,0 +1,694 @@
+// Common cut-off and tree construction for the mixture draft tree.
+//
+// The tree is the B best prefixes by best-mode score, which is the union of
+// the per-mode trees at the common cut-off (project page, "In one minute" and
+// "How it works" step 3).  Both calls here run the same level-synchronous
+// search over prefix depth, one 1024-thread workgroup per tree:
+//
+//   level d:  every kept (node, mode) entry of depth d-1 expands into the
+//             candidates of row (mode, d) whose score reaches the threshold.
+//             Candidates are sorted by rank, so the expansion of one entry is
+//             a prefix of its row, found by binary search (scores only fall
+//             with depth: log-probabilities are <= 0).  The children of all
+//             entries are written as 64-bit keys (parent node, token, mode,
+//             slot) into LDS and bitonic-sorted, so the copies of one prefix
+//             produced by different modes become adjacent: each run is one
+//             node (built once, "shared prefixes are built once"), its score
+//             is the run's maximum and its best mode the first mode attaining
+//             it.  The run members become the node's per-mode entries for the
+//             next level.
+//
+// mfd_mixture_threshold starts from a lower bound on the cut-off (any single
+// mode's B-th depth-1 candidate) and, after every level, raises the threshold
+// to the B-th best score among the unique nodes found so far -- a valid lower
+// bound on the final cut-off, since those nodes are distinct prefixes.  Every
+// prefix scoring at least the final cut-off is still generated (its parent
+// scores at least as much under the same mode), so the B-th best found node
+// is the exact cut-off.  If one level would overflow the LDS sort, the
+// threshold is first raised by bisection on a lower bound of the unique count
+// (each parent counts only its largest per-mode child set).
+//
+// mfd_tree_build runs the same search at the fixed cut-off, so it materialises
+// exactly the prefixes that reach it (the per-mode keeps and their union),
+// breaks the ties at the cut-off by (best mode, token sequence), and lays the
+// selection out by (depth, token sequence).
+#include <math.h>
+
+#include "mfd_device.hpp"
+#include "mfd_launch.hpp"
+
+namespace mfd {
+
+namespace {
+
+constexpr int kNT = 1024;
+constexpr int kMaxSort = 16384;
+
+// Per-tree workspace layout (offsets in bytes from the tree's base).
+struct WsLayout {
+  size_t node_parent, node_token, node_depth, node_S, node_mu, node_aux;
+  size_t ent_node, ent_mode, ent_raw, ent_s;
+  size_t fr, fr_off;
+  size_t ch_raw, ch_s, ch_mode, ch_pnode, ch_tok, grp;
+  size_t total;
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+__host__ __device__ inline WsLayout ws_layout(int sort_cap, int ent_cap, int node_cap) {
+  WsLayout w;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t r = o;
+    o = align256(o + bytes);
+    return r;
+  };
+  w.node_parent = take((size_t)node_cap * 4);
+  w.node_token = take((size_t)node_cap * 4);
+  w.node_depth = take((size_t)node_cap * 4);
+  w.node_S = take((size_t)node_cap * 8);
+  w.node_mu = take((size_t)node_cap * 4);
+  w.node_aux = take((size_t)node_cap * 4);
+  w.ent_node = take((size_t)ent_cap * 4);
+  w.ent_mode = take((size_t)ent_cap * 4);
+  w.ent_raw = take((size_t)ent_cap * 8);
+  w.ent_s = take((size_t)ent_cap * 8);
+  w.fr = take((size_t)ent_cap * 4);
+  w.fr_off = take((size_t)ent_cap * 4);
+  w.ch_raw = take((size_t)sort_cap * 8);
+  w.ch_s = take((size_t)sort_cap * 8);
+  w.ch_mode = take((size_t)sort_cap * 4);
+  w.ch_pnode = take((size_t)sort_cap * 4);
+  w.ch_tok = take((size_t)sort_cap * 4);
+  w.grp = take((size_t)sort_cap * 4);
+  w.total = o;
+  return w;
+}
+
+struct TreeArgs {
+  const int32_t* topk_id;
+  const float* topk_raw;
+  const double* lse;
+  int K, L, k, B;
+  int sort_cap, ent_cap, node_cap, tie_cap;
+  unsigned char* ws;
+  size_t ws_stride;
+  int32_t* status;
+  // threshold outputs
+  double* cutoff_out;
+  int32_t* n_select_out;
+  int32_t* per_mode_kept;
+  // build inputs / outputs
+  const double* cutoff_in;
+  const int32_t* n_select_in;
+  const int32_t* anchor;
+  int32_t* node_token;
+  int32_t* parent;
+  int32_t* depth;
+  double* score;
+  int32_t* best_mode;
+  int32_t* n_nodes;
+};
+
+struct Tree {
+  int32_t *node_parent, *node_token, *node_depth, *node_mu, *node_aux;
+  double* node_S;
+  int32_t *ent_node, *ent_mode;
+  double *ent_raw, *ent_s;
+  int32_t *fr, *fr_off;
+  double *ch_raw, *ch_s;
+  int32_t *ch_mode, *ch_pnode, *ch_tok, *grp;
+};
+
+struct Ctl {
+  double tau;
+  int node_count, ent_count, fsize, fail;
+  int C;
+  int level_start[34];
+  int sh[8];
+  int scan[kNT / kWave];
+  uint32_t hist[256];
+  int kept[32];
+};
+
+__device__ __forceinline__ Tree tree_ptrs(const TreeArgs& a, int n) {
+  const WsLayout w = ws_layout(a.sort_cap, a.ent_cap, a.node_cap);
+  unsigned char* b = a.ws + (size_t)n * a.ws_stride;
+  Tree t;
+  t.node_parent = (int32_t*)(b + w.node_parent);
+  t.node_token = (int32_t*)(b + w.node_token);
+  t.node_depth = (int32_t*)(b + w.node_depth);
+  t.node_S = (double*)(b + w.node_S);
+  t.node_mu = (int32_t*)(b + w.node_mu);
+  t.node_aux = (int32_t*)(b + w.node_aux);
+  t.ent_node = (int32_t*)(b + w.ent_node);
+  t.ent_mode = (int32_t*)(b + w.ent_mode);
+  t.ent_raw = (double*)(b + w.ent_raw);
+  t.ent_s = (double*)(b + w.ent_s);
+  t.fr = (int32_t*)(b + w.fr);
+  t.fr_off = (int32_t*)(b + w.fr_off);
+  t.ch_raw = (double*)(b + w.ch_raw);
+  t.ch_s = (double*)(b + w.ch_s);
+  t.ch_mode = (int32_t*)(b + w.ch_mode);
+  t.ch_pnode = (int32_t*)(b + w.ch_pnode);
+  t.ch_tok = (int32_t*)(b + w.ch_tok);
+  t.grp = (int32_t*)(b + w.grp);
+  return t;
+}
+
+// Number of leading candidates j of a rank-sorted row with
+// (raw + x_j) - norm >= tau and x_j > -inf.
+__device__ __forceinline__ int count_children(const float* vals, int k, double raw, double norm, double tau) {
+  int lo = 0, hi = k;  // answer in [lo, hi]
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    const float x = vals[mid];
+    const bool ok = (x != -INFINITY) && ((raw + (double)x) - norm >= tau);
+    if (ok) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// Chunked exclusive scan of `val(i)` for i in [0, n) writing out[i]; returns the total.
+template <typename Val, typename Out>
+__device__ int block_scan_range(int n, Val val, Out out, int* scan_smem) {
+  int carry = 0;
+  for (int base = 0; base < n; base += kNT) {
+    const int i = base + (int)threadIdx.x;
+    const int v = (i < n) ? val(i) : 0;
+    int tot;
+    const int ex = block_exclusive_scan<kNT>(v, scan_smem, &tot);
+    if (i < n) out(i, carry + ex, v);
+    carry += tot;
+  }
+  __syncthreads();  // outputs visible to the whole block
+  return carry;
+}
+
+// The search.  Returns with ctl.node_count nodes (node 0 = root) and
+// ctl.ent_count entries; ctl.fail set on capacity overflow.
+template <bool BUILD>
+__device__ void level_search(const TreeArgs& a, const Tree& t, int n, Ctl& ctl, uint64_t* keys, const double* norm) {
+  const int K = a.K, L = a.L, k = a.k, B = a.B;
+  const int tid = threadIdx.x;
+  const int Lp1 = L + 1;
+
+  for (int d = 1; d <= L; ++d) {
+    if (tid == 0) ctl.level_start[d] = ctl.node_count;
+    __syncthreads();
+    const int fsize = ctl.fsize;
+    if (fsize == 0 || ctl.fail) break;
+    double tau = ctl.tau;
+
+    // 1. per frontier entry: number of children reaching tau; exclusive offsets
+    auto count_at = [&](int f, double th) -> int {
+      const int e = t.fr[f];
+      const int m = t.ent_mode[e];
+      const float* vals = a.topk_raw + ((size_t)(n * K + m) * L + (d - 1)) * k;
+      return count_children(vals, k, t.ent_raw[e], norm[m * Lp1 + d], th);
+    };
+    int C = block_scan_range(
+        fsize, [&](int f) { return count_at(f, tau); }, [&](int f, int off, int) { t.fr_off[f] = off; },
+        ctl.scan);
+
+    const bool too_big = (C > a.sort_cap) || (ctl.ent_count + C > a.ent_cap) || (ctl.node_count + C > a.node_cap);
+    if (!BUILD && too_big) {
+      // Raise tau by bisection on a lower bound of the unique prefixes
+      // reaching it: nodes already found plus, per parent node, its largest
+      // per-mode child count.
+      uint64_t lo = f64_key(tau == -INFINITY ? -INFINITY : tau), hi = f64_key(INFINITY);
+      for (int it = 0; it < 70 && hi - lo > 1; ++it) {
+        const uint64_t mid = lo + (hi - lo) / 2;
+        const double th = f64_from_key(mid);
+        int local = 0;
+        for (int f = tid; f < fsize; f += kNT) {
+          const int node = t.ent_node[t.fr[f]];
+          if (f > 0 && t.ent_node[t.fr[f - 1]] == node) continue;  // group head only
+          int best = 0;
+          for (int g = f; g < fsize && t.ent_node[t.fr[g]] == node; ++g) best = max(best, count_at(g, th));
+          local += best;
+        }
+        for (int i = 1 + tid; i < ctl.node_count; i += kNT) local += (t.node_S[i] >= th) ? 1 : 0;
+        const int cnt = block_sum<kNT>(local, ctl.scan);
+        if (cnt >= B) lo = mid;
+        else hi = mid;
+      }
+      tau = f64_from_key(lo);
+      if (tid == 0) ctl.tau = tau;
+      C = block_scan_range(
+          fsize, [&](int f) { return count_at(f, tau); }, [&](int f, int off, int) { t.fr_off[f] = off; },
+          ctl.scan);
+    }
+    if ((C > a.sort_cap) || (ctl.ent_count + C > a.ent_cap) || (ctl.node_count + C > a.node_cap)) {
+      if (tid == 0) ctl.fail = 1;
+      __syncthreads();
+      break;
+    }
+    if (C == 0) break;
+
+    // 2. materialise children and their sort keys
+    for (int c = tid; c < C; c += kNT) {
+      int lo = 0, hi = fsize - 1;  // largest f with fr_off[f] <= c
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (t.fr_off[mid] <= c) lo = mid;
+        else hi = mid - 1;
+      }
+      const int f = lo;
+      const int e = t.fr[f];
+      const int m = t.ent_mode[e];
+      const int j = c - t.fr_off[f];
+      const size_t row = ((size_t)(n * K + m) * L + (d - 1)) * k;
+      const float x = a.topk_raw[row + j];
+      const int tok = a.topk_id[row + j];
+      const double raw = t.ent_raw[e] + (double)x;
+      const double s = raw - norm[m * Lp1 + d];
+      const int pnode = t.ent_node[e];
+      t.ch_raw[c] = raw;
+      t.ch_s[c] = s;
+      t.ch_mode[c] = m;
+      t.ch_pnode[c] = pnode;
+      t.ch_tok[c] = tok;
+      keys[c] = ((uint64_t)pnode << 40) | ((uint64_t)tok << 20) | ((uint64_t)m << 15) | (uint64_t)c;
+    }
+    const int P = next_pow2(C);
+    for (int c = C + tid; c < P; c += kNT) keys[c] = ~0ull;
+    __syncthreads();
+    block_bitonic_sort<kNT>(keys, P);
+
+    // 3. runs of equal (parent, token) are one node
+    const int node0 = ctl.node_count, ent0 = ctl.ent_count;
+    const int G = block_scan_range(
+        C, [&](int i) { return (i == 0 || (keys[i] >> 20) != (keys[i - 1] >> 20)) ? 1 : 0; },
+        [&](int i, int off, int head) { t.grp[i] = head ? off : -1; }, ctl.scan);
+    // each run head builds its node; each member records its entry
+    for (int i = tid; i < C; i += kNT) {
+      if (t.grp[i] < 0) continue;
+      const int g = t.grp[i];
+      const uint64_t prefix = keys[i] >> 20;
+      double best = -INFINITY;
+      int mu = -1;
+      int j = i;
+      for (; j < C && (keys[j] >> 20) == prefix; ++j) {
+        const int c = (int)(keys[j] & 0x7FFFu);
+        const double s = t.ch_s[c];
+        if (mu < 0 || s > best) {
+          best = s;
+          mu = t.ch_mode[c];
+        }
+      }
+      const int node = node0 + g;
+      const int c0 = (int)(keys[i] & 0x7FFFu);
+      t.node_parent[node] = t.ch_pnode[c0];
+      t.node_token[node] = t.ch_tok[c0];
+      t.node_depth[node] = d;
+      t.node_S[node] = best;
+      t.node_mu[node] = mu;
+      for (int q = i; q < j; ++q) {
+        const int c = (int)(keys[q] & 0x7FFFu);
+        const int e = ent0 + q;
+        t.ent_node[e] = node;
+        t.ent_mode[e] = t.ch_mode[c];
+        t.ent_raw[e] = t.ch_raw[c];
+        t.ent_s[e] = t.ch_s[c];
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      ctl.node_count = node0 + G;
+      ctl.ent_count = ent0 + C;
+    }
+    __syncthreads();
+
+    // 4. (threshold call) raise tau to the B-th best unique node so far
+    if (!BUILD) {
+      int local = 0;
+      for (int i = 1 + tid; i < ctl.node_count; i += kNT) local += (t.node_S[i] >= tau) ? 1 : 0;
+      const int alive = block_sum<kNT>(local, ctl.scan);
+      if (alive >= B && B > 0) {
+        const double tcur = tau;
+        auto get = [&](int i, uint64_t* key) -> bool {
+          const double s = t.node_S[i + 1];
+          if (!(s >= tcur)) return false;
+          *key = f64_key(s);
+          return true;
+        };
+        const uint64_t kb = block_kth_largest<kNT, 64>(ctl.node_count - 1, B, get, ctl.hist, ctl.sh);
+        const double nt = f64_from_key(kb);
+        if (nt > tau) tau = nt;
+        if (tid == 0) ctl.tau = tau;
+      }
+      __syncthreads();
+    }
+
+    // 5. next frontier: this level's entries still reaching tau
+    const double tnext = ctl.tau;
+    const int fs = block_scan_range(
+        C, [&](int i) { return (t.ent_s[ent0 + i] >= tnext) ? 1 : 0; },
+        [&](int i, int off, int v) {
+          if (v) t.fr[off] = ent0 + i;
+        },
+        ctl.scan);
+    if (tid == 0) ctl.fsize = fs;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    for (int d = 1; d <= L + 1; ++d)
+      if (ctl.level_start[d] < 0) ctl.level_start[d] = ctl.node_count;
+  }
+  __syncthreads();
+}
+
+template <bool BUILD>
+__global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
+  const int n = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int K = a.K, L = a.L, k = a.k, B = a.B, Lp1 = L + 1;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  uint64_t* keys = reinterpret_cast<uint64_t*>(smem_raw);
+  double* norm = reinterpret_cast<double*>(keys + a.sort_cap);
+  Ctl& ctl = *reinterpret_cast<Ctl*>(norm + K * Lp1);
+  const Tree t = tree_ptrs(a, n);
+
+  // norm[m][d] = sum_{i<d} lse[m][i], fp64, from i = 0 upward
+  for (int m = tid; m < K; m += kNT) {
+    double acc = 0.0;
+    norm[m * Lp1] = 0.0;
+    for (int i = 0; i < L; ++i) {
+      acc = acc + a.lse[(size_t)(n * K + m) * L + i];
+      norm[m * Lp1 + i + 1] = acc;
+    }
+  }
+  for (int i = tid; i < 32; i += kNT) ctl.kept[i] = 0;
+  if (tid == 0) {
+    ctl.node_count = 1;
+    ctl.ent_count = K;
+    ctl.fsize = K;
+    ctl.fail = 0;
+    for (int d = 0; d < 34; ++d) ctl.level_start[d] = -1;
+    t.node_parent[0] = -1;
+    t.node_token[0] = -1;
+    t.node_depth[0] = 0;
+    t.node_S[0] = 0.0;
+    t.node_mu[0] = -1;
+  }
+  for (int m = tid; m < K; m += kNT) {
+    t.ent_node[m] = 0;
+    t.ent_mode[m] = m;
+    t.ent_raw[m] = 0.0;
+    t.ent_s[m] = 0.0;
+    t.fr[m] = m;
+  }
+  __syncthreads();
+
+  double cutoff_in = 0.0;
+  int nsel_in = 0;
+  if (BUILD) {
+    cutoff_in = a.cutoff_in[n];
+    nsel_in = a.n_select_in[n];
+    if (nsel_in > B) nsel_in = B;
+    if (nsel_in < 0) nsel_in = 0;
+    if (tid == 0) {
+      ctl.tau = cutoff_in;
+      if (nsel_in == 0) ctl.fsize = 0;
+    }
+  } else {
+    if (tid == 0) {
+      double t0 = -INFINITY;
+      if (B == 0) ctl.fsize = 0;
+      else if (k >= B) {
+        for (int m = 0; m < K; ++m) {
+          const float x = a.topk_raw[((size_t)(n * K + m) * L) * k + (B - 1)];
+          if (x != -INFINITY) {
+            const double s0 = (0.0 + (double)x) - norm[m * Lp1 + 1];
+            if (s0 > t0) t0 = s0;
+          }
+        }
+      }
+      ctl.tau = t0;
+    }
+  }
+  __syncthreads();
+
+  level_search<BUILD>(a, t, n, ctl, keys, norm);
+
+  const int nc = ctl.node_count;
+  const int fail = ctl.fail;
+  if (fail && a.status && tid == 0) atomicOr(&a.status[n], MFD_TREE_CAPACITY);
+
+  if (!BUILD) {
+    // ---------------------------------------------------------- cut-off
+    const int total = nc - 1;
+    int nsel = 0;
+    double cut = INFINITY;
+    if (!fail && B > 0 && total > 0) {
+      if (total >= B) {
+        nsel = B;
+        auto get = [&](int i, uint64_t* key) -> bool {
+          *key = f64_key(t.node_S[i + 1]);
+          return true;
+        };
+        cut = f64_from_key(block_kth_largest<kNT, 64>(total, B, get, ctl.hist, ctl.sh));
+      } else {
+        nsel = total;
+        auto get = [&](int i, uint64_t* key) -> bool {
+          *key = f64_key(t.node_S[i + 1]);
+          return true;
+        };
+        cut = f64_from_key(block_kth_largest<kNT, 64>(total, total, get, ctl.hist, ctl.sh));
+      }
+    }
+    if (fail) cut = NAN;
+    if (a.per_mode_kept) {
+      for (int e = K + tid; e < ctl.ent_count; e += kNT)
+        if (!fail && nsel > 0 && t.ent_s[e] >= cut) atomicAdd(&ctl.kept[t.ent_mode[e]], 1);
+      __syncthreads();
+      for (int m = tid; m < K; m += kNT) a.per_mode_kept[(size_t)n * K + m] = ctl.kept[m];
+    }
+    if (tid == 0) {
+      a.cutoff_out[n] = cut;
+      a.n_select_out[n] = nsel;
+    }
+    return;
+  }
+
+  // ------------------------------------------------------------ tree build
+  const int Bp1 = B + 1;
+  const int M = nc - 1;
+  int nsel = fail ? 0 : (nsel_in < M ? nsel_in : M);
+  // node_aux: 1 = selected, then the canonical row index
+  if (M > nsel && nsel > 0) {
+    auto get = [&](int i, uint64_t* key) -> bool {
+      *key = f64_key(t.node_S[i + 1]);
+      return true;
+    };
+    const double cstar = f64_from_key(block_kth_largest<kNT, 64>(M, nsel, get, ctl.hist, ctl.sh));
+    int lgt = 0;
+    for (int i = 1 + tid; i < nc; i += kNT) lgt += (t.node_S[i] > cstar) ? 1 : 0;
+    const int gt = block_sum<kNT>(lgt, ctl.scan);
+    const int need = nsel - gt;
+    // collect the ties at cstar (node ids in node_aux order via keys[] as int list)
+    int32_t* tied = reinterpret_cast<int32_t*>(keys);
+    const int T = block_scan_range(
+        M, [&](int i) { return (t.node_S[i + 1] == cstar) ? 1 : 0; },
+        [&](int i, int off, int v) {
+          if (v && off < a.tie_cap) tied[off] = i + 1;
+        },
+        ctl.scan);
+    for (int i = 1 + tid; i < nc; i += kNT) t.node_aux[i] = (t.node_S[i] > cstar) ? 1 : 0;
+    __syncthreads();
+    if (T > a.tie_cap) {
+      if (tid == 0) {
+        if (a.status) atomicOr(&a.status[n], MFD_TREE_CAPACITY);
+        ctl.fail = 1;
+      }
+    } else {
+      // token paths of the tied nodes, then rank by (best mode, tokens)
+      int32_t* paths = tied + a.tie_cap;
+      for (int q = tid; q < T; q += kNT) {
+        int node = tied[q];
+        const int dq = t.node_depth[node];
+        for (int x = 0; x < L; ++x) paths[q * L + x] = -1;
+        while (node > 0) {
+          paths[q * L + t.node_depth[node] - 1] = t.node_token[node];
+          node = t.node_parent[node];
+        }
+        (void)dq;
+      }
+      __syncthreads();
+      for (int q = tid; q < T; q += kNT) {
+        const int nq = tied[q];
+        const int mq = t.node_mu[nq], dq = t.node_depth[nq];
+        int rank = 0;
+        for (int r = 0; r < T; ++r) {
+          if (r == q) continue;
+          const int nr = tied[r];
+          const int mr = t.node_mu[nr], dr = t.node_depth[nr];
+          bool less;
+          if (mr != mq) less = mr < mq;
+          else {
+            int x = 0;
+            const int dm = dr < dq ? dr : dq;
+            while (x < dm && paths[r * L + x] == paths[q * L + x]) ++x;
+            if (x < dm) less = paths[r * L + x] < paths[q * L + x];
+            else less = dr < dq;
+          }
+          rank += less ? 1 : 0;
+        }
+        if (rank < need) t.node_aux[nq] = 1;
+      }
+    }
+    __syncthreads();
+  } else {
+    for (int i = 1 + tid; i < nc; i += kNT) t.node_aux[i] = (i - 1 < nsel) ? 1 : 0;
+    __syncthreads();
+  }
+  const int fail2 = ctl.fail;
+
+  // canonical layout: per depth, sort selected nodes by (parent row, token)
+  int base = 1;
+  if (!fail2) {
+    for (int d = 1; d <= L; ++d) {
+      const int s0 = ctl.level_start[d], s1 = ctl.level_start[d + 1];
+      if (s1 <= s0) break;
+      const int cnt = block_scan_range(
+          s1 - s0, [&](int i) { return t.node_aux[s0 + i] == 1 ? 1 : 0; },
+          [&](int i, int off, int v) {
+            if (v) {
+              const int node = s0 + i;
+              const int p = t.node_parent[node];
+              const int prow = (p == 0) ? 0 : (t.node_aux[p] - 2);  // rows of depth d-1 are final
+              keys[off] = ((uint64_t)prow << 36) | ((uint64_t)t.node_token[node] << 16) | (uint64_t)(node - s0);
+            }
+          },
+          ctl.scan);
+      if (cnt == 0) break;
+      const int P = next_pow2(cnt);
+      for (int c = cnt + tid; c < P; c += kNT) keys[c] = ~0ull;
+      __syncthreads();
+      block_bitonic_sort<kNT>(keys, P);
+      for (int i = tid; i < cnt; i += kNT) {
+        const int node = s0 + (int)(keys[i] & 0xFFFFu);
+        const int rowi = base + i;
+        const int p = t.node_parent[node];
+        const int prow = (p == 0) ? 0 : (t.node_aux[p] - 2);
+        const size_t o = (size_t)n * Bp1 + rowi;
+        a.node_token[o] = t.node_token[node];
+        a.parent[o] = prow;
+        a.depth[o] = d;
+        a.score[o] = t.node_S[node];
+        a.best_mode[o] = t.node_mu[node];
+        t.node_aux[node] = rowi + 2;  // canonical row, offset past the flags
+      }
+      __syncthreads();
+      base += cnt;
+    }
+  }
+  const int rows = fail2 ? 1 : base;
+  for (int i = tid; i < Bp1; i += kNT) {
+    const size_t o = (size_t)n * Bp1 + i;
+    if (i == 0) {
+      a.node_token[o] = a.anchor[n];
+      a.parent[o] = -1;
+      a.depth[o] = 0;
+      a.score[o] = 0.0;
+      a.best_mode[o] = -1;
+    } else if (i >= rows) {
+      a.node_token[o] = -1;
+      a.parent[o] = -1;
+      a.depth[o] = -1;
+      a.score[o] = -INFINITY;
+      a.best_mode[o] = -1;
+    }
+  }
+  if (tid == 0) a.n_nodes[n] = rows;
+}
+
+}  // namespace
+
+TreeCaps tree_caps(int K, int L, int k, int B) {
+  TreeCaps c;
+  long long want = 2LL * K * k;
+  if (want < 2LL * (B + 1)) want = 2LL * (B + 1);
+  if (want < 1024) want = 1024;
+  if (want > kMaxSort) want = kMaxSort;
+  c.sort_cap = next_pow2((int)want);
+  c.ent_cap = 4 * c.sort_cap;
+  c.node_cap = 4 * c.sort_cap;
+  if (c.node_cap > 65535) c.node_cap = 65535;  // node ids fit 16 bits in the layout keys
+  const WsLayout w = ws_layout(c.sort_cap, c.ent_cap, c.node_cap);
+  c.ws_bytes_per_tree = w.total;
+  c.lds_bytes = (size_t)c.sort_cap * 8 + (size_t)K * (L + 1) * 8 + sizeof(Ctl) + 64;
+  return c;
+}
+
+static int tie_cap_for(const TreeCaps& c, int L) {
+  // tied ids + paths share the sort buffer: cap * (1 + L) ints <= sort_cap * 2 ints
+  int t = (c.sort_cap * 2) / (1 + L);
+  return t < 1 ? 1 : t;
+}
+
+static hipError_t launch_tree(bool build, TreeArgs& a, int N, hipStream_t stream) {
+  const TreeCaps c = tree_caps(a.K, a.L, a.k, a.B);
+  a.sort_cap = c.sort_cap;
+  a.ent_cap = c.ent_cap;
+  a.node_cap = c.node_cap;
+  a.tie_cap = tie_cap_for(c, a.L);
+  a.ws_stride = c.ws_bytes_per_tree;
+  const void* fn = build ? reinterpret_cast<const void*>(&tree_kernel<true>)
+                         : reinterpret_cast<const void*>(&tree_kernel<false>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)c.lds_bytes);
+  if (e != hipSuccess) return e;
+  if (N == 0) return hipSuccess;
+  if (build) hipLaunchKernelGGL(tree_kernel<true>, dim3(N), dim3(kNT), c.lds_bytes, stream, a);
+  else hipLaunchKernelGGL(tree_kernel<false>, dim3(N), dim3(kNT), c.lds_bytes, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_mixture_threshold(const int32_t* topk_id, const float* topk_raw, const double* lse, int N, int K,
+                                    int L, int k, int B, double* cutoff, int32_t* n_select, int32_t* per_mode_kept,
+                                    int32_t* status, void* ws, hipStream_t stream) {
+  TreeArgs a = {};
+  a.topk_id = topk_id;
+  a.topk_raw = topk_raw;
+  a.lse = lse;
+  a.K = K;
+  a.L = L;
+  a.k = k;
+  a.B = B;
+  a.ws = static_cast<unsigned char*>(ws);
+  a.status = status;
+  a.cutoff_out = cutoff;
+  a.n_select_out = n_select;
+  a.per_mode_kept = per_mode_kept;
+  return launch_tree(false, a, N, stream);
+}
+
+hipError_t launch_tree_build(const int32_t* topk_id, const float* topk_raw, const double* lse, const double* cutoff,
+                             const int32_t* n_select, const int32_t* anchor, int N, int K, int L, int k, int B,
+                             int32_t* node_token, int32_t* parent, int32_t* depth, double* score,
+                             int32_t* best_mode, int32_t* n_nodes, int32_t* status, void* ws, hipStream_t stream) {
+  TreeArgs a = {};
+  a.topk_id = topk_id;
+  a.topk_raw = topk_raw;
+  a.lse = lse;
+  a.K = K;
+  a.L = L;
+  a.k = k;
+  a.B = B;
+  a.ws = static_cast<unsigned char*>(ws);
+  a.status = status;
+  a.cutoff_in = cutoff;
+  a.n_select_in = n_select;
+  a.anchor = anchor;
+  a.node_token = node_token;
+  a.parent = parent;
+  a.depth = depth;
+  a.score = score;
+  a.best_mode = best_mode;
+  a.n_nodes = n_nodes;
+  return launch_tree(true, a, N, stream);
+}
+
+}  // namespace mfd

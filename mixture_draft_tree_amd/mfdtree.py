@@ -1,0 +1,202 @@
+"""ctypes binding of libmfdtree (include/mfdtree.h).
+
+Argument marshalling only: each function checks tensor dtypes, shapes and
+devices, passes raw device pointers and the stream to the library, and raises
+MfdError when the library rejects the call.  Every step of the path runs in the
+library's HIP kernels; importing this module fails if the library is missing.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmfdtree.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing; build it with `python -m mixture_draft_tree_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+MFD_OK, MFD_ERR_INVALID_ARG, MFD_ERR_DTYPE, MFD_ERR_WORKSPACE, MFD_ERR_DEVICE = 0, 1, 2, 3, 4
+MFD_BF16, MFD_F32 = 0, 1
+(MFD_OP_LOGSOFTMAX_TOPK, MFD_OP_MIXTURE_THRESHOLD, MFD_OP_TREE_BUILD,
+ MFD_OP_TREE_MASK, MFD_OP_VERIFY_WALK) = range(5)
+MFD_TREE_NONFINITE, MFD_TREE_CAPACITY, MFD_TREE_BAD_TEMPERATURE = 1, 2, 4
+
+EXPORTED = ["mfd_last_error", "mfd_version", "mfd_workspace_size", "mfd_logsoftmax_topk",
+            "mfd_mixture_threshold", "mfd_tree_build", "mfd_tree_mask", "mfd_verify_walk"]
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+
+_lib.mfd_last_error.restype = ctypes.c_char_p
+_lib.mfd_last_error.argtypes = []
+_lib.mfd_version.restype = ctypes.c_char_p
+_lib.mfd_version.argtypes = []
+_lib.mfd_workspace_size.restype = _i
+_lib.mfd_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i, ctypes.POINTER(_sz)]
+_lib.mfd_logsoftmax_topk.restype = _i
+_lib.mfd_logsoftmax_topk.argtypes = [_p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p]
+_lib.mfd_mixture_threshold.restype = _i
+_lib.mfd_mixture_threshold.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _sz, _p]
+_lib.mfd_tree_build.restype = _i
+_lib.mfd_tree_build.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i,
+                                _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]
+_lib.mfd_tree_mask.restype = _i
+_lib.mfd_tree_mask.argtypes = [_p, _p, _p, _p, _i, _i, _p, _p, _p, _p]
+_lib.mfd_verify_walk.restype = _i
+_lib.mfd_verify_walk.argtypes = [_p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]
+
+
+class MfdError(RuntimeError):
+    def __init__(self, code: int, call: str):
+        self.code = code
+        msg = _lib.mfd_last_error().decode(errors="replace")
+        super().__init__(f"{call} failed with status {code}: {msg}")
+
+
+def _check(code: int, call: str) -> None:
+    if code != MFD_OK:
+        raise MfdError(code, call)
+
+
+def version() -> str:
+    return _lib.mfd_version().decode()
+
+
+def last_error() -> str:
+    return _lib.mfd_last_error().decode(errors="replace")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _want(t: Optional[torch.Tensor], name: str, dtype, shape, optional=False):
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MFD_BF16
+    if t.dtype == torch.float32:
+        return MFD_F32
+    raise ValueError(f"unsupported logits dtype {t.dtype}")
+
+
+def workspace_size(op: int, N: int, K: int, L: int, V: int, B: int) -> int:
+    out = _sz(0)
+    _check(_lib.mfd_workspace_size(op, N, K, L, V, B, ctypes.byref(out)), "mfd_workspace_size")
+    return int(out.value)
+
+
+def mfd_logsoftmax_topk(logits, k, lse, topk_id, topk_raw, topk_logp=None, status=None, stream=None):
+    """logits [N, K, L, V] bf16/fp32 -> lse [N, K, L] fp64, topk_* [N, K, L, k]."""
+    if logits.dim() != 4 or not logits.is_contiguous() or logits.device.type != "cuda":
+        raise ValueError("logits must be a contiguous [N, K, L, V] GPU tensor")
+    N, K, L, V = logits.shape
+    _want(lse, "lse", torch.float64, (N, K, L))
+    _want(topk_id, "topk_id", torch.int32, (N, K, L, k))
+    _want(topk_raw, "topk_raw", torch.float32, (N, K, L, k))
+    _want(topk_logp, "topk_logp", torch.float32, (N, K, L, k), optional=True)
+    _want(status, "status", torch.int32, (N,), optional=True)
+    _check(_lib.mfd_logsoftmax_topk(_ptr(logits), _dtype_code(logits), N, K, L, V, k, _ptr(lse), _ptr(topk_id),
+                                    _ptr(topk_raw), _ptr(topk_logp), _ptr(status), None, 0,
+                                    _stream_handle(stream)), "mfd_logsoftmax_topk")
+
+
+def mfd_mixture_threshold(topk_id, topk_raw, lse, B, cutoff, n_select, per_mode_kept=None, status=None,
+                          ws=None, stream=None):
+    N, K, L, k = topk_id.shape
+    _want(topk_id, "topk_id", torch.int32, (N, K, L, k))
+    _want(topk_raw, "topk_raw", torch.float32, (N, K, L, k))
+    _want(lse, "lse", torch.float64, (N, K, L))
+    _want(cutoff, "cutoff", torch.float64, (N,))
+    _want(n_select, "n_select", torch.int32, (N,))
+    _want(per_mode_kept, "per_mode_kept", torch.int32, (N, K), optional=True)
+    _want(status, "status", torch.int32, (N,), optional=True)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.mfd_mixture_threshold(_ptr(topk_id), _ptr(topk_raw), _ptr(lse), N, K, L, k, B, _ptr(cutoff),
+                                      _ptr(n_select), _ptr(per_mode_kept), _ptr(status), _ptr(ws), ws_bytes,
+                                      _stream_handle(stream)), "mfd_mixture_threshold")
+
+
+def mfd_tree_build(topk_id, topk_raw, lse, cutoff, n_select, anchor_token, B, node_token, parent, depth, score,
+                   best_mode, n_nodes, status=None, ws=None, stream=None):
+    N, K, L, k = topk_id.shape
+    Bp1 = B + 1
+    _want(topk_id, "topk_id", torch.int32, (N, K, L, k))
+    _want(topk_raw, "topk_raw", torch.float32, (N, K, L, k))
+    _want(lse, "lse", torch.float64, (N, K, L))
+    _want(cutoff, "cutoff", torch.float64, (N,))
+    _want(n_select, "n_select", torch.int32, (N,))
+    _want(anchor_token, "anchor_token", torch.int32, (N,))
+    for name, t, dt in (("node_token", node_token, torch.int32), ("parent", parent, torch.int32),
+                        ("depth", depth, torch.int32), ("score", score, torch.float64),
+                        ("best_mode", best_mode, torch.int32)):
+        _want(t, name, dt, (N, Bp1))
+    _want(n_nodes, "n_nodes", torch.int32, (N,))
+    _want(status, "status", torch.int32, (N,), optional=True)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.mfd_tree_build(_ptr(topk_id), _ptr(topk_raw), _ptr(lse), _ptr(cutoff), _ptr(n_select),
+                               _ptr(anchor_token), N, K, L, k, B, _ptr(node_token), _ptr(parent), _ptr(depth),
+                               _ptr(score), _ptr(best_mode), _ptr(n_nodes), _ptr(status), _ptr(ws), ws_bytes,
+                               _stream_handle(stream)), "mfd_tree_build")
+
+
+def mfd_tree_mask(parent, depth, n_nodes, pos_base, mask_words, position_ids, dense_mask=None, stream=None):
+    N, Bp1 = parent.shape
+    W = (Bp1 + 63) // 64
+    _want(parent, "parent", torch.int32, (N, Bp1))
+    _want(depth, "depth", torch.int32, (N, Bp1))
+    _want(n_nodes, "n_nodes", torch.int32, (N,))
+    _want(pos_base, "pos_base", torch.int64, (N,))
+    _want(mask_words, "mask_words", torch.int64, (N, Bp1, W))
+    _want(position_ids, "position_ids", torch.int64, (N, Bp1))
+    _want(dense_mask, "dense_mask", torch.uint8, (N, Bp1, Bp1), optional=True)
+    _check(_lib.mfd_tree_mask(_ptr(parent), _ptr(depth), _ptr(n_nodes), _ptr(pos_base), N, Bp1, _ptr(mask_words),
+                              _ptr(position_ids), _ptr(dense_mask), _stream_handle(stream)), "mfd_tree_mask")
+
+
+def mfd_verify_walk(target_logits, L, node_token, parent, depth, n_nodes, temperature, seed, tau, out_tokens,
+                    path_nodes, status=None, stream=None):
+    """target_logits [N, B+1, V] bf16/fp32; seed [N] int64 holding the uint64 bits."""
+    if target_logits.dim() != 3 or not target_logits.is_contiguous() or target_logits.device.type != "cuda":
+        raise ValueError("target_logits must be a contiguous [N, B+1, V] GPU tensor")
+    N, Bp1, V = target_logits.shape
+    for name, t in (("node_token", node_token), ("parent", parent), ("depth", depth)):
+        _want(t, name, torch.int32, (N, Bp1))
+    _want(n_nodes, "n_nodes", torch.int32, (N,))
+    _want(temperature, "temperature", torch.float32, (N,))
+    _want(seed, "seed", torch.int64, (N,))
+    _want(tau, "tau", torch.int32, (N,))
+    _want(out_tokens, "out_tokens", torch.int32, (N, L + 1))
+    _want(path_nodes, "path_nodes", torch.int32, (N, L + 1))
+    _want(status, "status", torch.int32, (N,), optional=True)
+    _check(_lib.mfd_verify_walk(_ptr(target_logits), _dtype_code(target_logits), N, Bp1, V, L, _ptr(node_token),
+                                _ptr(parent), _ptr(depth), _ptr(n_nodes), _ptr(temperature), _ptr(seed), _ptr(tau),
+                                _ptr(out_tokens), _ptr(path_nodes), _ptr(status), None, 0,
+                                _stream_handle(stream)), "mfd_verify_walk")

@@ -1,0 +1,118 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+symbol, sizes workspaces, and rejects bad arguments before launching anything.
+No call here reaches a kernel, so these run without a GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mfdtree.h")
+
+M = pytest.importorskip("mixture_draft_tree_amd.mfdtree", reason="libmfdtree.so not built")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mfd_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert set(names) == set(M.EXPORTED)
+    lib = ctypes.CDLL(M.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_clean_error():
+    assert "gfx950" in M.version()
+    assert M.last_error() == ""
+
+
+def test_workspace_sizes():
+    for op in (M.MFD_OP_LOGSOFTMAX_TOPK, M.MFD_OP_TREE_MASK, M.MFD_OP_VERIFY_WALK):
+        assert M.workspace_size(op, 64, 8, 15, 151936, 256) == 0
+    one = M.workspace_size(M.MFD_OP_MIXTURE_THRESHOLD, 1, 8, 15, 151936, 256)
+    many = M.workspace_size(M.MFD_OP_MIXTURE_THRESHOLD, 64, 8, 15, 151936, 256)
+    assert one > 0 and many == 64 * one
+    assert M.workspace_size(M.MFD_OP_TREE_BUILD, 1, 16, 15, 248320, 1024) > one
+    assert M.workspace_size(M.MFD_OP_TREE_BUILD, 0, 8, 15, 151936, 256) == 0
+    with pytest.raises(M.MfdError) as e:
+        M.workspace_size(M.MFD_OP_TREE_BUILD, 1, 33, 15, 100, 8)
+    assert e.value.code == M.MFD_ERR_INVALID_ARG and "K must be" in str(e.value)
+    with pytest.raises(M.MfdError):
+        M.workspace_size(M.MFD_OP_TREE_BUILD, 1, 8, 15, 1 << 20, 8)
+    with pytest.raises(M.MfdError):
+        M.workspace_size(99, 1, 8, 15, 100, 8)
+
+
+FAKE = ctypes.c_void_p(0x100000)  # never dereferenced: every call below fails its checks first
+
+
+def _lsm(**kw):
+    a = dict(logits=FAKE, dt=M.MFD_BF16, N=1, K=8, L=15, V=1000, k=256, lse=FAKE, tid=FAKE, raw=FAKE)
+    a.update(kw)
+    return M._lib.mfd_logsoftmax_topk(a["logits"], a["dt"], a["N"], a["K"], a["L"], a["V"], a["k"], a["lse"],
+                                      a["tid"], a["raw"], None, None, None, 0, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(K=0), M.MFD_ERR_INVALID_ARG), (dict(K=33), M.MFD_ERR_INVALID_ARG), (dict(L=0), M.MFD_ERR_INVALID_ARG),
+    (dict(L=33), M.MFD_ERR_INVALID_ARG), (dict(V=0), M.MFD_ERR_INVALID_ARG), (dict(N=-1), M.MFD_ERR_INVALID_ARG),
+    (dict(k=0), M.MFD_ERR_INVALID_ARG), (dict(k=1001), M.MFD_ERR_INVALID_ARG), (dict(k=4096, V=10000), M.MFD_ERR_INVALID_ARG),
+    (dict(dt=7), M.MFD_ERR_DTYPE), (dict(logits=None), M.MFD_ERR_INVALID_ARG), (dict(lse=None), M.MFD_ERR_INVALID_ARG),
+    (dict(logits=ctypes.c_void_p(0x100001)), M.MFD_ERR_INVALID_ARG),
+])
+def test_logsoftmax_topk_rejects(kw, code):
+    assert _lsm(**kw) == code
+    assert M.last_error() != ""
+
+
+def test_zero_trees_is_a_no_op():
+    assert _lsm(N=0, logits=None, lse=None, tid=None, raw=None) == M.MFD_OK
+
+
+def _thr(ws=None, ws_bytes=0, **kw):
+    a = dict(N=2, K=8, L=15, k=256, B=256)
+    a.update(kw)
+    return M._lib.mfd_mixture_threshold(FAKE, FAKE, FAKE, a["N"], a["K"], a["L"], a["k"], a["B"], FAKE, FAKE, None,
+                                        None, ws, ws_bytes, None)
+
+
+def test_tree_calls_check_workspace_and_limits():
+    need = M.workspace_size(M.MFD_OP_MIXTURE_THRESHOLD, 2, 8, 15, 151936, 256)
+    assert _thr() == M.MFD_ERR_WORKSPACE
+    assert "workspace needs" in M.last_error()
+    assert _thr(ws=FAKE, ws_bytes=need - 1) == M.MFD_ERR_WORKSPACE
+    assert _thr(K=17, k=1024, B=1024) == M.MFD_ERR_INVALID_ARG  # K*k > 16384
+    assert _thr(B=-1) == M.MFD_ERR_INVALID_ARG
+    assert _thr(B=16384) == M.MFD_ERR_INVALID_ARG
+    rc = M._lib.mfd_tree_build(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 15, 256, 256, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               None, None, FAKE, 1 << 30, None)
+    assert rc == M.MFD_ERR_INVALID_ARG and "n_nodes" in M.last_error()
+
+
+def test_mask_and_walk_reject():
+    assert M._lib.mfd_tree_mask(FAKE, FAKE, FAKE, FAKE, 1, 0, FAKE, FAKE, None, None) == M.MFD_ERR_INVALID_ARG
+    assert M._lib.mfd_tree_mask(FAKE, FAKE, FAKE, None, 1, 9, FAKE, FAKE, None, None) == M.MFD_ERR_INVALID_ARG
+    args = [FAKE, M.MFD_F32, 1, 9, 16, 4] + [FAKE] * 9 + [None, None, 0, None]
+    bad = list(args)
+    bad[1] = 5
+    assert M._lib.mfd_verify_walk(*bad) == M.MFD_ERR_DTYPE
+    bad = list(args)
+    bad[5] = 0
+    assert M._lib.mfd_verify_walk(*bad) == M.MFD_ERR_INVALID_ARG
+    bad = list(args)
+    bad[6] = None
+    assert M._lib.mfd_verify_walk(*bad) == M.MFD_ERR_INVALID_ARG
+
+
+def test_binding_checks_shapes_on_cpu_tensors():
+    import torch
+    x = torch.zeros((1, 2, 3, 16), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        M.mfd_logsoftmax_topk(x, 4, None, None, None)

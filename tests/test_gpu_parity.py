@@ -1,0 +1,339 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bars: ids, node sets, parents, depths, masks, tau and tokens bit-exact (trees
+whose cut-off band is not decided by exact comparisons are reported and
+excluded from node-set exactness); log-normalisers within 1e-5, scores within
+1e-4."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mixture_draft_tree_amd import synth
+from mixture_draft_tree_amd import mfdtree as M
+from mixture_draft_tree_amd.pipeline import MixtureTreePath
+
+from gpu_helpers import (check_lsm, check_mask, check_walk, compare_tree, tree_rows, upload_tree)
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_module(_):
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _lsm_run(x_cpu: torch.Tensor, k: int, logp=True, offset_bytes=0):
+    N, K, L, V = x_cpu.shape
+    if offset_bytes:
+        esz = x_cpu.element_size()
+        raw = torch.empty(x_cpu.numel() + 16, dtype=x_cpu.dtype, device="cuda")
+        x = raw[offset_bytes // esz: offset_bytes // esz + x_cpu.numel()].view(N, K, L, V)
+        x.copy_(x_cpu.cuda())
+    else:
+        x = x_cpu.cuda()
+    lse = torch.empty((N, K, L), dtype=torch.float64, device="cuda")
+    tid = torch.empty((N, K, L, k), dtype=torch.int32, device="cuda")
+    raw_ = torch.empty((N, K, L, k), dtype=torch.float32, device="cuda")
+    lp = torch.empty((N, K, L, k), dtype=torch.float32, device="cuda") if logp else None
+    st = torch.zeros((N,), dtype=torch.int32, device="cuda")
+    M.mfd_logsoftmax_topk(x, k, lse, tid, raw_, lp, st)
+    torch.cuda.synchronize()
+    return lse, tid, raw_, lp, st
+
+
+# ------------------------------------------------------------------ logits pass
+
+LSM_CASES = [
+    # name, N, K, L, V, k, dtype, maker
+    ("f32_tiny", 1, 2, 4, 16, 8, torch.float32, "normal"),
+    ("bf16_ragged", 2, 3, 2, 5003, 37, torch.bfloat16, "normal"),
+    ("f32_ragged", 1, 2, 3, 1027, 100, torch.float32, "normal"),
+    ("bf16_int_ties", 1, 2, 2, 4099, 300, torch.bfloat16, "ints"),
+    ("bf16_constant", 1, 1, 2, 3000, 256, torch.bfloat16, "const"),
+    ("bf16_neginf", 1, 2, 2, 2000, 256, torch.bfloat16, "neginf"),
+    ("bf16_all_neginf", 1, 1, 1, 777, 64, torch.bfloat16, "allneginf"),
+    ("bf16_k_eq_V", 1, 2, 2, 300, 300, torch.bfloat16, "normal"),
+    ("bf16_ascending", 1, 1, 2, 20000, 256, torch.bfloat16, "ascending"),
+    ("bf16_k1024", 1, 2, 1, 248320, 1024, torch.bfloat16, "normal"),
+    ("bf16_signed_zero", 1, 1, 1, 1000, 200, torch.bfloat16, "zeros"),
+]
+
+
+def _make(kind, shape, dtype, seed):
+    g = torch.Generator().manual_seed(seed)
+    if kind == "normal":
+        x = torch.randn(shape, generator=g) * 3
+    elif kind == "ints":
+        x = torch.randint(-3, 4, shape, generator=g).float()
+    elif kind == "const":
+        x = torch.full(shape, 1.5)
+    elif kind == "neginf":
+        x = torch.randn(shape, generator=g) * 2
+        x[torch.rand(shape, generator=g) < 0.95] = -float("inf")
+    elif kind == "allneginf":
+        x = torch.full(shape, -float("inf"))
+    elif kind == "ascending":
+        x = torch.linspace(-8, 8, shape[-1]).expand(shape).clone()
+    elif kind == "zeros":
+        x = torch.zeros(shape)
+        x[..., ::3] = -0.0
+        x[..., 1::7] = 0.5
+    return x.to(dtype)
+
+
+@pytest.mark.parametrize("case", LSM_CASES, ids=[c[0] for c in LSM_CASES])
+def test_logsoftmax_topk_parity(case):
+    name, N, K, L, V, k, dt, kind = case
+    say(f"[lsm] {name} N={N} K={K} L={L} V={V} k={k}")
+    x = _make(kind, (N, K, L, V), dt, seed=hash(name) % 1000)
+    lse, tid, raw, lp, st = _lsm_run(x, k)
+    err = check_lsm(x, lse, tid, raw, k, lp)
+    assert st.cpu().eq(0).all()
+    say(f"[lsm] {name} max |lse err| = {err:.2e}")
+
+
+def test_logsoftmax_topk_unaligned_rows():
+    x = _make("normal", (1, 2, 3, 1001), torch.bfloat16, 5)
+    for off in (2, 6, 14):
+        lse, tid, raw, lp, st = _lsm_run(x, 64, offset_bytes=off)
+        check_lsm(x, lse, tid, raw, 64, lp)
+
+
+def test_logsoftmax_topk_nonfinite_status():
+    x = _make("normal", (3, 2, 2, 500), torch.bfloat16, 6)
+    x[1, 1, 0, 17] = float("nan")
+    x[2, 0, 1, 3] = float("inf")
+    _, _, _, _, st = _lsm_run(x, 16)
+    assert st.cpu().tolist() == [0, M.MFD_TREE_NONFINITE, M.MFD_TREE_NONFINITE]
+
+
+# ------------------------------------------------------------------ tree stages on small cases
+
+def _small_tree_case(seed, K, L, V, B, ints=False, neginf=0.0, dtype=torch.float32):
+    g = torch.Generator().manual_seed(seed)
+    if ints:
+        x = torch.randint(-3, 4, (1, K, L, V), generator=g).float()
+    else:
+        x = torch.randn((1, K, L, V), generator=g) * 2
+    if neginf:
+        x[torch.rand(x.shape, generator=g) < neginf] = -float("inf")
+        x[..., 0] = torch.where(torch.isinf(x[..., 0]), torch.zeros_like(x[..., 0]), x[..., 0])
+    return x.to(dtype)
+
+
+SMALL = [
+    # seed, K, L, V, B, ints, neginf
+    (1, 2, 4, 16, 8, False, 0.0),
+    (2, 3, 5, 40, 30, False, 0.0),
+    (3, 1, 6, 20, 50, False, 0.0),
+    (4, 4, 3, 9, 60, True, 0.0),
+    (5, 2, 3, 6, 20, False, 0.0),     # V < B: k = V
+    (6, 3, 4, 12, 25, False, 0.4),
+    (7, 2, 1, 50, 10, False, 0.0),    # L = 1
+    (8, 5, 4, 30, 1, False, 0.0),     # B = 1
+    (9, 2, 4, 10, 0, False, 0.0),     # B = 0
+    (10, 8, 6, 64, 200, True, 0.0),
+    (11, 3, 8, 7, 300, False, 0.0),   # deep, narrow
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"s{c[0]}" for c in SMALL])
+def test_tree_small_cases(case):
+    seed, K, L, V, B, ints, neginf = case
+    say(f"[tree] seed={seed} K={K} L={L} V={V} B={B}")
+    x = _small_tree_case(seed, K, L, V, B, ints, neginf)
+    P = MixtureTreePath(1, K, L, V, B, with_logp=True, with_dense_mask=True)
+    anchor = torch.tensor([7], dtype=torch.int32, device="cuda")
+    pos = torch.tensor([100], dtype=torch.int64, device="cuda")
+    P.build(x.cuda(), anchor, pos)
+    torch.cuda.synchronize()
+    assert P.buf.status.item() == 0
+    x64 = x[0].double().numpy()
+    r = compare_tree(x64, B, 7, tree_rows(P, 0))
+    if V ** min(L, 3) < 5000 and B > 0:  # brute force agrees with the oracle heap on small spaces
+        bf = O.mixture_select_bruteforce(x64, B)
+        assert bf.selected == r["sel"].selected
+    g = tree_rows(P, 0)
+    check_mask(g["parent"], g["depth"], g["n_nodes"], 100, B + 1,
+               P.buf.mask_words[0].cpu().numpy(), P.buf.position_ids[0].cpu().numpy(),
+               P.buf.dense_mask[0].cpu().numpy())
+    say(f"[tree] seed={seed} exact={r['exact']} n_nodes={g['n_nodes']}")
+
+
+@pytest.mark.parametrize("seed", [21, 22, 23])
+def test_tree_build_from_lower_cutoff(seed):
+    """The build call alone, fed a cut-off well below the true one (so it
+    materialises extra prefixes and must pick the first n_select by the total
+    order), gives the oracle's tree."""
+    x = _small_tree_case(seed, 3, 5, 30, 40, ints=(seed % 2 == 1))
+    x64 = x[0].double().numpy()
+    sel = O.mixture_select_heap(x64, 40, band=1e-4)
+    P = MixtureTreePath(1, 3, 5, 30, 40)
+    P.logsoftmax_topk(x.cuda())
+    P.buf.cutoff.fill_(sel.cutoff - 0.75)
+    P.buf.n_select.fill_(sel.n_select)
+    P.tree_build(torch.tensor([3], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert P.buf.status.item() == 0
+    g = tree_rows(P, 0)
+    g["cutoff"] = sel.cutoff
+    g.pop("per_mode_kept")
+    r = compare_tree(x64, 40, 3, g, sel=sel)
+    say(f"[build-only] seed={seed} exact={r['exact']}")
+
+
+def test_walk_parity_small():
+    """Walk kernel vs oracle walk on oracle trees, T = 0 and T > 0, fp32 and bf16 rows."""
+    rng = np.random.default_rng(3)
+    for dt in (torch.float32, torch.bfloat16):
+        trees, Rs = [], []
+        K, L, V, B = 2, 5, 33, 24
+        for t in range(6):
+            x = rng.normal(0, 2, size=(K, L, V))
+            sel = O.mixture_select_heap(x, B)
+            tr = O.canonical_tree(sel, 1, B)
+            trees.append(tr)
+            R = rng.normal(0, 1, size=(B + 1, V))
+            # follow the first drafted path for a while so walks go deep
+            for i in range(tr["n_nodes"]):
+                kids = [j for j in range(1, tr["n_nodes"]) if tr["parent"][j] == i]
+                if kids:
+                    R[i, tr["node_token"][kids[0]]] += 6.0
+            Rs.append(R)
+        Rt = torch.tensor(np.stack(Rs)).to(dt)
+        R64 = Rt.double().numpy()
+        tok, par, dep, nn = upload_tree(trees, B + 1)
+        N = len(trees)
+        temps = torch.tensor([0.0, 1.0, 0.5, 2.0, 0.0, 1.0], dtype=torch.float32, device="cuda")
+        seeds = torch.tensor([11, 12, 13, 2 ** 62 + 5, 15, -7], dtype=torch.int64, device="cuda")
+        tau = torch.empty(N, dtype=torch.int32, device="cuda")
+        ot = torch.empty((N, L + 1), dtype=torch.int32, device="cuda")
+        pn = torch.empty((N, L + 1), dtype=torch.int32, device="cuda")
+        st = torch.zeros(N, dtype=torch.int32, device="cuda")
+        M.mfd_verify_walk(Rt.cuda(), L, tok, par, dep, nn, temps, seeds, tau, ot, pn, st)
+        torch.cuda.synchronize()
+        assert st.eq(0).all()
+        for n in range(N):
+            seed_u64 = int(seeds[n].item()) & ((1 << 64) - 1)
+            check_walk(trees[n], R64[n], float(temps[n].item()), seed_u64, L, tau[n].item(),
+                       ot[n].cpu().numpy(), pn[n].cpu().numpy())
+
+
+def test_walk_bad_temperature():
+    x = _small_tree_case(31, 2, 3, 16, 8)
+    P = MixtureTreePath(2, 2, 3, 16, 8)
+    xx = torch.cat([x, x]).cuda()
+    P.build(xx, torch.tensor([1, 2], dtype=torch.int32, device="cuda"), torch.zeros(2, dtype=torch.int64, device="cuda"))
+    R = torch.randn((2, 9, 16), device="cuda")
+    P.verify_walk(R, torch.tensor([-1.0, float("nan")], device="cuda"), torch.tensor([1, 2], device="cuda"))
+    torch.cuda.synchronize()
+    assert P.buf.status.cpu().tolist() == [M.MFD_TREE_BAD_TEMPERATURE] * 2
+    assert P.buf.tau.cpu().tolist() == [0, 0]
+    assert (P.buf.out_tokens == -1).all()
+
+
+# ------------------------------------------------------------------ the workloads end to end
+
+def _run_workload(name, N=None, sample=None, device_gen="cpu"):
+    w = synth.WORKLOADS[name]
+    b = synth.draft_batch(name, device=device_gen, N=N)
+    N = b.logits.shape[0]
+    logits = b.logits.cuda()
+    P = MixtureTreePath(N, w.K, w.L, w.V, w.B, with_logp=True)
+    anchor, pos = b.anchor.cuda(), b.pos_base.cuda()
+    say(f"[{name}] build N={N}")
+    P.build(logits, anchor, pos)
+    torch.cuda.synchronize()
+    assert P.buf.status.eq(0).all(), P.buf.status
+    sample = list(range(N)) if sample is None else sample
+    trees, results = {}, {}
+    for n in sample:
+        x_cpu = b.logits[n].cpu()
+        x64 = x_cpu.double().numpy()
+        check_lsm(x_cpu[None], P.buf.lse[n:n + 1], P.buf.topk_id[n:n + 1], P.buf.topk_raw[n:n + 1], P.k,
+                  P.buf.topk_logp[n:n + 1])
+        r = compare_tree(x64, w.B, int(b.anchor[n]), tree_rows(P, n))
+        g = tree_rows(P, n)
+        check_mask(g["parent"], g["depth"], g["n_nodes"], int(b.pos_base[n]), w.B + 1,
+                   P.buf.mask_words[n].cpu().numpy(), P.buf.position_ids[n].cpu().numpy())
+        trees[n], results[n] = r["tree"], r
+        say(f"[{name}] tree {n}: exact={r['exact']} n_nodes={g['n_nodes']} cutoff={g['cutoff']:.6f}")
+    # target rows: sampled trees from the oracle's tree, others from the built tree
+    dep = P.buf.depth.cpu().clone()
+    nn = P.buf.n_nodes.cpu().clone()
+    for n in sample:
+        dep[n] = torch.from_numpy(trees[n]["depth"]).to(torch.int32)
+        nn[n] = trees[n]["n_nodes"]
+    R = synth.target_logits(b, dep, nn, device=device_gen)
+    temps = b.temperature.cuda()
+    seeds = b.seed.cuda()
+    P.verify_walk(R.cuda(), temps, seeds)
+    torch.cuda.synchronize()
+    # the walk kernel on the oracle trees, for every sampled tree
+    tok, par, dp, nnn = upload_tree([trees[n] for n in sample], w.B + 1)
+    Rs = R[sample].cuda().contiguous()
+    tau = torch.empty(len(sample), dtype=torch.int32, device="cuda")
+    ot = torch.empty((len(sample), w.L + 1), dtype=torch.int32, device="cuda")
+    pn = torch.empty_like(ot)
+    M.mfd_verify_walk(Rs, w.L, tok, par, dp, nnn, temps[sample], seeds[sample], tau, ot, pn)
+    torch.cuda.synchronize()
+    for j, n in enumerate(sample):
+        R64 = R[n].cpu().double().numpy()
+        T = float(b.temperature[n])
+        seed_u64 = int(b.seed[n]) & ((1 << 64) - 1)
+        check_walk(trees[n], R64, T, seed_u64, w.L, tau[j].item(), ot[j].cpu().numpy(), pn[j].cpu().numpy())
+        if results[n]["exact"]:
+            assert P.buf.tau[n].item() == tau[j].item()
+            assert torch.equal(P.buf.out_tokens[n], ot[j])
+        say(f"[{name}] walk {n}: T={T} tau={tau[j].item()}")
+    return b, P, trees
+
+
+def test_workload_tiny():
+    b, P, trees = _run_workload("tiny")
+    # brute force over all 2 * 16^4 full-length prefixes (and shorter ones)
+    x64 = b.logits[0].double().numpy()
+    assert set(O.mixture_select_bruteforce(x64, 8).selected) == set(trees[0]["prefixes"][1:])
+
+
+def test_workload_product_chimeras():
+    b, P, trees = _run_workload("product")
+    A, Bf = b.futures[0, 0].tolist(), b.futures[0, 1].tolist()
+    chims = O.chimera_nodes(trees[0]["prefixes"], A, Bf)
+    assert len([c for c in chims if len(c) == max(synth.PRODUCT_SPLIT_POSITIONS) + 1]) >= 3
+
+
+def test_workload_single():
+    _run_workload("single")
+
+
+def test_workload_batched_sampled():
+    _run_workload("batched", sample=[0, 1, 37, 63], device_gen="cuda")
+
+
+def test_workload_stress():
+    _run_workload("stress")
+
+
+def test_determinism_and_batch_order():
+    """Same trees in another batch order give identical outputs."""
+    b = synth.draft_batch("single", base_seed=5, N=3)
+    w = b.workload
+    outs = []
+    for perm in ([0, 1, 2], [2, 0, 1]):
+        P = MixtureTreePath(3, w.K, w.L, w.V, w.B)
+        P.build(b.logits[perm].cuda(), b.anchor[perm].cuda(), b.pos_base[perm].cuda())
+        torch.cuda.synchronize()
+        inv = np.argsort(perm)
+        outs.append([getattr(P.buf, f).cpu()[inv] for f in ("node_token", "parent", "depth", "score", "best_mode",
+                                                               "cutoff", "n_select", "per_mode_kept", "mask_words")])
+    for a, c in zip(*outs):
+        assert torch.equal(a, c)
