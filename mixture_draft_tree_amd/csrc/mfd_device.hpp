@@ -102,7 +102,7 @@ __device__ __forceinline__ int block_sum(int v, int* smem) {
 // ---------------------------------------------------------------- bitonic sort
 // Sorts a[0..n) ascending in LDS; n must be a power of two.  Barriers inside.
 template <int NT>
-__device__ void block_bitonic_sort(uint64_t* a, int n) {
+__device__ __forceinline__ void block_bitonic_sort(uint64_t* a, int n) {
   for (int size = 2; size <= n; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       for (int t = threadIdx.x; t < (n >> 1); t += NT) {
@@ -159,7 +159,7 @@ __device__ __forceinline__ void wave_pick_digit(const uint32_t* hist, int remain
 // which get(i, &key) returns true.  The caller guarantees at least `rank`
 // such items.  `hist` needs 256 uint32, `sh` 2 ints.  Barriers inside.
 template <int NT, int BITS, typename Get>
-__device__ uint64_t block_kth_largest(int n, int rank, Get get, uint32_t* hist, int* sh) {
+__device__ __forceinline__ uint64_t block_kth_largest(int n, int rank, Get get, uint32_t* hist, int* sh) {
   uint64_t prefix = 0;
   int remaining = rank;
   for (int shift = BITS - 8; shift >= 0; shift -= 8) {
