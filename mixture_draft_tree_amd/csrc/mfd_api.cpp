@@ -69,8 +69,11 @@ mfd_status mfd_workspace_size(mfd_op op, int N, int K, int L, int V, int B, size
   switch (op) {
     case MFD_OP_LOGSOFTMAX_TOPK:
     case MFD_OP_TREE_MASK:
+      if (N < 0) return fail(MFD_ERR_INVALID_ARG, "N must be >= 0 (got %d)", N);
+      return ok();
     case MFD_OP_VERIFY_WALK:
       if (N < 0) return fail(MFD_ERR_INVALID_ARG, "N must be >= 0 (got %d)", N);
+      *bytes = N == 0 ? 0 : mfd::walk_ws_bytes(N);
       return ok();
     case MFD_OP_MIXTURE_THRESHOLD:
     case MFD_OP_TREE_BUILD: {
@@ -178,8 +181,6 @@ mfd_status mfd_verify_walk(const void* target_logits, mfd_dtype dtype, int N, in
                            const int32_t* n_nodes, const float* temperature, const uint64_t* seed, int32_t* tau,
                            int32_t* out_tokens, int32_t* path_nodes, int32_t* status, void* ws, size_t ws_bytes,
                            hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (N < 0) return fail(MFD_ERR_INVALID_ARG, "N must be >= 0 (got %d)", N);
   if (Bp1 < 1 || Bp1 > kMaxB + 1) return fail(MFD_ERR_INVALID_ARG, "Bp1 must be in [1, %d] (got %d)", kMaxB + 1, Bp1);
   if (V < 1 || V > kMaxV) return fail(MFD_ERR_INVALID_ARG, "V must be in [1, %d] (got %d)", kMaxV, V);
@@ -199,8 +200,12 @@ mfd_status mfd_verify_walk(const void* target_logits, mfd_dtype dtype, int N, in
   const size_t esz = dtype == MFD_BF16 ? 2 : 4;
   if (reinterpret_cast<uintptr_t>(target_logits) % esz)
     return fail(MFD_ERR_INVALID_ARG, "target_logits not aligned to its element size");
+  const size_t need = mfd::walk_ws_bytes(N);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(MFD_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws == nullptr ? (size_t)0 : ws_bytes);
+  if (reinterpret_cast<uintptr_t>(ws) % 8) return fail(MFD_ERR_INVALID_ARG, "workspace must be 8-byte aligned");
   return from_hip(mfd::launch_verify_walk(target_logits, dtype == MFD_BF16, N, Bp1, V, L, node_token, parent, depth,
-                                          n_nodes, temperature, seed, tau, out_tokens, path_nodes, status, stream),
+                                          n_nodes, temperature, seed, tau, out_tokens, path_nodes, status, ws, stream),
                   "mfd_verify_walk launch");
 }
 

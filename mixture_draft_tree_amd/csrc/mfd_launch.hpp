@@ -39,9 +39,12 @@ hipError_t launch_tree_mask(const int32_t* parent, const int32_t* depth, const i
                             const int64_t* pos_base, int N, int Bp1, uint64_t* mask_words, int64_t* position_ids,
                             uint8_t* dense_mask, hipStream_t stream);
 
+size_t walk_ws_bytes(int N);
+
 hipError_t launch_verify_walk(const void* target, bool bf16, int N, int Bp1, long long V, int L,
                               const int32_t* node_token, const int32_t* parent, const int32_t* depth,
                               const int32_t* n_nodes, const float* temperature, const uint64_t* seed, int32_t* tau,
-                              int32_t* out_tokens, int32_t* path_nodes, int32_t* status, hipStream_t stream);
+                              int32_t* out_tokens, int32_t* path_nodes, int32_t* status, void* ws,
+                              hipStream_t stream);
 
 }  // namespace mfd

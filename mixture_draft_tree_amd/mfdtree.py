@@ -107,6 +107,12 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise ValueError(f"unsupported logits dtype {t.dtype}")
 
 
+def walk_workspace(N: int, device="cuda") -> torch.Tensor:
+    """A device workspace for mfd_verify_walk on N trees."""
+    n = workspace_size(MFD_OP_VERIFY_WALK, N, 1, 1, 1, 0)
+    return torch.empty((max(n, 8) + 7) // 8, dtype=torch.int64, device=device)
+
+
 def workspace_size(op: int, N: int, K: int, L: int, V: int, B: int) -> int:
     out = _sz(0)
     _check(_lib.mfd_workspace_size(op, N, K, L, V, B, ctypes.byref(out)), "mfd_workspace_size")
@@ -182,7 +188,7 @@ def mfd_tree_mask(parent, depth, n_nodes, pos_base, mask_words, position_ids, de
 
 
 def mfd_verify_walk(target_logits, L, node_token, parent, depth, n_nodes, temperature, seed, tau, out_tokens,
-                    path_nodes, status=None, stream=None):
+                    path_nodes, status=None, ws=None, stream=None):
     """target_logits [N, B+1, V] bf16/fp32; seed [N] int64 holding the uint64 bits."""
     if target_logits.dim() != 3 or not target_logits.is_contiguous() or target_logits.device.type != "cuda":
         raise ValueError("target_logits must be a contiguous [N, B+1, V] GPU tensor")
@@ -196,7 +202,8 @@ def mfd_verify_walk(target_logits, L, node_token, parent, depth, n_nodes, temper
     _want(out_tokens, "out_tokens", torch.int32, (N, L + 1))
     _want(path_nodes, "path_nodes", torch.int32, (N, L + 1))
     _want(status, "status", torch.int32, (N,), optional=True)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(_lib.mfd_verify_walk(_ptr(target_logits), _dtype_code(target_logits), N, Bp1, V, L, _ptr(node_token),
                                 _ptr(parent), _ptr(depth), _ptr(n_nodes), _ptr(temperature), _ptr(seed), _ptr(tau),
-                                _ptr(out_tokens), _ptr(path_nodes), _ptr(status), None, 0,
+                                _ptr(out_tokens), _ptr(path_nodes), _ptr(status), _ptr(ws), ws_bytes,
                                 _stream_handle(stream)), "mfd_verify_walk")

@@ -54,7 +54,8 @@ class MixtureTreePath:
         Bp1 = B + 1
         W = (Bp1 + 63) // 64
         ws_bytes = max(M.workspace_size(M.MFD_OP_MIXTURE_THRESHOLD, N, K, L, V, B),
-                       M.workspace_size(M.MFD_OP_TREE_BUILD, N, K, L, V, B))
+                       M.workspace_size(M.MFD_OP_TREE_BUILD, N, K, L, V, B),
+                       M.workspace_size(M.MFD_OP_VERIFY_WALK, N, K, L, V, B))
         e = lambda shape, dt: torch.empty(shape, dtype=dt, device=d)
         self.buf = TreeBatch(
             lse=e((N, K, L), torch.float64),
@@ -77,7 +78,7 @@ class MixtureTreePath:
             out_tokens=e((N, L + 1), torch.int32),
             path_nodes=e((N, L + 1), torch.int32),
             status=torch.zeros((N,), dtype=torch.int32, device=d),
-            ws=torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=d),
+            ws=torch.empty(((max(ws_bytes, 8) + 7) // 8,), dtype=torch.int64, device=d),
         )
 
     def logsoftmax_topk(self, logits, stream=None):
@@ -102,7 +103,7 @@ class MixtureTreePath:
     def verify_walk(self, target, temperature, seed, stream=None):
         b = self.buf
         M.mfd_verify_walk(target, self.L, b.node_token, b.parent, b.depth, b.n_nodes, temperature, seed, b.tau,
-                          b.out_tokens, b.path_nodes, b.status, stream=stream)
+                          b.out_tokens, b.path_nodes, b.status, ws=b.ws, stream=stream)
 
     def build(self, logits, anchor, pos_base, stream=None):
         """Calls 1-4: logits -> tree, mask, position ids."""

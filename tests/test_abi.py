@@ -34,8 +34,10 @@ def test_version_and_clean_error():
 
 
 def test_workspace_sizes():
-    for op in (M.MFD_OP_LOGSOFTMAX_TOPK, M.MFD_OP_TREE_MASK, M.MFD_OP_VERIFY_WALK):
+    for op in (M.MFD_OP_LOGSOFTMAX_TOPK, M.MFD_OP_TREE_MASK):
         assert M.workspace_size(op, 64, 8, 15, 151936, 256) == 0
+    assert M.workspace_size(M.MFD_OP_VERIFY_WALK, 64, 8, 15, 151936, 256) > 0
+    assert M.workspace_size(M.MFD_OP_VERIFY_WALK, 0, 8, 15, 151936, 256) == 0
     one = M.workspace_size(M.MFD_OP_MIXTURE_THRESHOLD, 1, 8, 15, 151936, 256)
     many = M.workspace_size(M.MFD_OP_MIXTURE_THRESHOLD, 64, 8, 15, 151936, 256)
     assert one > 0 and many == 64 * one
@@ -109,6 +111,7 @@ def test_mask_and_walk_reject():
     bad = list(args)
     bad[6] = None
     assert M._lib.mfd_verify_walk(*bad) == M.MFD_ERR_INVALID_ARG
+    assert M._lib.mfd_verify_walk(*args) == M.MFD_ERR_WORKSPACE  # no workspace
 
 
 def test_binding_checks_shapes_on_cpu_tensors():

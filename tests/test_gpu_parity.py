@@ -218,7 +218,7 @@ def test_walk_parity_small():
         ot = torch.empty((N, L + 1), dtype=torch.int32, device="cuda")
         pn = torch.empty((N, L + 1), dtype=torch.int32, device="cuda")
         st = torch.zeros(N, dtype=torch.int32, device="cuda")
-        M.mfd_verify_walk(Rt.cuda(), L, tok, par, dep, nn, temps, seeds, tau, ot, pn, st)
+        M.mfd_verify_walk(Rt.cuda(), L, tok, par, dep, nn, temps, seeds, tau, ot, pn, st, ws=M.walk_workspace(N))
         torch.cuda.synchronize()
         assert st.eq(0).all()
         for n in range(N):
@@ -283,7 +283,8 @@ def _run_workload(name, N=None, sample=None, device_gen="cpu"):
     tau = torch.empty(len(sample), dtype=torch.int32, device="cuda")
     ot = torch.empty((len(sample), w.L + 1), dtype=torch.int32, device="cuda")
     pn = torch.empty_like(ot)
-    M.mfd_verify_walk(Rs, w.L, tok, par, dp, nnn, temps[sample], seeds[sample], tau, ot, pn)
+    M.mfd_verify_walk(Rs, w.L, tok, par, dp, nnn, temps[sample], seeds[sample], tau, ot, pn,
+                      ws=M.walk_workspace(len(sample)))
     torch.cuda.synchronize()
     for j, n in enumerate(sample):
         R64 = R[n].cpu().double().numpy()
