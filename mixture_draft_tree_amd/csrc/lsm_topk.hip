@@ -4,35 +4,28 @@
 // (project page, Figure 2); the tree search needs, per (tree, mode, position)
 // row, the log-normaliser and the candidates in rank order (project page,
 // "How it works" step 3: best-first searches take each position's tokens from
-// most to least probable).  This kernel reads each logit exactly once from
-// HBM.
+// most to least probable).  This kernel reads each logit once from HBM.
 //
 // Design (gfx950, wave64):
 //  * One workgroup of 256 threads (4 waves) per row; rows are independent, so
-//    the grid is N*K*L workgroups and no cross-workgroup traffic exists.
-//  * 16-byte non-temporal vector loads (8 bf16 or 4 fp32), consecutive lanes
-//    on consecutive 16-byte chunks, four per lane per chunk, double-buffered
-//    in registers so the next chunk is in flight while one is consumed.
+//    the grid is N*K*L workgroups with no cross-workgroup traffic.
+//  * 16-byte non-temporal vector loads (8 bf16 or 4 fp32), consecutive lanes on
+//    consecutive 16-byte chunks, four per lane per chunk, double-buffered in
+//    registers so the next chunk is in flight while one is consumed.
 //  * Online log-sum-exp per lane in base 2 (one FMA and one v_exp_f32 per
 //    element, fp32 terms summed per vector into an fp64 running sum); lanes,
 //    waves and the block are combined in fp64.
-//  * Top-k in the same pass.  A lane whose vector maximum reaches the wave's
-//    threshold stages the whole 16-byte vector into a small per-wave LDS ring
-//    (slot from ballot + popcount: a few instructions per round, however many
-//    lanes hold candidates).  When the ring fills, the wave processes the
-//    staged vectors 64 at a time (one per lane) and appends the elements whose
-//    ordered key reaches the threshold to a per-wave candidate buffer.  When
-//    that buffer fills, the wave radix-selects the k-th largest key of its own
-//    buffer -- a lower bound on the row's k-th largest, since the buffer holds
-//    distinct row elements -- drops what lies below and publishes the value to
-//    the other waves (LDS atomicMax).  The threshold only rises; the
-//    streaming loop has no block barrier.
-//  * At the end the block radix-selects the exact k-th largest composite
-//    (key, ~index) over all wave buffers, keeps exactly k, sorts them
-//    (bitonic, LDS) and writes ids, values and log-probs.
-//  * A buffer that cannot make room (more than ~256 exact ties at the
-//    threshold) sends the row to an exact multi-pass radix top-k that
-//    re-reads the row.
+//  * Top-k in the same pass.  The first chunk (8192 bf16 elements) is a sample:
+//    the block radix-selects the key that should leave about 3k elements of
+//    the row above it.  During the stream a lane whose vector maximum reaches
+//    that key copies the whole 16-byte vector into its wave's LDS area (slot
+//    from ballot + popcount).  At the end the block radix-selects the exact
+//    k-th key over the staged elements, gathers those at or above it, and
+//    bitonic-sorts them by (key descending, token ascending).
+//  * Whenever the guess does not hold (fewer than k elements reach it, a
+//    wave's area fills up, or too many ties sit at the k-th key), the row
+//    takes an exact multi-pass radix top-k that re-reads the row.  The guess
+//    changes speed only, never results.
 #include <math.h>
 
 #include "mfd_device.hpp"
@@ -45,9 +38,7 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kUnroll = 4;
 constexpr long long kStep = (long long)kThreads * kUnroll;
-constexpr int kStage = 192;      // staged vectors per wave
-constexpr int kFlushAt = 64;     // flush after a chunk once this many are staged
-constexpr int kOversample = 3;   // the sampled threshold aims at ~3k survivors per row
+constexpr int kOversample = 3;
 constexpr float kLog2e = 1.44269504088896340736f;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -75,10 +66,11 @@ struct Elem<false> {
   __device__ static float val_of_bits(uint32_t b) { return __uint_as_float(b); }
 };
 
-// Element j of a 16-byte vector, as raw bits / as a float.
+// Element j of a 16-byte vector (j may be a run-time value), as raw bits / as a float.
 template <bool BF16>
 __device__ __forceinline__ uint32_t vec_bits(const u32x4& v, int j) {
-  const uint32_t w = v[BF16 ? (j >> 1) : j];
+  const int wi = BF16 ? (j >> 1) : j;
+  const uint32_t w = wi == 0 ? v.x : (wi == 1 ? v.y : (wi == 2 ? v.z : v.w));
   if (BF16) return (j & 1) ? (w >> 16) : (w & 0xFFFFu);
   return w;
 }
@@ -90,15 +82,18 @@ __device__ __forceinline__ float vec_val(const u32x4& v, int j) {
 }
 
 struct Shared {
-  uint32_t thr;     // shared threshold key (max over waves)
-  int overflow;     // a wave lost candidates
-  int cnt[kWaves];  // final per-wave candidate counts
+  uint32_t thr;     // the row's sampled threshold key
+  int overflow;     // the staged guess cannot be used: take the exact fallback
+  int cnt[kWaves];  // staged vectors per wave
   int nsurv;
   int sh[4];
   int scan[kWaves];
   float red_m[kWaves];
   double red_s[kWaves];
   double lse;
+  uint32_t skey[64];  // head/tail scalars: keys
+  uint32_t sidx[64];  //                    and indices
+  int nscal;
 };
 
 // Smallest non-NaN key (that of -inf) for the element type.
@@ -112,121 +107,22 @@ __device__ __forceinline__ float thr_float(uint32_t thr) {
   return thr <= min_real_key<BF16>() ? -INFINITY : Elem<BF16>::val_of_key(thr);
 }
 
-template <bool BF16>
-struct WaveTopk {
-  uint64_t* cand;   // candidate buffer (composite keys)
-  uint32_t* hist;   // 256-bin histogram
-  u32x4* svec;      // staged vectors
-  uint32_t* sidx;   // element index of each staged vector's first element
+// Per-wave staging of candidate vectors.
+struct Stager {
+  u32x4* svec;     // staged vectors
+  uint32_t* sidx;  // index of each staged vector's first element
   int cap;
-  int k;
-  int cnt;          // wave-uniform
-  int scnt;         // wave-uniform
-  uint32_t thr;     // wave-uniform threshold key
-  float thr_f;      // its value (-inf below the smallest real key)
-  bool overflow;    // wave-uniform
+  int scnt;        // wave-uniform
+  float thr_f;     // value of the threshold key (-inf below the smallest real key)
+  bool full;       // wave-uniform: a candidate did not fit
 
-  __device__ __forceinline__ void raise(uint32_t t) {
-    if (t > thr) {
-      thr = t;
-      thr_f = thr_float<BF16>(t);
-    }
-  }
-
-  // Raise the threshold to the k-th largest key in the candidate buffer and
-  // drop everything below it.  Wave-synchronous.
-  __device__ __forceinline__ void compact(uint32_t* shared_thr) {
-    if (cnt < k) return;
-    const int lane = lane_id();
-    uint32_t prefix = 0;
-    int remaining = k;
-    for (int shift = Elem<BF16>::KEYBITS - 8; shift >= 0; shift -= 8) {
-      for (int b = lane; b < 256; b += kWave) hist[b] = 0;
-      wave_sync();
-      const uint32_t hi_mask = (shift + 8 >= 32) ? 0u : (~0u << (shift + 8));
-      for (int i = lane; i < cnt; i += kWave) {
-        const uint32_t key = (uint32_t)(cand[i] >> 32);
-        if ((key & hi_mask) == (prefix & hi_mask)) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-      }
-      wave_sync();
-      int digit = 0, above = 0;
-      wave_pick_digit(hist, remaining, &digit, &above);
-#pragma unroll
-      for (int o = kWave / 2; o > 0; o >>= 1) {
-        digit = max(digit, __shfl_xor(digit, o, kWave));
-        above = max(above, __shfl_xor(above, o, kWave));
-      }
-      prefix |= (uint32_t)digit << shift;
-      remaining -= above;
-      wave_sync();
-    }
-    // keep key >= prefix, in place (writes never pass the chunk being read)
-    int w = 0;
-    for (int base = 0; base < cnt; base += kWave) {
-      const int i = base + lane;
-      const uint64_t c = (i < cnt) ? cand[i] : 0ull;
-      const bool keep = (i < cnt) && ((uint32_t)(c >> 32) >= prefix);
-      const uint64_t m = __ballot(keep);
-      wave_sync();
-      if (keep) cand[w + __popcll(m & lanemask_lt())] = c;
-      w += __popcll(m);
-      wave_sync();
-    }
-    cnt = w;
-    raise(prefix);
-    if (lane == 0) atomicMax(shared_thr, prefix);
-  }
-
-  // Wave-level append: every lane offers at most one element.
-  __device__ __forceinline__ void append(bool has, uint32_t key, uint32_t idx, uint32_t* shared_thr) {
-    bool p = has && key >= thr;
-    uint64_t m = __ballot(p);
-    if (m == 0ull || overflow) return;
-    if (cnt + kWave > cap) {
-      compact(shared_thr);
-      p = has && key >= thr;
-      m = __ballot(p);
-      if (m == 0ull) return;
-      if (cnt + kWave > cap) {
-        overflow = true;
-        return;
-      }
-    }
-    if (p) cand[cnt + __popcll(m & lanemask_lt())] = ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - idx);
-    cnt += __popcll(m);
-  }
-
-  // Process the staged vectors, 64 at a time (one per lane).
-  __device__ __forceinline__ void flush(uint32_t* shared_thr) {
-    constexpr int VEC = Elem<BF16>::VEC;
-    const int lane = lane_id();
-    wave_sync();
-    for (int b = 0; b < scnt; b += kWave) {
-      const int i = b + lane;
-      const bool has = i < scnt;
-      const u32x4 v = has ? svec[i] : u32x4{0u, 0u, 0u, 0u};
-      const uint32_t i0 = has ? sidx[i] : 0u;
-#pragma unroll 1
-      for (int j = 0; j < VEC; ++j) {
-        const int wi = BF16 ? (j >> 1) : j;
-        const uint32_t w = wi == 0 ? v.x : (wi == 1 ? v.y : (wi == 2 ? v.z : v.w));
-        const uint32_t bits = BF16 ? ((j & 1) ? (w >> 16) : (w & 0xFFFFu)) : w;
-        append(has, Elem<BF16>::key_of_bits(bits), i0 + j, shared_thr);
-      }
-    }
-    wave_sync();
-    scnt = 0;
-  }
-
-  // Wave-level: lanes with `p` stage their vector.  The caller flushes after
-  // each chunk once kFlushAt are staged; a ring that still fills marks the
-  // row for the exact fallback.
+  // Wave-level: lanes with `p` stage their vector.
   __device__ __forceinline__ void stage(bool p, const u32x4& v, uint32_t i0) {
     const uint64_t m = __ballot(p);
     if (m == 0ull) return;
     const int n = __popcll(m);
-    if (scnt + n > kStage) {
-      overflow = true;
+    if (scnt + n > cap) {
+      full = true;
       return;
     }
     if (p) {
@@ -250,7 +146,7 @@ struct LaneLse {
   __device__ __forceinline__ void rescale(float vm) {
     if (vm > m) {
       const float mln = vm * kLog2e;
-      s *= (double)__builtin_amdgcn_exp2f(ml - mln);  // one fp32 rounding per new maximum
+      s *= (double)__builtin_amdgcn_exp2f(ml - mln);
       m = vm;
       ml = mln;
     }
@@ -263,8 +159,8 @@ struct LaneLse {
   }
 };
 
-template <bool BF16, bool FULL, bool STAGE = true>
-__device__ __forceinline__ void consume_vector(const u32x4& v, uint32_t i0, bool valid, LaneLse& st, WaveTopk<BF16>& wt) {
+template <bool BF16, bool FULL, bool STAGE>
+__device__ __forceinline__ void consume_vector(const u32x4& v, uint32_t i0, bool valid, LaneLse& st, Stager& sg) {
   constexpr int VEC = Elem<BF16>::VEC;
   float f[VEC];
 #pragma unroll
@@ -278,7 +174,7 @@ __device__ __forceinline__ void consume_vector(const u32x4& v, uint32_t i0, bool
 #pragma unroll
   for (int j = 0; j < VEC; ++j) acc += __builtin_amdgcn_exp2f(fmaf(f[j], kLog2e, -b));
   st.s += (double)acc;
-  if (STAGE) wt.stage((FULL || valid) && !(vm < wt.thr_f), v, i0);
+  if (STAGE) sg.stage((FULL || valid) && !(vm < sg.thr_f), v, i0);
 }
 
 __device__ __forceinline__ void load_chunk(u32x4* buf, const u32x4* vrow, long long c, long long nvec, int tid) {
@@ -290,32 +186,51 @@ __device__ __forceinline__ void load_chunk(u32x4* buf, const u32x4* vrow, long l
   }
 }
 
-template <bool BF16>
+template <bool BF16, bool STAGE>
 __device__ __forceinline__ void consume_chunk(const u32x4* buf, long long c, long long nvec, long long head, int tid,
-                                              LaneLse& st, WaveTopk<BF16>& wt, uint32_t* shared_thr) {
+                                              LaneLse& st, Stager& sg) {
   constexpr int VEC = Elem<BF16>::VEC;
-  wt.raise(*shared_thr);
   const long long base = c * kStep;
   if (base + kStep <= nvec) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const long long q = base + (long long)u * kThreads + tid;
-      consume_vector<BF16, true>(buf[u], (uint32_t)(head + q * VEC), true, st, wt);
+      consume_vector<BF16, true, STAGE>(buf[u], (uint32_t)(head + q * VEC), true, st, sg);
     }
   } else {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const long long q = base + (long long)u * kThreads + tid;
-      consume_vector<BF16, false>(buf[u], (uint32_t)(head + q * VEC), q < nvec, st, wt);
+      consume_vector<BF16, false, STAGE>(buf[u], (uint32_t)(head + q * VEC), q < nvec, st, sg);
     }
   }
-  if (wt.scnt >= kFlushAt) wt.flush(shared_thr);
+}
+
+// Calls f(key, index) for every staged element (and head/tail scalar) whose
+// key reaches `thr`.  Block-strided; no barrier.
+template <bool BF16, typename F>
+__device__ __forceinline__ void for_each_staged(const u32x4* svec_all, const uint32_t* sidx_all, int cap,
+                                                const Shared& S, uint32_t thr, F f) {
+  constexpr int VEC = Elem<BF16>::VEC;
+  for (int i = threadIdx.x; i < kWaves * cap; i += kThreads) {
+    const int w = i / cap, j = i - w * cap;
+    if (j >= S.cnt[w]) continue;
+    const u32x4 v = svec_all[i];
+    const uint32_t i0 = sidx_all[i];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const uint32_t key = Elem<BF16>::key_of_bits(vec_bits<BF16>(v, e));
+      if (key >= thr) f(key, i0 + e);
+    }
+  }
+  for (int i = threadIdx.x; i < S.nscal; i += kThreads)
+    if (S.skey[i] >= thr) f(S.skey[i], S.sidx[i]);
 }
 
 template <bool BF16>
 __global__ void __launch_bounds__(kThreads, 4) lsm_topk_kernel(const typename Elem<BF16>::T* __restrict__ logits,
-                                                               long long V, int k, int cap_w, int rows_per_tree,
-                                                               double* __restrict__ lse_out,
+                                                               long long V, int k, int cap_w, int sort_cap,
+                                                               int rows_per_tree, double* __restrict__ lse_out,
                                                                int32_t* __restrict__ topk_id,
                                                                float* __restrict__ topk_raw,
                                                                float* __restrict__ topk_logp,
@@ -325,11 +240,9 @@ __global__ void __launch_bounds__(kThreads, 4) lsm_topk_kernel(const typename El
   constexpr int VEC = E::VEC;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   u32x4* svec_all = reinterpret_cast<u32x4*>(smem_raw);
-  uint64_t* cand_all = reinterpret_cast<uint64_t*>(svec_all + kWaves * kStage);
-  uint32_t* hist_all = reinterpret_cast<uint32_t*>(cand_all + (size_t)kWaves * cap_w);
-  uint32_t* sidx_all = hist_all + kWaves * 256;
-  const int kp = next_pow2(k);
-  uint64_t* sortbuf = reinterpret_cast<uint64_t*>(sidx_all + kWaves * kStage);
+  uint64_t* sortbuf = reinterpret_cast<uint64_t*>(svec_all + (size_t)kWaves * cap_w);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(sortbuf + sort_cap);
+  uint32_t* sidx_all = hist + 256;
   __shared__ Shared S;
 
   const int tid = threadIdx.x, lane = lane_id(), wid = wave_id();
@@ -341,20 +254,14 @@ __global__ void __launch_bounds__(kThreads, 4) lsm_topk_kernel(const typename El
     S.overflow = 0;
     S.nsurv = 0;
   }
-  __syncthreads();
 
-  WaveTopk<BF16> wt;
-  wt.cand = cand_all + (size_t)wid * cap_w;
-  wt.hist = hist_all + wid * 256;
-  wt.svec = svec_all + wid * kStage;
-  wt.sidx = sidx_all + wid * kStage;
-  wt.cap = cap_w;
-  wt.k = k;
-  wt.cnt = 0;
-  wt.scnt = 0;
-  wt.thr = 0;
-  wt.thr_f = -INFINITY;
-  wt.overflow = false;
+  Stager sg;
+  sg.svec = svec_all + (size_t)wid * cap_w;
+  sg.sidx = sidx_all + (size_t)wid * cap_w;
+  sg.cap = cap_w;
+  sg.scnt = 0;
+  sg.thr_f = -INFINITY;
+  sg.full = false;
 
   LaneLse st;
 
@@ -367,31 +274,39 @@ __global__ void __launch_bounds__(kThreads, 4) lsm_topk_kernel(const typename El
   const long long tail0 = head + nvec * VEC;
   const int nscalar = (int)(head + (V - tail0));
 
-  // Vectors, double-buffered chunks.  Chunk 0 doubles as a sample: the block
-  // picks a threshold key such that about kOversample * k elements of the row
-  // are expected above it; if fewer than k turn out to be, the row takes the
-  // exact fallback below, so the guess affects speed only.
+  // scalars (head / tail, at most 2 * (VEC - 1) < 64): wave 0, one per lane
+  if (wid == 0) {
+    const bool has = lane < nscalar;
+    const long long i = has ? (lane < head ? (long long)lane : tail0 + (lane - head)) : 0;
+    const uint32_t bits = has ? E::bits_at(rowp, i) : 0u;
+    const float x = has ? E::val_of_bits(bits) : -INFINITY;
+    st.rescale(x);
+    st.s += (double)__builtin_amdgcn_exp2f(fmaf(x, kLog2e, -st.bias()));
+    if (has) {
+      S.skey[lane] = E::key_of_bits(bits);
+      S.sidx[lane] = (uint32_t)i;
+    }
+    if (lane == 0) S.nscal = nscalar;
+  }
+  __syncthreads();
+
+  // Vectors, double-buffered chunks.  Chunk 0 doubles as the sample.
   const u32x4* vrow = reinterpret_cast<const u32x4*>(rowp + head);
   if (nvec > 0) {
     const long long nchunks = (nvec + kStep - 1) / kStep;
     u32x4 bufA[kUnroll], bufB[kUnroll];
     load_chunk(bufA, vrow, 0, nvec, tid);
     load_chunk(bufB, vrow, 1, nvec, tid);
-    const bool full0 = kStep <= nvec;
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const long long q = (long long)u * kThreads + tid;
-      if (full0) consume_vector<BF16, true, false>(bufA[u], (uint32_t)(head + q * VEC), true, st, wt);
-      else consume_vector<BF16, false, false>(bufA[u], (uint32_t)(head + q * VEC), q < nvec, st, wt);
-    }
-    // sampled threshold: the r-th largest key of chunk 0
-    const long long n0 = (full0 ? kStep : nvec) * VEC;
+    consume_chunk<BF16, false>(bufA, 0, nvec, head, tid, st, sg);
+    // sampled threshold: the r-th largest key of chunk 0, r chosen so that
+    // about kOversample * k elements of the row are expected above it
+    const long long n0 = (kStep <= nvec ? kStep : nvec) * VEC;
     long long r = (kOversample * (long long)k * n0 + V - 1) / V;
     r = r < 1 ? 1 : (r > n0 ? n0 : r);
     uint32_t prefix = 0;
     int remaining = (int)r;
     for (int shift = E::KEYBITS - 8; shift >= 0; shift -= 8) {
-      hist_all[tid] = 0;
+      hist[tid] = 0;
       __syncthreads();
       const uint32_t hi_mask = (shift + 8 >= 32) ? 0u : (~0u << (shift + 8));
 #pragma unroll
@@ -401,14 +316,14 @@ __global__ void __launch_bounds__(kThreads, 4) lsm_topk_kernel(const typename El
 #pragma unroll
           for (int j = 0; j < VEC; ++j) {
             const uint32_t key = E::key_of_bits(vec_bits<BF16>(bufA[u], j));
-            if ((key & hi_mask) == (prefix & hi_mask)) atomicAdd(&hist_all[(key >> shift) & 255u], 1u);
+            if ((key & hi_mask) == (prefix & hi_mask)) atomicAdd(&hist[(key >> shift) & 255u], 1u);
           }
         }
       }
       __syncthreads();
       if (wid == 0) {
         int digit = 0, above = 0;
-        wave_pick_digit(hist_all, remaining, &digit, &above);
+        wave_pick_digit(hist, remaining, &digit, &above);
 #pragma unroll
         for (int o = kWave / 2; o > 0; o >>= 1) {
           digit = max(digit, __shfl_xor(digit, o, kWave));
@@ -424,40 +339,25 @@ __global__ void __launch_bounds__(kThreads, 4) lsm_topk_kernel(const typename El
       remaining -= S.sh[1];
       __syncthreads();
     }
-    wt.raise(prefix);
     if (tid == 0) S.thr = prefix;
+    sg.thr_f = thr_float<BF16>(prefix);
     // stage chunk 0's survivors
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const long long q = (long long)u * kThreads + tid;
-      const bool valid = q < nvec;
       float vm = -INFINITY;
 #pragma unroll
       for (int j = 0; j < VEC; ++j) vm = fmaxf(vm, vec_val<BF16>(bufA[u], j));
-      wt.stage(valid && !(vm < wt.thr_f), bufA[u], (uint32_t)(head + q * VEC));
+      sg.stage(q < nvec && !(vm < sg.thr_f), bufA[u], (uint32_t)(head + q * VEC));
     }
-    if (wt.scnt >= kFlushAt) wt.flush(&S.thr);
     for (long long c = 1; c < nchunks; c += 2) {
       load_chunk(bufA, vrow, c + 1, nvec, tid);
-      consume_chunk<BF16>(bufB, c, nvec, head, tid, st, wt, &S.thr);
+      consume_chunk<BF16, true>(bufB, c, nvec, head, tid, st, sg);
       if (c + 1 >= nchunks) break;
       load_chunk(bufB, vrow, c + 2, nvec, tid);
-      consume_chunk<BF16>(bufA, c + 1, nvec, head, tid, st, wt, &S.thr);
+      consume_chunk<BF16, true>(bufA, c + 1, nvec, head, tid, st, sg);
     }
   }
-
-  // scalars (head / tail, at most 2 * (VEC - 1) < 64): wave 0, one per lane
-  if (wid == 0) {
-    wt.raise(S.thr);
-    const bool has = lane < nscalar;
-    const long long i = has ? (lane < head ? (long long)lane : tail0 + (lane - head)) : 0;
-    const uint32_t bits = has ? E::bits_at(rowp, i) : 0u;
-    const float x = has ? E::val_of_bits(bits) : -INFINITY;
-    st.rescale(x);
-    st.s += (double)__builtin_amdgcn_exp2f(fmaf(x, kLog2e, -st.bias()));
-    wt.append(has, E::key_of_bits(bits), (uint32_t)i, &S.thr);
-  }
-  if (wt.scnt > 0) wt.flush(&S.thr);
   const float m = st.m;
   const double s = st.natural_sum();
 
@@ -473,8 +373,8 @@ __global__ void __launch_bounds__(kThreads, 4) lsm_topk_kernel(const typename El
     if (lane == 0) {
       S.red_m[wid] = mw;
       S.red_s[wid] = sw;
-      S.cnt[wid] = wt.cnt;
-      if (wt.overflow) S.overflow = 1;
+      S.cnt[wid] = sg.scnt;
+      if (sg.full) S.overflow = 1;
     }
   }
   __syncthreads();
@@ -495,41 +395,75 @@ __global__ void __launch_bounds__(kThreads, 4) lsm_topk_kernel(const typename El
   const double lse = S.lse;
 
   // ------------------------------------------------------------ exact top-k
-  constexpr int CBITS = E::KEYBITS + 32;
-  int total = 0;
-  for (int w = 0; w < kWaves; ++w) total += S.cnt[w];
-  if (!S.overflow && total >= k) {
-    auto get = [&](int i, uint64_t* out) -> bool {
-      const int w = i / cap_w, j = i - w * cap_w;
-      if (j >= S.cnt[w]) return false;
-      *out = cand_all[i];
-      return true;
-    };
-    const uint64_t ck = block_kth_largest<kThreads, CBITS>(kWaves * cap_w, k, get, hist_all, S.sh);
-    for (int i = tid; i < kWaves * cap_w; i += kThreads) {
-      const int w = i / cap_w, j = i - w * cap_w;
-      if (j < S.cnt[w] && cand_all[i] >= ck) {
-        const int slot = atomicAdd(&S.nsurv, 1);
-        if (slot < kp) sortbuf[slot] = cand_all[i];
+  if (!S.overflow) {
+    // the k-th largest key among the staged elements reaching the threshold
+    const uint32_t thr = S.thr;
+    uint32_t prefix = 0;
+    int remaining = k;
+    for (int shift = E::KEYBITS - 8; shift >= 0; shift -= 8) {
+      hist[tid] = 0;
+      __syncthreads();
+      const uint32_t hi_mask = (shift + 8 >= 32) ? 0u : (~0u << (shift + 8));
+      for_each_staged<BF16>(svec_all, sidx_all, cap_w, S, thr, [&](uint32_t key, uint32_t) {
+        if ((key & hi_mask) == (prefix & hi_mask)) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      });
+      __syncthreads();
+      if (wid == 0) {
+        int tot = 0;
+        for (int b = lane; b < 256; b += kWave) tot += (int)hist[b];
+        tot = wave_sum(tot);
+        int digit = 0, above = 0;
+        wave_pick_digit(hist, remaining, &digit, &above);
+#pragma unroll
+        for (int o = kWave / 2; o > 0; o >>= 1) {
+          digit = max(digit, __shfl_xor(digit, o, kWave));
+          above = max(above, __shfl_xor(above, o, kWave));
+        }
+        if (tid == 0) {
+          S.sh[0] = digit;
+          S.sh[1] = above;
+          if (shift == E::KEYBITS - 8 && tot < k) S.overflow = 1;  // fewer than k reached the guess
+        }
       }
+      __syncthreads();
+      if (S.overflow) break;
+      prefix |= (uint32_t)S.sh[0] << shift;
+      remaining -= S.sh[1];
+      __syncthreads();
     }
-  } else {
+    if (!S.overflow) {
+      // gather everything at or above the k-th key (k plus the ties)
+      for_each_staged<BF16>(svec_all, sidx_all, cap_w, S, prefix, [&](uint32_t key, uint32_t idx) {
+        const int slot = atomicAdd(&S.nsurv, 1);
+        if (slot < sort_cap) sortbuf[slot] = ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - idx);
+      });
+      __syncthreads();
+      if (tid == 0 && S.nsurv > sort_cap) {
+        S.overflow = 1;  // too many ties at the k-th key for the sort buffer
+        S.nsurv = 0;
+      }
+      __syncthreads();
+    }
+  }
+  if (S.overflow) {
     // Exact fallback: radix-select the k-th largest key over the row, then
     // take every element above it and the lowest-index ties at it.
     auto getk = [&](int i, uint64_t* out) -> bool {
       *out = E::key_of_bits(E::bits_at(rowp, i));
       return true;
     };
-    const uint32_t kk = (uint32_t)block_kth_largest<kThreads, E::KEYBITS>((int)V, k, getk, hist_all, S.sh);
+    const uint32_t kk = (uint32_t)block_kth_largest<kThreads, E::KEYBITS>((int)V, k, getk, hist, S.sh);
+    if (tid == 0) S.nsurv = 0;
+    __syncthreads();
     for (long long i = tid; i < V; i += kThreads) {
       const uint32_t key = E::key_of_bits(E::bits_at(rowp, i));
       if (key > kk) {
         const int slot = atomicAdd(&S.nsurv, 1);
-        if (slot < kp) sortbuf[slot] = ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
+        if (slot < sort_cap) sortbuf[slot] = ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
       }
     }
     __syncthreads();
-    const int taken = S.nsurv;  // elements strictly above the k-th key
+    const int taken = S.nsurv;  // elements strictly above the k-th key: fewer than k
     const int need = k - taken;
     int ties_before = 0;
     for (long long b0 = 0; b0 < V && ties_before < need; b0 += kThreads) {
@@ -537,17 +471,21 @@ __global__ void __launch_bounds__(kThreads, 4) lsm_topk_kernel(const typename El
       const bool tie = i < V && E::key_of_bits(E::bits_at(rowp, i)) == kk;
       int tot;
       const int r = ties_before + block_exclusive_scan<kThreads>(tie ? 1 : 0, S.scan, &tot);
-      if (tie && r < need && taken + r < kp)
+      if (tie && r < need && taken + r < sort_cap)
         sortbuf[taken + r] = ((uint64_t)kk << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
       ties_before += tot;
     }
+    if (tid == 0) S.nsurv = k;
+    __syncthreads();
   }
+  // sort the survivors (descending composite = key descending, token ascending)
+  const int ns = S.nsurv;
+  const int P = next_pow2(ns < k ? k : ns);
+  for (int i = ns + tid; i < P; i += kThreads) sortbuf[i] = 0ull;
   __syncthreads();
-  for (int i = k + tid; i < kp; i += kThreads) sortbuf[i] = 0ull;
-  __syncthreads();
-  block_bitonic_sort<kThreads>(sortbuf, kp);
+  block_bitonic_sort<kThreads>(sortbuf, P);
   for (int j = tid; j < k; j += kThreads) {
-    const uint64_t c = sortbuf[kp - 1 - j];
+    const uint64_t c = sortbuf[P - 1 - j];
     const uint32_t key = (uint32_t)(c >> 32);
     const uint32_t idx = 0xFFFFFFFFu - (uint32_t)c;
     const float x = E::val_of_key(key);
@@ -558,17 +496,19 @@ __global__ void __launch_bounds__(kThreads, 4) lsm_topk_kernel(const typename El
   }
 }
 
-// Candidate buffer per wave: k survivors, up to ~256 ties at the threshold,
-// and room for one append round (64).
+// Staging area per wave: 1.5x the expected survivor vectors of one wave, plus
+// one full round of slack.
 int wave_cap(int k) {
-  int c = k + 256 + kWave;
+  int c = (kOversample * k * 3) / (2 * kWaves) + kWave;
   return (c + 63) / 64 * 64;
 }
 
+// Sort buffer: k survivors plus room for ties at the k-th key.
+int sort_cap_for(int k) { return 2 * next_pow2(k); }
+
 size_t lsm_lds_bytes(int k) {
-  const int cap = wave_cap(k);
-  return (size_t)kWaves * kStage * 16 + (size_t)kWaves * cap * 8 + (size_t)kWaves * 256 * 4 +
-         (size_t)kWaves * kStage * 4 + (size_t)next_pow2(k) * 8 + 64;
+  return (size_t)kWaves * wave_cap(k) * 16 + (size_t)sort_cap_for(k) * 8 + 256 * 4 +
+         (size_t)kWaves * wave_cap(k) * 4 + 64;
 }
 
 }  // namespace
@@ -578,20 +518,21 @@ hipError_t launch_logsoftmax_topk(const void* logits, bool bf16, int rows, int r
                                   int32_t* status, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   const int cap = wave_cap(k);
+  const int scap = sort_cap_for(k);
   const size_t lds = lsm_lds_bytes(k);
   if (bf16) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lsm_topk_kernel<true>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(lsm_topk_kernel<true>, dim3(rows), dim3(kThreads), lds, stream,
-                       static_cast<const uint16_t*>(logits), V, k, cap, rows_per_tree, lse, topk_id, topk_raw,
+                       static_cast<const uint16_t*>(logits), V, k, cap, scap, rows_per_tree, lse, topk_id, topk_raw,
                        topk_logp, status);
   } else {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lsm_topk_kernel<false>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(lsm_topk_kernel<false>, dim3(rows), dim3(kThreads), lds, stream,
-                       static_cast<const float*>(logits), V, k, cap, rows_per_tree, lse, topk_id, topk_raw,
+                       static_cast<const float*>(logits), V, k, cap, scap, rows_per_tree, lse, topk_id, topk_raw,
                        topk_logp, status);
   }
   return hipGetLastError();
