@@ -12,20 +12,27 @@
 //  * 16-byte non-temporal vector loads (8 bf16 or 4 fp32), consecutive lanes on
 //    consecutive 16-byte chunks, four per lane per chunk, double-buffered in
 //    registers so the next chunk is in flight while one is consumed.
-//  * Online log-sum-exp per lane in base 2 (one FMA and one v_exp_f32 per
-//    element, fp32 terms summed per vector into an fp64 running sum); lanes,
-//    waves and the block are combined in fp64.
-//  * Top-k in the same pass.  The first chunk (8192 bf16 elements) is a sample:
-//    the block radix-selects the key that should leave about 3k elements of
-//    the row above it.  During the stream a lane whose vector maximum reaches
-//    that key copies the whole 16-byte vector into its wave's LDS area (slot
-//    from ballot + popcount).  At the end the block radix-selects the exact
-//    k-th key over the staged elements, gathers those at or above it, and
-//    bitonic-sorts them by (key descending, token ascending).
-//  * Whenever the guess does not hold (fewer than k elements reach it, a
-//    wave's area fills up, or too many ties sit at the k-th key), the row
-//    takes an exact multi-pass radix top-k that re-reads the row.  The guess
-//    changes speed only, never results.
+//  * The first two chunks (16384 bf16 elements, already in registers when the
+//    stream starts) are a sample.  Their maximum M0 fixes the exponent bias of
+//    the whole row: every element adds 2^(x*log2e - M0*log2e) (one FMA and one
+//    v_exp_f32), summed pairwise in fp32 per chunk and in fp64 across chunks;
+//    no running maximum, no rescaling.  If that sum overflows or underflows
+//    (the row maximum lies far from M0), it is redone with the true maximum.
+//  * The r-th largest of the 256 lanes' sample maxima (a bitwise search on
+//    ballot counts) is a threshold that leaves, with high probability, between
+//    k and a few k elements of the row at or above it.  During the stream a
+//    lane whose vector's term sum reaches that of the threshold copies the
+//    whole 16-byte vector into its wave's LDS area (slot from ballot +
+//    popcount), or into a shared pool once that area is full.
+//  * At the end the staged elements that reach the threshold are compacted
+//    into a candidate list, the block radix-selects the exact k-th key over
+//    it, gathers the candidates at or above it (k plus ties) and sorts them by
+//    (key descending, token ascending), mostly in registers.
+//  * Whenever the guess does not hold the row still gets the exact answer:
+//    too many candidates -> select straight from the staged vectors; fewer
+//    than k, or the staging space overflowed -> a radix top-k over the row,
+//    streamed again with the same vector loads.  The guess changes speed only,
+//    never results.
 #include <math.h>
 
 #include "mfd_device.hpp"
@@ -38,8 +45,10 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kUnroll = 4;
 constexpr long long kStep = (long long)kThreads * kUnroll;
-constexpr int kOversample = 3;
 constexpr float kLog2e = 1.44269504088896340736f;
+constexpr double kLn2 = 0.693147180559945309417232121458;
+// LDS one workgroup may use (of 160 KB per CU), static part included.
+constexpr size_t kMaxLds = 156 * 1024;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -54,6 +63,7 @@ struct Elem<true> {
   __device__ static float val_of_key(uint32_t k) { return bf16_bits_to_f32(bf16_from_key(k)); }
   __device__ static uint32_t bits_at(const T* p, long long i) { return p[i]; }
   __device__ static float val_of_bits(uint32_t b) { return bf16_bits_to_f32(b); }
+  __device__ static uint32_t key_of_float(float x) { return bf16_key(__float_as_uint(x) >> 16); }
 };
 template <>
 struct Elem<false> {
@@ -64,6 +74,7 @@ struct Elem<false> {
   __device__ static float val_of_key(uint32_t k) { return __uint_as_float(f32_from_key(k)); }
   __device__ static uint32_t bits_at(const T* p, long long i) { return __float_as_uint(p[i]); }
   __device__ static float val_of_bits(uint32_t b) { return __uint_as_float(b); }
+  __device__ static uint32_t key_of_float(float x) { return f32_key(__float_as_uint(x)); }
 };
 
 // Element j of a 16-byte vector (j may be a run-time value), as raw bits / as a float.
@@ -81,19 +92,42 @@ __device__ __forceinline__ float vec_val(const u32x4& v, int j) {
   return __uint_as_float(w);
 }
 
+__device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t idx) {
+  return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - idx);
+}
+
+__device__ __forceinline__ float term(float x, float bias) {
+  return __builtin_amdgcn_exp2f(fmaf(x, kLog2e, -bias));
+}
+
+// Rank of the sample threshold among the lanes' sample maxima.  The number of
+// row elements at or above the r-th largest of n0 sampled ones is about
+// (V / n0) * Gamma(r); r is the smallest value whose mean minus 4.5 standard
+// deviations still reaches k.  Host and device use the same formula.
+__host__ __device__ __forceinline__ int sample_rank(long long V, long long n0, int k) {
+  const double a = (double)k * (double)n0 / (double)V;
+  const double sr = 0.5 * (4.5 + sqrt(20.25 + 4.0 * a));
+  long long r = (long long)ceil(sr * sr);
+  if (r < 1) r = 1;
+  if (r > kThreads) r = kThreads;
+  return (int)r;
+}
+
 struct Shared {
-  uint32_t thr;     // the row's sampled threshold key
-  int overflow;     // the staged guess cannot be used: take the exact fallback
-  int cnt[kWaves];  // staged vectors per wave
+  int overflow;         // the staged guess cannot be used: take the exact fallback
+  int cnt[kWaves];      // staged vectors per wave
+  int pool;             // pool slots handed out (may exceed the pool on overflow)
+  uint32_t fail_at;     // index of the first element whose vector found no room
   int nsurv;
+  int ncand;
   int sh[4];
   int scan[kWaves];
-  float red_m[kWaves];
+  float red_max[kWaves];
   double red_s[kWaves];
-  double lse;
-  uint32_t skey[64];  // head/tail scalars: keys
-  uint32_t sidx[64];  //                    and indices
+  uint32_t skey[64];    // head/tail scalars: keys
+  uint32_t sidx[64];    //                    and indices
   int nscal;
+  uint32_t hist[256];   // radix histogram; the lanes' sample keys before that
 };
 
 // Smallest non-NaN key (that of -inf) for the element type.
@@ -107,130 +141,201 @@ __device__ __forceinline__ float thr_float(uint32_t thr) {
   return thr <= min_real_key<BF16>() ? -INFINITY : Elem<BF16>::val_of_key(thr);
 }
 
-// Per-wave staging of candidate vectors.
+// Staging of candidate vectors: a wave's own area first, then the shared pool.
 struct Stager {
-  u32x4* svec;     // staged vectors
-  uint32_t* sidx;  // index of each staged vector's first element
+  u32x4* svec;     // own area: staged vectors
+  uint32_t* sidx;  //           index of each staged vector's first element
+  u32x4* pvec;     // shared pool
+  uint32_t* pidx;
+  int* pool_used;
+  uint32_t* fail_at;
+  int pool_cap;
   int cap;
   int scnt;        // wave-uniform
-  float thr_f;     // value of the threshold key (-inf below the smallest real key)
   bool full;       // wave-uniform: a candidate did not fit
 
-  // Wave-level: lanes with `p` stage their vector.
-  __device__ __forceinline__ void stage(bool p, const u32x4& v, uint32_t i0) {
+  // Wave-level: lanes with `p` stage their vector, whose first element has
+  // index ibase + ioff.
+  __device__ __forceinline__ void stage(bool p, const u32x4& v, uint32_t ibase, uint32_t ioff) {
+    if (full) return;  // the row is staged again anyway
     const uint64_t m = __ballot(p);
     if (m == 0ull) return;
     const int n = __popcll(m);
-    if (scnt + n > cap) {
+    const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    const uint32_t i0 = ibase + ioff;
+    if (scnt + n <= cap) {
+      if (p) {
+        svec[scnt + rank] = v;
+        sidx[scnt + rank] = i0;
+      }
+      scnt = __builtin_amdgcn_readfirstlane(scnt + n);
+      return;
+    }
+    int base = 0;
+    if (lane_id() == 0) base = atomicAdd(pool_used, n);
+    base = __shfl(base, 0, kWave);
+    if (base + n > pool_cap) {
+      if (lane_id() == 0) atomicMin(fail_at, ibase);
       full = true;
       return;
     }
     if (p) {
-      const int slot = scnt + __popcll(m & lanemask_lt());
-      svec[slot] = v;
-      sidx[slot] = i0;
+      pvec[base + rank] = v;
+      pidx[base + rank] = i0;
     }
-    scnt += n;
   }
 };
 
-// Per-lane running log-sum-exp in base 2: s = sum 2^(x*log2e - ml) with
-// ml = m*log2e rounded to fp32 (m the lane's running max).  The rounding of ml
-// is undone exactly at the end, in fp64; each rise of the maximum costs one
-// fp32 rounding of the rescale factor (a few per lane per row).
-struct LaneLse {
-  float m = -INFINITY;
-  float ml = -INFINITY;
-  double s = 0.0;
-
-  __device__ __forceinline__ void rescale(float vm) {
-    if (vm > m) {
-      const float mln = vm * kLog2e;
-      s *= (double)__builtin_amdgcn_exp2f(ml - mln);
-      m = vm;
-      ml = mln;
-    }
-  }
-  __device__ __forceinline__ float bias() const { return (m == -INFINITY) ? 0.f : ml; }
-  // sum exp(x - m) in natural units
-  __device__ __forceinline__ double natural_sum() const {
-    if (m == -INFINITY || m == INFINITY) return s;
-    return s * exp2((double)ml - (double)m * (double)kLog2e);
-  }
-};
-
-template <bool BF16, bool FULL, bool STAGE>
-__device__ __forceinline__ void consume_vector(const u32x4& v, uint32_t i0, bool valid, LaneLse& st, Stager& sg) {
+// One vector: returns the sum of its terms (pairwise, fp32) and stages the
+// vector if that sum reaches tau.  With tau = 0.999 * term(threshold) this
+// keeps every vector holding an element at or above the threshold: such an
+// element's term is at least term(threshold) up to an ulp or two of exp2,
+// and the other terms are not negative.  (NaN terms stage nothing.)
+template <bool BF16, bool FULL>
+__device__ __forceinline__ float consume_vector(const u32x4& v, uint32_t ibase, uint32_t ioff, bool valid, float bias,
+                                                float tau, Stager& sg) {
   constexpr int VEC = Elem<BF16>::VEC;
-  float f[VEC];
+  float e[VEC];
 #pragma unroll
-  for (int j = 0; j < VEC; ++j) f[j] = (FULL || valid) ? vec_val<BF16>(v, j) : -INFINITY;
-  float vm = f[0];
+  for (int j = 0; j < VEC; ++j) e[j] = (FULL || valid) ? term(vec_val<BF16>(v, j), bias) : 0.f;
 #pragma unroll
-  for (int j = 1; j < VEC; ++j) vm = fmaxf(vm, f[j]);
-  st.rescale(vm);
-  const float b = st.bias();
-  float acc = 0.f;
+  for (int w = VEC / 2; w > 0; w >>= 1) {
 #pragma unroll
-  for (int j = 0; j < VEC; ++j) acc += __builtin_amdgcn_exp2f(fmaf(f[j], kLog2e, -b));
-  st.s += (double)acc;
-  if (STAGE) sg.stage((FULL || valid) && !(vm < sg.thr_f), v, i0);
+    for (int j = 0; j < w; ++j) e[j] += e[j + w];
+  }
+  sg.stage((FULL || valid) && e[0] >= tau, v, ibase, ioff);
+  return e[0];
 }
 
-__device__ __forceinline__ void load_chunk(u32x4* buf, const u32x4* vrow, long long c, long long nvec, int tid) {
+// Loads chunk c (four 16-byte vectors per lane).  Byte offsets are 32-bit
+// and clamped to the row's last vector, so every load is in bounds and there
+// is no branch between the loads of the two buffers.
+__device__ __forceinline__ void load_chunk(u32x4* buf, const u32x4* vrow, long long c, uint32_t last_byte, int tid) {
+  const uint32_t cbyte = (uint32_t)(c * kStep) * (uint32_t)sizeof(u32x4);
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
-    long long q = c * kStep + (long long)u * kThreads + tid;
-    q = q < nvec ? q : nvec - 1;  // clamped: every load is valid
-    buf[u] = __builtin_nontemporal_load(vrow + q);
+    const uint32_t off = min(cbyte + (uint32_t)((u * kThreads + tid) * (int)sizeof(u32x4)), last_byte);
+    buf[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(vrow) + off));
   }
 }
 
-template <bool BF16, bool STAGE>
-__device__ __forceinline__ void consume_chunk(const u32x4* buf, long long c, long long nvec, long long head, int tid,
-                                              LaneLse& st, Stager& sg) {
+template <bool BF16>
+__device__ __forceinline__ float consume_chunk(const u32x4* buf, long long c, long long nvec, long long head, int tid,
+                                               float bias, float tau, Stager& sg) {
   constexpr int VEC = Elem<BF16>::VEC;
   const long long base = c * kStep;
+  const uint32_t ibase = (uint32_t)(head + base * VEC);
+  float t[kUnroll];
   if (base + kStep <= nvec) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const long long q = base + (long long)u * kThreads + tid;
-      consume_vector<BF16, true, STAGE>(buf[u], (uint32_t)(head + q * VEC), true, st, sg);
-    }
+    for (int u = 0; u < kUnroll; ++u)
+      t[u] = consume_vector<BF16, true>(buf[u], ibase, (uint32_t)((u * kThreads + tid) * VEC), true, bias, tau, sg);
   } else {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const long long q = base + (long long)u * kThreads + tid;
-      consume_vector<BF16, false, STAGE>(buf[u], (uint32_t)(head + q * VEC), q < nvec, st, sg);
+      t[u] = consume_vector<BF16, false>(buf[u], ibase, (uint32_t)((u * kThreads + tid) * VEC), q < nvec, bias, tau,
+                                         sg);
+    }
+  }
+  return (t[0] + t[1]) + (t[2] + t[3]);
+}
+
+// Streams the row's aligned vectors once more (same loads as the main pass)
+// and calls f(v, q, valid) for each lane's vector q.  Every lane of the block
+// makes the same calls, so f may use wave-level operations.
+template <typename F>
+__device__ __forceinline__ void stream_vectors(const u32x4* vrow, long long nvec, int tid, F f) {
+  if (nvec <= 0) return;
+  const long long nchunks = (nvec + kStep - 1) / kStep;
+  const uint32_t last_byte = (uint32_t)(nvec - 1) * (uint32_t)sizeof(u32x4);
+  u32x4 a[kUnroll], b[kUnroll];
+  load_chunk(a, vrow, 0, last_byte, tid);
+  for (long long c = 0; c < nchunks; c += 2) {
+    load_chunk(b, vrow, c + 1, last_byte, tid);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const long long q = c * kStep + (long long)u * kThreads + tid;
+      f(a[u], q, q < nvec);
+    }
+    if (c + 1 >= nchunks) break;
+    load_chunk(a, vrow, c + 2, last_byte, tid);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const long long q = (c + 1) * kStep + (long long)u * kThreads + tid;
+      f(b[u], q, q < nvec);
     }
   }
 }
 
-// Calls f(key, index) for every staged element (and head/tail scalar) whose
-// key reaches `thr`.  Block-strided; no barrier.
-template <bool BF16, typename F>
-__device__ __forceinline__ void for_each_staged(const u32x4* svec_all, const uint32_t* sidx_all, int cap,
-                                                const Shared& S, uint32_t thr, F f) {
-  constexpr int VEC = Elem<BF16>::VEC;
-  for (int i = threadIdx.x; i < kWaves * cap; i += kThreads) {
-    const int w = i / cap, j = i - w * cap;
-    if (j >= S.cnt[w]) continue;
-    const u32x4 v = svec_all[i];
-    const uint32_t i0 = sidx_all[i];
+// Appends the composites of the lanes with `p` to buf[*counter ...] (entries
+// past `cap` are counted but not written).  Wave-level; one LDS atomic per wave.
+__device__ __forceinline__ void wave_append(bool p, uint64_t c, uint64_t* buf, int cap, int* counter) {
+  const uint64_t m = __ballot(p);
+  int base = 0;
+  if (lane_id() == 0 && m) base = atomicAdd(counter, __popcll(m));
+  base = __shfl(base, 0, kWave);
+  const int pos = base + __popcll(m & lanemask_lt());
+  if (p && pos < cap) buf[pos] = c;
+}
+
+// Wave 0 helper of the radix selections: digit of the `remaining`-th largest
+// key in S.hist and the count above it, into S.sh[0..1].
+__device__ __forceinline__ void pick_digit_into(Shared& S, int remaining) {
+  int digit = 0, above = 0;
+  wave_pick_digit(S.hist, remaining, &digit, &above);
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      const uint32_t key = Elem<BF16>::key_of_bits(vec_bits<BF16>(v, e));
-      if (key >= thr) f(key, i0 + e);
-    }
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    digit = max(digit, __shfl_xor(digit, o, kWave));
+    above = max(above, __shfl_xor(above, o, kWave));
   }
-  for (int i = threadIdx.x; i < S.nscal; i += kThreads)
-    if (S.skey[i] >= thr) f(S.skey[i], S.sidx[i]);
+  if (lane_id() == 0) {
+    S.sh[0] = digit;
+    S.sh[1] = above;
+  }
+}
+
+// Exact k-th largest key of the whole row (vectors streamed again, scalars
+// from S).  Barriers inside; every thread returns the same key.
+template <bool BF16>
+__device__ __forceinline__ uint32_t row_kth_largest(const u32x4* vrow, long long nvec, int k, Shared& S) {
+  using E = Elem<BF16>;
+  constexpr int VEC = E::VEC;
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0;
+  int remaining = k;
+  for (int shift = E::KEYBITS - 8; shift >= 0; shift -= 8) {
+    S.hist[tid] = 0;
+    __syncthreads();
+    const uint32_t hi_mask = (shift + 8 >= 32) ? 0u : (~0u << (shift + 8));
+    const uint32_t want = prefix & hi_mask;
+    stream_vectors(vrow, nvec, tid, [&](const u32x4& v, long long, bool valid) {
+      if (!valid) return;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const uint32_t key = E::key_of_bits(vec_bits<BF16>(v, e));
+        if ((key & hi_mask) == want) atomicAdd(&S.hist[(key >> shift) & 255u], 1u);
+      }
+    });
+    if (tid < S.nscal) {
+      const uint32_t key = S.skey[tid];
+      if ((key & hi_mask) == want) atomicAdd(&S.hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (wave_id() == 0) pick_digit_into(S, remaining);
+    __syncthreads();
+    prefix |= (uint32_t)S.sh[0] << shift;
+    remaining -= S.sh[1];
+    __syncthreads();
+  }
+  return prefix;
 }
 
 template <bool BF16>
-__global__ void __launch_bounds__(kThreads, 4) lsm_topk_kernel(const typename Elem<BF16>::T* __restrict__ logits,
-                                                               long long V, int k, int cap_w, int sort_cap,
-                                                               int rows_per_tree, double* __restrict__ lse_out,
+__global__ void __launch_bounds__(kThreads, 5) lsm_topk_kernel(const typename Elem<BF16>::T* __restrict__ logits,
+                                                               long long V, int k, int cap_w, int pool_cap,
+                                                               int sort_cap, int cand_cap, int rows_per_tree,
+                                                               double* __restrict__ lse_out,
                                                                int32_t* __restrict__ topk_id,
                                                                float* __restrict__ topk_raw,
                                                                float* __restrict__ topk_logp,
@@ -239,10 +344,14 @@ __global__ void __launch_bounds__(kThreads, 4) lsm_topk_kernel(const typename El
   using T = typename E::T;
   constexpr int VEC = E::VEC;
   extern __shared__ __align__(16) unsigned char smem_raw[];
+  // LDS: staged vectors (4 wave areas, then the pool) | their indices |
+  // candidate list.  Once the staged vectors have been compacted the start of
+  // their area holds the sort buffer.
+  const int nslot = kWaves * cap_w + pool_cap;
   u32x4* svec_all = reinterpret_cast<u32x4*>(smem_raw);
-  uint64_t* sortbuf = reinterpret_cast<uint64_t*>(svec_all + (size_t)kWaves * cap_w);
-  uint32_t* hist = reinterpret_cast<uint32_t*>(sortbuf + sort_cap);
-  uint32_t* sidx_all = hist + 256;
+  uint32_t* sidx_all = reinterpret_cast<uint32_t*>(svec_all + nslot);
+  uint64_t* cand = reinterpret_cast<uint64_t*>(sidx_all + nslot);
+  uint64_t* sortbuf = reinterpret_cast<uint64_t*>(smem_raw);
   __shared__ Shared S;
 
   const int tid = threadIdx.x, lane = lane_id(), wid = wave_id();
@@ -250,20 +359,24 @@ __global__ void __launch_bounds__(kThreads, 4) lsm_topk_kernel(const typename El
   const T* rowp = logits + row * V;
 
   if (tid == 0) {
-    S.thr = 0;
     S.overflow = 0;
+    S.pool = 0;
+    S.fail_at = 0xFFFFFFFFu;
     S.nsurv = 0;
+    S.ncand = 0;
   }
 
   Stager sg;
   sg.svec = svec_all + (size_t)wid * cap_w;
   sg.sidx = sidx_all + (size_t)wid * cap_w;
+  sg.pvec = svec_all + (size_t)kWaves * cap_w;
+  sg.pidx = sidx_all + (size_t)kWaves * cap_w;
+  sg.pool_used = &S.pool;
+  sg.fail_at = &S.fail_at;
+  sg.pool_cap = pool_cap;
   sg.cap = cap_w;
   sg.scnt = 0;
-  sg.thr_f = -INFINITY;
   sg.full = false;
-
-  LaneLse st;
 
   // Split the row into a scalar head (to 16-byte alignment), aligned vectors
   // and a scalar tail.
@@ -273,219 +386,378 @@ __global__ void __launch_bounds__(kThreads, 4) lsm_topk_kernel(const typename El
   const long long nvec = (V - head) / VEC;
   const long long tail0 = head + nvec * VEC;
   const int nscalar = (int)(head + (V - tail0));
-
-  // scalars (head / tail, at most 2 * (VEC - 1) < 64): wave 0, one per lane
-  if (wid == 0) {
-    const bool has = lane < nscalar;
-    const long long i = has ? (lane < head ? (long long)lane : tail0 + (lane - head)) : 0;
-    const uint32_t bits = has ? E::bits_at(rowp, i) : 0u;
-    const float x = has ? E::val_of_bits(bits) : -INFINITY;
-    st.rescale(x);
-    st.s += (double)__builtin_amdgcn_exp2f(fmaf(x, kLog2e, -st.bias()));
-    if (has) {
-      S.skey[lane] = E::key_of_bits(bits);
-      S.sidx[lane] = (uint32_t)i;
-    }
-    if (lane == 0) S.nscal = nscalar;
-  }
-  __syncthreads();
-
-  // Vectors, double-buffered chunks.  Chunk 0 doubles as the sample.
   const u32x4* vrow = reinterpret_cast<const u32x4*>(rowp + head);
+  const long long nchunks = (nvec + kStep - 1) / kStep;
+  const uint32_t last_byte = nvec > 0 ? (uint32_t)(nvec - 1) * (uint32_t)sizeof(u32x4) : 0u;
+
+  // Scalars (head / tail, at most 2 * (VEC - 1) < 64): wave 0, one per lane.
+  // Loaded before the chunks and used after them, so that waiting for them
+  // does not wait for the chunks too.
+  const bool shas = wid == 0 && lane < nscalar;
+  const long long si = shas ? (lane < head ? (long long)lane : tail0 + (lane - head)) : 0;
+  const uint32_t sbits = E::bits_at(rowp, si);  // every lane loads (element 0 if none), no branch
+
+  // Three chunk buffers: two chunks stay in flight while one is consumed.
+  u32x4 bufA[kUnroll], bufB[kUnroll], bufC[kUnroll];
   if (nvec > 0) {
-    const long long nchunks = (nvec + kStep - 1) / kStep;
-    u32x4 bufA[kUnroll], bufB[kUnroll];
-    load_chunk(bufA, vrow, 0, nvec, tid);
-    load_chunk(bufB, vrow, 1, nvec, tid);
-    consume_chunk<BF16, false>(bufA, 0, nvec, head, tid, st, sg);
-    // sampled threshold: the r-th largest key of chunk 0, r chosen so that
-    // about kOversample * k elements of the row are expected above it
-    const long long n0 = (kStep <= nvec ? kStep : nvec) * VEC;
-    long long r = (kOversample * (long long)k * n0 + V - 1) / V;
-    r = r < 1 ? 1 : (r > n0 ? n0 : r);
-    uint32_t prefix = 0;
-    int remaining = (int)r;
-    for (int shift = E::KEYBITS - 8; shift >= 0; shift -= 8) {
-      hist[tid] = 0;
-      __syncthreads();
-      const uint32_t hi_mask = (shift + 8 >= 32) ? 0u : (~0u << (shift + 8));
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const long long q = (long long)u * kThreads + tid;
-        if (q < nvec) {
-#pragma unroll
-          for (int j = 0; j < VEC; ++j) {
-            const uint32_t key = E::key_of_bits(vec_bits<BF16>(bufA[u], j));
-            if ((key & hi_mask) == (prefix & hi_mask)) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-          }
-        }
-      }
-      __syncthreads();
-      if (wid == 0) {
-        int digit = 0, above = 0;
-        wave_pick_digit(hist, remaining, &digit, &above);
-#pragma unroll
-        for (int o = kWave / 2; o > 0; o >>= 1) {
-          digit = max(digit, __shfl_xor(digit, o, kWave));
-          above = max(above, __shfl_xor(above, o, kWave));
-        }
-        if (tid == 0) {
-          S.sh[0] = digit;
-          S.sh[1] = above;
-        }
-      }
-      __syncthreads();
-      prefix |= (uint32_t)S.sh[0] << shift;
-      remaining -= S.sh[1];
-      __syncthreads();
-    }
-    if (tid == 0) S.thr = prefix;
-    sg.thr_f = thr_float<BF16>(prefix);
-    // stage chunk 0's survivors
+    load_chunk(bufA, vrow, 0, last_byte, tid);
+    load_chunk(bufB, vrow, 1, last_byte, tid);
+    load_chunk(bufC, vrow, 2, last_byte, tid);
+  }
+
+  const float xs = shas ? E::val_of_bits(sbits) : -INFINITY;
+  if (shas) {
+    S.skey[lane] = E::key_of_bits(sbits);
+    S.sidx[lane] = (uint32_t)si;
+  }
+  if (tid == 0) S.nscal = nscalar;
+
+  // ------------------------------------------------------------ the sample
+  // The sample is chunks 0 and 1 (both already in registers) and the scalars.
+  // Lane maxima over it; NaN is skipped by fmaxf.
+  // (Selects, not branches, so the wait covers chunks 0 and 1 only.)
+  float lmax = xs;
+  if (nvec > 0) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const long long q = (long long)u * kThreads + tid;
-      float vm = -INFINITY;
+      float ma = vec_val<BF16>(bufA[u], 0), mb = vec_val<BF16>(bufB[u], 0);
 #pragma unroll
-      for (int j = 0; j < VEC; ++j) vm = fmaxf(vm, vec_val<BF16>(bufA[u], j));
-      sg.stage(q < nvec && !(vm < sg.thr_f), bufA[u], (uint32_t)(head + q * VEC));
-    }
-    for (long long c = 1; c < nchunks; c += 2) {
-      load_chunk(bufA, vrow, c + 1, nvec, tid);
-      consume_chunk<BF16, true>(bufB, c, nvec, head, tid, st, sg);
-      if (c + 1 >= nchunks) break;
-      load_chunk(bufB, vrow, c + 2, nvec, tid);
-      consume_chunk<BF16, true>(bufA, c + 1, nvec, head, tid, st, sg);
+      for (int j = 1; j < VEC; ++j) {
+        ma = fmaxf(ma, vec_val<BF16>(bufA[u], j));
+        mb = fmaxf(mb, vec_val<BF16>(bufB[u], j));
+      }
+      lmax = fmaxf(lmax, q < nvec ? ma : -INFINITY);
+      lmax = fmaxf(lmax, q + kStep < nvec ? mb : -INFINITY);
     }
   }
-  const float m = st.m;
-  const double s = st.natural_sum();
+  S.hist[tid] = E::key_of_float(lmax);
+  __syncthreads();
+  const uint32_t k0 = S.hist[lane], k1 = S.hist[lane + kWave], k2 = S.hist[lane + 2 * kWave],
+                 k3 = S.hist[lane + 3 * kWave];
+  // Threshold: the r-th largest lane maximum, so at least r sampled elements
+  // reach it.  Every wave runs the same bitwise search over all 256 keys (four
+  // ballots per bit), so all agree without another barrier.
+  const long long n0 = (2 * kStep <= nvec ? 2 * kStep : nvec) * VEC + nscalar;
+  const int r = sample_rank(V, n0, k);
+  uint32_t thr = 0;
+#pragma unroll 1
+  for (int bit = E::KEYBITS - 1; bit >= 0; --bit) {
+    const uint32_t tt = thr | (1u << bit);
+    const int c = __popcll(__ballot(k0 >= tt)) + __popcll(__ballot(k1 >= tt)) + __popcll(__ballot(k2 >= tt)) +
+                  __popcll(__ballot(k3 >= tt));
+    if (c >= r) thr = tt;
+  }
+  // Bias: the sample maximum M0 in log2 units (0 if M0 is not finite).
+  uint32_t mkey = max(max(k0, k1), max(k2, k3));
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) mkey = max(mkey, (uint32_t)__shfl_xor((int)mkey, o, kWave));
+  const float m0 = thr_float<BF16>(mkey);
+  const float bias = isfinite(m0) ? m0 * kLog2e : 0.f;
+  // Staging cut on a vector's term sum (see consume_vector); 0 stages every vector.
+  const float thr_f = thr_float<BF16>(thr);
+  const float tau = thr_f == -INFINITY ? 0.f : 0.999f * term(thr_f, bias);
+
+  // ------------------------------------------------------------ the stream
+  double s = (double)term(xs, bias);
+  if (nvec > 0) {
+    s += (double)consume_chunk<BF16>(bufA, 0, nvec, head, tid, bias, tau, sg);
+    // invariant at the loop head: B holds chunk c, C chunk c + 1
+    long long c = 1;
+    for (; c + 2 < nchunks; c += 3) {
+      load_chunk(bufA, vrow, c + 2, last_byte, tid);
+      s += (double)consume_chunk<BF16>(bufB, c, nvec, head, tid, bias, tau, sg);
+      load_chunk(bufB, vrow, c + 3, last_byte, tid);
+      s += (double)consume_chunk<BF16>(bufC, c + 1, nvec, head, tid, bias, tau, sg);
+      load_chunk(bufC, vrow, c + 4, last_byte, tid);
+      s += (double)consume_chunk<BF16>(bufA, c + 2, nvec, head, tid, bias, tau, sg);
+    }
+    if (c < nchunks) s += (double)consume_chunk<BF16>(bufB, c, nvec, head, tid, bias, tau, sg);
+    if (c + 1 < nchunks) s += (double)consume_chunk<BF16>(bufC, c + 1, nvec, head, tid, bias, tau, sg);
+  }
 
   // ------------------------------------------------------------ log-normaliser
-  // m is never NaN (it only moves on `>`); a NaN logit turns s into NaN.
-  {
-    float mw = m;
 #pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) mw = fmaxf(mw, __shfl_xor(mw, o, kWave));
-    double sw = s * ((m == -INFINITY) ? 0.0 : exp((double)m - (double)mw));
+  for (int o = kWave / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, kWave);
+  if (lane == 0) {
+    S.red_s[wid] = s;
+    S.cnt[wid] = sg.scnt;
+    if (sg.full) S.overflow = 1;
+  }
+  __syncthreads();
+  double sum = 0.0;
 #pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) sw += __shfl_xor(sw, o, kWave);
-    if (lane == 0) {
-      S.red_m[wid] = mw;
-      S.red_s[wid] = sw;
-      S.cnt[wid] = sg.scnt;
-      if (sg.full) S.overflow = 1;
+  for (int w = 0; w < kWaves; ++w) sum += S.red_s[w];
+  double lse;
+  if (isnan(sum)) {
+    lse = NAN;
+  } else if (isfinite(sum) && sum >= 0x1p-60) {
+    // no term overflowed, and every term that matters is a normal float
+    lse = (double)bias * kLn2 + log(sum);
+  } else {
+    // The sample maximum was too far from the row maximum (or the row holds
+    // +inf or only -inf): find the row maximum, then sum again with it as the
+    // bias.
+    float mx = xs;
+    stream_vectors(vrow, nvec, tid, [&](const u32x4& v, long long, bool valid) {
+      if (!valid) return;
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) mx = fmaxf(mx, vec_val<BF16>(v, j));
+    });
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+    __syncthreads();
+    if (lane == 0) S.red_max[wid] = mx;
+    __syncthreads();
+    float rmax = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) rmax = fmaxf(rmax, S.red_max[w]);
+    if (rmax == INFINITY) {
+      lse = INFINITY;
+    } else if (rmax == -INFINITY) {
+      lse = -INFINITY;  // every element is -inf
+    } else {
+      const float b2 = rmax * kLog2e;
+      double s2 = (double)term(xs, b2);
+      stream_vectors(vrow, nvec, tid, [&](const u32x4& v, long long, bool valid) {
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) acc += valid ? term(vec_val<BF16>(v, j), b2) : 0.f;
+        s2 += (double)acc;
+      });
+#pragma unroll
+      for (int o = kWave / 2; o > 0; o >>= 1) s2 += __shfl_xor(s2, o, kWave);
+      if (lane == 0) S.red_s[wid] = s2;
+      __syncthreads();
+      double sum2 = 0.0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) sum2 += S.red_s[w];
+      lse = (double)b2 * kLn2 + log(sum2);
     }
   }
-  __syncthreads();
   if (tid == 0) {
-    float mb = S.red_m[0];
-    for (int w = 1; w < kWaves; ++w) mb = fmaxf(mb, S.red_m[w]);
-    double sb = 0.0;
-    for (int w = 0; w < kWaves; ++w)
-      sb += S.red_s[w] * ((S.red_m[w] == -INFINITY) ? 0.0 : exp((double)S.red_m[w] - (double)mb));
-    double l;
-    if (mb == -INFINITY) l = (sb == 0.0) ? -INFINITY : NAN;
-    else l = (double)mb + log(sb);
-    S.lse = l;
-    lse_out[row] = l;
-    if (status && (isnan(l) || l == INFINITY)) atomicOr(&status[row / rows_per_tree], 1);
+    lse_out[row] = lse;
+    if (status && (isnan(lse) || lse == INFINITY)) atomicOr(&status[row / rows_per_tree], 1);
   }
-  __syncthreads();
-  const double lse = S.lse;
 
   // ------------------------------------------------------------ exact top-k
-  if (!S.overflow) {
-    // the k-th largest key among the staged elements reaching the threshold
-    const uint32_t thr = S.thr;
-    uint32_t prefix = 0;
-    int remaining = k;
-    for (int shift = E::KEYBITS - 8; shift >= 0; shift -= 8) {
-      hist[tid] = 0;
+  uint64_t* sb = sortbuf;  // where the survivors end up
+  uint32_t sel = thr;      // every row element at or above `sel` is staged
+  // Staged vectors: wave areas 0..3, then the pool, indexed g in [0, tot).
+  int o1, o2, o3, o4, tot;
+  auto staged_layout = [&]() {
+    const int c4 = S.pool < pool_cap ? S.pool : pool_cap;
+    o1 = S.cnt[0];
+    o2 = o1 + S.cnt[1];
+    o3 = o2 + S.cnt[2];
+    o4 = o3 + S.cnt[3];
+    tot = o4 + c4;
+  };
+  auto slot_of = [&](int g) -> int {
+    const int w = (g >= o1) + (g >= o2) + (g >= o3) + (g >= o4);
+    const int off = w == 0 ? 0 : (w == 1 ? o1 : (w == 2 ? o2 : (w == 3 ? o3 : o4)));
+    return w * cap_w + (g - off);
+  };
+  // Element i of the staged data (scalars after the vectors), if it reaches `sel`.
+  auto staged_key = [&](int i, uint64_t* out) -> bool {
+    const int nst = tot * VEC;
+    uint32_t key;
+    if (i < nst) key = E::key_of_bits(vec_bits<BF16>(svec_all[slot_of(i / VEC)], i % VEC));
+    else key = S.skey[i - nst];
+    *out = key;
+    return key >= sel;
+  };
+  staged_layout();
+  if (S.overflow) {
+    // The staging space overflowed: far more elements reached the threshold
+    // than the sample predicted.  The staged ones cover about the first
+    // fail_at elements of the row; take the rank among them that scales to
+    // 2.5k over the whole row, and stage the row once more with that key as
+    // the threshold.  (If the row's tail differs, the next attempt overflows
+    // or finds fewer than k, and the row takes the exact fallback.)
+    const int n = tot * VEC + S.nscal;
+    const long long covered = S.fail_at < (uint32_t)V ? (long long)S.fail_at : V;
+    int r2 = (int)((5LL * k * covered + 2 * V - 1) / (2 * V));
+    r2 = r2 < 1 ? 1 : r2;
+    int mine = 0;
+    for (int i = tid; i < n; i += kThreads) {
+      uint64_t key;
+      mine += staged_key(i, &key) ? 1 : 0;
+    }
+    const int have = block_sum<kThreads>(mine, S.scan);
+    if (have >= r2) {
+      const uint32_t t2 = (uint32_t)block_kth_largest<kThreads, E::KEYBITS>(n, r2, staged_key, S.hist, S.sh);
+      if (tid == 0) {
+        S.pool = 0;
+        S.overflow = 0;
+      }
+      sg.scnt = 0;
+      sg.full = false;
       __syncthreads();
-      const uint32_t hi_mask = (shift + 8 >= 32) ? 0u : (~0u << (shift + 8));
-      for_each_staged<BF16>(svec_all, sidx_all, cap_w, S, thr, [&](uint32_t key, uint32_t) {
-        if ((key & hi_mask) == (prefix & hi_mask)) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-      });
-      __syncthreads();
-      if (wid == 0) {
-        int tot = 0;
-        for (int b = lane; b < 256; b += kWave) tot += (int)hist[b];
-        tot = wave_sum(tot);
-        int digit = 0, above = 0;
-        wave_pick_digit(hist, remaining, &digit, &above);
+      stream_vectors(vrow, nvec, tid, [&](const u32x4& v, long long q, bool valid) {
+        uint32_t mk = 0;
 #pragma unroll
-        for (int o = kWave / 2; o > 0; o >>= 1) {
-          digit = max(digit, __shfl_xor(digit, o, kWave));
-          above = max(above, __shfl_xor(above, o, kWave));
-        }
-        if (tid == 0) {
-          S.sh[0] = digit;
-          S.sh[1] = above;
-          if (shift == E::KEYBITS - 8 && tot < k) S.overflow = 1;  // fewer than k reached the guess
-        }
-      }
-      __syncthreads();
-      if (S.overflow) break;
-      prefix |= (uint32_t)S.sh[0] << shift;
-      remaining -= S.sh[1];
-      __syncthreads();
-    }
-    if (!S.overflow) {
-      // gather everything at or above the k-th key (k plus the ties)
-      for_each_staged<BF16>(svec_all, sidx_all, cap_w, S, prefix, [&](uint32_t key, uint32_t idx) {
-        const int slot = atomicAdd(&S.nsurv, 1);
-        if (slot < sort_cap) sortbuf[slot] = ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - idx);
+        for (int e = 0; e < VEC; ++e) mk = max(mk, E::key_of_bits(vec_bits<BF16>(v, e)));
+        sg.stage(valid && mk >= t2, v, (uint32_t)(head + q * VEC), 0u);
       });
-      __syncthreads();
-      if (tid == 0 && S.nsurv > sort_cap) {
-        S.overflow = 1;  // too many ties at the k-th key for the sort buffer
-        S.nsurv = 0;
+      if (lane == 0) {
+        S.cnt[wid] = sg.scnt;
+        if (sg.full) S.overflow = 1;
       }
       __syncthreads();
+      sel = t2;
+      staged_layout();
     }
+  }
+  if (!S.overflow) {
+    // (1) compact the staged elements that reach the threshold into cand[]
+    for (int g0 = 0; g0 < tot; g0 += kThreads) {
+      const int g = g0 + tid;
+      uint32_t hit = 0;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      uint32_t i0 = 0;
+      if (g < tot) {
+        const int sl = slot_of(g);
+        v = svec_all[sl];
+        i0 = sidx_all[sl];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          hit |= (E::key_of_bits(vec_bits<BF16>(v, e)) >= sel ? 1u : 0u) << e;
+      }
+      const int c = __popc(hit);
+      const int incl = wave_inclusive_scan(c);
+      int base = 0;
+      if (lane == kWave - 1) base = atomicAdd(&S.ncand, incl);
+      base = __shfl(base, kWave - 1, kWave);
+      int pos = base + incl - c;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        if ((hit >> e) & 1u) {
+          if (pos < cand_cap) cand[pos] = composite(E::key_of_bits(vec_bits<BF16>(v, e)), i0 + e);
+          ++pos;
+        }
+      }
+    }
+    if (wid == 0) {
+      const bool p = lane < S.nscal && S.skey[lane] >= sel;
+      wave_append(p, p ? composite(S.skey[lane], S.sidx[lane]) : 0ull, cand, cand_cap, &S.ncand);
+    }
+    __syncthreads();
+    const int ncand = S.ncand;
+    if (ncand >= k && ncand <= cand_cap) {
+      // (2) the exact k-th largest key among the candidates
+      auto getc = [&](int i, uint64_t* out) -> bool {
+        *out = cand[i] >> 32;
+        return true;
+      };
+      const uint32_t kth = (uint32_t)block_kth_largest<kThreads, E::KEYBITS>(ncand, k, getc, S.hist, S.sh);
+      // (3) gather the candidates at or above it (k plus the ties)
+      for (int i0 = 0; i0 < ncand; i0 += kThreads) {
+        const int i = i0 + tid;
+        const uint64_t cv = i < ncand ? cand[i] : 0ull;
+        wave_append(i < ncand && (uint32_t)(cv >> 32) >= kth, cv, sortbuf, sort_cap, &S.nsurv);
+      }
+    } else if (ncand > cand_cap) {
+      // Too many candidates for the list: select straight from the staged
+      // vectors.
+      const int nst = tot * VEC;
+      const int n = nst + S.nscal;
+      const uint32_t kth = (uint32_t)block_kth_largest<kThreads, E::KEYBITS>(n, k, staged_key, S.hist, S.sh);
+      sb = cand;  // the staged vectors are still being read: gather into the list instead
+      for (int i0 = 0; i0 < n; i0 += kThreads) {
+        const int i = i0 + tid;
+        uint64_t key = 0;
+        const bool p = i < n && staged_key(i, &key) && (uint32_t)key >= kth;
+        uint32_t idx = 0;
+        if (p) idx = i < nst ? sidx_all[slot_of(i / VEC)] + (uint32_t)(i % VEC) : S.sidx[i - nst];
+        wave_append(p, composite((uint32_t)key, idx), cand, sort_cap, &S.nsurv);
+      }
+    } else if (tid == 0) {
+      S.overflow = 1;  // fewer than k reached the guess
+    }
+    __syncthreads();
+    if (tid == 0 && S.nsurv > sort_cap) {
+      S.overflow = 1;  // too many ties at the k-th key for the sort buffer
+      S.nsurv = 0;
+    }
+    __syncthreads();
   }
   if (S.overflow) {
-    // Exact fallback: radix-select the k-th largest key over the row, then
-    // take every element above it and the lowest-index ties at it.
-    auto getk = [&](int i, uint64_t* out) -> bool {
-      *out = E::key_of_bits(E::bits_at(rowp, i));
-      return true;
-    };
-    const uint32_t kk = (uint32_t)block_kth_largest<kThreads, E::KEYBITS>((int)V, k, getk, hist, S.sh);
-    if (tid == 0) S.nsurv = 0;
-    __syncthreads();
-    for (long long i = tid; i < V; i += kThreads) {
-      const uint32_t key = E::key_of_bits(E::bits_at(rowp, i));
-      if (key > kk) {
-        const int slot = atomicAdd(&S.nsurv, 1);
-        if (slot < sort_cap) sortbuf[slot] = ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
+    // Exact fallback over the row: radix-select the k-th largest key, then
+    // gather every element at or above it.
+    sb = sortbuf;
+    const uint32_t kk = row_kth_largest<BF16>(vrow, nvec, k, S);
+    stream_vectors(vrow, nvec, tid, [&](const u32x4& v, long long q, bool valid) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const uint32_t key = E::key_of_bits(vec_bits<BF16>(v, e));
+        wave_append(valid && key >= kk, composite(key, (uint32_t)(head + q * VEC + e)), sortbuf, sort_cap,
+                    &S.nsurv);
       }
+    });
+    if (wid == 0) {
+      const bool p = lane < S.nscal && S.skey[lane] >= kk;
+      wave_append(p, p ? composite(S.skey[lane], S.sidx[lane]) : 0ull, sortbuf, sort_cap, &S.nsurv);
     }
     __syncthreads();
-    const int taken = S.nsurv;  // elements strictly above the k-th key: fewer than k
-    const int need = k - taken;
-    int ties_before = 0;
-    for (long long b0 = 0; b0 < V && ties_before < need; b0 += kThreads) {
-      const long long i = b0 + tid;
-      const bool tie = i < V && E::key_of_bits(E::bits_at(rowp, i)) == kk;
-      int tot;
-      const int r = ties_before + block_exclusive_scan<kThreads>(tie ? 1 : 0, S.scan, &tot);
-      if (tie && r < need && taken + r < sort_cap)
-        sortbuf[taken + r] = ((uint64_t)kk << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
-      ties_before += tot;
+    const int nall = S.nsurv;
+    __syncthreads();
+    if (nall > sort_cap) {
+      // So many ties at the k-th key that they do not fit: keep the elements
+      // above it and the lowest-index ties.
+      if (tid == 0) S.nsurv = 0;
+      __syncthreads();
+      for (long long b0 = 0; b0 < V; b0 += kThreads) {
+        const long long i = b0 + tid;
+        const uint32_t key = i < V ? E::key_of_bits(E::bits_at(rowp, i)) : 0u;
+        wave_append(i < V && key > kk, composite(key, (uint32_t)i), sortbuf, sort_cap, &S.nsurv);
+      }
+      __syncthreads();
+      const int taken = S.nsurv;  // fewer than k
+      const int need = k - taken;
+      int ties_before = 0;
+      for (long long b0 = 0; b0 < V && ties_before < need; b0 += kThreads) {
+        const long long i = b0 + tid;
+        const bool tie = i < V && E::key_of_bits(E::bits_at(rowp, i)) == kk;
+        int tot;
+        const int rr = ties_before + block_exclusive_scan<kThreads>(tie ? 1 : 0, S.scan, &tot);
+        if (tie && rr < need && taken + rr < sort_cap) sortbuf[taken + rr] = composite(kk, (uint32_t)i);
+        ties_before += tot;
+      }
+      if (tid == 0) S.nsurv = k;
     }
-    if (tid == 0) S.nsurv = k;
     __syncthreads();
   }
+
   // sort the survivors (descending composite = key descending, token ascending)
   const int ns = S.nsurv;
   const int P = next_pow2(ns < k ? k : ns);
-  for (int i = ns + tid; i < P; i += kThreads) sortbuf[i] = 0ull;
+  if (P <= 2 * kThreads) {
+    uint64_t a0 = 2 * tid < ns ? sb[2 * tid] : 0ull;
+    uint64_t a1 = 2 * tid + 1 < ns ? sb[2 * tid + 1] : 0ull;
+    __syncthreads();
+    block_sort_pairs<kThreads>(a0, a1, sb);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int j = 2 * kThreads - 1 - (2 * tid + e);
+      if (j < k) {
+        const uint64_t c = e ? a1 : a0;
+        const uint32_t key = (uint32_t)(c >> 32);
+        const uint32_t idx = 0xFFFFFFFFu - (uint32_t)c;
+        const float x = E::val_of_key(key);
+        const long long o = row * k + j;
+        topk_id[o] = (int32_t)idx;
+        topk_raw[o] = x;
+        if (topk_logp) topk_logp[o] = (float)((double)x - lse);
+      }
+    }
+    return;
+  }
+  for (int i = ns + tid; i < P; i += kThreads) sb[i] = 0ull;
   __syncthreads();
-  block_bitonic_sort<kThreads>(sortbuf, P);
+  block_bitonic_sort<kThreads>(sb, P);
   for (int j = tid; j < k; j += kThreads) {
-    const uint64_t c = sortbuf[P - 1 - j];
+    const uint64_t c = sb[P - 1 - j];
     const uint32_t key = (uint32_t)(c >> 32);
     const uint32_t idx = 0xFFFFFFFFu - (uint32_t)c;
     const float x = E::val_of_key(key);
@@ -496,19 +768,44 @@ __global__ void __launch_bounds__(kThreads, 4) lsm_topk_kernel(const typename El
   }
 }
 
-// Staging area per wave: 1.5x the expected survivor vectors of one wave, plus
-// one full round of slack.
-int wave_cap(int k) {
-  int c = (kOversample * k * 3) / (2 * kWaves) + kWave;
-  return (c + 63) / 64 * 64;
-}
+// Capacities of one row's LDS areas.
+struct LsmCaps {
+  int cap_w;     // staged vectors per wave area
+  int pool;      // staged vectors in the shared pool
+  int sort_cap;  // survivors (k plus ties)
+  int cand_cap;  // candidates (staged elements reaching the threshold)
+  size_t lds;    // dynamic LDS bytes
+};
 
-// Sort buffer: k survivors plus room for ties at the k-th key.
-int sort_cap_for(int k) { return 2 * next_pow2(k); }
-
-size_t lsm_lds_bytes(int k) {
-  return (size_t)kWaves * wave_cap(k) * 16 + (size_t)sort_cap_for(k) * 8 + 256 * 4 +
-         (size_t)kWaves * wave_cap(k) * 4 + 64;
+LsmCaps lsm_caps(long long V, int k, bool bf16) {
+  const int vec = bf16 ? 8 : 4;
+  LsmCaps c;
+  c.sort_cap = 2 * next_pow2(k) > 2 * kThreads ? 2 * next_pow2(k) : 2 * kThreads;
+  c.cand_cap = 4 * next_pow2(k) > c.sort_cap ? 4 * next_pow2(k) : c.sort_cap;
+  // expected staged vectors: about one per element at or above the threshold;
+  // a row that fits in the sample is staged whole
+  const long long n0 = (2 * kStep * vec < V ? 2 * kStep * vec : V);
+  const double expect = (double)V / (double)(n0 > 0 ? n0 : 1) * sample_rank(V, n0 > 0 ? n0 : 1, k) * 1.1 + 32.0;
+  long long e = (long long)expect;
+  if (V <= 2 * kStep * vec && V / vec + 2 > e) e = V / vec + 2;
+  long long cap_w = (e / kWaves + 15) / 16 * 16;       // a quarter each
+  long long total = (e * 27 / 20 + 64 + 63) / 64 * 64;  // 1.35x in all
+  // the sort buffer lives in the staged-vector area once staging is over
+  const long long need = ((long long)c.sort_cap * 8 + 15) / 16;
+  if (total < need) total = need;
+  if (total < kWaves * cap_w + 64) total = kWaves * cap_w + 64;
+  // keep the workgroup within the LDS budget (more rows then take the exact
+  // fallback, results are unchanged)
+  const size_t fixed = sizeof(Shared) + (size_t)c.cand_cap * 8;
+  const long long max_slots = (long long)((kMaxLds - fixed) / 20);
+  if (total > max_slots) {
+    total = max_slots < need ? need : max_slots;
+    cap_w = (total / 2 / kWaves) / 16 * 16;
+  }
+  c.cap_w = (int)cap_w;
+  c.pool = (int)(total - kWaves * cap_w);
+  c.lds = (size_t)total * 20 + (size_t)c.cand_cap * 8;
+  return c;
 }
 
 }  // namespace
@@ -517,23 +814,21 @@ hipError_t launch_logsoftmax_topk(const void* logits, bool bf16, int rows, int r
                                   double* lse, int32_t* topk_id, float* topk_raw, float* topk_logp,
                                   int32_t* status, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  const int cap = wave_cap(k);
-  const int scap = sort_cap_for(k);
-  const size_t lds = lsm_lds_bytes(k);
+  const LsmCaps c = lsm_caps(V, k, bf16);
   if (bf16) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lsm_topk_kernel<true>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)c.lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(lsm_topk_kernel<true>, dim3(rows), dim3(kThreads), lds, stream,
-                       static_cast<const uint16_t*>(logits), V, k, cap, scap, rows_per_tree, lse, topk_id, topk_raw,
-                       topk_logp, status);
+    hipLaunchKernelGGL(lsm_topk_kernel<true>, dim3(rows), dim3(kThreads), c.lds, stream,
+                       static_cast<const uint16_t*>(logits), V, k, c.cap_w, c.pool, c.sort_cap, c.cand_cap,
+                       rows_per_tree, lse, topk_id, topk_raw, topk_logp, status);
   } else {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lsm_topk_kernel<false>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)c.lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(lsm_topk_kernel<false>, dim3(rows), dim3(kThreads), lds, stream,
-                       static_cast<const float*>(logits), V, k, cap, scap, rows_per_tree, lse, topk_id, topk_raw,
-                       topk_logp, status);
+    hipLaunchKernelGGL(lsm_topk_kernel<false>, dim3(rows), dim3(kThreads), c.lds, stream,
+                       static_cast<const float*>(logits), V, k, c.cap_w, c.pool, c.sort_cap, c.cand_cap,
+                       rows_per_tree, lse, topk_id, topk_raw, topk_logp, status);
   }
   return hipGetLastError();
 }

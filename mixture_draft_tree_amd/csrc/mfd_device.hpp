@@ -120,6 +120,52 @@ __device__ __forceinline__ void block_bitonic_sort(uint64_t* a, int n) {
   }
 }
 
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const int lo = __shfl_xor((int)(uint32_t)v, m, kWave);
+  const int hi = __shfl_xor((int)(uint32_t)(v >> 32), m, kWave);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo;
+}
+
+// Sorts the 2*NT values held two per thread (thread t holds elements 2t and
+// 2t+1 in a0, a1) ascending, with the same bitonic network as
+// block_bitonic_sort.  Strides inside a wave go through lane shuffles; only the
+// strides that cross waves go through `xchg` (2*NT uint64 of LDS), two
+// barriers each.  Every thread of the block must call it.
+template <int NT>
+__device__ __forceinline__ void block_sort_pairs(uint64_t& a0, uint64_t& a1, uint64_t* xchg) {
+  constexpr int P = 2 * NT;
+  const int i0 = 2 * (int)threadIdx.x;
+#pragma unroll
+  for (int size = 2; size <= P; size <<= 1) {
+#pragma unroll
+    for (int s = size >> 1; s > 0; s >>= 1) {
+      const bool up = (i0 & size) == 0;
+      if (s == 1) {
+        const uint64_t lo = a0 < a1 ? a0 : a1, hi = a0 < a1 ? a1 : a0;
+        a0 = up ? lo : hi;
+        a1 = up ? hi : lo;
+        continue;
+      }
+      uint64_t b0, b1;
+      if (s < 2 * kWave) {
+        b0 = shfl_xor_u64(a0, s >> 1);
+        b1 = shfl_xor_u64(a1, s >> 1);
+      } else {
+        xchg[i0] = a0;
+        xchg[i0 + 1] = a1;
+        __syncthreads();
+        b0 = xchg[i0 ^ s];
+        b1 = xchg[(i0 + 1) ^ s];
+        __syncthreads();
+      }
+      // for s >= 2 both elements share the lower/upper role and the direction
+      const bool keep_min = ((i0 & s) == 0) == up;
+      a0 = keep_min ? (a0 < b0 ? a0 : b0) : (a0 < b0 ? b0 : a0);
+      a1 = keep_min ? (a1 < b1 ? a1 : b1) : (a1 < b1 ? b1 : a1);
+    }
+  }
+}
+
 __host__ __device__ __forceinline__ int next_pow2(int x) {
   int p = 1;
   while (p < x) p <<= 1;

@@ -6,6 +6,7 @@ excluded from node-set exactness); log-normalisers within 1e-5, scores within
 1e-4."""
 
 import sys
+import zlib
 
 import numpy as np
 import pytest
@@ -64,6 +65,16 @@ LSM_CASES = [
     ("bf16_ascending", 1, 1, 2, 20000, 256, torch.bfloat16, "ascending"),
     ("bf16_k1024", 1, 2, 1, 248320, 1024, torch.bfloat16, "normal"),
     ("bf16_signed_zero", 1, 1, 1, 1000, 200, torch.bfloat16, "zeros"),
+    # full-vocabulary rows: the sampled-threshold path and each of its exits
+    ("bf16_vocab", 1, 2, 3, 151936, 256, torch.bfloat16, "normal"),
+    ("f32_vocab", 1, 1, 2, 151936, 256, torch.float32, "normal"),
+    ("bf16_vocab_clustered", 1, 1, 2, 151936, 256, torch.bfloat16, "clustered"),
+    ("bf16_vocab_late_mass", 1, 1, 2, 151936, 256, torch.bfloat16, "late"),
+    ("bf16_vocab_early_mass", 1, 1, 2, 151936, 256, torch.bfloat16, "early"),
+    ("bf16_vocab_shifted_block", 1, 1, 2, 151936, 256, torch.bfloat16, "shifted"),
+    # the row maximum lies far from the sample maximum: the sum is redone
+    ("bf16_vocab_spike", 1, 1, 2, 151936, 256, torch.bfloat16, "spike"),
+    ("f32_deep_after_neginf", 1, 1, 2, 20000, 64, torch.float32, "deep"),
 ]
 
 
@@ -82,6 +93,29 @@ def _make(kind, shape, dtype, seed):
         x = torch.full(shape, -float("inf"))
     elif kind == "ascending":
         x = torch.linspace(-8, 8, shape[-1]).expand(shape).clone()
+    elif kind == "clustered":
+        # more elements above the sampled threshold than the candidate list holds
+        x = torch.randn(shape, generator=g)
+        x[..., 60000:61600] = 10 + 0.5 * torch.randn(shape[:-1] + (1600,), generator=g)
+    elif kind == "late":
+        # the sample chunk sits far below the rest: staging overflows
+        x = torch.randn(shape, generator=g) * 3
+        x[..., :20000] -= 30
+    elif kind == "early":
+        # the sample chunk sits far above the rest: fewer than k reach the threshold
+        x = torch.randn(shape, generator=g) * 3
+        x[..., :8192] += 30
+    elif kind == "shifted":
+        # a block after the sample sits higher: staging overflows, and the row
+        # is staged again with a threshold taken from what was staged
+        x = torch.randn(shape, generator=g) * 3
+        x[..., 30000:40000] += 5
+    elif kind == "spike":
+        x = torch.randn(shape, generator=g)
+        x[..., 100000] = 200.0
+    elif kind == "deep":
+        x = torch.randn(shape, generator=g) - 300
+        x[..., :9000] = -float("inf")
     elif kind == "zeros":
         x = torch.zeros(shape)
         x[..., ::3] = -0.0
@@ -93,7 +127,7 @@ def _make(kind, shape, dtype, seed):
 def test_logsoftmax_topk_parity(case):
     name, N, K, L, V, k, dt, kind = case
     say(f"[lsm] {name} N={N} K={K} L={L} V={V} k={k}")
-    x = _make(kind, (N, K, L, V), dt, seed=hash(name) % 1000)
+    x = _make(kind, (N, K, L, V), dt, seed=zlib.crc32(name.encode()) % 1000)
     lse, tid, raw, lp, st = _lsm_run(x, k)
     err = check_lsm(x, lse, tid, raw, k, lp)
     assert st.cpu().eq(0).all()
