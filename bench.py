@@ -14,6 +14,7 @@ timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import statistics
@@ -24,6 +25,40 @@ import torch
 
 METRIC = "mixture trees built+verified/sec (K=8,L=15,B=256,V=152K); logits HBM GB/s"
 HBM_PEAK_GBS = 8000.0
+HERE = os.path.dirname(os.path.abspath(__file__))
+# Sources of the logits kernel: a traffic figure measured on other sources is stale.
+LSM_SOURCES = ["mixture_draft_tree_amd/csrc/lsm_topk.hip", "mixture_draft_tree_amd/csrc/mfd_device.hpp",
+               "mixture_draft_tree_amd/csrc/mfd_launch.hpp"]
+TRAFFIC_FILE = "profiles/lsm_topk_kernel_batched_64x8x15x151936_hbm_traffic.txt"
+
+
+def lsm_source_sha() -> str:
+    h = hashlib.sha256()
+    for rel in LSM_SOURCES:
+        with open(os.path.join(HERE, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the logits kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None if there is
+    none for this workload or the kernel sources changed since it was taken."""
+    path = os.path.join(HERE, TRAFFIC_FILE)
+    if workload != "batched" or not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith((" ", "#", "$")):
+                key, val = line.split(":", 1)
+                fields[key.strip()] = val.strip()
+    if fields.get("kernel_source_sha256") != lsm_source_sha():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def parse():
@@ -35,6 +70,11 @@ def parse():
     ap.add_argument("--cpu-baseline-trees", type=int, default=2,
                     help="trees of the workload the fp64 oracle is timed on (0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-gib", type=int, default=0,
+                    help="after the run, copy a buffer of this many GiB device to device: a plain copy of "
+                         "known size against which hardware byte counters are calibrated (0 = skip)")
+    ap.add_argument("--latency-steps", type=int, default=20,
+                    help="steps of the single-tree workload timed for per-tree latency (0 = skip)")
     return ap.parse_args()
 
 
@@ -71,43 +111,17 @@ def cpu_baseline(name: str, base_seed: int, n_trees: int):
                       f"{dt:.1f} s on one host core"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); trees are independent, "
-              f"so N GPUs would each run this same per-GPU batch.", file=sys.stderr)
-        sys.exit(2)
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    from mixture_draft_tree_amd import synth
-    from mixture_draft_tree_amd.pipeline import MixtureTreePath
-
-    name = args.workload
-    w = synth.WORKLOADS[name]
-    dev = "cuda"
-    b = synth.draft_batch(name, base_seed=args.seed, device=dev)
-    N = b.logits.shape[0]
-    P = MixtureTreePath(N, w.K, w.L, w.V, w.B)
-    logits = b.logits.contiguous()
-    anchor, pos = b.anchor.to(dev), b.pos_base.to(dev)
-    temps, seeds = b.temperature.to(dev), b.seed.to(dev)
-    # the target's per-node rows depend on the tree they verify: build once
-    P.build(logits, anchor, pos)
-    torch.cuda.synchronize()
-    R = synth.target_logits(b, P.buf.depth, P.buf.n_nodes, device=dev, base_seed=args.seed).contiguous()
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream()
-    names = ["logsoftmax_topk", "mixture_threshold", "tree_build", "tree_mask", "verify_walk"]
-    for _ in range(args.warmup):
+def run_steps(P, logits, anchor, pos, R, temps, seeds, steps, warmup, stream):
+    """Times `steps` whole steps; returns (total ms, per-stage ms lists)."""
+    for _ in range(warmup):
         P.step(logits, anchor, pos, R, temps, seeds)
     torch.cuda.synchronize()
-
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
-    for s in range(args.steps):
+    for s in range(steps):
         e = ev[s]
         e[0].record(stream)
         P.logsoftmax_topk(logits)
@@ -122,7 +136,47 @@ def main():
         e[5].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
+    return t_start.elapsed_time(t_end), ev
+
+
+def setup(name, seed, dev):
+    from mixture_draft_tree_amd import synth
+    from mixture_draft_tree_amd.pipeline import MixtureTreePath
+
+    w = synth.WORKLOADS[name]
+    b = synth.draft_batch(name, base_seed=seed, device=dev)
+    N = b.logits.shape[0]
+    P = MixtureTreePath(N, w.K, w.L, w.V, w.B)
+    logits = b.logits.contiguous()
+    anchor, pos = b.anchor.to(dev), b.pos_base.to(dev)
+    temps, seeds = b.temperature.to(dev), b.seed.to(dev)
+    # the target's per-node rows depend on the tree they verify: build once
+    P.build(logits, anchor, pos)
+    torch.cuda.synchronize()
+    R = synth.target_logits(b, P.buf.depth, P.buf.n_nodes, device=dev, base_seed=seed).contiguous()
+    torch.cuda.synchronize()
+    return w, N, P, logits, anchor, pos, temps, seeds, R
+
+
+def single_tree_latency(seed, steps, stream):
+    """Mean time of one whole step on the single-tree workload (N=1), ms."""
+    w, N, P, logits, anchor, pos, temps, seeds, R = setup("single", seed, "cuda")
+    total, _ = run_steps(P, logits, anchor, pos, R, temps, seeds, steps, 3, stream)
+    return total / steps
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); trees are independent, "
+              f"so N GPUs would each run this same per-GPU batch.", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    name = args.workload
+    stream = torch.cuda.current_stream()
+    w, N, P, logits, anchor, pos, temps, seeds, R = setup(name, args.seed, "cuda")
+    names = ["logsoftmax_topk", "mixture_threshold", "tree_build", "tree_mask", "verify_walk"]
+    total_ms, ev = run_steps(P, logits, anchor, pos, R, temps, seeds, args.steps, args.warmup, stream)
     ms_per_step = total_ms / args.steps
     stage = {nm: [ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)] for i, nm in enumerate(names)}
     stage_ms = {nm: statistics.mean(v) for nm, v in stage.items()}
@@ -151,16 +205,25 @@ def main():
                    "trees": N, "K": w.K, "L": w.L, "V": w.V, "B": w.B},
         "roofline": {"bound": "hbm", "kernel": "lsm_topk_kernel (mfd_logsoftmax_topk)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(name),
                      "algorithmic_bytes_per_launch": logits_bytes, "avg_launch_ms": lsm_ms},
         "stages_ms": stage_ms,
         "logits_GBps": achieved,
         "per_tree_latency_ms": ms_per_step if N == 1 else None,
+        "single_tree_latency_ms": None,
         "tau_mean": float(tau.mean()),
     }
+    if args.latency_steps > 0 and name != "single":
+        out["single_tree_latency_ms"] = single_tree_latency(args.seed, args.latency_steps, stream)
     if args.cpu_baseline_trees > 0:
         out["cpu_baseline"] = cpu_baseline(name, args.seed, args.cpu_baseline_trees)
     print(json.dumps(out), flush=True)
+    if args.copy_gib > 0:
+        src = torch.ones(args.copy_gib << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
 
 
 if __name__ == "__main__":
