@@ -173,7 +173,7 @@ struct Stager {
     }
     int base = 0;
     if (lane_id() == 0) base = atomicAdd(pool_used, n);
-    base = __shfl(base, 0, kWave);
+    base = __builtin_amdgcn_readfirstlane(base);
     if (base + n > pool_cap) {
       if (lane_id() == 0) atomicMin(fail_at, ibase);
       full = true;
@@ -269,12 +269,13 @@ __device__ __forceinline__ void stream_vectors(const u32x4* vrow, long long nvec
 }
 
 // Appends the composites of the lanes with `p` to buf[*counter ...] (entries
-// past `cap` are counted but not written).  Wave-level; one LDS atomic per wave.
+// past `cap` are counted but not written).  Wave-level, whole wave active; one
+// LDS atomic per wave.
 __device__ __forceinline__ void wave_append(bool p, uint64_t c, uint64_t* buf, int cap, int* counter) {
   const uint64_t m = __ballot(p);
   int base = 0;
   if (lane_id() == 0 && m) base = atomicAdd(counter, __popcll(m));
-  base = __shfl(base, 0, kWave);
+  base = __builtin_amdgcn_readfirstlane(base);
   const int pos = base + __popcll(m & lanemask_lt());
   if (p && pos < cap) buf[pos] = c;
 }
@@ -651,11 +652,32 @@ __global__ void __launch_bounds__(kThreads, 5) lsm_topk_kernel(const typename El
         return true;
       };
       const uint32_t kth = (uint32_t)block_kth_largest<kThreads, E::KEYBITS>(ncand, k, getc, S.hist, S.sh);
-      // (3) gather the candidates at or above it (k plus the ties)
+      // (3) gather the candidates above the k-th key (fewer than k), then
+      // those at it
       for (int i0 = 0; i0 < ncand; i0 += kThreads) {
         const int i = i0 + tid;
         const uint64_t cv = i < ncand ? cand[i] : 0ull;
-        wave_append(i < ncand && (uint32_t)(cv >> 32) >= kth, cv, sortbuf, sort_cap, &S.nsurv);
+        wave_append(i < ncand && (uint32_t)(cv >> 32) > kth, cv, sortbuf, sort_cap, &S.nsurv);
+      }
+      __syncthreads();
+      const int nabove = S.nsurv;
+      for (int i0 = 0; i0 < ncand; i0 += kThreads) {
+        const int i = i0 + tid;
+        const uint64_t cv = i < ncand ? cand[i] : 0ull;
+        wave_append(i < ncand && (uint32_t)(cv >> 32) == kth, cv, sortbuf, sort_cap, &S.nsurv);
+      }
+      __syncthreads();
+      // (4) keep only the k - nabove lowest-index ties when there are a few
+      // more (one wave sorts them; at equal keys the composite orders by index)
+      const int nties = S.nsurv - nabove, need = k - nabove;
+      if (nties > need && nties <= kWave) {
+        if (wid == 0) {
+          uint64_t tv = lane < nties ? sortbuf[nabove + lane] : 0ull;
+          tv = wave_sort_desc(tv);
+          if (lane < need) sortbuf[nabove + lane] = tv;
+          if (lane == 0) S.nsurv = k;
+        }
+        __syncthreads();
       }
     } else if (ncand > cand_cap) {
       // Too many candidates for the list: select straight from the staged
@@ -732,6 +754,22 @@ __global__ void __launch_bounds__(kThreads, 5) lsm_topk_kernel(const typename El
   // sort the survivors (descending composite = key descending, token ascending)
   const int ns = S.nsurv;
   const int P = next_pow2(ns < k ? k : ns);
+  if (P <= kThreads) {
+    uint64_t a0 = tid < ns ? sb[tid] : 0ull;
+    __syncthreads();
+    block_sort_single<kThreads>(a0, sb);
+    const int j = kThreads - 1 - tid;
+    if (j < k) {
+      const uint32_t key = (uint32_t)(a0 >> 32);
+      const uint32_t idx = 0xFFFFFFFFu - (uint32_t)a0;
+      const float x = E::val_of_key(key);
+      const long long o = row * k + j;
+      topk_id[o] = (int32_t)idx;
+      topk_raw[o] = x;
+      if (topk_logp) topk_logp[o] = (float)((double)x - lse);
+    }
+    return;
+  }
   if (P <= 2 * kThreads) {
     uint64_t a0 = 2 * tid < ns ? sb[2 * tid] : 0ull;
     uint64_t a1 = 2 * tid + 1 < ns ? sb[2 * tid + 1] : 0ull;

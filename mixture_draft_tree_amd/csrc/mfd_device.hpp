@@ -166,6 +166,48 @@ __device__ __forceinline__ void block_sort_pairs(uint64_t& a0, uint64_t& a1, uin
   }
 }
 
+// Sorts the NT values held one per thread (thread t holds element t) ascending
+// with the bitonic network; strides inside a wave use lane shuffles, strides
+// across waves go through `xchg` (NT uint64 of LDS, two barriers each).  Every
+// thread of the block must call it.
+template <int NT>
+__device__ __forceinline__ void block_sort_single(uint64_t& a, uint64_t* xchg) {
+  const int t = (int)threadIdx.x;
+#pragma unroll
+  for (int size = 2; size <= NT; size <<= 1) {
+#pragma unroll
+    for (int s = size >> 1; s > 0; s >>= 1) {
+      uint64_t b;
+      if (s < kWave) {
+        b = shfl_xor_u64(a, s);
+      } else {
+        xchg[t] = a;
+        __syncthreads();
+        b = xchg[t ^ s];
+        __syncthreads();
+      }
+      const bool keep_min = ((t & s) == 0) == ((t & size) == 0);
+      a = keep_min ? (a < b ? a : b) : (a < b ? b : a);
+    }
+  }
+}
+
+// Sorts the 64 values held one per lane of a wave descending (lane 0 gets the
+// largest).  Wave-level, no barrier.
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t a) {
+  const int t = lane_id();
+#pragma unroll
+  for (int size = 2; size <= kWave; size <<= 1) {
+#pragma unroll
+    for (int s = size >> 1; s > 0; s >>= 1) {
+      const uint64_t b = shfl_xor_u64(a, s);
+      const bool keep_max = ((t & s) == 0) == ((t & size) == 0);
+      a = keep_max ? (a < b ? b : a) : (a < b ? a : b);
+    }
+  }
+  return a;
+}
+
 __host__ __device__ __forceinline__ int next_pow2(int x) {
   int p = 1;
   while (p < x) p <<= 1;

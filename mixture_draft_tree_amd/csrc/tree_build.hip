@@ -129,6 +129,7 @@ struct Ctl {
   int scan[kNT / kWave];
   uint32_t hist[256];
   int kept[32];
+  int fcount[kNT / kWave];
 };
 
 __device__ __forceinline__ Tree tree_ptrs(const TreeArgs& a, int n) {
@@ -170,6 +171,100 @@ __device__ __forceinline__ int count_children(const float* vals, int k, double r
   return lo;
 }
 
+// count_children by one wave: the condition holds on a prefix of the row
+// (ranks are in descending order and the score is monotone in the logit), so
+// the count is the number of positions where it holds; all loads of a block
+// of 4 * 64 positions are issued together.
+__device__ __forceinline__ int wave_count_children(const float* vals, int k, double raw, double norm, double tau) {
+  const int lane = lane_id();
+  int total = 0;
+  for (int b = 0; b < k; b += 4 * kWave) {
+    float x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = b + u * kWave + lane;
+      x[u] = j < k ? vals[j] : -INFINITY;
+    }
+    int cnt = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool ok = (x[u] != -INFINITY) && ((raw + (double)x[u]) - norm >= tau);
+      cnt += __popcll(__ballot(ok));
+    }
+    total += cnt;
+    const int valid = k - b < 4 * kWave ? k - b : 4 * kWave;
+    if (cnt < valid) break;
+  }
+  return total;
+}
+
+// A lower bound of the rank-th largest of the doubles score(i), i in [0, n),
+// for which use(i) holds (the caller guarantees at least `rank` of them):
+// the rank-th largest of their ordered keys with the low 48 bits cleared,
+// which is at or below every key it stands for.  Two radix passes.
+template <typename Score, typename Use>
+__device__ __forceinline__ double kth_lower_bound(int n, int rank, Score score, Use use, Ctl& ctl) {
+  auto get = [&](int i, uint64_t* key) -> bool {
+    if (!use(i)) return false;
+    *key = f64_key(score(i)) >> 48;
+    return true;
+  };
+  const uint64_t kb = block_kth_largest<kNT, 16>(n, rank, get, ctl.hist, ctl.sh);
+  return f64_from_key(kb << 48);
+}
+
+// The exact rank-th largest (rank >= 1, at most n) of the doubles score(i),
+// i in [0, n).  The 16-bit lower bound first fixes the bucket of keys that
+// holds the answer; the members of that bucket (listed in `buf`, capacity
+// `cap`) then rank themselves by direct comparison.  Falls back to the full
+// 64-bit radix select if the bucket does not fit.  Barriers inside.
+template <typename Score>
+__device__ double exact_kth(int n, int rank, Score score, Ctl& ctl, uint64_t* buf, int cap) {
+  const int tid = threadIdx.x;
+  const double lb = kth_lower_bound(n, rank, score, [](int) { return true; }, ctl);
+  const uint64_t b16 = f64_key(lb) >> 48;
+  if (tid == 0) {
+    ctl.sh[4] = 0;  // members of the bucket
+    ctl.sh[5] = 0;  // keys above the bucket
+  }
+  __syncthreads();
+  int above = 0;
+  for (int i = tid; i < n; i += kNT) {
+    const uint64_t key = f64_key(score(i));
+    if ((key >> 48) > b16) ++above;
+    else if ((key >> 48) == b16) {
+      const int slot = atomicAdd(&ctl.sh[4], 1);
+      if (slot < cap) buf[slot] = key;
+    }
+  }
+  above = block_sum<kNT>(above, ctl.scan);
+  const int nb = ctl.sh[4];
+  const int need = rank - above;  // 1 <= need <= nb
+  if (nb > cap) {
+    auto get = [&](int i, uint64_t* key) -> bool {
+      *key = f64_key(score(i));
+      return true;
+    };
+    return f64_from_key(block_kth_largest<kNT, 64>(n, rank, get, ctl.hist, ctl.sh));
+  }
+  // the member with fewer than `need` members above it and at least `need`
+  // at or above it holds the answer
+  for (int q = tid; q < nb; q += kNT) {
+    const uint64_t mine = buf[q];
+    int gt = 0, ge = 0;
+    for (int r = 0; r < nb; ++r) {
+      const uint64_t o = buf[r];
+      gt += o > mine ? 1 : 0;
+      ge += o >= mine ? 1 : 0;
+    }
+    if (gt < need && need <= ge) ctl.sh[6] = (int)(uint32_t)(mine >> 32), ctl.sh[7] = (int)(uint32_t)mine;
+  }
+  __syncthreads();
+  const uint64_t ans = ((uint64_t)(uint32_t)ctl.sh[6] << 32) | (uint64_t)(uint32_t)ctl.sh[7];
+  __syncthreads();
+  return f64_from_key(ans);
+}
+
 // Chunked exclusive scan of `val(i)` for i in [0, n) writing out[i]; returns the total.
 template <typename Val, typename Out>
 __device__ int block_scan_range(int n, Val val, Out out, int* scan_smem) {
@@ -208,9 +303,25 @@ __device__ void level_search(const TreeArgs& a, const Tree& t, int n, Ctl& ctl, 
       const float* vals = a.topk_raw + ((size_t)(n * K + m) * L + (d - 1)) * k;
       return count_children(vals, k, t.ent_raw[e], norm[m * Lp1 + d], th);
     };
-    int C = block_scan_range(
-        fsize, [&](int f) { return count_at(f, tau); }, [&](int f, int off, int) { t.fr_off[f] = off; },
-        ctl.scan);
+    int C;
+    if (fsize <= kNT / kWave) {
+      // a few entries (the first level): one wave per entry
+      const int w = tid / kWave;
+      if (w < fsize) {
+        const int e = t.fr[w];
+        const int m = t.ent_mode[e];
+        const float* vals = a.topk_raw + ((size_t)(n * K + m) * L + (d - 1)) * k;
+        const int cnt = wave_count_children(vals, k, t.ent_raw[e], norm[m * Lp1 + d], tau);
+        if (lane_id() == 0) ctl.fcount[w] = cnt;
+      }
+      __syncthreads();
+      C = block_scan_range(
+          fsize, [&](int f) { return ctl.fcount[f]; }, [&](int f, int off, int) { t.fr_off[f] = off; }, ctl.scan);
+    } else {
+      C = block_scan_range(
+          fsize, [&](int f) { return count_at(f, tau); }, [&](int f, int off, int) { t.fr_off[f] = off; },
+          ctl.scan);
+    }
 
     const bool too_big = (C > a.sort_cap) || (ctl.ent_count + C > a.ent_cap) || (ctl.node_count + C > a.node_cap);
     if (!BUILD && too_big) {
@@ -327,15 +438,12 @@ __device__ void level_search(const TreeArgs& a, const Tree& t, int n, Ctl& ctl, 
       for (int i = 1 + tid; i < ctl.node_count; i += kNT) local += (t.node_S[i] >= tau) ? 1 : 0;
       const int alive = block_sum<kNT>(local, ctl.scan);
       if (alive >= B && B > 0) {
+        // any lower bound of the B-th best node score is a valid threshold;
+        // a 16-bit one takes two radix passes instead of eight
         const double tcur = tau;
-        auto get = [&](int i, uint64_t* key) -> bool {
-          const double s = t.node_S[i + 1];
-          if (!(s >= tcur)) return false;
-          *key = f64_key(s);
-          return true;
-        };
-        const uint64_t kb = block_kth_largest<kNT, 64>(ctl.node_count - 1, B, get, ctl.hist, ctl.sh);
-        const double nt = f64_from_key(kb);
+        const double nt = kth_lower_bound(
+            ctl.node_count - 1, B, [&](int i) { return t.node_S[i + 1]; },
+            [&](int i) { return t.node_S[i + 1] >= tcur; }, ctl);
         if (nt > tau) tau = nt;
         if (tid == 0) ctl.tau = tau;
       }
@@ -371,12 +479,18 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
   Ctl& ctl = *reinterpret_cast<Ctl*>(norm + K * Lp1);
   const Tree t = tree_ptrs(a, n);
 
-  // norm[m][d] = sum_{i<d} lse[m][i], fp64, from i = 0 upward
+  // norm[m][d] = sum_{i<d} lse[m][i], fp64, from i = 0 upward (all K*L
+  // values loaded at once, then one running sum per mode)
+  for (int q = tid; q < K * L; q += kNT) {
+    const int m = q / L, i = q - m * L;
+    norm[m * Lp1 + i + 1] = a.lse[(size_t)n * K * L + q];
+  }
+  __syncthreads();
   for (int m = tid; m < K; m += kNT) {
     double acc = 0.0;
     norm[m * Lp1] = 0.0;
     for (int i = 0; i < L; ++i) {
-      acc = acc + a.lse[(size_t)(n * K + m) * L + i];
+      acc = acc + norm[m * Lp1 + i + 1];
       norm[m * Lp1 + i + 1] = acc;
     }
   }
@@ -443,21 +557,8 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
     int nsel = 0;
     double cut = INFINITY;
     if (!fail && B > 0 && total > 0) {
-      if (total >= B) {
-        nsel = B;
-        auto get = [&](int i, uint64_t* key) -> bool {
-          *key = f64_key(t.node_S[i + 1]);
-          return true;
-        };
-        cut = f64_from_key(block_kth_largest<kNT, 64>(total, B, get, ctl.hist, ctl.sh));
-      } else {
-        nsel = total;
-        auto get = [&](int i, uint64_t* key) -> bool {
-          *key = f64_key(t.node_S[i + 1]);
-          return true;
-        };
-        cut = f64_from_key(block_kth_largest<kNT, 64>(total, total, get, ctl.hist, ctl.sh));
-      }
+      nsel = total >= B ? B : total;
+      cut = exact_kth(total, nsel, [&](int i) { return t.node_S[i + 1]; }, ctl, keys, a.sort_cap);
     }
     if (fail) cut = NAN;
     if (a.per_mode_kept) {
@@ -479,11 +580,7 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
   int nsel = fail ? 0 : (nsel_in < M ? nsel_in : M);
   // node_aux: 1 = selected, then the canonical row index
   if (M > nsel && nsel > 0) {
-    auto get = [&](int i, uint64_t* key) -> bool {
-      *key = f64_key(t.node_S[i + 1]);
-      return true;
-    };
-    const double cstar = f64_from_key(block_kth_largest<kNT, 64>(M, nsel, get, ctl.hist, ctl.sh));
+    const double cstar = exact_kth(M, nsel, [&](int i) { return t.node_S[i + 1]; }, ctl, keys, a.sort_cap);
     int lgt = 0;
     for (int i = 1 + tid; i < nc; i += kNT) lgt += (t.node_S[i] > cstar) ? 1 : 0;
     const int gt = block_sum<kNT>(lgt, ctl.scan);
@@ -564,13 +661,25 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
           },
           ctl.scan);
       if (cnt == 0) break;
-      const int P = next_pow2(cnt);
-      for (int c = cnt + tid; c < P; c += kNT) keys[c] = ~0ull;
-      __syncthreads();
-      block_bitonic_sort<kNT>(keys, P);
+      // position of each key in (parent row, token) order: by direct counting
+      // for up to 2048 keys (all distinct: the low bits hold the node), else
+      // by a bitonic sort
+      const bool small = cnt <= 2 * kNT;
+      if (!small) {
+        const int P = next_pow2(cnt);
+        for (int c = cnt + tid; c < P; c += kNT) keys[c] = ~0ull;
+        __syncthreads();
+        block_bitonic_sort<kNT>(keys, P);
+      }
       for (int i = tid; i < cnt; i += kNT) {
+        int pos = i;
+        if (small) {
+          const uint64_t mine = keys[i];
+          pos = 0;
+          for (int r = 0; r < cnt; ++r) pos += keys[r] < mine ? 1 : 0;
+        }
         const int node = s0 + (int)(keys[i] & 0xFFFFu);
-        const int rowi = base + i;
+        const int rowi = base + pos;
         const int p = t.node_parent[node];
         const int prow = (p == 0) ? 0 : (t.node_aux[p] - 2);
         const size_t o = (size_t)n * Bp1 + rowi;
