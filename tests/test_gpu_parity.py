@@ -261,6 +261,46 @@ def test_walk_parity_small():
                        ot[n].cpu().numpy(), pn[n].cpu().numpy())
 
 
+def test_walk_near_tie_exact():
+    """Two tokens whose perturbed values differ by 3e-5 (built from the oracle's
+    own noise): too close for the fp32 noise estimate, so the kernel must take
+    the exact fp64 round, and must agree with the oracle on the winner."""
+    V, Bp1, L = 20000, 8, 3
+    temps = [1.0, 1.0, 0.5, 2.0]
+    seeds = [101, 2 ** 63 + 3, 77, 5]
+    deltas = [3e-5, -3e-5, 3e-5, -3e-5]
+    trees, Rs = [], []
+    for T, sd, dl in zip(temps, seeds, deltas):
+        g = O.gumbel_noise(sd, 0, V)
+        R = np.full((Bp1, V), -1000.0)
+        a, b = 100, V - 50
+        R[0, a] = T * (20.0 - g[a])
+        R[0, b] = T * (20.0 - g[b] + dl)
+        Rs.append(R)
+        tr = {"node_token": np.full(Bp1, -1, dtype=np.int64), "parent": np.full(Bp1, -1, dtype=np.int64),
+              "depth": np.full(Bp1, -1, dtype=np.int64), "n_nodes": 1}
+        tr["node_token"][0] = 7
+        tr["depth"][0] = 0
+        trees.append(tr)
+    Rt = torch.tensor(np.stack(Rs), dtype=torch.float32)
+    R64 = Rt.double().numpy()
+    tok, par, dep, nn = upload_tree(trees, Bp1)
+    N = len(trees)
+    tt = torch.tensor(temps, dtype=torch.float32, device="cuda")
+    sd_t = torch.tensor([s if s < 2 ** 63 else s - 2 ** 64 for s in seeds], dtype=torch.int64, device="cuda")
+    tau = torch.empty(N, dtype=torch.int32, device="cuda")
+    ot = torch.empty((N, L + 1), dtype=torch.int32, device="cuda")
+    pn = torch.empty((N, L + 1), dtype=torch.int32, device="cuda")
+    st = torch.zeros(N, dtype=torch.int32, device="cuda")
+    M.mfd_verify_walk(Rt.cuda(), L, tok, par, dep, nn, tt, sd_t, tau, ot, pn, st, ws=M.walk_workspace(N))
+    torch.cuda.synchronize()
+    assert st.eq(0).all()
+    for n in range(N):
+        assert check_walk(trees[n], R64[n], temps[n], seeds[n], L, tau[n].item(), ot[n].cpu().numpy(),
+                          pn[n].cpu().numpy())
+        assert int(ot[n, 0].item()) == (V - 50 if deltas[n] > 0 else 100)
+
+
 def test_walk_bad_temperature():
     x = _small_tree_case(31, 2, 3, 16, 8)
     P = MixtureTreePath(2, 2, 3, 16, 8)
