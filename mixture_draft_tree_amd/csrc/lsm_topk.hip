@@ -45,6 +45,9 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kUnroll = 4;
 constexpr long long kStep = (long long)kThreads * kUnroll;
+// Chunks at the head of the row that form the sample (2 or 3; all three chunk
+// buffers are in flight before the sample is taken).
+constexpr int kSampleChunks = 2;
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr double kLn2 = 0.693147180559945309417232121458;
 // LDS one workgroup may use (of 160 KB per CU), static part included.
@@ -102,11 +105,15 @@ __device__ __forceinline__ float term(float x, float bias) {
 
 // Rank of the sample threshold among the lanes' sample maxima.  The number of
 // row elements at or above the r-th largest of n0 sampled ones is about
-// (V / n0) * Gamma(r); r is the smallest value whose mean minus 4.5 standard
-// deviations still reaches k.  Host and device use the same formula.
+// (V / n0) * Gamma(r); r is the smallest value whose mean minus 3 standard
+// deviations still reaches k.  (The r-th largest lane maximum lies at or below
+// the r-th largest sampled element, so the true margin is wider.)  A row that
+// still ends up with fewer than k takes the exact fallback, which costs a few
+// more passes over that row only; a wider margin would stage more elements on
+// every row.  Host and device use the same formula.
 __host__ __device__ __forceinline__ int sample_rank(long long V, long long n0, int k) {
   const double a = (double)k * (double)n0 / (double)V;
-  const double sr = 0.5 * (4.5 + sqrt(20.25 + 4.0 * a));
+  const double sr = 0.5 * (3.0 + sqrt(9.0 + 4.0 * a));
   long long r = (long long)ceil(sr * sr);
   if (r < 1) r = 1;
   if (r > kThreads) r = kThreads;
@@ -422,14 +429,16 @@ __global__ void __launch_bounds__(kThreads, 5) lsm_topk_kernel(const typename El
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const long long q = (long long)u * kThreads + tid;
-      float ma = vec_val<BF16>(bufA[u], 0), mb = vec_val<BF16>(bufB[u], 0);
+      float ma = vec_val<BF16>(bufA[u], 0), mb = vec_val<BF16>(bufB[u], 0), mc = vec_val<BF16>(bufC[u], 0);
 #pragma unroll
       for (int j = 1; j < VEC; ++j) {
         ma = fmaxf(ma, vec_val<BF16>(bufA[u], j));
         mb = fmaxf(mb, vec_val<BF16>(bufB[u], j));
+        if (kSampleChunks > 2) mc = fmaxf(mc, vec_val<BF16>(bufC[u], j));
       }
       lmax = fmaxf(lmax, q < nvec ? ma : -INFINITY);
       lmax = fmaxf(lmax, q + kStep < nvec ? mb : -INFINITY);
+      if (kSampleChunks > 2) lmax = fmaxf(lmax, q + 2 * kStep < nvec ? mc : -INFINITY);
     }
   }
   S.hist[tid] = E::key_of_float(lmax);
@@ -439,7 +448,7 @@ __global__ void __launch_bounds__(kThreads, 5) lsm_topk_kernel(const typename El
   // Threshold: the r-th largest lane maximum, so at least r sampled elements
   // reach it.  Every wave runs the same bitwise search over all 256 keys (four
   // ballots per bit), so all agree without another barrier.
-  const long long n0 = (2 * kStep <= nvec ? 2 * kStep : nvec) * VEC + nscalar;
+  const long long n0 = (kSampleChunks * kStep <= nvec ? kSampleChunks * kStep : nvec) * VEC + nscalar;
   const int r = sample_rank(V, n0, k);
   uint32_t thr = 0;
 #pragma unroll 1
@@ -822,10 +831,10 @@ LsmCaps lsm_caps(long long V, int k, bool bf16) {
   c.cand_cap = 4 * next_pow2(k) > c.sort_cap ? 4 * next_pow2(k) : c.sort_cap;
   // expected staged vectors: about one per element at or above the threshold;
   // a row that fits in the sample is staged whole
-  const long long n0 = (2 * kStep * vec < V ? 2 * kStep * vec : V);
+  const long long n0 = (kSampleChunks * kStep * vec < V ? kSampleChunks * kStep * vec : V);
   const double expect = (double)V / (double)(n0 > 0 ? n0 : 1) * sample_rank(V, n0 > 0 ? n0 : 1, k) * 1.1 + 32.0;
   long long e = (long long)expect;
-  if (V <= 2 * kStep * vec && V / vec + 2 > e) e = V / vec + 2;
+  if (V <= kSampleChunks * kStep * vec && V / vec + 2 > e) e = V / vec + 2;
   long long cap_w = (e / kWaves + 15) / 16 * 16;       // a quarter each
   long long total = (e * 27 / 20 + 64 + 63) / 64 * 64;  // 1.35x in all
   // the sort buffer lives in the staged-vector area once staging is over
