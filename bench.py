@@ -199,7 +199,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded; drafter logits N(0,9) + per-mode futures at +8, target rows N(0,1) + 10 on one future)",
+        "data": "synthetic (seeded; confident drafter: N(0,4) noise, 16 Zipf alternatives, each mode's future at 16+N(0,2.25); target rows N(0,1) + 16 on one future up to a random deviation depth)",
         "config": {"workload": f"{name}: {N} trees, K={w.K}, L={w.L}, V={w.V}, B={w.B}, "
                                f"T pattern {list(w.temperatures)}",
                    "trees": N, "K": w.K, "L": w.L, "V": w.V, "B": w.B},

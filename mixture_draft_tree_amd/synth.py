@@ -10,6 +10,12 @@ none of that is used here. What is kept from the pages is the shape of the
 problem: a block of 16 slots with 15 drafted positions (MFD-Qwen3.5-4B model
 card, "Model"), K = 8 modes and a budget of B = 256 (same card, "Results"), and
 modes that each draft one coherent future (project page, "How it works", step 2).
+The mixture workloads model a trained, confident drafter: each mode's future
+token takes most of its row's mass (log-probability about -0.1 to -1.3), a few
+alternatives sit far below it, and the target follows the chosen future for a
+random number of tokens, so trees reach the full depth of 15 and acceptance
+lengths land near the pages' figures (tau of 6 to 11 at B = 256, project page,
+Table 1; about 10.7 for MFD on Qwen3.5-4B at T = 0, model card, "Results").
 
 Five named workloads:
 
@@ -47,14 +53,21 @@ class Workload:
     boost: float          # added to each mode's future tokens
     target_boost: float   # added to the chosen future in the target rows
     temperatures: tuple   # per-tree temperature pattern (cycled)
+    jitter: float = 0.0   # std of a per-(mode, position) offset of the future token's boost
+    alt_n: int = 0        # per (mode, position) row: alternative tokens given a Zipf bump ...
+    alt_height: float = 0.0  # ... of alt_height * r^-1.1, r = 1..alt_n
+    dev_lo: int = 0       # target leaves the chosen future at a depth D ~ U{dev_lo..L} (0: never)
 
 
 WORKLOADS = {
     "tiny": Workload("tiny", 1, 2, 4, 16, 8, 1, torch.float32, 2.0, 4.0, 5.0, (0.0,)),
     "product": Workload("product", 2, 1, 15, 32000, 64, 1, torch.bfloat16, 2.0, 0.0, 10.0, (0.0,)),
-    "single": Workload("single", 3, 8, 15, 151936, 256, 1, torch.bfloat16, 3.0, 8.0, 10.0, (0.0, 1.0)),
-    "batched": Workload("batched", 4, 8, 15, 151936, 256, 64, torch.bfloat16, 3.0, 8.0, 10.0, (0.0, 1.0)),
-    "stress": Workload("stress", 5, 16, 15, 248320, 1024, 1, torch.bfloat16, 3.0, 8.0, 10.0, (1.0,)),
+    "single": Workload("single", 3, 8, 15, 151936, 256, 1, torch.bfloat16, 2.0, 16.0, 16.0, (0.0, 1.0),
+                       jitter=1.5, alt_n=16, alt_height=10.0, dev_lo=3),
+    "batched": Workload("batched", 4, 8, 15, 151936, 256, 64, torch.bfloat16, 2.0, 16.0, 16.0, (0.0, 1.0),
+                        jitter=1.5, alt_n=16, alt_height=10.0, dev_lo=3),
+    "stress": Workload("stress", 5, 16, 15, 248320, 1024, 1, torch.bfloat16, 2.0, 16.0, 16.0, (1.0,),
+                       jitter=1.5, alt_n=16, alt_height=10.0, dev_lo=3),
 }
 
 
@@ -172,12 +185,24 @@ def _mode_futures(w, g, device):
 
 
 def _mixture_tree(w, g, device, ties: bool):
+    """A confident drafter: per (mode, position) row, N(0, sigma^2) noise, a
+    Zipf bump on `alt_n` alternative tokens, and the mode's future token set
+    to boost + N(0, jitter^2), which puts most of the row's mass on it."""
     K, L, V = w.K, w.L, w.V
     x = torch.randn((K, L, V), generator=g, device=device, dtype=torch.float32) * w.sigma
+    if w.alt_n > 0:
+        r = torch.arange(1, w.alt_n + 1, device=device, dtype=torch.float32)
+        bump = w.alt_height * r.pow(-1.1)
+        alt = torch.randint(0, V, (K, L, w.alt_n), generator=g, device=device)
+        x.scatter_add_(2, alt, bump.expand(K, L, w.alt_n).contiguous())
     fut = _mode_futures(w, g, device)
     ar = torch.arange(L, device=device)
     for k in range(K):
-        x[k, ar, fut[k]] += w.boost
+        if w.jitter > 0:
+            jit = torch.randn((L,), generator=g, device=device, dtype=torch.float32) * w.jitter
+            x[k, ar, fut[k]] = w.boost + jit
+        else:
+            x[k, ar, fut[k]] += w.boost
     if ties:
         # In 10% of (mode, position) rows a second token gets the bit-identical
         # (after bf16 rounding) value of the boosted future token.
@@ -226,8 +251,10 @@ def target_logits(batch: DraftBatch, depth: torch.Tensor, n_nodes: torch.Tensor,
 
     Rows are N(0,1).  The target follows one future F (the chosen mode's): every
     tree node at depth d < L gets `target_boost` on F[d], so from the root the
-    target's preferred continuation is F token by token.  `depth` / `n_nodes`
-    describe the tree the rows belong to (node i of tree n has depth depth[n, i]).
+    target's preferred continuation is F token by token.  With `dev_lo` > 0 the
+    target leaves F at a depth D ~ U{dev_lo..L}: from depth D on the boost goes
+    to another token G[d] != F[d] instead.  `depth` / `n_nodes` describe the tree
+    the rows belong to (node i of tree n has depth depth[n, i]).
     """
     w = batch.workload
     N = batch.logits.shape[0]
@@ -238,7 +265,11 @@ def target_logits(batch: DraftBatch, depth: torch.Tensor, n_nodes: torch.Tensor,
     for n in range(N):
         g = _gen(device, tree_seed(w.wid + 100, n, base_seed))
         r = torch.randn((Bp1, w.V), generator=g, device=device, dtype=torch.float32)
-        F = batch.futures[n, int(batch.chosen_mode[n])].to(device)
+        F = batch.futures[n, int(batch.chosen_mode[n])].to(device).clone()
+        if w.dev_lo > 0:
+            D = w.dev_lo + int(_randint(g, w.L - w.dev_lo + 1, (1,), device).item())
+            for q in range(D, w.L):
+                F[q] = _distinct_other(g, int(F[q]), w.V, device)
         nn_ = int(n_nodes[n])
         d = depth[n, :nn_].to(torch.int64)
         rows = torch.nonzero(d < w.L).flatten()
