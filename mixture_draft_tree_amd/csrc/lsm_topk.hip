@@ -194,10 +194,14 @@ struct Stager {
 };
 
 // One vector: returns the sum of its terms (pairwise, fp32) and stages the
-// vector if that sum reaches tau.  With tau = 0.999 * term(threshold) this
-// keeps every vector holding an element at or above the threshold: such an
-// element's term is at least term(threshold) up to an ulp or two of exp2,
-// and the other terms are not negative.  (NaN terms stage nothing.)
+// vector if one of its two half sums (the last two partial sums of the
+// pairwise tree) reaches tau.  With tau = 0.999 * term(threshold) this keeps
+// every vector holding an element at or above the threshold: such an
+// element's term is at least term(threshold) up to an ulp or two of exp2, and
+// the other terms of its half are not negative.  Testing the halves rather
+// than the whole sum stages far fewer vectors whose elements all lie below
+// the threshold (several medium terms that add up), for one v_max.  (NaN
+// terms stage nothing from their half.)
 template <bool BF16, bool FULL>
 __device__ __forceinline__ float consume_vector(const u32x4& v, uint32_t ibase, uint32_t ioff, bool valid, float bias,
                                                 float tau, Stager& sg) {
@@ -206,12 +210,12 @@ __device__ __forceinline__ float consume_vector(const u32x4& v, uint32_t ibase, 
 #pragma unroll
   for (int j = 0; j < VEC; ++j) e[j] = (FULL || valid) ? term(vec_val<BF16>(v, j), bias) : 0.f;
 #pragma unroll
-  for (int w = VEC / 2; w > 0; w >>= 1) {
+  for (int w = VEC / 2; w > 1; w >>= 1) {
 #pragma unroll
     for (int j = 0; j < w; ++j) e[j] += e[j + w];
   }
-  sg.stage((FULL || valid) && e[0] >= tau, v, ibase, ioff);
-  return e[0];
+  sg.stage((FULL || valid) && fmaxf(e[0], e[1]) >= tau, v, ibase, ioff);
+  return e[0] + e[1];
 }
 
 // Loads chunk c (four 16-byte vectors per lane).  Byte offsets are 32-bit
@@ -829,14 +833,15 @@ LsmCaps lsm_caps(long long V, int k, bool bf16) {
   LsmCaps c;
   c.sort_cap = 2 * next_pow2(k) > 2 * kThreads ? 2 * next_pow2(k) : 2 * kThreads;
   c.cand_cap = 4 * next_pow2(k) > c.sort_cap ? 4 * next_pow2(k) : c.sort_cap;
-  // expected staged vectors: about one per element at or above the threshold;
-  // a row that fits in the sample is staged whole
+  // expected staged vectors: about one per element at or above the threshold,
+  // plus a quarter for vectors staged on a half sum of medium terms (rows of
+  // low spread); a row that fits in the sample is staged whole
   const long long n0 = (kSampleChunks * kStep * vec < V ? kSampleChunks * kStep * vec : V);
-  const double expect = (double)V / (double)(n0 > 0 ? n0 : 1) * sample_rank(V, n0 > 0 ? n0 : 1, k) * 1.1 + 32.0;
+  const double expect = (double)V / (double)(n0 > 0 ? n0 : 1) * sample_rank(V, n0 > 0 ? n0 : 1, k) * 1.25 + 32.0;
   long long e = (long long)expect;
   if (V <= kSampleChunks * kStep * vec && V / vec + 2 > e) e = V / vec + 2;
-  long long cap_w = (e / kWaves + 15) / 16 * 16;       // a quarter each
-  long long total = (e * 27 / 20 + 64 + 63) / 64 * 64;  // 1.35x in all
+  long long cap_w = (e * 11 / 10 / kWaves + 15) / 16 * 16;  // a quarter each, 10% over
+  long long total = (e * 8 / 5 + 63) / 64 * 64;               // 1.6x in all
   // the sort buffer lives in the staged-vector area once staging is over
   const long long need = ((long long)c.sort_cap * 8 + 15) / 16;
   if (total < need) total = need;
