@@ -214,13 +214,15 @@ mfd_status mfd_tree_mask(const int32_t* parent, const int32_t* depth, const int3
  *             bonus token; -1 after.
  *   path_nodes device [N, L+1] int32 out: rows visited, root first; -1 after.
  *   status    device [N] int32 or NULL: MFD_TREE_BAD_TEMPERATURE; MFD_TREE_CAPACITY
- *             if the workgroups sharing a tree stopped waiting for each other
- *             (a bounded wait that should never run out; tau is then 0).
+ *             if the call gave up waiting for work to finish (a bounded wait,
+ *             seconds long, that never runs out in a correct run; tau is then 0).
  *   ws        device workspace, 8-byte aligned, of at least
- *             mfd_workspace_size(MFD_OP_VERIFY_WALK) bytes (partial maxima and
- *             per-tree arrival counters; cleared by the call itself).
- * The rows of one tree are split over several workgroups of one cooperative
- * launch; the call fails with MFD_ERR_DEVICE if the device cannot launch it.
+ *             mfd_workspace_size(MFD_OP_VERIFY_WALK) bytes (per-tree control
+ *             blocks, per-round counters and slice results; set up by the call
+ *             itself, so it needs no clearing).
+ * Each visited row is cut into slices that any of the launch's workgroups may
+ * take, so the device's resident workgroups share the open rows of all trees;
+ * calls on one stream are ordered, calls that overlap must not share `ws`.
  */
 mfd_status mfd_verify_walk(const void* target_logits, mfd_dtype dtype, int N, int Bp1, int V, int L,
                            const int32_t* node_token, const int32_t* parent, const int32_t* depth,

@@ -10,14 +10,19 @@
 // is counter-based (Philox4x64-10) and keyed by (seed, depth, token), so a
 // given seed samples the same tokens whatever the tree's shape.
 //
-// Work layout: each tree gets C workgroups (C from the device's occupancy, up
-// to 32) in one cooperative launch, so a visited row of V tokens is split C
-// ways across the chip.  Per round every workgroup reduces its slice, publishes
-// the result (double-buffered by round parity) and waits on the tree's arrival
-// counter; then all C workgroups read the C results at once (one lane each),
-// agree on the same token and child, and move on together.  Waits are
-// bounded; a wait that runs out flags the tree and ends its walk, so every
-// wave exits.  Only the rows on the walked path are read.
+// Work layout: the token chosen at a node depends only on that node's row,
+// T, the seed and its depth, so the only order the walk imposes is one row
+// after the other within a tree.  Every row is cut into S slices, and a round
+// is one row (or its exact re-evaluation, below) of one tree.  The launch's
+// workgroups, all resident at once (cooperative launch), form G groups of S:
+// tree n belongs to group n mod G, and workgroup s of a group always reduces
+// slice s of its trees' rows.  A workgroup serves every tree of its group, in
+// whatever order their rounds open, so one waiting tree does not idle it.
+// After its slice a workgroup publishes a top-two and counts itself in; the
+// one that completes the round merges the S results, finds the child (tree
+// nodes sit in LDS) and opens the tree's next round with one packed word, or
+// ends the tree.  Waits are polls of those words, bounded; a workgroup leaves
+// once all its trees have ended.  Only the rows on the walked path are read.
 //
 // At T > 0 the noise is first estimated in fp32 (two v_log_f32, error below
 // kGumbelTol, see gumbel_estimate) and y = x / T + g is formed in fp64 from
@@ -37,14 +42,15 @@ namespace {
 
 constexpr int kWalkThreads = 256;
 constexpr int kWalkWaves = kWalkThreads / kWave;
-constexpr int kMaxC = 32;
-constexpr long long kSpinLimit = 1LL << 21;  // bounded wait (~0.5 us sleeps), far beyond any real step
-constexpr int kPollSleep = 8;                // s_sleep units (64 clocks each) between polls
-constexpr int kCounterStride = 32;           // ints: one 128-byte line per tree's arrival counter
+constexpr int kSlices = 64;                  // slices per row, at most
+constexpr int kMaxRounds = 2 * (32 + 1);     // two rounds per depth, L <= 32
+constexpr int kMaxServed = kWave;            // trees one workgroup serves, at most
+constexpr long long kIdleLimit = 1LL << 22;  // polls without work before giving up (seconds; never in practice)
+constexpr int kPollSleep = 2;                // s_sleep units (64 clocks each) between polls
 constexpr double kGumbelTol = 1e-4;
 constexpr float kLn2f = 0.693147180559945309f;
-constexpr int kSliceVec = 8;
-constexpr int kMaxNodesLds = 4096;  // tree nodes staged in LDS for the child lookup
+constexpr int kSliceVec = 2;                 // 16-byte vectors per thread per round of loads
+constexpr int kNodesLds = 2048;              // node (parent, token) pairs of the served trees kept in LDS
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -108,11 +114,19 @@ __device__ __forceinline__ Top2 top2_shfl_xor(const Top2& t, int o) {
   return r;
 }
 
+// Per-tree round word: 0 = no round open, kEnded = the tree has ended, else
+// (round + 1) | kind << 7 | step << 8 | node << 14, where kind 1 marks an
+// exact re-evaluation of the row (its cut-off is in `cut`) and step is the
+// number of moves from the root (the output position of the round's token).
+constexpr uint32_t kEnded = 0xFFFFFFFFu;
+__host__ __device__ __forceinline__ uint32_t round_word(int r, int kind, int step, int u) {
+  return (uint32_t)(r + 1) | ((uint32_t)kind << 7) | ((uint32_t)step << 8) | ((uint32_t)u << 14);
+}
+
 struct WalkArgs {
   const void* target;
-  int Bp1;
+  int N, Bp1, L, S, G;
   long long V;
-  int L;
   const int32_t* node_token;
   const int32_t* parent;
   const int32_t* depth;
@@ -123,18 +137,41 @@ struct WalkArgs {
   int32_t* out_tokens;
   int32_t* path_nodes;
   int32_t* status;
-  int C;
-  double* part_y1;  // [trees][2][C]
-  double* part_y2;  // [trees][2][C]
-  int32_t* part_i;  // [trees][2][C]
-  int32_t* arrive;  // [trees][kCounterStride], element 0 used
+  uint32_t* word;  // [N] round words
+  double* cut;     // [N] cut-off of an exact round
+  int32_t* done;   // [N][kMaxRounds] slices finished per round
+  double* py1;     // [N][kSlices] slice results of the open round
+  double* py2;
+  int32_t* pi;
 };
+
+// Ordering between workgroups.  Everything one workgroup hands to another
+// (slice results, cut-offs, counters, round words) is written and read with
+// agent-scope atomic stores, loads and RMWs, which act at the device's
+// coherence point, and a value is published only after the atomic stores
+// before it have completed (`drain`).  Plain data the kernel reads (rows,
+// nodes) is never written by it, so no acquire or release -- and none of the
+// L2 writeback and invalidation they cost on this device -- is needed.
+__device__ __forceinline__ void drain() { __builtin_amdgcn_s_waitcnt(0); }
+
+template <typename T>
+__device__ __forceinline__ T ld(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ void st(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 struct WalkShared {
   Top2 w[kWalkWaves];
-  Top2 g;  // the tree's result of the round
+  Top2 g;  // merged result of a round
   int child;
-  int timeout;
+  int j, quit, last;
+  uint32_t word;
+  double cut;
+  int seen[kMaxServed];   // last round this workgroup reduced, per served tree
+  int node0[kMaxServed];  // first LDS slot of the tree's nodes, -1 if not in LDS
 };
 
 // Element value as float (bf16 or fp32 storage).
@@ -145,8 +182,7 @@ __device__ __forceinline__ float elem_at(const void* row, long long i) {
 
 // Calls f(i, x) for every element i of [e0, e1): scalars before and after the
 // 16-byte aligned part, then the aligned vectors kSliceVec per thread at a
-// time (all loads of a round issued before any is used; one round covers a
-// slice of up to kSliceVec * 256 vectors).
+// time (all loads of a round issued before any is used).
 template <bool BF16, typename F>
 __device__ __forceinline__ void for_slice(const void* row, long long e0, long long e1, F f) {
   constexpr int VEC = BF16 ? 8 : 4;
@@ -159,6 +195,7 @@ __device__ __forceinline__ void for_slice(const void* row, long long e0, long lo
   const long long b = a + nv * VEC;
   for (long long i = e0 + tid; i < a; i += kWalkThreads) f(i, elem_at<BF16>(row, i));
   for (long long i = b + tid; i < e1; i += kWalkThreads) f(i, elem_at<BF16>(row, i));
+  if (nv <= 0) return;
   const u32x4* vp = reinterpret_cast<const u32x4*>(static_cast<const char*>(row) + a * ESZ);
   for (long long q0 = 0; q0 < nv; q0 += kSliceVec * kWalkThreads) {
     u32x4 v[kSliceVec];
@@ -184,6 +221,21 @@ __device__ __forceinline__ void for_slice(const void* row, long long e0, long lo
   }
 }
 
+// Element range [e0, e1) of slice s of S of a row: the row's aligned vectors
+// are split evenly; slice 0 also takes the unaligned head, slice S-1 the tail.
+template <bool BF16>
+__device__ __forceinline__ void slice_range(const void* row, long long V, int S, int s, long long& e0,
+                                            long long& e1) {
+  constexpr int VEC = BF16 ? 8 : 4;
+  constexpr int ESZ = BF16 ? 2 : 4;
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(row) & 15u;
+  long long a = mis ? (long long)((16u - mis) / ESZ) : 0;
+  if (a > V) a = V;
+  const long long nv = (V - a) / VEC;
+  e0 = s == 0 ? 0 : a + (nv * s / S) * VEC;
+  e1 = s == S - 1 ? V : a + (nv * (s + 1) / S) * VEC;
+}
+
 // Philox block of element i (four words per counter), cached across calls.
 struct NoiseCache {
   long long blk = -1;
@@ -198,7 +250,7 @@ struct NoiseCache {
   }
 };
 
-// Block-wide Top2 of the per-thread values (barrier inside); every thread gets it.
+// Block-wide Top2 of the per-thread values (barriers inside); every thread gets it.
 __device__ __forceinline__ Top2 block_top2(Top2 t, WalkShared& sh) {
 #pragma unroll
   for (int o = kWave / 2; o > 0; o >>= 1) top2_merge(t, top2_shfl_xor(t, o));
@@ -206,196 +258,264 @@ __device__ __forceinline__ Top2 block_top2(Top2 t, WalkShared& sh) {
   __syncthreads();
   Top2 r = sh.w[0];
   for (int w = 1; w < kWalkWaves; ++w) top2_merge(r, sh.w[w]);
+  __syncthreads();  // sh.w may be reused
   return r;
+}
+
+// Opens round 0 (the root) of every tree with a valid temperature and ends
+// the others; clears the per-round counters.
+__global__ void walk_init_kernel(WalkArgs a) {
+  const int N = a.N, Lp1 = a.L + 1;
+  const int i0 = blockIdx.x * blockDim.x + threadIdx.x, stride = gridDim.x * blockDim.x;
+  for (int i = i0; i < N * kMaxRounds; i += stride) a.done[i] = 0;
+  for (int n = i0; n < N; n += stride) {
+    const float T = a.temperature[n];
+    a.cut[n] = 0.0;
+    if (!(T >= 0.f) || isinf(T)) {
+      for (int i = 0; i < Lp1; ++i) {
+        a.out_tokens[(size_t)n * Lp1 + i] = -1;
+        a.path_nodes[(size_t)n * Lp1 + i] = -1;
+      }
+      a.tau[n] = 0;
+      if (a.status) atomicOr(&a.status[n], MFD_TREE_BAD_TEMPERATURE);
+      a.word[n] = kEnded;
+    } else {
+      a.word[n] = round_word(0, 0, 0, 0);
+    }
+  }
 }
 
 template <bool BF16>
 __global__ void __launch_bounds__(kWalkThreads, 4) verify_walk_kernel(WalkArgs a) {
   __shared__ WalkShared sh;
-  // dynamic LDS: the tree's parents, then its tokens (min(B + 1, kMaxNodesLds) each)
-  extern __shared__ int32_t node_lds[];
-  const int C = a.C;
-  const int n = blockIdx.x / C;
-  const int c = blockIdx.x - n * C;
-  const int tid = threadIdx.x;
-  const int L = a.L, Lp1 = L + 1, Bp1 = a.Bp1;
+  __shared__ int32_t lpar[kNodesLds];
+  __shared__ int32_t ltok[kNodesLds];
+  const int tid = threadIdx.x, lane = lane_id(), wid = wave_id();
+  const int N = a.N, S = a.S, G = a.G, L = a.L, Lp1 = L + 1, Bp1 = a.Bp1;
   const long long V = a.V;
-  const float Tf = a.temperature[n];
-  const size_t tb = (size_t)n * Bp1;
-  int32_t* ot = a.out_tokens + (size_t)n * Lp1;
-  int32_t* pn = a.path_nodes + (size_t)n * Lp1;
-  if (!(Tf >= 0.f) || isinf(Tf)) {
-    if (c == 0) {
-      for (int i = tid; i < Lp1; i += kWalkThreads) {
-        ot[i] = -1;
-        pn[i] = -1;
-      }
-      if (tid == 0) {
-        a.tau[n] = 0;
-        if (a.status) atomicOr(&a.status[n], MFD_TREE_BAD_TEMPERATURE);
-      }
-    }
-    return;
-  }
-  const double T = (double)Tf;
-  const double invT = T > 0.0 ? 1.0 / T : 0.0;
-  const uint64_t sd = a.seed[n];
-  int nn = a.n_nodes[n];
-  nn = nn < 1 ? 1 : (nn > Bp1 ? Bp1 : nn);
-  const char* tbase = static_cast<const char*>(a.target);
   const size_t esz = BF16 ? 2 : 4;
-  const long long e0 = (V * c) / C, e1 = (V * (c + 1)) / C;  // this workgroup's slice
-  double* py1 = a.part_y1 + (size_t)n * 2 * C;
-  double* py2 = a.part_y2 + (size_t)n * 2 * C;
-  int32_t* pi = a.part_i + (size_t)n * 2 * C;
-  int32_t* ctr = a.arrive + (size_t)n * kCounterStride;  // this tree's arrival counter
-  // the tree's parents and tokens, for the child lookup of every step
-  const int ncap = Bp1 < kMaxNodesLds ? Bp1 : kMaxNodesLds;
-  int32_t* lpar = node_lds;
-  int32_t* ltok = node_lds + ncap;
-  const bool nodes_lds = nn <= ncap;
-  if (nodes_lds) {
-    for (int q = tid; q < nn; q += kWalkThreads) {
-      lpar[q] = a.parent[tb + q];
-      ltok[q] = a.node_token[tb + q];
+  const int grp = blockIdx.x / S, s = blockIdx.x - grp * S;
+  // served trees: n = grp + j * G
+  const int served = grp < N ? (N - 1 - grp) / G + 1 : 0;
+  if (tid < kMaxServed) sh.seen[tid] = 0;
+  if (tid == 0) {
+    int slot = 0;
+    for (int j = 0; j < served; ++j) {
+      const int n = grp + j * G;
+      int nn = a.n_nodes[n];
+      nn = nn < 1 ? 1 : (nn > Bp1 ? Bp1 : nn);
+      sh.node0[j] = slot + nn <= kNodesLds ? slot : -1;
+      if (slot + nn <= kNodesLds) slot += nn;
     }
   }
-  int round = 0;
+  __syncthreads();
+  for (int j = 0; j < served; ++j) {
+    const int o = sh.node0[j];
+    if (o < 0) continue;
+    const int n = grp + j * G;
+    int nn = a.n_nodes[n];
+    nn = nn < 1 ? 1 : (nn > Bp1 ? Bp1 : nn);
+    for (int q = tid; q < nn; q += kWalkThreads) {
+      lpar[o + q] = a.parent[(size_t)n * Bp1 + q];
+      ltok[o + q] = a.node_token[(size_t)n * Bp1 + q];
+    }
+  }
+  long long idle = 0;
+  int backoff = 1;
 
-  // One exchange round: publish this workgroup's Top2, wait for the tree's
-  // other workgroups (bounded), read all C results (lane q reads workgroup
-  // q's) and merge them in the same order everywhere.  Result in sh.g.
-  auto exchange = [&](const Top2& mine) {
-    const int slot = (round & 1) * C;
-    if (wave_id() == 0) {
-      const int lane = lane_id();
-      int to = 0;
+  while (true) {
+    __syncthreads();  // everyone is done with the previous iteration's shared fields
+    // ------------------------------------------------ find an open round (wave 0)
+    if (wid == 0) {
+      int quit = 0, pick = -1;
+      uint32_t w = kEnded;
+      if (lane < served) w = ld(&a.word[grp + lane * G]);
+      const bool ended = w == kEnded;
+      const bool ready = !ended && w != 0u && (int)(w & 0x7Fu) > sh.seen[lane < kMaxServed ? lane : 0];
+      const uint64_t rm = __ballot(lane < served && ready);
+      if (rm != 0ull) {
+        pick = __builtin_ctzll(rm);
+        backoff = 1;
+        idle = 0;
+      } else if (__ballot(lane < served && !ended) == 0ull) {
+        quit = 1;  // every served tree has ended
+      } else if (++idle > kIdleLimit) {
+        quit = 2;
+      } else {
+        // back off while nothing is ready (up to ~1 us between polls)
+        backoff = backoff < 16 ? backoff * 2 : 16;
+        for (int z = 0; z < backoff; ++z) __builtin_amdgcn_s_sleep(kPollSleep);
+      }
+      w = __shfl(w, pick < 0 ? 0 : pick, kWave);
       if (lane == 0) {
-        __hip_atomic_store(&py1[slot + c], mine.y1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&py2[slot + c], mine.y2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&pi[slot + c], mine.i1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        const int want = C * (round + 1);
-        long long spins = 0;
-        while (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < want) {
-          if (++spins > kSpinLimit) {
-            to = 1;
-            break;
+        sh.quit = quit;
+        sh.j = pick;
+        sh.word = w;
+        sh.child = 0x7FFFFFFF;
+        if (pick >= 0 && ((w >> 7) & 1u)) sh.cut = ld(&a.cut[grp + pick * G]);
+      }
+    }
+    __syncthreads();
+    const int quit = sh.quit, j = sh.j;
+    if (quit) {
+      if (quit == 2 && tid == 0) {
+        // gave up waiting: flag every served tree that has not ended
+        for (int q = 0; q < served; ++q) {
+          const int n = grp + q * G;
+          if (ld(&a.word[n]) != kEnded) {
+            if (a.status) atomicOr(&a.status[n], MFD_TREE_CAPACITY);
+            a.tau[n] = 0;
           }
-          __builtin_amdgcn_s_sleep(kPollSleep);
         }
       }
-      to = __shfl(to, 0, kWave);
-      // every lane acquires the counter itself (it already reached `want`), so
-      // the results published before the other workgroups' arrivals are visible
-      (void)__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-      Top2 t = {-INFINITY, 0x7FFFFFFF, -INFINITY};
-      if (lane < C) {
-        t.y1 = __hip_atomic_load(&py1[slot + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        t.y2 = __hip_atomic_load(&py2[slot + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        t.i1 = __hip_atomic_load(&pi[slot + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-#pragma unroll
-      for (int o = kWave / 2; o > 0; o >>= 1) top2_merge(t, top2_shfl_xor(t, o));
-      if (lane == 0) {
-        sh.g = t;
-        sh.timeout = to;
-        sh.child = 0x7FFFFFFF;
-      }
+      break;
     }
-    ++round;
-    __syncthreads();
-  };
+    if (j < 0) continue;
+    const uint32_t word = sh.word;
+    const int r = (int)(word & 0x7Fu) - 1, kind = (int)((word >> 7) & 1u), step = (int)((word >> 8) & 0x3Fu),
+              u = (int)(word >> 14);
+    const double cut = sh.cut;
+    const int n = grp + j * G;
+    if (tid == 0) sh.seen[j] = r + 1;
 
-  int u = 0, step = 0;
-  bool timed_out = false;
-  while (true) {
+    // ------------------------------------------------ reduce this workgroup's slice
+    const size_t tb = (size_t)n * Bp1;
+    const double T = (double)a.temperature[n];
+    const double invT = T > 0.0 ? 1.0 / T : 0.0;
+    const uint64_t sd = a.seed[n];
     const int d = a.depth[tb + u];
-    const void* row = tbase + ((tb + u) * (size_t)V) * esz;
+    const void* row = static_cast<const char*>(a.target) + ((tb + u) * (size_t)V) * esz;
+    long long e0, e1;
+    slice_range<BF16>(row, V, S, s, e0, e1);
     Top2 t = {-INFINITY, 0x7FFFFFFF, -INFINITY};
     NoiseCache nc;
     if (T == 0.0) {
       for_slice<BF16>(row, e0, e1, [&](long long i, float x) { top2_add(t, (double)x, (int)i); });
-    } else {
+    } else if (kind == 0) {
       for_slice<BF16>(row, e0, e1, [&](long long i, float x) {
         const float g = gumbel_estimate(nc.word(i, sd, d));
         top2_add(t, (double)x * invT + (double)g, (int)i);
       });
+    } else {
+      // exact fp64 noise for every element whose estimate comes within the
+      // slack of the best estimate
+      for_slice<BF16>(row, e0, e1, [&](long long i, float x) {
+        const uint64_t w = nc.word(i, sd, d);
+        if ((double)x * invT + (double)gumbel_estimate(w) >= cut)
+          top2_add(t, (double)x / T + gumbel_from_word(w), (int)i);
+      });
     }
     const Top2 mine = block_top2(t, sh);
-    exchange(mine);
-    if (sh.timeout) {
-      timed_out = true;
-      break;
+    double* py1 = a.py1 + (size_t)n * kSlices;
+    double* py2 = a.py2 + (size_t)n * kSlices;
+    int32_t* pi = a.pi + (size_t)n * kSlices;
+    int32_t* done = a.done + (size_t)n * kMaxRounds + r;
+    if (tid == 0) {
+      st(&py1[s], mine.y1);
+      st(&py2[s], mine.y2);
+      st(&pi[s], mine.i1);
+      drain();  // the result is in place before the slice counts as done
+      const int old = __hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sh.last = old == S - 1;
     }
-    int tstar = sh.g.i1;
-    // the estimates also carry the rounding of x / T (a few ulp of |y|)
-    const double slack = 2.0 * kGumbelTol + (fabs(sh.g.y1) + fabs(sh.g.y2)) * 0x1.0p-48;
-    if (T != 0.0 && !(sh.g.y1 - sh.g.y2 > slack)) {
-      // too close to call from the estimates: exact fp64 noise for every
-      // element whose estimate comes within the slack of the best
-      const double cut = sh.g.y1 - slack;
-      Top2 ex = {-INFINITY, 0x7FFFFFFF, -INFINITY};
-      NoiseCache nc2;
-      for_slice<BF16>(row, e0, e1, [&](long long i, float x) {
-        const uint64_t w = nc2.word(i, sd, d);
-        if ((double)x * invT + (double)gumbel_estimate(w) >= cut)
-          top2_add(ex, (double)x / T + gumbel_from_word(w), (int)i);
-      });
-      __syncthreads();  // sh.w is reused
-      const Top2 mex = block_top2(ex, sh);
-      exchange(mex);
-      if (sh.timeout) {
-        timed_out = true;
-        break;
+    __syncthreads();
+    if (!sh.last) continue;
+
+    // ------------------------------------------------ finish the round
+    if (wid == 0) {
+      // every slice stored its result before counting itself done, and the
+      // count has reached S: the S results are in place
+      Top2 g = {-INFINITY, 0x7FFFFFFF, -INFINITY};
+      for (int q = lane; q < S; q += kWave) {
+        Top2 o;
+        o.y1 = ld(&py1[q]);
+        o.y2 = ld(&py2[q]);
+        o.i1 = ld(&pi[q]);
+        top2_merge(g, o);
       }
-      tstar = sh.g.i1;
+#pragma unroll
+      for (int o = kWave / 2; o > 0; o >>= 1) top2_merge(g, top2_shfl_xor(g, o));
+      if (lane == 0) sh.g = g;
     }
-    if (tstar == 0x7FFFFFFF) tstar = 0;
-    if (nodes_lds) {
+    __syncthreads();
+    const Top2 g = sh.g;
+    // the estimates also carry the rounding of x / T (a few ulp of |y|)
+    const double slack = 2.0 * kGumbelTol + (fabs(g.y1) + fabs(g.y2)) * 0x1.0p-48;
+    if (T != 0.0 && kind == 0 && !(g.y1 - g.y2 > slack) && r + 1 < kMaxRounds) {
+      // too close to call from the estimates: the same row once more, exactly
+      if (tid == 0) {
+        st(&a.cut[n], g.y1 - slack);
+        drain();
+        st(&a.word[n], round_word(r + 1, 1, step, u));
+      }
+      continue;
+    }
+    const int tstar = g.i1 == 0x7FFFFFFF ? 0 : g.i1;
+    int nn = a.n_nodes[n];
+    nn = nn < 1 ? 1 : (nn > Bp1 ? Bp1 : nn);
+    const int o = sh.node0[j];
+    if (o >= 0) {
       for (int q = 1 + tid; q < nn; q += kWalkThreads)
-        if (lpar[q] == u && ltok[q] == tstar) atomicMin(&sh.child, q);
+        if (lpar[o + q] == u && ltok[o + q] == tstar) atomicMin(&sh.child, q);
     } else {
       for (int q = 1 + tid; q < nn; q += kWalkThreads)
         if (a.parent[tb + q] == u && a.node_token[tb + q] == tstar) atomicMin(&sh.child, q);
     }
     __syncthreads();
     const int child = sh.child;
-    if (c == 0 && tid == 0) {
-      ot[step] = tstar;
-      pn[step] = u;
-    }
-    if (child == 0x7FFFFFFF || step >= L) {
-      if (c == 0 && tid == 0) a.tau[n] = d + 1;
-      break;
-    }
-    u = child;
-    ++step;
-    __syncthreads();
-  }
-  if (timed_out) {
-    if (tid == 0 && a.status) atomicOr(&a.status[n], MFD_TREE_CAPACITY);
-    if (c == 0 && tid == 0) a.tau[n] = 0;
-  }
-  if (c == 0) {
-    for (int i = step + 1 + tid; i < Lp1; i += kWalkThreads) {
-      ot[i] = -1;
-      pn[i] = -1;
+    int32_t* ot = a.out_tokens + (size_t)n * Lp1;
+    int32_t* pn = a.path_nodes + (size_t)n * Lp1;
+    if (child != 0x7FFFFFFF && step < L && r + 1 < kMaxRounds) {
+      if (tid == 0) {
+        ot[step] = tstar;
+        pn[step] = u;
+        st(&a.word[n], round_word(r + 1, 0, step + 1, child));
+      }
+    } else {
+      for (int i = step + 1 + tid; i < Lp1; i += kWalkThreads) {
+        ot[i] = -1;
+        pn[i] = -1;
+      }
+      if (tid == 0) {
+        ot[step] = tstar;
+        pn[step] = u;
+        a.tau[n] = d + 1;
+        st(&a.word[n], kEnded);
+      }
     }
   }
 }
 
-__global__ void zero_i32(int32_t* p, int n) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+template <size_t A>
+constexpr size_t round_up(size_t x) {
+  return (x + A - 1) / A * A;
+}
+
+struct WalkWsLayout {
+  size_t word, cut, done, py1, py2, pi, total;
+};
+
+WalkWsLayout walk_ws_layout(int N) {
+  WalkWsLayout w;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t r = o;
+    o = round_up<128>(o + bytes);
+    return r;
+  };
+  w.word = take((size_t)N * sizeof(uint32_t));
+  w.cut = take((size_t)N * sizeof(double));
+  w.done = take((size_t)N * kMaxRounds * sizeof(int32_t));
+  w.py1 = take((size_t)N * kSlices * sizeof(double));
+  w.py2 = take((size_t)N * kSlices * sizeof(double));
+  w.pi = take((size_t)N * kSlices * sizeof(int32_t));
+  w.total = o + 128;  // room to align the base
+  return w;
 }
 
 }  // namespace
 
-size_t walk_ws_bytes(int N) {
-  // per tree: the round results (two values and an index), double-buffered,
-  // for up to kMaxC workgroups, and an arrival counter on a line of its own
-  return (size_t)N * (2 * kMaxC * (2 * sizeof(double) + sizeof(int32_t)) + kCounterStride * sizeof(int32_t)) + 256;
-}
+size_t walk_ws_bytes(int N) { return walk_ws_layout(N).total; }
 
 hipError_t launch_verify_walk(const void* target, bool bf16, int N, int Bp1, long long V, int L,
                               const int32_t* node_token, const int32_t* parent, const int32_t* depth,
@@ -410,55 +530,54 @@ hipError_t launch_verify_walk(const void* target, bool bf16, int N, int Bp1, lon
   if (e != hipSuccess) return e;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  const size_t lds = (size_t)2 * (Bp1 < kMaxNodesLds ? Bp1 : kMaxNodesLds) * sizeof(int32_t);
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kWalkThreads, lds);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kWalkThreads, 0);
   if (e != hipSuccess) return e;
-  long long resident = (long long)cus * per_cu;
-  if (resident < 1) resident = 1;
-  int C = (int)(resident / N);
-  if (C > kMaxC) C = kMaxC;
-  if (C < 1) C = 1;
-  // with more trees than resident workgroups, walk them in several launches
-  const int per_launch = (int)(resident / C < 1 ? 1 : resident / C);
+  long long resident = (long long)cus * (per_cu < 1 ? 1 : per_cu);
+  // slices per row: about kSliceVec vectors per thread, at most kSlices and
+  // at most the resident workgroups
+  const long long nvec = V / (bf16 ? 8 : 4);
+  long long S = (nvec + (long long)kSliceVec * kWalkThreads - 1) / ((long long)kSliceVec * kWalkThreads);
+  if (S > kSlices) S = kSlices;
+  if (S > resident) S = resident;
+  if (S < 1) S = 1;
+  // groups: as many as fit, at most one per tree, and few enough that a
+  // group serves at most kMaxServed trees
+  long long G = resident / S;
+  if (G > N) G = N;
+  if (G < (N + kMaxServed - 1) / kMaxServed) return hipErrorCooperativeLaunchTooLarge;
+  if (G < 1) G = 1;
 
-  char* w = static_cast<char*>(ws);
-  double* part_y1 = reinterpret_cast<double*>(w);
-  double* part_y2 = part_y1 + (size_t)N * 2 * kMaxC;
-  int32_t* part_i = reinterpret_cast<int32_t*>(part_y2 + (size_t)N * 2 * kMaxC);
-  // 128-byte aligned counters, one line per tree
-  const uintptr_t cbase = (reinterpret_cast<uintptr_t>(part_i + (size_t)N * 2 * kMaxC) + 127) & ~uintptr_t(127);
-  int32_t* arrive = reinterpret_cast<int32_t*>(cbase);
-  hipLaunchKernelGGL(zero_i32, dim3((N * kCounterStride + 255) / 256), dim3(256), 0, stream, arrive,
-                     N * kCounterStride);
+  const WalkWsLayout l = walk_ws_layout(N);
+  char* w = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(ws) + 127) & ~uintptr_t(127));
+  WalkArgs a;
+  a.target = target;
+  a.N = N;
+  a.Bp1 = Bp1;
+  a.L = L;
+  a.S = (int)S;
+  a.G = (int)G;
+  a.V = V;
+  a.node_token = node_token;
+  a.parent = parent;
+  a.depth = depth;
+  a.n_nodes = n_nodes;
+  a.temperature = temperature;
+  a.seed = seed;
+  a.tau = tau;
+  a.out_tokens = out_tokens;
+  a.path_nodes = path_nodes;
+  a.status = status;
+  a.word = reinterpret_cast<uint32_t*>(w + l.word);
+  a.cut = reinterpret_cast<double*>(w + l.cut);
+  a.done = reinterpret_cast<int32_t*>(w + l.done);
+  a.py1 = reinterpret_cast<double*>(w + l.py1);
+  a.py2 = reinterpret_cast<double*>(w + l.py2);
+  a.pi = reinterpret_cast<int32_t*>(w + l.pi);
+  hipLaunchKernelGGL(walk_init_kernel, dim3((N * kMaxRounds + 255) / 256), dim3(256), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  for (int n0 = 0; n0 < N; n0 += per_launch) {
-    const int nb = (N - n0 < per_launch) ? N - n0 : per_launch;
-    WalkArgs a;
-    a.target = static_cast<const char*>(target) + (size_t)n0 * Bp1 * V * (bf16 ? 2 : 4);
-    a.Bp1 = Bp1;
-    a.V = V;
-    a.L = L;
-    a.node_token = node_token + (size_t)n0 * Bp1;
-    a.parent = parent + (size_t)n0 * Bp1;
-    a.depth = depth + (size_t)n0 * Bp1;
-    a.n_nodes = n_nodes + n0;
-    a.temperature = temperature + n0;
-    a.seed = seed + n0;
-    a.tau = tau + n0;
-    a.out_tokens = out_tokens + (size_t)n0 * (L + 1);
-    a.path_nodes = path_nodes + (size_t)n0 * (L + 1);
-    a.status = status ? status + n0 : nullptr;
-    a.C = C;
-    a.part_y1 = part_y1 + (size_t)n0 * 2 * C;
-    a.part_y2 = part_y2 + (size_t)n0 * 2 * C;
-    a.part_i = part_i + (size_t)n0 * 2 * C;
-    a.arrive = arrive + (size_t)n0 * kCounterStride;
-    void* args[] = {&a};
-    e = hipLaunchCooperativeKernel(fn, dim3(nb * C), dim3(kWalkThreads), args, lds, stream);
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  void* args[] = {&a};
+  return hipLaunchCooperativeKernel(fn, dim3((unsigned)(G * S)), dim3(kWalkThreads), args, 0, stream);
 }
 
 }  // namespace mfd
