@@ -130,6 +130,7 @@ struct Ctl {
   uint32_t hist[256];
   int kept[32];
   int fcount[kNT / kWave];
+  int small;  // children of a level built by small_level, -1 if it did not fit
 };
 
 __device__ __forceinline__ Tree tree_ptrs(const TreeArgs& a, int n) {
@@ -265,6 +266,146 @@ __device__ double exact_kth(int n, int rank, Score score, Ctl& ctl, uint64_t* bu
   return f64_from_key(ans);
 }
 
+// One wave builds a whole level when the frontier has at most 64 entries and
+// each of them at most 8 children reaching tau (so at most 64 children): the
+// counts come from the first 8 candidates of every entry's row (one round of
+// loads), the children are gathered by shuffles, sorted by (parent, token,
+// mode, index) with a wave sort and split into runs with ballots.  It writes
+// exactly what the block path writes (same node and entry order) and keeps
+// each child's score in `my_s` (lane = the child's position in that order).
+// Returns the number of children, or -1, writing nothing, if the level does
+// not fit.  Wave 0 only, no block barrier.
+__device__ int small_level(const TreeArgs& a, const Tree& t, int n, int d, int fsize, double tau,
+                           const double* norm, Ctl& ctl, double& my_s) {
+  const int lane = lane_id();
+  const int K = a.K, L = a.L, k = a.k, Lp1 = L + 1;
+  int m = 0, pnode = 0, cnt = 0;
+  double raw = 0.0, nrm = 0.0;
+  float v[8];
+  int id[8];
+  bool more = false;
+  if (lane < fsize) {
+    const int e = t.fr[lane];
+    m = t.ent_mode[e];
+    raw = t.ent_raw[e];
+    pnode = t.ent_node[e];
+    nrm = norm[m * Lp1 + d];
+    const size_t row = ((size_t)(n * K + m) * L + (d - 1)) * k;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      v[j] = j < k ? a.topk_raw[row + j] : -INFINITY;
+      id[j] = j < k ? a.topk_id[row + j] : 0;
+    }
+    bool run = true;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      run = run && (v[j] != -INFINITY) && ((raw + (double)v[j]) - nrm >= tau);
+      cnt += run ? 1 : 0;
+    }
+    more = cnt == 8 && k > 8;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      v[j] = -INFINITY;
+      id[j] = 0;
+    }
+  }
+  if (__ballot(more) != 0ull) return -1;
+  const int incl = wave_inclusive_scan(cnt);
+  const int off = incl - cnt;
+  const int C = __shfl(incl, kWave - 1, kWave);
+  if (C > kWave) return -1;
+  if (C == 0) return 0;
+  if (ctl.ent_count + C > a.ent_cap || ctl.node_count + C > a.node_cap) return -1;
+
+  // child c = lane: its entry f is the last one whose offset is at most c
+  const int c = lane;
+  int lo = 0, hi = fsize - 1;
+#pragma unroll
+  for (int it = 0; it < 6; ++it) {
+    const int mid = (lo + hi + 1) >> 1;
+    const int om = __shfl(off, mid, kWave);
+    if (lo < hi) {
+      if (om <= c) lo = mid;
+      else hi = mid - 1;
+    }
+  }
+  const int f = lo;
+  const int j = c - __shfl(off, f, kWave);
+  float x = -INFINITY;
+  int tok = 0;
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    const float xv = __shfl(v[jj], f, kWave);
+    const int tv = __shfl(id[jj], f, kWave);
+    if (jj == j) {
+      x = xv;
+      tok = tv;
+    }
+  }
+  const double craw = __shfl(raw, f, kWave) + (double)x;
+  const double cs = craw - __shfl(nrm, f, kWave);
+  const int cm = __shfl(m, f, kWave);
+  const int cp = __shfl(pnode, f, kWave);
+  const bool valid = c < C;
+  const uint64_t key =
+      valid ? (((uint64_t)cp << 40) | ((uint64_t)tok << 20) | ((uint64_t)cm << 15) | (uint64_t)c) : ~0ull;
+  // ascending order of the keys (the descending sort of their complements)
+  const uint64_t sk = ~wave_sort_desc(~key);
+  const bool sv = lane < C;
+  const int sc = sv ? (int)(sk & 0x7FFFu) : 0;
+  const double sraw = __shfl(craw, sc, kWave);
+  const double ss = __shfl(cs, sc, kWave);
+  const int smode = __shfl(cm, sc, kWave);
+  // runs of equal (parent, token) are one node; members are in mode order
+  const uint64_t prefix = sk >> 20;
+  const uint64_t prev = __shfl_up(prefix, 1, kWave);
+  const bool head = sv && (lane == 0 || prefix != prev);
+  const uint64_t hb = __ballot(head);
+  const int g = __popcll(hb & (lanemask_lt() | (1ull << lane))) - 1;
+  const int G = __popcll(hb);
+  // run length of a head: up to the next head or C
+  const uint64_t after = lane == kWave - 1 ? 0ull : (hb & ~((2ull << lane) - 1ull));
+  const int nexth = after ? __builtin_ctzll(after) : C;
+  int runlen = head ? nexth - lane : 0;
+  int maxlen = runlen;
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) maxlen = max(maxlen, __shfl_xor(maxlen, o, kWave));
+  double best = -INFINITY;
+  int mu = -1;
+  for (int q = 0; q < maxlen; ++q) {
+    const int src = lane + q < kWave ? lane + q : kWave - 1;
+    const double sq = __shfl(ss, src, kWave);
+    const int mq = __shfl(smode, src, kWave);
+    if (q < runlen && (mu < 0 || sq > best)) {
+      best = sq;
+      mu = mq;
+    }
+  }
+  const int node0 = ctl.node_count, ent0 = ctl.ent_count;
+  if (head) {
+    const int node = node0 + g;
+    t.node_parent[node] = (int)(sk >> 40);
+    t.node_token[node] = (int)((sk >> 20) & 0xFFFFFu);
+    t.node_depth[node] = d;
+    t.node_S[node] = best;
+    t.node_mu[node] = mu;
+  }
+  if (sv) {
+    const int e = ent0 + lane;
+    t.ent_node[e] = node0 + g;
+    t.ent_mode[e] = smode;
+    t.ent_raw[e] = sraw;
+    t.ent_s[e] = ss;
+  }
+  if (lane == 0) {
+    ctl.node_count = node0 + G;
+    ctl.ent_count = ent0 + C;
+  }
+  my_s = sv ? ss : -INFINITY;
+  return C;
+}
+
 // Chunked exclusive scan of `val(i)` for i in [0, n) writing out[i]; returns the total.
 template <typename Val, typename Out>
 __device__ int block_scan_range(int n, Val val, Out out, int* scan_smem) {
@@ -295,6 +436,49 @@ __device__ void level_search(const TreeArgs& a, const Tree& t, int n, Ctl& ctl, 
     const int fsize = ctl.fsize;
     if (fsize == 0 || ctl.fail) break;
     double tau = ctl.tau;
+
+    // (threshold call) raise tau to the B-th best unique node so far
+    auto raise_tau = [&]() {
+      int local = 0;
+      for (int i = 1 + tid; i < ctl.node_count; i += kNT) local += (t.node_S[i] >= tau) ? 1 : 0;
+      const int alive = block_sum<kNT>(local, ctl.scan);
+      if (alive >= B && B > 0) {
+        // any lower bound of the B-th best node score is a valid threshold;
+        // a 16-bit one takes two radix passes instead of eight
+        const double tcur = tau;
+        const double nt = kth_lower_bound(
+            ctl.node_count - 1, B, [&](int i) { return t.node_S[i + 1]; },
+            [&](int i) { return t.node_S[i + 1] >= tcur; }, ctl);
+        if (nt > tau) tau = nt;
+        if (tid == 0) ctl.tau = tau;
+      }
+      __syncthreads();
+    };
+
+    if (fsize <= kWave) {
+      // a small level: one wave builds it (or finds that it does not fit)
+      const int ent0 = ctl.ent_count;
+      double my_s = -INFINITY;
+      if (tid < kWave) {
+        const int cs = small_level(a, t, n, d, fsize, tau, norm, ctl, my_s);
+        if (tid == 0) ctl.small = cs;
+      }
+      __syncthreads();
+      const int Cs = ctl.small;
+      if (Cs == 0) break;
+      if (Cs > 0) {
+        if (!BUILD) raise_tau();
+        if (tid < kWave) {
+          const double tnext = ctl.tau;
+          const bool keep = tid < Cs && my_s >= tnext;
+          const uint64_t kb = __ballot(keep);
+          if (keep) t.fr[__popcll(kb & lanemask_lt())] = ent0 + tid;
+          if (tid == 0) ctl.fsize = __popcll(kb);
+        }
+        __syncthreads();
+        continue;
+      }
+    }
 
     // 1. per frontier entry: number of children reaching tau; exclusive offsets
     auto count_at = [&](int f, double th) -> int {
@@ -433,22 +617,7 @@ __device__ void level_search(const TreeArgs& a, const Tree& t, int n, Ctl& ctl, 
     __syncthreads();
 
     // 4. (threshold call) raise tau to the B-th best unique node so far
-    if (!BUILD) {
-      int local = 0;
-      for (int i = 1 + tid; i < ctl.node_count; i += kNT) local += (t.node_S[i] >= tau) ? 1 : 0;
-      const int alive = block_sum<kNT>(local, ctl.scan);
-      if (alive >= B && B > 0) {
-        // any lower bound of the B-th best node score is a valid threshold;
-        // a 16-bit one takes two radix passes instead of eight
-        const double tcur = tau;
-        const double nt = kth_lower_bound(
-            ctl.node_count - 1, B, [&](int i) { return t.node_S[i + 1]; },
-            [&](int i) { return t.node_S[i + 1] >= tcur; }, ctl);
-        if (nt > tau) tau = nt;
-        if (tid == 0) ctl.tau = tau;
-      }
-      __syncthreads();
-    }
+    if (!BUILD) raise_tau();
 
     // 5. next frontier: this level's entries still reaching tau
     const double tnext = ctl.tau;
