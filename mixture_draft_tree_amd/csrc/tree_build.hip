@@ -43,6 +43,7 @@ namespace {
 
 constexpr int kNT = 1024;
 constexpr int kMaxSort = 16384;
+constexpr size_t kTreeLdsMax = 156 * 1024;  // LDS one workgroup may use (of 160 KB per CU)
 
 // Per-tree workspace layout (offsets in bytes from the tree's base).
 struct WsLayout {
@@ -91,6 +92,7 @@ struct TreeArgs {
   const double* lse;
   int K, L, k, B;
   int sort_cap, ent_cap, node_cap, tie_cap;
+  int nk_lds;  // threshold call: the nodes' 16-bit score keys are kept in LDS
   unsigned char* ws;
   size_t ws_stride;
   int32_t* status;
@@ -132,6 +134,11 @@ struct Ctl {
   int fcount[kNT / kWave];
   int small;  // children of a level built by small_level, -1 if it did not fit
 };
+
+// Bytes of LDS before the optional node-key array: sort keys, norms, Ctl.
+__host__ __device__ inline size_t tree_lds_base(int sort_cap, int K, int L) {
+  return (size_t)sort_cap * 8 + (size_t)K * (L + 1) * 8 + sizeof(Ctl);
+}
 
 __device__ __forceinline__ Tree tree_ptrs(const TreeArgs& a, int n) {
   const WsLayout w = ws_layout(a.sort_cap, a.ent_cap, a.node_cap);
@@ -276,7 +283,7 @@ __device__ double exact_kth(int n, int rank, Score score, Ctl& ctl, uint64_t* bu
 // Returns the number of children, or -1, writing nothing, if the level does
 // not fit.  Wave 0 only, no block barrier.
 __device__ int small_level(const TreeArgs& a, const Tree& t, int n, int d, int fsize, double tau,
-                           const double* norm, Ctl& ctl, double& my_s) {
+                           const double* norm, Ctl& ctl, uint16_t* nk, double& my_s) {
   const int lane = lane_id();
   const int K = a.K, L = a.L, k = a.k, Lp1 = L + 1;
   int m = 0, pnode = 0, cnt = 0;
@@ -390,6 +397,7 @@ __device__ int small_level(const TreeArgs& a, const Tree& t, int n, int d, int f
     t.node_depth[node] = d;
     t.node_S[node] = best;
     t.node_mu[node] = mu;
+    if (nk) nk[node] = (uint16_t)(f64_key(best) >> 48);
   }
   if (sv) {
     const int e = ent0 + lane;
@@ -425,7 +433,8 @@ __device__ int block_scan_range(int n, Val val, Out out, int* scan_smem) {
 // The search.  Returns with ctl.node_count nodes (node 0 = root) and
 // ctl.ent_count entries; ctl.fail set on capacity overflow.
 template <bool BUILD>
-__device__ void level_search(const TreeArgs& a, const Tree& t, int n, Ctl& ctl, uint64_t* keys, const double* norm) {
+__device__ void level_search(const TreeArgs& a, const Tree& t, int n, Ctl& ctl, uint64_t* keys, const double* norm,
+                             uint16_t* nk) {
   const int K = a.K, L = a.L, k = a.k, B = a.B;
   const int tid = threadIdx.x;
   const int Lp1 = L + 1;
@@ -439,6 +448,26 @@ __device__ void level_search(const TreeArgs& a, const Tree& t, int n, Ctl& ctl, 
 
     // (threshold call) raise tau to the B-th best unique node so far
     auto raise_tau = [&]() {
+      if (nk) {
+        // on the 16-bit keys in LDS: the B-th largest key among those at or
+        // above tau's stands for B distinct nodes scoring at least its value
+        const uint32_t kt = (uint32_t)(f64_key(tau) >> 48);
+        int local = 0;
+        for (int i = 1 + tid; i < ctl.node_count; i += kNT) local += nk[i] >= kt ? 1 : 0;
+        const int alive = block_sum<kNT>(local, ctl.scan);
+        if (alive >= B && B > 0) {
+          auto get = [&](int i, uint64_t* key) -> bool {
+            *key = nk[i + 1];
+            return nk[i + 1] >= kt;
+          };
+          const uint64_t kb = block_kth_largest<kNT, 16>(ctl.node_count - 1, B, get, ctl.hist, ctl.sh);
+          const double nt = f64_from_key(kb << 48);
+          if (nt > tau) tau = nt;
+          if (tid == 0) ctl.tau = tau;
+        }
+        __syncthreads();
+        return;
+      }
       int local = 0;
       for (int i = 1 + tid; i < ctl.node_count; i += kNT) local += (t.node_S[i] >= tau) ? 1 : 0;
       const int alive = block_sum<kNT>(local, ctl.scan);
@@ -460,7 +489,7 @@ __device__ void level_search(const TreeArgs& a, const Tree& t, int n, Ctl& ctl, 
       const int ent0 = ctl.ent_count;
       double my_s = -INFINITY;
       if (tid < kWave) {
-        const int cs = small_level(a, t, n, d, fsize, tau, norm, ctl, my_s);
+        const int cs = small_level(a, t, n, d, fsize, tau, norm, ctl, nk, my_s);
         if (tid == 0) ctl.small = cs;
       }
       __syncthreads();
@@ -600,6 +629,7 @@ __device__ void level_search(const TreeArgs& a, const Tree& t, int n, Ctl& ctl, 
       t.node_depth[node] = d;
       t.node_S[node] = best;
       t.node_mu[node] = mu;
+      if (nk) nk[node] = (uint16_t)(f64_key(best) >> 48);
       for (int q = i; q < j; ++q) {
         const int c = (int)(keys[q] & 0x7FFFu);
         const int e = ent0 + q;
@@ -646,6 +676,9 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
   uint64_t* keys = reinterpret_cast<uint64_t*>(smem_raw);
   double* norm = reinterpret_cast<double*>(keys + a.sort_cap);
   Ctl& ctl = *reinterpret_cast<Ctl*>(norm + K * Lp1);
+  uint16_t* nk = (!BUILD && a.nk_lds)
+                     ? reinterpret_cast<uint16_t*>(smem_raw + ((tree_lds_base(a.sort_cap, K, L) + 15) & ~size_t(15)))
+                     : nullptr;
   const Tree t = tree_ptrs(a, n);
 
   // norm[m][d] = sum_{i<d} lse[m][i], fp64, from i = 0 upward (all K*L
@@ -714,7 +747,7 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
   }
   __syncthreads();
 
-  level_search<BUILD>(a, t, n, ctl, keys, norm);
+  level_search<BUILD>(a, t, n, ctl, keys, norm, nk);
 
   const int nc = ctl.node_count;
   const int fail = ctl.fail;
@@ -897,7 +930,7 @@ TreeCaps tree_caps(int K, int L, int k, int B) {
   if (c.node_cap > 65535) c.node_cap = 65535;  // node ids fit 16 bits in the layout keys
   const WsLayout w = ws_layout(c.sort_cap, c.ent_cap, c.node_cap);
   c.ws_bytes_per_tree = w.total;
-  c.lds_bytes = (size_t)c.sort_cap * 8 + (size_t)K * (L + 1) * 8 + sizeof(Ctl) + 64;
+  c.lds_bytes = tree_lds_base(c.sort_cap, K, L) + 64;
   return c;
 }
 
@@ -916,11 +949,17 @@ static hipError_t launch_tree(bool build, TreeArgs& a, int N, hipStream_t stream
   a.ws_stride = c.ws_bytes_per_tree;
   const void* fn = build ? reinterpret_cast<const void*>(&tree_kernel<true>)
                          : reinterpret_cast<const void*>(&tree_kernel<false>);
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)c.lds_bytes);
+  // the threshold call keeps a 16-bit score key per node in LDS when it fits
+  size_t lds = c.lds_bytes;
+  const size_t nk_off = (tree_lds_base(c.sort_cap, a.K, a.L) + 15) & ~size_t(15);
+  const size_t nk_end = nk_off + (size_t)c.node_cap * sizeof(uint16_t);
+  a.nk_lds = (!build && nk_end <= kTreeLdsMax) ? 1 : 0;
+  if (a.nk_lds && nk_end > lds) lds = nk_end;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   if (N == 0) return hipSuccess;
-  if (build) hipLaunchKernelGGL(tree_kernel<true>, dim3(N), dim3(kNT), c.lds_bytes, stream, a);
-  else hipLaunchKernelGGL(tree_kernel<false>, dim3(N), dim3(kNT), c.lds_bytes, stream, a);
+  if (build) hipLaunchKernelGGL(tree_kernel<true>, dim3(N), dim3(kNT), lds, stream, a);
+  else hipLaunchKernelGGL(tree_kernel<false>, dim3(N), dim3(kNT), lds, stream, a);
   return hipGetLastError();
 }
 
