@@ -66,7 +66,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="batched", choices=["batched", "single", "stress"])
+    ap.add_argument("--workload", default="batched", choices=["batched", "single", "stress", "deep", "batched_deep"])
     ap.add_argument("--cpu-baseline-trees", type=int, default=2,
                     help="trees of the workload the fp64 oracle is timed on (0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
@@ -75,6 +75,8 @@ def parse():
                          "known size against which hardware byte counters are calibrated (0 = skip)")
     ap.add_argument("--latency-steps", type=int, default=20,
                     help="steps of the single-tree workload timed for per-tree latency (0 = skip)")
+    ap.add_argument("--deep-workload", default="batched_deep", choices=["batched_deep", "none"],
+                    help="also time the confident-drafter batch (deep trees, pages-like acceptance lengths)")
     return ap.parse_args()
 
 
@@ -158,11 +160,25 @@ def setup(name, seed, dev):
     return w, N, P, logits, anchor, pos, temps, seeds, R
 
 
-def single_tree_latency(seed, steps, stream):
-    """Mean time of one whole step on the single-tree workload (N=1), ms."""
-    w, N, P, logits, anchor, pos, temps, seeds, R = setup("single", seed, "cuda")
+def single_tree_latency(seed, steps, stream, name="single"):
+    """Mean time of one whole step on a one-tree workload (N=1), ms."""
+    w, N, P, logits, anchor, pos, temps, seeds, R = setup(name, seed, "cuda")
     total, _ = run_steps(P, logits, anchor, pos, R, temps, seeds, steps, 3, stream)
     return total / steps
+
+
+STAGES = ["logsoftmax_topk", "mixture_threshold", "tree_build", "tree_mask", "verify_walk"]
+
+
+def timed_workload(name, seed, steps, warmup, stream):
+    """Whole steps on workload `name`: (ms per step, per-stage ms, N, buffers)."""
+    w, N, P, logits, anchor, pos, temps, seeds, R = setup(name, seed, "cuda")
+    total_ms, ev = run_steps(P, logits, anchor, pos, R, temps, seeds, steps, warmup, stream)
+    stage = {nm: statistics.mean(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps))
+             for i, nm in enumerate(STAGES)}
+    status = P.buf.status.cpu()
+    assert int(status.abs().sum()) == 0, f"per-tree status flags set ({name}): {status.tolist()}"
+    return total_ms / steps, stage, N, w, P, logits
 
 
 def main():
@@ -174,14 +190,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     name = args.workload
     stream = torch.cuda.current_stream()
-    w, N, P, logits, anchor, pos, temps, seeds, R = setup(name, args.seed, "cuda")
-    names = ["logsoftmax_topk", "mixture_threshold", "tree_build", "tree_mask", "verify_walk"]
-    total_ms, ev = run_steps(P, logits, anchor, pos, R, temps, seeds, args.steps, args.warmup, stream)
-    ms_per_step = total_ms / args.steps
-    stage = {nm: [ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)] for i, nm in enumerate(names)}
-    stage_ms = {nm: statistics.mean(v) for nm, v in stage.items()}
-    status = P.buf.status.cpu()
-    assert int(status.abs().sum()) == 0, f"per-tree status flags set: {status.tolist()}"
+    ms_per_step, stage_ms, N, w, P, logits = timed_workload(name, args.seed, args.steps, args.warmup, stream)
 
     logits_bytes = N * w.K * w.L * w.V * logits.element_size()
     lsm_ms = stage_ms["logsoftmax_topk"]
@@ -199,7 +208,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded; confident drafter: N(0,4) noise, 16 Zipf alternatives, each mode's future at 16+N(0,2.25); target rows N(0,1) + 16 on one future up to a random deviation depth)",
+        "data": "synthetic (seeded; drafter logits N(0,9) + per-mode futures at +8, target rows N(0,1) + 10 on one future)",
         "config": {"workload": f"{name}: {N} trees, K={w.K}, L={w.L}, V={w.V}, B={w.B}, "
                                f"T pattern {list(w.temperatures)}",
                    "trees": N, "K": w.K, "L": w.L, "V": w.V, "B": w.B},
@@ -215,6 +224,19 @@ def main():
     }
     if args.latency_steps > 0 and name != "single":
         out["single_tree_latency_ms"] = single_tree_latency(args.seed, args.latency_steps, stream)
+    if args.deep_workload != "none" and name == "batched":
+        del P, logits
+        dms, dstage, dN, dw, dP, _ = timed_workload(args.deep_workload, args.seed, args.steps, args.warmup, stream)
+        out["deep"] = {
+            "workload": f"{args.deep_workload}: {dN} trees, K={dw.K}, L={dw.L}, V={dw.V}, B={dw.B}, "
+                        f"T pattern {list(dw.temperatures)}",
+            "data": "synthetic (seeded; confident drafter: N(0,4) noise, 16 Zipf alternatives, each mode's future "
+                    "at 16+N(0,2.25); target rows N(0,1) + 16 on one future up to a random deviation depth)",
+            "value": dN / (dms * 1e-3), "unit": "trees/s", "ms_per_step": dms, "stages_ms": dstage,
+            "tau_mean": float(dP.buf.tau.cpu().float().mean()),
+            "single_tree_latency_ms": (single_tree_latency(args.seed, args.latency_steps, stream, "deep")
+                                       if args.latency_steps > 0 else None),
+        }
     if args.cpu_baseline_trees > 0:
         out["cpu_baseline"] = cpu_baseline(name, args.seed, args.cpu_baseline_trees)
     print(json.dumps(out), flush=True)

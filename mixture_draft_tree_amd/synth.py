@@ -10,20 +10,27 @@ none of that is used here. What is kept from the pages is the shape of the
 problem: a block of 16 slots with 15 drafted positions (MFD-Qwen3.5-4B model
 card, "Model"), K = 8 modes and a budget of B = 256 (same card, "Results"), and
 modes that each draft one coherent future (project page, "How it works", step 2).
-The mixture workloads model a trained, confident drafter: each mode's future
-token takes most of its row's mass (log-probability about -0.1 to -1.3), a few
-alternatives sit far below it, and the target follows the chosen future for a
-random number of tokens, so trees reach the full depth of 15 and acceptance
-lengths land near the pages' figures (tau of 6 to 11 at B = 256, project page,
-Table 1; about 10.7 for MFD on Qwen3.5-4B at T = 0, model card, "Results").
+The `single`, `batched` and `stress` workloads follow a fixed recipe: drafter
+noise N(0, 3^2) with each mode's future boosted by +8, and target rows N(0,1)
+with +10 on the chosen future.  That drafter is nearly flat over 151936
+tokens, so its trees are shallow (depth 2 or so, acceptance length about 1.4).
+The `deep` and `batched_deep` workloads model a trained, confident drafter
+instead: each mode's future token takes most of its row's mass
+(log-probability about -0.1 to -1.3), a few alternatives sit far below it, and
+the target follows the chosen future for a random number of tokens, so trees
+reach the full depth of 15 and acceptance lengths land near the pages'
+figures (tau of 6 to 11 at B = 256, project page, Table 1; about 10.7 for MFD
+on Qwen3.5-4B at T = 0, model card, "Results").
 
-Five named workloads:
+Seven named workloads:
 
-  tiny      K=2,  L=4,  V=16,     B=8     fp32, brute-forceable
-  product   K=1,  L=15, V=32000,  B=64    bf16, two injected futures at equal mass
-  single    K=8,  L=15, V=151936, B=256   bf16, one tree
-  batched   64 trees of the `single` shape, T alternating 0 / 1
-  stress    K=16, L=15, V=248320, B=1024  bf16, heavy exact ties
+  tiny          K=2,  L=4,  V=16,     B=8     fp32, brute-forceable
+  product       K=1,  L=15, V=32000,  B=64    bf16, two injected futures at equal mass
+  single        K=8,  L=15, V=151936, B=256   bf16, one tree
+  batched       64 trees of the `single` shape, T alternating 0 / 1
+  stress        K=16, L=15, V=248320, B=1024  bf16, heavy exact ties
+  deep          K=8,  L=15, V=151936, B=256   bf16, one tree, confident drafter
+  batched_deep  64 trees of the `deep` shape, T alternating 0 / 1
 
 Every draw comes from a torch.Generator seeded from (workload id, tree index,
 base seed), on the device the caller names, so a given (device, seed) always
@@ -62,12 +69,13 @@ class Workload:
 WORKLOADS = {
     "tiny": Workload("tiny", 1, 2, 4, 16, 8, 1, torch.float32, 2.0, 4.0, 5.0, (0.0,)),
     "product": Workload("product", 2, 1, 15, 32000, 64, 1, torch.bfloat16, 2.0, 0.0, 10.0, (0.0,)),
-    "single": Workload("single", 3, 8, 15, 151936, 256, 1, torch.bfloat16, 2.0, 16.0, 16.0, (0.0, 1.0),
-                       jitter=1.5, alt_n=16, alt_height=10.0, dev_lo=3),
-    "batched": Workload("batched", 4, 8, 15, 151936, 256, 64, torch.bfloat16, 2.0, 16.0, 16.0, (0.0, 1.0),
-                        jitter=1.5, alt_n=16, alt_height=10.0, dev_lo=3),
-    "stress": Workload("stress", 5, 16, 15, 248320, 1024, 1, torch.bfloat16, 2.0, 16.0, 16.0, (1.0,),
-                       jitter=1.5, alt_n=16, alt_height=10.0, dev_lo=3),
+    "single": Workload("single", 3, 8, 15, 151936, 256, 1, torch.bfloat16, 3.0, 8.0, 10.0, (0.0, 1.0)),
+    "batched": Workload("batched", 4, 8, 15, 151936, 256, 64, torch.bfloat16, 3.0, 8.0, 10.0, (0.0, 1.0)),
+    "stress": Workload("stress", 5, 16, 15, 248320, 1024, 1, torch.bfloat16, 3.0, 8.0, 10.0, (1.0,)),
+    "deep": Workload("deep", 6, 8, 15, 151936, 256, 1, torch.bfloat16, 2.0, 16.0, 16.0, (0.0, 1.0),
+                     jitter=1.5, alt_n=16, alt_height=10.0, dev_lo=3),
+    "batched_deep": Workload("batched_deep", 7, 8, 15, 151936, 256, 64, torch.bfloat16, 2.0, 16.0, 16.0,
+                             (0.0, 1.0), jitter=1.5, alt_n=16, alt_height=10.0, dev_lo=3),
 }
 
 

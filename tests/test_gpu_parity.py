@@ -398,6 +398,16 @@ def test_workload_stress():
     _run_workload("stress")
 
 
+def test_workload_deep():
+    """Confident drafter: trees of full depth, walks of pages-like length."""
+    b, P, trees = _run_workload("deep")
+    assert max(int(trees[0]["depth"].max()), 0) == b.workload.L
+
+
+def test_workload_batched_deep_sampled():
+    _run_workload("batched_deep", sample=[0, 1, 22, 63], device_gen="cuda")
+
+
 def test_determinism_and_batch_order():
     """Same trees in another batch order give identical outputs."""
     b = synth.draft_batch("single", base_seed=5, N=3)
