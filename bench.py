@@ -66,7 +66,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="batched", choices=["batched", "single", "stress", "deep", "batched_deep"])
+    ap.add_argument("--workload", default="batched",
+                    choices=["batched", "single", "stress", "deep", "batched_deep", "subset", "batched_subset"])
     ap.add_argument("--cpu-baseline-trees", type=int, default=2,
                     help="trees of the workload the fp64 oracle is timed on (0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
@@ -77,6 +78,8 @@ def parse():
                     help="steps of the single-tree workload timed for per-tree latency (0 = skip)")
     ap.add_argument("--deep-workload", default="batched_deep", choices=["batched_deep", "none"],
                     help="also time the confident-drafter batch (deep trees, pages-like acceptance lengths)")
+    ap.add_argument("--subset-workload", default="batched_subset", choices=["batched_subset", "none"],
+                    help="also time drafting over a 65536-token subset of the vocabulary (walk over all of it)")
     return ap.parse_args()
 
 
@@ -148,7 +151,8 @@ def setup(name, seed, dev):
     w = synth.WORKLOADS[name]
     b = synth.draft_batch(name, base_seed=seed, device=dev)
     N = b.logits.shape[0]
-    P = MixtureTreePath(N, w.K, w.L, w.V, w.B)
+    vmap = None if b.vocab_map is None else b.vocab_map.to(dev)
+    P = MixtureTreePath(N, w.K, w.L, b.logits.shape[-1], w.B, vocab_map=vmap, V_full=w.V)
     logits = b.logits.contiguous()
     anchor, pos = b.anchor.to(dev), b.pos_base.to(dev)
     temps, seeds = b.temperature.to(dev), b.seed.to(dev)
@@ -237,6 +241,19 @@ def main():
             "single_tree_latency_ms": (single_tree_latency(args.seed, args.latency_steps, stream, "deep")
                                        if args.latency_steps > 0 else None),
         }
+    if args.subset_workload != "none" and name == "batched":
+        sms, sstage, sN, sw, sP, slog = timed_workload(args.subset_workload, args.seed, args.steps, args.warmup,
+                                                       stream)
+        sbytes = sN * sw.K * sw.L * slog.shape[-1] * slog.element_size()
+        sgbs = sbytes / (sstage["logsoftmax_topk"] * 1e-3) / 1e9
+        out["reduced_vocab"] = {
+            "workload": f"{args.subset_workload}: {sN} trees, K={sw.K}, L={sw.L}, drafting over {slog.shape[-1]} of "
+                        f"V={sw.V} tokens, B={sw.B}, T pattern {list(sw.temperatures)}",
+            "value": sN / (sms * 1e-3), "unit": "trees/s", "ms_per_step": sms, "stages_ms": sstage,
+            "logits_GBps": sgbs, "logits_frac_of_peak": sgbs / HBM_PEAK_GBS,
+            "algorithmic_bytes_per_launch": sbytes, "tau_mean": float(sP.buf.tau.cpu().float().mean()),
+        }
+        del sP, slog
     if args.cpu_baseline_trees > 0:
         out["cpu_baseline"] = cpu_baseline(name, args.seed, args.cpu_baseline_trees)
     print(json.dumps(out), flush=True)

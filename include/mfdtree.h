@@ -119,6 +119,28 @@ mfd_status mfd_logsoftmax_topk(const void* logits, mfd_dtype dtype, int N, int K
                                int32_t* status, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * The same pass over a reduced drafting vocabulary (project page, "In a
+ * serving engine": the drafter drafts over the target's 64K most frequent
+ * tokens and the target verifies over the full vocabulary).  The logits cover
+ * the V drafting tokens only; each listed token is reported by its id in the
+ * full vocabulary of V_full tokens, so the tree and the walk work in target
+ * ids.
+ *
+ *   vocab_map device [V] int32: full-vocabulary id of drafting token j, in
+ *             strictly increasing order (the subset sorted by id), each in
+ *             [0, V_full).  Ties between equal logits then break by full id
+ *             exactly as in mfd_logsoftmax_topk over full-vocabulary logits
+ *             that are -inf outside the subset.  Not checked on the device; a
+ *             map out of order gives an unspecified tie order.
+ *   V_full    size of the full vocabulary, V <= V_full < 2^20.
+ *   Other arguments as for mfd_logsoftmax_topk; topk_id holds full ids.
+ */
+mfd_status mfd_logsoftmax_topk_mapped(const void* logits, mfd_dtype dtype, int N, int K, int L, int V,
+                                      const int32_t* vocab_map, int V_full, int k, double* lse,
+                                      int32_t* topk_id, float* topk_raw, float* topk_logp, int32_t* status,
+                                      hipStream_t stream);
+
+/*
  * The common cut-off ("In one minute": the B-th best score over all modes is
  * one cut-off shared by every mode; step 3: every prefix is scored by its best
  * mode).  A prefix t = (t_1..t_d), 1 <= d <= L, scores

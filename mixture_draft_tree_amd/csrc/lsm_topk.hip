@@ -348,6 +348,7 @@ __global__ void __launch_bounds__(kThreads, 5) lsm_topk_kernel(const typename El
                                                                long long V, int k, int cap_w, int pool_cap,
                                                                int sort_cap, int cand_cap, int rows_per_tree,
                                                                double* __restrict__ lse_out,
+                                                               const int32_t* __restrict__ vocab_map,
                                                                int32_t* __restrict__ topk_id,
                                                                float* __restrict__ topk_raw,
                                                                float* __restrict__ topk_logp,
@@ -777,7 +778,7 @@ __global__ void __launch_bounds__(kThreads, 5) lsm_topk_kernel(const typename El
       const uint32_t idx = 0xFFFFFFFFu - (uint32_t)a0;
       const float x = E::val_of_key(key);
       const long long o = row * k + j;
-      topk_id[o] = (int32_t)idx;
+      topk_id[o] = vocab_map ? vocab_map[idx] : (int32_t)idx;
       topk_raw[o] = x;
       if (topk_logp) topk_logp[o] = (float)((double)x - lse);
     }
@@ -797,7 +798,7 @@ __global__ void __launch_bounds__(kThreads, 5) lsm_topk_kernel(const typename El
         const uint32_t idx = 0xFFFFFFFFu - (uint32_t)c;
         const float x = E::val_of_key(key);
         const long long o = row * k + j;
-        topk_id[o] = (int32_t)idx;
+        topk_id[o] = vocab_map ? vocab_map[idx] : (int32_t)idx;
         topk_raw[o] = x;
         if (topk_logp) topk_logp[o] = (float)((double)x - lse);
       }
@@ -813,7 +814,7 @@ __global__ void __launch_bounds__(kThreads, 5) lsm_topk_kernel(const typename El
     const uint32_t idx = 0xFFFFFFFFu - (uint32_t)c;
     const float x = E::val_of_key(key);
     const long long o = row * k + j;
-    topk_id[o] = (int32_t)idx;
+    topk_id[o] = vocab_map ? vocab_map[idx] : (int32_t)idx;
     topk_raw[o] = x;
     if (topk_logp) topk_logp[o] = (float)((double)x - lse);
   }
@@ -863,8 +864,8 @@ LsmCaps lsm_caps(long long V, int k, bool bf16) {
 }  // namespace
 
 hipError_t launch_logsoftmax_topk(const void* logits, bool bf16, int rows, int rows_per_tree, long long V, int k,
-                                  double* lse, int32_t* topk_id, float* topk_raw, float* topk_logp,
-                                  int32_t* status, hipStream_t stream) {
+                                  const int32_t* vocab_map, double* lse, int32_t* topk_id, float* topk_raw,
+                                  float* topk_logp, int32_t* status, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   const LsmCaps c = lsm_caps(V, k, bf16);
   if (bf16) {
@@ -873,14 +874,14 @@ hipError_t launch_logsoftmax_topk(const void* logits, bool bf16, int rows, int r
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(lsm_topk_kernel<true>, dim3(rows), dim3(kThreads), c.lds, stream,
                        static_cast<const uint16_t*>(logits), V, k, c.cap_w, c.pool, c.sort_cap, c.cand_cap,
-                       rows_per_tree, lse, topk_id, topk_raw, topk_logp, status);
+                       rows_per_tree, lse, vocab_map, topk_id, topk_raw, topk_logp, status);
   } else {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lsm_topk_kernel<false>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)c.lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(lsm_topk_kernel<false>, dim3(rows), dim3(kThreads), c.lds, stream,
                        static_cast<const float*>(logits), V, k, c.cap_w, c.pool, c.sort_cap, c.cand_cap,
-                       rows_per_tree, lse, topk_id, topk_raw, topk_logp, status);
+                       rows_per_tree, lse, vocab_map, topk_id, topk_raw, topk_logp, status);
   }
   return hipGetLastError();
 }

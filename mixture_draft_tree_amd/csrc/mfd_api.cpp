@@ -90,11 +90,9 @@ mfd_status mfd_workspace_size(mfd_op op, int N, int K, int L, int V, int B, size
   return fail(MFD_ERR_INVALID_ARG, "unknown op %d", (int)op);
 }
 
-mfd_status mfd_logsoftmax_topk(const void* logits, mfd_dtype dtype, int N, int K, int L, int V, int k, double* lse,
-                               int32_t* topk_id, float* topk_raw, float* topk_logp, int32_t* status, void* ws,
-                               size_t ws_bytes, hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
+static mfd_status logsoftmax_topk_impl(const char* call, const void* logits, mfd_dtype dtype, int N, int K, int L,
+                                       int V, const int32_t* vocab_map, int k, double* lse, int32_t* topk_id,
+                                       float* topk_raw, float* topk_logp, int32_t* status, hipStream_t stream) {
   mfd_status s = check_dims(N, K, L, V);
   if (s != MFD_OK) return s;
   if (dtype != MFD_BF16 && dtype != MFD_F32) return fail(MFD_ERR_DTYPE, "dtype must be MFD_BF16 or MFD_F32");
@@ -108,9 +106,28 @@ mfd_status mfd_logsoftmax_topk(const void* logits, mfd_dtype dtype, int N, int K
   if (reinterpret_cast<uintptr_t>(logits) % esz) return fail(MFD_ERR_INVALID_ARG, "logits not aligned to its element size");
   const long long rows = (long long)N * K * L;
   if (rows > 0x7FFFFFFFLL) return fail(MFD_ERR_INVALID_ARG, "too many rows (%lld)", rows);
-  return from_hip(mfd::launch_logsoftmax_topk(logits, dtype == MFD_BF16, (int)rows, K * L, V, k, lse, topk_id, topk_raw,
-                                              topk_logp, status, stream),
-                  "mfd_logsoftmax_topk launch");
+  return from_hip(mfd::launch_logsoftmax_topk(logits, dtype == MFD_BF16, (int)rows, K * L, V, k, vocab_map, lse,
+                                              topk_id, topk_raw, topk_logp, status, stream),
+                  call);
+}
+
+mfd_status mfd_logsoftmax_topk(const void* logits, mfd_dtype dtype, int N, int K, int L, int V, int k, double* lse,
+                               int32_t* topk_id, float* topk_raw, float* topk_logp, int32_t* status, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  return logsoftmax_topk_impl("mfd_logsoftmax_topk launch", logits, dtype, N, K, L, V, nullptr, k, lse, topk_id,
+                              topk_raw, topk_logp, status, stream);
+}
+
+mfd_status mfd_logsoftmax_topk_mapped(const void* logits, mfd_dtype dtype, int N, int K, int L, int V,
+                                      const int32_t* vocab_map, int V_full, int k, double* lse, int32_t* topk_id,
+                                      float* topk_raw, float* topk_logp, int32_t* status, hipStream_t stream) {
+  if (V_full < V || V_full > kMaxV)
+    return fail(MFD_ERR_INVALID_ARG, "V_full must be in [V, %d] (got %d, V = %d)", kMaxV, V_full, V);
+  if (N > 0) REQUIRE_PTR(vocab_map);
+  return logsoftmax_topk_impl("mfd_logsoftmax_topk_mapped launch", logits, dtype, N, K, L, V, vocab_map, k, lse,
+                              topk_id, topk_raw, topk_logp, status, stream);
 }
 
 mfd_status mfd_mixture_threshold(const int32_t* topk_id, const float* topk_raw, const double* lse, int N, int K, int L,

@@ -12,7 +12,8 @@
 namespace mfd {
 
 hipError_t launch_logsoftmax_topk(const void* logits, bool bf16, int rows, int rows_per_tree, long long V, int k,
-                                  double* lse, int32_t* topk_id, float* topk_raw, float* topk_logp,
+                                  const int32_t* vocab_map, double* lse, int32_t* topk_id, float* topk_raw,
+                                  float* topk_logp,
                                   int32_t* status, hipStream_t stream);
 
 // Working capacities of the tree search for one tree (shared by the threshold

@@ -540,44 +540,49 @@ hipError_t launch_verify_walk(const void* target, bool bf16, int N, int Bp1, lon
   if (S > kSlices) S = kSlices;
   if (S > resident) S = resident;
   if (S < 1) S = 1;
-  // groups: as many as fit, at most one per tree, and few enough that a
-  // group serves at most kMaxServed trees
-  long long G = resident / S;
-  if (G > N) G = N;
-  if (G < (N + kMaxServed - 1) / kMaxServed) return hipErrorCooperativeLaunchTooLarge;
-  if (G < 1) G = 1;
+  // groups: as many as fit and at most one per tree; each group serves at
+  // most kMaxServed trees, so a larger batch is walked in several launches
+  long long Gmax = resident / S;
+  if (Gmax < 1) Gmax = 1;
+  const long long per_launch = Gmax * kMaxServed;
 
   const WalkWsLayout l = walk_ws_layout(N);
   char* w = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(ws) + 127) & ~uintptr_t(127));
-  WalkArgs a;
-  a.target = target;
-  a.N = N;
-  a.Bp1 = Bp1;
-  a.L = L;
-  a.S = (int)S;
-  a.G = (int)G;
-  a.V = V;
-  a.node_token = node_token;
-  a.parent = parent;
-  a.depth = depth;
-  a.n_nodes = n_nodes;
-  a.temperature = temperature;
-  a.seed = seed;
-  a.tau = tau;
-  a.out_tokens = out_tokens;
-  a.path_nodes = path_nodes;
-  a.status = status;
-  a.word = reinterpret_cast<uint32_t*>(w + l.word);
-  a.cut = reinterpret_cast<double*>(w + l.cut);
-  a.done = reinterpret_cast<int32_t*>(w + l.done);
-  a.py1 = reinterpret_cast<double*>(w + l.py1);
-  a.py2 = reinterpret_cast<double*>(w + l.py2);
-  a.pi = reinterpret_cast<int32_t*>(w + l.pi);
-  hipLaunchKernelGGL(walk_init_kernel, dim3((N * kMaxRounds + 255) / 256), dim3(256), 0, stream, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  void* args[] = {&a};
-  return hipLaunchCooperativeKernel(fn, dim3((unsigned)(G * S)), dim3(kWalkThreads), args, 0, stream);
+  for (long long n0 = 0; n0 < N; n0 += per_launch) {
+    const int nb = (int)(N - n0 < per_launch ? N - n0 : per_launch);
+    long long G = Gmax < nb ? Gmax : nb;
+    WalkArgs a;
+    a.target = static_cast<const char*>(target) + (size_t)n0 * Bp1 * V * (bf16 ? 2 : 4);
+    a.N = nb;
+    a.Bp1 = Bp1;
+    a.L = L;
+    a.S = (int)S;
+    a.G = (int)G;
+    a.V = V;
+    a.node_token = node_token + (size_t)n0 * Bp1;
+    a.parent = parent + (size_t)n0 * Bp1;
+    a.depth = depth + (size_t)n0 * Bp1;
+    a.n_nodes = n_nodes + n0;
+    a.temperature = temperature + n0;
+    a.seed = seed + n0;
+    a.tau = tau + n0;
+    a.out_tokens = out_tokens + (size_t)n0 * (L + 1);
+    a.path_nodes = path_nodes + (size_t)n0 * (L + 1);
+    a.status = status ? status + n0 : nullptr;
+    a.word = reinterpret_cast<uint32_t*>(w + l.word) + n0;
+    a.cut = reinterpret_cast<double*>(w + l.cut) + n0;
+    a.done = reinterpret_cast<int32_t*>(w + l.done) + (size_t)n0 * kMaxRounds;
+    a.py1 = reinterpret_cast<double*>(w + l.py1) + (size_t)n0 * kSlices;
+    a.py2 = reinterpret_cast<double*>(w + l.py2) + (size_t)n0 * kSlices;
+    a.pi = reinterpret_cast<int32_t*>(w + l.pi) + (size_t)n0 * kSlices;
+    hipLaunchKernelGGL(walk_init_kernel, dim3((nb * kMaxRounds + 255) / 256), dim3(256), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    void* args[] = {&a};
+    e = hipLaunchCooperativeKernel(fn, dim3((unsigned)(G * S)), dim3(kWalkThreads), args, 0, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace mfd

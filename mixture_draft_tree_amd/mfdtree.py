@@ -29,7 +29,8 @@ MFD_BF16, MFD_F32 = 0, 1
 MFD_TREE_NONFINITE, MFD_TREE_CAPACITY, MFD_TREE_BAD_TEMPERATURE = 1, 2, 4
 
 EXPORTED = ["mfd_last_error", "mfd_version", "mfd_workspace_size", "mfd_logsoftmax_topk",
-            "mfd_mixture_threshold", "mfd_tree_build", "mfd_tree_mask", "mfd_verify_walk"]
+            "mfd_logsoftmax_topk_mapped", "mfd_mixture_threshold", "mfd_tree_build", "mfd_tree_mask",
+            "mfd_verify_walk"]
 
 _p = ctypes.c_void_p
 _i = ctypes.c_int
@@ -43,6 +44,8 @@ _lib.mfd_workspace_size.restype = _i
 _lib.mfd_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i, ctypes.POINTER(_sz)]
 _lib.mfd_logsoftmax_topk.restype = _i
 _lib.mfd_logsoftmax_topk.argtypes = [_p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p]
+_lib.mfd_logsoftmax_topk_mapped.restype = _i
+_lib.mfd_logsoftmax_topk_mapped.argtypes = [_p, _i, _i, _i, _i, _i, _p, _i, _i, _p, _p, _p, _p, _p, _p]
 _lib.mfd_mixture_threshold.restype = _i
 _lib.mfd_mixture_threshold.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _sz, _p]
 _lib.mfd_tree_build.restype = _i
@@ -132,6 +135,24 @@ def mfd_logsoftmax_topk(logits, k, lse, topk_id, topk_raw, topk_logp=None, statu
     _check(_lib.mfd_logsoftmax_topk(_ptr(logits), _dtype_code(logits), N, K, L, V, k, _ptr(lse), _ptr(topk_id),
                                     _ptr(topk_raw), _ptr(topk_logp), _ptr(status), None, 0,
                                     _stream_handle(stream)), "mfd_logsoftmax_topk")
+
+
+def mfd_logsoftmax_topk_mapped(logits, vocab_map, V_full, k, lse, topk_id, topk_raw, topk_logp=None, status=None,
+                               stream=None):
+    """logits [N, K, L, V] over a drafting vocabulary; vocab_map [V] int32 (increasing
+    full-vocabulary ids) -> lse [N, K, L] fp64, topk_* [N, K, L, k] with full ids."""
+    if logits.dim() != 4 or not logits.is_contiguous() or logits.device.type != "cuda":
+        raise ValueError("logits must be a contiguous [N, K, L, V] GPU tensor")
+    N, K, L, V = logits.shape
+    _want(vocab_map, "vocab_map", torch.int32, (V,))
+    _want(lse, "lse", torch.float64, (N, K, L))
+    _want(topk_id, "topk_id", torch.int32, (N, K, L, k))
+    _want(topk_raw, "topk_raw", torch.float32, (N, K, L, k))
+    _want(topk_logp, "topk_logp", torch.float32, (N, K, L, k), optional=True)
+    _want(status, "status", torch.int32, (N,), optional=True)
+    _check(_lib.mfd_logsoftmax_topk_mapped(_ptr(logits), _dtype_code(logits), N, K, L, V, _ptr(vocab_map), V_full, k,
+                                           _ptr(lse), _ptr(topk_id), _ptr(topk_raw), _ptr(topk_logp), _ptr(status),
+                                           _stream_handle(stream)), "mfd_logsoftmax_topk_mapped")
 
 
 def mfd_mixture_threshold(topk_id, topk_raw, lse, B, cutoff, n_select, per_mode_kept=None, status=None,

@@ -44,8 +44,13 @@ class MixtureTreePath:
     """Buffers for N trees of shape (K, L, V, B) and the calls that fill them."""
 
     def __init__(self, N: int, K: int, L: int, V: int, B: int, device="cuda", k: Optional[int] = None,
-                 with_logp: bool = False, with_dense_mask: bool = False):
+                 with_logp: bool = False, with_dense_mask: bool = False,
+                 vocab_map: Optional[torch.Tensor] = None, V_full: Optional[int] = None):
+        """V is the drafting vocabulary; with `vocab_map` ([V] int32, increasing ids in a
+        vocabulary of V_full tokens) the tree is built in full-vocabulary ids."""
         self.N, self.K, self.L, self.V, self.B = N, K, L, V, B
+        self.vocab_map = vocab_map
+        self.V_full = V if V_full is None else V_full
         self.k = min(B, V) if k is None else k
         if self.k < 1:
             self.k = 1
@@ -83,7 +88,12 @@ class MixtureTreePath:
 
     def logsoftmax_topk(self, logits, stream=None):
         b = self.buf
-        M.mfd_logsoftmax_topk(logits, self.k, b.lse, b.topk_id, b.topk_raw, b.topk_logp, b.status, stream=stream)
+        if self.vocab_map is not None:
+            M.mfd_logsoftmax_topk_mapped(logits, self.vocab_map, self.V_full, self.k, b.lse, b.topk_id, b.topk_raw,
+                                         b.topk_logp, b.status, stream=stream)
+        else:
+            M.mfd_logsoftmax_topk(logits, self.k, b.lse, b.topk_id, b.topk_raw, b.topk_logp, b.status,
+                                  stream=stream)
 
     def mixture_threshold(self, stream=None):
         b = self.buf

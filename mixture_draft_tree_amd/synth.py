@@ -31,6 +31,13 @@ Seven named workloads:
   stress        K=16, L=15, V=248320, B=1024  bf16, heavy exact ties
   deep          K=8,  L=15, V=151936, B=256   bf16, one tree, confident drafter
   batched_deep  64 trees of the `deep` shape, T alternating 0 / 1
+  subset        as `single`, drafting over a 65536-token subset of the V tokens
+  batched_subset  64 trees of the `subset` shape
+
+The subset workloads draft over a sorted random subset of 65536 of the 151936
+target tokens (the project page's serving setup drafts over the target's 64K
+most frequent tokens and verifies over the full vocabulary): drafter logits
+cover the subset, futures are drawn from it, target rows cover all V tokens.
 
 Every draw comes from a torch.Generator seeded from (workload id, tree index,
 base seed), on the device the caller names, so a given (device, seed) always
@@ -64,6 +71,7 @@ class Workload:
     alt_n: int = 0        # per (mode, position) row: alternative tokens given a Zipf bump ...
     alt_height: float = 0.0  # ... of alt_height * r^-1.1, r = 1..alt_n
     dev_lo: int = 0       # target leaves the chosen future at a depth D ~ U{dev_lo..L} (0: never)
+    v_draft: int = 0      # drafting vocabulary: a sorted random subset of this many of the V tokens (0: all)
 
 
 WORKLOADS = {
@@ -76,6 +84,10 @@ WORKLOADS = {
                      jitter=1.5, alt_n=16, alt_height=10.0, dev_lo=3),
     "batched_deep": Workload("batched_deep", 7, 8, 15, 151936, 256, 64, torch.bfloat16, 2.0, 16.0, 16.0,
                              (0.0, 1.0), jitter=1.5, alt_n=16, alt_height=10.0, dev_lo=3),
+    "subset": Workload("subset", 8, 8, 15, 151936, 256, 1, torch.bfloat16, 3.0, 8.0, 10.0, (0.0, 1.0),
+                       v_draft=65536),
+    "batched_subset": Workload("batched_subset", 9, 8, 15, 151936, 256, 64, torch.bfloat16, 3.0, 8.0, 10.0,
+                               (0.0, 1.0), v_draft=65536),
 }
 
 
@@ -121,6 +133,7 @@ class DraftBatch:
     temperature: torch.Tensor   # [N] float32
     seed: torch.Tensor          # [N] uint64 stored as int64 (two's complement)
     tree_seeds: list            # python ints, one per tree
+    vocab_map: Optional[torch.Tensor] = None  # [v_draft] int32 full ids (sorted) of the drafting tokens
 
 
 def _tiny_tree(w, g, device):
@@ -223,11 +236,23 @@ def _mixture_tree(w, g, device, ties: bool):
     return x, fut
 
 
+def vocab_subset(w: Workload, base_seed: int = 0, device="cpu") -> Optional[torch.Tensor]:
+    """The workload's drafting vocabulary: v_draft sorted distinct ids of [0, V), seeded."""
+    if not w.v_draft:
+        return None
+    g = _gen(device, tree_seed(w.wid + 200, 0, base_seed))
+    ids = torch.randperm(w.V, generator=g, device=device)[:w.v_draft]
+    return torch.sort(ids).values.to(torch.int32)
+
+
 def draft_batch(name: str, base_seed: int = 0, device="cpu", N: Optional[int] = None) -> DraftBatch:
-    """Drafter logits and per-tree metadata for workload `name`."""
+    """Drafter logits and per-tree metadata for workload `name` (over the drafting
+    vocabulary when the workload has one; futures are then reported as full ids)."""
     w = WORKLOADS[name]
     N = w.N if N is None else N
-    logits = torch.empty((N, w.K, w.L, w.V), dtype=w.dtype, device=device)
+    vmap = vocab_subset(w, base_seed, device)
+    wd = dataclasses.replace(w, V=w.v_draft) if w.v_draft else w
+    logits = torch.empty((N, w.K, w.L, wd.V), dtype=w.dtype, device=device)
     futs, chosen, anchors, seeds = [], [], [], []
     for n in range(N):
         s = tree_seed(w.wid, n, base_seed)
@@ -238,7 +263,9 @@ def draft_batch(name: str, base_seed: int = 0, device="cpu", N: Optional[int] = 
         elif name == "product":
             x, fut = _product_tree(w, g, device)
         else:
-            x, fut = _mixture_tree(w, g, device, ties=(name == "stress"))
+            x, fut = _mixture_tree(wd, g, device, ties=(name == "stress"))
+            if vmap is not None:
+                fut = vmap.to(torch.int64)[fut]
         logits[n] = x.to(w.dtype)
         futs.append(fut)
         chosen.append(int(_randint(g, fut.shape[0], (1,), device).item()))
@@ -250,7 +277,7 @@ def draft_batch(name: str, base_seed: int = 0, device="cpu", N: Optional[int] = 
         chosen_mode=torch.tensor(chosen, dtype=torch.int64),
         anchor=torch.tensor(anchors, dtype=torch.int32),
         pos_base=torch.tensor([1000 + 17 * n for n in range(N)], dtype=torch.int64),
-        temperature=temps, seed=seed_t, tree_seeds=seeds)
+        temperature=temps, seed=seed_t, tree_seeds=seeds, vocab_map=vmap)
 
 
 def target_logits(batch: DraftBatch, depth: torch.Tensor, n_nodes: torch.Tensor,

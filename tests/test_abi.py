@@ -74,6 +74,25 @@ def test_logsoftmax_topk_rejects(kw, code):
     assert M.last_error() != ""
 
 
+def _lsm_mapped(N=1, K=2, L=3, V=1000, vmap=FAKE, V_full=5000, k=10, dt=M.MFD_BF16):
+    return M._lib.mfd_logsoftmax_topk_mapped(FAKE, dt, N, K, L, V, vmap, V_full, k, FAKE, FAKE, FAKE, None, None,
+                                             None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(V_full=999), M.MFD_ERR_INVALID_ARG), (dict(V_full=1 << 20), M.MFD_ERR_INVALID_ARG),
+    (dict(vmap=None), M.MFD_ERR_INVALID_ARG), (dict(k=1001), M.MFD_ERR_INVALID_ARG),
+    (dict(dt=7), M.MFD_ERR_DTYPE),
+])
+def test_logsoftmax_topk_mapped_rejects(kw, code):
+    assert _lsm_mapped(**kw) == code
+    assert M.last_error() != ""
+
+
+def test_logsoftmax_topk_mapped_zero_trees():
+    assert _lsm_mapped(N=0, vmap=None) == M.MFD_OK
+
+
 def test_zero_trees_is_a_no_op():
     assert _lsm(N=0, logits=None, lse=None, tid=None, raw=None) == M.MFD_OK
 

@@ -321,7 +321,8 @@ def _run_workload(name, N=None, sample=None, device_gen="cpu"):
     b = synth.draft_batch(name, device=device_gen, N=N)
     N = b.logits.shape[0]
     logits = b.logits.cuda()
-    P = MixtureTreePath(N, w.K, w.L, w.V, w.B, with_logp=True)
+    vmap = None if b.vocab_map is None else b.vocab_map.cuda()
+    P = MixtureTreePath(N, w.K, w.L, logits.shape[-1], w.B, with_logp=True, vocab_map=vmap, V_full=w.V)
     anchor, pos = b.anchor.cuda(), b.pos_base.cuda()
     say(f"[{name}] build N={N}")
     P.build(logits, anchor, pos)
@@ -331,6 +332,11 @@ def _run_workload(name, N=None, sample=None, device_gen="cpu"):
     trees, results = {}, {}
     for n in sample:
         x_cpu = b.logits[n].cpu()
+        if b.vocab_map is not None:
+            # the oracle sees full-vocabulary rows, -inf outside the drafting subset
+            x_full = torch.full((w.K, w.L, w.V), float("-inf"), dtype=torch.float32)
+            x_full[:, :, b.vocab_map.cpu().long()] = x_cpu.float()
+            x_cpu = x_full
         x64 = x_cpu.double().numpy()
         check_lsm(x_cpu[None], P.buf.lse[n:n + 1], P.buf.topk_id[n:n + 1], P.buf.topk_raw[n:n + 1], P.k,
                   P.buf.topk_logp[n:n + 1])
@@ -406,6 +412,15 @@ def test_workload_deep():
 
 def test_workload_batched_deep_sampled():
     _run_workload("batched_deep", sample=[0, 1, 22, 63], device_gen="cuda")
+
+
+def test_workload_subset():
+    """Drafting over a 65536-token subset, tree in full ids, walk over the full vocabulary."""
+    _run_workload("subset")
+
+
+def test_workload_batched_subset_sampled():
+    _run_workload("batched_subset", sample=[0, 5, 63], device_gen="cuda")
 
 
 def test_determinism_and_batch_order():

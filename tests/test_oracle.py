@@ -194,6 +194,35 @@ def test_shift_invariance():
     assert max(abs(a.S[t] - b.S[t]) for t in a.selected) < 1e-12
 
 
+@pytest.mark.parametrize("seed", range(3))
+def test_drafting_subset_equals_full_vocab_with_neginf(seed):
+    """A drafting vocabulary that is a sorted subset of the target's: the tree
+    over the subset's logits, relabelled to full ids, is the tree over full-
+    vocabulary logits that are -inf outside the subset (same normalisers, same
+    ranks, ties by full id), so drafting over the subset and verifying over
+    the full vocabulary stays consistent (project page, "In a serving
+    engine")."""
+    rng = np.random.default_rng(40 + seed)
+    K, L, V_full, Vd, B = 3, 4, 40, 16, 25
+    vmap = np.sort(rng.choice(V_full, size=Vd, replace=False))
+    x_sub = rng.integers(-3, 4, size=(K, L, Vd)).astype(np.float64)  # integer logits: many exact ties
+    x_full = np.full((K, L, V_full), -np.inf)
+    x_full[:, :, vmap] = x_sub
+    lse_sub = O.lse_rows(x_sub.reshape(-1, Vd))
+    lse_full = O.lse_rows(x_full.reshape(-1, V_full))
+    # equal up to summation order (numpy sums the longer row in other blocks)
+    assert np.max(np.abs(lse_sub - lse_full)) < 1e-12
+    for r in range(K * L):
+        ranks_sub = vmap[O.rank_order(x_sub.reshape(-1, Vd)[r], Vd)]
+        ranks_full = O.rank_order(x_full.reshape(-1, V_full)[r], Vd)
+        assert np.array_equal(ranks_sub, ranks_full)
+    a = O.mixture_select_heap(x_sub, B)
+    b = O.mixture_select_heap(x_full, B)
+    relabel = {tuple(int(vmap[t]) for t in p) for p in a.selected}
+    assert relabel == set(b.selected)
+    assert abs(a.cutoff - b.cutoff) < 1e-12
+
+
 def test_budget_edges():
     rng = np.random.default_rng(7)
     x = _rand_logits(rng, 2, 3, 4)
