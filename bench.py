@@ -26,9 +26,8 @@ import torch
 METRIC = "mixture trees built+verified/sec (K=8,L=15,B=256,V=152K); logits HBM GB/s"
 HBM_PEAK_GBS = 8000.0
 HERE = os.path.dirname(os.path.abspath(__file__))
-# Sources of the logits kernel: a traffic figure measured on other sources is stale.
-LSM_SOURCES = ["mixture_draft_tree_amd/csrc/lsm_topk.hip", "mixture_draft_tree_amd/csrc/mfd_device.hpp",
-               "mixture_draft_tree_amd/csrc/mfd_launch.hpp"]
+# Sources of the logits kernel's code: a traffic figure measured on other code is stale.
+LSM_SOURCES = ["mixture_draft_tree_amd/csrc/lsm_topk.hip", "mixture_draft_tree_amd/csrc/mfd_device.hpp"]
 TRAFFIC_FILE = "profiles/lsm_topk_kernel_batched_64x8x15x151936_hbm_traffic.txt"
 
 
@@ -174,7 +173,27 @@ def single_tree_latency(seed, steps, stream, name="single"):
 STAGES = ["logsoftmax_topk", "mixture_threshold", "tree_build", "tree_mask", "verify_walk"]
 
 
-def timed_workload(name, seed, steps, warmup, stream):
+def covered_mass_stats(P, R, temps, stream, reps=5):
+    """Time mfd_covered_mass over the built trees; mean covered mass next to the
+    walks' mean accepted count (the two agree in expectation)."""
+    from mixture_draft_tree_amd import mfdtree as M
+    N = R.shape[0]
+    mass = torch.empty(N, dtype=torch.float64, device="cuda")
+    ws = M.covered_mass_workspace(N, R.shape[1])
+    args = (R, P.buf.node_token, P.buf.parent, P.buf.n_nodes, temps, mass)
+    M.mfd_covered_mass(*args, ws=ws, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        M.mfd_covered_mass(*args, ws=ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return {"covered_mass_ms": e0.elapsed_time(e1) / reps, "mean_covered_mass": float(mass.mean()),
+            "mean_accepted_walk": float((P.buf.tau - 1).float().mean())}
+
+
+def timed_workload(name, seed, steps, warmup, stream, diagnostics=False):
     """Whole steps on workload `name`: (ms per step, per-stage ms, N, buffers)."""
     w, N, P, logits, anchor, pos, temps, seeds, R = setup(name, seed, "cuda")
     total_ms, ev = run_steps(P, logits, anchor, pos, R, temps, seeds, steps, warmup, stream)
@@ -182,6 +201,8 @@ def timed_workload(name, seed, steps, warmup, stream):
              for i, nm in enumerate(STAGES)}
     status = P.buf.status.cpu()
     assert int(status.abs().sum()) == 0, f"per-tree status flags set ({name}): {status.tolist()}"
+    if diagnostics:
+        stage["diagnostics"] = covered_mass_stats(P, R, temps, stream)
     return total_ms / steps, stage, N, w, P, logits
 
 
@@ -194,7 +215,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     name = args.workload
     stream = torch.cuda.current_stream()
-    ms_per_step, stage_ms, N, w, P, logits = timed_workload(name, args.seed, args.steps, args.warmup, stream)
+    ms_per_step, stage_ms, N, w, P, logits = timed_workload(name, args.seed, args.steps, args.warmup, stream,
+                                                            diagnostics=True)
+    diag = stage_ms.pop("diagnostics")
 
     logits_bytes = N * w.K * w.L * w.V * logits.element_size()
     lsm_ms = stage_ms["logsoftmax_topk"]
@@ -225,12 +248,15 @@ def main():
         "per_tree_latency_ms": ms_per_step if N == 1 else None,
         "single_tree_latency_ms": None,
         "tau_mean": float(tau.mean()),
+        "diagnostics": diag,
     }
     if args.latency_steps > 0 and name != "single":
         out["single_tree_latency_ms"] = single_tree_latency(args.seed, args.latency_steps, stream)
     if args.deep_workload != "none" and name == "batched":
         del P, logits
-        dms, dstage, dN, dw, dP, _ = timed_workload(args.deep_workload, args.seed, args.steps, args.warmup, stream)
+        dms, dstage, dN, dw, dP, _ = timed_workload(args.deep_workload, args.seed, args.steps, args.warmup, stream,
+                                                    diagnostics=True)
+        ddiag = dstage.pop("diagnostics")
         out["deep"] = {
             "workload": f"{args.deep_workload}: {dN} trees, K={dw.K}, L={dw.L}, V={dw.V}, B={dw.B}, "
                         f"T pattern {list(dw.temperatures)}",
@@ -240,6 +266,7 @@ def main():
             "tau_mean": float(dP.buf.tau.cpu().float().mean()),
             "single_tree_latency_ms": (single_tree_latency(args.seed, args.latency_steps, stream, "deep")
                                        if args.latency_steps > 0 else None),
+            "diagnostics": ddiag,
         }
     if args.subset_workload != "none" and name == "batched":
         sms, sstage, sN, sw, sP, slog = timed_workload(args.subset_workload, args.seed, args.steps, args.warmup,

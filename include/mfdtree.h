@@ -78,7 +78,8 @@ typedef enum mfd_op {
   MFD_OP_MIXTURE_THRESHOLD = 1,
   MFD_OP_TREE_BUILD = 2,
   MFD_OP_TREE_MASK = 3,
-  MFD_OP_VERIFY_WALK = 4
+  MFD_OP_VERIFY_WALK = 4,
+  MFD_OP_COVERED_MASS = 5
 } mfd_op;
 
 #define MFD_TREE_NONFINITE 1
@@ -251,6 +252,49 @@ mfd_status mfd_verify_walk(const void* target_logits, mfd_dtype dtype, int N, in
                            const int32_t* n_nodes, const float* temperature, const uint64_t* seed,
                            int32_t* tau, int32_t* out_tokens, int32_t* path_nodes, int32_t* status,
                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Covered target mass of each tree (project page, "Abstract": under tree
+ * verification the expected number of accepted drafted tokens is the
+ * probability mass the tree covers).  For tree n at temperature T = T[n]:
+ *     mass[n] = sum over drafted nodes v of  prod over the edges (u -> w) on
+ *               the path root .. v of  p_T(token(w) | row u),
+ *     p_T(t | u) = exp(R[u, t] / T) / sum_v exp(R[u, v] / T)      (T > 0),
+ *     p_0(t | u) = 1 if t is the lowest-id argmax of R[u, :], else 0.
+ * At T = 0 the mass is the greedy walk's number of accepted drafted tokens.
+ *
+ *   target_logits device [N, Bp1, V] bf16 or fp32: the rows of the nodes that
+ *             have a child are read (twice at T > 0, once at T = 0).
+ *   node_token, parent, n_nodes  the tree (any node order; a parent outside
+ *             the tree, or a token outside [0, V), makes the mass NaN).
+ *   temperature device [N] fp32; T < 0 or not finite gives NaN and
+ *             MFD_TREE_BAD_TEMPERATURE in status (if not NULL).
+ *   mass      device [N] fp64 out.
+ *   ws        device workspace of mfd_workspace_size(MFD_OP_COVERED_MASS, N,
+ *             0, 0, 0, Bp1 - 1) bytes (per-node normalisers).
+ * N is at most 65535.  Row probabilities use fp32 exponentials summed in fp64
+ * (relative error about 1e-7 per edge).
+ */
+mfd_status mfd_covered_mass(const void* target_logits, mfd_dtype dtype, int N, int Bp1, int V,
+                            const int32_t* node_token, const int32_t* parent, const int32_t* n_nodes,
+                            const float* temperature, double* mass, int32_t* status, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/*
+ * Chimeras of each tree relative to two futures (project page, "TL;DR" and
+ * "Abstract": prefixes stitched together from different futures, which the
+ * target never produces).  count[n] = number of drafted nodes whose token at
+ * every depth d is future_a[n][d-1] or future_b[n][d-1] while their path is a
+ * prefix of neither future.
+ *
+ *   node_token, parent, depth, n_nodes  the tree (depth d in [1, L] for drafted
+ *             nodes; a node whose path leaves the tree or [1, L] is not counted).
+ *   future_a, future_b  device [N, L] int32.
+ *   count     device [N] int32 out.
+ */
+mfd_status mfd_chimera_count(const int32_t* node_token, const int32_t* parent, const int32_t* depth,
+                             const int32_t* n_nodes, int N, int Bp1, int L, const int32_t* future_a,
+                             const int32_t* future_b, int32_t* count, hipStream_t stream);
 
 #ifdef __cplusplus
 }

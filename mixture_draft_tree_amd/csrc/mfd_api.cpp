@@ -75,6 +75,11 @@ mfd_status mfd_workspace_size(mfd_op op, int N, int K, int L, int V, int B, size
       if (N < 0) return fail(MFD_ERR_INVALID_ARG, "N must be >= 0 (got %d)", N);
       *bytes = N == 0 ? 0 : mfd::walk_ws_bytes(N);
       return ok();
+    case MFD_OP_COVERED_MASS:
+      if (N < 0) return fail(MFD_ERR_INVALID_ARG, "N must be >= 0 (got %d)", N);
+      if (B < 0 || B > kMaxB) return fail(MFD_ERR_INVALID_ARG, "B must be in [0, %d] (got %d)", kMaxB, B);
+      *bytes = N == 0 ? 0 : mfd::covered_mass_ws_bytes(N, B + 1);
+      return ok();
     case MFD_OP_MIXTURE_THRESHOLD:
     case MFD_OP_TREE_BUILD: {
       mfd_status s = check_dims(N, K, L, V);
@@ -224,6 +229,51 @@ mfd_status mfd_verify_walk(const void* target_logits, mfd_dtype dtype, int N, in
   return from_hip(mfd::launch_verify_walk(target_logits, dtype == MFD_BF16, N, Bp1, V, L, node_token, parent, depth,
                                           n_nodes, temperature, seed, tau, out_tokens, path_nodes, status, ws, stream),
                   "mfd_verify_walk launch");
+}
+
+mfd_status mfd_covered_mass(const void* target_logits, mfd_dtype dtype, int N, int Bp1, int V,
+                            const int32_t* node_token, const int32_t* parent, const int32_t* n_nodes,
+                            const float* temperature, double* mass, int32_t* status, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  if (N < 0 || N > 65535) return fail(MFD_ERR_INVALID_ARG, "N must be in [0, 65535] (got %d)", N);
+  if (Bp1 < 1 || Bp1 > kMaxB + 1) return fail(MFD_ERR_INVALID_ARG, "Bp1 must be in [1, %d] (got %d)", kMaxB + 1, Bp1);
+  if (V < 1 || V > kMaxV) return fail(MFD_ERR_INVALID_ARG, "V must be in [1, %d] (got %d)", kMaxV, V);
+  if (dtype != MFD_BF16 && dtype != MFD_F32) return fail(MFD_ERR_DTYPE, "dtype must be MFD_BF16 or MFD_F32");
+  if (N == 0) return ok();
+  REQUIRE_PTR(target_logits);
+  REQUIRE_PTR(node_token);
+  REQUIRE_PTR(parent);
+  REQUIRE_PTR(n_nodes);
+  REQUIRE_PTR(temperature);
+  REQUIRE_PTR(mass);
+  const size_t esz = dtype == MFD_BF16 ? 2 : 4;
+  if (reinterpret_cast<uintptr_t>(target_logits) % esz)
+    return fail(MFD_ERR_INVALID_ARG, "target_logits not aligned to its element size");
+  const size_t need = mfd::covered_mass_ws_bytes(N, Bp1);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(MFD_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws == nullptr ? (size_t)0 : ws_bytes);
+  return from_hip(mfd::launch_covered_mass(target_logits, dtype == MFD_BF16, N, Bp1, V, node_token, parent, n_nodes,
+                                           temperature, mass, status, ws, stream),
+                  "mfd_covered_mass launch");
+}
+
+mfd_status mfd_chimera_count(const int32_t* node_token, const int32_t* parent, const int32_t* depth,
+                             const int32_t* n_nodes, int N, int Bp1, int L, const int32_t* future_a,
+                             const int32_t* future_b, int32_t* count, hipStream_t stream) {
+  if (N < 0) return fail(MFD_ERR_INVALID_ARG, "N must be >= 0 (got %d)", N);
+  if (Bp1 < 1 || Bp1 > kMaxB + 1) return fail(MFD_ERR_INVALID_ARG, "Bp1 must be in [1, %d] (got %d)", kMaxB + 1, Bp1);
+  if (L < 1 || L > kMaxL) return fail(MFD_ERR_INVALID_ARG, "L must be in [1, %d] (got %d)", kMaxL, L);
+  if (N == 0) return ok();
+  REQUIRE_PTR(node_token);
+  REQUIRE_PTR(parent);
+  REQUIRE_PTR(depth);
+  REQUIRE_PTR(n_nodes);
+  REQUIRE_PTR(future_a);
+  REQUIRE_PTR(future_b);
+  REQUIRE_PTR(count);
+  return from_hip(mfd::launch_chimera_count(node_token, parent, depth, n_nodes, N, Bp1, L, future_a, future_b, count,
+                                            stream),
+                  "mfd_chimera_count launch");
 }
 
 }  // extern "C"

@@ -42,6 +42,15 @@ hipError_t launch_tree_mask(const int32_t* parent, const int32_t* depth, const i
 
 size_t walk_ws_bytes(int N);
 
+size_t covered_mass_ws_bytes(int N, int Bp1);
+hipError_t launch_covered_mass(const void* target, bool bf16, int N, int Bp1, long long V,
+                               const int32_t* node_token, const int32_t* parent, const int32_t* n_nodes,
+                               const float* temperature, double* mass, int32_t* status, void* ws,
+                               hipStream_t stream);
+hipError_t launch_chimera_count(const int32_t* node_token, const int32_t* parent, const int32_t* depth,
+                                const int32_t* n_nodes, int N, int Bp1, int L, const int32_t* future_a,
+                                const int32_t* future_b, int32_t* count, hipStream_t stream);
+
 hipError_t launch_verify_walk(const void* target, bool bf16, int N, int Bp1, long long V, int L,
                               const int32_t* node_token, const int32_t* parent, const int32_t* depth,
                               const int32_t* n_nodes, const float* temperature, const uint64_t* seed, int32_t* tau,

@@ -25,12 +25,12 @@ _lib = ctypes.CDLL(LIB_PATH)
 MFD_OK, MFD_ERR_INVALID_ARG, MFD_ERR_DTYPE, MFD_ERR_WORKSPACE, MFD_ERR_DEVICE = 0, 1, 2, 3, 4
 MFD_BF16, MFD_F32 = 0, 1
 (MFD_OP_LOGSOFTMAX_TOPK, MFD_OP_MIXTURE_THRESHOLD, MFD_OP_TREE_BUILD,
- MFD_OP_TREE_MASK, MFD_OP_VERIFY_WALK) = range(5)
+ MFD_OP_TREE_MASK, MFD_OP_VERIFY_WALK, MFD_OP_COVERED_MASS) = range(6)
 MFD_TREE_NONFINITE, MFD_TREE_CAPACITY, MFD_TREE_BAD_TEMPERATURE = 1, 2, 4
 
 EXPORTED = ["mfd_last_error", "mfd_version", "mfd_workspace_size", "mfd_logsoftmax_topk",
             "mfd_logsoftmax_topk_mapped", "mfd_mixture_threshold", "mfd_tree_build", "mfd_tree_mask",
-            "mfd_verify_walk"]
+            "mfd_verify_walk", "mfd_covered_mass", "mfd_chimera_count"]
 
 _p = ctypes.c_void_p
 _i = ctypes.c_int
@@ -53,6 +53,10 @@ _lib.mfd_tree_build.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i,
                                 _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]
 _lib.mfd_tree_mask.restype = _i
 _lib.mfd_tree_mask.argtypes = [_p, _p, _p, _p, _i, _i, _p, _p, _p, _p]
+_lib.mfd_covered_mass.restype = _i
+_lib.mfd_covered_mass.argtypes = [_p, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _sz, _p]
+_lib.mfd_chimera_count.restype = _i
+_lib.mfd_chimera_count.argtypes = [_p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p]
 _lib.mfd_verify_walk.restype = _i
 _lib.mfd_verify_walk.argtypes = [_p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]
 
@@ -228,3 +232,43 @@ def mfd_verify_walk(target_logits, L, node_token, parent, depth, n_nodes, temper
                                 _ptr(parent), _ptr(depth), _ptr(n_nodes), _ptr(temperature), _ptr(seed), _ptr(tau),
                                 _ptr(out_tokens), _ptr(path_nodes), _ptr(status), _ptr(ws), ws_bytes,
                                 _stream_handle(stream)), "mfd_verify_walk")
+
+
+def covered_mass_workspace(N: int, Bp1: int, device="cuda") -> torch.Tensor:
+    """A device workspace for mfd_covered_mass on N trees of Bp1 rows."""
+    n = workspace_size(MFD_OP_COVERED_MASS, N, 0, 0, 0, Bp1 - 1)
+    return torch.empty((max(n, 8) + 7) // 8, dtype=torch.int64, device=device)
+
+
+def mfd_covered_mass(target_logits, node_token, parent, n_nodes, temperature, mass, status=None, ws=None,
+                     stream=None):
+    """Expected accepted drafted tokens per tree: target_logits [N, B+1, V] -> mass [N] fp64."""
+    if target_logits.dim() != 3 or not target_logits.is_contiguous() or target_logits.device.type != "cuda":
+        raise ValueError("target_logits must be a contiguous [N, B+1, V] GPU tensor")
+    N, Bp1, V = target_logits.shape
+    for name, t in (("node_token", node_token), ("parent", parent)):
+        _want(t, name, torch.int32, (N, Bp1))
+    _want(n_nodes, "n_nodes", torch.int32, (N,))
+    _want(temperature, "temperature", torch.float32, (N,))
+    _want(mass, "mass", torch.float64, (N,))
+    _want(status, "status", torch.int32, (N,), optional=True)
+    if ws is None:
+        ws = covered_mass_workspace(N, Bp1, target_logits.device)
+    ws_bytes = ws.numel() * ws.element_size()
+    _check(_lib.mfd_covered_mass(_ptr(target_logits), _dtype_code(target_logits), N, Bp1, V, _ptr(node_token),
+                                 _ptr(parent), _ptr(n_nodes), _ptr(temperature), _ptr(mass), _ptr(status), _ptr(ws),
+                                 ws_bytes, _stream_handle(stream)), "mfd_covered_mass")
+
+
+def mfd_chimera_count(node_token, parent, depth, n_nodes, L, future_a, future_b, count, stream=None):
+    """Chimeras per tree relative to two futures [N, L] -> count [N] int32."""
+    N, Bp1 = node_token.shape
+    for name, t in (("node_token", node_token), ("parent", parent), ("depth", depth)):
+        _want(t, name, torch.int32, (N, Bp1))
+    _want(n_nodes, "n_nodes", torch.int32, (N,))
+    _want(future_a, "future_a", torch.int32, (N, L))
+    _want(future_b, "future_b", torch.int32, (N, L))
+    _want(count, "count", torch.int32, (N,))
+    _check(_lib.mfd_chimera_count(_ptr(node_token), _ptr(parent), _ptr(depth), _ptr(n_nodes), N, Bp1, L,
+                                  _ptr(future_a), _ptr(future_b), _ptr(count), _stream_handle(stream)),
+           "mfd_chimera_count")

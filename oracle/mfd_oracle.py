@@ -577,17 +577,22 @@ def verify_walk(node_token, parent, depth, n_nodes: int, R: np.ndarray, T: float
 def covered_mass(node_token, parent, n_nodes: int, R: np.ndarray, T: float) -> float:
     """Sum over drafted nodes of the target probability of reaching them
     ([PP] "Abstract": under tree verification the expected number of accepted
-    tokens equals the probability mass the tree covers)."""
+    tokens equals the probability mass the tree covers).  At T = 0 the target's
+    token at a node is its argmax (lowest id among equal maxima, as in the
+    walk), taken with probability one.  Parents must precede their children."""
     R = np.asarray(R, dtype=np.float64)
     reach = np.zeros(n_nodes)
     reach[0] = 1.0
     total = 0.0
     for i in range(1, n_nodes):
         p = int(parent[i])
-        z = R[p] / T
-        z = z - z.max()
-        prob = np.exp(z) / np.exp(z).sum()
-        reach[i] = reach[p] * prob[int(node_token[i])]
+        if T == 0:
+            prob_t = 1.0 if int(np.argmax(R[p])) == int(node_token[i]) else 0.0
+        else:
+            z = R[p] / T
+            z = z - z.max()
+            prob_t = (np.exp(z) / np.exp(z).sum())[int(node_token[i])]
+        reach[i] = reach[p] * prob_t
         total += reach[i]
     return total
 

@@ -93,6 +93,31 @@ def test_logsoftmax_topk_mapped_zero_trees():
     assert _lsm_mapped(N=0, vmap=None) == M.MFD_OK
 
 
+def _mass(N=2, Bp1=9, V=16, dt=M.MFD_BF16, ws=FAKE, ws_bytes=1 << 20, mass=FAKE):
+    return M._lib.mfd_covered_mass(FAKE, dt, N, Bp1, V, FAKE, FAKE, FAKE, FAKE, mass, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=70000), M.MFD_ERR_INVALID_ARG), (dict(Bp1=0), M.MFD_ERR_INVALID_ARG), (dict(V=0), M.MFD_ERR_INVALID_ARG),
+    (dict(dt=9), M.MFD_ERR_DTYPE), (dict(ws=None), M.MFD_ERR_WORKSPACE), (dict(ws_bytes=8), M.MFD_ERR_WORKSPACE),
+    (dict(mass=None), M.MFD_ERR_INVALID_ARG),
+])
+def test_covered_mass_rejects(kw, code):
+    assert _mass(**kw) == code
+    assert M.last_error() != ""
+
+
+def test_chimera_count_rejects_and_zero_trees():
+    f = M._lib.mfd_chimera_count
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 9, 0, FAKE, FAKE, FAKE, None) == M.MFD_ERR_INVALID_ARG  # L = 0
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 0, 4, FAKE, FAKE, FAKE, None) == M.MFD_ERR_INVALID_ARG  # Bp1 = 0
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 9, 4, None, FAKE, FAKE, None) == M.MFD_ERR_INVALID_ARG
+    assert f(None, None, None, None, 0, 9, 4, None, None, None, None) == M.MFD_OK
+    assert _mass(N=0, ws=None, mass=None) == M.MFD_OK
+    n = M.workspace_size(M.MFD_OP_COVERED_MASS, 3, 0, 0, 0, 8)
+    assert n >= 3 * 9 * 12
+
+
 def test_zero_trees_is_a_no_op():
     assert _lsm(N=0, logits=None, lse=None, tid=None, raw=None) == M.MFD_OK
 

@@ -5,6 +5,7 @@ whose cut-off band is not decided by exact comparisons are reported and
 excluded from node-set exactness); log-normalisers within 1e-5, scores within
 1e-4."""
 
+import math
 import sys
 import zlib
 
@@ -437,3 +438,73 @@ def test_determinism_and_batch_order():
                                                                "cutoff", "n_select", "per_mode_kept", "mask_words")])
     for a, c in zip(*outs):
         assert torch.equal(a, c)
+
+
+# ------------------------------------------------------------------ diagnostics (next row f3)
+
+def _oracle_trees(name, N, seed):
+    """Oracle trees, target rows and futures for N trees of workload `name`."""
+    w = synth.WORKLOADS[name]
+    b = synth.draft_batch(name, base_seed=seed, N=N)
+    trees = [O.canonical_tree(O.mixture_select_heap(b.logits[n].double().numpy(), w.B), int(b.anchor[n]), w.B)
+             for n in range(N)]
+    dep = torch.stack([torch.from_numpy(t["depth"]).to(torch.int32) for t in trees])
+    nn = torch.tensor([t["n_nodes"] for t in trees], dtype=torch.int32)
+    R = synth.target_logits(b, dep, nn, base_seed=seed)
+    return w, b, trees, R
+
+
+@pytest.mark.parametrize("name,T,dtype", [("tiny", 0.0, torch.float32), ("tiny", 0.7, torch.float32),
+                                          ("product", 1.0, torch.bfloat16), ("deep", 0.0, torch.bfloat16),
+                                          ("deep", 1.0, torch.bfloat16), ("single", 1.0, torch.bfloat16)])
+def test_covered_mass_parity(name, T, dtype):
+    """Expected accepted tokens (covered target mass) against the oracle, per tree."""
+    N = 2
+    w, b, trees, R = _oracle_trees(name, N, seed=3)
+    say(f"[mass] {name} T={T}")
+    tok, par, dep, nn = upload_tree(trees, w.B + 1)
+    Rg = R.to(dtype).cuda().contiguous()
+    temps = torch.full((N,), T, dtype=torch.float32, device="cuda")
+    mass = torch.empty(N, dtype=torch.float64, device="cuda")
+    M.mfd_covered_mass(Rg, tok, par, nn, temps, mass)
+    torch.cuda.synchronize()
+    for n in range(N):
+        want = O.covered_mass(trees[n]["node_token"], trees[n]["parent"], trees[n]["n_nodes"],
+                              R[n].to(dtype).double().numpy(), T)
+        got = mass[n].item()
+        assert abs(got - want) <= 1e-6 * max(1.0, abs(want)), (n, got, want)
+        if T == 0.0:
+            tau, *_ = O.verify_walk(trees[n]["node_token"], trees[n]["parent"], trees[n]["depth"],
+                                    trees[n]["n_nodes"], R[n].to(dtype).double().numpy(), 0.0, 0, w.L)
+            assert got == tau - 1
+
+
+def test_covered_mass_bad_temperature_and_nan_tree():
+    w, b, trees, R = _oracle_trees("tiny", 2, seed=4)
+    tok, par, dep, nn = upload_tree(trees, w.B + 1)
+    par[1, 1] = w.B + 5  # a parent outside the tree
+    temps = torch.tensor([-1.0, 1.0], dtype=torch.float32, device="cuda")
+    mass = torch.empty(2, dtype=torch.float64, device="cuda")
+    status = torch.zeros(2, dtype=torch.int32, device="cuda")
+    M.mfd_covered_mass(R.cuda().contiguous(), tok, par, nn, temps, mass, status)
+    torch.cuda.synchronize()
+    assert math.isnan(mass[0].item()) and status[0].item() == M.MFD_TREE_BAD_TEMPERATURE
+    assert math.isnan(mass[1].item()) and status[1].item() == 0
+
+
+@pytest.mark.parametrize("name", ["product", "single", "tiny"])
+def test_chimera_count_parity(name):
+    """Chimeras relative to two futures against the oracle's list."""
+    N = 2 if name != "product" else 1
+    w, b, trees, R = _oracle_trees(name, N, seed=5)
+    tok, par, dep, nn = upload_tree(trees, w.B + 1)
+    fa = b.futures[:, 0].to(torch.int32).cuda().contiguous()
+    fb = b.futures[:, 1].to(torch.int32).cuda().contiguous()
+    count = torch.empty(N, dtype=torch.int32, device="cuda")
+    M.mfd_chimera_count(tok, par, dep, nn, w.L, fa, fb, count)
+    torch.cuda.synchronize()
+    for n in range(N):
+        want = len(O.chimera_nodes(trees[n]["prefixes"], b.futures[n, 0].tolist(), b.futures[n, 1].tolist()))
+        assert count[n].item() == want, (n, count[n].item(), want)
+    if name == "product":
+        assert count[0].item() >= 3  # the 2^(m-1)-1 = 3 spliced prefixes at full split depth, at least

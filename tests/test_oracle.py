@@ -491,6 +491,27 @@ def test_walk_expected_accepted_equals_covered_mass():
     assert abs(acc.mean() - mass) < 5 * se + 1e-3
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_covered_mass_greedy_limit(seed):
+    """At T = 0 the target's choices are certain, so the covered mass is the
+    greedy walk's accepted count (project page 'Abstract': expected accepted
+    tokens = covered mass), and it is the T -> 0+ limit of the T > 0 mass."""
+    rng = np.random.default_rng(60 + seed)
+    K, L, V, B = 3, 4, 8, 20
+    x = rng.normal(0, 1, size=(K, L, V))
+    tr = O.canonical_tree(O.mixture_select_heap(x, B), 0, B)
+    R = rng.normal(0, 1, size=(B + 1, V))
+    # make the target follow the tree for a while: boost one drafted child per node
+    for i in range(1, tr["n_nodes"]):
+        if rng.random() < 0.7:
+            R[tr["parent"][i], tr["node_token"][i]] += 4.0
+    m0 = O.covered_mass(tr["node_token"], tr["parent"], tr["n_nodes"], R, 0.0)
+    tau, *_ = O.verify_walk(tr["node_token"], tr["parent"], tr["depth"], tr["n_nodes"], R, 0.0, 0, L)
+    assert m0 == tau - 1
+    m_small = O.covered_mass(tr["node_token"], tr["parent"], tr["n_nodes"], R, 1e-3)
+    assert abs(m_small - m0) < 1e-6
+
+
 def test_band_criterion():
     rng = np.random.default_rng(13)
     x = _rand_logits(rng, 2, 3, 8)
