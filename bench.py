@@ -66,7 +66,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="batched",
-                    choices=["batched", "single", "stress", "deep", "batched_deep", "subset", "batched_subset"])
+                    choices=["batched", "single", "stress", "deep", "batched_deep", "subset", "batched_subset",
+                             "batched_modes"])
     ap.add_argument("--cpu-baseline-trees", type=int, default=2,
                     help="trees of the workload the fp64 oracle is timed on (0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
@@ -79,6 +80,8 @@ def parse():
                     help="also time the confident-drafter batch (deep trees, pages-like acceptance lengths)")
     ap.add_argument("--subset-workload", default="batched_subset", choices=["batched_subset", "none"],
                     help="also time drafting over a 65536-token subset of the vocabulary (walk over all of it)")
+    ap.add_argument("--modes-workload", default="batched_modes", choices=["batched_modes", "none"],
+                    help="also time a batch mixing K_n = 8 and K_n = 1 trees (per-request mode counts)")
     return ap.parse_args()
 
 
@@ -151,7 +154,8 @@ def setup(name, seed, dev):
     b = synth.draft_batch(name, base_seed=seed, device=dev)
     N = b.logits.shape[0]
     vmap = None if b.vocab_map is None else b.vocab_map.to(dev)
-    P = MixtureTreePath(N, w.K, w.L, b.logits.shape[-1], w.B, vocab_map=vmap, V_full=w.V)
+    modes = None if b.modes is None else b.modes.to(dev)
+    P = MixtureTreePath(N, w.K, w.L, b.logits.shape[-1], w.B, vocab_map=vmap, V_full=w.V, modes=modes)
     logits = b.logits.contiguous()
     anchor, pos = b.anchor.to(dev), b.pos_base.to(dev)
     temps, seeds = b.temperature.to(dev), b.seed.to(dev)
@@ -219,7 +223,8 @@ def main():
                                                             diagnostics=True)
     diag = stage_ms.pop("diagnostics")
 
-    logits_bytes = N * w.K * w.L * w.V * logits.element_size()
+    rows = N * w.K * w.L if P.modes is None else int(P.modes.sum()) * w.L   # rows the logits pass reads
+    logits_bytes = rows * logits.shape[-1] * logits.element_size()
     lsm_ms = stage_ms["logsoftmax_topk"]
     achieved = logits_bytes / (lsm_ms * 1e-3) / 1e9
     tau = P.buf.tau.cpu().float()
@@ -281,6 +286,22 @@ def main():
             "algorithmic_bytes_per_launch": sbytes, "tau_mean": float(sP.buf.tau.cpu().float().mean()),
         }
         del sP, slog
+    if args.modes_workload != "none" and name == "batched":
+        mms, mstage, mN, mw, mP, mlog = timed_workload(args.modes_workload, args.seed, args.steps, args.warmup,
+                                                       stream)
+        kn = mP.modes.cpu()
+        mbytes = int(kn.sum()) * mw.L * mw.V * mlog.element_size()
+        mgbs = mbytes / (mstage["logsoftmax_topk"] * 1e-3) / 1e9
+        mtau = mP.buf.tau.cpu().float()
+        out["per_request_modes"] = {
+            "workload": f"{args.modes_workload}: {mN} trees of the confident-drafter shape, K={mw.K}, L={mw.L}, "
+                        f"V={mw.V}, B={mw.B}, K_n cycling {list(mw.modes)}, T pattern {list(mw.temperatures)}",
+            "value": mN / (mms * 1e-3), "unit": "trees/s", "ms_per_step": mms, "stages_ms": mstage,
+            "active_rows": int(kn.sum()) * mw.L, "logits_GBps": mgbs, "logits_frac_of_peak": mgbs / HBM_PEAK_GBS,
+            "algorithmic_bytes_per_launch": mbytes,
+            "tau_mean_by_modes": {str(k): float(mtau[kn == k].mean()) for k in sorted(set(kn.tolist()))},
+        }
+        del mP, mlog
     if args.cpu_baseline_trees > 0:
         out["cpu_baseline"] = cpu_baseline(name, args.seed, args.cpu_baseline_trees)
     print(json.dumps(out), flush=True)

@@ -43,6 +43,8 @@
  *                                 mfd_tree_build); that tree's outputs are
  *                                 not valid
  *       MFD_TREE_BAD_TEMPERATURE  temperature < 0 or not finite
+ *       MFD_TREE_BAD_MODES        a per-tree mode count outside [1, K]
+ *                                 (the *_modes calls; it is clamped)
  *   - Shapes: N trees, K modes, L drafted positions, V vocabulary, B budget
  *     (drafted nodes; the root is extra, so trees have B+1 rows), k = number
  *     of ranked candidates kept per row (use k = min(B, V)).
@@ -85,6 +87,7 @@ typedef enum mfd_op {
 #define MFD_TREE_NONFINITE 1
 #define MFD_TREE_CAPACITY 2
 #define MFD_TREE_BAD_TEMPERATURE 4
+#define MFD_TREE_BAD_MODES 8
 
 /* Message for the last failed call on this host thread ("" if none). */
 const char* mfd_last_error(void);
@@ -197,6 +200,43 @@ mfd_status mfd_tree_build(const int32_t* topk_id, const float* topk_raw, const d
                           int32_t* node_token, int32_t* parent, int32_t* depth, double* score,
                           int32_t* best_mode, int32_t* n_nodes, int32_t* status,
                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Per-request mode count inside one batched launch (project page, "In a
+ * serving engine": the MFD-D configuration runs the same drafter through a
+ * single-mode default path once three or more requests are in flight, and is
+ * the fastest option at every batch size of Figure 5).  Tree n is built from
+ * its first K_n = modes[n] futures only; with K_n = 1 it is the single-future
+ * (product) tree of that one mode.  The buffers keep the [N, K, L, ...]
+ * layout of the calls above, so requests of any mode count share one launch.
+ *
+ *   modes     device [N] int32: K_n, in [1, K].  A value outside is clamped to
+ *             it; the threshold and build calls then OR MFD_TREE_BAD_MODES into
+ *             status (if not NULL).
+ *
+ * mfd_logsoftmax_topk_modes: as mfd_logsoftmax_topk, except that the rows of
+ *   modes m >= K_n are neither read nor written (their lse, topk_* entries keep
+ *   whatever the caller left there; the logits need not be computed).
+ * mfd_mixture_threshold_modes, mfd_tree_build_modes: as mfd_mixture_threshold
+ *   and mfd_tree_build over the first K_n modes of tree n; they read no row of
+ *   a mode m >= K_n.  per_mode_kept is 0 for those modes.  The workspace is that
+ *   of the full-K call (mfd_workspace_size with K).
+ */
+mfd_status mfd_logsoftmax_topk_modes(const void* logits, mfd_dtype dtype, int N, int K, int L, int V,
+                                     const int32_t* modes, int k, double* lse, int32_t* topk_id,
+                                     float* topk_raw, float* topk_logp, int32_t* status, hipStream_t stream);
+
+mfd_status mfd_mixture_threshold_modes(const int32_t* topk_id, const float* topk_raw, const double* lse,
+                                       int N, int K, int L, int k, int B, const int32_t* modes,
+                                       double* cutoff, int32_t* n_select, int32_t* per_mode_kept,
+                                       int32_t* status, void* ws, size_t ws_bytes, hipStream_t stream);
+
+mfd_status mfd_tree_build_modes(const int32_t* topk_id, const float* topk_raw, const double* lse,
+                                const double* cutoff, const int32_t* n_select, const int32_t* anchor_token,
+                                int N, int K, int L, int k, int B, const int32_t* modes,
+                                int32_t* node_token, int32_t* parent, int32_t* depth, double* score,
+                                int32_t* best_mode, int32_t* n_nodes, int32_t* status,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Tree-verification inputs (model card summary: the target checks the whole

@@ -347,6 +347,7 @@ template <bool BF16>
 __global__ void __launch_bounds__(kThreads, 5) lsm_topk_kernel(const typename Elem<BF16>::T* __restrict__ logits,
                                                                long long V, int k, int cap_w, int pool_cap,
                                                                int sort_cap, int cand_cap, int rows_per_tree,
+                                                               int L, const int32_t* __restrict__ modes,
                                                                double* __restrict__ lse_out,
                                                                const int32_t* __restrict__ vocab_map,
                                                                int32_t* __restrict__ topk_id,
@@ -370,6 +371,14 @@ __global__ void __launch_bounds__(kThreads, 5) lsm_topk_kernel(const typename El
   const int tid = threadIdx.x, lane = lane_id(), wid = wave_id();
   const long long row = blockIdx.x;
   const T* rowp = logits + row * V;
+  if (modes) {
+    // rows of a mode at or past the tree's mode count are neither read nor
+    // written (the whole workgroup leaves before its first barrier)
+    const int n = (int)(row / rows_per_tree);
+    const int m = (int)(row - (long long)n * rows_per_tree) / L;
+    const int kn = modes[n];
+    if (m >= (kn < 1 ? 1 : kn)) return;
+  }
 
   if (tid == 0) {
     S.overflow = 0;
@@ -863,9 +872,10 @@ LsmCaps lsm_caps(long long V, int k, bool bf16) {
 
 }  // namespace
 
-hipError_t launch_logsoftmax_topk(const void* logits, bool bf16, int rows, int rows_per_tree, long long V, int k,
-                                  const int32_t* vocab_map, double* lse, int32_t* topk_id, float* topk_raw,
-                                  float* topk_logp, int32_t* status, hipStream_t stream) {
+hipError_t launch_logsoftmax_topk(const void* logits, bool bf16, int rows, int rows_per_tree, int L, long long V,
+                                  int k, const int32_t* vocab_map, const int32_t* modes, double* lse,
+                                  int32_t* topk_id, float* topk_raw, float* topk_logp, int32_t* status,
+                                  hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   const LsmCaps c = lsm_caps(V, k, bf16);
   if (bf16) {
@@ -874,14 +884,14 @@ hipError_t launch_logsoftmax_topk(const void* logits, bool bf16, int rows, int r
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(lsm_topk_kernel<true>, dim3(rows), dim3(kThreads), c.lds, stream,
                        static_cast<const uint16_t*>(logits), V, k, c.cap_w, c.pool, c.sort_cap, c.cand_cap,
-                       rows_per_tree, lse, vocab_map, topk_id, topk_raw, topk_logp, status);
+                       rows_per_tree, L, modes, lse, vocab_map, topk_id, topk_raw, topk_logp, status);
   } else {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lsm_topk_kernel<false>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)c.lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(lsm_topk_kernel<false>, dim3(rows), dim3(kThreads), c.lds, stream,
                        static_cast<const float*>(logits), V, k, c.cap_w, c.pool, c.sort_cap, c.cand_cap,
-                       rows_per_tree, lse, vocab_map, topk_id, topk_raw, topk_logp, status);
+                       rows_per_tree, L, modes, lse, vocab_map, topk_id, topk_raw, topk_logp, status);
   }
   return hipGetLastError();
 }

@@ -96,8 +96,9 @@ mfd_status mfd_workspace_size(mfd_op op, int N, int K, int L, int V, int B, size
 }
 
 static mfd_status logsoftmax_topk_impl(const char* call, const void* logits, mfd_dtype dtype, int N, int K, int L,
-                                       int V, const int32_t* vocab_map, int k, double* lse, int32_t* topk_id,
-                                       float* topk_raw, float* topk_logp, int32_t* status, hipStream_t stream) {
+                                       int V, const int32_t* vocab_map, const int32_t* modes, int k, double* lse,
+                                       int32_t* topk_id, float* topk_raw, float* topk_logp, int32_t* status,
+                                       hipStream_t stream) {
   mfd_status s = check_dims(N, K, L, V);
   if (s != MFD_OK) return s;
   if (dtype != MFD_BF16 && dtype != MFD_F32) return fail(MFD_ERR_DTYPE, "dtype must be MFD_BF16 or MFD_F32");
@@ -111,8 +112,8 @@ static mfd_status logsoftmax_topk_impl(const char* call, const void* logits, mfd
   if (reinterpret_cast<uintptr_t>(logits) % esz) return fail(MFD_ERR_INVALID_ARG, "logits not aligned to its element size");
   const long long rows = (long long)N * K * L;
   if (rows > 0x7FFFFFFFLL) return fail(MFD_ERR_INVALID_ARG, "too many rows (%lld)", rows);
-  return from_hip(mfd::launch_logsoftmax_topk(logits, dtype == MFD_BF16, (int)rows, K * L, V, k, vocab_map, lse,
-                                              topk_id, topk_raw, topk_logp, status, stream),
+  return from_hip(mfd::launch_logsoftmax_topk(logits, dtype == MFD_BF16, (int)rows, K * L, L, V, k, vocab_map, modes,
+                                              lse, topk_id, topk_raw, topk_logp, status, stream),
                   call);
 }
 
@@ -121,8 +122,8 @@ mfd_status mfd_logsoftmax_topk(const void* logits, mfd_dtype dtype, int N, int K
                                size_t ws_bytes, hipStream_t stream) {
   (void)ws;
   (void)ws_bytes;
-  return logsoftmax_topk_impl("mfd_logsoftmax_topk launch", logits, dtype, N, K, L, V, nullptr, k, lse, topk_id,
-                              topk_raw, topk_logp, status, stream);
+  return logsoftmax_topk_impl("mfd_logsoftmax_topk launch", logits, dtype, N, K, L, V, nullptr, nullptr, k, lse,
+                              topk_id, topk_raw, topk_logp, status, stream);
 }
 
 mfd_status mfd_logsoftmax_topk_mapped(const void* logits, mfd_dtype dtype, int N, int K, int L, int V,
@@ -131,13 +132,22 @@ mfd_status mfd_logsoftmax_topk_mapped(const void* logits, mfd_dtype dtype, int N
   if (V_full < V || V_full > kMaxV)
     return fail(MFD_ERR_INVALID_ARG, "V_full must be in [V, %d] (got %d, V = %d)", kMaxV, V_full, V);
   if (N > 0) REQUIRE_PTR(vocab_map);
-  return logsoftmax_topk_impl("mfd_logsoftmax_topk_mapped launch", logits, dtype, N, K, L, V, vocab_map, k, lse,
+  return logsoftmax_topk_impl("mfd_logsoftmax_topk_mapped launch", logits, dtype, N, K, L, V, vocab_map, nullptr, k,
+                              lse, topk_id, topk_raw, topk_logp, status, stream);
+}
+
+mfd_status mfd_logsoftmax_topk_modes(const void* logits, mfd_dtype dtype, int N, int K, int L, int V,
+                                     const int32_t* modes, int k, double* lse, int32_t* topk_id, float* topk_raw,
+                                     float* topk_logp, int32_t* status, hipStream_t stream) {
+  if (N > 0) REQUIRE_PTR(modes);
+  return logsoftmax_topk_impl("mfd_logsoftmax_topk_modes launch", logits, dtype, N, K, L, V, nullptr, modes, k, lse,
                               topk_id, topk_raw, topk_logp, status, stream);
 }
 
-mfd_status mfd_mixture_threshold(const int32_t* topk_id, const float* topk_raw, const double* lse, int N, int K, int L,
-                                 int k, int B, double* cutoff, int32_t* n_select, int32_t* per_mode_kept,
-                                 int32_t* status, void* ws, size_t ws_bytes, hipStream_t stream) {
+static mfd_status mixture_threshold_impl(const char* call, const int32_t* topk_id, const float* topk_raw,
+                                         const double* lse, int N, int K, int L, int k, int B, const int32_t* modes,
+                                         double* cutoff, int32_t* n_select, int32_t* per_mode_kept, int32_t* status,
+                                         void* ws, size_t ws_bytes, hipStream_t stream) {
   mfd_status s = check_tree_dims(N, K, L, k, B);
   if (s != MFD_OK) return s;
   if (N == 0) return ok();
@@ -149,15 +159,32 @@ mfd_status mfd_mixture_threshold(const int32_t* topk_id, const float* topk_raw, 
   const size_t need = (size_t)N * mfd::tree_caps(K, L, k, B).ws_bytes_per_tree;
   if (ws == nullptr || ws_bytes < need)
     return fail(MFD_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws == nullptr ? (size_t)0 : ws_bytes);
-  return from_hip(mfd::launch_mixture_threshold(topk_id, topk_raw, lse, N, K, L, k, B, cutoff, n_select, per_mode_kept,
-                                                status, ws, stream),
-                  "mfd_mixture_threshold launch");
+  return from_hip(mfd::launch_mixture_threshold(topk_id, topk_raw, lse, N, K, L, k, B, modes, cutoff, n_select,
+                                                per_mode_kept, status, ws, stream),
+                  call);
 }
 
-mfd_status mfd_tree_build(const int32_t* topk_id, const float* topk_raw, const double* lse, const double* cutoff,
-                          const int32_t* n_select, const int32_t* anchor_token, int N, int K, int L, int k, int B,
-                          int32_t* node_token, int32_t* parent, int32_t* depth, double* score, int32_t* best_mode,
-                          int32_t* n_nodes, int32_t* status, void* ws, size_t ws_bytes, hipStream_t stream) {
+mfd_status mfd_mixture_threshold(const int32_t* topk_id, const float* topk_raw, const double* lse, int N, int K, int L,
+                                 int k, int B, double* cutoff, int32_t* n_select, int32_t* per_mode_kept,
+                                 int32_t* status, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return mixture_threshold_impl("mfd_mixture_threshold launch", topk_id, topk_raw, lse, N, K, L, k, B, nullptr, cutoff,
+                                n_select, per_mode_kept, status, ws, ws_bytes, stream);
+}
+
+mfd_status mfd_mixture_threshold_modes(const int32_t* topk_id, const float* topk_raw, const double* lse, int N, int K,
+                                       int L, int k, int B, const int32_t* modes, double* cutoff, int32_t* n_select,
+                                       int32_t* per_mode_kept, int32_t* status, void* ws, size_t ws_bytes,
+                                       hipStream_t stream) {
+  if (N > 0) REQUIRE_PTR(modes);
+  return mixture_threshold_impl("mfd_mixture_threshold_modes launch", topk_id, topk_raw, lse, N, K, L, k, B, modes,
+                                cutoff, n_select, per_mode_kept, status, ws, ws_bytes, stream);
+}
+
+static mfd_status tree_build_impl(const char* call, const int32_t* topk_id, const float* topk_raw, const double* lse,
+                                  const double* cutoff, const int32_t* n_select, const int32_t* anchor_token, int N,
+                                  int K, int L, int k, int B, const int32_t* modes, int32_t* node_token,
+                                  int32_t* parent, int32_t* depth, double* score, int32_t* best_mode,
+                                  int32_t* n_nodes, int32_t* status, void* ws, size_t ws_bytes, hipStream_t stream) {
   mfd_status s = check_tree_dims(N, K, L, k, B);
   if (s != MFD_OK) return s;
   if (N == 0) return ok();
@@ -176,9 +203,29 @@ mfd_status mfd_tree_build(const int32_t* topk_id, const float* topk_raw, const d
   const size_t need = (size_t)N * mfd::tree_caps(K, L, k, B).ws_bytes_per_tree;
   if (ws == nullptr || ws_bytes < need)
     return fail(MFD_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws == nullptr ? (size_t)0 : ws_bytes);
-  return from_hip(mfd::launch_tree_build(topk_id, topk_raw, lse, cutoff, n_select, anchor_token, N, K, L, k, B,
+  return from_hip(mfd::launch_tree_build(topk_id, topk_raw, lse, cutoff, n_select, anchor_token, N, K, L, k, B, modes,
                                          node_token, parent, depth, score, best_mode, n_nodes, status, ws, stream),
-                  "mfd_tree_build launch");
+                  call);
+}
+
+mfd_status mfd_tree_build(const int32_t* topk_id, const float* topk_raw, const double* lse, const double* cutoff,
+                          const int32_t* n_select, const int32_t* anchor_token, int N, int K, int L, int k, int B,
+                          int32_t* node_token, int32_t* parent, int32_t* depth, double* score, int32_t* best_mode,
+                          int32_t* n_nodes, int32_t* status, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return tree_build_impl("mfd_tree_build launch", topk_id, topk_raw, lse, cutoff, n_select, anchor_token, N, K, L, k,
+                         B, nullptr, node_token, parent, depth, score, best_mode, n_nodes, status, ws, ws_bytes,
+                         stream);
+}
+
+mfd_status mfd_tree_build_modes(const int32_t* topk_id, const float* topk_raw, const double* lse, const double* cutoff,
+                                const int32_t* n_select, const int32_t* anchor_token, int N, int K, int L, int k,
+                                int B, const int32_t* modes, int32_t* node_token, int32_t* parent, int32_t* depth,
+                                double* score, int32_t* best_mode, int32_t* n_nodes, int32_t* status, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+  if (N > 0) REQUIRE_PTR(modes);
+  return tree_build_impl("mfd_tree_build_modes launch", topk_id, topk_raw, lse, cutoff, n_select, anchor_token, N, K,
+                         L, k, B, modes, node_token, parent, depth, score, best_mode, n_nodes, status, ws, ws_bytes,
+                         stream);
 }
 
 mfd_status mfd_tree_mask(const int32_t* parent, const int32_t* depth, const int32_t* n_nodes, const int64_t* pos_base,

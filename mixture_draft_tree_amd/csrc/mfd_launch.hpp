@@ -11,10 +11,11 @@
 
 namespace mfd {
 
-hipError_t launch_logsoftmax_topk(const void* logits, bool bf16, int rows, int rows_per_tree, long long V, int k,
-                                  const int32_t* vocab_map, double* lse, int32_t* topk_id, float* topk_raw,
-                                  float* topk_logp,
-                                  int32_t* status, hipStream_t stream);
+// modes (device [N] or null): rows of mode m >= modes[n] are skipped
+hipError_t launch_logsoftmax_topk(const void* logits, bool bf16, int rows, int rows_per_tree, int L, long long V,
+                                  int k, const int32_t* vocab_map, const int32_t* modes, double* lse,
+                                  int32_t* topk_id, float* topk_raw, float* topk_logp, int32_t* status,
+                                  hipStream_t stream);
 
 // Working capacities of the tree search for one tree (shared by the threshold
 // and build calls, and by the workspace query).
@@ -27,14 +28,16 @@ struct TreeCaps {
 };
 TreeCaps tree_caps(int K, int L, int k, int B);
 
+// modes (device [N] or null): tree n uses its first clamp(modes[n], 1, K) modes
 hipError_t launch_mixture_threshold(const int32_t* topk_id, const float* topk_raw, const double* lse, int N, int K,
-                                    int L, int k, int B, double* cutoff, int32_t* n_select, int32_t* per_mode_kept,
-                                    int32_t* status, void* ws, hipStream_t stream);
+                                    int L, int k, int B, const int32_t* modes, double* cutoff, int32_t* n_select,
+                                    int32_t* per_mode_kept, int32_t* status, void* ws, hipStream_t stream);
 
 hipError_t launch_tree_build(const int32_t* topk_id, const float* topk_raw, const double* lse, const double* cutoff,
                              const int32_t* n_select, const int32_t* anchor, int N, int K, int L, int k, int B,
-                             int32_t* node_token, int32_t* parent, int32_t* depth, double* score,
-                             int32_t* best_mode, int32_t* n_nodes, int32_t* status, void* ws, hipStream_t stream);
+                             const int32_t* modes, int32_t* node_token, int32_t* parent, int32_t* depth,
+                             double* score, int32_t* best_mode, int32_t* n_nodes, int32_t* status, void* ws,
+                             hipStream_t stream);
 
 hipError_t launch_tree_mask(const int32_t* parent, const int32_t* depth, const int32_t* n_nodes,
                             const int64_t* pos_base, int N, int Bp1, uint64_t* mask_words, int64_t* position_ids,

@@ -96,6 +96,8 @@ struct TreeArgs {
   unsigned char* ws;
   size_t ws_stride;
   int32_t* status;
+  // per-tree number of active modes (modes 0..K_n-1), or null for K everywhere
+  const int32_t* modes;
   // threshold outputs
   double* cutoff_out;
   int32_t* n_select_out;
@@ -680,15 +682,25 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
                      ? reinterpret_cast<uint16_t*>(smem_raw + ((tree_lds_base(a.sort_cap, K, L) + 15) & ~size_t(15)))
                      : nullptr;
   const Tree t = tree_ptrs(a, n);
+  // a tree built from its first K_n futures only: the inactive modes' rows
+  // are never read (the strides keep the full K)
+  int Kn = K;
+  if (a.modes) {
+    Kn = a.modes[n];
+    if (Kn < 1 || Kn > K) {
+      if (a.status && tid == 0) atomicOr(&a.status[n], MFD_TREE_BAD_MODES);
+      Kn = Kn < 1 ? 1 : K;
+    }
+  }
 
-  // norm[m][d] = sum_{i<d} lse[m][i], fp64, from i = 0 upward (all K*L
+  // norm[m][d] = sum_{i<d} lse[m][i], fp64, from i = 0 upward (all Kn*L
   // values loaded at once, then one running sum per mode)
-  for (int q = tid; q < K * L; q += kNT) {
+  for (int q = tid; q < Kn * L; q += kNT) {
     const int m = q / L, i = q - m * L;
     norm[m * Lp1 + i + 1] = a.lse[(size_t)n * K * L + q];
   }
   __syncthreads();
-  for (int m = tid; m < K; m += kNT) {
+  for (int m = tid; m < Kn; m += kNT) {
     double acc = 0.0;
     norm[m * Lp1] = 0.0;
     for (int i = 0; i < L; ++i) {
@@ -699,8 +711,8 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
   for (int i = tid; i < 32; i += kNT) ctl.kept[i] = 0;
   if (tid == 0) {
     ctl.node_count = 1;
-    ctl.ent_count = K;
-    ctl.fsize = K;
+    ctl.ent_count = Kn;
+    ctl.fsize = Kn;
     ctl.fail = 0;
     for (int d = 0; d < 34; ++d) ctl.level_start[d] = -1;
     t.node_parent[0] = -1;
@@ -709,7 +721,7 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
     t.node_S[0] = 0.0;
     t.node_mu[0] = -1;
   }
-  for (int m = tid; m < K; m += kNT) {
+  for (int m = tid; m < Kn; m += kNT) {
     t.ent_node[m] = 0;
     t.ent_mode[m] = m;
     t.ent_raw[m] = 0.0;
@@ -734,7 +746,7 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
       double t0 = -INFINITY;
       if (B == 0) ctl.fsize = 0;
       else if (k >= B) {
-        for (int m = 0; m < K; ++m) {
+        for (int m = 0; m < Kn; ++m) {
           const float x = a.topk_raw[((size_t)(n * K + m) * L) * k + (B - 1)];
           if (x != -INFINITY) {
             const double s0 = (0.0 + (double)x) - norm[m * Lp1 + 1];
@@ -764,7 +776,7 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
     }
     if (fail) cut = NAN;
     if (a.per_mode_kept) {
-      for (int e = K + tid; e < ctl.ent_count; e += kNT)
+      for (int e = Kn + tid; e < ctl.ent_count; e += kNT)
         if (!fail && nsel > 0 && t.ent_s[e] >= cut) atomicAdd(&ctl.kept[t.ent_mode[e]], 1);
       __syncthreads();
       for (int m = tid; m < K; m += kNT) a.per_mode_kept[(size_t)n * K + m] = ctl.kept[m];
@@ -964,9 +976,10 @@ static hipError_t launch_tree(bool build, TreeArgs& a, int N, hipStream_t stream
 }
 
 hipError_t launch_mixture_threshold(const int32_t* topk_id, const float* topk_raw, const double* lse, int N, int K,
-                                    int L, int k, int B, double* cutoff, int32_t* n_select, int32_t* per_mode_kept,
-                                    int32_t* status, void* ws, hipStream_t stream) {
+                                    int L, int k, int B, const int32_t* modes, double* cutoff, int32_t* n_select,
+                                    int32_t* per_mode_kept, int32_t* status, void* ws, hipStream_t stream) {
   TreeArgs a = {};
+  a.modes = modes;
   a.topk_id = topk_id;
   a.topk_raw = topk_raw;
   a.lse = lse;
@@ -984,9 +997,11 @@ hipError_t launch_mixture_threshold(const int32_t* topk_id, const float* topk_ra
 
 hipError_t launch_tree_build(const int32_t* topk_id, const float* topk_raw, const double* lse, const double* cutoff,
                              const int32_t* n_select, const int32_t* anchor, int N, int K, int L, int k, int B,
-                             int32_t* node_token, int32_t* parent, int32_t* depth, double* score,
-                             int32_t* best_mode, int32_t* n_nodes, int32_t* status, void* ws, hipStream_t stream) {
+                             const int32_t* modes, int32_t* node_token, int32_t* parent, int32_t* depth,
+                             double* score, int32_t* best_mode, int32_t* n_nodes, int32_t* status, void* ws,
+                             hipStream_t stream) {
   TreeArgs a = {};
+  a.modes = modes;
   a.topk_id = topk_id;
   a.topk_raw = topk_raw;
   a.lse = lse;

@@ -26,11 +26,12 @@ MFD_OK, MFD_ERR_INVALID_ARG, MFD_ERR_DTYPE, MFD_ERR_WORKSPACE, MFD_ERR_DEVICE = 
 MFD_BF16, MFD_F32 = 0, 1
 (MFD_OP_LOGSOFTMAX_TOPK, MFD_OP_MIXTURE_THRESHOLD, MFD_OP_TREE_BUILD,
  MFD_OP_TREE_MASK, MFD_OP_VERIFY_WALK, MFD_OP_COVERED_MASS) = range(6)
-MFD_TREE_NONFINITE, MFD_TREE_CAPACITY, MFD_TREE_BAD_TEMPERATURE = 1, 2, 4
+MFD_TREE_NONFINITE, MFD_TREE_CAPACITY, MFD_TREE_BAD_TEMPERATURE, MFD_TREE_BAD_MODES = 1, 2, 4, 8
 
 EXPORTED = ["mfd_last_error", "mfd_version", "mfd_workspace_size", "mfd_logsoftmax_topk",
             "mfd_logsoftmax_topk_mapped", "mfd_mixture_threshold", "mfd_tree_build", "mfd_tree_mask",
-            "mfd_verify_walk", "mfd_covered_mass", "mfd_chimera_count"]
+            "mfd_verify_walk", "mfd_covered_mass", "mfd_chimera_count", "mfd_logsoftmax_topk_modes",
+            "mfd_mixture_threshold_modes", "mfd_tree_build_modes"]
 
 _p = ctypes.c_void_p
 _i = ctypes.c_int
@@ -51,6 +52,13 @@ _lib.mfd_mixture_threshold.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _
 _lib.mfd_tree_build.restype = _i
 _lib.mfd_tree_build.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i,
                                 _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]
+_lib.mfd_logsoftmax_topk_modes.restype = _i
+_lib.mfd_logsoftmax_topk_modes.argtypes = [_p, _i, _i, _i, _i, _i, _p, _i, _p, _p, _p, _p, _p, _p]
+_lib.mfd_mixture_threshold_modes.restype = _i
+_lib.mfd_mixture_threshold_modes.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p]
+_lib.mfd_tree_build_modes.restype = _i
+_lib.mfd_tree_build_modes.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p,
+                                      _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]
 _lib.mfd_tree_mask.restype = _i
 _lib.mfd_tree_mask.argtypes = [_p, _p, _p, _p, _i, _i, _p, _p, _p, _p]
 _lib.mfd_covered_mass.restype = _i
@@ -159,8 +167,32 @@ def mfd_logsoftmax_topk_mapped(logits, vocab_map, V_full, k, lse, topk_id, topk_
                                            _stream_handle(stream)), "mfd_logsoftmax_topk_mapped")
 
 
+def mfd_logsoftmax_topk_modes(logits, modes, k, lse, topk_id, topk_raw, topk_logp=None, status=None, stream=None):
+    """As mfd_logsoftmax_topk for the rows of modes m < modes[n] (modes: [N] int32 on
+    the GPU); the other rows are neither read nor written."""
+    if logits.dim() != 4 or not logits.is_contiguous() or logits.device.type != "cuda":
+        raise ValueError("logits must be a contiguous [N, K, L, V] GPU tensor")
+    N, K, L, V = logits.shape
+    _want(modes, "modes", torch.int32, (N,))
+    _want(lse, "lse", torch.float64, (N, K, L))
+    _want(topk_id, "topk_id", torch.int32, (N, K, L, k))
+    _want(topk_raw, "topk_raw", torch.float32, (N, K, L, k))
+    _want(topk_logp, "topk_logp", torch.float32, (N, K, L, k), optional=True)
+    _want(status, "status", torch.int32, (N,), optional=True)
+    _check(_lib.mfd_logsoftmax_topk_modes(_ptr(logits), _dtype_code(logits), N, K, L, V, _ptr(modes), k, _ptr(lse),
+                                          _ptr(topk_id), _ptr(topk_raw), _ptr(topk_logp), _ptr(status),
+                                          _stream_handle(stream)), "mfd_logsoftmax_topk_modes")
+
+
 def mfd_mixture_threshold(topk_id, topk_raw, lse, B, cutoff, n_select, per_mode_kept=None, status=None,
                           ws=None, stream=None):
+    mfd_mixture_threshold_modes(topk_id, topk_raw, lse, B, None, cutoff, n_select, per_mode_kept, status, ws, stream)
+
+
+def mfd_mixture_threshold_modes(topk_id, topk_raw, lse, B, modes, cutoff, n_select, per_mode_kept=None, status=None,
+                                ws=None, stream=None):
+    """The common cut-off; with modes ([N] int32 on the GPU) tree n uses its first
+    modes[n] futures (modes=None: the plain mfd_mixture_threshold call)."""
     N, K, L, k = topk_id.shape
     _want(topk_id, "topk_id", torch.int32, (N, K, L, k))
     _want(topk_raw, "topk_raw", torch.float32, (N, K, L, k))
@@ -170,13 +202,27 @@ def mfd_mixture_threshold(topk_id, topk_raw, lse, B, cutoff, n_select, per_mode_
     _want(per_mode_kept, "per_mode_kept", torch.int32, (N, K), optional=True)
     _want(status, "status", torch.int32, (N,), optional=True)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(_lib.mfd_mixture_threshold(_ptr(topk_id), _ptr(topk_raw), _ptr(lse), N, K, L, k, B, _ptr(cutoff),
-                                      _ptr(n_select), _ptr(per_mode_kept), _ptr(status), _ptr(ws), ws_bytes,
-                                      _stream_handle(stream)), "mfd_mixture_threshold")
+    if modes is None:
+        _check(_lib.mfd_mixture_threshold(_ptr(topk_id), _ptr(topk_raw), _ptr(lse), N, K, L, k, B, _ptr(cutoff),
+                                          _ptr(n_select), _ptr(per_mode_kept), _ptr(status), _ptr(ws), ws_bytes,
+                                          _stream_handle(stream)), "mfd_mixture_threshold")
+        return
+    _want(modes, "modes", torch.int32, (N,))
+    _check(_lib.mfd_mixture_threshold_modes(_ptr(topk_id), _ptr(topk_raw), _ptr(lse), N, K, L, k, B, _ptr(modes),
+                                            _ptr(cutoff), _ptr(n_select), _ptr(per_mode_kept), _ptr(status),
+                                            _ptr(ws), ws_bytes, _stream_handle(stream)), "mfd_mixture_threshold_modes")
 
 
 def mfd_tree_build(topk_id, topk_raw, lse, cutoff, n_select, anchor_token, B, node_token, parent, depth, score,
                    best_mode, n_nodes, status=None, ws=None, stream=None):
+    mfd_tree_build_modes(topk_id, topk_raw, lse, cutoff, n_select, anchor_token, B, None, node_token, parent, depth,
+                         score, best_mode, n_nodes, status, ws, stream)
+
+
+def mfd_tree_build_modes(topk_id, topk_raw, lse, cutoff, n_select, anchor_token, B, modes, node_token, parent, depth,
+                         score, best_mode, n_nodes, status=None, ws=None, stream=None):
+    """The tree; with modes ([N] int32 on the GPU) tree n is built from its first
+    modes[n] futures (modes=None: the plain mfd_tree_build call)."""
     N, K, L, k = topk_id.shape
     Bp1 = B + 1
     _want(topk_id, "topk_id", torch.int32, (N, K, L, k))
@@ -192,10 +238,17 @@ def mfd_tree_build(topk_id, topk_raw, lse, cutoff, n_select, anchor_token, B, no
     _want(n_nodes, "n_nodes", torch.int32, (N,))
     _want(status, "status", torch.int32, (N,), optional=True)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(_lib.mfd_tree_build(_ptr(topk_id), _ptr(topk_raw), _ptr(lse), _ptr(cutoff), _ptr(n_select),
-                               _ptr(anchor_token), N, K, L, k, B, _ptr(node_token), _ptr(parent), _ptr(depth),
-                               _ptr(score), _ptr(best_mode), _ptr(n_nodes), _ptr(status), _ptr(ws), ws_bytes,
-                               _stream_handle(stream)), "mfd_tree_build")
+    if modes is None:
+        _check(_lib.mfd_tree_build(_ptr(topk_id), _ptr(topk_raw), _ptr(lse), _ptr(cutoff), _ptr(n_select),
+                                   _ptr(anchor_token), N, K, L, k, B, _ptr(node_token), _ptr(parent), _ptr(depth),
+                                   _ptr(score), _ptr(best_mode), _ptr(n_nodes), _ptr(status), _ptr(ws), ws_bytes,
+                                   _stream_handle(stream)), "mfd_tree_build")
+        return
+    _want(modes, "modes", torch.int32, (N,))
+    _check(_lib.mfd_tree_build_modes(_ptr(topk_id), _ptr(topk_raw), _ptr(lse), _ptr(cutoff), _ptr(n_select),
+                                     _ptr(anchor_token), N, K, L, k, B, _ptr(modes), _ptr(node_token), _ptr(parent),
+                                     _ptr(depth), _ptr(score), _ptr(best_mode), _ptr(n_nodes), _ptr(status),
+                                     _ptr(ws), ws_bytes, _stream_handle(stream)), "mfd_tree_build_modes")
 
 
 def mfd_tree_mask(parent, depth, n_nodes, pos_base, mask_words, position_ids, dense_mask=None, stream=None):

@@ -45,11 +45,17 @@ class MixtureTreePath:
 
     def __init__(self, N: int, K: int, L: int, V: int, B: int, device="cuda", k: Optional[int] = None,
                  with_logp: bool = False, with_dense_mask: bool = False,
-                 vocab_map: Optional[torch.Tensor] = None, V_full: Optional[int] = None):
+                 vocab_map: Optional[torch.Tensor] = None, V_full: Optional[int] = None,
+                 modes: Optional[torch.Tensor] = None):
         """V is the drafting vocabulary; with `vocab_map` ([V] int32, increasing ids in a
-        vocabulary of V_full tokens) the tree is built in full-vocabulary ids."""
+        vocabulary of V_full tokens) the tree is built in full-vocabulary ids.  With
+        `modes` ([N] int32 on the GPU, values in [1, K]) tree n uses its first modes[n]
+        futures; its contents may change between steps, its storage may not."""
+        if modes is not None and vocab_map is not None:
+            raise ValueError("per-tree mode counts and a drafting vocabulary map are separate calls")
         self.N, self.K, self.L, self.V, self.B = N, K, L, V, B
         self.vocab_map = vocab_map
+        self.modes = modes
         self.V_full = V if V_full is None else V_full
         self.k = min(B, V) if k is None else k
         if self.k < 1:
@@ -91,19 +97,23 @@ class MixtureTreePath:
         if self.vocab_map is not None:
             M.mfd_logsoftmax_topk_mapped(logits, self.vocab_map, self.V_full, self.k, b.lse, b.topk_id, b.topk_raw,
                                          b.topk_logp, b.status, stream=stream)
+        elif self.modes is not None:
+            M.mfd_logsoftmax_topk_modes(logits, self.modes, self.k, b.lse, b.topk_id, b.topk_raw, b.topk_logp,
+                                        b.status, stream=stream)
         else:
             M.mfd_logsoftmax_topk(logits, self.k, b.lse, b.topk_id, b.topk_raw, b.topk_logp, b.status,
                                   stream=stream)
 
     def mixture_threshold(self, stream=None):
         b = self.buf
-        M.mfd_mixture_threshold(b.topk_id, b.topk_raw, b.lse, self.B, b.cutoff, b.n_select, b.per_mode_kept,
-                                b.status, b.ws, stream=stream)
+        M.mfd_mixture_threshold_modes(b.topk_id, b.topk_raw, b.lse, self.B, self.modes, b.cutoff, b.n_select,
+                                      b.per_mode_kept, b.status, b.ws, stream=stream)
 
     def tree_build(self, anchor, stream=None):
         b = self.buf
-        M.mfd_tree_build(b.topk_id, b.topk_raw, b.lse, b.cutoff, b.n_select, anchor, self.B, b.node_token,
-                         b.parent, b.depth, b.score, b.best_mode, b.n_nodes, b.status, b.ws, stream=stream)
+        M.mfd_tree_build_modes(b.topk_id, b.topk_raw, b.lse, b.cutoff, b.n_select, anchor, self.B, self.modes,
+                               b.node_token, b.parent, b.depth, b.score, b.best_mode, b.n_nodes, b.status, b.ws,
+                               stream=stream)
 
     def tree_mask(self, pos_base, stream=None):
         b = self.buf

@@ -22,7 +22,7 @@ reach the full depth of 15 and acceptance lengths land near the pages'
 figures (tau of 6 to 11 at B = 256, project page, Table 1; about 10.7 for MFD
 on Qwen3.5-4B at T = 0, model card, "Results").
 
-Seven named workloads:
+Named workloads:
 
   tiny          K=2,  L=4,  V=16,     B=8     fp32, brute-forceable
   product       K=1,  L=15, V=32000,  B=64    bf16, two injected futures at equal mass
@@ -33,11 +33,19 @@ Seven named workloads:
   batched_deep  64 trees of the `deep` shape, T alternating 0 / 1
   subset        as `single`, drafting over a 65536-token subset of the V tokens
   batched_subset  64 trees of the `subset` shape
+  batched_modes   64 trees of the `deep` shape, K_n alternating 8 / 1 (T 0, 0, 1, 1)
 
 The subset workloads draft over a sorted random subset of 65536 of the 151936
 target tokens (the project page's serving setup drafts over the target's 64K
 most frequent tokens and verifies over the full vocabulary): drafter logits
 cover the subset, futures are drawn from it, target rows cover all V tokens.
+
+The `batched_modes` workload mixes requests drafted with all K modes and
+requests drafted with mode 0 only in one batch (the single-mode default path
+that the project page's MFD-D configuration switches to in a busy engine, "In
+a serving engine").  Logits of the modes a tree does not use are NaN, so any
+read of them shows up as a non-finite flag or a wrong tree.  The target follows
+one of all K futures either way, as the full drafter's chosen future.
 
 Every draw comes from a torch.Generator seeded from (workload id, tree index,
 base seed), on the device the caller names, so a given (device, seed) always
@@ -72,6 +80,7 @@ class Workload:
     alt_height: float = 0.0  # ... of alt_height * r^-1.1, r = 1..alt_n
     dev_lo: int = 0       # target leaves the chosen future at a depth D ~ U{dev_lo..L} (0: never)
     v_draft: int = 0      # drafting vocabulary: a sorted random subset of this many of the V tokens (0: all)
+    modes: tuple = ()     # per-tree number of active modes, cycled over the trees (empty: K for every tree)
 
 
 WORKLOADS = {
@@ -88,6 +97,9 @@ WORKLOADS = {
                        v_draft=65536),
     "batched_subset": Workload("batched_subset", 9, 8, 15, 151936, 256, 64, torch.bfloat16, 3.0, 8.0, 10.0,
                                (0.0, 1.0), v_draft=65536),
+    "batched_modes": Workload("batched_modes", 10, 8, 15, 151936, 256, 64, torch.bfloat16, 2.0, 16.0, 16.0,
+                              (0.0, 0.0, 1.0, 1.0), jitter=1.5, alt_n=16, alt_height=10.0, dev_lo=3,
+                              modes=(8, 1)),
 }
 
 
@@ -134,6 +146,7 @@ class DraftBatch:
     seed: torch.Tensor          # [N] uint64 stored as int64 (two's complement)
     tree_seeds: list            # python ints, one per tree
     vocab_map: Optional[torch.Tensor] = None  # [v_draft] int32 full ids (sorted) of the drafting tokens
+    modes: Optional[torch.Tensor] = None      # [N] int32: active modes of each tree (None: all K)
 
 
 def _tiny_tree(w, g, device):
@@ -266,6 +279,8 @@ def draft_batch(name: str, base_seed: int = 0, device="cpu", N: Optional[int] = 
             x, fut = _mixture_tree(wd, g, device, ties=(name == "stress"))
             if vmap is not None:
                 fut = vmap.to(torch.int64)[fut]
+        if w.modes:
+            x[w.modes[n % len(w.modes)]:] = float("nan")
         logits[n] = x.to(w.dtype)
         futs.append(fut)
         chosen.append(int(_randint(g, fut.shape[0], (1,), device).item()))
@@ -277,7 +292,9 @@ def draft_batch(name: str, base_seed: int = 0, device="cpu", N: Optional[int] = 
         chosen_mode=torch.tensor(chosen, dtype=torch.int64),
         anchor=torch.tensor(anchors, dtype=torch.int32),
         pos_base=torch.tensor([1000 + 17 * n for n in range(N)], dtype=torch.int64),
-        temperature=temps, seed=seed_t, tree_seeds=seeds, vocab_map=vmap)
+        temperature=temps, seed=seed_t, tree_seeds=seeds, vocab_map=vmap,
+        modes=(torch.tensor([w.modes[n % len(w.modes)] for n in range(N)], dtype=torch.int32)
+               if w.modes else None))
 
 
 def target_logits(batch: DraftBatch, depth: torch.Tensor, n_nodes: torch.Tensor,

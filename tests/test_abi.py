@@ -163,3 +163,29 @@ def test_binding_checks_shapes_on_cpu_tensors():
     x = torch.zeros((1, 2, 3, 16), dtype=torch.float32)
     with pytest.raises(ValueError):
         M.mfd_logsoftmax_topk(x, 4, None, None, None)
+
+
+def test_modes_calls_reject_before_launch():
+    """The per-tree mode-count calls: a missing modes array and the checks of the
+    calls they extend are reported before anything launches."""
+    lsm = M._lib.mfd_logsoftmax_topk_modes
+    assert lsm(FAKE, M.MFD_BF16, 1, 8, 15, 1000, None, 256, FAKE, FAKE, FAKE, None, None, None) == M.MFD_ERR_INVALID_ARG
+    assert "modes" in M.last_error()
+    assert lsm(FAKE, M.MFD_BF16, 1, 8, 15, 1000, FAKE, 1001, FAKE, FAKE, FAKE, None, None, None) == M.MFD_ERR_INVALID_ARG
+    assert lsm(FAKE, 7, 1, 8, 15, 1000, FAKE, 256, FAKE, FAKE, FAKE, None, None, None) == M.MFD_ERR_DTYPE
+    assert lsm(None, M.MFD_BF16, 0, 8, 15, 1000, None, 256, None, None, None, None, None, None) == M.MFD_OK
+    thr = M._lib.mfd_mixture_threshold_modes
+    need = M.workspace_size(M.MFD_OP_MIXTURE_THRESHOLD, 2, 8, 15, 151936, 256)
+    assert thr(FAKE, FAKE, FAKE, 2, 8, 15, 256, 256, None, FAKE, FAKE, None, None, FAKE, need,
+               None) == M.MFD_ERR_INVALID_ARG
+    assert thr(FAKE, FAKE, FAKE, 2, 8, 15, 256, 256, FAKE, FAKE, FAKE, None, None, FAKE, need - 1,
+               None) == M.MFD_ERR_WORKSPACE
+    assert thr(FAKE, FAKE, FAKE, 2, 33, 15, 256, 256, FAKE, FAKE, FAKE, None, None, FAKE, need,
+               None) == M.MFD_ERR_INVALID_ARG
+    bld = M._lib.mfd_tree_build_modes
+    nb = M.workspace_size(M.MFD_OP_TREE_BUILD, 1, 8, 15, 151936, 256)
+    args = [FAKE] * 6 + [1, 8, 15, 256, 256]
+    outs = [FAKE] * 6
+    assert bld(*args, None, *outs, None, FAKE, nb, None) == M.MFD_ERR_INVALID_ARG
+    assert bld(*args, FAKE, *outs, None, None, 0, None) == M.MFD_ERR_WORKSPACE
+    assert bld(*[None] * 6, 0, 8, 15, 256, 256, None, *[None] * 6, None, None, 0, None) == M.MFD_OK

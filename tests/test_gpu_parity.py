@@ -203,6 +203,41 @@ def test_tree_small_cases(case):
     say(f"[tree] seed={seed} exact={r['exact']} n_nodes={g['n_nodes']}")
 
 
+def test_modes_small_batch():
+    """Per-tree mode counts in one launch: each tree equals the oracle over its first
+    K_n modes, a tree with K_n = K equals the plain calls bit for bit, and counts
+    outside [1, K] are clamped and flagged."""
+    K, L, V, B = 4, 5, 40, 30
+    modes_h = [4, 1, 2, 3, 0, 7]
+    kn = [min(max(m, 1), K) for m in modes_h]
+    N = len(modes_h)
+    x = torch.cat([_small_tree_case(40 + n, K, L, V, B, ints=(n % 2 == 1)) for n in range(N)])
+    anchor = torch.arange(N, dtype=torch.int32, device="cuda") + 3
+    pos = torch.full((N,), 50, dtype=torch.int64, device="cuda")
+    modes = torch.tensor(modes_h, dtype=torch.int32, device="cuda")
+    P = MixtureTreePath(N, K, L, V, B, with_logp=True, modes=modes)
+    Q = MixtureTreePath(N, K, L, V, B, with_logp=True)
+    P.build(x.cuda(), anchor, pos)
+    Q.build(x.cuda(), anchor, pos)
+    torch.cuda.synchronize()
+    want_status = [M.MFD_TREE_BAD_MODES if m != c else 0 for m, c in zip(modes_h, kn)]
+    assert P.buf.status.cpu().tolist() == want_status
+    assert Q.buf.status.eq(0).all()
+    for n in range(N):
+        say(f"[modes] tree {n}: K_n={modes_h[n]} -> {kn[n]}")
+        x64 = x[n, :kn[n]].double().numpy()
+        check_lsm(x[n:n + 1, :kn[n]], P.buf.lse[n:n + 1, :kn[n]], P.buf.topk_id[n:n + 1, :kn[n]],
+                  P.buf.topk_raw[n:n + 1, :kn[n]], P.k, P.buf.topk_logp[n:n + 1, :kn[n]])
+        g = tree_rows(P, n)
+        assert np.all(g["per_mode_kept"][kn[n]:] == 0)
+        g["per_mode_kept"] = g["per_mode_kept"][:kn[n]]
+        compare_tree(x64, B, n + 3, g)
+        if kn[n] == K:
+            for f in ("lse", "topk_id", "topk_raw", "cutoff", "n_select", "per_mode_kept", "node_token", "parent",
+                      "depth", "score", "best_mode", "n_nodes", "mask_words", "position_ids"):
+                assert torch.equal(getattr(P.buf, f)[n], getattr(Q.buf, f)[n]), f
+
+
 @pytest.mark.parametrize("seed", [21, 22, 23])
 def test_tree_build_from_lower_cutoff(seed):
     """The build call alone, fed a cut-off well below the true one (so it
@@ -323,7 +358,13 @@ def _run_workload(name, N=None, sample=None, device_gen="cpu"):
     N = b.logits.shape[0]
     logits = b.logits.cuda()
     vmap = None if b.vocab_map is None else b.vocab_map.cuda()
-    P = MixtureTreePath(N, w.K, w.L, logits.shape[-1], w.B, with_logp=True, vocab_map=vmap, V_full=w.V)
+    modes = None if b.modes is None else b.modes.cuda()
+    P = MixtureTreePath(N, w.K, w.L, logits.shape[-1], w.B, with_logp=True, vocab_map=vmap, V_full=w.V,
+                        modes=modes)
+    if modes is not None:
+        # rows of inactive modes must come back untouched
+        for t, v in ((P.buf.lse, -123.5), (P.buf.topk_id, -7), (P.buf.topk_raw, -5.25), (P.buf.topk_logp, -9.5)):
+            t.fill_(v)
     anchor, pos = b.anchor.cuda(), b.pos_base.cuda()
     say(f"[{name}] build N={N}")
     P.build(logits, anchor, pos)
@@ -333,16 +374,23 @@ def _run_workload(name, N=None, sample=None, device_gen="cpu"):
     trees, results = {}, {}
     for n in sample:
         x_cpu = b.logits[n].cpu()
+        Kn = w.K if b.modes is None else int(b.modes[n])
+        if Kn < w.K:
+            assert torch.all(P.buf.lse[n, Kn:] == -123.5) and torch.all(P.buf.topk_id[n, Kn:] == -7)
+            assert torch.all(P.buf.topk_raw[n, Kn:] == -5.25) and torch.all(P.buf.topk_logp[n, Kn:] == -9.5)
+            x_cpu = x_cpu[:Kn]
         if b.vocab_map is not None:
             # the oracle sees full-vocabulary rows, -inf outside the drafting subset
             x_full = torch.full((w.K, w.L, w.V), float("-inf"), dtype=torch.float32)
             x_full[:, :, b.vocab_map.cpu().long()] = x_cpu.float()
             x_cpu = x_full
         x64 = x_cpu.double().numpy()
-        check_lsm(x_cpu[None], P.buf.lse[n:n + 1], P.buf.topk_id[n:n + 1], P.buf.topk_raw[n:n + 1], P.k,
-                  P.buf.topk_logp[n:n + 1])
-        r = compare_tree(x64, w.B, int(b.anchor[n]), tree_rows(P, n))
+        check_lsm(x_cpu[None], P.buf.lse[n:n + 1, :Kn], P.buf.topk_id[n:n + 1, :Kn], P.buf.topk_raw[n:n + 1, :Kn],
+                  P.k, P.buf.topk_logp[n:n + 1, :Kn])
         g = tree_rows(P, n)
+        assert np.all(g["per_mode_kept"][Kn:] == 0)
+        g["per_mode_kept"] = g["per_mode_kept"][:Kn]
+        r = compare_tree(x64, w.B, int(b.anchor[n]), g)
         check_mask(g["parent"], g["depth"], g["n_nodes"], int(b.pos_base[n]), w.B + 1,
                    P.buf.mask_words[n].cpu().numpy(), P.buf.position_ids[n].cpu().numpy())
         trees[n], results[n] = r["tree"], r
@@ -422,6 +470,16 @@ def test_workload_subset():
 
 def test_workload_batched_subset_sampled():
     _run_workload("batched_subset", sample=[0, 5, 63], device_gen="cuda")
+
+
+def test_workload_batched_modes():
+    """K_n = 8 and K_n = 1 trees in one launch; each against the oracle over its own
+    first K_n modes (the K_n = 1 trees are single-future product trees)."""
+    b, P, trees = _run_workload("batched_modes", sample=[0, 1, 2, 3, 62, 63], device_gen="cuda")
+    # a single-mode tree takes best_mode 0 everywhere
+    for n in (1, 3, 63):
+        nn_ = int(P.buf.n_nodes[n])
+        assert torch.all(P.buf.best_mode[n, 1:nn_] == 0)
 
 
 def test_determinism_and_batch_order():
