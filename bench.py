@@ -29,6 +29,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # Sources of the logits kernel's code: a traffic figure measured on other code is stale.
 LSM_SOURCES = ["mixture_draft_tree_amd/csrc/lsm_topk.hip", "mixture_draft_tree_amd/csrc/mfd_device.hpp"]
 TRAFFIC_FILE = "profiles/lsm_topk_kernel_batched_64x8x15x151936_hbm_traffic.txt"
+SQ_FILE = "profiles/sq_counters_batched_64x8x15x151936.md"
 
 
 def lsm_source_sha() -> str:
@@ -39,25 +40,31 @@ def lsm_source_sha() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of the logits kernel from the committed counter
-    summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None if there is
-    none for this workload or the kernel sources changed since it was taken."""
-    path = os.path.join(HERE, TRAFFIC_FILE)
+def profile_field(rel: str, workload: str, key: str):
+    """A figure of the logits kernel from a committed counter summary of the
+    batched workload, or None if there is none for this workload or the kernel
+    sources changed since the counters were taken."""
+    path = os.path.join(HERE, rel)
     if workload != "batched" or not os.path.exists(path):
         return None
     fields = {}
     with open(path) as f:
         for line in f:
-            if ":" in line and not line.startswith((" ", "#", "$")):
-                key, val = line.split(":", 1)
-                fields[key.strip()] = val.strip()
+            if ":" in line and not line.startswith((" ", "#", "$", "|")):
+                k, val = line.split(":", 1)
+                fields[k.strip()] = val.strip()
     if fields.get("kernel_source_sha256") != lsm_source_sha():
         return None
     try:
-        return float(fields["hbm_bytes_per_launch"])
+        return float(fields[key])
     except (KeyError, ValueError):
         return None
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the logits kernel (FETCH_SIZE + WRITE_SIZE,
+    copy-calibrated), or None."""
+    return profile_field(TRAFFIC_FILE, workload, "hbm_bytes_per_launch")
 
 
 def parse():
@@ -68,8 +75,8 @@ def parse():
     ap.add_argument("--workload", default="batched",
                     choices=["batched", "single", "stress", "deep", "batched_deep", "subset", "batched_subset",
                              "batched_modes"])
-    ap.add_argument("--cpu-baseline-trees", type=int, default=2,
-                    help="trees of the workload the fp64 oracle is timed on (0 = skip)")
+    ap.add_argument("--cpu-baseline-trees", type=int, default=16,
+                    help="trees of the workload the fp64 oracle is timed on, one process per core (0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-gib", type=int, default=0,
                     help="after the run, copy a buffer of this many GiB device to device: a plain copy of "
@@ -85,37 +92,75 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(name: str, base_seed: int, n_trees: int):
-    """Time the fp64 oracle end to end (log-softmax, ranks, heap, layout, mask,
-    walk) on the first `n_trees` trees of the workload, on this host's cores."""
-    import numpy as np
+def _oracle_worker(name, base_seed, trees, barrier, results):
+    """One pool worker: draws its trees and their target rows (untimed), waits
+    until every worker is ready, then runs the whole oracle path on each tree."""
+    try:
+        import threadpoolctl
+        threadpoolctl.threadpool_limits(1)
+    except ImportError:
+        pass
+    torch.set_num_threads(1)
     import oracle as O
     from mixture_draft_tree_amd import synth
 
     w = synth.WORKLOADS[name]
-    b = synth.draft_batch(name, base_seed=base_seed, device="cpu", N=n_trees)
-    xs = [b.logits[n].double().numpy() for n in range(n_trees)]
-    # target rows come from the oracle's own trees (generated outside the timed part)
-    trees = []
-    for n in range(n_trees):
-        sel = O.mixture_select_heap(xs[n], w.B)
-        trees.append(O.canonical_tree(sel, int(b.anchor[n]), w.B))
-    dep = torch.stack([torch.from_numpy(t["depth"]).to(torch.int32) for t in trees])
-    nn = torch.tensor([t["n_nodes"] for t in trees], dtype=torch.int32)
-    R = synth.target_logits(b, dep, nn, device="cpu", base_seed=base_seed)
-    Rs = [R[n].double().numpy() for n in range(n_trees)]
+    work = []
+    for n in trees:
+        b = synth.draft_batch(name, base_seed=base_seed, device="cpu", N=1, start=n)
+        x = b.logits[0].double().numpy()
+        # target rows come from the oracle's own tree, drawn outside the timed part
+        tr = O.canonical_tree(O.mixture_select_heap(x, w.B), int(b.anchor[0]), w.B)
+        dep = torch.from_numpy(tr["depth"]).to(torch.int32)[None]
+        nn = torch.tensor([tr["n_nodes"]], dtype=torch.int32)
+        R = synth.target_logits(b, dep, nn, device="cpu", base_seed=base_seed)[0].double().numpy()
+        work.append((x, R, int(b.anchor[0]), int(b.pos_base[0]), float(b.temperature[0]),
+                     int(b.seed[0]) & ((1 << 64) - 1)))
+    barrier.wait(timeout=900)
     t0 = time.perf_counter()
-    for n in range(n_trees):
-        sel = O.mixture_select_heap(xs[n], w.B)
-        tr = O.canonical_tree(sel, int(b.anchor[n]), w.B)
-        O.tree_mask(tr["parent"], tr["depth"], tr["n_nodes"], int(b.pos_base[n]), w.B + 1)
-        O.verify_walk(tr["node_token"], tr["parent"], tr["depth"], tr["n_nodes"], Rs[n],
-                      float(b.temperature[n]), int(b.seed[n]) & ((1 << 64) - 1), w.L)
-    dt = time.perf_counter() - t0
-    temps = sorted({float(b.temperature[n]) for n in range(n_trees)})
-    return {"value": n_trees / dt, "unit": "trees/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_trees} tree(s) of the {name} workload (T in {temps}), full oracle path, "
-                      f"{dt:.1f} s on one host core"}
+    per_tree = []
+    for x, R, anchor, pos, T, seed in work:
+        t1 = time.perf_counter()
+        sel = O.mixture_select_heap(x, w.B)
+        tr = O.canonical_tree(sel, anchor, w.B)
+        O.tree_mask(tr["parent"], tr["depth"], tr["n_nodes"], pos, w.B + 1)
+        O.verify_walk(tr["node_token"], tr["parent"], tr["depth"], tr["n_nodes"], R, T, seed, w.L)
+        per_tree.append(time.perf_counter() - t1)
+    results.put((t0, time.perf_counter(), per_tree))
+
+
+def cpu_baseline(name: str, base_seed: int, n_trees: int, max_workers: int = 16):
+    """Time the fp64 oracle end to end (log-softmax, ranks, heap, layout, mask,
+    walk) on trees 0 .. n_trees-1 of the workload, spread over a pool of this
+    host's cores (one single-threaded process per core, at most max_workers).
+    Runs before the GPU is touched, so the workers are plain forks."""
+    import multiprocessing as mp
+
+    cores = max(1, min(n_trees, max_workers, len(os.sched_getaffinity(0))))
+    ctx = mp.get_context("fork")
+    barrier = ctx.Barrier(cores)
+    results = ctx.Queue()
+    procs = [ctx.Process(target=_oracle_worker, args=(name, base_seed, list(range(c, n_trees, cores)), barrier,
+                                                       results))
+             for c in range(cores)]
+    for pr in procs:
+        pr.start()
+    out = [results.get(timeout=1800) for _ in procs]
+    for pr in procs:
+        pr.join(timeout=60)
+    assert all(pr.exitcode == 0 for pr in procs), [pr.exitcode for pr in procs]
+    wall = max(o[1] for o in out) - min(o[0] for o in out)
+    per_tree = sorted(t for o in out for t in o[2])
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"value": n_trees / wall, "unit": "trees/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_trees} trees of the {name} workload, full oracle path, {cores} single-threaded "
+                      f"processes, {wall:.1f} s wall, {sum(per_tree):.1f} s of CPU work",
+            "per_tree_s_one_core_median": statistics.median(per_tree), "host_cpu": model}
 
 
 def run_steps(P, logits, anchor, pos, R, temps, seeds, steps, warmup, stream):
@@ -174,6 +219,26 @@ def single_tree_latency(seed, steps, stream, name="single"):
     return total / steps
 
 
+def read_ceiling(buf, reps, stream):
+    """Rate of mfd_stream_read over `buf` (one read of every byte), GB/s: the
+    achievable streaming-read rate, next to the nominal HBM peak."""
+    from mixture_draft_tree_amd import mfdtree as M
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        M.mfd_stream_read(buf, sink, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        M.mfd_stream_read(buf, sink, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = buf.numel() * buf.element_size()
+    return {"kernel": "stream_read_kernel (mfd_stream_read)", "bytes": nbytes, "avg_launch_ms": ms,
+            "GBps": nbytes / (ms * 1e-3) / 1e9, "frac_of_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 STAGES = ["logsoftmax_topk", "mixture_threshold", "tree_build", "tree_mask", "verify_walk"]
 
 
@@ -203,6 +268,9 @@ def timed_workload(name, seed, steps, warmup, stream, diagnostics=False):
     total_ms, ev = run_steps(P, logits, anchor, pos, R, temps, seeds, steps, warmup, stream)
     stage = {nm: statistics.mean(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps))
              for i, nm in enumerate(STAGES)}
+    per_step = sorted(ev[s][0].elapsed_time(ev[s][5]) for s in range(steps))
+    q = lambda f: per_step[min(len(per_step) - 1, int(f * len(per_step)))]
+    stage["step_ms_percentiles"] = {"p10": q(0.1), "p50": statistics.median(per_step), "p90": q(0.9)}
     status = P.buf.status.cpu()
     assert int(status.abs().sum()) == 0, f"per-tree status flags set ({name}): {status.tolist()}"
     if diagnostics:
@@ -216,18 +284,22 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); trees are independent, "
               f"so N GPUs would each run this same per-GPU batch.", file=sys.stderr)
         sys.exit(2)
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
     name = args.workload
+    # the CPU oracle runs first, in forked processes, before anything touches the GPU
+    cpu = cpu_baseline(name, args.seed, args.cpu_baseline_trees) if args.cpu_baseline_trees > 0 else None
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
     stream = torch.cuda.current_stream()
     ms_per_step, stage_ms, N, w, P, logits = timed_workload(name, args.seed, args.steps, args.warmup, stream,
                                                             diagnostics=True)
     diag = stage_ms.pop("diagnostics")
+    pcts = stage_ms.pop("step_ms_percentiles")
 
     rows = N * w.K * w.L if P.modes is None else int(P.modes.sum()) * w.L   # rows the logits pass reads
     logits_bytes = rows * logits.shape[-1] * logits.element_size()
     lsm_ms = stage_ms["logsoftmax_topk"]
     achieved = logits_bytes / (lsm_ms * 1e-3) / 1e9
     tau = P.buf.tau.cpu().float()
+    ceiling = read_ceiling(logits, args.steps, stream)
     out = {
         "metric": METRIC,
         "value": N / (ms_per_step * 1e-3),
@@ -247,7 +319,10 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "lsm_topk_kernel (mfd_logsoftmax_topk)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(name),
-                     "algorithmic_bytes_per_launch": logits_bytes, "avg_launch_ms": lsm_ms},
+                     "algorithmic_bytes_per_launch": logits_bytes, "avg_launch_ms": lsm_ms,
+                     "read_ceiling": ceiling, "frac_of_read_ceiling": achieved / ceiling["GBps"],
+                     "valu_issue_frac": profile_field(SQ_FILE, name, "lsm_valu_issue_frac")},
+        "step_ms_percentiles": pcts,
         "stages_ms": stage_ms,
         "logits_GBps": achieved,
         "per_tree_latency_ms": ms_per_step if N == 1 else None,
@@ -257,17 +332,21 @@ def main():
     }
     if args.latency_steps > 0 and name != "single":
         out["single_tree_latency_ms"] = single_tree_latency(args.seed, args.latency_steps, stream)
+    if args.latency_steps > 0 and name == "batched":
+        out["stress_tree_latency_ms"] = single_tree_latency(args.seed, args.latency_steps, stream, "stress")
     if args.deep_workload != "none" and name == "batched":
         del P, logits
         dms, dstage, dN, dw, dP, _ = timed_workload(args.deep_workload, args.seed, args.steps, args.warmup, stream,
                                                     diagnostics=True)
         ddiag = dstage.pop("diagnostics")
+        dpcts = dstage.pop("step_ms_percentiles")
         out["deep"] = {
             "workload": f"{args.deep_workload}: {dN} trees, K={dw.K}, L={dw.L}, V={dw.V}, B={dw.B}, "
                         f"T pattern {list(dw.temperatures)}",
             "data": "synthetic (seeded; confident drafter: N(0,4) noise, 16 Zipf alternatives, each mode's future "
                     "at 16+N(0,2.25); target rows N(0,1) + 16 on one future up to a random deviation depth)",
-            "value": dN / (dms * 1e-3), "unit": "trees/s", "ms_per_step": dms, "stages_ms": dstage,
+            "value": dN / (dms * 1e-3), "unit": "trees/s", "ms_per_step": dms, "step_ms_percentiles": dpcts,
+            "stages_ms": dstage,
             "tau_mean": float(dP.buf.tau.cpu().float().mean()),
             "single_tree_latency_ms": (single_tree_latency(args.seed, args.latency_steps, stream, "deep")
                                        if args.latency_steps > 0 else None),
@@ -276,12 +355,14 @@ def main():
     if args.subset_workload != "none" and name == "batched":
         sms, sstage, sN, sw, sP, slog = timed_workload(args.subset_workload, args.seed, args.steps, args.warmup,
                                                        stream)
+        spcts = sstage.pop("step_ms_percentiles")
         sbytes = sN * sw.K * sw.L * slog.shape[-1] * slog.element_size()
         sgbs = sbytes / (sstage["logsoftmax_topk"] * 1e-3) / 1e9
         out["reduced_vocab"] = {
             "workload": f"{args.subset_workload}: {sN} trees, K={sw.K}, L={sw.L}, drafting over {slog.shape[-1]} of "
                         f"V={sw.V} tokens, B={sw.B}, T pattern {list(sw.temperatures)}",
-            "value": sN / (sms * 1e-3), "unit": "trees/s", "ms_per_step": sms, "stages_ms": sstage,
+            "value": sN / (sms * 1e-3), "unit": "trees/s", "ms_per_step": sms, "step_ms_percentiles": spcts,
+            "stages_ms": sstage,
             "logits_GBps": sgbs, "logits_frac_of_peak": sgbs / HBM_PEAK_GBS,
             "algorithmic_bytes_per_launch": sbytes, "tau_mean": float(sP.buf.tau.cpu().float().mean()),
         }
@@ -289,6 +370,7 @@ def main():
     if args.modes_workload != "none" and name == "batched":
         mms, mstage, mN, mw, mP, mlog = timed_workload(args.modes_workload, args.seed, args.steps, args.warmup,
                                                        stream)
+        mpcts = mstage.pop("step_ms_percentiles")
         kn = mP.modes.cpu()
         mbytes = int(kn.sum()) * mw.L * mw.V * mlog.element_size()
         mgbs = mbytes / (mstage["logsoftmax_topk"] * 1e-3) / 1e9
@@ -296,14 +378,15 @@ def main():
         out["per_request_modes"] = {
             "workload": f"{args.modes_workload}: {mN} trees of the confident-drafter shape, K={mw.K}, L={mw.L}, "
                         f"V={mw.V}, B={mw.B}, K_n cycling {list(mw.modes)}, T pattern {list(mw.temperatures)}",
-            "value": mN / (mms * 1e-3), "unit": "trees/s", "ms_per_step": mms, "stages_ms": mstage,
+            "value": mN / (mms * 1e-3), "unit": "trees/s", "ms_per_step": mms, "step_ms_percentiles": mpcts,
+            "stages_ms": mstage,
             "active_rows": int(kn.sum()) * mw.L, "logits_GBps": mgbs, "logits_frac_of_peak": mgbs / HBM_PEAK_GBS,
             "algorithmic_bytes_per_launch": mbytes,
             "tau_mean_by_modes": {str(k): float(mtau[kn == k].mean()) for k in sorted(set(kn.tolist()))},
         }
         del mP, mlog
-    if args.cpu_baseline_trees > 0:
-        out["cpu_baseline"] = cpu_baseline(name, args.seed, args.cpu_baseline_trees)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
     if args.copy_gib > 0:
         src = torch.ones(args.copy_gib << 28, dtype=torch.float32, device="cuda")

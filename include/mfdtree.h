@@ -336,6 +336,19 @@ mfd_status mfd_chimera_count(const int32_t* node_token, const int32_t* parent, c
                              const int32_t* n_nodes, int N, int Bp1, int L, const int32_t* future_a,
                              const int32_t* future_b, int32_t* count, hipStream_t stream);
 
+/*
+ * Measurement reference, not a step of the method: reads `bytes` bytes of
+ * device memory once (16-byte nontemporal loads spread over every compute
+ * unit) and XORs every 32-bit word into *sink.  Its rate is the HBM read rate
+ * that a pass reading its input exactly once can reach on this device, the
+ * achievable ceiling for mfd_logsoftmax_topk beside the nominal peak.
+ *
+ *   buf    device, 16-byte aligned (may be NULL when bytes is 0).
+ *   bytes  a multiple of 16; MFD_ERR_INVALID_ARG otherwise.
+ *   sink   device [1] uint32, caller-initialised: *sink ^= XOR of all words.
+ */
+mfd_status mfd_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

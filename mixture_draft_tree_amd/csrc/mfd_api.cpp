@@ -323,4 +323,13 @@ mfd_status mfd_chimera_count(const int32_t* node_token, const int32_t* parent, c
                   "mfd_chimera_count launch");
 }
 
+mfd_status mfd_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (bytes % 16) return fail(MFD_ERR_INVALID_ARG, "bytes must be a multiple of 16 (got %zu)", bytes);
+  if (bytes == 0) return ok();
+  REQUIRE_PTR(buf);
+  REQUIRE_PTR(sink);
+  if (reinterpret_cast<uintptr_t>(buf) % 16) return fail(MFD_ERR_INVALID_ARG, "buf is not 16-byte aligned");
+  return from_hip(mfd::launch_stream_read(buf, bytes, sink, stream), "mfd_stream_read launch");
+}
+
 }  // extern "C"

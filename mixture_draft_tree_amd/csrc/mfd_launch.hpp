@@ -45,6 +45,8 @@ hipError_t launch_tree_mask(const int32_t* parent, const int32_t* depth, const i
 
 size_t walk_ws_bytes(int N);
 
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 size_t covered_mass_ws_bytes(int N, int Bp1);
 hipError_t launch_covered_mass(const void* target, bool bf16, int N, int Bp1, long long V,
                                const int32_t* node_token, const int32_t* parent, const int32_t* n_nodes,

@@ -31,7 +31,7 @@ MFD_TREE_NONFINITE, MFD_TREE_CAPACITY, MFD_TREE_BAD_TEMPERATURE, MFD_TREE_BAD_MO
 EXPORTED = ["mfd_last_error", "mfd_version", "mfd_workspace_size", "mfd_logsoftmax_topk",
             "mfd_logsoftmax_topk_mapped", "mfd_mixture_threshold", "mfd_tree_build", "mfd_tree_mask",
             "mfd_verify_walk", "mfd_covered_mass", "mfd_chimera_count", "mfd_logsoftmax_topk_modes",
-            "mfd_mixture_threshold_modes", "mfd_tree_build_modes"]
+            "mfd_mixture_threshold_modes", "mfd_tree_build_modes", "mfd_stream_read"]
 
 _p = ctypes.c_void_p
 _i = ctypes.c_int
@@ -59,6 +59,8 @@ _lib.mfd_mixture_threshold_modes.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p,
 _lib.mfd_tree_build_modes.restype = _i
 _lib.mfd_tree_build_modes.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p,
                                       _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]
+_lib.mfd_stream_read.restype = _i
+_lib.mfd_stream_read.argtypes = [_p, _sz, _p, _p]
 _lib.mfd_tree_mask.restype = _i
 _lib.mfd_tree_mask.argtypes = [_p, _p, _p, _p, _i, _i, _p, _p, _p, _p]
 _lib.mfd_covered_mass.restype = _i
@@ -325,3 +327,14 @@ def mfd_chimera_count(node_token, parent, depth, n_nodes, L, future_a, future_b,
     _check(_lib.mfd_chimera_count(_ptr(node_token), _ptr(parent), _ptr(depth), _ptr(n_nodes), N, Bp1, L,
                                   _ptr(future_a), _ptr(future_b), _ptr(count), _stream_handle(stream)),
            "mfd_chimera_count")
+
+
+def mfd_stream_read(buf, sink, stream=None):
+    """Reads every byte of the contiguous GPU tensor `buf` once (the device's
+    streaming-read reference rate); sink: [1] int32 on the GPU, XOR-ed with the
+    XOR of all 32-bit words of buf."""
+    if not buf.is_contiguous() or buf.device.type != "cuda":
+        raise ValueError("buf must be a contiguous GPU tensor")
+    _want(sink, "sink", torch.int32, (1,))
+    nbytes = buf.numel() * buf.element_size()
+    _check(_lib.mfd_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream_handle(stream)), "mfd_stream_read")

@@ -147,6 +147,7 @@ class DraftBatch:
     tree_seeds: list            # python ints, one per tree
     vocab_map: Optional[torch.Tensor] = None  # [v_draft] int32 full ids (sorted) of the drafting tokens
     modes: Optional[torch.Tensor] = None      # [N] int32: active modes of each tree (None: all K)
+    start: int = 0                            # index of the first tree within the workload
 
 
 def _tiny_tree(w, g, device):
@@ -258,16 +259,18 @@ def vocab_subset(w: Workload, base_seed: int = 0, device="cpu") -> Optional[torc
     return torch.sort(ids).values.to(torch.int32)
 
 
-def draft_batch(name: str, base_seed: int = 0, device="cpu", N: Optional[int] = None) -> DraftBatch:
-    """Drafter logits and per-tree metadata for workload `name` (over the drafting
-    vocabulary when the workload has one; futures are then reported as full ids)."""
+def draft_batch(name: str, base_seed: int = 0, device="cpu", N: Optional[int] = None, start: int = 0) -> DraftBatch:
+    """Drafter logits and per-tree metadata for trees start .. start+N-1 of workload
+    `name` (over the drafting vocabulary when the workload has one; futures are then
+    reported as full ids).  Tree n is the same whatever batch it is drawn in."""
     w = WORKLOADS[name]
     N = w.N if N is None else N
     vmap = vocab_subset(w, base_seed, device)
     wd = dataclasses.replace(w, V=w.v_draft) if w.v_draft else w
     logits = torch.empty((N, w.K, w.L, wd.V), dtype=w.dtype, device=device)
     futs, chosen, anchors, seeds = [], [], [], []
-    for n in range(N):
+    idx = list(range(start, start + N))
+    for j, n in enumerate(idx):
         s = tree_seed(w.wid, n, base_seed)
         seeds.append(s)
         g = _gen(device, s)
@@ -281,20 +284,20 @@ def draft_batch(name: str, base_seed: int = 0, device="cpu", N: Optional[int] = 
                 fut = vmap.to(torch.int64)[fut]
         if w.modes:
             x[w.modes[n % len(w.modes)]:] = float("nan")
-        logits[n] = x.to(w.dtype)
+        logits[j] = x.to(w.dtype)
         futs.append(fut)
         chosen.append(int(_randint(g, fut.shape[0], (1,), device).item()))
         anchors.append(int(_randint(g, w.V, (1,), device).item()))
-    temps = torch.tensor([w.temperatures[n % len(w.temperatures)] for n in range(N)], dtype=torch.float32)
+    temps = torch.tensor([w.temperatures[n % len(w.temperatures)] for n in idx], dtype=torch.float32)
     seed_t = torch.tensor([(s ^ 0x5DEECE66D) & ((1 << 63) - 1) for s in seeds], dtype=torch.int64)
     return DraftBatch(
         workload=w, logits=logits, futures=torch.stack(futs),
         chosen_mode=torch.tensor(chosen, dtype=torch.int64),
         anchor=torch.tensor(anchors, dtype=torch.int32),
-        pos_base=torch.tensor([1000 + 17 * n for n in range(N)], dtype=torch.int64),
+        pos_base=torch.tensor([1000 + 17 * n for n in idx], dtype=torch.int64),
         temperature=temps, seed=seed_t, tree_seeds=seeds, vocab_map=vmap,
-        modes=(torch.tensor([w.modes[n % len(w.modes)] for n in range(N)], dtype=torch.int32)
-               if w.modes else None))
+        modes=(torch.tensor([w.modes[n % len(w.modes)] for n in idx], dtype=torch.int32)
+               if w.modes else None), start=start)
 
 
 def target_logits(batch: DraftBatch, depth: torch.Tensor, n_nodes: torch.Tensor,
@@ -315,7 +318,7 @@ def target_logits(batch: DraftBatch, depth: torch.Tensor, n_nodes: torch.Tensor,
     depth = depth.to("cpu")
     n_nodes = n_nodes.to("cpu")
     for n in range(N):
-        g = _gen(device, tree_seed(w.wid + 100, n, base_seed))
+        g = _gen(device, tree_seed(w.wid + 100, batch.start + n, base_seed))
         r = torch.randn((Bp1, w.V), generator=g, device=device, dtype=torch.float32)
         F = batch.futures[n, int(batch.chosen_mode[n])].to(device).clone()
         if w.dev_lo > 0:

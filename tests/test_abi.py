@@ -189,3 +189,12 @@ def test_modes_calls_reject_before_launch():
     assert bld(*args, None, *outs, None, FAKE, nb, None) == M.MFD_ERR_INVALID_ARG
     assert bld(*args, FAKE, *outs, None, None, 0, None) == M.MFD_ERR_WORKSPACE
     assert bld(*[None] * 6, 0, 8, 15, 256, 256, None, *[None] * 6, None, None, 0, None) == M.MFD_OK
+
+
+def test_stream_read_rejects():
+    f = M._lib.mfd_stream_read
+    assert f(FAKE, 17, FAKE, None) == M.MFD_ERR_INVALID_ARG
+    assert "multiple of 16" in M.last_error()
+    assert f(ctypes.c_void_p(0x100008), 32, FAKE, None) == M.MFD_ERR_INVALID_ARG
+    assert f(FAKE, 32, None, None) == M.MFD_ERR_INVALID_ARG
+    assert f(None, 0, None, None) == M.MFD_OK

@@ -523,3 +523,19 @@ def test_band_criterion():
     y[1, 0] = [0.0, 1.0, -2.0, -1.0]
     s2 = O.mixture_select_heap(y, 1, band=1e-4)
     assert s2.selected == [(0,)] and not O.band_is_exact(y, s2)
+
+
+def test_synth_tree_is_independent_of_its_batch():
+    """Tree n of a workload is drawn the same whether it comes in a batch from 0 or
+    on its own (the pooled oracle timing draws trees one by one)."""
+    full = synth.draft_batch("tiny", base_seed=4, N=5)
+    part = synth.draft_batch("tiny", base_seed=4, N=2, start=3)
+    assert torch.equal(full.logits[3:], part.logits)
+    for f in ("anchor", "pos_base", "temperature", "seed", "futures", "chosen_mode"):
+        assert torch.equal(getattr(full, f)[3:], getattr(part, f)), f
+    dep = torch.zeros((5, 9), dtype=torch.int32)
+    nn = torch.full((5,), 3, dtype=torch.int32)
+    dep[:, 1:3] = 1
+    R_full = synth.target_logits(full, dep, nn, base_seed=4)
+    R_part = synth.target_logits(part, dep[3:], nn[3:], base_seed=4)
+    assert torch.equal(R_full[3:], R_part)
