@@ -192,6 +192,99 @@ __device__ __forceinline__ void block_sort_single(uint64_t& a, uint64_t* xchg) {
   }
 }
 
+// block_bitonic_sort's network with each wave's segment of P keys held in
+// registers: thread (wave w, lane l) holds elements w*64E + e*64 + l,
+// e < E.  Strides below 64 are lane shuffles, strides from 64 to 64E - 1 swap
+// registers within a thread, and only strides of a whole segment or more
+// go through LDS, one barrier each (plus one on either side of such a run).
+// P is a power of two: 64 <= P <= NT for E = 1, P = E * NT for E > 1.
+// Waves past P/(64E) hold nothing and only join the barriers.
+template <int NT, int E>
+__device__ __forceinline__ void block_sort_regs(uint64_t* a, int P) {
+  constexpr int S = kWave * E;
+  const int W = P / S;
+  const int w = wave_id(), lane = lane_id();
+  const bool act = w < W;
+  const int base = w * S;
+  uint64_t r[E];
+  if (act) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) r[e] = a[base + e * kWave + lane];
+  }
+  for (int k = 2; k <= P; k <<= 1) {
+    int j = k >> 1;
+    if (j >= S) {
+      if (act) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) a[base + e * kWave + lane] = r[e];
+      }
+      __syncthreads();
+      for (; j >= S; j >>= 1) {
+        for (int t = (int)threadIdx.x; t < (P >> 1); t += NT) {
+          const int i = 2 * t - (t & (j - 1));
+          const int i2 = i + j;
+          const bool up = (i & k) == 0;
+          const uint64_t x = a[i], y = a[i2];
+          if ((x > y) == up) {
+            a[i] = y;
+            a[i2] = x;
+          }
+        }
+        __syncthreads();
+      }
+      if (act) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) r[e] = a[base + e * kWave + lane];
+      }
+    }
+    if (!act) continue;
+    for (; j >= kWave; j >>= 1) {
+      const int m = j / kWave;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (e & m) continue;
+        const int e2 = e | m;
+        const bool up = ((base + e * kWave + lane) & k) == 0;
+        const uint64_t x = r[e], y = r[e2];
+        const bool sw = (x > y) == up;
+        r[e] = sw ? y : x;
+        r[e2] = sw ? x : y;
+      }
+    }
+    for (; j > 0; j >>= 1) {
+      const bool lower = (lane & j) == 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const uint64_t o = shfl_xor_u64(r[e], j);
+        const bool up = ((base + e * kWave + lane) & k) == 0;
+        const bool keep_min = lower == up;
+        r[e] = keep_min ? (r[e] < o ? r[e] : o) : (r[e] < o ? o : r[e]);
+      }
+    }
+  }
+  if (act) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) a[base + e * kWave + lane] = r[e];
+  }
+  __syncthreads();
+}
+
+// Sorts a[0, P) ascending, P a power of two (a[] written and visible to the
+// block on entry, sorted and visible on return).  Sizes from 64 to 4*NT take
+// the register-resident network, others the LDS one.  Every thread calls it.
+template <int NT>
+__device__ __forceinline__ void block_sort_keys(uint64_t* a, int P) {
+  if (P < kWave || P > 4 * NT) {
+    block_bitonic_sort<NT>(a, P);
+  } else if (P <= NT) {
+    block_sort_regs<NT, 1>(a, P);
+  } else if (P <= 2 * NT) {
+    block_sort_regs<NT, 2>(a, P);
+  } else {
+    block_sort_regs<NT, 4>(a, P);
+  }
+}
+
 // Sorts the 64 values held one per lane of a wave descending (lane 0 gets the
 // largest).  Wave-level, no barrier.
 __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t a) {

@@ -601,7 +601,7 @@ __device__ void level_search(const TreeArgs& a, const Tree& t, int n, Ctl& ctl, 
     const int P = next_pow2(C);
     for (int c = C + tid; c < P; c += kNT) keys[c] = ~0ull;
     __syncthreads();
-    block_bitonic_sort<kNT>(keys, P);
+    block_sort_keys<kNT>(keys, P);
 
     // 3. runs of equal (parent, token) are one node
     const int node0 = ctl.node_count, ent0 = ctl.ent_count;
@@ -883,7 +883,7 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
         const int P = next_pow2(cnt);
         for (int c = cnt + tid; c < P; c += kNT) keys[c] = ~0ull;
         __syncthreads();
-        block_bitonic_sort<kNT>(keys, P);
+        block_sort_keys<kNT>(keys, P);
       }
       for (int i = tid; i < cnt; i += kNT) {
         int pos = i;
