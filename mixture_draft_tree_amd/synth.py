@@ -332,3 +332,92 @@ def target_logits(batch: DraftBatch, depth: torch.Tensor, n_nodes: torch.Tensor,
             r[rows.to(device), F[d[rows].to(device)]] += w.target_boost
         out[n] = r.to(w.dtype)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Drafter hidden states and LM head (the fused-logits path)
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class LmHeadWorkload:
+    name: str
+    wid: int
+    K: int
+    L: int
+    V: int
+    D: int        # hidden width (2560 for the MFD drafter of Qwen3.5-4B)
+    B: int
+    N: int
+    grid: bool    # values on a coarse binary grid (every partial sum exact in fp32)
+
+
+LMHEAD_WORKLOADS = {
+    # small shapes: ragged row and vocabulary tiles, whole-row sample
+    "lmhead_small": LmHeadWorkload("lmhead_small", 20, 2, 5, 1000, 128, 32, 3, True),
+    "lmhead_ragged": LmHeadWorkload("lmhead_ragged", 21, 3, 7, 4133, 96, 64, 5, False),
+    # two row tiles (the second ragged) and a sampled threshold
+    "lmhead_mid": LmHeadWorkload("lmhead_mid", 22, 8, 15, 40000, 256, 256, 2, True),
+    # the MFD drafter's shape: K=8 modes x 15 positions over V=151936 at D=2560
+    "lmhead_single": LmHeadWorkload("lmhead_single", 23, 8, 15, 151936, 2560, 256, 1, False),
+    "lmhead_single_grid": LmHeadWorkload("lmhead_single_grid", 24, 8, 15, 151936, 2560, 256, 1, True),
+    "lmhead_batched": LmHeadWorkload("lmhead_batched", 25, 8, 15, 151936, 2560, 256, 64, False),
+}
+
+
+@dataclasses.dataclass
+class LmHeadBatch:
+    workload: LmHeadWorkload
+    hidden: torch.Tensor     # [N, K, L, D] bf16
+    weight: torch.Tensor     # [V, D] bf16
+    futures: torch.Tensor    # [N, K, L] int64: each mode's future
+    anchor: torch.Tensor     # [N] int32
+
+
+def lmhead_weight(w: LmHeadWorkload, base_seed: int = 0, device="cpu") -> torch.Tensor:
+    """The LM head [V, D] bf16, shared by every tree of the workload.
+
+    Gaussian recipe: N(0, (3 / sqrt(D))^2), so logits of a unit hidden state are
+    about N(0, 9) like the drafter noise of the `single` workload.  Grid recipe:
+    integers in [-8, 8] times 2^-5."""
+    g = _gen(device, tree_seed(w.wid, 1 << 20, base_seed))
+    if w.grid:
+        x = (torch.randint(-8, 9, (w.V, w.D), generator=g, device=device).to(torch.float32)) * 2.0 ** -5
+    else:
+        x = torch.randn((w.V, w.D), generator=g, device=device, dtype=torch.float32) * (3.0 / math.sqrt(w.D))
+    return x.to(torch.bfloat16)
+
+
+def lmhead_batch(name: str, base_seed: int = 0, device="cpu", N: Optional[int] = None) -> LmHeadBatch:
+    """Hidden states [N, K, L, D] whose logits favour each mode's future.
+
+    Futures are drawn as for the mixture workloads (shared prefix, then a few
+    resampled positions per mode).  Gaussian recipe: h = N(0, 1) + (8/9) W[f],
+    so the future token's logit gains about 8 (|W[f]|^2 is about 9).  Grid
+    recipe: h = integers in [-4, 4] times 2^-2, plus 2^-2 sign(W[f, d]) on a
+    random set of min(D, 240) coordinates d.  On the grid every product is a
+    multiple of 2^-7 below 0.32 in magnitude, so every partial sum of D <= 2560
+    of them is a multiple of 2^-7 below 2^10: exact in fp32 in any order."""
+    w = LMHEAD_WORKLOADS[name]
+    N = w.N if N is None else N
+    W = lmhead_weight(w, base_seed, device)
+    Wf = W.to(torch.float32)
+    H = torch.empty((N, w.K, w.L, w.D), dtype=torch.bfloat16, device=device)
+    futs, anchors = [], []
+    for n in range(N):
+        g = _gen(device, tree_seed(w.wid, n, base_seed))
+        fut = _mode_futures(w, g, device)
+        if w.grid:
+            h = torch.randint(-4, 5, (w.K, w.L, w.D), generator=g, device=device).to(torch.float32) * 0.25
+            nb = min(w.D, 240)
+            for k in range(w.K):
+                for i in range(w.L):
+                    dims = torch.randperm(w.D, generator=g, device=device)[:nb]
+                    h[k, i, dims] += 0.25 * torch.sign(Wf[fut[k, i], dims])
+        else:
+            h = torch.randn((w.K, w.L, w.D), generator=g, device=device, dtype=torch.float32)
+            h += (8.0 / 9.0) * Wf[fut]
+        H[n] = h.to(torch.bfloat16)
+        futs.append(fut)
+        anchors.append(int(_randint(g, w.V, (1,), device).item()))
+    return LmHeadBatch(workload=w, hidden=H, weight=W, futures=torch.stack(futs),
+                       anchor=torch.tensor(anchors, dtype=torch.int32))

@@ -40,7 +40,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 __all__ = [
-    "lse_rows", "rank_order", "prefix_norms", "MixtureSelection",
+    "lse_rows", "rank_order", "prefix_norms", "lmhead_logits", "lmhead_abs_bound", "MixtureSelection",
     "mixture_select_heap", "mixture_select_bruteforce", "ddtree_product_select",
     "mode_scores", "union_at_cutoff", "canonical_tree", "tree_mask",
     "pack_mask_words", "philox4x64_10", "gumbel_noise", "verify_walk",
@@ -91,6 +91,38 @@ def prefix_norms(lse: np.ndarray) -> np.ndarray:
             acc = acc + float(lse[k, i])
             norm[k, i + 1] = acc
     return norm
+
+
+def lmhead_logits(hidden: np.ndarray, weight: np.ndarray) -> np.ndarray:
+    """Drafter logits from final hidden states and the LM head, fp64.
+
+    The drafter has no LM head of its own: it uses its target's at run time
+    ([MC] "Model", "Parameters"), and the pages' tree step can take the logits
+    fused with that head ([MC] "Usage", fused_logits=True).  A language model's
+    logit for token v is the inner product of the hidden state with row v of
+    the head:  x[..., v] = sum_d hidden[..., d] * weight[v, d].  hidden has
+    shape [..., D], weight [V, D]; the result has shape [..., V].  Its rows then
+    go through lse_rows and rank_order like any other logits.
+    """
+    h = np.asarray(hidden, dtype=np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    if h.shape[-1] != w.shape[1]:
+        raise ValueError(f"hidden width {h.shape[-1]} != head width {w.shape[1]}")
+    return h @ w.T
+
+
+def lmhead_abs_bound(hidden: np.ndarray, weight: np.ndarray, unit: float = 2.0 ** -23) -> np.ndarray:
+    """Bound on |computed - exact| for the logits of lmhead_logits when the D
+    products (exact: bf16 times bf16 fits an fp32 significand) are added in
+    binary32 in any order:  gamma_D * sum_d |h_d w_vd|, gamma_n = n u / (1 - n u)
+    (Higham, Accuracy and Stability of Numerical Algorithms, 2nd ed., sec. 4.2).
+    unit = 2^-23 covers rounding toward zero as well as to nearest.
+    """
+    h = np.abs(np.asarray(hidden, dtype=np.float64))
+    w = np.abs(np.asarray(weight, dtype=np.float64))
+    n = h.shape[-1]
+    gamma = n * unit / (1.0 - n * unit)
+    return gamma * (h @ w.T)
 
 
 # ---------------------------------------------------------------------------

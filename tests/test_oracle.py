@@ -539,3 +539,71 @@ def test_synth_tree_is_independent_of_its_batch():
     R_full = synth.target_logits(full, dep, nn, base_seed=4)
     R_part = synth.target_logits(part, dep[3:], nn[3:], base_seed=4)
     assert torch.equal(R_full[3:], R_part)
+
+
+# ---------------------------------------------------------------------------
+# Drafter logits from hidden states and the LM head (fused-logits path)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["lmhead_small", "lmhead_mid"])
+def test_lmhead_logits_grid_equals_integer_product(name):
+    # Grid inputs are integers times 2^-2 (hidden) and 2^-5 (head): the logits
+    # are an integer matrix product times 2^-7, computed here in int64.
+    b = synth.lmhead_batch(name)
+    h = b.hidden.float().numpy()
+    w = b.weight.float().numpy()
+    hi = np.rint(h * 4).astype(np.int64)
+    wi = np.rint(w * 32).astype(np.int64)
+    assert np.array_equal(hi / 4.0, h) and np.array_equal(wi / 32.0, w)
+    exact = (hi.reshape(-1, h.shape[-1]) @ wi.T).reshape(h.shape[:-1] + (w.shape[0],))
+    x = O.lmhead_logits(h, w)
+    assert np.array_equal(x * 128.0, exact.astype(np.float64))
+
+
+def test_lmhead_logits_against_fsum_loops():
+    # Correctly rounded sums of the exact bf16 products, one logit at a time.
+    g = torch.Generator().manual_seed(7)
+    h = torch.randn((2, 3, 40), generator=g).to(torch.bfloat16).float().numpy()
+    w = torch.randn((11, 40), generator=g).to(torch.bfloat16).float().numpy()
+    x = O.lmhead_logits(h, w)
+    assert x.shape == (2, 3, 11)
+    for a in range(2):
+        for i in range(3):
+            for v in range(11):
+                ref = math.fsum(float(h[a, i, d]) * float(w[v, d]) for d in range(40))
+                assert abs(x[a, i, v] - ref) <= 1e-12 * max(1.0, abs(ref))
+    with pytest.raises(ValueError):
+        O.lmhead_logits(h, w[:, :39])
+
+
+def test_lmhead_bound_covers_fp32_summation_orders():
+    # The bound holds for fp32 sums of the exact products in several orders,
+    # rounding to nearest (numpy) and toward zero (emulated by truncating).
+    g = torch.Generator().manual_seed(11)
+    D = 512
+    h = torch.randn((6, D), generator=g).to(torch.bfloat16).float().numpy()
+    w = (torch.randn((50, D), generator=g) * 0.1).to(torch.bfloat16).float().numpy()
+    exact = O.lmhead_logits(h, w)
+    bound = O.lmhead_abs_bound(h, w)
+    prods = (h[:, None, :].astype(np.float32) * w[None, :, :].astype(np.float32))  # exact in fp32
+    seq = np.zeros(prods.shape[:2], dtype=np.float32)
+    for d in range(D):
+        seq = seq + prods[:, :, d]
+    rev = np.zeros(prods.shape[:2], dtype=np.float32)
+    for d in reversed(range(D)):
+        rev = rev + prods[:, :, d]
+    blk = prods.reshape(6, 50, D // 16, 16).sum(axis=-1, dtype=np.float32).sum(axis=-1, dtype=np.float32)
+
+    def trunc_add(a, b):
+        s = a.astype(np.float64) + b.astype(np.float64)
+        r = s.astype(np.float32)
+        over = np.abs(r.astype(np.float64)) > np.abs(s)
+        return np.where(over, np.nextafter(r, np.float32(0)), r)
+
+    tz = np.zeros(prods.shape[:2], dtype=np.float32)
+    for d in range(D):
+        tz = trunc_add(tz, prods[:, :, d])
+    for got in (seq, rev, blk, tz):
+        err = np.abs(got.astype(np.float64) - exact)
+        assert np.all(err <= bound)
+    assert np.max(np.abs(tz.astype(np.float64) - exact)) > 0  # the orders do round
