@@ -81,7 +81,8 @@ typedef enum mfd_op {
   MFD_OP_TREE_BUILD = 2,
   MFD_OP_TREE_MASK = 3,
   MFD_OP_VERIFY_WALK = 4,
-  MFD_OP_COVERED_MASS = 5
+  MFD_OP_COVERED_MASS = 5,
+  MFD_OP_LMHEAD_TOPK = 6
 } mfd_op;
 
 #define MFD_TREE_NONFINITE 1
@@ -237,6 +238,40 @@ mfd_status mfd_tree_build_modes(const int32_t* topk_id, const float* topk_raw, c
                                 int32_t* node_token, int32_t* parent, int32_t* depth, double* score,
                                 int32_t* best_mode, int32_t* n_nodes, int32_t* status,
                                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Fused LM head + per-(mode, position) log-softmax and top-k.  The drafter
+ * uses its target's LM head at run time (model card "MFD drafter for
+ * Qwen3.5-4B", "Model" and "Parameters"), and the pages' interface runs the
+ * tree step with fused_logits=True (same card, "Usage").  The logits
+ * x[r, v] = sum_d hidden[r, d] * weight[v, d] are formed on the matrix cores
+ * (bf16 products, exact; fp32 accumulation) and reduced in the same pass, so
+ * the [N, K, L, V] logits are never written.  Outputs are those of
+ * mfd_logsoftmax_topk over x.
+ *
+ *   hidden    device [N, K, L, D] bf16: the drafter's final hidden states, row
+ *             r = (n, k, i); 16-byte aligned.
+ *   weight    device [V, D] bf16: the LM head, one row per token; 16-byte aligned.
+ *   D         hidden width, a multiple of 32 in [32, 16384].
+ *   lse, topk_id, topk_raw, topk_logp: as for mfd_logsoftmax_topk; topk_raw
+ *             is the fp32 logit as accumulated (ties break by token id).
+ *   status    device [N] int32 or NULL: MFD_TREE_NONFINITE for a tree with a
+ *             non-finite logit; MFD_TREE_CAPACITY for a tree with a row whose
+ *             candidate list overflowed the workspace (rows whose logits pile
+ *             up at one value, e.g. all equal).  That row's topk_id is -1 and
+ *             topk_raw -inf; its lse is valid.  Such a tree can be redone
+ *             unfused (write the logits, call mfd_logsoftmax_topk).
+ *   ws        device workspace of at least mfd_workspace_size(MFD_OP_LMHEAD_TOPK,
+ *             N, K, L, V, k) bytes (B = k there), 256-byte aligned.  Its
+ *             contents on entry do not matter.
+ *
+ * Errors (nothing launched): MFD_ERR_INVALID_ARG for shapes outside the limits
+ * above, k outside [1, min(V, 2048)], NULL or misaligned pointers;
+ * MFD_ERR_WORKSPACE for a missing, small or misaligned workspace.
+ */
+mfd_status mfd_lmhead_logsoftmax_topk(const void* hidden, const void* weight, int N, int K, int L, int D, int V,
+                                      int k, double* lse, int32_t* topk_id, float* topk_raw, float* topk_logp,
+                                      int32_t* status, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Tree-verification inputs (model card summary: the target checks the whole

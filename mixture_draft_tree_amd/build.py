@@ -26,7 +26,7 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
-SOURCES = ["lsm_topk.hip", "tree_build.hip", "tree_mask.hip", "verify_walk.hip", "diagnostics.hip", "stream_read.hip",
+SOURCES = ["lsm_topk.hip", "lmhead_topk.hip", "tree_build.hip", "tree_mask.hip", "verify_walk.hip", "diagnostics.hip", "stream_read.hip",
            "mfd_api.cpp"]
 
 

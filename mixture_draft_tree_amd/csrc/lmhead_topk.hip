@@ -1,0 +1,464 @@
+// Fused LM head + per-row log-softmax and top-k (mfd_lmhead_logsoftmax_topk).
+//
+// The drafter shares its target's LM head (model card "MFD drafter for
+// Qwen3.5-4B", "Model" and "Parameters"), and the pages' Python interface
+// turns on a fused logits path (same card, "Usage": fused_logits=True).  Here
+// the drafter's final hidden states H [M, D] (M = N*K*L rows) meet the head
+// W [V, D] on the matrix cores, and each row's log-normaliser and k best
+// tokens come out without the [M, V] logits ever being stored.
+//
+// Four launches on the caller's stream:
+//   1. lmh_tile_kernel<true>   (sample)  S spread V-tiles of the product; per
+//      row the maximum of every disjoint group of 4 columns goes to `samp`.
+//   2. lmh_threshold_kernel    per row: thr = the k-th largest of those group
+//      maxima.  They are k distinct elements of the row, so the row's k-th
+//      largest logit is >= thr: every top-k element passes x >= thr.  Rows with
+//      fewer than k groups take thr = "everything".
+//   3. lmh_tile_kernel<false>  (main)  every tile of the product; per row and
+//      tile the partial (max, sum exp(x - max)); every logit >= thr is appended
+//      to its row's candidate list.
+//   4. lmh_select_kernel       per row: lse from the partials (fp64), the exact
+//      k-th largest (logit desc, id asc) among the candidates, those k sorted.
+//
+// Tiles: 128 rows x 256 vocabulary columns per 256-thread workgroup, k in
+// steps of 32 through double-buffered LDS, four waves of 64 x 128 each built
+// from v_mfma_f32_32x32x16_bf16 (fp32 accumulation).  Each product element is
+// computed from the same operands in the same k order in both tile launches,
+// so the sample and main launches see identical logits.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "mfd_device.hpp"
+#include "mfd_launch.hpp"
+
+namespace mfd {
+namespace {
+
+constexpr int kBM = 128, kBN = 256, kBK = 32, kNT = 256;
+constexpr int kLdk = kBK + 8;  // bf16 per LDS row: 80 bytes, conflict-free 16-byte reads
+constexpr int kGroupsPerTile = 64;
+constexpr int kSelNT = 256;
+constexpr int kSelLdsCap = 8192;  // candidates a select workgroup holds in LDS
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+struct LmhArgs {
+  const uint16_t* H;  // [M, D] bf16 bits
+  const uint16_t* W;  // [V, D] bf16 bits
+  int M, D, V, T, S, rows_per_tree;
+  uint32_t* samp;       // [M, S * 64] group-maximum keys (0 = empty group)
+  uint32_t* thr;        // [M] candidate threshold keys
+  float2* part;         // [M, 2T] (max, sum exp(x - max)) per tile and wave column
+  uint64_t* cand;       // [M, C] candidate composites
+  int* cand_count;      // [M]
+  int C;
+  int32_t* status;      // [N] or null
+};
+
+__device__ __forceinline__ uint64_t cand_composite(uint32_t key, uint32_t col) {
+  return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - col);
+}
+
+// Tile t of the XCD-aware order: workgroup b runs on XCD b % 8 and takes the
+// (b / 8)-th tile of that XCD's contiguous share.  The shares cut a linear
+// order of (row group, vocabulary tile, row tile in group), a row group being
+// ceil(nM / 8) row tiles, so one XCD works through few row tiles and all their
+// vocabulary tiles: the weight tile is fetched once into that XCD's L2 for the
+// row tiles of its group, and the group's hidden rows stay warm.
+__device__ __forceinline__ bool tile_of(int b, int nM, int nVt, int* m_out, int* v_out) {
+  const long long ntiles = (long long)nM * nVt;
+  const long long per = (ntiles + 7) / 8;
+  const long long t = (long long)(b & 7) * per + (b >> 3);
+  if (t >= ntiles) return false;
+  const int G = (nM + 7) / 8;
+  const long long gsz_full = (long long)G * nVt;
+  const int mg = (int)(t / gsz_full);
+  const long long r = t - (long long)mg * gsz_full;
+  const int gsz = min(G, nM - mg * G);
+  *v_out = (int)(r / gsz);
+  *m_out = mg * G + (int)(r % gsz);
+  return true;
+}
+
+template <bool SAMPLE>
+__global__ void __launch_bounds__(kNT) lmh_tile_kernel(LmhArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kBM][kLdk];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kBN][kLdk];
+  __shared__ uint32_t sthr[kBM];
+
+  const int nM = (a.M + kBM - 1) / kBM;
+  const int nVt = SAMPLE ? a.S : a.T;
+  int mt, vt_i;
+  if (!tile_of((int)blockIdx.x, nM, nVt, &mt, &vt_i)) return;  // whole workgroup, before any barrier
+  const int vt = SAMPLE ? (int)(((long long)vt_i * a.T) / a.S) : vt_i;
+  const int row0 = mt * kBM, col0 = vt * kBN;
+  const int tid = (int)threadIdx.x, lane = lane_id(), w = wave_id();
+  const int wm = w >> 1, wn = w & 1;
+  const int D = a.D;
+
+  if (!SAMPLE) {
+    for (int i = tid; i < kBM; i += kNT) sthr[i] = row0 + i < a.M ? a.thr[row0 + i] : 0xFFFFFFFFu;
+  }
+
+  // global -> register chunks of 8 bf16: A 512 per stage (2 per thread), B 1024
+  // (4 per thread).  Chunk c is row c / 4, k-offset 8 (c % 4) of the stage.
+  // Rows past the matrix read its last row (their results are dropped).
+  const int q8 = (tid & 3) * 8, r0 = tid >> 2;
+  const uint16_t* a0p = a.H + (size_t)min(row0 + r0, a.M - 1) * D + q8;
+  const uint16_t* a1p = a.H + (size_t)min(row0 + r0 + 64, a.M - 1) * D + q8;
+  const uint16_t* b0p = a.W + (size_t)min(col0 + r0, a.V - 1) * D + q8;
+  const uint16_t* b1p = a.W + (size_t)min(col0 + r0 + 64, a.V - 1) * D + q8;
+  const uint16_t* b2p = a.W + (size_t)min(col0 + r0 + 128, a.V - 1) * D + q8;
+  const uint16_t* b3p = a.W + (size_t)min(col0 + r0 + 192, a.V - 1) * D + q8;
+  uint4 ra0, ra1, rb0, rb1, rb2, rb3;
+#define LMH_GLOAD(k0)                                        \
+  do {                                                       \
+    ra0 = *reinterpret_cast<const uint4*>(a0p + (k0));       \
+    ra1 = *reinterpret_cast<const uint4*>(a1p + (k0));       \
+    rb0 = *reinterpret_cast<const uint4*>(b0p + (k0));       \
+    rb1 = *reinterpret_cast<const uint4*>(b1p + (k0));       \
+    rb2 = *reinterpret_cast<const uint4*>(b2p + (k0));       \
+    rb3 = *reinterpret_cast<const uint4*>(b3p + (k0));       \
+  } while (0)
+#define LMH_LSTORE(buf)                                               \
+  do {                                                                \
+    *reinterpret_cast<uint4*>(&sA[buf][r0][q8]) = ra0;                \
+    *reinterpret_cast<uint4*>(&sA[buf][r0 + 64][q8]) = ra1;           \
+    *reinterpret_cast<uint4*>(&sB[buf][r0][q8]) = rb0;                \
+    *reinterpret_cast<uint4*>(&sB[buf][r0 + 64][q8]) = rb1;           \
+    *reinterpret_cast<uint4*>(&sB[buf][r0 + 128][q8]) = rb2;          \
+    *reinterpret_cast<uint4*>(&sB[buf][r0 + 192][q8]) = rb3;          \
+  } while (0)
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  // lane l feeds row (or column) l % 32 of a 32 x 16 operand, k-half l / 32
+  const int lr = lane & 31, lk = (lane >> 5) * 8;
+  const int nS = D / kBK;
+  LMH_GLOAD(0);
+  LMH_LSTORE(0);
+  __syncthreads();
+  for (int s = 0; s < nS; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < nS) LMH_GLOAD((s + 1) * kBK);
+#pragma unroll
+    for (int kk = 0; kk < kBK; kk += 16) {
+      bf16x8 af[2], bfv[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][wm * 64 + i * 32 + lr][kk + lk]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bfv[j] = *reinterpret_cast<const bf16x8*>(&sB[buf][wn * 128 + j * 32 + lr][kk + lk]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
+    }
+    if (s + 1 < nS) LMH_LSTORE(buf ^ 1);
+    __syncthreads();
+  }
+#undef LMH_GLOAD
+#undef LMH_LSTORE
+
+  // Epilogue.  Accumulator element e of block (i, j) is row
+  // wm*64 + i*32 + 8*(e/4) + 4*(lane/32) + e%4 and column wn*128 + j*32 + lane%32
+  // of the tile.  For one (i, e) a lane holds 4 columns of one row (j = 0..3):
+  // a group; the 32 lanes of a half-wave hold that row's other groups.
+  const uint64_t half = lane < 32 ? 0x00000000FFFFFFFFull : 0xFFFFFFFF00000000ull;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int rt = wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      const int grow = row0 + rt;
+      float x[4];
+      bool ok[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[j] = acc[i][j][e];
+        ok[j] = col0 + wn * 128 + j * 32 + lr < a.V;
+      }
+      if (SAMPLE) {
+        uint32_t g = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (ok[j]) g = max(g, f32_key(__float_as_uint(x[j])));
+        if (grow < a.M)
+          a.samp[(size_t)grow * ((size_t)a.S * kGroupsPerTile) + (size_t)vt_i * kGroupsPerTile + wn * 32 + lr] = g;
+      } else {
+        // partial log-sum-exp over this wave's 128 columns of the row
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (ok[j]) {
+            bad |= !__builtin_isfinite(x[j]);
+            mx = fmaxf(mx, x[j]);
+          }
+        }
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+        float sm = 0.0f;
+        if (mx > -INFINITY) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (ok[j]) sm += __expf(x[j] - mx);
+        }
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) sm += __shfl_xor(sm, o, kWave);
+        if (lr == 0 && grow < a.M) a.part[(size_t)grow * (2 * (size_t)a.T) + 2 * vt + wn] = make_float2(mx, sm);
+
+        // candidates: logits at or above the row's threshold
+        const uint32_t th = sthr[rt];
+        bool p[4];
+        uint32_t kx[4];
+        int mine = 0, before = 0, total = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          kx[j] = f32_key(__float_as_uint(x[j]));
+          p[j] = ok[j] && kx[j] >= th;
+          const uint64_t b = __ballot(p[j]);
+          before += __popcll(b & half & lt);
+          total += __popcll(b & half);
+          mine += p[j] ? 1 : 0;
+        }
+        int base = 0;
+        if (lr == 0 && total > 0 && grow < a.M) base = atomicAdd(&a.cand_count[grow], total);
+        base = __shfl(base, lane & 32, kWave);
+        if (grow < a.M) {
+          int pos = base + before;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (p[j]) {
+              if (pos < a.C) a.cand[(size_t)grow * a.C + pos] = cand_composite(kx[j], (uint32_t)(col0 + wn * 128 + j * 32 + lr));
+              ++pos;
+            }
+          }
+        }
+        (void)mine;
+      }
+    }
+  }
+  if (!SAMPLE && bad && a.status != nullptr) {
+    // rows of this lane's tile part: flag every tree the tile touches that holds a bad value
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int grow = row0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        bool rb_ = false;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          rb_ |= (col0 + wn * 128 + j * 32 + lr < a.V) && !__builtin_isfinite(acc[i][j][e]);
+        if (rb_ && grow < a.M) atomicOr(&a.status[grow / a.rows_per_tree], MFD_TREE_NONFINITE);
+      }
+    }
+  }
+}
+
+// Per row: the candidate threshold (k-th largest group maximum, or 0 = take
+// every column when the sample holds fewer than k groups); resets the row's
+// candidate count.
+__global__ void __launch_bounds__(kSelNT) lmh_threshold_kernel(LmhArgs a, int k) {
+  __shared__ uint32_t hist[256];
+  __shared__ int sh[2];
+  __shared__ int red[kSelNT / kWave];
+  const int row = (int)blockIdx.x;
+  const int n = a.S * kGroupsPerTile;
+  const uint32_t* g = a.samp + (size_t)row * n;
+  int cnt = 0;
+  for (int i = threadIdx.x; i < n; i += kSelNT) cnt += g[i] != 0u ? 1 : 0;
+  cnt = block_sum<kSelNT>(cnt, red);
+  uint32_t thr = 0;
+  if (cnt >= k) {
+    thr = (uint32_t)block_kth_largest<kSelNT, 32>(
+        n, k,
+        [&](int i, uint64_t* key) {
+          *key = g[i];
+          return g[i] != 0u;
+        },
+        hist, sh);
+  }
+  if (threadIdx.x == 0) {
+    a.thr[row] = thr;
+    a.cand_count[row] = 0;
+  }
+}
+
+// Per row: log-normaliser from the tile partials, then the exact top-k of the
+// candidate list (largest composites = largest logits, ties by lower id),
+// written in descending order.
+__global__ void __launch_bounds__(kSelNT) lmh_select_kernel(LmhArgs a, int k, double* __restrict__ lse,
+                                                            int32_t* __restrict__ topk_id,
+                                                            float* __restrict__ topk_raw,
+                                                            float* __restrict__ topk_logp) {
+  extern __shared__ __attribute__((aligned(16))) uint64_t lds[];  // kSelLdsCap candidates, then the sort area
+  __shared__ uint32_t hist[256];
+  __shared__ int sh[2];
+  __shared__ float redf[kSelNT / kWave];
+  __shared__ double redd[kSelNT / kWave];
+  __shared__ int nsel;
+  const int row = (int)blockIdx.x;
+  const int tid = (int)threadIdx.x, lane = lane_id(), w = wave_id();
+  const int np = 2 * a.T;
+  const float2* part = a.part + (size_t)row * np;
+
+  // 1. lse = M + log sum_t s_t exp(m_t - M), fp64, fixed reduction order
+  float mx = -INFINITY;
+  for (int i = tid; i < np; i += kSelNT) mx = fmaxf(mx, part[i].x);
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+  if (lane == 0) redf[w] = mx;
+  __syncthreads();
+  mx = redf[0];
+#pragma unroll
+  for (int i = 1; i < kSelNT / kWave; ++i) mx = fmaxf(mx, redf[i]);
+  double s = 0.0;
+  if (mx > -INFINITY) {
+    for (int i = tid; i < np; i += kSelNT) {
+      const float2 p = part[i];
+      if (p.x > -INFINITY) s += (double)p.y * exp((double)p.x - (double)mx);
+    }
+  }
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, kWave);
+  if (lane == 0) redd[w] = s;
+  __syncthreads();
+  double tot = 0.0;
+#pragma unroll
+  for (int i = 0; i < kSelNT / kWave; ++i) tot += redd[i];
+  const double l = mx > -INFINITY ? (double)mx + log(tot) : -INFINITY;
+  if (tid == 0) lse[row] = l;
+
+  // 2. candidates
+  const int cnt = a.cand_count[row];
+  int32_t* oid = topk_id + (size_t)row * k;
+  float* oraw = topk_raw + (size_t)row * k;
+  float* olp = topk_logp ? topk_logp + (size_t)row * k : nullptr;
+  if (cnt > a.C || cnt < k) {
+    // more candidates than the workspace holds (or, defensively, too few)
+    for (int j = tid; j < k; j += kSelNT) {
+      oid[j] = -1;
+      oraw[j] = -INFINITY;
+      if (olp) olp[j] = -INFINITY;
+    }
+    if (tid == 0 && a.status) atomicOr(&a.status[row / a.rows_per_tree], MFD_TREE_CAPACITY);
+    return;
+  }
+  const uint64_t* cg = a.cand + (size_t)row * a.C;
+  const bool in_lds = cnt <= kSelLdsCap;
+  uint64_t* sortb = lds + kSelLdsCap;
+  if (in_lds)
+    for (int i = tid; i < cnt; i += kSelNT) lds[i] = cg[i];
+  __syncthreads();
+  const uint64_t* src = in_lds ? lds : cg;
+  const uint64_t kth = block_kth_largest<kSelNT, 64>(
+      cnt, k,
+      [&](int i, uint64_t* key) {
+        *key = src[i];
+        return true;
+      },
+      hist, sh);
+
+  // 3. gather the k composites >= kth (composites are distinct), sort, write descending
+  const int P = next_pow2(k);
+  for (int i = tid; i < P; i += kSelNT) sortb[i] = 0ull;
+  if (tid == 0) nsel = 0;
+  __syncthreads();
+  for (int i = tid; i < cnt; i += kSelNT) {
+    const uint64_t c = src[i];
+    if (c >= kth) {
+      const int slot = atomicAdd(&nsel, 1);
+      if (slot < k) sortb[P - k + slot] = c;
+    }
+  }
+  __syncthreads();
+  block_sort_keys<kSelNT>(sortb, P);
+  for (int j = tid; j < k; j += kSelNT) {
+    const uint64_t c = sortb[P - 1 - j];
+    const uint32_t key = (uint32_t)(c >> 32);
+    const float raw = __uint_as_float(f32_from_key(key));
+    oid[j] = (int32_t)(0xFFFFFFFFu - (uint32_t)c);
+    oraw[j] = raw;
+    if (olp) olp[j] = (float)((double)raw - l);
+  }
+}
+
+}  // namespace
+
+LmhWorkspace lmhead_workspace(long long M, int V, int k) {
+  LmhWorkspace w{};
+  w.T = (V + kBN - 1) / kBN;
+  w.S = w.T < 32 ? w.T : 32;
+  // about k V / (S * 256) candidates per row for rows of independent logits;
+  // four times that leaves room for rows of uneven spread
+  const long long expect = ((long long)k * V + (long long)w.S * kBN - 1) / ((long long)w.S * kBN);
+  long long C = 4 * expect;
+  if (C < 2LL * k) C = 2LL * k;
+  if (C < 4096) C = 4096;
+  C = (C + 255) / 256 * 256;
+  const long long vcap = ((long long)V + 255) / 256 * 256;
+  if (C > vcap) C = vcap;
+  w.C = (int)C;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) / 256 * 256;
+    return o;
+  };
+  w.off_samp = take((size_t)M * w.S * kGroupsPerTile * sizeof(uint32_t));
+  w.off_thr = take((size_t)M * sizeof(uint32_t));
+  w.off_count = take((size_t)M * sizeof(int));
+  w.off_part = take((size_t)M * 2 * w.T * sizeof(float2));
+  w.off_cand = take((size_t)M * w.C * sizeof(uint64_t));
+  w.bytes = off;
+  return w;
+}
+
+hipError_t launch_lmhead_topk(const void* hidden, const void* weight, int M, int rows_per_tree, int D, int V, int k,
+                              double* lse, int32_t* topk_id, float* topk_raw, float* topk_logp, int32_t* status,
+                              void* ws, hipStream_t stream) {
+  const LmhWorkspace wsl = lmhead_workspace(M, V, k);
+  char* base = static_cast<char*>(ws);
+  LmhArgs a;
+  a.H = static_cast<const uint16_t*>(hidden);
+  a.W = static_cast<const uint16_t*>(weight);
+  a.M = M;
+  a.D = D;
+  a.V = V;
+  a.T = wsl.T;
+  a.S = wsl.S;
+  a.rows_per_tree = rows_per_tree;
+  a.samp = reinterpret_cast<uint32_t*>(base + wsl.off_samp);
+  a.thr = reinterpret_cast<uint32_t*>(base + wsl.off_thr);
+  a.cand_count = reinterpret_cast<int*>(base + wsl.off_count);
+  a.part = reinterpret_cast<float2*>(base + wsl.off_part);
+  a.cand = reinterpret_cast<uint64_t*>(base + wsl.off_cand);
+  a.C = wsl.C;
+  a.status = status;
+  const int nM = (M + kBM - 1) / kBM;
+  const long long ns = (long long)nM * a.S, nm = (long long)nM * a.T;
+  const long long gs = (ns + 7) / 8 * 8, gm = (nm + 7) / 8 * 8;
+  hipLaunchKernelGGL(lmh_tile_kernel<true>, dim3((unsigned)gs), dim3(kNT), 0, stream, a);
+  hipLaunchKernelGGL(lmh_threshold_kernel, dim3(M), dim3(kSelNT), 0, stream, a, k);
+  hipLaunchKernelGGL(lmh_tile_kernel<false>, dim3((unsigned)gm), dim3(kNT), 0, stream, a);
+  const size_t lds = (size_t)(kSelLdsCap + next_pow2(k)) * sizeof(uint64_t);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lmh_select_kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(lmh_select_kernel, dim3(M), dim3(kSelNT), lds, stream, a, k, lse, topk_id, topk_raw, topk_logp);
+  return hipGetLastError();
+}
+
+}  // namespace mfd

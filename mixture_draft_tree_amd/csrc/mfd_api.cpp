@@ -30,6 +30,7 @@ mfd_status from_hip(hipError_t e, const char* what) {
   return fail(MFD_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
 }
 
+constexpr int kMaxLmhD = 16384;
 constexpr int kMaxK = 32, kMaxL = 32, kMaxV = (1 << 20) - 1, kMaxB = 16383, kMaxTopk = 2048, kMaxKk = 16384;
 
 mfd_status check_dims(int N, int K, int L, int V) {
@@ -80,6 +81,16 @@ mfd_status mfd_workspace_size(mfd_op op, int N, int K, int L, int V, int B, size
       if (B < 0 || B > kMaxB) return fail(MFD_ERR_INVALID_ARG, "B must be in [0, %d] (got %d)", kMaxB, B);
       *bytes = N == 0 ? 0 : mfd::covered_mass_ws_bytes(N, B + 1);
       return ok();
+    case MFD_OP_LMHEAD_TOPK: {
+      mfd_status s = check_dims(N, K, L, V);
+      if (s != MFD_OK) return s;
+      if (B < 0 || B > kMaxB) return fail(MFD_ERR_INVALID_ARG, "B must be in [0, %d] (got %d)", kMaxB, B);
+      const int k = B < V ? (B < 1 ? 1 : B) : V;
+      if (k > kMaxTopk) return fail(MFD_ERR_INVALID_ARG, "k = min(B, V) must be <= %d (got %d)", kMaxTopk, k);
+      const long long M = (long long)N * K * L;
+      *bytes = M == 0 ? 0 : mfd::lmhead_workspace(M, V, k).bytes;
+      return ok();
+    }
     case MFD_OP_MIXTURE_THRESHOLD:
     case MFD_OP_TREE_BUILD: {
       mfd_status s = check_dims(N, K, L, V);
@@ -142,6 +153,33 @@ mfd_status mfd_logsoftmax_topk_modes(const void* logits, mfd_dtype dtype, int N,
   if (N > 0) REQUIRE_PTR(modes);
   return logsoftmax_topk_impl("mfd_logsoftmax_topk_modes launch", logits, dtype, N, K, L, V, nullptr, modes, k, lse,
                               topk_id, topk_raw, topk_logp, status, stream);
+}
+
+mfd_status mfd_lmhead_logsoftmax_topk(const void* hidden, const void* weight, int N, int K, int L, int D, int V, int k,
+                                      double* lse, int32_t* topk_id, float* topk_raw, float* topk_logp,
+                                      int32_t* status, void* ws, size_t ws_bytes, hipStream_t stream) {
+  mfd_status s = check_dims(N, K, L, V);
+  if (s != MFD_OK) return s;
+  if (D < 32 || D > kMaxLmhD || D % 32 != 0)
+    return fail(MFD_ERR_INVALID_ARG, "D must be a multiple of 32 in [32, %d] (got %d)", kMaxLmhD, D);
+  if (k < 1 || k > kMaxTopk || k > V) return fail(MFD_ERR_INVALID_ARG, "k must be in [1, min(V, %d)] (got %d)", kMaxTopk, k);
+  const long long M = (long long)N * K * L;
+  if (M > 0x7FFFFFFFLL) return fail(MFD_ERR_INVALID_ARG, "too many rows (%lld)", M);
+  if (N == 0) return ok();
+  REQUIRE_PTR(hidden);
+  REQUIRE_PTR(weight);
+  REQUIRE_PTR(lse);
+  REQUIRE_PTR(topk_id);
+  REQUIRE_PTR(topk_raw);
+  if (reinterpret_cast<uintptr_t>(hidden) % 16 || reinterpret_cast<uintptr_t>(weight) % 16)
+    return fail(MFD_ERR_INVALID_ARG, "hidden and weight must be 16-byte aligned");
+  const size_t need = mfd::lmhead_workspace(M, V, k).bytes;
+  if (ws == nullptr || ws_bytes < need)
+    return fail(MFD_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws == nullptr ? (size_t)0 : ws_bytes);
+  if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(MFD_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  return from_hip(mfd::launch_lmhead_topk(hidden, weight, (int)M, K * L, D, V, k, lse, topk_id, topk_raw, topk_logp,
+                                          status, ws, stream),
+                  "mfd_lmhead_logsoftmax_topk launch");
 }
 
 static mfd_status mixture_threshold_impl(const char* call, const int32_t* topk_id, const float* topk_raw,

@@ -62,4 +62,18 @@ hipError_t launch_verify_walk(const void* target, bool bf16, int N, int Bp1, lon
                               int32_t* out_tokens, int32_t* path_nodes, int32_t* status, void* ws,
                               hipStream_t stream);
 
+
+// Fused LM head + log-softmax/top-k: workspace layout (byte offsets into the
+// caller's buffer) and launcher.
+struct LmhWorkspace {
+  int T;  // vocabulary tiles of 256 columns
+  int S;  // tiles in the threshold sample
+  int C;  // candidate capacity per row
+  size_t off_samp, off_thr, off_count, off_part, off_cand, bytes;
+};
+LmhWorkspace lmhead_workspace(long long M, int V, int k);
+hipError_t launch_lmhead_topk(const void* hidden, const void* weight, int M, int rows_per_tree, int D, int V, int k,
+                              double* lse, int32_t* topk_id, float* topk_raw, float* topk_logp, int32_t* status,
+                              void* ws, hipStream_t stream);
+
 }  // namespace mfd

@@ -25,13 +25,14 @@ _lib = ctypes.CDLL(LIB_PATH)
 MFD_OK, MFD_ERR_INVALID_ARG, MFD_ERR_DTYPE, MFD_ERR_WORKSPACE, MFD_ERR_DEVICE = 0, 1, 2, 3, 4
 MFD_BF16, MFD_F32 = 0, 1
 (MFD_OP_LOGSOFTMAX_TOPK, MFD_OP_MIXTURE_THRESHOLD, MFD_OP_TREE_BUILD,
- MFD_OP_TREE_MASK, MFD_OP_VERIFY_WALK, MFD_OP_COVERED_MASS) = range(6)
+ MFD_OP_TREE_MASK, MFD_OP_VERIFY_WALK, MFD_OP_COVERED_MASS, MFD_OP_LMHEAD_TOPK) = range(7)
 MFD_TREE_NONFINITE, MFD_TREE_CAPACITY, MFD_TREE_BAD_TEMPERATURE, MFD_TREE_BAD_MODES = 1, 2, 4, 8
 
 EXPORTED = ["mfd_last_error", "mfd_version", "mfd_workspace_size", "mfd_logsoftmax_topk",
             "mfd_logsoftmax_topk_mapped", "mfd_mixture_threshold", "mfd_tree_build", "mfd_tree_mask",
             "mfd_verify_walk", "mfd_covered_mass", "mfd_chimera_count", "mfd_logsoftmax_topk_modes",
-            "mfd_mixture_threshold_modes", "mfd_tree_build_modes", "mfd_stream_read"]
+            "mfd_mixture_threshold_modes", "mfd_tree_build_modes", "mfd_stream_read",
+            "mfd_lmhead_logsoftmax_topk"]
 
 _p = ctypes.c_void_p
 _i = ctypes.c_int
@@ -59,6 +60,8 @@ _lib.mfd_mixture_threshold_modes.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p,
 _lib.mfd_tree_build_modes.restype = _i
 _lib.mfd_tree_build_modes.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p,
                                       _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]
+_lib.mfd_lmhead_logsoftmax_topk.restype = _i
+_lib.mfd_lmhead_logsoftmax_topk.argtypes = [_p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p]
 _lib.mfd_stream_read.restype = _i
 _lib.mfd_stream_read.argtypes = [_p, _sz, _p, _p]
 _lib.mfd_tree_mask.restype = _i
@@ -184,6 +187,41 @@ def mfd_logsoftmax_topk_modes(logits, modes, k, lse, topk_id, topk_raw, topk_log
     _check(_lib.mfd_logsoftmax_topk_modes(_ptr(logits), _dtype_code(logits), N, K, L, V, _ptr(modes), k, _ptr(lse),
                                           _ptr(topk_id), _ptr(topk_raw), _ptr(topk_logp), _ptr(status),
                                           _stream_handle(stream)), "mfd_logsoftmax_topk_modes")
+
+
+def lmhead_workspace(N: int, K: int, L: int, V: int, k: int, device="cuda") -> torch.Tensor:
+    """A device workspace (256-byte aligned) for mfd_lmhead_logsoftmax_topk."""
+    n = workspace_size(MFD_OP_LMHEAD_TOPK, N, K, L, V, k)
+    return torch.empty((max(n, 256) + 255) // 8, dtype=torch.int64, device=device)
+
+
+def mfd_lmhead_logsoftmax_topk(hidden, weight, k, lse, topk_id, topk_raw, topk_logp=None, status=None, ws=None,
+                               stream=None):
+    """hidden [N, K, L, D] bf16, weight [V, D] bf16 -> lse [N, K, L] fp64, topk_* [N, K, L, k]
+    over the logits hidden . weight^T (never stored)."""
+    if hidden.dim() != 4 or not hidden.is_contiguous() or hidden.device.type != "cuda":
+        raise ValueError("hidden must be a contiguous [N, K, L, D] GPU tensor")
+    if hidden.dtype != torch.bfloat16:
+        raise ValueError(f"hidden must be bf16, got {hidden.dtype}")
+    N, K, L, D = hidden.shape
+    if weight.dim() != 2 or weight.shape[1] != D:
+        raise ValueError(f"weight must be [V, {D}], got {tuple(weight.shape)}")
+    V = weight.shape[0]
+    _want(weight, "weight", torch.bfloat16, (V, D))
+    _want(lse, "lse", torch.float64, (N, K, L))
+    _want(topk_id, "topk_id", torch.int32, (N, K, L, k))
+    _want(topk_raw, "topk_raw", torch.float32, (N, K, L, k))
+    _want(topk_logp, "topk_logp", torch.float32, (N, K, L, k), optional=True)
+    _want(status, "status", torch.int32, (N,), optional=True)
+    if ws is None:
+        ws = lmhead_workspace(N, K, L, V, k, hidden.device)
+    ptr = ws.data_ptr()
+    off = (-ptr) % 256
+    nbytes = ws.numel() * ws.element_size() - off
+    _check(_lib.mfd_lmhead_logsoftmax_topk(_ptr(hidden), _ptr(weight), N, K, L, D, V, k, _ptr(lse), _ptr(topk_id),
+                                           _ptr(topk_raw), _ptr(topk_logp), _ptr(status),
+                                           ctypes.c_void_p(ptr + off), max(nbytes, 0), _stream_handle(stream)),
+           "mfd_lmhead_logsoftmax_topk")
 
 
 def mfd_mixture_threshold(topk_id, topk_raw, lse, B, cutoff, n_select, per_mode_kept=None, status=None,

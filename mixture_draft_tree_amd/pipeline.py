@@ -104,6 +104,23 @@ class MixtureTreePath:
             M.mfd_logsoftmax_topk(logits, self.k, b.lse, b.topk_id, b.topk_raw, b.topk_logp, b.status,
                                   stream=stream)
 
+    def lmhead_logsoftmax_topk(self, hidden, weight, stream=None):
+        """Call 1 fused with the LM head: hidden [N, K, L, D] bf16, weight [V, D] bf16."""
+        b = self.buf
+        if self.vocab_map is not None or self.modes is not None:
+            raise ValueError("the fused LM-head call covers full-vocabulary trees of K modes")
+        if getattr(self, "_lmh_ws", None) is None:
+            self._lmh_ws = M.lmhead_workspace(self.N, self.K, self.L, self.V, self.k, hidden.device)
+        M.mfd_lmhead_logsoftmax_topk(hidden, weight, self.k, b.lse, b.topk_id, b.topk_raw, b.topk_logp, b.status,
+                                     ws=self._lmh_ws, stream=stream)
+
+    def build_from_hidden(self, hidden, weight, anchor, pos_base, stream=None):
+        """Calls 1-4 with the fused LM head: hidden states -> tree, mask, position ids."""
+        self.lmhead_logsoftmax_topk(hidden, weight, stream)
+        self.mixture_threshold(stream)
+        self.tree_build(anchor, stream)
+        self.tree_mask(pos_base, stream)
+
     def mixture_threshold(self, stream=None):
         b = self.buf
         M.mfd_mixture_threshold_modes(b.topk_id, b.topk_raw, b.lse, self.B, self.modes, b.cutoff, b.n_select,

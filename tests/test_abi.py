@@ -198,3 +198,37 @@ def test_stream_read_rejects():
     assert f(ctypes.c_void_p(0x100008), 32, FAKE, None) == M.MFD_ERR_INVALID_ARG
     assert f(FAKE, 32, None, None) == M.MFD_ERR_INVALID_ARG
     assert f(None, 0, None, None) == M.MFD_OK
+
+
+def _lmh(**kw):
+    a = dict(h=FAKE, w=FAKE, N=1, K=8, L=15, D=2560, V=151936, k=256, lse=FAKE, tid=FAKE, raw=FAKE,
+             ws=ctypes.c_void_p(0x100000), ws_bytes=1 << 40)
+    a.update(kw)
+    return M._lib.mfd_lmhead_logsoftmax_topk(a["h"], a["w"], a["N"], a["K"], a["L"], a["D"], a["V"], a["k"],
+                                             a["lse"], a["tid"], a["raw"], None, None, a["ws"], a["ws_bytes"], None)
+
+
+def test_lmhead_call_rejects_before_launch():
+    assert _lmh(D=100) == M.MFD_ERR_INVALID_ARG and "multiple of 32" in M.last_error()
+    assert _lmh(D=0) == M.MFD_ERR_INVALID_ARG
+    assert _lmh(D=16416) == M.MFD_ERR_INVALID_ARG
+    assert _lmh(k=0) == M.MFD_ERR_INVALID_ARG
+    assert _lmh(V=100, k=101) == M.MFD_ERR_INVALID_ARG
+    assert _lmh(k=2049) == M.MFD_ERR_INVALID_ARG
+    assert _lmh(K=33) == M.MFD_ERR_INVALID_ARG
+    assert _lmh(h=None) == M.MFD_ERR_INVALID_ARG
+    assert _lmh(h=ctypes.c_void_p(0x100008)) == M.MFD_ERR_INVALID_ARG and "aligned" in M.last_error()
+    assert _lmh(ws=None) == M.MFD_ERR_WORKSPACE
+    assert _lmh(ws_bytes=1000) == M.MFD_ERR_WORKSPACE and "workspace needs" in M.last_error()
+    assert _lmh(ws=ctypes.c_void_p(0x100010)) == M.MFD_ERR_WORKSPACE
+    assert _lmh(N=0, h=None, w=None) == M.MFD_OK
+
+
+def test_lmhead_workspace_size():
+    one = M.workspace_size(M.MFD_OP_LMHEAD_TOPK, 1, 8, 15, 151936, 256)
+    many = M.workspace_size(M.MFD_OP_LMHEAD_TOPK, 64, 8, 15, 151936, 256)
+    assert 0 < one < many and many <= 64 * one + 4096
+    assert M.workspace_size(M.MFD_OP_LMHEAD_TOPK, 0, 8, 15, 151936, 256) == 0
+    assert M.workspace_size(M.MFD_OP_LMHEAD_TOPK, 1, 8, 15, 151936, 1024) > one
+    with pytest.raises(M.MfdError):
+        M.workspace_size(M.MFD_OP_LMHEAD_TOPK, 1, 8, 15, 151936, 4096)

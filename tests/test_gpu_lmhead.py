@@ -1,0 +1,164 @@
+"""GPU parity of the fused LM head + log-softmax/top-k call against the fp64 oracle.
+
+Grid workloads have every fp32 partial sum exact, so the fused logits equal the
+oracle's and ids, values and trees must match bit for bit.  Gaussian workloads
+are compared through the rigorous fp32 summation bound of oracle.lmhead_abs_bound:
+an id may differ from the oracle's only where the two logits lie within twice
+the bound of each other."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mixture_draft_tree_amd import synth
+from tests.gpu_helpers import LSE_TOL, compare_tree, oracle_rows, tree_rows
+
+pytestmark = pytest.mark.gpu
+
+M = pytest.importorskip("mixture_draft_tree_amd.mfdtree", reason="libmfdtree.so not built")
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _run(hidden, weight, k):
+    N, K, L, D = hidden.shape
+    d = "cuda"
+    H, W = hidden.to(d).contiguous(), weight.to(d).contiguous()
+    lse = torch.empty((N, K, L), dtype=torch.float64, device=d)
+    ids = torch.empty((N, K, L, k), dtype=torch.int32, device=d)
+    raw = torch.empty((N, K, L, k), dtype=torch.float32, device=d)
+    lp = torch.empty((N, K, L, k), dtype=torch.float32, device=d)
+    st = torch.zeros((N,), dtype=torch.int32, device=d)
+    M.mfd_lmhead_logsoftmax_topk(H, W, k, lse, ids, raw, lp, st)
+    torch.cuda.synchronize()
+    return lse.cpu().numpy(), ids.cpu().numpy(), raw.cpu().numpy(), lp.cpu().numpy(), st.cpu().numpy()
+
+
+def _check_exact(x64, k, lse, ids, raw, lp):
+    o_lse, o_ids = oracle_rows(x64, k)
+    assert np.max(np.abs(lse - o_lse)) < LSE_TOL
+    assert np.array_equal(ids, o_ids), "top-k ids differ"
+    want = np.take_along_axis(x64, o_ids.astype(np.int64), axis=-1)
+    assert np.array_equal(raw.astype(np.float64), want), "top-k logits differ"
+    assert np.max(np.abs(lp.astype(np.float64) - (want - o_lse[..., None]))) < LSE_TOL
+
+
+def _check_bounded(x64, eps, k, lse, ids, raw):
+    """Rows of x64 [R, V] (exact logits), eps [R, V] (summation bound)."""
+    for r in range(x64.shape[0]):
+        x, e = x64[r], eps[r]
+        g = ids[r].astype(np.int64)
+        em = float(e.max())
+        assert len(set(g.tolist())) == k and g.min() >= 0 and g.max() < x.shape[0]
+        assert np.all(np.abs(raw[r].astype(np.float64) - x[g]) <= e[g]), "logit outside the fp32 bound"
+        order = O.rank_order(x, k)
+        xk = x[order[-1]]
+        must = np.nonzero(x > xk + 2 * em)[0]
+        assert np.all(np.isin(must, g)), "a clear top-k token is missing"
+        assert np.all(x[g] >= xk - 2 * em), "a clearly outside token was listed"
+        assert np.all(x[g[:-1]] >= x[g[1:]] - 2 * em), "listed out of order beyond the bound"
+        same = np.abs(x[g] - x[order]) <= 2 * em
+        assert np.all(same | (g == order))
+        assert abs(lse[r] - O.lse_rows(x)) < LSE_TOL + em
+
+
+@pytest.mark.parametrize("name", ["lmhead_small", "lmhead_mid"])
+def test_lmhead_grid_bit_exact(name):
+    _say(f"lmhead grid parity {name}")
+    b = synth.lmhead_batch(name)
+    w = b.workload
+    k = min(w.B, w.V)
+    lse, ids, raw, lp, st = _run(b.hidden, b.weight, k)
+    assert np.all(st == 0)
+    x64 = O.lmhead_logits(b.hidden.float().numpy(), b.weight.float().numpy())
+    _check_exact(x64, k, lse, ids, raw, lp)
+
+
+def test_lmhead_gaussian_within_bound():
+    _say("lmhead gaussian parity lmhead_ragged")
+    b = synth.lmhead_batch("lmhead_ragged")
+    w = b.workload
+    k = min(w.B, w.V)
+    lse, ids, raw, lp, st = _run(b.hidden, b.weight, k)
+    assert np.all(st == 0)
+    h, W = b.hidden.float().numpy(), b.weight.float().numpy()
+    x64 = O.lmhead_logits(h, W).reshape(-1, w.V)
+    eps = O.lmhead_abs_bound(h, W).reshape(-1, w.V)
+    _check_bounded(x64, eps, k, lse.reshape(-1), ids.reshape(-1, k), raw.reshape(-1, k))
+
+
+@pytest.mark.parametrize("k", [1, 7, 100])
+def test_lmhead_grid_other_k(k):
+    _say(f"lmhead grid parity lmhead_small k={k}")
+    b = synth.lmhead_batch("lmhead_small")
+    lse, ids, raw, lp, st = _run(b.hidden, b.weight, k)
+    assert np.all(st == 0)
+    x64 = O.lmhead_logits(b.hidden.float().numpy(), b.weight.float().numpy())
+    _check_exact(x64, k, lse, ids, raw, lp)
+
+
+@pytest.mark.parametrize("name", ["lmhead_small", "lmhead_mid"])
+def test_lmhead_tree_equals_oracle_tree(name):
+    # The tree built from the fused outputs equals the oracle's tree over the
+    # exact logits (grid inputs).
+    from mixture_draft_tree_amd.pipeline import MixtureTreePath
+    _say(f"lmhead tree parity {name}")
+    b = synth.lmhead_batch(name)
+    w = b.workload
+    P = MixtureTreePath(w.N, w.K, w.L, w.V, w.B)
+    anchor = b.anchor.cuda()
+    pos = torch.arange(w.N, dtype=torch.int64, device="cuda") * 100
+    P.build_from_hidden(b.hidden.cuda(), b.weight.cuda(), anchor, pos)
+    torch.cuda.synchronize()
+    assert int(P.buf.status.abs().sum().item()) == 0
+    x64 = O.lmhead_logits(b.hidden.float().numpy(), b.weight.float().numpy())
+    n_exact = 0
+    for n in range(w.N):
+        res = compare_tree(x64[n], w.B, int(b.anchor[n]), tree_rows(P, n))
+        n_exact += int(res["exact"])
+    assert n_exact >= 1
+
+
+def test_lmhead_full_size_sampled_rows():
+    # The drafter's shape (K=8, L=15, V=151936, D=2560, k=256), one tree: grid
+    # inputs bit-exact on sampled rows, Gaussian inputs within the bound.
+    for name in ("lmhead_single_grid", "lmhead_single"):
+        _say(f"lmhead full-size sampled rows {name}")
+        b = synth.lmhead_batch(name)
+        w = b.workload
+        k = min(w.B, w.V)
+        lse, ids, raw, lp, st = _run(b.hidden, b.weight, k)
+        assert np.all(st == 0)
+        h = b.hidden.float().numpy().reshape(-1, w.D)
+        W = b.weight.float().numpy()
+        rows = [0, 1, 14, 15, 59, 60, 100, 119]
+        x64 = O.lmhead_logits(h[rows], W)
+        if w.grid:
+            _check_exact(x64, k, lse.reshape(-1)[rows], ids.reshape(-1, k)[rows], raw.reshape(-1, k)[rows],
+                         lp.reshape(-1, k)[rows])
+        else:
+            eps = O.lmhead_abs_bound(h[rows], W)
+            _check_bounded(x64, eps, k, lse.reshape(-1)[rows], ids.reshape(-1, k)[rows], raw.reshape(-1, k)[rows])
+
+
+def test_lmhead_capacity_and_nonfinite_flags():
+    _say("lmhead flags lmhead_mid")
+    b = synth.lmhead_batch("lmhead_mid")
+    w = b.workload
+    k = min(w.B, w.V)
+    # tree 0: every logit 0 (all tie) -> more candidates than the workspace holds
+    # tree 1: a NaN hidden value -> non-finite logits
+    H = b.hidden.clone()
+    H[0] = 0
+    H[1, 3, 2, 5] = float("nan")
+    lse, ids, raw, lp, st = _run(H, b.weight, k)
+    assert st[0] == M.MFD_TREE_CAPACITY
+    assert st[1] & M.MFD_TREE_NONFINITE
+    assert np.all(ids[0] == -1) and np.all(np.isneginf(raw[0]))
+    assert np.max(np.abs(lse[0] - np.log(w.V))) < LSE_TOL
