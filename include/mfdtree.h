@@ -252,7 +252,8 @@ mfd_status mfd_tree_build_modes(const int32_t* topk_id, const float* topk_raw, c
  *   hidden    device [N, K, L, D] bf16: the drafter's final hidden states, row
  *             r = (n, k, i); 16-byte aligned.
  *   weight    device [V, D] bf16: the LM head, one row per token; 16-byte aligned.
- *   D         hidden width, a multiple of 32 in [32, 16384].
+ *   D         hidden width, a multiple of 64 in [64, 16384]; N*K*L*D and V*D
+ *             must be below 2^31.
  *   lse, topk_id, topk_raw, topk_logp: as for mfd_logsoftmax_topk; topk_raw
  *             is the fp32 logit as accumulated (ties break by token id).
  *   status    device [N] int32 or NULL: MFD_TREE_NONFINITE for a tree with a

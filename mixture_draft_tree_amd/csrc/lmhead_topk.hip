@@ -20,8 +20,9 @@
 //   4. lmh_select_kernel       per row: lse from the partials (fp64), the exact
 //      k-th largest (logit desc, id asc) among the candidates, those k sorted.
 //
-// Tiles: 128 rows x 256 vocabulary columns per 256-thread workgroup, k in
-// steps of 32 through double-buffered LDS, four waves of 64 x 128 each built
+// Tiles: 128 rows x 256 vocabulary columns per 256-thread workgroup, two
+// workgroups per CU, k in steps of 32 through double-buffered LDS (global loads
+// two steps ahead), four waves of 64 x 128 each built
 // from v_mfma_f32_32x32x16_bf16 (fp32 accumulation).  Each product element is
 // computed from the same operands in the same k order in both tile launches,
 // so the sample and main launches see identical logits.
@@ -83,7 +84,7 @@ __device__ __forceinline__ bool tile_of(int b, int nM, int nVt, int* m_out, int*
 }
 
 template <bool SAMPLE>
-__global__ void __launch_bounds__(kNT) lmh_tile_kernel(LmhArgs a) {
+__global__ void __launch_bounds__(kNT, 2) lmh_tile_kernel(LmhArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][kBM][kLdk];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][kBN][kLdk];
   __shared__ uint32_t sthr[kBM];
@@ -112,24 +113,28 @@ __global__ void __launch_bounds__(kNT) lmh_tile_kernel(LmhArgs a) {
   const uint16_t* b1p = a.W + (size_t)min(col0 + r0 + 64, a.V - 1) * D + q8;
   const uint16_t* b2p = a.W + (size_t)min(col0 + r0 + 128, a.V - 1) * D + q8;
   const uint16_t* b3p = a.W + (size_t)min(col0 + r0 + 192, a.V - 1) * D + q8;
-  uint4 ra0, ra1, rb0, rb1, rb2, rb3;
-#define LMH_GLOAD(k0)                                        \
-  do {                                                       \
-    ra0 = *reinterpret_cast<const uint4*>(a0p + (k0));       \
-    ra1 = *reinterpret_cast<const uint4*>(a1p + (k0));       \
-    rb0 = *reinterpret_cast<const uint4*>(b0p + (k0));       \
-    rb1 = *reinterpret_cast<const uint4*>(b1p + (k0));       \
-    rb2 = *reinterpret_cast<const uint4*>(b2p + (k0));       \
-    rb3 = *reinterpret_cast<const uint4*>(b3p + (k0));       \
+  // Register staging, two stages deep: stage j's chunks sit in register set
+  // j % 2 from their global load (issued at step j - 2) until they are copied
+  // to LDS at the end of step j - 1.
+  uint4 p0a0, p0a1, p0b0, p0b1, p0b2, p0b3;
+  uint4 p1a0, p1a1, p1b0, p1b1, p1b2, p1b3;
+#define LMH_GLOAD(P, k0)                                       \
+  do {                                                         \
+    P##a0 = *reinterpret_cast<const uint4*>(a0p + (k0));       \
+    P##a1 = *reinterpret_cast<const uint4*>(a1p + (k0));       \
+    P##b0 = *reinterpret_cast<const uint4*>(b0p + (k0));       \
+    P##b1 = *reinterpret_cast<const uint4*>(b1p + (k0));       \
+    P##b2 = *reinterpret_cast<const uint4*>(b2p + (k0));       \
+    P##b3 = *reinterpret_cast<const uint4*>(b3p + (k0));       \
   } while (0)
-#define LMH_LSTORE(buf)                                               \
-  do {                                                                \
-    *reinterpret_cast<uint4*>(&sA[buf][r0][q8]) = ra0;                \
-    *reinterpret_cast<uint4*>(&sA[buf][r0 + 64][q8]) = ra1;           \
-    *reinterpret_cast<uint4*>(&sB[buf][r0][q8]) = rb0;                \
-    *reinterpret_cast<uint4*>(&sB[buf][r0 + 64][q8]) = rb1;           \
-    *reinterpret_cast<uint4*>(&sB[buf][r0 + 128][q8]) = rb2;          \
-    *reinterpret_cast<uint4*>(&sB[buf][r0 + 192][q8]) = rb3;          \
+#define LMH_LSTORE(P, buf)                                          \
+  do {                                                              \
+    *reinterpret_cast<uint4*>(&sA[buf][r0][q8]) = P##a0;            \
+    *reinterpret_cast<uint4*>(&sA[buf][r0 + 64][q8]) = P##a1;       \
+    *reinterpret_cast<uint4*>(&sB[buf][r0][q8]) = P##b0;            \
+    *reinterpret_cast<uint4*>(&sB[buf][r0 + 64][q8]) = P##b1;       \
+    *reinterpret_cast<uint4*>(&sB[buf][r0 + 128][q8]) = P##b2;      \
+    *reinterpret_cast<uint4*>(&sB[buf][r0 + 192][q8]) = P##b3;      \
   } while (0)
 
   f32x16 acc[2][4];
@@ -143,30 +148,53 @@ __global__ void __launch_bounds__(kNT) lmh_tile_kernel(LmhArgs a) {
   // lane l feeds row (or column) l % 32 of a 32 x 16 operand, k-half l / 32
   const int lr = lane & 31, lk = (lane >> 5) * 8;
   const int nS = D / kBK;
-  LMH_GLOAD(0);
-  LMH_LSTORE(0);
-  __syncthreads();
-  for (int s = 0; s < nS; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nS) LMH_GLOAD((s + 1) * kBK);
-#pragma unroll
-    for (int kk = 0; kk < kBK; kk += 16) {
-      bf16x8 af[2], bfv[4];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][wm * 64 + i * 32 + lr][kk + lk]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfv[j] = *reinterpret_cast<const bf16x8*>(&sB[buf][wn * 128 + j * 32 + lr][kk + lk]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
-    }
-    if (s + 1 < nS) LMH_LSTORE(buf ^ 1);
-    __syncthreads();
+#define LMH_COMPUTE(buf)                                                                          \
+  do {                                                                                            \
+    _Pragma("unroll") for (int kk = 0; kk < kBK; kk += 16) {                                      \
+      bf16x8 af[2], bfv[4];                                                                       \
+      _Pragma("unroll") for (int i = 0; i < 2; ++i)                                               \
+        af[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][wm * 64 + i * 32 + lr][kk + lk]);       \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                               \
+        bfv[j] = *reinterpret_cast<const bf16x8*>(&sB[buf][wn * 128 + j * 32 + lr][kk + lk]);     \
+      _Pragma("unroll") for (int i = 0; i < 2; ++i)                                               \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j)                                             \
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0); \
+    }                                                                                             \
+  } while (0)
+  // Steady state: the prefetch load is unconditional (past the last stage it
+  // re-reads that stage, unused), so the compiler can count the loads in
+  // flight and wait only for the stage it stores, never for the prefetch.
+#define LMH_STEP(CUR, NXT)                                  \
+  {                                                         \
+    const int buf = s & 1;                                  \
+    LMH_GLOAD(CUR, min(s + 2, nS - 1) * kBK);               \
+    LMH_COMPUTE(buf);                                       \
+    if (s + 1 < nS) LMH_LSTORE(NXT, buf ^ 1);               \
+    __syncthreads();                                        \
+    ++s;                                                    \
   }
+#define LMH_TAIL_STEP(NXT)                                  \
+  if (s < nS) {                                             \
+    const int buf = s & 1;                                  \
+    LMH_COMPUTE(buf);                                       \
+    if (s + 1 < nS) LMH_LSTORE(NXT, buf ^ 1);               \
+    __syncthreads();                                        \
+    ++s;                                                    \
+  }
+
+  LMH_GLOAD(p0, 0);
+  LMH_GLOAD(p1, min(1, nS - 1) * kBK);
+  LMH_LSTORE(p0, 0);
+  __syncthreads();
+  int s = 0;
+  while (s + 2 <= nS) {
+    LMH_STEP(p0, p1)
+    LMH_STEP(p1, p0)
+  }
+  LMH_TAIL_STEP(p1)
+#undef LMH_TAIL_STEP
+#undef LMH_STEP
+#undef LMH_COMPUTE
 #undef LMH_GLOAD
 #undef LMH_LSTORE
 

@@ -160,11 +160,13 @@ mfd_status mfd_lmhead_logsoftmax_topk(const void* hidden, const void* weight, in
                                       int32_t* status, void* ws, size_t ws_bytes, hipStream_t stream) {
   mfd_status s = check_dims(N, K, L, V);
   if (s != MFD_OK) return s;
-  if (D < 32 || D > kMaxLmhD || D % 32 != 0)
-    return fail(MFD_ERR_INVALID_ARG, "D must be a multiple of 32 in [32, %d] (got %d)", kMaxLmhD, D);
+  if (D < 64 || D > kMaxLmhD || D % 64 != 0)
+    return fail(MFD_ERR_INVALID_ARG, "D must be a multiple of 64 in [64, %d] (got %d)", kMaxLmhD, D);
   if (k < 1 || k > kMaxTopk || k > V) return fail(MFD_ERR_INVALID_ARG, "k must be in [1, min(V, %d)] (got %d)", kMaxTopk, k);
   const long long M = (long long)N * K * L;
-  if (M > 0x7FFFFFFFLL) return fail(MFD_ERR_INVALID_ARG, "too many rows (%lld)", M);
+  if (M * D > 0x7FFFFFFFLL) return fail(MFD_ERR_INVALID_ARG, "N*K*L*D must be < 2^31 (got %lld)", M * D);
+  if ((long long)V * D > 0x7FFFFFFFLL)
+    return fail(MFD_ERR_INVALID_ARG, "V*D must be < 2^31 (got %lld)", (long long)V * D);
   if (N == 0) return ok();
   REQUIRE_PTR(hidden);
   REQUIRE_PTR(weight);

@@ -354,7 +354,7 @@ class LmHeadWorkload:
 LMHEAD_WORKLOADS = {
     # small shapes: ragged row and vocabulary tiles, whole-row sample
     "lmhead_small": LmHeadWorkload("lmhead_small", 20, 2, 5, 1000, 128, 32, 3, True),
-    "lmhead_ragged": LmHeadWorkload("lmhead_ragged", 21, 3, 7, 4133, 96, 64, 5, False),
+    "lmhead_ragged": LmHeadWorkload("lmhead_ragged", 21, 3, 7, 4133, 192, 64, 5, False),
     # two row tiles (the second ragged) and a sampled threshold
     "lmhead_mid": LmHeadWorkload("lmhead_mid", 22, 8, 15, 40000, 256, 256, 2, True),
     # the MFD drafter's shape: K=8 modes x 15 positions over V=151936 at D=2560

@@ -209,7 +209,10 @@ def _lmh(**kw):
 
 
 def test_lmhead_call_rejects_before_launch():
-    assert _lmh(D=100) == M.MFD_ERR_INVALID_ARG and "multiple of 32" in M.last_error()
+    assert _lmh(D=100) == M.MFD_ERR_INVALID_ARG and "multiple of 64" in M.last_error()
+    assert _lmh(D=96) == M.MFD_ERR_INVALID_ARG
+    assert _lmh(D=16384) == M.MFD_ERR_INVALID_ARG and "V*D" in M.last_error()
+    assert _lmh(N=20000, D=16384, V=1000) == M.MFD_ERR_INVALID_ARG and "N*K*L*D" in M.last_error()
     assert _lmh(D=0) == M.MFD_ERR_INVALID_ARG
     assert _lmh(D=16416) == M.MFD_ERR_INVALID_ARG
     assert _lmh(k=0) == M.MFD_ERR_INVALID_ARG
