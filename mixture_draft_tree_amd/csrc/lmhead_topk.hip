@@ -334,6 +334,7 @@ __global__ void __launch_bounds__(kSelNT) lmh_select_kernel(LmhArgs a, int k, do
   extern __shared__ __attribute__((aligned(16))) uint64_t lds[];  // kSelLdsCap candidates, then the sort area
   __shared__ uint32_t hist[256];
   __shared__ int sh[2];
+  __shared__ int red[kSelNT / kWave];
   __shared__ float redf[kSelNT / kWave];
   __shared__ double redd[kSelNT / kWave];
   __shared__ int nsel;
@@ -391,15 +392,69 @@ __global__ void __launch_bounds__(kSelNT) lmh_select_kernel(LmhArgs a, int k, do
     for (int i = tid; i < cnt; i += kSelNT) lds[i] = cg[i];
   __syncthreads();
   const uint64_t* src = in_lds ? lds : cg;
-  const uint64_t kth = block_kth_largest<kSelNT, 64>(
-      cnt, k,
-      [&](int i, uint64_t* key) {
-        *key = src[i];
-        return true;
-      },
-      hist, sh);
 
-  // 3. gather the k composites >= kth (composites are distinct), sort, write descending
+  // 3. The k-th largest key.  Every candidate's key is >= the row's threshold
+  //    key, so the search runs on rel = key - thr from the highest byte that is
+  //    not zero in every rel: candidates spread over the histogram bins instead
+  //    of piling into the one or two bins of their shared top byte.
+  const uint32_t thr = a.thr[row];
+  uint32_t mr = 0;
+  for (int i = tid; i < cnt; i += kSelNT) mr = max(mr, (uint32_t)(src[i] >> 32) - thr);
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) mr = max(mr, (uint32_t)__shfl_xor((int)mr, o, kWave));
+  if (lane == 0) red[w] = (int)mr;
+  __syncthreads();
+  mr = 0;
+#pragma unroll
+  for (int i = 0; i < kSelNT / kWave; ++i) mr = max(mr, (uint32_t)red[i]);
+  const int top = mr == 0 ? 0 : 31 - __clz((int)mr);
+  uint32_t prefix = 0;
+  int remaining = k, ties = 0;
+  for (int shift = (top / 8) * 8; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += kSelNT) hist[i] = 0;
+    __syncthreads();
+    const uint64_t hi = (uint64_t)prefix >> (shift + 8);
+    for (int i = tid; i < cnt; i += kSelNT) {
+      const uint32_t rel = (uint32_t)(src[i] >> 32) - thr;
+      if (((uint64_t)rel >> (shift + 8)) == hi) atomicAdd(&hist[(rel >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid < kWave) {
+      int digit = 0, above = 0;
+      wave_pick_digit(hist, remaining, &digit, &above);
+      int d = digit, ab = above;
+#pragma unroll
+      for (int o = kWave / 2; o > 0; o >>= 1) {
+        d = max(d, __shfl_xor(d, o, kWave));
+        ab = max(ab, __shfl_xor(ab, o, kWave));
+      }
+      if (tid == 0) {
+        sh[0] = d;
+        sh[1] = ab;
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)sh[0] << shift;
+    remaining -= sh[1];
+    ties = (int)hist[sh[0]];
+    __syncthreads();
+  }
+  // candidates above the k-th key all make the list (k - remaining of them);
+  // of the `ties` candidates at it, the `remaining` with the lowest ids do
+  const uint32_t kkey = thr + prefix;
+  uint64_t kth = (uint64_t)kkey << 32;  // every tie is taken
+  if (ties > remaining) {
+    kth = block_kth_largest<kSelNT, 32>(
+              cnt, remaining,
+              [&](int i, uint64_t* key) {
+                *key = (uint32_t)src[i];
+                return (uint32_t)(src[i] >> 32) == kkey;
+              },
+              hist, sh) |
+          ((uint64_t)kkey << 32);
+  }
+
+  // 4. gather the k composites >= kth (composites are distinct), sort, write descending
   const int P = next_pow2(k);
   for (int i = tid; i < P; i += kSelNT) sortb[i] = 0ull;
   if (tid == 0) nsel = 0;
