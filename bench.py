@@ -89,7 +89,65 @@ def parse():
                     help="also time drafting over a 65536-token subset of the vocabulary (walk over all of it)")
     ap.add_argument("--modes-workload", default="batched_modes", choices=["batched_modes", "none"],
                     help="also time a batch mixing K_n = 8 and K_n = 1 trees (per-request mode counts)")
+    ap.add_argument("--lmhead-workload", default="lmhead", choices=["lmhead", "none"],
+                    help="also time the fused LM head + log-softmax/top-k call (one tree and 64 trees)")
     return ap.parse_args()
+
+
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def fused_lmhead(steps: int, stream) -> dict:
+    """Time mfd_lmhead_logsoftmax_topk on the drafter's shape (K=8, L=15,
+    V=151936, D=2560, k=256) at one tree and at 64 trees, beside the unfused
+    route it replaces: the LM-head product into bf16 logits (torch.matmul,
+    a library GEMM) followed by mfd_logsoftmax_topk."""
+    from mixture_draft_tree_amd import mfdtree as M
+    from mixture_draft_tree_amd import synth
+    out = {}
+    reps = max(3, min(steps, 20))
+    for name in ("lmhead_single", "lmhead_batched"):
+        b = synth.lmhead_batch(name, device="cuda")
+        w = b.workload
+        N, K, L, D, V, k = w.N, w.K, w.L, w.D, w.V, min(w.B, w.V)
+        H, W = b.hidden, b.weight
+        e = lambda shape, dt: torch.empty(shape, dtype=dt, device="cuda")
+        lse, ids, raw = e((N, K, L), torch.float64), e((N, K, L, k), torch.int32), e((N, K, L, k), torch.float32)
+        st = torch.zeros((N,), dtype=torch.int32, device="cuda")
+        ws = M.lmhead_workspace(N, K, L, V, k)
+
+        def timed(fn):
+            for _ in range(3):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        fused_ms = timed(lambda: M.mfd_lmhead_logsoftmax_topk(H, W, k, lse, ids, raw, None, st, ws=ws, stream=stream))
+        flops = 2.0 * N * K * L * V * D
+        ok = int(st.abs().sum().item()) == 0
+        logits = e((N * K * L, V), torch.bfloat16)
+        Hf = H.view(N * K * L, D)
+        mm_ms = timed(lambda: torch.matmul(Hf, W.t(), out=logits))
+        lg = logits.view(N, K, L, V)
+        lsm_ms = timed(lambda: M.mfd_logsoftmax_topk(lg, k, lse, ids, raw, None, st, stream=stream))
+        tflops = flops / (fused_ms * 1e-3) / 1e12
+        out[name] = {
+            "workload": f"{name}: {N} tree(s), K={K}, L={L}, V={V}, D={D}, k={k}, bf16 hidden states and LM head",
+            "fused_ms": fused_ms, "status_ok": ok,
+            "tflops": tflops, "frac_of_bf16_mfma_peak": tflops / BF16_MFMA_PEAK_TFLOPS,
+            "head_read_GBps": V * D * 2 / (fused_ms * 1e-3) / 1e9,
+            "unfused_matmul_ms": mm_ms, "unfused_logsoftmax_topk_ms": lsm_ms,
+            "unfused_total_ms": mm_ms + lsm_ms, "fused_over_unfused": fused_ms / (mm_ms + lsm_ms),
+        }
+        del b, H, W, logits, lg, ws
+        torch.cuda.empty_cache()
+    return out
 
 
 def _oracle_worker(name, base_seed, trees, barrier, results):
@@ -385,6 +443,8 @@ def main():
             "tau_mean_by_modes": {str(k): float(mtau[kn == k].mean()) for k in sorted(set(kn.tolist()))},
         }
         del mP, mlog
+    if args.lmhead_workload != "none" and name == "batched":
+        out["fused_lmhead"] = fused_lmhead(args.steps, stream)
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
