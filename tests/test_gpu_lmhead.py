@@ -162,3 +162,53 @@ def test_lmhead_capacity_and_nonfinite_flags():
     assert st[1] & M.MFD_TREE_NONFINITE
     assert np.all(ids[0] == -1) and np.all(np.isneginf(raw[0]))
     assert np.max(np.abs(lse[0] - np.log(w.V))) < LSE_TOL
+
+
+def _grid_inputs(N, K, L, D, V, seed):
+    g = torch.Generator().manual_seed(seed)
+    h = torch.randint(-4, 5, (N, K, L, D), generator=g).to(torch.float32) * 0.25
+    w = torch.randint(-8, 9, (V, D), generator=g).to(torch.float32) * 2.0 ** -5
+    return h.to(torch.bfloat16), w.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("N,K,L,D,V,k", [
+    (1, 1, 1, 64, 16, 16),      # one row in a 128-row tile, one partial vocabulary tile, k = V
+    (2, 3, 2, 64, 300, 256),    # fewer sample groups than k: every column is a candidate
+    (1, 2, 3, 128, 1000, 1000), # k = V: the whole row, ranked
+    (5, 1, 30, 64, 2049, 5),    # 150 rows over two row tiles, V one past a tile multiple
+    (1, 4, 4, 2560, 8192, 2048),  # the largest k, full drafter width
+])
+def test_lmhead_grid_edge_shapes(N, K, L, D, V, k):
+    _say(f"lmhead grid edge N={N} K={K} L={L} D={D} V={V} k={k}")
+    h, w = _grid_inputs(N, K, L, D, V, seed=N * 1000 + V)
+    lse, ids, raw, lp, st = _run(h, w, k)
+    assert np.all(st == 0)
+    x64 = O.lmhead_logits(h.float().numpy(), w.float().numpy())
+    _check_exact(x64, k, lse, ids, raw, lp)
+
+
+def test_lmhead_repeat_calls_and_workspace_reuse():
+    # The same workspace serves calls of different sizes in a row; results
+    # do not depend on what an earlier call left in it.
+    _say("lmhead workspace reuse")
+    big_h, big_w = _grid_inputs(2, 2, 3, 128, 5000, seed=5)
+    small_h, small_w = _grid_inputs(1, 2, 2, 64, 700, seed=6)
+    k = 64
+    ws = M.lmhead_workspace(2, 2, 3, 5000, k)
+    outs = []
+    for h, w in ((big_h, big_w), (small_h, small_w), (big_h, big_w)):
+        N, K, L, D = h.shape
+        H, W = h.cuda(), w.cuda()
+        lse = torch.empty((N, K, L), dtype=torch.float64, device="cuda")
+        ids = torch.empty((N, K, L, k), dtype=torch.int32, device="cuda")
+        raw = torch.empty((N, K, L, k), dtype=torch.float32, device="cuda")
+        st = torch.zeros((N,), dtype=torch.int32, device="cuda")
+        M.mfd_lmhead_logsoftmax_topk(H, W, k, lse, ids, raw, None, st, ws=ws)
+        torch.cuda.synchronize()
+        assert int(st.abs().sum()) == 0
+        x64 = O.lmhead_logits(h.float().numpy(), w.float().numpy())
+        o_lse, o_ids = oracle_rows(x64, k)
+        assert np.array_equal(ids.cpu().numpy(), o_ids)
+        assert np.max(np.abs(lse.cpu().numpy() - o_lse)) < LSE_TOL
+        outs.append(ids.cpu().numpy())
+    assert np.array_equal(outs[0], outs[2])
