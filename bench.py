@@ -249,6 +249,36 @@ def run_steps(P, logits, anchor, pos, R, temps, seeds, steps, warmup, stream):
     return t_start.elapsed_time(t_end), ev
 
 
+def capture_step(P, logits, anchor, pos, R, temps, seeds):
+    """The five calls of one step captured in a HIP graph (torch.cuda.CUDAGraph)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        P.step(logits, anchor, pos, R, temps, seeds)   # warm-up on the capturing stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        P.step(logits, anchor, pos, R, temps, seeds)
+    torch.cuda.synchronize()
+    return g
+
+
+def graph_steps(g, steps, warmup, stream):
+    """Times `steps` replays of a captured step; returns (ms per step, sorted per-step ms)."""
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for s in range(steps):
+        g.replay()
+        ev[s + 1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(ev[s].elapsed_time(ev[s + 1]) for s in range(steps))
+    return ev[0].elapsed_time(ev[steps]) / steps, per
+
+
 def setup(name, seed, dev):
     from mixture_draft_tree_amd import synth
     from mixture_draft_tree_amd.pipeline import MixtureTreePath
@@ -331,9 +361,19 @@ def timed_workload(name, seed, steps, warmup, stream, diagnostics=False):
     stage["step_ms_percentiles"] = {"p10": q(0.1), "p50": statistics.median(per_step), "p90": q(0.9)}
     status = P.buf.status.cpu()
     assert int(status.abs().sum()) == 0, f"per-tree status flags set ({name}): {status.tolist()}"
+    # the same step captured in a HIP graph: no host launch work between the calls
+    g = capture_step(P, logits, anchor, pos, R, temps, seeds)
+    graph_ms, gper = graph_steps(g, steps, warmup, stream)
+    del g
+    stage["eager_ms_per_step"] = total_ms / steps
+    stage["eager_step_ms_percentiles"] = stage.pop("step_ms_percentiles")
+    q = lambda f: gper[min(len(gper) - 1, int(f * len(gper)))]
+    stage["step_ms_percentiles"] = {"p10": q(0.1), "p50": statistics.median(gper), "p90": q(0.9)}
+    status = P.buf.status.cpu()
+    assert int(status.abs().sum()) == 0, f"per-tree status flags set ({name}): {status.tolist()}"
     if diagnostics:
         stage["diagnostics"] = covered_mass_stats(P, R, temps, stream)
-    return total_ms / steps, stage, N, w, P, logits
+    return graph_ms, stage, N, w, P, logits
 
 
 def main():
@@ -351,6 +391,8 @@ def main():
                                                             diagnostics=True)
     diag = stage_ms.pop("diagnostics")
     pcts = stage_ms.pop("step_ms_percentiles")
+    eager_ms = stage_ms.pop("eager_ms_per_step")
+    eager_pcts = stage_ms.pop("eager_step_ms_percentiles")
 
     rows = N * w.K * w.L if P.modes is None else int(P.modes.sum()) * w.L   # rows the logits pass reads
     logits_bytes = rows * logits.shape[-1] * logits.element_size()
@@ -381,6 +423,10 @@ def main():
                      "read_ceiling": ceiling, "frac_of_read_ceiling": achieved / ceiling["GBps"],
                      "valu_issue_frac": profile_field(SQ_FILE, name, "lsm_valu_issue_frac")},
         "step_ms_percentiles": pcts,
+        "launch": "each step is one replay of a HIP graph holding the five calls; stages_ms are timed on eager "
+                  "launches with events between the calls",
+        "eager_ms_per_step": eager_ms,
+        "eager_step_ms_percentiles": eager_pcts,
         "stages_ms": stage_ms,
         "logits_GBps": achieved,
         "per_tree_latency_ms": ms_per_step if N == 1 else None,
@@ -398,12 +444,15 @@ def main():
                                                     diagnostics=True)
         ddiag = dstage.pop("diagnostics")
         dpcts = dstage.pop("step_ms_percentiles")
+        deager = dstage.pop("eager_ms_per_step")
+        dstage.pop("eager_step_ms_percentiles")
         out["deep"] = {
             "workload": f"{args.deep_workload}: {dN} trees, K={dw.K}, L={dw.L}, V={dw.V}, B={dw.B}, "
                         f"T pattern {list(dw.temperatures)}",
             "data": "synthetic (seeded; confident drafter: N(0,4) noise, 16 Zipf alternatives, each mode's future "
                     "at 16+N(0,2.25); target rows N(0,1) + 16 on one future up to a random deviation depth)",
             "value": dN / (dms * 1e-3), "unit": "trees/s", "ms_per_step": dms, "step_ms_percentiles": dpcts,
+            "eager_ms_per_step": deager,
             "stages_ms": dstage,
             "tau_mean": float(dP.buf.tau.cpu().float().mean()),
             "single_tree_latency_ms": (single_tree_latency(args.seed, args.latency_steps, stream, "deep")
@@ -414,12 +463,15 @@ def main():
         sms, sstage, sN, sw, sP, slog = timed_workload(args.subset_workload, args.seed, args.steps, args.warmup,
                                                        stream)
         spcts = sstage.pop("step_ms_percentiles")
+        seager = sstage.pop("eager_ms_per_step")
+        sstage.pop("eager_step_ms_percentiles")
         sbytes = sN * sw.K * sw.L * slog.shape[-1] * slog.element_size()
         sgbs = sbytes / (sstage["logsoftmax_topk"] * 1e-3) / 1e9
         out["reduced_vocab"] = {
             "workload": f"{args.subset_workload}: {sN} trees, K={sw.K}, L={sw.L}, drafting over {slog.shape[-1]} of "
                         f"V={sw.V} tokens, B={sw.B}, T pattern {list(sw.temperatures)}",
             "value": sN / (sms * 1e-3), "unit": "trees/s", "ms_per_step": sms, "step_ms_percentiles": spcts,
+            "eager_ms_per_step": seager,
             "stages_ms": sstage,
             "logits_GBps": sgbs, "logits_frac_of_peak": sgbs / HBM_PEAK_GBS,
             "algorithmic_bytes_per_launch": sbytes, "tau_mean": float(sP.buf.tau.cpu().float().mean()),
@@ -429,6 +481,8 @@ def main():
         mms, mstage, mN, mw, mP, mlog = timed_workload(args.modes_workload, args.seed, args.steps, args.warmup,
                                                        stream)
         mpcts = mstage.pop("step_ms_percentiles")
+        meager = mstage.pop("eager_ms_per_step")
+        mstage.pop("eager_step_ms_percentiles")
         kn = mP.modes.cpu()
         mbytes = int(kn.sum()) * mw.L * mw.V * mlog.element_size()
         mgbs = mbytes / (mstage["logsoftmax_topk"] * 1e-3) / 1e9
@@ -437,6 +491,7 @@ def main():
             "workload": f"{args.modes_workload}: {mN} trees of the confident-drafter shape, K={mw.K}, L={mw.L}, "
                         f"V={mw.V}, B={mw.B}, K_n cycling {list(mw.modes)}, T pattern {list(mw.temperatures)}",
             "value": mN / (mms * 1e-3), "unit": "trees/s", "ms_per_step": mms, "step_ms_percentiles": mpcts,
+            "eager_ms_per_step": meager,
             "stages_ms": mstage,
             "active_rows": int(kn.sum()) * mw.L, "logits_GBps": mgbs, "logits_frac_of_peak": mgbs / HBM_PEAK_GBS,
             "algorithmic_bytes_per_launch": mbytes,
