@@ -36,9 +36,20 @@
 namespace mfd {
 namespace {
 
-constexpr int kBM = 128, kBN = 256, kBK = 32, kNT = 256;
+constexpr int kBM = 128, kBK = 32, kNT = 256;
 constexpr int kLdk = kBK + 8;  // bf16 per LDS row: 80 bytes, conflict-free 16-byte reads
-constexpr int kGroupsPerTile = 64;
+constexpr int kSampleCols = 8192;  // vocabulary columns in the threshold sample
+constexpr int kSmallM = 256;       // up to this many rows, tiles are 128 columns wide
+
+// Tile shapes.  The four waves of a workgroup split its 128 rows x BN columns
+// as WGM (rows) x WGN (columns) waves of (128 / WGM) x 128; a wave's part is
+// IM x 4 blocks of 32 x 32.  WGM = 2: 128 x 256 tiles (large M: the head tile
+// serves more rows per fetch).  WGM = 4: 128 x 128 tiles (few rows: twice the
+// tiles, so one tree's 1187 tiles spread over the CUs in fewer idle rounds).
+template <int WGM>
+struct TileShape {
+  static constexpr int WGN = 4 / WGM, BN = WGN * 128, IM = 4 / WGM, GPT = WGN * 32, NB = BN / 64;
+};
 constexpr int kSelNT = 256;
 constexpr int kSelLdsCap = 8192;  // candidates a select workgroup holds in LDS
 
@@ -49,9 +60,11 @@ struct LmhArgs {
   const uint16_t* H;  // [M, D] bf16 bits
   const uint16_t* W;  // [V, D] bf16 bits
   int M, D, V, T, S, rows_per_tree;
-  uint32_t* samp;       // [M, S * 64] group-maximum keys (0 = empty group)
+  int gpt;              // groups of 4 columns per tile (WGN * 32)
+  int wgn;              // waves across a tile's columns
+  uint32_t* samp;       // [M, S * gpt] group-maximum keys (0 = empty group)
   uint32_t* thr;        // [M] candidate threshold keys
-  float2* part;         // [M, 2T] (max, sum exp(x - max)) per tile and wave column
+  float2* part;         // [M, wgn * T] (max, sum exp(x - max)) per tile and wave column
   uint64_t* cand;       // [M, C] candidate composites
   int* cand_count;      // [M]
   int C;
@@ -83,10 +96,12 @@ __device__ __forceinline__ bool tile_of(int b, int nM, int nVt, int* m_out, int*
   return true;
 }
 
-template <bool SAMPLE>
+template <bool SAMPLE, int WGM>
 __global__ void __launch_bounds__(kNT, 2) lmh_tile_kernel(LmhArgs a) {
+  using TS = TileShape<WGM>;
+  constexpr int BN = TS::BN, WGN = TS::WGN, IM = TS::IM, GPT = TS::GPT;
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][kBM][kLdk];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kBN][kLdk];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN][kLdk];
   __shared__ uint32_t sthr[kBM];
 
   const int nM = (a.M + kBM - 1) / kBM;
@@ -94,17 +109,17 @@ __global__ void __launch_bounds__(kNT, 2) lmh_tile_kernel(LmhArgs a) {
   int mt, vt_i;
   if (!tile_of((int)blockIdx.x, nM, nVt, &mt, &vt_i)) return;  // whole workgroup, before any barrier
   const int vt = SAMPLE ? (int)(((long long)vt_i * a.T) / a.S) : vt_i;
-  const int row0 = mt * kBM, col0 = vt * kBN;
+  const int row0 = mt * kBM, col0 = vt * BN;
   const int tid = (int)threadIdx.x, lane = lane_id(), w = wave_id();
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / WGN, wn = w % WGN;
   const int D = a.D;
 
   if (!SAMPLE) {
     for (int i = tid; i < kBM; i += kNT) sthr[i] = row0 + i < a.M ? a.thr[row0 + i] : 0xFFFFFFFFu;
   }
 
-  // global -> register chunks of 8 bf16: A 512 per stage (2 per thread), B 1024
-  // (4 per thread).  Chunk c is row c / 4, k-offset 8 (c % 4) of the stage.
+  // global -> register chunks of 8 bf16: A 512 per stage (2 per thread), B 4 BN
+  // (BN / 64 per thread).  Chunk c is row c / 4, k-offset 8 (c % 4) of the stage.
   // Rows past the matrix read its last row (their results are dropped).
   const int q8 = (tid & 3) * 8, r0 = tid >> 2;
   const uint16_t* a0p = a.H + (size_t)min(row0 + r0, a.M - 1) * D + q8;
@@ -124,8 +139,10 @@ __global__ void __launch_bounds__(kNT, 2) lmh_tile_kernel(LmhArgs a) {
     P##a1 = *reinterpret_cast<const uint4*>(a1p + (k0));       \
     P##b0 = *reinterpret_cast<const uint4*>(b0p + (k0));       \
     P##b1 = *reinterpret_cast<const uint4*>(b1p + (k0));       \
-    P##b2 = *reinterpret_cast<const uint4*>(b2p + (k0));       \
-    P##b3 = *reinterpret_cast<const uint4*>(b3p + (k0));       \
+    if constexpr (TS::NB == 4) {                               \
+      P##b2 = *reinterpret_cast<const uint4*>(b2p + (k0));     \
+      P##b3 = *reinterpret_cast<const uint4*>(b3p + (k0));     \
+    }                                                          \
   } while (0)
 #define LMH_LSTORE(P, buf)                                          \
   do {                                                              \
@@ -133,13 +150,15 @@ __global__ void __launch_bounds__(kNT, 2) lmh_tile_kernel(LmhArgs a) {
     *reinterpret_cast<uint4*>(&sA[buf][r0 + 64][q8]) = P##a1;       \
     *reinterpret_cast<uint4*>(&sB[buf][r0][q8]) = P##b0;            \
     *reinterpret_cast<uint4*>(&sB[buf][r0 + 64][q8]) = P##b1;       \
-    *reinterpret_cast<uint4*>(&sB[buf][r0 + 128][q8]) = P##b2;      \
-    *reinterpret_cast<uint4*>(&sB[buf][r0 + 192][q8]) = P##b3;      \
+    if constexpr (TS::NB == 4) {                                    \
+      *reinterpret_cast<uint4*>(&sB[buf][r0 + 128][q8]) = P##b2;    \
+      *reinterpret_cast<uint4*>(&sB[buf][r0 + 192][q8]) = P##b3;    \
+    }                                                               \
   } while (0)
 
-  f32x16 acc[2][4];
+  f32x16 acc[IM][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < IM; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -151,12 +170,12 @@ __global__ void __launch_bounds__(kNT, 2) lmh_tile_kernel(LmhArgs a) {
 #define LMH_COMPUTE(buf)                                                                          \
   do {                                                                                            \
     _Pragma("unroll") for (int kk = 0; kk < kBK; kk += 16) {                                      \
-      bf16x8 af[2], bfv[4];                                                                       \
-      _Pragma("unroll") for (int i = 0; i < 2; ++i)                                               \
-        af[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][wm * 64 + i * 32 + lr][kk + lk]);       \
+      bf16x8 af[IM], bfv[4];                                                                      \
+      _Pragma("unroll") for (int i = 0; i < IM; ++i)                                              \
+        af[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][wm * 32 * IM + i * 32 + lr][kk + lk]);  \
       _Pragma("unroll") for (int j = 0; j < 4; ++j)                                               \
         bfv[j] = *reinterpret_cast<const bf16x8*>(&sB[buf][wn * 128 + j * 32 + lr][kk + lk]);     \
-      _Pragma("unroll") for (int i = 0; i < 2; ++i)                                               \
+      _Pragma("unroll") for (int i = 0; i < IM; ++i)                                              \
         _Pragma("unroll") for (int j = 0; j < 4; ++j)                                             \
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0); \
     }                                                                                             \
@@ -199,17 +218,17 @@ __global__ void __launch_bounds__(kNT, 2) lmh_tile_kernel(LmhArgs a) {
 #undef LMH_LSTORE
 
   // Epilogue.  Accumulator element e of block (i, j) is row
-  // wm*64 + i*32 + 8*(e/4) + 4*(lane/32) + e%4 and column wn*128 + j*32 + lane%32
+  // wm*32*IM + i*32 + 8*(e/4) + 4*(lane/32) + e%4 and column wn*128 + j*32 + lane%32
   // of the tile.  For one (i, e) a lane holds 4 columns of one row (j = 0..3):
   // a group; the 32 lanes of a half-wave hold that row's other groups.
   const uint64_t half = lane < 32 ? 0x00000000FFFFFFFFull : 0xFFFFFFFF00000000ull;
   const uint64_t lt = (1ull << lane) - 1ull;
   bool bad = false;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < IM; ++i) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int rt = wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      const int rt = wm * 32 * IM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
       const int grow = row0 + rt;
       float x[4];
       bool ok[4];
@@ -224,7 +243,7 @@ __global__ void __launch_bounds__(kNT, 2) lmh_tile_kernel(LmhArgs a) {
         for (int j = 0; j < 4; ++j)
           if (ok[j]) g = max(g, f32_key(__float_as_uint(x[j])));
         if (grow < a.M)
-          a.samp[(size_t)grow * ((size_t)a.S * kGroupsPerTile) + (size_t)vt_i * kGroupsPerTile + wn * 32 + lr] = g;
+          a.samp[(size_t)grow * ((size_t)a.S * GPT) + (size_t)vt_i * GPT + wn * 32 + lr] = g;
       } else {
         // partial log-sum-exp over this wave's 128 columns of the row
         float mx = -INFINITY;
@@ -245,13 +264,13 @@ __global__ void __launch_bounds__(kNT, 2) lmh_tile_kernel(LmhArgs a) {
         }
 #pragma unroll
         for (int o = 16; o > 0; o >>= 1) sm += __shfl_xor(sm, o, kWave);
-        if (lr == 0 && grow < a.M) a.part[(size_t)grow * (2 * (size_t)a.T) + 2 * vt + wn] = make_float2(mx, sm);
+        if (lr == 0 && grow < a.M) a.part[(size_t)grow * (WGN * (size_t)a.T) + WGN * vt + wn] = make_float2(mx, sm);
 
         // candidates: logits at or above the row's threshold
         const uint32_t th = sthr[rt];
         bool p[4];
         uint32_t kx[4];
-        int mine = 0, before = 0, total = 0;
+        int before = 0, total = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           kx[j] = f32_key(__float_as_uint(x[j]));
@@ -259,7 +278,6 @@ __global__ void __launch_bounds__(kNT, 2) lmh_tile_kernel(LmhArgs a) {
           const uint64_t b = __ballot(p[j]);
           before += __popcll(b & half & lt);
           total += __popcll(b & half);
-          mine += p[j] ? 1 : 0;
         }
         int base = 0;
         if (lr == 0 && total > 0 && grow < a.M) base = atomicAdd(&a.cand_count[grow], total);
@@ -274,17 +292,16 @@ __global__ void __launch_bounds__(kNT, 2) lmh_tile_kernel(LmhArgs a) {
             }
           }
         }
-        (void)mine;
       }
     }
   }
   if (!SAMPLE && bad && a.status != nullptr) {
     // rows of this lane's tile part: flag every tree the tile touches that holds a bad value
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < IM; ++i) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int grow = row0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int grow = row0 + wm * 32 * IM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
         bool rb_ = false;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -303,7 +320,7 @@ __global__ void __launch_bounds__(kSelNT) lmh_threshold_kernel(LmhArgs a, int k)
   __shared__ int sh[2];
   __shared__ int red[kSelNT / kWave];
   const int row = (int)blockIdx.x;
-  const int n = a.S * kGroupsPerTile;
+  const int n = a.S * a.gpt;
   const uint32_t* g = a.samp + (size_t)row * n;
   int cnt = 0;
   for (int i = threadIdx.x; i < n; i += kSelNT) cnt += g[i] != 0u ? 1 : 0;
@@ -340,7 +357,7 @@ __global__ void __launch_bounds__(kSelNT) lmh_select_kernel(LmhArgs a, int k, do
   __shared__ int nsel;
   const int row = (int)blockIdx.x;
   const int tid = (int)threadIdx.x, lane = lane_id(), w = wave_id();
-  const int np = 2 * a.T;
+  const int np = a.wgn * a.T;
   const float2* part = a.part + (size_t)row * np;
 
   // 1. lse = M + log sum_t s_t exp(m_t - M), fp64, fixed reduction order
@@ -482,11 +499,15 @@ __global__ void __launch_bounds__(kSelNT) lmh_select_kernel(LmhArgs a, int k, do
 
 LmhWorkspace lmhead_workspace(long long M, int V, int k) {
   LmhWorkspace w{};
-  w.T = (V + kBN - 1) / kBN;
-  w.S = w.T < 32 ? w.T : 32;
-  // about k V / (S * 256) candidates per row for rows of independent logits;
+  w.small = M <= kSmallM;
+  const int BN = w.small ? TileShape<4>::BN : TileShape<2>::BN;
+  w.gpt = w.small ? TileShape<4>::GPT : TileShape<2>::GPT;
+  w.wgn = w.small ? TileShape<4>::WGN : TileShape<2>::WGN;
+  w.T = (V + BN - 1) / BN;
+  w.S = w.T < kSampleCols / BN ? w.T : kSampleCols / BN;
+  // about k V / (S * BN) candidates per row for rows of independent logits;
   // four times that leaves room for rows of uneven spread
-  const long long expect = ((long long)k * V + (long long)w.S * kBN - 1) / ((long long)w.S * kBN);
+  const long long expect = ((long long)k * V + (long long)w.S * BN - 1) / ((long long)w.S * BN);
   long long C = 4 * expect;
   if (C < 2LL * k) C = 2LL * k;
   if (C < 4096) C = 4096;
@@ -500,10 +521,10 @@ LmhWorkspace lmhead_workspace(long long M, int V, int k) {
     off += (bytes + 255) / 256 * 256;
     return o;
   };
-  w.off_samp = take((size_t)M * w.S * kGroupsPerTile * sizeof(uint32_t));
+  w.off_samp = take((size_t)M * w.S * w.gpt * sizeof(uint32_t));
   w.off_thr = take((size_t)M * sizeof(uint32_t));
   w.off_count = take((size_t)M * sizeof(int));
-  w.off_part = take((size_t)M * 2 * w.T * sizeof(float2));
+  w.off_part = take((size_t)M * w.wgn * w.T * sizeof(float2));
   w.off_cand = take((size_t)M * w.C * sizeof(uint64_t));
   w.bytes = off;
   return w;
@@ -522,6 +543,8 @@ hipError_t launch_lmhead_topk(const void* hidden, const void* weight, int M, int
   a.V = V;
   a.T = wsl.T;
   a.S = wsl.S;
+  a.gpt = wsl.gpt;
+  a.wgn = wsl.wgn;
   a.rows_per_tree = rows_per_tree;
   a.samp = reinterpret_cast<uint32_t*>(base + wsl.off_samp);
   a.thr = reinterpret_cast<uint32_t*>(base + wsl.off_thr);
@@ -533,9 +556,15 @@ hipError_t launch_lmhead_topk(const void* hidden, const void* weight, int M, int
   const int nM = (M + kBM - 1) / kBM;
   const long long ns = (long long)nM * a.S, nm = (long long)nM * a.T;
   const long long gs = (ns + 7) / 8 * 8, gm = (nm + 7) / 8 * 8;
-  hipLaunchKernelGGL(lmh_tile_kernel<true>, dim3((unsigned)gs), dim3(kNT), 0, stream, a);
-  hipLaunchKernelGGL(lmh_threshold_kernel, dim3(M), dim3(kSelNT), 0, stream, a, k);
-  hipLaunchKernelGGL(lmh_tile_kernel<false>, dim3((unsigned)gm), dim3(kNT), 0, stream, a);
+  if (wsl.small) {
+    hipLaunchKernelGGL((lmh_tile_kernel<true, 4>), dim3((unsigned)gs), dim3(kNT), 0, stream, a);
+    hipLaunchKernelGGL(lmh_threshold_kernel, dim3(M), dim3(kSelNT), 0, stream, a, k);
+    hipLaunchKernelGGL((lmh_tile_kernel<false, 4>), dim3((unsigned)gm), dim3(kNT), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((lmh_tile_kernel<true, 2>), dim3((unsigned)gs), dim3(kNT), 0, stream, a);
+    hipLaunchKernelGGL(lmh_threshold_kernel, dim3(M), dim3(kSelNT), 0, stream, a, k);
+    hipLaunchKernelGGL((lmh_tile_kernel<false, 2>), dim3((unsigned)gm), dim3(kNT), 0, stream, a);
+  }
   const size_t lds = (size_t)(kSelLdsCap + next_pow2(k)) * sizeof(uint64_t);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lmh_select_kernel),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -66,9 +66,12 @@ hipError_t launch_verify_walk(const void* target, bool bf16, int N, int Bp1, lon
 // Fused LM head + log-softmax/top-k: workspace layout (byte offsets into the
 // caller's buffer) and launcher.
 struct LmhWorkspace {
-  int T;  // vocabulary tiles of 256 columns
-  int S;  // tiles in the threshold sample
-  int C;  // candidate capacity per row
+  bool small;  // 128-column tiles (few rows) instead of 256-column ones
+  int gpt;     // groups of 4 columns per tile
+  int wgn;     // partials per row and tile
+  int T;       // vocabulary tiles
+  int S;       // tiles in the threshold sample
+  int C;       // candidate capacity per row
   size_t off_samp, off_thr, off_count, off_part, off_cand, bytes;
 };
 LmhWorkspace lmhead_workspace(long long M, int V, int k);

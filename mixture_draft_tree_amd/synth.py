@@ -357,6 +357,8 @@ LMHEAD_WORKLOADS = {
     "lmhead_ragged": LmHeadWorkload("lmhead_ragged", 21, 3, 7, 4133, 192, 64, 5, False),
     # two row tiles (the second ragged) and a sampled threshold
     "lmhead_mid": LmHeadWorkload("lmhead_mid", 22, 8, 15, 40000, 256, 256, 2, True),
+    # 360 rows: more than 256, so the 256-column tiles of large batches are used
+    "lmhead_wide": LmHeadWorkload("lmhead_wide", 26, 8, 15, 40000, 256, 256, 3, True),
     # the MFD drafter's shape: K=8 modes x 15 positions over V=151936 at D=2560
     "lmhead_single": LmHeadWorkload("lmhead_single", 23, 8, 15, 151936, 2560, 256, 1, False),
     "lmhead_single_grid": LmHeadWorkload("lmhead_single_grid", 24, 8, 15, 151936, 2560, 256, 1, True),

@@ -68,7 +68,7 @@ def _check_bounded(x64, eps, k, lse, ids, raw):
         assert abs(lse[r] - O.lse_rows(x)) < LSE_TOL + em
 
 
-@pytest.mark.parametrize("name", ["lmhead_small", "lmhead_mid"])
+@pytest.mark.parametrize("name", ["lmhead_small", "lmhead_mid", "lmhead_wide"])
 def test_lmhead_grid_bit_exact(name):
     _say(f"lmhead grid parity {name}")
     b = synth.lmhead_batch(name)
@@ -103,7 +103,7 @@ def test_lmhead_grid_other_k(k):
     _check_exact(x64, k, lse, ids, raw, lp)
 
 
-@pytest.mark.parametrize("name", ["lmhead_small", "lmhead_mid"])
+@pytest.mark.parametrize("name", ["lmhead_small", "lmhead_mid", "lmhead_wide"])
 def test_lmhead_tree_equals_oracle_tree(name):
     # The tree built from the fused outputs equals the oracle's tree over the
     # exact logits (grid inputs).
@@ -126,9 +126,10 @@ def test_lmhead_tree_equals_oracle_tree(name):
 
 
 def test_lmhead_full_size_sampled_rows():
-    # The drafter's shape (K=8, L=15, V=151936, D=2560, k=256), one tree: grid
-    # inputs bit-exact on sampled rows, Gaussian inputs within the bound.
-    for name in ("lmhead_single_grid", "lmhead_single"):
+    # The drafter's shape (K=8, L=15, V=151936, D=2560, k=256): one tree with
+    # grid inputs bit-exact on sampled rows, one tree and the 64-tree batch
+    # (256-column tiles) with Gaussian inputs within the bound.
+    for name in ("lmhead_single_grid", "lmhead_single", "lmhead_batched"):
         _say(f"lmhead full-size sampled rows {name}")
         b = synth.lmhead_batch(name)
         w = b.workload
@@ -137,7 +138,7 @@ def test_lmhead_full_size_sampled_rows():
         assert np.all(st == 0)
         h = b.hidden.float().numpy().reshape(-1, w.D)
         W = b.weight.float().numpy()
-        rows = [0, 1, 14, 15, 59, 60, 100, 119]
+        rows = [0, 1, 14, 15, 59, 60, 100, 119] if w.N == 1 else [0, 127, 128, 3001, 7679]
         x64 = O.lmhead_logits(h[rows], W)
         if w.grid:
             _check_exact(x64, k, lse.reshape(-1)[rows], ids.reshape(-1, k)[rows], raw.reshape(-1, k)[rows],
