@@ -128,11 +128,15 @@ __global__ void __launch_bounds__(kNT, 2) lmh_tile_kernel(LmhArgs a) {
   const uint16_t* b1p = a.W + (size_t)min(col0 + r0 + 64, a.V - 1) * D + q8;
   const uint16_t* b2p = a.W + (size_t)min(col0 + r0 + 128, a.V - 1) * D + q8;
   const uint16_t* b3p = a.W + (size_t)min(col0 + r0 + 192, a.V - 1) * D + q8;
-  // Register staging, two stages deep: stage j's chunks sit in register set
-  // j % 2 from their global load (issued at step j - 2) until they are copied
-  // to LDS at the end of step j - 1.
+  // Register staging, NSET stages deep: stage j's chunks sit in register set
+  // j % NSET from their global load (issued at step j - NSET) until they are
+  // copied to LDS at the end of step j - 1.  Narrow tiles have the registers
+  // for four sets (loads three steps ahead of their use); wide tiles two.
+  constexpr int NSET = WGM == 4 ? 4 : 2;
   uint4 p0a0, p0a1, p0b0, p0b1, p0b2, p0b3;
   uint4 p1a0, p1a1, p1b0, p1b1, p1b2, p1b3;
+  uint4 p2a0, p2a1, p2b0, p2b1, p2b2, p2b3;
+  uint4 p3a0, p3a1, p3b0, p3b1, p3b2, p3b3;
 #define LMH_GLOAD(P, k0)                                       \
   do {                                                         \
     P##a0 = *reinterpret_cast<const uint4*>(a0p + (k0));       \
@@ -186,7 +190,7 @@ __global__ void __launch_bounds__(kNT, 2) lmh_tile_kernel(LmhArgs a) {
 #define LMH_STEP(CUR, NXT)                                  \
   {                                                         \
     const int buf = s & 1;                                  \
-    LMH_GLOAD(CUR, min(s + 2, nS - 1) * kBK);               \
+    LMH_GLOAD(CUR, min(s + NSET, nS - 1) * kBK);            \
     LMH_COMPUTE(buf);                                       \
     if (s + 1 < nS) LMH_LSTORE(NXT, buf ^ 1);               \
     __syncthreads();                                        \
@@ -203,14 +207,30 @@ __global__ void __launch_bounds__(kNT, 2) lmh_tile_kernel(LmhArgs a) {
 
   LMH_GLOAD(p0, 0);
   LMH_GLOAD(p1, min(1, nS - 1) * kBK);
+  if constexpr (NSET == 4) {
+    LMH_GLOAD(p2, min(2, nS - 1) * kBK);
+    LMH_GLOAD(p3, min(3, nS - 1) * kBK);
+  }
   LMH_LSTORE(p0, 0);
   __syncthreads();
   int s = 0;
-  while (s + 2 <= nS) {
-    LMH_STEP(p0, p1)
-    LMH_STEP(p1, p0)
+  if constexpr (NSET == 4) {
+    while (s + 4 <= nS) {
+      LMH_STEP(p0, p1)
+      LMH_STEP(p1, p2)
+      LMH_STEP(p2, p3)
+      LMH_STEP(p3, p0)
+    }
+    LMH_TAIL_STEP(p1)
+    LMH_TAIL_STEP(p2)
+    LMH_TAIL_STEP(p3)
+  } else {
+    while (s + 2 <= nS) {
+      LMH_STEP(p0, p1)
+      LMH_STEP(p1, p0)
+    }
+    LMH_TAIL_STEP(p1)
   }
-  LMH_TAIL_STEP(p1)
 #undef LMH_TAIL_STEP
 #undef LMH_STEP
 #undef LMH_COMPUTE
