@@ -191,8 +191,10 @@ mfd_status mfd_mixture_threshold(const int32_t* topk_id, const float* topk_raw, 
  *   score     device [N, B+1] fp64 out: S of each node.
  *   n_nodes   device [N] int32 out: n_select + 1.
  *   status    device [N] int32 or NULL: MFD_TREE_CAPACITY if the prefixes
- *             reaching the cut-off (or the ties at it) exceed the working
- *             capacity; that tree's rows are then not valid.
+ *             reaching the cut-off exceed the working capacity, or more than
+ *             2 C / (1 + L) prefixes tie exactly at the n_select-th score, with
+ *             C = the next power of two of max(2 K k, 2 (B + 1), 2048), at most
+ *             16384; that tree's rows are then not valid.
  *   ws        device workspace of at least mfd_workspace_size(MFD_OP_TREE_BUILD).
  */
 mfd_status mfd_tree_build(const int32_t* topk_id, const float* topk_raw, const double* lse,

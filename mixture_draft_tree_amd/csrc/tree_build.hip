@@ -934,7 +934,7 @@ TreeCaps tree_caps(int K, int L, int k, int B) {
   TreeCaps c;
   long long want = 2LL * K * k;
   if (want < 2LL * (B + 1)) want = 2LL * (B + 1);
-  if (want < 1024) want = 1024;
+  if (want < 2048) want = 2048;  // small trees: room for ~4096 / (1 + L) exact ties at the cut-off
   if (want > kMaxSort) want = kMaxSort;
   c.sort_cap = next_pow2((int)want);
   c.ent_cap = 4 * c.sort_cap;

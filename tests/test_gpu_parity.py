@@ -566,3 +566,48 @@ def test_chimera_count_parity(name):
         assert count[n].item() == want, (n, count[n].item(), want)
     if name == "product":
         assert count[0].item() >= 3  # the 2^(m-1)-1 = 3 spliced prefixes at full split depth, at least
+
+
+SWEEP = [
+    # K, L, V, B, sigma (0: small integers, many ties); first-level children K * min(B, V)
+    (8, 3, 600, 1200, 0.5),    # ~4800 children: past the register sorts (LDS network)
+    (3, 5, 1000, 1000, 0.3),   # ~3000: register sort of 4096 keys (four per lane)
+    (2, 4, 1000, 1000, 0.3),   # ~2000: register sort of 2048 keys (two per lane)
+    (6, 4, 300, 700, 1.0),     # ~1800
+    (4, 6, 100, 400, 0.0),     # ~400 with ties: one key per lane
+    (2, 10, 64, 150, 2.0),     # deeper, small levels
+    (8, 15, 2000, 256, 3.0),   # the specified mixture shape at a small vocabulary
+]
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=[f"K{c[0]}L{c[1]}V{c[2]}B{c[3]}" for c in SWEEP])
+def test_tree_sweep_level_sizes(case):
+    """Batches of flat-logit trees whose search levels span every level-sort
+    size (one key per lane up to past 4096 keys): each tree, mask and the
+    per-mode keep counts against the oracle."""
+    K, L, V, B, sigma = case
+    N = 4
+    say(f"[sweep] K={K} L={L} V={V} B={B} sigma={sigma}")
+    xs = []
+    for n in range(N):
+        g = torch.Generator().manual_seed(1000 * K + 10 * L + n)
+        if sigma == 0.0:
+            xs.append(torch.randint(-2, 3, (1, K, L, V), generator=g).float())
+        else:
+            xs.append(torch.randn((1, K, L, V), generator=g) * sigma)
+    x = torch.cat(xs)
+    P = MixtureTreePath(N, K, L, V, B)
+    anchor = torch.arange(N, dtype=torch.int32, device="cuda") + 11
+    pos = torch.arange(N, dtype=torch.int64, device="cuda") * 64
+    P.build(x.cuda(), anchor, pos)
+    torch.cuda.synchronize()
+    assert P.buf.status.eq(0).all()
+    n_exact = 0
+    for n in range(N):
+        r = compare_tree(x[n].double().numpy(), B, n + 11, tree_rows(P, n))
+        n_exact += int(r["exact"])
+        g = tree_rows(P, n)
+        check_mask(g["parent"], g["depth"], g["n_nodes"], n * 64, B + 1,
+                   P.buf.mask_words[n].cpu().numpy(), P.buf.position_ids[n].cpu().numpy())
+    say(f"[sweep] exact trees {n_exact}/{N}")
+    assert n_exact >= 1
