@@ -21,8 +21,8 @@
 //      k-th largest (logit desc, id asc) among the candidates, those k sorted.
 //
 // Tiles: 128 rows x 256 vocabulary columns per 256-thread workgroup, two
-// workgroups per CU, k in steps of 32 through double-buffered LDS (global loads
-// two steps ahead), four waves of 64 x 128 each built
+// workgroups per CU, k in steps of 32 through double-buffered, XOR-swizzled LDS
+// (global loads two steps ahead), four waves of 64 x 128 each built
 // from v_mfma_f32_32x32x16_bf16 (fp32 accumulation).  Each product element is
 // computed from the same operands in the same k order in both tile launches,
 // so the sample and main launches see identical logits.
@@ -37,7 +37,15 @@ namespace mfd {
 namespace {
 
 constexpr int kBM = 128, kBK = 32, kNT = 256;
-constexpr int kLdk = kBK + 8;  // bf16 per LDS row: 80 bytes, conflict-free 16-byte reads
+constexpr int kLdk = kBK;  // bf16 per LDS row: 64 bytes, four 16-byte chunks, XOR-swizzled
+
+// Physical chunk of logical chunk q (16 bytes, k-offset 8q) in LDS row r.  The
+// swizzle f(r) = ((r >> 1) ^ (r >> 3)) & 3 differs over rows of equal parity
+// among 8 consecutive rows and over rows of equal r % 4 among 16, so the
+// 16-byte fragment reads of 8 or 16 consecutive rows at one k-offset, and the
+// staging writes of 2 or 4 consecutive rows' 4 chunks, fall in distinct bank
+// groups whether a pass serves 8 lanes over 32 banks or 16 lanes over 64.
+__device__ __forceinline__ int lds_chunk(int r, int q) { return q ^ (((r >> 1) ^ (r >> 3)) & 3); }
 constexpr int kSampleCols = 8192;  // vocabulary columns in the threshold sample
 constexpr int kSmallM = 256;       // up to this many rows, tiles are 128 columns wide
 
@@ -122,6 +130,7 @@ __global__ void __launch_bounds__(kNT, 2) lmh_tile_kernel(LmhArgs a) {
   // (BN / 64 per thread).  Chunk c is row c / 4, k-offset 8 (c % 4) of the stage.
   // Rows past the matrix read its last row (their results are dropped).
   const int q8 = (tid & 3) * 8, r0 = tid >> 2;
+  const int qs8 = lds_chunk(r0, tid & 3) * 8;  // rows r0 + 64 j share r0's swizzle
   const uint16_t* a0p = a.H + (size_t)min(row0 + r0, a.M - 1) * D + q8;
   const uint16_t* a1p = a.H + (size_t)min(row0 + r0 + 64, a.M - 1) * D + q8;
   const uint16_t* b0p = a.W + (size_t)min(col0 + r0, a.V - 1) * D + q8;
@@ -150,13 +159,13 @@ __global__ void __launch_bounds__(kNT, 2) lmh_tile_kernel(LmhArgs a) {
   } while (0)
 #define LMH_LSTORE(P, buf)                                          \
   do {                                                              \
-    *reinterpret_cast<uint4*>(&sA[buf][r0][q8]) = P##a0;            \
-    *reinterpret_cast<uint4*>(&sA[buf][r0 + 64][q8]) = P##a1;       \
-    *reinterpret_cast<uint4*>(&sB[buf][r0][q8]) = P##b0;            \
-    *reinterpret_cast<uint4*>(&sB[buf][r0 + 64][q8]) = P##b1;       \
+    *reinterpret_cast<uint4*>(&sA[buf][r0][qs8]) = P##a0;            \
+    *reinterpret_cast<uint4*>(&sA[buf][r0 + 64][qs8]) = P##a1;       \
+    *reinterpret_cast<uint4*>(&sB[buf][r0][qs8]) = P##b0;            \
+    *reinterpret_cast<uint4*>(&sB[buf][r0 + 64][qs8]) = P##b1;       \
     if constexpr (TS::NB == 4) {                                    \
-      *reinterpret_cast<uint4*>(&sB[buf][r0 + 128][q8]) = P##b2;    \
-      *reinterpret_cast<uint4*>(&sB[buf][r0 + 192][q8]) = P##b3;    \
+      *reinterpret_cast<uint4*>(&sB[buf][r0 + 128][qs8]) = P##b2;    \
+      *reinterpret_cast<uint4*>(&sB[buf][r0 + 192][qs8]) = P##b3;    \
     }                                                               \
   } while (0)
 
@@ -168,17 +177,19 @@ __global__ void __launch_bounds__(kNT, 2) lmh_tile_kernel(LmhArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  // lane l feeds row (or column) l % 32 of a 32 x 16 operand, k-half l / 32
+  // lane l feeds row (or column) l % 32 of a 32 x 16 operand, k-half l / 32;
+  // every operand row starts at a multiple of 32, so its swizzle is lds_chunk(l % 32, .)
   const int lr = lane & 31, lk = (lane >> 5) * 8;
   const int nS = D / kBK;
 #define LMH_COMPUTE(buf)                                                                          \
   do {                                                                                            \
     _Pragma("unroll") for (int kk = 0; kk < kBK; kk += 16) {                                      \
       bf16x8 af[IM], bfv[4];                                                                      \
+      const int kc = (lds_chunk(lr, ((kk + lk) >> 3))) * 8;                                       \
       _Pragma("unroll") for (int i = 0; i < IM; ++i)                                              \
-        af[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][wm * 32 * IM + i * 32 + lr][kk + lk]);  \
+        af[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][wm * 32 * IM + i * 32 + lr][kc]);       \
       _Pragma("unroll") for (int j = 0; j < 4; ++j)                                               \
-        bfv[j] = *reinterpret_cast<const bf16x8*>(&sB[buf][wn * 128 + j * 32 + lr][kk + lk]);     \
+        bfv[j] = *reinterpret_cast<const bf16x8*>(&sB[buf][wn * 128 + j * 32 + lr][kc]);          \
       _Pragma("unroll") for (int i = 0; i < IM; ++i)                                              \
         _Pragma("unroll") for (int j = 0; j < 4; ++j)                                             \
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0); \
