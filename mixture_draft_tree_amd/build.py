@@ -62,7 +62,26 @@ def build(jobs: int = 8) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB)
+    build_c_smoke()
     return LIB
+
+
+C_SMOKE_SRC = os.path.join(ROOT, "tests", "c", "abi_smoke.c")
+C_SMOKE_BIN = os.path.join(ROOT, "tests", "c", "abi_smoke")
+
+
+def build_c_smoke() -> None:
+    """The plain-C caller of the C ABI used by the tests (host code only, gcc)."""
+    if not os.path.exists(C_SMOKE_SRC) or shutil.which("gcc") is None:
+        return
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cmd = ["gcc", "-std=c11", "-Wall", "-Werror", "-O2", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+           "-I", os.path.join(rocm, "include"), C_SMOKE_SRC, "-L", HERE, "-lmfdtree", "-L", os.path.join(rocm, "lib"),
+           "-lamdhip64", "-Wl,-rpath,$ORIGIN/../../mixture_draft_tree_amd", "-Wl,-rpath," + os.path.join(rocm, "lib"),
+           "-o", C_SMOKE_BIN]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"C smoke build failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
 
 
 def main() -> None:
