@@ -58,7 +58,8 @@ template <int WGM>
 struct TileShape {
   static constexpr int WGN = 4 / WGM, BN = WGN * 128, IM = 4 / WGM, GPT = WGN * 32, NB = BN / 64;
 };
-constexpr int kSelNT = 256;
+constexpr int kThrNT = 256;   // threshold kernel: 2048 sample keys per row
+constexpr int kSelNT = 1024;  // select kernel: thousands of candidates per row
 constexpr int kSelLdsCap = 8192;  // candidates a select workgroup holds in LDS
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -346,19 +347,19 @@ __global__ void __launch_bounds__(kNT, 2) lmh_tile_kernel(LmhArgs a) {
 // Per row: the candidate threshold (k-th largest group maximum, or 0 = take
 // every column when the sample holds fewer than k groups); resets the row's
 // candidate count.
-__global__ void __launch_bounds__(kSelNT) lmh_threshold_kernel(LmhArgs a, int k) {
+__global__ void __launch_bounds__(kThrNT) lmh_threshold_kernel(LmhArgs a, int k) {
   __shared__ uint32_t hist[256];
   __shared__ int sh[2];
-  __shared__ int red[kSelNT / kWave];
+  __shared__ int red[kThrNT / kWave];
   const int row = (int)blockIdx.x;
   const int n = a.S * a.gpt;
   const uint32_t* g = a.samp + (size_t)row * n;
   int cnt = 0;
-  for (int i = threadIdx.x; i < n; i += kSelNT) cnt += g[i] != 0u ? 1 : 0;
-  cnt = block_sum<kSelNT>(cnt, red);
+  for (int i = threadIdx.x; i < n; i += kThrNT) cnt += g[i] != 0u ? 1 : 0;
+  cnt = block_sum<kThrNT>(cnt, red);
   uint32_t thr = 0;
   if (cnt >= k) {
-    thr = (uint32_t)block_kth_largest<kSelNT, 32>(
+    thr = (uint32_t)block_kth_largest<kThrNT, 32>(
         n, k,
         [&](int i, uint64_t* key) {
           *key = g[i];
@@ -589,11 +590,11 @@ hipError_t launch_lmhead_topk(const void* hidden, const void* weight, int M, int
   const long long gs = (ns + 7) / 8 * 8, gm = (nm + 7) / 8 * 8;
   if (wsl.small) {
     hipLaunchKernelGGL((lmh_tile_kernel<true, 4>), dim3((unsigned)gs), dim3(kNT), 0, stream, a);
-    hipLaunchKernelGGL(lmh_threshold_kernel, dim3(M), dim3(kSelNT), 0, stream, a, k);
+    hipLaunchKernelGGL(lmh_threshold_kernel, dim3(M), dim3(kThrNT), 0, stream, a, k);
     hipLaunchKernelGGL((lmh_tile_kernel<false, 4>), dim3((unsigned)gm), dim3(kNT), 0, stream, a);
   } else {
     hipLaunchKernelGGL((lmh_tile_kernel<true, 2>), dim3((unsigned)gs), dim3(kNT), 0, stream, a);
-    hipLaunchKernelGGL(lmh_threshold_kernel, dim3(M), dim3(kSelNT), 0, stream, a, k);
+    hipLaunchKernelGGL(lmh_threshold_kernel, dim3(M), dim3(kThrNT), 0, stream, a, k);
     hipLaunchKernelGGL((lmh_tile_kernel<false, 2>), dim3((unsigned)gm), dim3(kNT), 0, stream, a);
   }
   const size_t lds = (size_t)(kSelLdsCap + next_pow2(k)) * sizeof(uint64_t);
