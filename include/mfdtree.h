@@ -277,6 +277,24 @@ mfd_status mfd_lmhead_logsoftmax_topk(const void* hidden, const void* weight, in
                                       int32_t* status, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * The fused call over a reduced drafting vocabulary (project page, "In a
+ * serving engine": drafting over the target's 64K most frequent tokens,
+ * verification over the full vocabulary).  `weight` holds the LM-head rows
+ * of the V drafting tokens only, in increasing order of their full ids
+ * vocab_map[0..V); each listed token is reported by its full id, and equal
+ * logits break ties by full id.  The workspace is that of
+ * mfd_lmhead_logsoftmax_topk with this V.
+ *
+ *   vocab_map device [V] int32, strictly increasing, each in [0, V_full).
+ *   V_full    size of the full vocabulary, V <= V_full < 2^20.
+ *   Other arguments as for mfd_lmhead_logsoftmax_topk.
+ */
+mfd_status mfd_lmhead_logsoftmax_topk_mapped(const void* hidden, const void* weight, const int32_t* vocab_map,
+                                             int V_full, int N, int K, int L, int D, int V, int k, double* lse,
+                                             int32_t* topk_id, float* topk_raw, float* topk_logp, int32_t* status,
+                                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Tree-verification inputs (model card summary: the target checks the whole
  * tree in one pass with standard tree verification).  Row i of the mask has
  * bit j set iff node j is node i or one of its ancestors (the root included).

@@ -78,6 +78,7 @@ struct LmhArgs {
   int* cand_count;      // [M]
   int C;
   int32_t* status;      // [N] or null
+  const int32_t* vocab_map;  // [V] full-vocabulary id of column v (increasing), or null
 };
 
 __device__ __forceinline__ uint64_t cand_composite(uint32_t key, uint32_t col) {
@@ -521,7 +522,8 @@ __global__ void __launch_bounds__(kSelNT) lmh_select_kernel(LmhArgs a, int k, do
     const uint64_t c = sortb[P - 1 - j];
     const uint32_t key = (uint32_t)(c >> 32);
     const float raw = __uint_as_float(f32_from_key(key));
-    oid[j] = (int32_t)(0xFFFFFFFFu - (uint32_t)c);
+    const int32_t col = (int32_t)(0xFFFFFFFFu - (uint32_t)c);
+    oid[j] = a.vocab_map ? a.vocab_map[col] : col;
     oraw[j] = raw;
     if (olp) olp[j] = (float)((double)raw - l);
   }
@@ -562,9 +564,9 @@ LmhWorkspace lmhead_workspace(long long M, int V, int k) {
   return w;
 }
 
-hipError_t launch_lmhead_topk(const void* hidden, const void* weight, int M, int rows_per_tree, int D, int V, int k,
-                              double* lse, int32_t* topk_id, float* topk_raw, float* topk_logp, int32_t* status,
-                              void* ws, hipStream_t stream) {
+hipError_t launch_lmhead_topk(const void* hidden, const void* weight, const int32_t* vocab_map, int M,
+                              int rows_per_tree, int D, int V, int k, double* lse, int32_t* topk_id, float* topk_raw,
+                              float* topk_logp, int32_t* status, void* ws, hipStream_t stream) {
   const LmhWorkspace wsl = lmhead_workspace(M, V, k);
   char* base = static_cast<char*>(ws);
   LmhArgs a;
@@ -585,6 +587,7 @@ hipError_t launch_lmhead_topk(const void* hidden, const void* weight, int M, int
   a.cand = reinterpret_cast<uint64_t*>(base + wsl.off_cand);
   a.C = wsl.C;
   a.status = status;
+  a.vocab_map = vocab_map;
   const int nM = (M + kBM - 1) / kBM;
   const long long ns = (long long)nM * a.S, nm = (long long)nM * a.T;
   const long long gs = (ns + 7) / 8 * 8, gm = (nm + 7) / 8 * 8;

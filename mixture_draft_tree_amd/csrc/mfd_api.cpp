@@ -155,9 +155,10 @@ mfd_status mfd_logsoftmax_topk_modes(const void* logits, mfd_dtype dtype, int N,
                               topk_id, topk_raw, topk_logp, status, stream);
 }
 
-mfd_status mfd_lmhead_logsoftmax_topk(const void* hidden, const void* weight, int N, int K, int L, int D, int V, int k,
-                                      double* lse, int32_t* topk_id, float* topk_raw, float* topk_logp,
-                                      int32_t* status, void* ws, size_t ws_bytes, hipStream_t stream) {
+static mfd_status lmhead_impl(const char* call, const void* hidden, const void* weight, const int32_t* vocab_map,
+                              int N, int K, int L, int D, int V, int k, double* lse, int32_t* topk_id,
+                              float* topk_raw, float* topk_logp, int32_t* status, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
   mfd_status s = check_dims(N, K, L, V);
   if (s != MFD_OK) return s;
   if (D < 64 || D > kMaxLmhD || D % 64 != 0)
@@ -179,9 +180,27 @@ mfd_status mfd_lmhead_logsoftmax_topk(const void* hidden, const void* weight, in
   if (ws == nullptr || ws_bytes < need)
     return fail(MFD_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws == nullptr ? (size_t)0 : ws_bytes);
   if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(MFD_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  return from_hip(mfd::launch_lmhead_topk(hidden, weight, (int)M, K * L, D, V, k, lse, topk_id, topk_raw, topk_logp,
-                                          status, ws, stream),
-                  "mfd_lmhead_logsoftmax_topk launch");
+  return from_hip(mfd::launch_lmhead_topk(hidden, weight, vocab_map, (int)M, K * L, D, V, k, lse, topk_id, topk_raw,
+                                          topk_logp, status, ws, stream),
+                  call);
+}
+
+mfd_status mfd_lmhead_logsoftmax_topk(const void* hidden, const void* weight, int N, int K, int L, int D, int V, int k,
+                                      double* lse, int32_t* topk_id, float* topk_raw, float* topk_logp,
+                                      int32_t* status, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return lmhead_impl("mfd_lmhead_logsoftmax_topk launch", hidden, weight, nullptr, N, K, L, D, V, k, lse, topk_id,
+                     topk_raw, topk_logp, status, ws, ws_bytes, stream);
+}
+
+mfd_status mfd_lmhead_logsoftmax_topk_mapped(const void* hidden, const void* weight, const int32_t* vocab_map,
+                                             int V_full, int N, int K, int L, int D, int V, int k, double* lse,
+                                             int32_t* topk_id, float* topk_raw, float* topk_logp, int32_t* status,
+                                             void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (V_full < V || V_full > kMaxV)
+    return fail(MFD_ERR_INVALID_ARG, "V_full must be in [V, %d] (got %d, V = %d)", kMaxV, V_full, V);
+  if (N > 0) REQUIRE_PTR(vocab_map);
+  return lmhead_impl("mfd_lmhead_logsoftmax_topk_mapped launch", hidden, weight, vocab_map, N, K, L, D, V, k, lse,
+                     topk_id, topk_raw, topk_logp, status, ws, ws_bytes, stream);
 }
 
 static mfd_status mixture_threshold_impl(const char* call, const int32_t* topk_id, const float* topk_raw,

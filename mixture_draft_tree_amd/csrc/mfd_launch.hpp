@@ -75,8 +75,9 @@ struct LmhWorkspace {
   size_t off_samp, off_thr, off_count, off_part, off_cand, bytes;
 };
 LmhWorkspace lmhead_workspace(long long M, int V, int k);
-hipError_t launch_lmhead_topk(const void* hidden, const void* weight, int M, int rows_per_tree, int D, int V, int k,
-                              double* lse, int32_t* topk_id, float* topk_raw, float* topk_logp, int32_t* status,
-                              void* ws, hipStream_t stream);
+// vocab_map (device [V] or null): topk_id reports vocab_map[column]
+hipError_t launch_lmhead_topk(const void* hidden, const void* weight, const int32_t* vocab_map, int M,
+                              int rows_per_tree, int D, int V, int k, double* lse, int32_t* topk_id, float* topk_raw,
+                              float* topk_logp, int32_t* status, void* ws, hipStream_t stream);
 
 }  // namespace mfd

@@ -32,7 +32,7 @@ EXPORTED = ["mfd_last_error", "mfd_version", "mfd_workspace_size", "mfd_logsoftm
             "mfd_logsoftmax_topk_mapped", "mfd_mixture_threshold", "mfd_tree_build", "mfd_tree_mask",
             "mfd_verify_walk", "mfd_covered_mass", "mfd_chimera_count", "mfd_logsoftmax_topk_modes",
             "mfd_mixture_threshold_modes", "mfd_tree_build_modes", "mfd_stream_read",
-            "mfd_lmhead_logsoftmax_topk"]
+            "mfd_lmhead_logsoftmax_topk", "mfd_lmhead_logsoftmax_topk_mapped"]
 
 _p = ctypes.c_void_p
 _i = ctypes.c_int
@@ -62,6 +62,9 @@ _lib.mfd_tree_build_modes.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i
                                       _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]
 _lib.mfd_lmhead_logsoftmax_topk.restype = _i
 _lib.mfd_lmhead_logsoftmax_topk.argtypes = [_p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p]
+_lib.mfd_lmhead_logsoftmax_topk_mapped.restype = _i
+_lib.mfd_lmhead_logsoftmax_topk_mapped.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p,
+                                                   _sz, _p]
 _lib.mfd_stream_read.restype = _i
 _lib.mfd_stream_read.argtypes = [_p, _sz, _p, _p]
 _lib.mfd_tree_mask.restype = _i
@@ -196,9 +199,11 @@ def lmhead_workspace(N: int, K: int, L: int, V: int, k: int, device="cuda") -> t
 
 
 def mfd_lmhead_logsoftmax_topk(hidden, weight, k, lse, topk_id, topk_raw, topk_logp=None, status=None, ws=None,
-                               stream=None):
+                               stream=None, vocab_map=None, V_full=None):
     """hidden [N, K, L, D] bf16, weight [V, D] bf16 -> lse [N, K, L] fp64, topk_* [N, K, L, k]
-    over the logits hidden . weight^T (never stored)."""
+    over the logits hidden . weight^T (never stored).  With vocab_map ([V] int32,
+    increasing ids in a vocabulary of V_full tokens; weight holds those tokens'
+    rows) topk_id holds full-vocabulary ids."""
     if hidden.dim() != 4 or not hidden.is_contiguous() or hidden.device.type != "cuda":
         raise ValueError("hidden must be a contiguous [N, K, L, D] GPU tensor")
     if hidden.dtype != torch.bfloat16:
@@ -218,6 +223,13 @@ def mfd_lmhead_logsoftmax_topk(hidden, weight, k, lse, topk_id, topk_raw, topk_l
     ptr = ws.data_ptr()
     off = (-ptr) % 256
     nbytes = ws.numel() * ws.element_size() - off
+    if vocab_map is not None:
+        _want(vocab_map, "vocab_map", torch.int32, (V,))
+        _check(_lib.mfd_lmhead_logsoftmax_topk_mapped(
+            _ptr(hidden), _ptr(weight), _ptr(vocab_map), V if V_full is None else V_full, N, K, L, D, V, k,
+            _ptr(lse), _ptr(topk_id), _ptr(topk_raw), _ptr(topk_logp), _ptr(status), ctypes.c_void_p(ptr + off),
+            max(nbytes, 0), _stream_handle(stream)), "mfd_lmhead_logsoftmax_topk_mapped")
+        return
     _check(_lib.mfd_lmhead_logsoftmax_topk(_ptr(hidden), _ptr(weight), N, K, L, D, V, k, _ptr(lse), _ptr(topk_id),
                                            _ptr(topk_raw), _ptr(topk_logp), _ptr(status),
                                            ctypes.c_void_p(ptr + off), max(nbytes, 0), _stream_handle(stream)),

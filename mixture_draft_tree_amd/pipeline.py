@@ -105,14 +105,15 @@ class MixtureTreePath:
                                   stream=stream)
 
     def lmhead_logsoftmax_topk(self, hidden, weight, stream=None):
-        """Call 1 fused with the LM head: hidden [N, K, L, D] bf16, weight [V, D] bf16."""
+        """Call 1 fused with the LM head: hidden [N, K, L, D] bf16, weight [V, D] bf16 (the
+        drafting tokens' rows when the path has a vocabulary map)."""
         b = self.buf
-        if self.vocab_map is not None or self.modes is not None:
-            raise ValueError("the fused LM-head call covers full-vocabulary trees of K modes")
+        if self.modes is not None:
+            raise ValueError("the fused LM-head call covers trees of all K modes")
         if getattr(self, "_lmh_ws", None) is None:
             self._lmh_ws = M.lmhead_workspace(self.N, self.K, self.L, self.V, self.k, hidden.device)
         M.mfd_lmhead_logsoftmax_topk(hidden, weight, self.k, b.lse, b.topk_id, b.topk_raw, b.topk_logp, b.status,
-                                     ws=self._lmh_ws, stream=stream)
+                                     ws=self._lmh_ws, stream=stream, vocab_map=self.vocab_map, V_full=self.V_full)
 
     def build_from_hidden(self, hidden, weight, anchor, pos_base, stream=None):
         """Calls 1-4 with the fused LM head: hidden states -> tree, mask, position ids."""

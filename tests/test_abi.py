@@ -238,3 +238,14 @@ def test_lmhead_workspace_size():
     assert M.workspace_size(M.MFD_OP_LMHEAD_TOPK, 1, 8, 15, 151936, 1024) > one
     with pytest.raises(M.MfdError):
         M.workspace_size(M.MFD_OP_LMHEAD_TOPK, 1, 8, 15, 151936, 4096)
+
+
+def test_lmhead_mapped_rejects_before_launch():
+    f = M._lib.mfd_lmhead_logsoftmax_topk_mapped
+    args = lambda vm=FAKE, V_full=200000, V=65536, N=1: (FAKE, FAKE, vm, V_full, N, 8, 15, 2560, V, 256, FAKE, FAKE, FAKE,
+                                                       None, None, ctypes.c_void_p(0x100000), 1000, None)
+    assert f(*args(V_full=1000)) == M.MFD_ERR_INVALID_ARG and "V_full" in M.last_error()
+    assert f(*args(V_full=1 << 20)) == M.MFD_ERR_INVALID_ARG
+    assert f(*args(vm=None)) == M.MFD_ERR_INVALID_ARG and "vocab_map" in M.last_error()
+    assert f(*args()) == M.MFD_ERR_WORKSPACE          # 1000 bytes of workspace: rejected, nothing launched
+    assert f(*args(vm=None, N=0)) == M.MFD_OK

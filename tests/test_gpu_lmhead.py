@@ -213,3 +213,29 @@ def test_lmhead_repeat_calls_and_workspace_reuse():
         assert np.max(np.abs(lse.cpu().numpy() - o_lse)) < LSE_TOL
         outs.append(ids.cpu().numpy())
     assert np.array_equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("V_full,V_draft,k", [(40000, 9000, 256), (5000, 300, 32)])
+def test_lmhead_mapped_subset_bit_exact(V_full, V_draft, k):
+    # Drafting over a sorted subset of the vocabulary: the head's rows of the
+    # subset, ids reported through the map; equal to the oracle's ranking of
+    # the subset logits, relabelled (grid inputs, exact).
+    _say(f"lmhead mapped subset V_full={V_full} V_draft={V_draft} k={k}")
+    h, w_full = _grid_inputs(2, 8, 15, 128, V_full, seed=V_full + V_draft)
+    g = torch.Generator().manual_seed(77)
+    vmap = torch.sort(torch.randperm(V_full, generator=g)[:V_draft]).values.to(torch.int32)
+    w = w_full[vmap.long()].contiguous()
+    N, K, L, D = h.shape
+    H, W, VM = h.cuda(), w.cuda(), vmap.cuda()
+    lse = torch.empty((N, K, L), dtype=torch.float64, device="cuda")
+    ids = torch.empty((N, K, L, k), dtype=torch.int32, device="cuda")
+    raw = torch.empty((N, K, L, k), dtype=torch.float32, device="cuda")
+    st = torch.zeros((N,), dtype=torch.int32, device="cuda")
+    M.mfd_lmhead_logsoftmax_topk(H, W, k, lse, ids, raw, None, st, vocab_map=VM, V_full=V_full)
+    torch.cuda.synchronize()
+    assert int(st.abs().sum()) == 0
+    x64 = O.lmhead_logits(h.float().numpy(), w.float().numpy())
+    o_lse, o_ids = oracle_rows(x64, k)
+    assert np.array_equal(ids.cpu().numpy(), vmap.numpy()[o_ids])
+    assert np.array_equal(raw.cpu().numpy().astype(np.float64), np.take_along_axis(x64, o_ids.astype(np.int64), -1))
+    assert np.max(np.abs(lse.cpu().numpy() - o_lse)) < LSE_TOL
