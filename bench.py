@@ -129,6 +129,10 @@ def fused_lmhead(steps: int, stream) -> dict:
             return e0.elapsed_time(e1) / reps
 
         fused_ms = timed(lambda: M.mfd_lmhead_logsoftmax_topk(H, W, k, lse, ids, raw, None, st, ws=ws, stream=stream))
+        pk = M.mfd_lmhead_pack_weight(W, stream=stream)
+        packed_ms = timed(lambda: M.mfd_lmhead_logsoftmax_topk(H, pk, k, lse, ids, raw, None, st, ws=ws,
+                                                               stream=stream))
+        del pk
         flops = 2.0 * N * K * L * V * D
         ok = int(st.abs().sum().item()) == 0
         logits = e((N * K * L, V), torch.bfloat16)
@@ -155,6 +159,7 @@ def fused_lmhead(steps: int, stream) -> dict:
             "unfused_matmul_ms": mm_ms, "unfused_logsoftmax_topk_ms": lsm_ms,
             "unfused_total_ms": mm_ms + lsm_ms, "fused_over_unfused": fused_ms / (mm_ms + lsm_ms),
             "reduced_vocab_fused_ms": sub_ms, "reduced_vocab_tokens": 65536,
+            "packed_head_fused_ms": packed_ms,
         }
         del b, H, W, logits, lg, ws
         torch.cuda.empty_cache()

@@ -241,6 +241,25 @@ mfd_status mfd_tree_build_modes(const int32_t* topk_id, const float* topk_raw, c
                                 int32_t* best_mode, int32_t* n_nodes, int32_t* status,
                                 void* ws, size_t ws_bytes, hipStream_t stream);
 
+typedef enum mfd_head_layout { MFD_HEAD_ROWS = 0, MFD_HEAD_PACKED = 1 } mfd_head_layout;
+
+/*
+ * Packed LM head for the fused calls (a one-time re-layout of the weights,
+ * for callers who stream the same head every round).  Rows are padded with
+ * zeros to a multiple of 256 and cut into blocks of 64 rows x 32 columns;
+ * block (vb, s) (rows 64 vb.., columns 32 s..) is stored contiguously at
+ * element ((vb * D / 32) + s) * 2048, row-major inside the block.
+ *
+ *   mfd_lmhead_packed_size: bytes of the packed head, ceil(V / 256) * 256 * D * 2.
+ *   weight  device [V, D] bf16, 16-byte aligned; packed: device, 16-byte
+ *           aligned, at least mfd_lmhead_packed_size bytes, caller-owned.
+ *   Errors: MFD_ERR_INVALID_ARG for V or D outside the fused call's limits,
+ *           NULL or misaligned pointers, or a small packed buffer.
+ */
+mfd_status mfd_lmhead_packed_size(int V, int D, size_t* bytes);
+mfd_status mfd_lmhead_pack_weight(const void* weight, int V, int D, void* packed, size_t packed_bytes,
+                                  hipStream_t stream);
+
 /*
  * Fused LM head + per-(mode, position) log-softmax and top-k.  The drafter
  * uses its target's LM head at run time (model card "MFD drafter for
@@ -253,7 +272,11 @@ mfd_status mfd_tree_build_modes(const int32_t* topk_id, const float* topk_raw, c
  *
  *   hidden    device [N, K, L, D] bf16: the drafter's final hidden states, row
  *             r = (n, k, i); 16-byte aligned.
- *   weight    device [V, D] bf16: the LM head, one row per token; 16-byte aligned.
+ *   weight    device bf16, 16-byte aligned: the LM head.  layout MFD_HEAD_ROWS:
+ *             [V, D], one row per token.  layout MFD_HEAD_PACKED: the same head
+ *             re-laid out once by mfd_lmhead_pack_weight, so every 64-row x
+ *             32-column block a tile reads per step is one contiguous 4 KB
+ *             run.  Results are identical for both layouts.
  *   D         hidden width, a multiple of 64 in [64, 16384]; N*K*L*D and V*D
  *             must be below 2^31.
  *   lse, topk_id, topk_raw, topk_logp: as for mfd_logsoftmax_topk; topk_raw
@@ -272,9 +295,10 @@ mfd_status mfd_tree_build_modes(const int32_t* topk_id, const float* topk_raw, c
  * above, k outside [1, min(V, 2048)], NULL or misaligned pointers;
  * MFD_ERR_WORKSPACE for a missing, small or misaligned workspace.
  */
-mfd_status mfd_lmhead_logsoftmax_topk(const void* hidden, const void* weight, int N, int K, int L, int D, int V,
-                                      int k, double* lse, int32_t* topk_id, float* topk_raw, float* topk_logp,
-                                      int32_t* status, void* ws, size_t ws_bytes, hipStream_t stream);
+mfd_status mfd_lmhead_logsoftmax_topk(const void* hidden, const void* weight, mfd_head_layout layout, int N,
+                                      int K, int L, int D, int V, int k, double* lse, int32_t* topk_id,
+                                      float* topk_raw, float* topk_logp, int32_t* status, void* ws,
+                                      size_t ws_bytes, hipStream_t stream);
 
 /*
  * The fused call over a reduced drafting vocabulary (project page, "In a
@@ -289,10 +313,11 @@ mfd_status mfd_lmhead_logsoftmax_topk(const void* hidden, const void* weight, in
  *   V_full    size of the full vocabulary, V <= V_full < 2^20.
  *   Other arguments as for mfd_lmhead_logsoftmax_topk.
  */
-mfd_status mfd_lmhead_logsoftmax_topk_mapped(const void* hidden, const void* weight, const int32_t* vocab_map,
-                                             int V_full, int N, int K, int L, int D, int V, int k, double* lse,
-                                             int32_t* topk_id, float* topk_raw, float* topk_logp, int32_t* status,
-                                             void* ws, size_t ws_bytes, hipStream_t stream);
+mfd_status mfd_lmhead_logsoftmax_topk_mapped(const void* hidden, const void* weight, mfd_head_layout layout,
+                                             const int32_t* vocab_map, int V_full, int N, int K, int L, int D, int V,
+                                             int k, double* lse, int32_t* topk_id, float* topk_raw,
+                                             float* topk_logp, int32_t* status, void* ws, size_t ws_bytes,
+                                             hipStream_t stream);
 
 /*
  * Tree-verification inputs (model card summary: the target checks the whole

@@ -79,6 +79,7 @@ struct LmhArgs {
   int C;
   int32_t* status;      // [N] or null
   const int32_t* vocab_map;  // [V] full-vocabulary id of column v (increasing), or null
+  int packed;                // W in the packed layout of lmh_pack_kernel (else row-major [V, D])
 };
 
 __device__ __forceinline__ uint64_t cand_composite(uint32_t key, uint32_t col) {
@@ -135,10 +136,19 @@ __global__ void __launch_bounds__(kNT, 2) lmh_tile_kernel(LmhArgs a) {
   const int qs8 = lds_chunk(r0, tid & 3) * 8;  // rows r0 + 64 j share r0's swizzle
   const uint16_t* a0p = a.H + (size_t)min(row0 + r0, a.M - 1) * D + q8;
   const uint16_t* a1p = a.H + (size_t)min(row0 + r0 + 64, a.M - 1) * D + q8;
-  const uint16_t* b0p = a.W + (size_t)min(col0 + r0, a.V - 1) * D + q8;
-  const uint16_t* b1p = a.W + (size_t)min(col0 + r0 + 64, a.V - 1) * D + q8;
-  const uint16_t* b2p = a.W + (size_t)min(col0 + r0 + 128, a.V - 1) * D + q8;
-  const uint16_t* b3p = a.W + (size_t)min(col0 + r0 + 192, a.V - 1) * D + q8;
+  // Head rows: row-major (rows past V read row V - 1), or packed: the 64 rows x
+  // 32 k of block (col0 / 64 + j, step s) are one contiguous 4 KB run at
+  // ((col0 / 64 + j) * nS + s) * 2048 elements, thread t's chunk at 8 t.
+  const int nSt = D / kBK;
+  const size_t bmul = a.packed ? 64 : 1;  // elements per unit of k0
+  const uint16_t* b0p = a.packed ? a.W + ((size_t)(col0 / 64 + 0) * nSt) * 2048 + tid * 8
+                                 : a.W + (size_t)min(col0 + r0, a.V - 1) * D + q8;
+  const uint16_t* b1p = a.packed ? a.W + ((size_t)(col0 / 64 + 1) * nSt) * 2048 + tid * 8
+                                 : a.W + (size_t)min(col0 + r0 + 64, a.V - 1) * D + q8;
+  const uint16_t* b2p = a.packed ? a.W + ((size_t)(col0 / 64 + 2) * nSt) * 2048 + tid * 8
+                                 : a.W + (size_t)min(col0 + r0 + 128, a.V - 1) * D + q8;
+  const uint16_t* b3p = a.packed ? a.W + ((size_t)(col0 / 64 + 3) * nSt) * 2048 + tid * 8
+                                 : a.W + (size_t)min(col0 + r0 + 192, a.V - 1) * D + q8;
   // Register staging, NSET stages deep: stage j's chunks sit in register set
   // j % NSET from their global load (issued at step j - NSET) until they are
   // copied to LDS at the end of step j - 1.  Narrow tiles have the registers
@@ -152,11 +162,11 @@ __global__ void __launch_bounds__(kNT, 2) lmh_tile_kernel(LmhArgs a) {
   do {                                                         \
     P##a0 = *reinterpret_cast<const uint4*>(a0p + (k0));       \
     P##a1 = *reinterpret_cast<const uint4*>(a1p + (k0));       \
-    P##b0 = *reinterpret_cast<const uint4*>(b0p + (k0));       \
-    P##b1 = *reinterpret_cast<const uint4*>(b1p + (k0));       \
+    P##b0 = *reinterpret_cast<const uint4*>(b0p + (k0) * bmul);       \
+    P##b1 = *reinterpret_cast<const uint4*>(b1p + (k0) * bmul);       \
     if constexpr (TS::NB == 4) {                               \
-      P##b2 = *reinterpret_cast<const uint4*>(b2p + (k0));     \
-      P##b3 = *reinterpret_cast<const uint4*>(b3p + (k0));     \
+      P##b2 = *reinterpret_cast<const uint4*>(b2p + (k0) * bmul);     \
+      P##b3 = *reinterpret_cast<const uint4*>(b3p + (k0) * bmul);     \
     }                                                          \
   } while (0)
 #define LMH_LSTORE(P, buf)                                          \
@@ -529,7 +539,37 @@ __global__ void __launch_bounds__(kSelNT) lmh_select_kernel(LmhArgs a, int k, do
   }
 }
 
+// Packed head: rows padded to a multiple of 256 (zeros), cut into blocks of 64
+// rows x 32 k, block (vb, s) stored contiguously at ((vb * nS) + s) * 2048
+// elements, row-major inside (row r, k-chunk q of 8 at (4 r + q) * 8).  One
+// thread copies one 16-byte chunk.
+__global__ void __launch_bounds__(256) lmh_pack_kernel(const uint16_t* __restrict__ W, int V, int D,
+                                                      uint16_t* __restrict__ Wp, long long nchunks) {
+  const long long c = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (c >= nchunks) return;
+  const int nS = D / kBK;
+  const long long blk = c >> 8;
+  const int t = (int)(c & 255);
+  const long long vb = blk / nS;
+  const int s = (int)(blk - vb * nS);
+  const long long row = vb * 64 + (t >> 2);
+  const int k = s * kBK + (t & 3) * 8;
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (row < V) v = *reinterpret_cast<const uint4*>(W + row * (long long)D + k);
+  *reinterpret_cast<uint4*>(Wp + c * 8) = v;
+}
+
 }  // namespace
+
+size_t lmhead_packed_bytes(int V, int D) { return (size_t)((V + 255) / 256) * 256 * (size_t)D * 2; }
+
+hipError_t launch_lmhead_pack(const void* weight, int V, int D, void* packed, hipStream_t stream) {
+  const long long nchunks = (long long)((V + 255) / 256) * 256 * D / 8;
+  const long long blocks = (nchunks + 255) / 256;
+  hipLaunchKernelGGL(lmh_pack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(weight), V, D, static_cast<uint16_t*>(packed), nchunks);
+  return hipGetLastError();
+}
 
 LmhWorkspace lmhead_workspace(long long M, int V, int k) {
   LmhWorkspace w{};
@@ -564,7 +604,7 @@ LmhWorkspace lmhead_workspace(long long M, int V, int k) {
   return w;
 }
 
-hipError_t launch_lmhead_topk(const void* hidden, const void* weight, const int32_t* vocab_map, int M,
+hipError_t launch_lmhead_topk(const void* hidden, const void* weight, bool packed, const int32_t* vocab_map, int M,
                               int rows_per_tree, int D, int V, int k, double* lse, int32_t* topk_id, float* topk_raw,
                               float* topk_logp, int32_t* status, void* ws, hipStream_t stream) {
   const LmhWorkspace wsl = lmhead_workspace(M, V, k);
@@ -588,6 +628,7 @@ hipError_t launch_lmhead_topk(const void* hidden, const void* weight, const int3
   a.C = wsl.C;
   a.status = status;
   a.vocab_map = vocab_map;
+  a.packed = packed ? 1 : 0;
   const int nM = (M + kBM - 1) / kBM;
   const long long ns = (long long)nM * a.S, nm = (long long)nM * a.T;
   const long long gs = (ns + 7) / 8 * 8, gm = (nm + 7) / 8 * 8;

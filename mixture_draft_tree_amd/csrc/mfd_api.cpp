@@ -155,18 +155,50 @@ mfd_status mfd_logsoftmax_topk_modes(const void* logits, mfd_dtype dtype, int N,
                               topk_id, topk_raw, topk_logp, status, stream);
 }
 
-static mfd_status lmhead_impl(const char* call, const void* hidden, const void* weight, const int32_t* vocab_map,
-                              int N, int K, int L, int D, int V, int k, double* lse, int32_t* topk_id,
-                              float* topk_raw, float* topk_logp, int32_t* status, void* ws, size_t ws_bytes,
-                              hipStream_t stream) {
+static mfd_status check_head(int V, int D) {
+  if (V < 1 || V > kMaxV) return fail(MFD_ERR_INVALID_ARG, "V must be in [1, %d] (got %d)", kMaxV, V);
+  if (D < 64 || D > kMaxLmhD || D % 64 != 0)
+    return fail(MFD_ERR_INVALID_ARG, "D must be a multiple of 64 in [64, %d] (got %d)", kMaxLmhD, D);
+  if ((long long)((V + 255) / 256) * 256 * D > 0x7FFFFFFFLL)
+    return fail(MFD_ERR_INVALID_ARG, "V*D must be < 2^31 (got %lld)", (long long)V * D);
+  return MFD_OK;
+}
+
+mfd_status mfd_lmhead_packed_size(int V, int D, size_t* bytes) {
+  REQUIRE_PTR(bytes);
+  mfd_status s = check_head(V, D);
+  if (s != MFD_OK) return s;
+  *bytes = mfd::lmhead_packed_bytes(V, D);
+  return ok();
+}
+
+mfd_status mfd_lmhead_pack_weight(const void* weight, int V, int D, void* packed, size_t packed_bytes,
+                                  hipStream_t stream) {
+  mfd_status s = check_head(V, D);
+  if (s != MFD_OK) return s;
+  REQUIRE_PTR(weight);
+  REQUIRE_PTR(packed);
+  if (reinterpret_cast<uintptr_t>(weight) % 16 || reinterpret_cast<uintptr_t>(packed) % 16)
+    return fail(MFD_ERR_INVALID_ARG, "weight and packed must be 16-byte aligned");
+  const size_t need = mfd::lmhead_packed_bytes(V, D);
+  if (packed_bytes < need) return fail(MFD_ERR_INVALID_ARG, "packed needs %zu bytes (got %zu)", need, packed_bytes);
+  return from_hip(mfd::launch_lmhead_pack(weight, V, D, packed, stream), "mfd_lmhead_pack_weight launch");
+}
+
+static mfd_status lmhead_impl(const char* call, const void* hidden, const void* weight, mfd_head_layout layout,
+                              const int32_t* vocab_map, int N, int K, int L, int D, int V, int k, double* lse,
+                              int32_t* topk_id, float* topk_raw, float* topk_logp, int32_t* status, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
   mfd_status s = check_dims(N, K, L, V);
   if (s != MFD_OK) return s;
+  if (layout != MFD_HEAD_ROWS && layout != MFD_HEAD_PACKED)
+    return fail(MFD_ERR_INVALID_ARG, "layout must be MFD_HEAD_ROWS or MFD_HEAD_PACKED (got %d)", (int)layout);
   if (D < 64 || D > kMaxLmhD || D % 64 != 0)
     return fail(MFD_ERR_INVALID_ARG, "D must be a multiple of 64 in [64, %d] (got %d)", kMaxLmhD, D);
   if (k < 1 || k > kMaxTopk || k > V) return fail(MFD_ERR_INVALID_ARG, "k must be in [1, min(V, %d)] (got %d)", kMaxTopk, k);
   const long long M = (long long)N * K * L;
   if (M * D > 0x7FFFFFFFLL) return fail(MFD_ERR_INVALID_ARG, "N*K*L*D must be < 2^31 (got %lld)", M * D);
-  if ((long long)V * D > 0x7FFFFFFFLL)
+  if ((long long)((V + 255) / 256) * 256 * D > 0x7FFFFFFFLL)
     return fail(MFD_ERR_INVALID_ARG, "V*D must be < 2^31 (got %lld)", (long long)V * D);
   if (N == 0) return ok();
   REQUIRE_PTR(hidden);
@@ -180,27 +212,29 @@ static mfd_status lmhead_impl(const char* call, const void* hidden, const void* 
   if (ws == nullptr || ws_bytes < need)
     return fail(MFD_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws == nullptr ? (size_t)0 : ws_bytes);
   if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(MFD_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  return from_hip(mfd::launch_lmhead_topk(hidden, weight, vocab_map, (int)M, K * L, D, V, k, lse, topk_id, topk_raw,
-                                          topk_logp, status, ws, stream),
+  return from_hip(mfd::launch_lmhead_topk(hidden, weight, layout == MFD_HEAD_PACKED, vocab_map, (int)M, K * L, D, V,
+                                          k, lse, topk_id, topk_raw, topk_logp, status, ws, stream),
                   call);
 }
 
-mfd_status mfd_lmhead_logsoftmax_topk(const void* hidden, const void* weight, int N, int K, int L, int D, int V, int k,
-                                      double* lse, int32_t* topk_id, float* topk_raw, float* topk_logp,
-                                      int32_t* status, void* ws, size_t ws_bytes, hipStream_t stream) {
-  return lmhead_impl("mfd_lmhead_logsoftmax_topk launch", hidden, weight, nullptr, N, K, L, D, V, k, lse, topk_id,
-                     topk_raw, topk_logp, status, ws, ws_bytes, stream);
+mfd_status mfd_lmhead_logsoftmax_topk(const void* hidden, const void* weight, mfd_head_layout layout, int N, int K,
+                                      int L, int D, int V, int k, double* lse, int32_t* topk_id, float* topk_raw,
+                                      float* topk_logp, int32_t* status, void* ws, size_t ws_bytes,
+                                      hipStream_t stream) {
+  return lmhead_impl("mfd_lmhead_logsoftmax_topk launch", hidden, weight, layout, nullptr, N, K, L, D, V, k, lse,
+                     topk_id, topk_raw, topk_logp, status, ws, ws_bytes, stream);
 }
 
-mfd_status mfd_lmhead_logsoftmax_topk_mapped(const void* hidden, const void* weight, const int32_t* vocab_map,
-                                             int V_full, int N, int K, int L, int D, int V, int k, double* lse,
-                                             int32_t* topk_id, float* topk_raw, float* topk_logp, int32_t* status,
-                                             void* ws, size_t ws_bytes, hipStream_t stream) {
+mfd_status mfd_lmhead_logsoftmax_topk_mapped(const void* hidden, const void* weight, mfd_head_layout layout,
+                                             const int32_t* vocab_map, int V_full, int N, int K, int L, int D, int V,
+                                             int k, double* lse, int32_t* topk_id, float* topk_raw,
+                                             float* topk_logp, int32_t* status, void* ws, size_t ws_bytes,
+                                             hipStream_t stream) {
   if (V_full < V || V_full > kMaxV)
     return fail(MFD_ERR_INVALID_ARG, "V_full must be in [V, %d] (got %d, V = %d)", kMaxV, V_full, V);
   if (N > 0) REQUIRE_PTR(vocab_map);
-  return lmhead_impl("mfd_lmhead_logsoftmax_topk_mapped launch", hidden, weight, vocab_map, N, K, L, D, V, k, lse,
-                     topk_id, topk_raw, topk_logp, status, ws, ws_bytes, stream);
+  return lmhead_impl("mfd_lmhead_logsoftmax_topk_mapped launch", hidden, weight, layout, vocab_map, N, K, L, D, V, k,
+                     lse, topk_id, topk_raw, topk_logp, status, ws, ws_bytes, stream);
 }
 
 static mfd_status mixture_threshold_impl(const char* call, const int32_t* topk_id, const float* topk_raw,

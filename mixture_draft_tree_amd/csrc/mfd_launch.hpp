@@ -75,8 +75,11 @@ struct LmhWorkspace {
   size_t off_samp, off_thr, off_count, off_part, off_cand, bytes;
 };
 LmhWorkspace lmhead_workspace(long long M, int V, int k);
-// vocab_map (device [V] or null): topk_id reports vocab_map[column]
-hipError_t launch_lmhead_topk(const void* hidden, const void* weight, const int32_t* vocab_map, int M,
+// vocab_map (device [V] or null): topk_id reports vocab_map[column];
+// packed: weight in the layout written by launch_lmhead_pack
+size_t lmhead_packed_bytes(int V, int D);
+hipError_t launch_lmhead_pack(const void* weight, int V, int D, void* packed, hipStream_t stream);
+hipError_t launch_lmhead_topk(const void* hidden, const void* weight, bool packed, const int32_t* vocab_map, int M,
                               int rows_per_tree, int D, int V, int k, double* lse, int32_t* topk_id, float* topk_raw,
                               float* topk_logp, int32_t* status, void* ws, hipStream_t stream);
 

@@ -27,12 +27,14 @@ MFD_BF16, MFD_F32 = 0, 1
 (MFD_OP_LOGSOFTMAX_TOPK, MFD_OP_MIXTURE_THRESHOLD, MFD_OP_TREE_BUILD,
  MFD_OP_TREE_MASK, MFD_OP_VERIFY_WALK, MFD_OP_COVERED_MASS, MFD_OP_LMHEAD_TOPK) = range(7)
 MFD_TREE_NONFINITE, MFD_TREE_CAPACITY, MFD_TREE_BAD_TEMPERATURE, MFD_TREE_BAD_MODES = 1, 2, 4, 8
+MFD_HEAD_ROWS, MFD_HEAD_PACKED = 0, 1
 
 EXPORTED = ["mfd_last_error", "mfd_version", "mfd_workspace_size", "mfd_logsoftmax_topk",
             "mfd_logsoftmax_topk_mapped", "mfd_mixture_threshold", "mfd_tree_build", "mfd_tree_mask",
             "mfd_verify_walk", "mfd_covered_mass", "mfd_chimera_count", "mfd_logsoftmax_topk_modes",
             "mfd_mixture_threshold_modes", "mfd_tree_build_modes", "mfd_stream_read",
-            "mfd_lmhead_logsoftmax_topk", "mfd_lmhead_logsoftmax_topk_mapped"]
+            "mfd_lmhead_logsoftmax_topk", "mfd_lmhead_logsoftmax_topk_mapped",
+            "mfd_lmhead_packed_size", "mfd_lmhead_pack_weight"]
 
 _p = ctypes.c_void_p
 _i = ctypes.c_int
@@ -61,10 +63,14 @@ _lib.mfd_tree_build_modes.restype = _i
 _lib.mfd_tree_build_modes.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p,
                                       _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]
 _lib.mfd_lmhead_logsoftmax_topk.restype = _i
-_lib.mfd_lmhead_logsoftmax_topk.argtypes = [_p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p]
+_lib.mfd_lmhead_logsoftmax_topk.argtypes = [_p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz, _p]
+_lib.mfd_lmhead_packed_size.restype = _i
+_lib.mfd_lmhead_packed_size.argtypes = [_i, _i, ctypes.POINTER(_sz)]
+_lib.mfd_lmhead_pack_weight.restype = _i
+_lib.mfd_lmhead_pack_weight.argtypes = [_p, _i, _i, _p, _sz, _p]
 _lib.mfd_lmhead_logsoftmax_topk_mapped.restype = _i
-_lib.mfd_lmhead_logsoftmax_topk_mapped.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p,
-                                                   _sz, _p]
+_lib.mfd_lmhead_logsoftmax_topk_mapped.argtypes = [_p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p,
+                                                   _p, _sz, _p]
 _lib.mfd_stream_read.restype = _i
 _lib.mfd_stream_read.argtypes = [_p, _sz, _p, _p]
 _lib.mfd_tree_mask.restype = _i
@@ -198,6 +204,32 @@ def lmhead_workspace(N: int, K: int, L: int, V: int, k: int, device="cuda") -> t
     return torch.empty((max(n, 256) + 255) // 8, dtype=torch.int64, device=device)
 
 
+class PackedHead:
+    """An LM head re-laid out by mfd_lmhead_pack_weight (device buffer + its shape)."""
+
+    def __init__(self, buf: torch.Tensor, V: int, D: int):
+        self.buf, self.V, self.D = buf, V, D
+        self.device = buf.device
+
+
+def lmhead_packed_size(V: int, D: int) -> int:
+    out = _sz(0)
+    _check(_lib.mfd_lmhead_packed_size(V, D, ctypes.byref(out)), "mfd_lmhead_packed_size")
+    return int(out.value)
+
+
+def mfd_lmhead_pack_weight(weight, stream=None) -> PackedHead:
+    """weight [V, D] bf16 on the GPU -> the packed head (allocated here, with torch)."""
+    if weight.dim() != 2 or weight.dtype != torch.bfloat16 or not weight.is_contiguous() or weight.device.type != "cuda":
+        raise ValueError("weight must be a contiguous [V, D] bf16 GPU tensor")
+    V, D = weight.shape
+    n = lmhead_packed_size(V, D)
+    buf = torch.empty((n // 2,), dtype=torch.bfloat16, device=weight.device)
+    _check(_lib.mfd_lmhead_pack_weight(_ptr(weight), V, D, _ptr(buf), n, _stream_handle(stream)),
+           "mfd_lmhead_pack_weight")
+    return PackedHead(buf, V, D)
+
+
 def mfd_lmhead_logsoftmax_topk(hidden, weight, k, lse, topk_id, topk_raw, topk_logp=None, status=None, ws=None,
                                stream=None, vocab_map=None, V_full=None):
     """hidden [N, K, L, D] bf16, weight [V, D] bf16 -> lse [N, K, L] fp64, topk_* [N, K, L, k]
@@ -209,10 +241,16 @@ def mfd_lmhead_logsoftmax_topk(hidden, weight, k, lse, topk_id, topk_raw, topk_l
     if hidden.dtype != torch.bfloat16:
         raise ValueError(f"hidden must be bf16, got {hidden.dtype}")
     N, K, L, D = hidden.shape
-    if weight.dim() != 2 or weight.shape[1] != D:
-        raise ValueError(f"weight must be [V, {D}], got {tuple(weight.shape)}")
-    V = weight.shape[0]
-    _want(weight, "weight", torch.bfloat16, (V, D))
+    if isinstance(weight, PackedHead):
+        if weight.D != D:
+            raise ValueError(f"packed head has D = {weight.D}, hidden has {D}")
+        V, layout, wptr = weight.V, MFD_HEAD_PACKED, _ptr(weight.buf)
+    else:
+        if weight.dim() != 2 or weight.shape[1] != D:
+            raise ValueError(f"weight must be [V, {D}], got {tuple(weight.shape)}")
+        V = weight.shape[0]
+        _want(weight, "weight", torch.bfloat16, (V, D))
+        layout, wptr = MFD_HEAD_ROWS, _ptr(weight)
     _want(lse, "lse", torch.float64, (N, K, L))
     _want(topk_id, "topk_id", torch.int32, (N, K, L, k))
     _want(topk_raw, "topk_raw", torch.float32, (N, K, L, k))
@@ -226,11 +264,11 @@ def mfd_lmhead_logsoftmax_topk(hidden, weight, k, lse, topk_id, topk_raw, topk_l
     if vocab_map is not None:
         _want(vocab_map, "vocab_map", torch.int32, (V,))
         _check(_lib.mfd_lmhead_logsoftmax_topk_mapped(
-            _ptr(hidden), _ptr(weight), _ptr(vocab_map), V if V_full is None else V_full, N, K, L, D, V, k,
+            _ptr(hidden), wptr, layout, _ptr(vocab_map), V if V_full is None else V_full, N, K, L, D, V, k,
             _ptr(lse), _ptr(topk_id), _ptr(topk_raw), _ptr(topk_logp), _ptr(status), ctypes.c_void_p(ptr + off),
             max(nbytes, 0), _stream_handle(stream)), "mfd_lmhead_logsoftmax_topk_mapped")
         return
-    _check(_lib.mfd_lmhead_logsoftmax_topk(_ptr(hidden), _ptr(weight), N, K, L, D, V, k, _ptr(lse), _ptr(topk_id),
+    _check(_lib.mfd_lmhead_logsoftmax_topk(_ptr(hidden), wptr, layout, N, K, L, D, V, k, _ptr(lse), _ptr(topk_id),
                                            _ptr(topk_raw), _ptr(topk_logp), _ptr(status),
                                            ctypes.c_void_p(ptr + off), max(nbytes, 0), _stream_handle(stream)),
            "mfd_lmhead_logsoftmax_topk")

@@ -204,8 +204,9 @@ def _lmh(**kw):
     a = dict(h=FAKE, w=FAKE, N=1, K=8, L=15, D=2560, V=151936, k=256, lse=FAKE, tid=FAKE, raw=FAKE,
              ws=ctypes.c_void_p(0x100000), ws_bytes=1 << 40)
     a.update(kw)
-    return M._lib.mfd_lmhead_logsoftmax_topk(a["h"], a["w"], a["N"], a["K"], a["L"], a["D"], a["V"], a["k"],
-                                             a["lse"], a["tid"], a["raw"], None, None, a["ws"], a["ws_bytes"], None)
+    return M._lib.mfd_lmhead_logsoftmax_topk(a["h"], a["w"], a.get("layout", M.MFD_HEAD_ROWS), a["N"], a["K"], a["L"],
+                                             a["D"], a["V"], a["k"], a["lse"], a["tid"], a["raw"], None, None, a["ws"],
+                                             a["ws_bytes"], None)
 
 
 def test_lmhead_call_rejects_before_launch():
@@ -225,6 +226,7 @@ def test_lmhead_call_rejects_before_launch():
     assert _lmh(ws_bytes=1000) == M.MFD_ERR_WORKSPACE and "workspace needs" in M.last_error()
     assert _lmh(ws=ctypes.c_void_p(0x100010)) == M.MFD_ERR_WORKSPACE
     assert _lmh(N=0, h=None, w=None) == M.MFD_OK
+    assert _lmh(layout=2) == M.MFD_ERR_INVALID_ARG and "layout" in M.last_error()
 
 
 def test_lmhead_workspace_size():
@@ -242,10 +244,22 @@ def test_lmhead_workspace_size():
 
 def test_lmhead_mapped_rejects_before_launch():
     f = M._lib.mfd_lmhead_logsoftmax_topk_mapped
-    args = lambda vm=FAKE, V_full=200000, V=65536, N=1: (FAKE, FAKE, vm, V_full, N, 8, 15, 2560, V, 256, FAKE, FAKE, FAKE,
-                                                       None, None, ctypes.c_void_p(0x100000), 1000, None)
+    args = lambda vm=FAKE, V_full=200000, V=65536, N=1: (FAKE, FAKE, M.MFD_HEAD_ROWS, vm, V_full, N, 8, 15, 2560, V,
+                                                       256, FAKE, FAKE, FAKE, None, None, ctypes.c_void_p(0x100000),
+                                                       1000, None)
     assert f(*args(V_full=1000)) == M.MFD_ERR_INVALID_ARG and "V_full" in M.last_error()
     assert f(*args(V_full=1 << 20)) == M.MFD_ERR_INVALID_ARG
     assert f(*args(vm=None)) == M.MFD_ERR_INVALID_ARG and "vocab_map" in M.last_error()
     assert f(*args()) == M.MFD_ERR_WORKSPACE          # 1000 bytes of workspace: rejected, nothing launched
     assert f(*args(vm=None, N=0)) == M.MFD_OK
+
+
+def test_lmhead_pack_checks():
+    assert M.lmhead_packed_size(151936, 2560) == 152064 * 2560 * 2
+    assert M.lmhead_packed_size(1, 64) == 256 * 64 * 2
+    with pytest.raises(M.MfdError):
+        M.lmhead_packed_size(1000, 100)
+    f = M._lib.mfd_lmhead_pack_weight
+    assert f(FAKE, 1000, 128, FAKE, 1000, None) == M.MFD_ERR_INVALID_ARG and "packed needs" in M.last_error()
+    assert f(None, 1000, 128, FAKE, 1 << 30, None) == M.MFD_ERR_INVALID_ARG
+    assert f(FAKE, 1000, 128, ctypes.c_void_p(0x100008), 1 << 30, None) == M.MFD_ERR_INVALID_ARG

@@ -29,7 +29,8 @@ def _say(msg):
 def _run(hidden, weight, k):
     N, K, L, D = hidden.shape
     d = "cuda"
-    H, W = hidden.to(d).contiguous(), weight.to(d).contiguous()
+    H = hidden.to(d).contiguous()
+    W = weight if isinstance(weight, M.PackedHead) else weight.to(d).contiguous()
     lse = torch.empty((N, K, L), dtype=torch.float64, device=d)
     ids = torch.empty((N, K, L, k), dtype=torch.int32, device=d)
     raw = torch.empty((N, K, L, k), dtype=torch.float32, device=d)
@@ -239,3 +240,31 @@ def test_lmhead_mapped_subset_bit_exact(V_full, V_draft, k):
     assert np.array_equal(ids.cpu().numpy(), vmap.numpy()[o_ids])
     assert np.array_equal(raw.cpu().numpy().astype(np.float64), np.take_along_axis(x64, o_ids.astype(np.int64), -1))
     assert np.max(np.abs(lse.cpu().numpy() - o_lse)) < LSE_TOL
+
+
+def test_lmhead_pack_weight_layout():
+    # The packer is a pure re-layout: unpacking on the CPU gives the head back,
+    # padded rows are zero.
+    _say("lmhead pack layout")
+    _, w = _grid_inputs(1, 1, 1, 192, 1000, seed=3)
+    pk = M.mfd_lmhead_pack_weight(w.cuda())
+    torch.cuda.synchronize()
+    V, D = w.shape
+    Vp, nS = (V + 255) // 256 * 256, D // 32
+    p = pk.buf.cpu().view(Vp // 64, nS, 64, 32)                 # [row block, k block, row, k]
+    un = p.permute(0, 2, 1, 3).reshape(Vp, D)
+    assert torch.equal(un[:V], w) and torch.all(un[V:] == 0)
+
+
+@pytest.mark.parametrize("name", ["lmhead_small", "lmhead_ragged", "lmhead_wide", "lmhead_single"])
+def test_lmhead_packed_equals_rows(name):
+    # Same operands in the same k order: the packed head gives bit-identical outputs.
+    _say(f"lmhead packed vs rows {name}")
+    b = synth.lmhead_batch(name)
+    w = b.workload
+    k = min(w.B, w.V)
+    ref = _run(b.hidden, b.weight, k)
+    pk = M.mfd_lmhead_pack_weight(b.weight.cuda())
+    got = _run(b.hidden, pk, k)
+    for r, g in zip(ref, got):
+        assert np.array_equal(r, g)
