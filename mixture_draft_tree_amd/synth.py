@@ -359,6 +359,8 @@ LMHEAD_WORKLOADS = {
     "lmhead_mid": LmHeadWorkload("lmhead_mid", 22, 8, 15, 40000, 256, 256, 2, True),
     # 360 rows: more than 256, so the 256-column tiles of large batches are used
     "lmhead_wide": LmHeadWorkload("lmhead_wide", 26, 8, 15, 40000, 256, 256, 3, True),
+    # 2160 rows over 17 row tiles, the last one ragged
+    "lmhead_tall": LmHeadWorkload("lmhead_tall", 27, 8, 15, 10000, 128, 64, 18, True),
     # the MFD drafter's shape: K=8 modes x 15 positions over V=151936 at D=2560
     "lmhead_single": LmHeadWorkload("lmhead_single", 23, 8, 15, 151936, 2560, 256, 1, False),
     "lmhead_single_grid": LmHeadWorkload("lmhead_single_grid", 24, 8, 15, 151936, 2560, 256, 1, True),

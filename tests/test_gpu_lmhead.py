@@ -69,7 +69,7 @@ def _check_bounded(x64, eps, k, lse, ids, raw):
         assert abs(lse[r] - O.lse_rows(x)) < LSE_TOL + em
 
 
-@pytest.mark.parametrize("name", ["lmhead_small", "lmhead_mid", "lmhead_wide"])
+@pytest.mark.parametrize("name", ["lmhead_small", "lmhead_mid", "lmhead_wide", "lmhead_tall"])
 def test_lmhead_grid_bit_exact(name):
     _say(f"lmhead grid parity {name}")
     b = synth.lmhead_batch(name)
@@ -256,7 +256,7 @@ def test_lmhead_pack_weight_layout():
     assert torch.equal(un[:V], w) and torch.all(un[V:] == 0)
 
 
-@pytest.mark.parametrize("name", ["lmhead_small", "lmhead_ragged", "lmhead_wide", "lmhead_single"])
+@pytest.mark.parametrize("name", ["lmhead_small", "lmhead_ragged", "lmhead_wide", "lmhead_tall", "lmhead_single"])
 def test_lmhead_packed_equals_rows(name):
     # Same operands in the same k order: the packed head gives bit-identical outputs.
     _say(f"lmhead packed vs rows {name}")
