@@ -34,8 +34,11 @@
  *     nothing and keeps no state between calls; calls on different streams
  *     are independent when their workspaces differ.
  *   - Every call is asynchronous on `stream` (0 = the null stream).
- *   - A return value other than MFD_OK means nothing was launched; a
- *     thread-local message is available from mfd_last_error().
+ *   - A return value other than MFD_OK means the call's outputs were not
+ *     written: MFD_ERR_INVALID_ARG, MFD_ERR_DTYPE and MFD_ERR_WORKSPACE are
+ *     found before any launch; after MFD_ERR_DEVICE, kernels of the call that
+ *     were launched before the refused one may have written its workspace.
+ *     A thread-local message is available from mfd_last_error().
  *   - Data-dependent problems are reported per tree in an optional device
  *     array `status` [N] (int32, bit flags OR-ed in; the caller zeroes it):
  *       MFD_TREE_NONFINITE        a NaN or +inf drafter logit in the tree
@@ -367,6 +370,12 @@ mfd_status mfd_tree_mask(const int32_t* parent, const int32_t* depth, const int3
  * Each visited row is cut into slices that any of the launch's workgroups may
  * take, so the device's resident workgroups share the open rows of all trees;
  * calls on one stream are ordered, calls that overlap must not share `ws`.
+ * The workgroups wait on one another, so they are launched cooperatively
+ * (all resident at once).  The HIP runtime grants cooperative launches on a
+ * GPU to one process at a time: once a live process has made one, a second
+ * process's call fails with MFD_ERR_DEVICE ("the operation cannot be performed
+ * in the present state") and the walk does not run.  Keep the walks of a
+ * GPU in one process.
  */
 mfd_status mfd_verify_walk(const void* target_logits, mfd_dtype dtype, int N, int Bp1, int V, int L,
                            const int32_t* node_token, const int32_t* parent, const int32_t* depth,

@@ -10,3 +10,14 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built libmfdtree.so")
+    config.addinivalue_line("markers", "own_process_gpu: runs the GPU in a child process; collected first")
+
+
+def pytest_collection_modifyitems(config, items):
+    # The HIP runtime grants cooperative launches (the verification walk's) on
+    # a GPU to one process at a time.  The plain-C caller walks in a child
+    # process, so it runs before this process makes any GPU call of its own.
+    first = [it for it in items if it.get_closest_marker("own_process_gpu")]
+    if first:
+        rest = [it for it in items if not it.get_closest_marker("own_process_gpu")]
+        items[:] = first + rest

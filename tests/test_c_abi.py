@@ -28,6 +28,7 @@ def test_c_caller_cpu_checks():
 
 @needs_bin
 @pytest.mark.gpu
+@pytest.mark.own_process_gpu
 def test_c_caller_gpu_round(tmp_path):
     # two trees of the tiny workload; the second is walked at T = 1
     print("C caller: tiny workload, 2 trees", flush=True)
