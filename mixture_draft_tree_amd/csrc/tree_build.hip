@@ -44,6 +44,7 @@ namespace {
 constexpr int kNT = 1024;
 constexpr int kMaxSort = 16384;
 constexpr size_t kTreeLdsMax = 156 * 1024;  // LDS one workgroup may use (of 160 KB per CU)
+constexpr int kFirstQ = 64;  // depth-1 candidates per mode behind the threshold call's starting bound
 
 // Per-tree workspace layout (offsets in bytes from the tree's base).
 struct WsLayout {
@@ -758,6 +759,61 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
     }
   }
   __syncthreads();
+
+  if (!BUILD && B > 0) {
+    // A tighter start: pool each mode's first kFirstQ depth-1 candidates, give
+    // each distinct token the best of its pooled scores, and take (a 16-bit
+    // lower bound of) the B-th largest.  Those are B distinct prefixes whose
+    // node scores are at least their pooled scores, so it is a lower bound on
+    // the final cut-off too, and far above the single-mode one when the modes
+    // disagree.  Scores use the search's own expression.
+    const int q = k < kFirstQ ? k : kFirstQ;
+    const int np = Kn * q;
+    if (np >= B) {
+      const int P = next_pow2(np);
+      for (int c = tid; c < P; c += kNT) {
+        uint64_t key = ~0ull;
+        if (c < np) {
+          const int m = c / q, j = c - m * q;
+          const int tok = a.topk_id[((size_t)(n * K + m) * L) * k + j];
+          key = ((uint64_t)(uint32_t)tok << 32) | (uint64_t)c;
+        }
+        keys[c] = key;
+      }
+      __syncthreads();
+      block_sort_keys<kNT>(keys, P);
+      // runs of equal token: the head holds the best score, the rest NaN
+      for (int i = tid; i < np; i += kNT) {
+        double best = NAN;
+        const uint64_t tk = keys[i] >> 32;
+        if (i == 0 || (keys[i - 1] >> 32) != tk) {
+          best = -INFINITY;
+          bool bad = false;
+          for (int r = i; r < np && (keys[r] >> 32) == tk; ++r) {
+            const int c = (int)(uint32_t)keys[r];
+            const int m = c / q, j = c - m * q;
+            const float x = a.topk_raw[((size_t)(n * K + m) * L) * k + j];
+            const double sc = (0.0 + (double)x) - norm[m * Lp1 + 1];
+            if (sc != sc) bad = true;
+            else if (sc > best) best = sc;
+          }
+          if (bad) best = NAN;
+        }
+        t.ch_s[i] = best;
+      }
+      __syncthreads();
+      const double t0 = ctl.tau;
+      int local = 0;
+      for (int i = tid; i < np; i += kNT) local += t.ch_s[i] >= t0 ? 1 : 0;
+      const int alive = block_sum<kNT>(local, ctl.scan);
+      if (alive >= B) {
+        const double nb = kth_lower_bound(
+            np, B, [&](int i) { return t.ch_s[i]; }, [&](int i) { return t.ch_s[i] >= t0; }, ctl);
+        if (tid == 0 && nb > t0) ctl.tau = nb;
+      }
+      __syncthreads();
+    }
+  }
 
   level_search<BUILD>(a, t, n, ctl, keys, norm, nk);
 

@@ -203,6 +203,39 @@ def test_tree_small_cases(case):
     say(f"[tree] seed={seed} exact={r['exact']} n_nodes={g['n_nodes']}")
 
 
+# Modes that share their tokens: the cut-off's starting bound pools each
+# mode's first depth-1 candidates and merges equal tokens, so runs of one
+# token across modes, exact ties across modes (a constant shift leaves the
+# log-probabilities unchanged) and pools with fewer than B distinct tokens all
+# have to give the oracle's tree.
+SHARED = [
+    # seed, K, L, V, B, per-mode noise (0: identical modes), per-mode shift
+    (21, 4, 3, 200, 100, 0.0, 0.0),
+    (22, 8, 4, 300, 120, 0.3, 0.0),
+    (23, 6, 3, 500, 150, 0.0, 0.75),
+    (24, 8, 3, 1000, 256, 1.0, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", SHARED, ids=[f"m{c[0]}" for c in SHARED])
+def test_tree_shared_modes(case):
+    seed, K, L, V, B, noise, shift = case
+    say(f"[tree shared modes] seed={seed} K={K} L={L} V={V} B={B}")
+    g = torch.Generator().manual_seed(seed)
+    base = torch.randn((1, 1, L, V), generator=g) * 2
+    x = base.expand(1, K, L, V) + noise * torch.randn((1, K, L, V), generator=g)
+    x = x + shift * torch.arange(K, dtype=torch.float32).view(1, K, 1, 1)
+    x = x.contiguous()
+    P = MixtureTreePath(1, K, L, V, B, with_logp=True)
+    anchor = torch.tensor([3], dtype=torch.int32, device="cuda")
+    pos = torch.tensor([0], dtype=torch.int64, device="cuda")
+    P.build(x.cuda(), anchor, pos)
+    torch.cuda.synchronize()
+    assert P.buf.status.item() == 0
+    r = compare_tree(x[0].double().numpy(), B, 3, tree_rows(P, 0))
+    say(f"[tree shared modes] seed={seed} exact={r['exact']} n_nodes={tree_rows(P, 0)['n_nodes']}")
+
+
 def test_modes_small_batch():
     """Per-tree mode counts in one launch: each tree equals the oracle over its first
     K_n modes, a tree with K_n = K equals the plain calls bit for bit, and counts
