@@ -770,13 +770,19 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
     const int q = k < kFirstQ ? k : kFirstQ;
     const int np = Kn * q;
     if (np >= B) {
+      // keys[0, P) are sorted; the pooled scores wait in keys[P, 2P)
+      // (2P <= sort_cap: sort_cap >= 2 K k, or 16384)
       const int P = next_pow2(np);
+      double* pooled = reinterpret_cast<double*>(keys + P);
       for (int c = tid; c < P; c += kNT) {
         uint64_t key = ~0ull;
         if (c < np) {
           const int m = c / q, j = c - m * q;
-          const int tok = a.topk_id[((size_t)(n * K + m) * L) * k + j];
+          const size_t at = ((size_t)(n * K + m) * L) * k + j;
+          const int tok = a.topk_id[at];
+          const float x = a.topk_raw[at];
           key = ((uint64_t)(uint32_t)tok << 32) | (uint64_t)c;
+          pooled[c] = (0.0 + (double)x) - norm[m * Lp1 + 1];
         }
         keys[c] = key;
       }
@@ -790,10 +796,7 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
           best = -INFINITY;
           bool bad = false;
           for (int r = i; r < np && (keys[r] >> 32) == tk; ++r) {
-            const int c = (int)(uint32_t)keys[r];
-            const int m = c / q, j = c - m * q;
-            const float x = a.topk_raw[((size_t)(n * K + m) * L) * k + j];
-            const double sc = (0.0 + (double)x) - norm[m * Lp1 + 1];
+            const double sc = pooled[(uint32_t)keys[r]];
             if (sc != sc) bad = true;
             else if (sc > best) best = sc;
           }
@@ -850,10 +853,25 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
   int nsel = fail ? 0 : (nsel_in < M ? nsel_in : M);
   // node_aux: 1 = selected, then the canonical row index
   if (M > nsel && nsel > 0) {
-    const double cstar = exact_kth(M, nsel, [&](int i) { return t.node_S[i + 1]; }, ctl, keys, a.sort_cap);
-    int lgt = 0;
-    for (int i = 1 + tid; i < nc; i += kNT) lgt += (t.node_S[i] > cstar) ? 1 : 0;
-    const int gt = block_sum<kNT>(lgt, ctl.scan);
+    // The nsel-th best node score.  It is the given cut-off itself when fewer
+    // than nsel nodes lie above it and at least nsel at or above it, as for
+    // the threshold call's own cut-off; otherwise it is selected exactly.
+    int lgt = 0, lge = 0;
+    for (int i = 1 + tid; i < nc; i += kNT) {
+      const double sc = t.node_S[i];
+      lgt += (sc > cutoff_in) ? 1 : 0;
+      lge += (sc >= cutoff_in) ? 1 : 0;
+    }
+    const int gt_in = block_sum<kNT>(lgt, ctl.scan);
+    const int ge_in = block_sum<kNT>(lge, ctl.scan);
+    double cstar = cutoff_in;
+    int gt = gt_in;
+    if (!(gt_in < nsel && ge_in >= nsel)) {
+      cstar = exact_kth(M, nsel, [&](int i) { return t.node_S[i + 1]; }, ctl, keys, a.sort_cap);
+      lgt = 0;
+      for (int i = 1 + tid; i < nc; i += kNT) lgt += (t.node_S[i] > cstar) ? 1 : 0;
+      gt = block_sum<kNT>(lgt, ctl.scan);
+    }
     const int need = nsel - gt;
     // collect the ties at cstar (node ids in node_aux order via keys[] as int list)
     int32_t* tied = reinterpret_cast<int32_t*>(keys);
