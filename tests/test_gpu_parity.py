@@ -214,6 +214,8 @@ SHARED = [
     (22, 8, 4, 300, 120, 0.3, 0.0),
     (23, 6, 3, 500, 150, 0.0, 0.75),
     (24, 8, 3, 1000, 256, 1.0, 0.0),
+    (25, 32, 3, 2000, 300, 0.5, 0.0),   # K = 32: 2048 pooled candidates
+    (26, 32, 2, 500, 40, 0.2, 0.0),     # K = 32 with k = B = 40 < 64
 ]
 
 
