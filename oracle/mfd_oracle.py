@@ -368,9 +368,17 @@ def ddtree_product_select(x1: np.ndarray, B: int) -> list:
     return [t for _, t in got[:B]]
 
 
-def mode_scores(x: np.ndarray, t: tuple, k: int | None = None, lse=None, norm=None) -> np.ndarray:
-    """s_k(t) for every mode k.  With `k`, a mode whose rank order puts any token
-    of t at rank k or worse scores -inf (the truncated problem the search uses)."""
+def mode_scores(x: np.ndarray, t: tuple, k: int | None = None, lse=None, norm=None, ranked=None) -> np.ndarray:
+    """s_k(t) for every mode k: the log of the product of mode k's per-position
+    probabilities of t's tokens ([PP] "How it works" step 1), summed like the
+    search sums them (raw logits left to right, minus the normaliser sum).
+
+    With `k`, a mode whose rank order puts any token of t at rank k or worse
+    scores -inf (the truncated problem the search uses).  The rank of a token
+    is the number of tokens of its row ahead of it in (logit desc, id asc)
+    order.  `ranked` ([K][L] arrays of each row's first k ids in that order,
+    as MixtureSelection.topk holds them) answers "rank < k" by membership
+    instead of counting; the two give the same answer."""
     x = np.asarray(x, dtype=np.float64)
     K, L, V = x.shape
     if lse is None:
@@ -384,9 +392,13 @@ def mode_scores(x: np.ndarray, t: tuple, k: int | None = None, lse=None, norm=No
         for i, tok in enumerate(t):
             raw = raw + float(x[m, i, tok])
             if k is not None:
-                row = x[m, i]
-                better = np.count_nonzero(row > row[tok]) + np.count_nonzero((row == row[tok]) & (np.arange(V) < tok))
-                if better >= k:
+                if ranked is not None:
+                    inside = bool(np.any(np.asarray(ranked[m][i][:k]) == tok))
+                else:
+                    row = x[m, i]
+                    ahead = np.count_nonzero(row > row[tok]) + np.count_nonzero((row == row[tok]) & (np.arange(V) < tok))
+                    inside = ahead < k
+                if not inside:
                     ok = False
         out[m] = raw - norm[m, len(t)] if ok else -np.inf
     return out

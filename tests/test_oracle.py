@@ -525,6 +525,116 @@ def test_band_criterion():
     assert s2.selected == [(0,)] and not O.band_is_exact(y, s2)
 
 
+# ---------------------------------------------------------------- per-mode scores
+
+def _all_prefixes(L, V):
+    import itertools
+    for d in range(1, L + 1):
+        for t in itertools.product(range(V), repeat=d):
+            yield t
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_mode_scores_against_library_log_softmax(seed):
+    """s_m(t) is the sum of mode m's per-position log-probabilities of t's tokens
+    (project page 'How it works' step 1).  Here every prefix of a tiny tree is
+    scored from torch.log_softmax in fp64 (a library routine), and the best-mode
+    score and best mode of every prefix are compared with the brute-force
+    selection (the definition, model card summary / 'In one minute')."""
+    rng = np.random.default_rng(300 + seed)
+    K, L, V = 3, 3, 5
+    x = _rand_logits(rng, K, L, V, ints=(seed % 2 == 1))
+    if seed >= 2:
+        x[rng.random(x.shape) < 0.2] = -np.inf
+        x[:, :, 0] = np.where(np.isinf(x[:, :, 0]), 0.0, x[:, :, 0])
+    lp = torch.log_softmax(torch.from_numpy(x), dim=-1).numpy()
+    bf = O.mixture_select_bruteforce(x, 10 ** 6)
+    for t in _all_prefixes(L, V):
+        got = O.mode_scores(x, t)
+        want = np.array([sum(lp[m, i, tok] for i, tok in enumerate(t)) for m in range(K)])
+        fin = np.isfinite(want)
+        assert np.array_equal(np.isfinite(got), fin), t
+        assert np.allclose(got[fin], want[fin], rtol=0, atol=1e-12), (t, got, want)
+        if fin.any():
+            assert got.max() == bf.S[t] and int(np.argmax(got)) == bf.mu[t], t
+        else:
+            assert t not in bf.S
+
+
+def test_mode_scores_rank_truncation_hand_example():
+    """With a cap k, a mode scores -inf when a token of the prefix has k or more
+    tokens ahead of it in (logit desc, id asc) order, the only ranks the search
+    ever reads.  Row 0 = [1, 3, 3, 0]: token 1 has rank 0, token 2 rank 1 (tie
+    with token 1, higher id), token 0 rank 2, token 3 rank 3."""
+    x = np.array([[[1.0, 3.0, 3.0, 0.0], [0.0, 0.0, 0.0, 0.0]],
+                  [[3.0, 3.0, 1.0, 0.0], [2.0, 1.0, 0.0, -1.0]]])
+    lse = O.lse_rows(x)
+    for t, k, want_finite in [((2,), 2, [True, False]),    # mode 0: rank 1 < 2; mode 1: token 2 has rank 2
+                              ((2,), 1, [False, False]),
+                              ((0,), 3, [True, True]),     # mode 0: rank 2 < 3; mode 1: rank 0
+                              ((0,), 2, [False, True]),
+                              ((3,), 4, [True, True]),
+                              ((3,), 3, [False, False]),
+                              ((1, 3), 4, [True, True]),   # second position: mode 0 all tied, token 3 rank 3
+                              ((1, 3), 3, [False, False]),
+                              ((1, 1), 2, [True, True]),
+                              ((0, 2), 3, [True, True]),
+                              ((0, 2), 2, [False, False])]:
+        got = O.mode_scores(x, t, k=k)
+        assert list(np.isfinite(got)) == want_finite, (t, k, got)
+        full = O.mode_scores(x, t)
+        assert np.array_equal(got[np.isfinite(got)], full[np.isfinite(got)])
+        # the closed form: sum of logits minus the sum of row normalisers
+        for m in range(2):
+            if want_finite[m]:
+                raw = sum(x[m, i, tok] for i, tok in enumerate(t))
+                assert abs(got[m] - (raw - sum(lse[m, :len(t)]))) < 1e-12
+        ranked = [[O.rank_order(x[m, i], k) for i in range(2)] for m in range(2)]
+        assert np.array_equal(O.mode_scores(x, t, k=k, ranked=ranked), got)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_mode_scores_truncation_against_lexsort_ranks(seed):
+    """The rank cut, with ties, against ranks from numpy.lexsort (a library
+    sort): a mode is -inf exactly when some token's lexsort position is >= k."""
+    rng = np.random.default_rng(400 + seed)
+    K, L, V = 2, 3, 7
+    x = _rand_logits(rng, K, L, V, ints=True)
+    pos = np.empty((K, L, V), dtype=np.int64)
+    for m in range(K):
+        for i in range(L):
+            order = np.lexsort((np.arange(V), -x[m, i]))
+            pos[m, i, order] = np.arange(V)
+    for k in (1, 2, 4, 7):
+        ranked = [[O.rank_order(x[m, i], k) for i in range(L)] for m in range(K)]
+        for t in _all_prefixes(L, V):
+            got = O.mode_scores(x, t, k=k)
+            want_inf = [any(pos[m, i, tok] >= k for i, tok in enumerate(t)) for m in range(K)]
+            assert list(np.isneginf(got)) == want_inf, (t, k)
+            assert np.array_equal(O.mode_scores(x, t, k=k, ranked=ranked), got)
+
+
+def test_band_criterion_runner_up_mode():
+    """band_is_exact's runner-up test in isolation: the prefixes around the
+    cut-off all have best mode 0 and depth 1, so only the runner-up mode's
+    distance decides.  A second mode identical to the first (a tie at every
+    prefix) makes the tree undecidable by raw sums; a second mode that puts
+    its mass elsewhere leaves it decidable."""
+    row = np.array([2.0, 1.8, 1.7, -5.0])
+    same = np.stack([row, row])[:, None, :]               # K=2, L=1, V=4
+    sel = O.mixture_select_heap(same, 1, band=0.25, k=4)  # every rank visible
+    assert sel.selected == [(0,)] and sel.order[1] == (1,)
+    assert {sel.mu[(0,)], sel.mu[(1,)]} == {0}
+    assert not O.band_is_exact(same, sel, tol=0.25)
+    apart = np.stack([row, np.array([-5.0, -5.0, -5.0, 2.0])])[:, None, :]
+    sel2 = O.mixture_select_heap(apart, 2, band=0.25, k=4)
+    assert sel2.selected == [(3,), (0,)] and sel2.order[2] == (1,)
+    assert sel2.mu[(0,)] == 0 and sel2.mu[(1,)] == 0 and sel2.mu[(3,)] == 1
+    assert O.band_is_exact(apart, sel2, tol=0.25)
+    # the same two trees with a band that reaches no unselected prefix
+    assert O.band_is_exact(same, O.mixture_select_heap(same, 1, band=0.1, k=4), tol=0.1)
+
+
 def test_synth_tree_is_independent_of_its_batch():
     """Tree n of a workload is drawn the same whether it comes in a batch from 0 or
     on its own (the pooled oracle timing draws trees one by one)."""
@@ -574,6 +684,39 @@ def test_lmhead_logits_against_fsum_loops():
                 assert abs(x[a, i, v] - ref) <= 1e-12 * max(1.0, abs(ref))
     with pytest.raises(ValueError):
         O.lmhead_logits(h, w[:, :39])
+
+
+def test_lmhead_bound_closed_form_hand_example():
+    """gamma_n = n u / (1 - n u) times the sum of |h_d w_vd| (Higham, 2nd ed.,
+    sec. 4.2), worked out by hand for D = 2 and D = 3 with u = 2^-23."""
+    u = 2.0 ** -23
+    h = np.array([[1.0, -2.0]])
+    w = np.array([[3.0, 0.5], [-1.0, 4.0]])
+    g2 = 2 * u / (1 - 2 * u)
+    got = O.lmhead_abs_bound(h, w)
+    assert got.shape == (1, 2)
+    assert got[0, 0] == 4.0 * g2 and got[0, 1] == 9.0 * g2   # 1*3 + 2*0.5 and 1*1 + 2*4
+    h3 = np.array([[0.5, 0.25, -1.0], [2.0, 0.0, 1.0]])
+    w3 = np.array([[8.0, -4.0, 2.0]])
+    g3 = 3 * u / (1 - 3 * u)
+    got3 = O.lmhead_abs_bound(h3, w3)
+    assert got3[0, 0] == 7.0 * g3 and got3[1, 0] == 18.0 * g3  # 4 + 1 + 2 and 16 + 0 + 2
+    assert O.lmhead_abs_bound(h3, w3, unit=2.0 ** -24)[1, 0] == 18.0 * (3 * 2.0 ** -24 / (1 - 3 * 2.0 ** -24))
+
+
+def test_lmhead_bound_is_within_a_small_factor_of_attainable():
+    """The bound is not loose by more than the gamma_n construction itself:
+    for D = 2 one fp32 addition toward zero of two exact products loses almost
+    one ulp, at least a quarter of the bound."""
+    a = np.float32(1.0)
+    b = np.float32(2.0 ** -23 * (1 - 2.0 ** -10))   # just under one ulp of 1.0
+    h = np.array([[1.0, 1.0]])
+    w = np.array([[float(a), float(b)]])
+    exact = float(a) + float(b)
+    truncated = float(a)                              # 1 + b rounded toward zero
+    err = abs(truncated - exact)
+    bound = float(O.lmhead_abs_bound(h, w)[0, 0])
+    assert err <= bound < 4.0 * err
 
 
 def test_lmhead_bound_covers_fp32_summation_orders():
