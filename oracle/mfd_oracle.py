@@ -404,13 +404,20 @@ def mode_scores(x: np.ndarray, t: tuple, k: int | None = None, lse=None, norm=No
     return out
 
 
-def union_at_cutoff(x: np.ndarray, cutoff: float, k: int, L: int | None = None) -> tuple:
+def union_at_cutoff(x: np.ndarray, cutoff: float, k: int, L: int | None = None, sel: MixtureSelection = None) -> tuple:
     """Per mode, the prefixes with s_k >= cutoff (the per-mode keeps), and their union
     ([PP] "In one minute": each mode keeps what reaches the common cut-off and
-    the tree is built once from all keeps)."""
+    the tree is built once from all keeps).  With `sel` (a selection of the
+    same x whose rows were ranked to at least k) its normalisers and rank
+    lists are reused instead of being computed again."""
     x = np.asarray(x, dtype=np.float64)
     K, Lx, V = x.shape
-    lse, norm, ids, vals = _row_tables(x, k)
+    if sel is not None and sel.topk and len(sel.topk[0][0]) >= k:
+        norm = sel.norm
+        ids = [[sel.topk[m][i][:k] for i in range(Lx)] for m in range(K)]
+        vals = [[x[m, i][ids[m][i]] for i in range(Lx)] for m in range(K)]
+    else:
+        lse, norm, ids, vals = _row_tables(x, k)
     per_mode = []
     for m in range(K):
         keep = set()
