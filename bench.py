@@ -320,6 +320,8 @@ def single_tree_latency(seed, steps, stream, name="single"):
     """Mean time of one whole step on a one-tree workload (N=1), ms."""
     w, N, P, logits, anchor, pos, temps, seeds, R = setup(name, seed, "cuda")
     total, _ = run_steps(P, logits, anchor, pos, R, temps, seeds, steps, 3, stream)
+    status = P.buf.status.cpu()
+    assert int(status.abs().sum()) == 0, f"per-tree status flags set ({name}): {status.tolist()}"
     return total / steps
 
 

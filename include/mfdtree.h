@@ -22,9 +22,10 @@
  * block_size - 1 = L, temperature = T) and the project page "Multi-Future
  * Drafting: Mixture Block Drafters for Tree-Verified Speculative Decoding"
  * ("In one minute": the B-th best score is the common cut-off, each mode
- * keeps the prefixes that reach it, shared prefixes are built once; "How it
- * works" step 1: a prefix's probability under a mode is the product of that
- * mode's per-position probabilities; step 3: best-mode scoring, the union of
+ * keeps the prefixes that reach it, a prefix produced by several modes
+ * becomes one node; "How it works" step 1: a prefix's probability under a
+ * mode is the product of that mode's per-position probabilities; step 3:
+ * best-mode scoring, the union of
  * the per-mode trees, one verification pass; Figure 2: one distribution per
  * position per mode, tau counts the bonus token).
  *
@@ -176,9 +177,9 @@ mfd_status mfd_mixture_threshold(const int32_t* topk_id, const float* topk_raw, 
                                  int32_t* status, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * The tree ("In one minute": every node is pulled from the modes that keep it,
- * shared prefixes are built once; step 3: the B best prefixes over all modes
- * form one tree, the union of the per-mode trees).  Selects, among prefixes
+ * The tree (project page, "In one minute": a prefix kept by several modes
+ * becomes a single node; step 3: the B best prefixes over all modes form one
+ * tree, the union of the per-mode trees).  Selects, among prefixes
  * with S >= cutoff, the first n_select in the order (S descending, best mode
  * ascending, token ids lexicographically ascending with a proper prefix first);
  * the best mode of a prefix is the lowest mode attaining S.  The selection is

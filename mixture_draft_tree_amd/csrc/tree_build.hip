@@ -13,7 +13,7 @@
 //             entries are written as 64-bit keys (parent node, token, mode,
 //             slot) into LDS and bitonic-sorted, so the copies of one prefix
 //             produced by different modes become adjacent: each run is one
-//             node (built once, "shared prefixes are built once"), its score
+//             node (a prefix kept by several modes is one node), its score
 //             is the run's maximum and its best mode the first mode attaining
 //             it.  The run members become the node's per-mode entries for the
 //             next level.

@@ -147,12 +147,24 @@ struct WalkArgs {
 
 // Ordering between workgroups.  Everything one workgroup hands to another
 // (slice results, cut-offs, counters, round words) is written and read with
-// agent-scope atomic stores, loads and RMWs, which act at the device's
-// coherence point, and a value is published only after the atomic stores
-// before it have completed (`drain`).  Plain data the kernel reads (rows,
-// nodes) is never written by it, so no acquire or release -- and none of the
-// L2 writeback and invalidation they cost on this device -- is needed.
-__device__ __forceinline__ void drain() { __builtin_amdgcn_s_waitcnt(0); }
+// agent-scope atomic stores, loads and RMWs; on this device family those
+// loads and stores carry the sc1 (device-scope) cache policy and act at the
+// device's coherence point, as do the RMWs.  In the LLVM AMDGPU memory model
+// for this family an agent-scope release is "write back L2 (buffer_wbl2 sc1),
+// then wait for every earlier access to complete (s_waitcnt vmcnt(0))" and an
+// acquire is "wait, then invalidate (buffer_inv sc1)"; the writeback and the
+// invalidate exist for non-atomic data, and the kernel hands over none (the
+// rows and nodes it reads are never written by it).  What remains of a
+// release or an acquire is the wait, which `drain` issues: every access
+// before it has completed at the coherence point before any access after it
+// is issued.  The signal fences around it stop the compiler from moving
+// memory accesses across it (s_waitcnt alone is no compiler barrier), so
+// program order is the order the hardware sees.
+__device__ __forceinline__ void drain() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 template <typename T>
 __device__ __forceinline__ T ld(const T* p) {
@@ -352,7 +364,10 @@ __global__ void __launch_bounds__(kWalkThreads, 4) verify_walk_kernel(WalkArgs a
         sh.j = pick;
         sh.word = w;
         sh.child = 0x7FFFFFFF;
-        if (pick >= 0 && ((w >> 7) & 1u)) sh.cut = ld(&a.cut[grp + pick * G]);
+        if (pick >= 0 && ((w >> 7) & 1u)) {
+          drain();  // the word was read before the cut-off it announces
+          sh.cut = ld(&a.cut[grp + pick * G]);
+        }
       }
     }
     __syncthreads();
@@ -416,10 +431,12 @@ __global__ void __launch_bounds__(kWalkThreads, 4) verify_walk_kernel(WalkArgs a
       st(&pi[s], mine.i1);
       drain();  // the result is in place before the slice counts as done
       const int old = __hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      drain();  // the count is in before the merge below reads the other slices' results
       sh.last = old == S - 1;
     }
     __syncthreads();
     if (!sh.last) continue;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
     // ------------------------------------------------ finish the round
     if (wid == 0) {

@@ -117,6 +117,7 @@ class MixtureTreePath:
 
     def build_from_hidden(self, hidden, weight, anchor, pos_base, stream=None):
         """Calls 1-4 with the fused LM head: hidden states -> tree, mask, position ids."""
+        self.clear_status(stream)
         self.lmhead_logsoftmax_topk(hidden, weight, stream)
         self.mixture_threshold(stream)
         self.tree_build(anchor, stream)
@@ -143,8 +144,18 @@ class MixtureTreePath:
         M.mfd_verify_walk(target, self.L, b.node_token, b.parent, b.depth, b.n_nodes, temperature, seed, b.tau,
                           b.out_tokens, b.path_nodes, b.status, ws=b.ws, stream=stream)
 
+    def clear_status(self, stream=None):
+        """Zero the per-tree status flags (the kernels only OR flags in).  A fill
+        kernel, not a memset, so that a captured step clears them on every replay."""
+        if stream is None:
+            self.buf.status.zero_()
+        else:
+            with torch.cuda.stream(stream):
+                self.buf.status.zero_()
+
     def build(self, logits, anchor, pos_base, stream=None):
-        """Calls 1-4: logits -> tree, mask, position ids."""
+        """Calls 1-4: logits -> tree, mask, position ids (status flags cleared first)."""
+        self.clear_status(stream)
         self.logsoftmax_topk(logits, stream)
         self.mixture_threshold(stream)
         self.tree_build(anchor, stream)
