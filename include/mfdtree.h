@@ -385,6 +385,29 @@ mfd_status mfd_verify_walk(const void* target_logits, mfd_dtype dtype, int N, in
                            void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * mfd_verify_walk without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The call itself allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine).  The walk's workspace
+ * is a built-in 2 MiB device array of the library, one copy per GPU, held
+ * until the process ends; its address on a device is looked up on the first
+ * call made with that device current.  Same arguments, outputs and errors as
+ * mfd_verify_walk, plus:
+ *   - N is at most 1347 (the trees whose workspace fits 2 MiB); a larger N
+ *     returns MFD_ERR_WORKSPACE before any launch.
+ *   - The call clears what must start at zero itself; the array keeps the
+ *     last call's contents otherwise.
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap on
+ *     a GPU (different streams, or other threads, without ordering between
+ *     them) race and give wrong results.  Calls on one stream are ordered.
+ */
+mfd_status mfd_verify_walk_noalloc(const void* target_logits, mfd_dtype dtype, int N, int Bp1, int V, int L,
+                                   const int32_t* node_token, const int32_t* parent, const int32_t* depth,
+                                   const int32_t* n_nodes, const float* temperature, const uint64_t* seed,
+                                   int32_t* tau, int32_t* out_tokens, int32_t* path_nodes, int32_t* status,
+                                   hipStream_t stream);
+
+/*
  * Covered target mass of each tree (project page, "Abstract": under tree
  * verification the expected number of accepted drafted tokens is the
  * probability mass the tree covers).  For tree n at temperature T = T[n]:

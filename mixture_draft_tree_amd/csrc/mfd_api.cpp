@@ -338,11 +338,10 @@ mfd_status mfd_tree_mask(const int32_t* parent, const int32_t* depth, const int3
       "mfd_tree_mask launch");
 }
 
-mfd_status mfd_verify_walk(const void* target_logits, mfd_dtype dtype, int N, int Bp1, int V, int L,
-                           const int32_t* node_token, const int32_t* parent, const int32_t* depth,
-                           const int32_t* n_nodes, const float* temperature, const uint64_t* seed, int32_t* tau,
-                           int32_t* out_tokens, int32_t* path_nodes, int32_t* status, void* ws, size_t ws_bytes,
-                           hipStream_t stream) {
+static mfd_status verify_walk_checks(const void* target_logits, mfd_dtype dtype, int N, int Bp1, int V, int L,
+                                     const int32_t* node_token, const int32_t* parent, const int32_t* depth,
+                                     const int32_t* n_nodes, const float* temperature, const uint64_t* seed,
+                                     int32_t* tau, int32_t* out_tokens, int32_t* path_nodes) {
   if (N < 0) return fail(MFD_ERR_INVALID_ARG, "N must be >= 0 (got %d)", N);
   if (Bp1 < 1 || Bp1 > kMaxB + 1) return fail(MFD_ERR_INVALID_ARG, "Bp1 must be in [1, %d] (got %d)", kMaxB + 1, Bp1);
   if (V < 1 || V > kMaxV) return fail(MFD_ERR_INVALID_ARG, "V must be in [1, %d] (got %d)", kMaxV, V);
@@ -362,6 +361,17 @@ mfd_status mfd_verify_walk(const void* target_logits, mfd_dtype dtype, int N, in
   const size_t esz = dtype == MFD_BF16 ? 2 : 4;
   if (reinterpret_cast<uintptr_t>(target_logits) % esz)
     return fail(MFD_ERR_INVALID_ARG, "target_logits not aligned to its element size");
+  return MFD_OK;
+}
+
+mfd_status mfd_verify_walk(const void* target_logits, mfd_dtype dtype, int N, int Bp1, int V, int L,
+                           const int32_t* node_token, const int32_t* parent, const int32_t* depth,
+                           const int32_t* n_nodes, const float* temperature, const uint64_t* seed, int32_t* tau,
+                           int32_t* out_tokens, int32_t* path_nodes, int32_t* status, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  mfd_status s = verify_walk_checks(target_logits, dtype, N, Bp1, V, L, node_token, parent, depth, n_nodes,
+                                    temperature, seed, tau, out_tokens, path_nodes);
+  if (s != MFD_OK || N == 0) return s == MFD_OK ? ok() : s;
   const size_t need = mfd::walk_ws_bytes(N);
   if (ws == nullptr || ws_bytes < need)
     return fail(MFD_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws == nullptr ? (size_t)0 : ws_bytes);
@@ -369,6 +379,36 @@ mfd_status mfd_verify_walk(const void* target_logits, mfd_dtype dtype, int N, in
   return from_hip(mfd::launch_verify_walk(target_logits, dtype == MFD_BF16, N, Bp1, V, L, node_token, parent, depth,
                                           n_nodes, temperature, seed, tau, out_tokens, path_nodes, status, ws, stream),
                   "mfd_verify_walk launch");
+}
+
+static int walk_noalloc_max_trees() {
+  int lo = 0, hi = 1 << 20;  // the largest N whose workspace fits the built-in scratch
+  while (lo < hi) {
+    const int mid = lo + (hi - lo + 1) / 2;
+    if (mfd::walk_ws_bytes(mid) <= mfd::walk_scratch_bytes()) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+mfd_status mfd_verify_walk_noalloc(const void* target_logits, mfd_dtype dtype, int N, int Bp1, int V, int L,
+                                   const int32_t* node_token, const int32_t* parent, const int32_t* depth,
+                                   const int32_t* n_nodes, const float* temperature, const uint64_t* seed,
+                                   int32_t* tau, int32_t* out_tokens, int32_t* path_nodes, int32_t* status,
+                                   hipStream_t stream) {
+  mfd_status s = verify_walk_checks(target_logits, dtype, N, Bp1, V, L, node_token, parent, depth, n_nodes,
+                                    temperature, seed, tau, out_tokens, path_nodes);
+  if (s != MFD_OK || N == 0) return s == MFD_OK ? ok() : s;
+  const size_t need = mfd::walk_ws_bytes(N);
+  if (need > mfd::walk_scratch_bytes())
+    return fail(MFD_ERR_WORKSPACE, "N = %d trees need %zu bytes of walk workspace; the built-in one holds %zu (N <= %d)",
+                N, need, mfd::walk_scratch_bytes(), walk_noalloc_max_trees());
+  void* ws = nullptr;
+  mfd_status r = from_hip(mfd::walk_scratch(&ws), "mfd_verify_walk_noalloc scratch lookup");
+  if (r != MFD_OK) return r;
+  return from_hip(mfd::launch_verify_walk(target_logits, dtype == MFD_BF16, N, Bp1, V, L, node_token, parent, depth,
+                                          n_nodes, temperature, seed, tau, out_tokens, path_nodes, status, ws, stream),
+                  "mfd_verify_walk_noalloc launch");
 }
 
 mfd_status mfd_covered_mass(const void* target_logits, mfd_dtype dtype, int N, int Bp1, int V,

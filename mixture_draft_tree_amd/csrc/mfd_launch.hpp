@@ -44,6 +44,10 @@ hipError_t launch_tree_mask(const int32_t* parent, const int32_t* depth, const i
                             uint8_t* dense_mask, hipStream_t stream);
 
 size_t walk_ws_bytes(int N);
+// The walk's built-in workspace (mfd_verify_walk_noalloc): its size, and its
+// device address on the current device (looked up once per device).
+size_t walk_scratch_bytes();
+hipError_t walk_scratch(void** out);
 
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 

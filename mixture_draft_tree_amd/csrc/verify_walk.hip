@@ -34,10 +34,49 @@
 // maximum.
 #include <math.h>
 
+#include <mutex>
+
 #include "mfd_device.hpp"
 #include "mfd_launch.hpp"
 
 namespace mfd {
+
+// Walk workspace of mfd_verify_walk_noalloc, for callers that cannot
+// allocate: one copy per GPU, held until the process ends.  Host code never
+// uses this name as an address: it is a host-side stand-in, and a kernel
+// handed it would fault.  The device address comes from hipGetSymbolAddress,
+// once per device, below.
+constexpr size_t kWalkScratchBytes = size_t(2) << 20;
+static __device__ __align__(256) unsigned char scratch[kWalkScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+}  // namespace
+
+size_t walk_scratch_bytes() { return kWalkScratchBytes; }
+
+hipError_t walk_scratch(void** out) {
+  *out = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // this device's copy (the device is current)
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return hipSuccess;
+}
+
 namespace {
 
 constexpr int kWalkThreads = 256;

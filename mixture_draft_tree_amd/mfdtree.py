@@ -34,7 +34,7 @@ EXPORTED = ["mfd_last_error", "mfd_version", "mfd_workspace_size", "mfd_logsoftm
             "mfd_verify_walk", "mfd_covered_mass", "mfd_chimera_count", "mfd_logsoftmax_topk_modes",
             "mfd_mixture_threshold_modes", "mfd_tree_build_modes", "mfd_stream_read",
             "mfd_lmhead_logsoftmax_topk", "mfd_lmhead_logsoftmax_topk_mapped",
-            "mfd_lmhead_packed_size", "mfd_lmhead_pack_weight"]
+            "mfd_lmhead_packed_size", "mfd_lmhead_pack_weight", "mfd_verify_walk_noalloc"]
 
 _p = ctypes.c_void_p
 _i = ctypes.c_int
@@ -81,6 +81,8 @@ _lib.mfd_chimera_count.restype = _i
 _lib.mfd_chimera_count.argtypes = [_p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p]
 _lib.mfd_verify_walk.restype = _i
 _lib.mfd_verify_walk.argtypes = [_p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]
+_lib.mfd_verify_walk_noalloc.restype = _i
+_lib.mfd_verify_walk_noalloc.argtypes = [_p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]
 
 
 class MfdError(RuntimeError):
@@ -375,6 +377,31 @@ def mfd_verify_walk(target_logits, L, node_token, parent, depth, n_nodes, temper
                                 _ptr(parent), _ptr(depth), _ptr(n_nodes), _ptr(temperature), _ptr(seed), _ptr(tau),
                                 _ptr(out_tokens), _ptr(path_nodes), _ptr(status), _ptr(ws), ws_bytes,
                                 _stream_handle(stream)), "mfd_verify_walk")
+
+
+WALK_NOALLOC_MAX_TREES = 1347
+
+
+def mfd_verify_walk_noalloc(target_logits, L, node_token, parent, depth, n_nodes, temperature, seed, tau,
+                            out_tokens, path_nodes, status=None, stream=None):
+    """mfd_verify_walk on the library's built-in workspace (no workspace argument,
+    no allocation); at most WALK_NOALLOC_MAX_TREES trees, calls on one GPU must not overlap."""
+    if target_logits.dim() != 3 or not target_logits.is_contiguous() or target_logits.device.type != "cuda":
+        raise ValueError("target_logits must be a contiguous [N, B+1, V] GPU tensor")
+    N, Bp1, V = target_logits.shape
+    for name, t in (("node_token", node_token), ("parent", parent), ("depth", depth)):
+        _want(t, name, torch.int32, (N, Bp1))
+    _want(n_nodes, "n_nodes", torch.int32, (N,))
+    _want(temperature, "temperature", torch.float32, (N,))
+    _want(seed, "seed", torch.int64, (N,))
+    _want(tau, "tau", torch.int32, (N,))
+    _want(out_tokens, "out_tokens", torch.int32, (N, L + 1))
+    _want(path_nodes, "path_nodes", torch.int32, (N, L + 1))
+    _want(status, "status", torch.int32, (N,), optional=True)
+    _check(_lib.mfd_verify_walk_noalloc(_ptr(target_logits), _dtype_code(target_logits), N, Bp1, V, L,
+                                        _ptr(node_token), _ptr(parent), _ptr(depth), _ptr(n_nodes),
+                                        _ptr(temperature), _ptr(seed), _ptr(tau), _ptr(out_tokens), _ptr(path_nodes),
+                                        _ptr(status), _stream_handle(stream)), "mfd_verify_walk_noalloc")
 
 
 def covered_mass_workspace(N: int, Bp1: int, device="cuda") -> torch.Tensor:

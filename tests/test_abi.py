@@ -158,6 +158,24 @@ def test_mask_and_walk_reject():
     assert M._lib.mfd_verify_walk(*args) == M.MFD_ERR_WORKSPACE  # no workspace
 
 
+def test_walk_noalloc_limit_and_rejects():
+    """The built-in walk workspace holds 2 MiB: 1347 trees fit, 1348 do not, and
+    the larger call is refused before anything touches a device."""
+    assert M.workspace_size(M.MFD_OP_VERIFY_WALK, M.WALK_NOALLOC_MAX_TREES, 1, 1, 1, 0) <= 2 << 20
+    assert M.workspace_size(M.MFD_OP_VERIFY_WALK, M.WALK_NOALLOC_MAX_TREES + 1, 1, 1, 1, 0) > 2 << 20
+    args = [FAKE, M.MFD_F32, M.WALK_NOALLOC_MAX_TREES + 1, 9, 16, 4] + [FAKE] * 9 + [None, None]
+    assert M._lib.mfd_verify_walk_noalloc(*args) == M.MFD_ERR_WORKSPACE
+    assert f"N <= {M.WALK_NOALLOC_MAX_TREES}" in M.last_error()
+    bad = list(args)
+    bad[1] = 5
+    assert M._lib.mfd_verify_walk_noalloc(*bad) == M.MFD_ERR_DTYPE
+    bad = list(args)
+    bad[6] = None
+    assert M._lib.mfd_verify_walk_noalloc(*bad) == M.MFD_ERR_INVALID_ARG
+    zero = [None, M.MFD_F32, 0, 9, 16, 4] + [None] * 9 + [None, None]
+    assert M._lib.mfd_verify_walk_noalloc(*zero) == M.MFD_OK
+
+
 def test_binding_checks_shapes_on_cpu_tensors():
     import torch
     x = torch.zeros((1, 2, 3, 16), dtype=torch.float32)
