@@ -69,7 +69,18 @@
 extern "C" {
 #endif
 
-typedef enum mfd_status {
+/* Enumerations are passed as int.  A C caller may pass any int value (a
+ * value that is not an enumerator is rejected with an error); in C++ the
+ * types therefore have int as their fixed underlying type, so every int is
+ * a value of the type there too (without it, only the enumerators' range
+ * would be). */
+#ifdef __cplusplus
+#define MFD_ENUM_BASE : int
+#else
+#define MFD_ENUM_BASE
+#endif
+
+typedef enum mfd_status MFD_ENUM_BASE {
   MFD_OK = 0,
   MFD_ERR_INVALID_ARG = 1, /* a size, pointer or flag is out of range */
   MFD_ERR_DTYPE = 2,       /* unsupported element type */
@@ -77,9 +88,9 @@ typedef enum mfd_status {
   MFD_ERR_DEVICE = 4       /* the HIP runtime refused a launch or query */
 } mfd_status;
 
-typedef enum mfd_dtype { MFD_BF16 = 0, MFD_F32 = 1 } mfd_dtype;
+typedef enum mfd_dtype MFD_ENUM_BASE { MFD_BF16 = 0, MFD_F32 = 1 } mfd_dtype;
 
-typedef enum mfd_op {
+typedef enum mfd_op MFD_ENUM_BASE {
   MFD_OP_LOGSOFTMAX_TOPK = 0,
   MFD_OP_MIXTURE_THRESHOLD = 1,
   MFD_OP_TREE_BUILD = 2,
@@ -245,7 +256,7 @@ mfd_status mfd_tree_build_modes(const int32_t* topk_id, const float* topk_raw, c
                                 int32_t* best_mode, int32_t* n_nodes, int32_t* status,
                                 void* ws, size_t ws_bytes, hipStream_t stream);
 
-typedef enum mfd_head_layout { MFD_HEAD_ROWS = 0, MFD_HEAD_PACKED = 1 } mfd_head_layout;
+typedef enum mfd_head_layout MFD_ENUM_BASE { MFD_HEAD_ROWS = 0, MFD_HEAD_PACKED = 1 } mfd_head_layout;
 
 /*
  * Packed LM head for the fused calls (a one-time re-layout of the weights,

@@ -63,6 +63,7 @@ def build(jobs: int = 8) -> str:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB)
     build_c_smoke()
+    build_hostsan(jobs)
     return LIB
 
 
@@ -82,6 +83,53 @@ def build_c_smoke() -> None:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"C smoke build failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+
+
+HOSTSAN_DIR = os.path.join(ROOT, "tests", "c", "hostsan")
+# Host code only: each sanitizer flag goes to the host compilation (device
+# code is built as in the library proper).
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def _compile_hostsan(src: str) -> str:
+    obj = os.path.join(HOSTSAN_DIR, os.path.basename(src) + ".o")
+    flags = [f for f in COMMON if f != "-O3"] + ["-O1", "-g"] + HOST_SANITIZE
+    if src.endswith(".cpp"):
+        flags = ["-O1", "-g", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"), "-Wall"] + HOST_SANITIZE
+    cmd = [hipcc()] + flags + ["-c", os.path.join(CSRC, src), "-o", obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    return obj
+
+
+def build_hostsan(jobs: int = 8) -> None:
+    """The library with AddressSanitizer and UndefinedBehaviorSanitizer on its
+    host code, and the plain-C caller built with both, under tests/c/hostsan/.
+    Test infrastructure: the CPU tests run the caller's argument and workspace
+    checks through it."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        return
+    os.makedirs(HOSTSAN_DIR, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(_compile_hostsan, SOURCES))
+    lib = os.path.join(HOSTSAN_DIR, "libmfdtree.so")
+    cmd = [hipcc(), "-shared", f"--offload-arch={ARCH}"] + HOST_SANITIZE + ["-o", lib] + objs
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cmd = [clang, "-std=c11", "-O1", "-g", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer",
+           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(rocm, "include"), C_SMOKE_SRC,
+           "-L", HOSTSAN_DIR, "-lmfdtree", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN", "-Wl,-rpath," + os.path.join(rocm, "lib"),
+           "-o", os.path.join(HOSTSAN_DIR, "abi_smoke")]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"sanitized C caller build failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
 
 
 def main() -> None:

@@ -35,33 +35,167 @@ static void expect(int cond, const char* what) {
 
 static int cpu_checks(void) {
   size_t b = 0;
+  void* fake = (void*)(uintptr_t)0x100000; /* rejected before any launch: never dereferenced */
+  void* odd = (void*)(uintptr_t)0x100004;  /* 4-byte aligned only */
   expect(strstr(mfd_version(), "gfx950") != NULL, "version names gfx950");
+
+  /* workspace sizes */
   expect(mfd_workspace_size(MFD_OP_TREE_BUILD, 64, 8, 15, 151936, 256, &b) == MFD_OK && b > 0,
          "tree workspace for 64 trees");
   const size_t many = b;
   expect(mfd_workspace_size(MFD_OP_TREE_BUILD, 1, 8, 15, 151936, 256, &b) == MFD_OK && 64 * b == many,
          "tree workspace is per tree");
+  expect(mfd_workspace_size(MFD_OP_MIXTURE_THRESHOLD, 64, 8, 15, 151936, 256, &b) == MFD_OK && b == many,
+         "threshold and build share the tree workspace");
   expect(mfd_workspace_size(MFD_OP_LOGSOFTMAX_TOPK, 64, 8, 15, 151936, 256, &b) == MFD_OK && b == 0,
          "logits pass needs no workspace");
-  expect(mfd_workspace_size(MFD_OP_VERIFY_WALK, 64, 8, 15, 151936, 256, &b) == MFD_OK && b > 0,
-         "walk workspace");
+  expect(mfd_workspace_size(MFD_OP_TREE_MASK, 64, 8, 15, 151936, 256, &b) == MFD_OK && b == 0,
+         "mask needs no workspace");
+  expect(mfd_workspace_size(MFD_OP_VERIFY_WALK, 64, 8, 15, 151936, 256, &b) == MFD_OK && b > 0, "walk workspace");
+  expect(mfd_workspace_size(MFD_OP_VERIFY_WALK, 0, 8, 15, 151936, 256, &b) == MFD_OK && b == 0, "no trees, no bytes");
+  expect(mfd_workspace_size(MFD_OP_COVERED_MASS, 64, 0, 0, 0, 256, &b) == MFD_OK && b > 0, "covered-mass workspace");
   expect(mfd_workspace_size(MFD_OP_LMHEAD_TOPK, 1, 8, 15, 151936, 256, &b) == MFD_OK && b > 0,
          "fused LM-head workspace");
   expect(mfd_workspace_size(MFD_OP_TREE_BUILD, 1, 33, 15, 100, 8, &b) == MFD_ERR_INVALID_ARG &&
              strstr(mfd_last_error(), "K must be") != NULL,
          "K = 33 rejected with a message");
-  /* rejected before any launch: never dereferenced */
-  void* fake = (void*)(uintptr_t)0x100000;
+  expect(mfd_workspace_size((mfd_op)99, 1, 8, 15, 100, 8, &b) == MFD_ERR_INVALID_ARG, "unknown op rejected");
+  expect(mfd_workspace_size((mfd_op)-3, 1, 8, 15, 100, 8, &b) == MFD_ERR_INVALID_ARG, "negative op rejected");
+  expect(mfd_workspace_size(MFD_OP_VERIFY_WALK, -1, 8, 15, 100, 8, &b) == MFD_ERR_INVALID_ARG, "N < 0 rejected");
+  expect(mfd_workspace_size(MFD_OP_TREE_BUILD, 1, 8, 15, 100, 8, NULL) == MFD_ERR_INVALID_ARG, "NULL bytes rejected");
+  expect(mfd_workspace_size(MFD_OP_LMHEAD_TOPK, 1, 8, 15, 151936, 4096, &b) == MFD_ERR_INVALID_ARG,
+         "fused LM head: k above 2048 rejected");
+  expect(mfd_workspace_size(MFD_OP_TREE_BUILD, 1, 8, 15, 100, 8, &b) == MFD_OK && mfd_last_error()[0] == 0,
+         "a successful call clears the message");
+
+  /* logits pass */
   expect(mfd_logsoftmax_topk(fake, MFD_BF16, 1, 8, 15, 1000, 2049, fake, fake, fake, NULL, NULL, NULL, 0, 0) ==
              MFD_ERR_INVALID_ARG,
          "k > 2048 rejected");
+  expect(mfd_logsoftmax_topk(fake, MFD_BF16, 1, 8, 15, 100, 101, fake, fake, fake, NULL, NULL, NULL, 0, 0) ==
+             MFD_ERR_INVALID_ARG,
+         "k > V rejected");
   expect(mfd_logsoftmax_topk(fake, (mfd_dtype)7, 1, 8, 15, 1000, 8, fake, fake, fake, NULL, NULL, NULL, 0, 0) ==
              MFD_ERR_DTYPE,
          "unknown dtype rejected");
+  expect(mfd_logsoftmax_topk(fake, (mfd_dtype)-1, 1, 8, 15, 1000, 8, fake, fake, fake, NULL, NULL, NULL, 0, 0) ==
+             MFD_ERR_DTYPE,
+         "negative dtype rejected");
+  expect(mfd_logsoftmax_topk(fake, MFD_BF16, 1, 8, 15, 1000, 8, NULL, fake, fake, NULL, NULL, NULL, 0, 0) ==
+             MFD_ERR_INVALID_ARG,
+         "NULL lse rejected");
+  expect(mfd_logsoftmax_topk((void*)(uintptr_t)0x100001, MFD_BF16, 1, 8, 15, 1000, 8, fake, fake, fake, NULL, NULL,
+                             NULL, 0, 0) == MFD_ERR_INVALID_ARG,
+         "misaligned logits rejected");
+  expect(mfd_logsoftmax_topk(fake, MFD_BF16, 1, 8, 0, 1000, 8, fake, fake, fake, NULL, NULL, NULL, 0, 0) ==
+             MFD_ERR_INVALID_ARG,
+         "L = 0 rejected");
+  expect(mfd_logsoftmax_topk(fake, MFD_BF16, 1, 8, 15, 1 << 20, 8, fake, fake, fake, NULL, NULL, NULL, 0, 0) ==
+             MFD_ERR_INVALID_ARG,
+         "V = 2^20 rejected");
+  expect(mfd_logsoftmax_topk(NULL, MFD_BF16, 0, 8, 15, 1000, 8, NULL, NULL, NULL, NULL, NULL, NULL, 0, 0) == MFD_OK,
+         "logits pass: N = 0 is a no-op");
+  expect(mfd_logsoftmax_topk_mapped(fake, MFD_BF16, 1, 8, 15, 1000, fake, 999, 8, fake, fake, fake, NULL, NULL, 0) ==
+             MFD_ERR_INVALID_ARG,
+         "mapped: V_full < V rejected");
+  expect(mfd_logsoftmax_topk_mapped(fake, MFD_BF16, 1, 8, 15, 1000, NULL, 2000, 8, fake, fake, fake, NULL, NULL, 0) ==
+             MFD_ERR_INVALID_ARG,
+         "mapped: NULL map rejected");
+  expect(mfd_logsoftmax_topk_modes(fake, MFD_BF16, 1, 8, 15, 1000, NULL, 8, fake, fake, fake, NULL, NULL, 0) ==
+             MFD_ERR_INVALID_ARG,
+         "modes: NULL modes rejected");
+
+  /* cut-off and tree */
   expect(mfd_mixture_threshold(fake, fake, fake, 1, 8, 15, 256, 256, fake, fake, NULL, NULL, fake, 16, 0) ==
              MFD_ERR_WORKSPACE,
          "small workspace rejected");
+  expect(mfd_mixture_threshold(fake, fake, fake, 1, 8, 15, 256, 256, fake, fake, NULL, NULL, NULL, 1 << 30, 0) ==
+             MFD_ERR_WORKSPACE,
+         "NULL workspace rejected");
+  expect(mfd_mixture_threshold(fake, fake, fake, 1, 17, 15, 1024, 1024, fake, fake, NULL, NULL, fake, 1 << 30, 0) ==
+             MFD_ERR_INVALID_ARG,
+         "K*k > 16384 rejected");
+  expect(mfd_mixture_threshold(fake, fake, fake, 1, 8, 15, 256, 16384, fake, fake, NULL, NULL, fake, 1 << 30, 0) ==
+             MFD_ERR_INVALID_ARG,
+         "B > 16383 rejected");
+  expect(mfd_mixture_threshold(fake, fake, fake, 1, 8, 15, 256, 256, NULL, fake, NULL, NULL, fake, 1 << 30, 0) ==
+             MFD_ERR_INVALID_ARG,
+         "NULL cutoff rejected");
+  expect(mfd_mixture_threshold_modes(fake, fake, fake, 1, 8, 15, 256, 256, NULL, fake, fake, NULL, NULL, fake,
+                                     1 << 30, 0) == MFD_ERR_INVALID_ARG,
+         "threshold modes: NULL modes rejected");
+  expect(mfd_tree_build(fake, fake, fake, fake, fake, fake, 1, 8, 15, 256, 256, fake, fake, fake, fake, fake, NULL,
+                        NULL, fake, 1 << 30, 0) == MFD_ERR_INVALID_ARG &&
+             strstr(mfd_last_error(), "n_nodes") != NULL,
+         "NULL n_nodes rejected with its name");
+  expect(mfd_tree_build_modes(fake, fake, fake, fake, fake, fake, 1, 8, 15, 256, 256, NULL, fake, fake, fake, fake,
+                              fake, fake, NULL, fake, 1 << 30, 0) == MFD_ERR_INVALID_ARG,
+         "build modes: NULL modes rejected");
+  expect(mfd_tree_build(NULL, NULL, NULL, NULL, NULL, NULL, 0, 8, 15, 256, 256, NULL, NULL, NULL, NULL, NULL, NULL,
+                        NULL, NULL, 0, 0) == MFD_OK,
+         "build: N = 0 is a no-op");
+
+  /* mask */
   expect(mfd_tree_mask(NULL, NULL, NULL, NULL, 0, 9, NULL, NULL, NULL, 0) == MFD_OK, "N = 0 is a no-op");
+  expect(mfd_tree_mask(fake, fake, fake, fake, 1, 0, fake, fake, NULL, 0) == MFD_ERR_INVALID_ARG, "Bp1 = 0 rejected");
+  expect(mfd_tree_mask(fake, fake, fake, NULL, 1, 9, fake, fake, NULL, 0) == MFD_ERR_INVALID_ARG,
+         "NULL pos_base rejected");
+
+  /* walk */
+  expect(mfd_verify_walk(fake, (mfd_dtype)5, 1, 9, 16, 4, fake, fake, fake, fake, fake, fake, fake, fake, fake, NULL,
+                         NULL, 0, 0) == MFD_ERR_DTYPE,
+         "walk: unknown dtype rejected");
+  expect(mfd_verify_walk(fake, MFD_F32, 1, 9, 16, 0, fake, fake, fake, fake, fake, fake, fake, fake, fake, NULL, NULL,
+                         0, 0) == MFD_ERR_INVALID_ARG,
+         "walk: L = 0 rejected");
+  expect(mfd_verify_walk(fake, MFD_F32, 1, 9, 16, 4, NULL, fake, fake, fake, fake, fake, fake, fake, fake, NULL, NULL,
+                         0, 0) == MFD_ERR_INVALID_ARG,
+         "walk: NULL node_token rejected");
+  expect(mfd_verify_walk(fake, MFD_F32, 1, 9, 16, 4, fake, fake, fake, fake, fake, fake, fake, fake, fake, NULL, NULL,
+                         0, 0) == MFD_ERR_WORKSPACE,
+         "walk: missing workspace rejected");
+  expect(mfd_verify_walk(fake, MFD_F32, 1, 9, 16, 4, fake, fake, fake, fake, fake, fake, fake, fake, fake, NULL, odd,
+                         1 << 20, 0) == MFD_ERR_INVALID_ARG,
+         "walk: misaligned workspace rejected");
+  expect(mfd_verify_walk_noalloc(fake, MFD_F32, 1348, 9, 16, 4, fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                                 NULL, 0) == MFD_ERR_WORKSPACE &&
+             strstr(mfd_last_error(), "N <= 1347") != NULL,
+         "walk without workspace: 1348 trees rejected with the limit");
+  expect(mfd_verify_walk_noalloc(NULL, MFD_F32, 0, 9, 16, 4, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL,
+                                 NULL, 0) == MFD_OK,
+         "walk without workspace: N = 0 is a no-op");
+
+  /* diagnostics and the streaming reference */
+  expect(mfd_covered_mass(fake, MFD_F32, 65536, 9, 16, fake, fake, fake, fake, fake, NULL, fake, 1 << 30, 0) ==
+             MFD_ERR_INVALID_ARG,
+         "covered mass: N > 65535 rejected");
+  expect(mfd_covered_mass(fake, MFD_F32, 2, 9, 16, fake, fake, fake, fake, fake, NULL, NULL, 0, 0) ==
+             MFD_ERR_WORKSPACE,
+         "covered mass: missing workspace rejected");
+  expect(mfd_chimera_count(fake, fake, fake, fake, 1, 9, 0, fake, fake, fake, 0) == MFD_ERR_INVALID_ARG,
+         "chimera count: L = 0 rejected");
+  expect(mfd_chimera_count(NULL, NULL, NULL, NULL, 0, 9, 4, NULL, NULL, NULL, 0) == MFD_OK,
+         "chimera count: N = 0 is a no-op");
+  expect(mfd_stream_read(fake, 17, fake, 0) == MFD_ERR_INVALID_ARG, "stream read: ragged size rejected");
+  expect(mfd_stream_read(odd, 32, fake, 0) == MFD_ERR_INVALID_ARG, "stream read: misaligned buffer rejected");
+
+  /* fused LM head */
+  expect(mfd_lmhead_packed_size(151936, 2560, &b) == MFD_OK && b == (size_t)151936 * 2560 * 2 + (size_t)128 * 2560 * 2,
+         "packed head size: rows padded to 256");
+  expect(mfd_lmhead_packed_size(1000, 100, &b) == MFD_ERR_INVALID_ARG, "packed head: D not a multiple of 64");
+  expect(mfd_lmhead_pack_weight(fake, 1000, 128, fake, 16, 0) == MFD_ERR_INVALID_ARG, "pack: small output rejected");
+  expect(mfd_lmhead_logsoftmax_topk(fake, fake, (mfd_head_layout)5, 1, 8, 15, 128, 1000, 8, fake, fake, fake, NULL,
+                                    NULL, fake, 1 << 30, 0) == MFD_ERR_INVALID_ARG,
+         "fused head: unknown layout rejected");
+  expect(mfd_lmhead_logsoftmax_topk(fake, fake, MFD_HEAD_ROWS, 1, 8, 15, 100, 1000, 8, fake, fake, fake, NULL, NULL,
+                                    fake, 1 << 30, 0) == MFD_ERR_INVALID_ARG,
+         "fused head: D not a multiple of 64 rejected");
+  expect(mfd_lmhead_logsoftmax_topk(fake, fake, MFD_HEAD_ROWS, 1, 8, 15, 128, 1000, 8, fake, fake, fake, NULL, NULL,
+                                    fake, 16, 0) == MFD_ERR_WORKSPACE,
+         "fused head: small workspace rejected");
+  expect(mfd_lmhead_logsoftmax_topk_mapped(fake, fake, MFD_HEAD_ROWS, fake, 999, 1, 8, 15, 128, 1000, 8, fake, fake,
+                                           fake, NULL, NULL, fake, 1 << 30, 0) == MFD_ERR_INVALID_ARG,
+         "fused head mapped: V_full < V rejected");
   return fails == 0 ? 0 : 1;
 }
 

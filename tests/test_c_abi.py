@@ -26,6 +26,24 @@ def test_c_caller_cpu_checks():
     assert "abi_smoke cpu: ok" in r.stdout
 
 
+SAN_BIN = os.path.join(ROOT, "tests", "c", "hostsan", "abi_smoke")
+
+
+@pytest.mark.skipif(not os.path.exists(SAN_BIN), reason="tests/c/hostsan not built (run build())")
+def test_c_caller_cpu_checks_under_sanitizers():
+    """The host layer (argument checks, workspace sizes, error text) driven from
+    C with AddressSanitizer and UndefinedBehaviorSanitizer on the library's host
+    code and on the caller: any finding aborts the run."""
+    env = dict(os.environ)
+    env["ASAN_OPTIONS"] = "detect_leaks=1:halt_on_error=1:abort_on_error=0"
+    env["UBSAN_OPTIONS"] = "print_stacktrace=1:halt_on_error=1"
+    env.pop("LD_PRELOAD", None)
+    r = subprocess.run([SAN_BIN, "cpu"], capture_output=True, text=True, timeout=120, env=env)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "abi_smoke cpu: ok" in r.stdout
+    assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr, r.stderr
+
+
 @needs_bin
 @pytest.mark.gpu
 @pytest.mark.own_process_gpu
