@@ -76,7 +76,8 @@ def parse():
                     choices=["batched", "single", "stress", "deep", "batched_deep", "subset", "batched_subset",
                              "batched_modes"])
     ap.add_argument("--cpu-baseline-trees", type=int, default=16,
-                    help="trees of the workload the fp64 oracle is timed on, one process per core (0 = skip)")
+                    help="trees of the workload the fp64 oracle is timed on, at least one per core, one process "
+                         "per core (0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-gib", type=int, default=0,
                     help="after the run, copy a buffer of this many GiB device to device: a plain copy of "
@@ -200,17 +201,43 @@ def _oracle_worker(name, base_seed, trees, barrier, results):
         O.tree_mask(tr["parent"], tr["depth"], tr["n_nodes"], pos, w.B + 1)
         O.verify_walk(tr["node_token"], tr["parent"], tr["depth"], tr["n_nodes"], R, T, seed, w.L)
         per_tree.append(time.perf_counter() - t1)
-    results.put((t0, time.perf_counter(), per_tree))
+    t_end = time.perf_counter()
+    # untimed: whether each tree's node set is decided by exact comparisons
+    # (cut-off band of 1e-4, the score tolerance)
+    excluded = 0
+    for x, *_ in work:
+        excluded += 0 if O.band_is_exact(x, O.mixture_select_heap(x, w.B, band=1e-4), 1e-4) else 1
+    results.put((t0, t_end, per_tree, excluded))
 
 
-def cpu_baseline(name: str, base_seed: int, n_trees: int, max_workers: int = 16):
+def host_cpu_model() -> str:
+    """The host's CPU model as lscpu names it (falls back to /proc/cpuinfo)."""
+    import subprocess
+    try:
+        r = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20)
+        for ln in r.stdout.splitlines():
+            if ln.strip().startswith("Model name:"):
+                return ln.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            return next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        return ""
+
+
+def cpu_baseline(name: str, base_seed: int, n_trees: int):
     """Time the fp64 oracle end to end (log-softmax, ranks, heap, layout, mask,
-    walk) on trees 0 .. n_trees-1 of the workload, spread over a pool of this
-    host's cores (one single-threaded process per core, at most max_workers).
-    Runs before the GPU is touched, so the workers are plain forks."""
+    walk) on trees 0 .. n_trees-1 of the workload, spread over every core this
+    process may run on (one single-threaded process per core; n_trees is raised
+    to the core count so each core gets at least one tree).  Runs before the
+    GPU is touched, so the workers are plain forks."""
     import multiprocessing as mp
 
-    cores = max(1, min(n_trees, max_workers, len(os.sched_getaffinity(0))))
+    avail = len(os.sched_getaffinity(0))
+    n_trees = max(n_trees, avail)
+    cores = max(1, min(n_trees, avail))
     ctx = mp.get_context("fork")
     barrier = ctx.Barrier(cores)
     results = ctx.Queue()
@@ -225,16 +252,17 @@ def cpu_baseline(name: str, base_seed: int, n_trees: int, max_workers: int = 16)
     assert all(pr.exitcode == 0 for pr in procs), [pr.exitcode for pr in procs]
     wall = max(o[1] for o in out) - min(o[0] for o in out)
     per_tree = sorted(t for o in out for t in o[2])
-    model = ""
-    try:
-        with open("/proc/cpuinfo") as f:
-            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
-    except OSError:
-        pass
+    excluded = sum(o[3] for o in out)
     return {"value": n_trees / wall, "unit": "trees/s", "cores": cores, "kind": "oracle",
             "sample": f"{n_trees} trees of the {name} workload, full oracle path, {cores} single-threaded "
-                      f"processes, {wall:.1f} s wall, {sum(per_tree):.1f} s of CPU work",
-            "per_tree_s_one_core_median": statistics.median(per_tree), "host_cpu": model}
+                      f"processes (one per core this process may use), {wall:.1f} s wall, "
+                      f"{sum(per_tree):.1f} s of CPU work",
+            "per_tree_s_one_core_median": statistics.median(per_tree), "host_cpu": host_cpu_model(),
+            "band_excluded_trees": {"trees": n_trees, "excluded": excluded,
+                                    "reason": "node set not decided by exact comparisons: a selected and an "
+                                              "unselected prefix within 1e-4 of the cut-off differ in best mode "
+                                              "or depth, or have a runner-up mode within 1e-4; such trees are "
+                                              "checked for validity, not array for array"}}
 
 
 def run_steps(P, logits, anchor, pos, R, temps, seeds, steps, warmup, stream):
@@ -317,12 +345,24 @@ def setup(name, seed, dev):
 
 
 def single_tree_latency(seed, steps, stream, name="single"):
-    """Mean time of one whole step on a one-tree workload (N=1), ms."""
+    """One whole step on a one-tree workload (N=1): mean ms per step (eager
+    launches, events between the calls), the mean of each stage, and the mean
+    of a HIP-graph replay of the step."""
     w, N, P, logits, anchor, pos, temps, seeds, R = setup(name, seed, "cuda")
-    total, _ = run_steps(P, logits, anchor, pos, R, temps, seeds, steps, 3, stream)
+    total, ev = run_steps(P, logits, anchor, pos, R, temps, seeds, steps, 3, stream)
     status = P.buf.status.cpu()
     assert int(status.abs().sum()) == 0, f"per-tree status flags set ({name}): {status.tolist()}"
-    return total / steps
+    stages = {nm: statistics.mean(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps))
+              for i, nm in enumerate(STAGES)}
+    g = capture_step(P, logits, anchor, pos, R, temps, seeds)
+    graph_ms, _ = graph_steps(g, steps, 3, stream)
+    del g
+    status = P.buf.status.cpu()
+    assert int(status.abs().sum()) == 0, f"per-tree status flags set ({name}): {status.tolist()}"
+    return {"workload": f"{name}: 1 tree, K={w.K}, L={w.L}, V={w.V}, B={w.B}", "ms": graph_ms,
+            "eager_ms": total / steps, "stages_ms": stages, "tau": int(P.buf.tau[0]),
+            "n_nodes": int(P.buf.n_nodes[0]),
+            "logits_GBps": w.K * w.L * logits.shape[-1] * logits.element_size() / (stages["logsoftmax_topk"] * 1e-3) / 1e9}
 
 
 def read_ceiling(buf, reps, stream):
@@ -366,6 +406,28 @@ def covered_mass_stats(P, R, temps, stream, reps=5):
     torch.cuda.synchronize()
     return {"covered_mass_ms": e0.elapsed_time(e1) / reps, "mean_covered_mass": float(mass.mean()),
             "mean_accepted_walk": float((P.buf.tau - 1).float().mean())}
+
+
+def tree_stats(P) -> dict:
+    """Shape of the built trees and walks: tau and depth histograms, per-mode
+    keep counts at the cut-off (the per-mode keeps of the common cut-off)."""
+    tau = P.buf.tau.cpu()
+    nn = P.buf.n_nodes.cpu()
+    dep = P.buf.depth.cpu()
+    kept = P.buf.per_mode_kept.cpu().to(torch.float64)
+    dh = {}
+    for n in range(dep.shape[0]):
+        for d in dep[n, 1:int(nn[n])].tolist():
+            dh[d] = dh.get(d, 0) + 1
+    th = {}
+    for t in tau.tolist():
+        th[t] = th.get(t, 0) + 1
+    return {"tau_histogram": {str(k): th[k] for k in sorted(th)},
+            "node_depth_histogram": {str(k): dh[k] for k in sorted(dh)},
+            "mean_nodes": float(nn.to(torch.float64).mean()),
+            "per_mode_kept_mean": [round(float(v), 2) for v in kept.mean(0).tolist()],
+            "per_mode_kept_total_mean": float(kept.sum(1).mean()),
+            "n_select_mean": float(P.buf.n_select.cpu().to(torch.float64).mean())}
 
 
 def timed_workload(name, seed, steps, warmup, stream, diagnostics=False):
@@ -452,10 +514,13 @@ def main():
         "tau_mean": float(tau.mean()),
         "diagnostics": diag,
     }
-    if args.latency_steps > 0 and name != "single":
-        out["single_tree_latency_ms"] = single_tree_latency(args.seed, args.latency_steps, stream)
+    out["trees"] = tree_stats(P)
     if args.latency_steps > 0 and name == "batched":
-        out["stress_tree_latency_ms"] = single_tree_latency(args.seed, args.latency_steps, stream, "stress")
+        # one tree at a time (batch size 1, the pages' setting): each stage timed
+        b1 = {nm: single_tree_latency(args.seed, args.latency_steps, stream, nm) for nm in ("single", "deep", "stress")}
+        out["batch1"] = b1
+        out["single_tree_latency_ms"] = b1["single"]["ms"]
+        out["stress_tree_latency_ms"] = b1["stress"]["ms"]
     if args.deep_workload != "none" and name == "batched":
         del P, logits
         dms, dstage, dN, dw, dP, _ = timed_workload(args.deep_workload, args.seed, args.steps, args.warmup, stream,
@@ -473,8 +538,8 @@ def main():
             "eager_ms_per_step": deager,
             "stages_ms": dstage,
             "tau_mean": float(dP.buf.tau.cpu().float().mean()),
-            "single_tree_latency_ms": (single_tree_latency(args.seed, args.latency_steps, stream, "deep")
-                                       if args.latency_steps > 0 else None),
+            "single_tree_latency_ms": out.get("batch1", {}).get("deep", {}).get("ms"),
+            "trees": tree_stats(dP),
             "diagnostics": ddiag,
         }
     if args.subset_workload != "none" and name == "batched":
