@@ -270,7 +270,9 @@ def run_steps(P, logits, anchor, pos, R, temps, seeds, steps, warmup, stream):
     for _ in range(warmup):
         P.step(logits, anchor, pos, R, temps, seeds)
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)] for _ in range(steps)]
+    calls = [lambda: P.logsoftmax_topk(logits), lambda: P.mixture_tree(anchor), lambda: P.tree_mask(pos),
+             lambda: P.verify_walk(R, temps, seeds)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -278,19 +280,33 @@ def run_steps(P, logits, anchor, pos, R, temps, seeds, steps, warmup, stream):
     for s in range(steps):
         e = ev[s]
         e[0].record(stream)
-        P.logsoftmax_topk(logits)
-        e[1].record(stream)
-        P.mixture_threshold()
-        e[2].record(stream)
-        P.tree_build(anchor)
-        e[3].record(stream)
-        P.tree_mask(pos)
-        e[4].record(stream)
-        P.verify_walk(R, temps, seeds)
-        e[5].record(stream)
+        for i, call in enumerate(calls):
+            call()
+            e[i + 1].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     return t_start.elapsed_time(t_end), ev
+
+
+def separate_tree_calls_ms(P, anchor, reps, stream):
+    """The cut-off and the tree as two launches (mfd_mixture_threshold, then
+    mfd_tree_build), for comparison with the one-launch mfd_mixture_tree."""
+    for _ in range(2):
+        P.mixture_threshold()
+        P.tree_build(anchor)
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    thr, bld = 0.0, 0.0
+    for _ in range(reps):
+        e[0].record(stream)
+        P.mixture_threshold()
+        e[1].record(stream)
+        P.tree_build(anchor)
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        thr += e[0].elapsed_time(e[1])
+        bld += e[1].elapsed_time(e[2])
+    return {"mixture_threshold": thr / reps, "tree_build": bld / reps}
 
 
 def capture_step(P, logits, anchor, pos, R, temps, seeds):
@@ -354,6 +370,7 @@ def single_tree_latency(seed, steps, stream, name="single"):
     assert int(status.abs().sum()) == 0, f"per-tree status flags set ({name}): {status.tolist()}"
     stages = {nm: statistics.mean(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps))
               for i, nm in enumerate(STAGES)}
+    stages["separate_threshold_and_build"] = separate_tree_calls_ms(P, anchor, min(steps, 20), stream)
     g = capture_step(P, logits, anchor, pos, R, temps, seeds)
     graph_ms, _ = graph_steps(g, steps, 3, stream)
     del g
@@ -385,7 +402,7 @@ def read_ceiling(buf, reps, stream):
             "GBps": nbytes / (ms * 1e-3) / 1e9, "frac_of_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
-STAGES = ["logsoftmax_topk", "mixture_threshold", "tree_build", "tree_mask", "verify_walk"]
+STAGES = ["logsoftmax_topk", "mixture_tree", "tree_mask", "verify_walk"]
 
 
 def covered_mass_stats(P, R, temps, stream, reps=5):
@@ -436,7 +453,7 @@ def timed_workload(name, seed, steps, warmup, stream, diagnostics=False):
     total_ms, ev = run_steps(P, logits, anchor, pos, R, temps, seeds, steps, warmup, stream)
     stage = {nm: statistics.mean(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps))
              for i, nm in enumerate(STAGES)}
-    per_step = sorted(ev[s][0].elapsed_time(ev[s][5]) for s in range(steps))
+    per_step = sorted(ev[s][0].elapsed_time(ev[s][len(STAGES)]) for s in range(steps))
     q = lambda f: per_step[min(len(per_step) - 1, int(f * len(per_step)))]
     stage["step_ms_percentiles"] = {"p10": q(0.1), "p50": statistics.median(per_step), "p90": q(0.9)}
     status = P.buf.status.cpu()
@@ -451,6 +468,7 @@ def timed_workload(name, seed, steps, warmup, stream, diagnostics=False):
     stage["step_ms_percentiles"] = {"p10": q(0.1), "p50": statistics.median(gper), "p90": q(0.9)}
     status = P.buf.status.cpu()
     assert int(status.abs().sum()) == 0, f"per-tree status flags set ({name}): {status.tolist()}"
+    stage["separate_threshold_and_build"] = separate_tree_calls_ms(P, anchor, min(steps, 20), stream)
     if diagnostics:
         stage["diagnostics"] = covered_mass_stats(P, R, temps, stream)
     return graph_ms, stage, N, w, P, logits
@@ -503,7 +521,8 @@ def main():
                      "read_ceiling": ceiling, "frac_of_read_ceiling": achieved / ceiling["GBps"],
                      "valu_issue_frac": profile_field(SQ_FILE, name, "lsm_valu_issue_frac")},
         "step_ms_percentiles": pcts,
-        "launch": "each step is one replay of a HIP graph holding the five calls; stages_ms are timed on eager "
+        "launch": "each step is one replay of a HIP graph holding the path's calls (logits pass, cut-off and tree "
+                  "in one launch, mask, walk) and a status clear; stages_ms are timed on eager "
                   "launches with events between the calls",
         "eager_ms_per_step": eager_ms,
         "eager_step_ms_percentiles": eager_pcts,

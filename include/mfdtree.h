@@ -10,6 +10,7 @@
  *                          over all prefixes, counting each prefix once.
  *   mfd_tree_build         the prefixes that reach the cut-off, merged into
  *                          one deduplicated tree with ties broken, laid out.
+ *   mfd_mixture_tree       the two calls above from one search, in one launch.
  *   mfd_tree_mask          ancestor mask and position ids for verification.
  *   mfd_verify_walk        the verification walk over the target's per-node
  *                          logits: accepted length tau and the bonus token.
@@ -97,7 +98,8 @@ typedef enum mfd_op MFD_ENUM_BASE {
   MFD_OP_TREE_MASK = 3,
   MFD_OP_VERIFY_WALK = 4,
   MFD_OP_COVERED_MASS = 5,
-  MFD_OP_LMHEAD_TOPK = 6
+  MFD_OP_LMHEAD_TOPK = 6,
+  MFD_OP_MIXTURE_TREE = 7
 } mfd_op;
 
 #define MFD_TREE_NONFINITE 1
@@ -218,6 +220,33 @@ mfd_status mfd_tree_build(const int32_t* topk_id, const float* topk_raw, const d
                           int32_t* node_token, int32_t* parent, int32_t* depth, double* score,
                           int32_t* best_mode, int32_t* n_nodes, int32_t* status,
                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The cut-off and the tree together (project page, step 3: the union of the
+ * per-mode trees is what one merged best-first search produces): the outputs
+ * of mfd_mixture_threshold (cutoff, n_select, per_mode_kept) and of
+ * mfd_tree_build at that cut-off (node_token .. n_nodes), bit for bit, from a
+ * single search in one launch.  The search that finds the cut-off has by then
+ * built every prefix that reaches it, with its best-mode score and best mode,
+ * so the tree is laid out from those nodes instead of being searched for again.
+ * Arguments, layouts, status flags and capacities as for the two calls; the
+ * workspace is theirs (mfd_workspace_size with MFD_OP_MIXTURE_TREE, the same
+ * size).  mfd_mixture_tree_modes: the same over the first K_n = modes[n] modes
+ * of tree n (see the *_modes calls below).
+ */
+mfd_status mfd_mixture_tree(const int32_t* topk_id, const float* topk_raw, const double* lse,
+                            const int32_t* anchor_token, int N, int K, int L, int k, int B,
+                            double* cutoff, int32_t* n_select, int32_t* per_mode_kept,
+                            int32_t* node_token, int32_t* parent, int32_t* depth, double* score,
+                            int32_t* best_mode, int32_t* n_nodes, int32_t* status,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+mfd_status mfd_mixture_tree_modes(const int32_t* topk_id, const float* topk_raw, const double* lse,
+                                  const int32_t* anchor_token, int N, int K, int L, int k, int B,
+                                  const int32_t* modes, double* cutoff, int32_t* n_select,
+                                  int32_t* per_mode_kept, int32_t* node_token, int32_t* parent,
+                                  int32_t* depth, double* score, int32_t* best_mode, int32_t* n_nodes,
+                                  int32_t* status, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Per-request mode count inside one batched launch (project page, "In a

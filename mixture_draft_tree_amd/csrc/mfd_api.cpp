@@ -92,7 +92,8 @@ mfd_status mfd_workspace_size(mfd_op op, int N, int K, int L, int V, int B, size
       return ok();
     }
     case MFD_OP_MIXTURE_THRESHOLD:
-    case MFD_OP_TREE_BUILD: {
+    case MFD_OP_TREE_BUILD:
+    case MFD_OP_MIXTURE_TREE: {
       mfd_status s = check_dims(N, K, L, V);
       if (s != MFD_OK) return s;
       if (B < 0 || B > kMaxB) return fail(MFD_ERR_INVALID_ARG, "B must be in [0, %d] (got %d)", kMaxB, B);
@@ -319,6 +320,58 @@ mfd_status mfd_tree_build_modes(const int32_t* topk_id, const float* topk_raw, c
   return tree_build_impl("mfd_tree_build_modes launch", topk_id, topk_raw, lse, cutoff, n_select, anchor_token, N, K,
                          L, k, B, modes, node_token, parent, depth, score, best_mode, n_nodes, status, ws, ws_bytes,
                          stream);
+}
+
+static mfd_status mixture_tree_impl(const char* call, const int32_t* topk_id, const float* topk_raw,
+                                    const double* lse, const int32_t* anchor_token, int N, int K, int L, int k, int B,
+                                    const int32_t* modes, double* cutoff, int32_t* n_select, int32_t* per_mode_kept,
+                                    int32_t* node_token, int32_t* parent, int32_t* depth, double* score,
+                                    int32_t* best_mode, int32_t* n_nodes, int32_t* status, void* ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+  mfd_status s = check_tree_dims(N, K, L, k, B);
+  if (s != MFD_OK) return s;
+  if (N == 0) return ok();
+  REQUIRE_PTR(topk_id);
+  REQUIRE_PTR(topk_raw);
+  REQUIRE_PTR(lse);
+  REQUIRE_PTR(anchor_token);
+  REQUIRE_PTR(cutoff);
+  REQUIRE_PTR(n_select);
+  REQUIRE_PTR(node_token);
+  REQUIRE_PTR(parent);
+  REQUIRE_PTR(depth);
+  REQUIRE_PTR(score);
+  REQUIRE_PTR(best_mode);
+  REQUIRE_PTR(n_nodes);
+  const size_t need = (size_t)N * mfd::tree_caps(K, L, k, B).ws_bytes_per_tree;
+  if (ws == nullptr || ws_bytes < need)
+    return fail(MFD_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws == nullptr ? (size_t)0 : ws_bytes);
+  return from_hip(mfd::launch_mixture_tree(topk_id, topk_raw, lse, anchor_token, N, K, L, k, B, modes, cutoff,
+                                           n_select, per_mode_kept, node_token, parent, depth, score, best_mode,
+                                           n_nodes, status, ws, stream),
+                  call);
+}
+
+mfd_status mfd_mixture_tree(const int32_t* topk_id, const float* topk_raw, const double* lse,
+                            const int32_t* anchor_token, int N, int K, int L, int k, int B, double* cutoff,
+                            int32_t* n_select, int32_t* per_mode_kept, int32_t* node_token, int32_t* parent,
+                            int32_t* depth, double* score, int32_t* best_mode, int32_t* n_nodes, int32_t* status,
+                            void* ws, size_t ws_bytes, hipStream_t stream) {
+  return mixture_tree_impl("mfd_mixture_tree launch", topk_id, topk_raw, lse, anchor_token, N, K, L, k, B, nullptr,
+                           cutoff, n_select, per_mode_kept, node_token, parent, depth, score, best_mode, n_nodes,
+                           status, ws, ws_bytes, stream);
+}
+
+mfd_status mfd_mixture_tree_modes(const int32_t* topk_id, const float* topk_raw, const double* lse,
+                                  const int32_t* anchor_token, int N, int K, int L, int k, int B,
+                                  const int32_t* modes, double* cutoff, int32_t* n_select, int32_t* per_mode_kept,
+                                  int32_t* node_token, int32_t* parent, int32_t* depth, double* score,
+                                  int32_t* best_mode, int32_t* n_nodes, int32_t* status, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  if (N > 0) REQUIRE_PTR(modes);
+  return mixture_tree_impl("mfd_mixture_tree_modes launch", topk_id, topk_raw, lse, anchor_token, N, K, L, k, B,
+                           modes, cutoff, n_select, per_mode_kept, node_token, parent, depth, score, best_mode,
+                           n_nodes, status, ws, ws_bytes, stream);
 }
 
 mfd_status mfd_tree_mask(const int32_t* parent, const int32_t* depth, const int32_t* n_nodes, const int64_t* pos_base,

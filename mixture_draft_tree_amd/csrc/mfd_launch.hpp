@@ -39,6 +39,13 @@ hipError_t launch_tree_build(const int32_t* topk_id, const float* topk_raw, cons
                              double* score, int32_t* best_mode, int32_t* n_nodes, int32_t* status, void* ws,
                              hipStream_t stream);
 
+// The cut-off and the tree from one search (threshold and build outputs both)
+hipError_t launch_mixture_tree(const int32_t* topk_id, const float* topk_raw, const double* lse, const int32_t* anchor,
+                               int N, int K, int L, int k, int B, const int32_t* modes, double* cutoff,
+                               int32_t* n_select, int32_t* per_mode_kept, int32_t* node_token, int32_t* parent,
+                               int32_t* depth, double* score, int32_t* best_mode, int32_t* n_nodes, int32_t* status,
+                               void* ws, hipStream_t stream);
+
 hipError_t launch_tree_mask(const int32_t* parent, const int32_t* depth, const int32_t* n_nodes,
                             const int64_t* pos_base, int N, int Bp1, uint64_t* mask_words, int64_t* position_ids,
                             uint8_t* dense_mask, hipStream_t stream);

@@ -670,8 +670,17 @@ __device__ void level_search(const TreeArgs& a, const Tree& t, int n, Ctl& ctl, 
   __syncthreads();
 }
 
-template <bool BUILD>
+// What one launch of tree_kernel does: find the cut-off (mfd_mixture_threshold),
+// build the tree at a given cut-off (mfd_tree_build), or both from one search
+// (mfd_mixture_tree).
+enum TreeMode { kThreshold = 0, kBuild = 1, kFused = 2 };
+
+template <int MODE>
 __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
+  // the search raises its threshold as nodes are found (cut-off wanted), and
+  // a tree is laid out (from the same nodes, in the fused mode)
+  constexpr bool kRaise = MODE != kBuild;
+  constexpr bool kEmit = MODE != kThreshold;
   const int n = blockIdx.x;
   const int tid = threadIdx.x;
   const int K = a.K, L = a.L, k = a.k, B = a.B, Lp1 = L + 1;
@@ -679,7 +688,7 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
   uint64_t* keys = reinterpret_cast<uint64_t*>(smem_raw);
   double* norm = reinterpret_cast<double*>(keys + a.sort_cap);
   Ctl& ctl = *reinterpret_cast<Ctl*>(norm + K * Lp1);
-  uint16_t* nk = (!BUILD && a.nk_lds)
+  uint16_t* nk = (kRaise && a.nk_lds)
                      ? reinterpret_cast<uint16_t*>(smem_raw + ((tree_lds_base(a.sort_cap, K, L) + 15) & ~size_t(15)))
                      : nullptr;
   const Tree t = tree_ptrs(a, n);
@@ -733,7 +742,7 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
 
   double cutoff_in = 0.0;
   int nsel_in = 0;
-  if (BUILD) {
+  if (!kRaise) {
     cutoff_in = a.cutoff_in[n];
     nsel_in = a.n_select_in[n];
     if (nsel_in > B) nsel_in = B;
@@ -760,7 +769,7 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
   }
   __syncthreads();
 
-  if (!BUILD && B > 0) {
+  if (kRaise && B > 0) {
     // A tighter start: pool each mode's first kFirstQ depth-1 candidates, give
     // each distinct token the best of its pooled scores, and take (a 16-bit
     // lower bound of) the B-th largest.  Those are B distinct prefixes whose
@@ -818,13 +827,13 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
     }
   }
 
-  level_search<BUILD>(a, t, n, ctl, keys, norm, nk);
+  level_search<!kRaise>(a, t, n, ctl, keys, norm, nk);
 
   const int nc = ctl.node_count;
   const int fail = ctl.fail;
   if (fail && a.status && tid == 0) atomicOr(&a.status[n], MFD_TREE_CAPACITY);
 
-  if (!BUILD) {
+  if (kRaise) {
     // ---------------------------------------------------------- cut-off
     const int total = nc - 1;
     int nsel = 0;
@@ -844,7 +853,15 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
       a.cutoff_out[n] = cut;
       a.n_select_out[n] = nsel;
     }
-    return;
+    if (!kEmit) return;
+    // Fused: the search materialised every prefix with some per-mode score at
+    // or above its running threshold, which never exceeded the cut-off, so
+    // every prefix at or above the cut-off is a node, with all the modes that
+    // reach the cut-off among its entries: its score and best mode are those
+    // the build call would find.  Nodes below the cut-off are never selected.
+    cutoff_in = cut;
+    nsel_in = nsel;
+    __syncthreads();
   }
 
   // ------------------------------------------------------------ tree build
@@ -931,56 +948,37 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
   }
   const int fail2 = ctl.fail;
 
-  // canonical layout: per depth, sort selected nodes by (parent row, token)
+  // Canonical layout.  The search created nodes level by level, and within a
+  // level in ascending (parent node, token) order: a level's children are
+  // sorted by that key before its runs become nodes.  By induction over depth
+  // this is the order (depth, token sequence) of the prefixes -- at depth d
+  // two prefixes compare as their parents do, or by their last token under
+  // one parent -- and it stays so among the selected nodes, since a selected
+  // node's parent is selected.  A selected node's row is therefore one plus
+  // the number of selected nodes created before it: one scan, no sort.
   int base = 1;
   if (!fail2) {
-    for (int d = 1; d <= L; ++d) {
-      const int s0 = ctl.level_start[d], s1 = ctl.level_start[d + 1];
-      if (s1 <= s0) break;
-      const int cnt = block_scan_range(
-          s1 - s0, [&](int i) { return t.node_aux[s0 + i] == 1 ? 1 : 0; },
-          [&](int i, int off, int v) {
-            if (v) {
-              const int node = s0 + i;
-              const int p = t.node_parent[node];
-              const int prow = (p == 0) ? 0 : (t.node_aux[p] - 2);  // rows of depth d-1 are final
-              keys[off] = ((uint64_t)prow << 36) | ((uint64_t)t.node_token[node] << 16) | (uint64_t)(node - s0);
-            }
-          },
-          ctl.scan);
-      if (cnt == 0) break;
-      // position of each key in (parent row, token) order: by direct counting
-      // for up to 2048 keys (all distinct: the low bits hold the node), else
-      // by a bitonic sort
-      const bool small = cnt <= 2 * kNT;
-      if (!small) {
-        const int P = next_pow2(cnt);
-        for (int c = cnt + tid; c < P; c += kNT) keys[c] = ~0ull;
-        __syncthreads();
-        block_sort_keys<kNT>(keys, P);
-      }
-      for (int i = tid; i < cnt; i += kNT) {
-        int pos = i;
-        if (small) {
-          const uint64_t mine = keys[i];
-          pos = 0;
-          for (int r = 0; r < cnt; ++r) pos += keys[r] < mine ? 1 : 0;
-        }
-        const int node = s0 + (int)(keys[i] & 0xFFFFu);
-        const int rowi = base + pos;
-        const int p = t.node_parent[node];
-        const int prow = (p == 0) ? 0 : (t.node_aux[p] - 2);
-        const size_t o = (size_t)n * Bp1 + rowi;
-        a.node_token[o] = t.node_token[node];
-        a.parent[o] = prow;
-        a.depth[o] = d;
-        a.score[o] = t.node_S[node];
-        a.best_mode[o] = t.node_mu[node];
-        t.node_aux[node] = rowi + 2;  // canonical row, offset past the flags
-      }
-      __syncthreads();
-      base += cnt;
+    // node_aux: 1 = selected; after the scan, row + 2 for selected nodes
+    const int cnt = block_scan_range(
+        nc - 1, [&](int i) { return t.node_aux[i + 1] == 1 ? 1 : 0; },
+        [&](int i, int off, int v) {
+          if (v) t.node_aux[i + 1] = off + 3;
+        },
+        ctl.scan);
+    for (int node = 1 + tid; node < nc; node += kNT) {
+      const int aux = t.node_aux[node];
+      if (aux < 3) continue;
+      const int rowi = aux - 2;
+      const int p = t.node_parent[node];
+      const int prow = (p == 0) ? 0 : (t.node_aux[p] - 2);
+      const size_t o = (size_t)n * Bp1 + rowi;
+      a.node_token[o] = t.node_token[node];
+      a.parent[o] = prow;
+      a.depth[o] = t.node_depth[node];
+      a.score[o] = t.node_S[node];
+      a.best_mode[o] = t.node_mu[node];
     }
+    base = 1 + cnt;
   }
   const int rows = fail2 ? 1 : base;
   for (int i = tid; i < Bp1; i += kNT) {
@@ -1026,26 +1024,29 @@ static int tie_cap_for(const TreeCaps& c, int L) {
   return t < 1 ? 1 : t;
 }
 
-static hipError_t launch_tree(bool build, TreeArgs& a, int N, hipStream_t stream) {
+static hipError_t launch_tree(int mode, TreeArgs& a, int N, hipStream_t stream) {
   const TreeCaps c = tree_caps(a.K, a.L, a.k, a.B);
   a.sort_cap = c.sort_cap;
   a.ent_cap = c.ent_cap;
   a.node_cap = c.node_cap;
   a.tie_cap = tie_cap_for(c, a.L);
   a.ws_stride = c.ws_bytes_per_tree;
-  const void* fn = build ? reinterpret_cast<const void*>(&tree_kernel<true>)
-                         : reinterpret_cast<const void*>(&tree_kernel<false>);
-  // the threshold call keeps a 16-bit score key per node in LDS when it fits
+  const void* fn = mode == kBuild  ? reinterpret_cast<const void*>(&tree_kernel<kBuild>)
+                   : mode == kFused ? reinterpret_cast<const void*>(&tree_kernel<kFused>)
+                                    : reinterpret_cast<const void*>(&tree_kernel<kThreshold>);
+  // the searches that raise their threshold keep a 16-bit score key per node
+  // in LDS when it fits
   size_t lds = c.lds_bytes;
   const size_t nk_off = (tree_lds_base(c.sort_cap, a.K, a.L) + 15) & ~size_t(15);
   const size_t nk_end = nk_off + (size_t)c.node_cap * sizeof(uint16_t);
-  a.nk_lds = (!build && nk_end <= kTreeLdsMax) ? 1 : 0;
+  a.nk_lds = (mode != kBuild && nk_end <= kTreeLdsMax) ? 1 : 0;
   if (a.nk_lds && nk_end > lds) lds = nk_end;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   if (N == 0) return hipSuccess;
-  if (build) hipLaunchKernelGGL(tree_kernel<true>, dim3(N), dim3(kNT), lds, stream, a);
-  else hipLaunchKernelGGL(tree_kernel<false>, dim3(N), dim3(kNT), lds, stream, a);
+  if (mode == kBuild) hipLaunchKernelGGL(tree_kernel<kBuild>, dim3(N), dim3(kNT), lds, stream, a);
+  else if (mode == kFused) hipLaunchKernelGGL(tree_kernel<kFused>, dim3(N), dim3(kNT), lds, stream, a);
+  else hipLaunchKernelGGL(tree_kernel<kThreshold>, dim3(N), dim3(kNT), lds, stream, a);
   return hipGetLastError();
 }
 
@@ -1066,7 +1067,7 @@ hipError_t launch_mixture_threshold(const int32_t* topk_id, const float* topk_ra
   a.cutoff_out = cutoff;
   a.n_select_out = n_select;
   a.per_mode_kept = per_mode_kept;
-  return launch_tree(false, a, N, stream);
+  return launch_tree(kThreshold, a, N, stream);
 }
 
 hipError_t launch_tree_build(const int32_t* topk_id, const float* topk_raw, const double* lse, const double* cutoff,
@@ -1094,7 +1095,36 @@ hipError_t launch_tree_build(const int32_t* topk_id, const float* topk_raw, cons
   a.score = score;
   a.best_mode = best_mode;
   a.n_nodes = n_nodes;
-  return launch_tree(true, a, N, stream);
+  return launch_tree(kBuild, a, N, stream);
+}
+
+hipError_t launch_mixture_tree(const int32_t* topk_id, const float* topk_raw, const double* lse, const int32_t* anchor,
+                               int N, int K, int L, int k, int B, const int32_t* modes, double* cutoff,
+                               int32_t* n_select, int32_t* per_mode_kept, int32_t* node_token, int32_t* parent,
+                               int32_t* depth, double* score, int32_t* best_mode, int32_t* n_nodes, int32_t* status,
+                               void* ws, hipStream_t stream) {
+  TreeArgs a = {};
+  a.modes = modes;
+  a.topk_id = topk_id;
+  a.topk_raw = topk_raw;
+  a.lse = lse;
+  a.K = K;
+  a.L = L;
+  a.k = k;
+  a.B = B;
+  a.ws = static_cast<unsigned char*>(ws);
+  a.status = status;
+  a.cutoff_out = cutoff;
+  a.n_select_out = n_select;
+  a.per_mode_kept = per_mode_kept;
+  a.anchor = anchor;
+  a.node_token = node_token;
+  a.parent = parent;
+  a.depth = depth;
+  a.score = score;
+  a.best_mode = best_mode;
+  a.n_nodes = n_nodes;
+  return launch_tree(kFused, a, N, stream);
 }
 
 }  // namespace mfd

@@ -25,7 +25,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 MFD_OK, MFD_ERR_INVALID_ARG, MFD_ERR_DTYPE, MFD_ERR_WORKSPACE, MFD_ERR_DEVICE = 0, 1, 2, 3, 4
 MFD_BF16, MFD_F32 = 0, 1
 (MFD_OP_LOGSOFTMAX_TOPK, MFD_OP_MIXTURE_THRESHOLD, MFD_OP_TREE_BUILD,
- MFD_OP_TREE_MASK, MFD_OP_VERIFY_WALK, MFD_OP_COVERED_MASS, MFD_OP_LMHEAD_TOPK) = range(7)
+ MFD_OP_TREE_MASK, MFD_OP_VERIFY_WALK, MFD_OP_COVERED_MASS, MFD_OP_LMHEAD_TOPK, MFD_OP_MIXTURE_TREE) = range(8)
 MFD_TREE_NONFINITE, MFD_TREE_CAPACITY, MFD_TREE_BAD_TEMPERATURE, MFD_TREE_BAD_MODES = 1, 2, 4, 8
 MFD_HEAD_ROWS, MFD_HEAD_PACKED = 0, 1
 
@@ -34,7 +34,8 @@ EXPORTED = ["mfd_last_error", "mfd_version", "mfd_workspace_size", "mfd_logsoftm
             "mfd_verify_walk", "mfd_covered_mass", "mfd_chimera_count", "mfd_logsoftmax_topk_modes",
             "mfd_mixture_threshold_modes", "mfd_tree_build_modes", "mfd_stream_read",
             "mfd_lmhead_logsoftmax_topk", "mfd_lmhead_logsoftmax_topk_mapped",
-            "mfd_lmhead_packed_size", "mfd_lmhead_pack_weight", "mfd_verify_walk_noalloc"]
+            "mfd_lmhead_packed_size", "mfd_lmhead_pack_weight", "mfd_verify_walk_noalloc",
+            "mfd_mixture_tree", "mfd_mixture_tree_modes"]
 
 _p = ctypes.c_void_p
 _i = ctypes.c_int
@@ -55,6 +56,12 @@ _lib.mfd_mixture_threshold.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _
 _lib.mfd_tree_build.restype = _i
 _lib.mfd_tree_build.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i,
                                 _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]
+_lib.mfd_mixture_tree.restype = _i
+_lib.mfd_mixture_tree.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                  _p, _sz, _p]
+_lib.mfd_mixture_tree_modes.restype = _i
+_lib.mfd_mixture_tree_modes.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                        _p, _p, _p, _sz, _p]
 _lib.mfd_logsoftmax_topk_modes.restype = _i
 _lib.mfd_logsoftmax_topk_modes.argtypes = [_p, _i, _i, _i, _i, _i, _p, _i, _p, _p, _p, _p, _p, _p]
 _lib.mfd_mixture_threshold_modes.restype = _i
@@ -341,6 +348,37 @@ def mfd_tree_build_modes(topk_id, topk_raw, lse, cutoff, n_select, anchor_token,
                                      _ptr(anchor_token), N, K, L, k, B, _ptr(modes), _ptr(node_token), _ptr(parent),
                                      _ptr(depth), _ptr(score), _ptr(best_mode), _ptr(n_nodes), _ptr(status),
                                      _ptr(ws), ws_bytes, _stream_handle(stream)), "mfd_tree_build_modes")
+
+
+def mfd_mixture_tree(topk_id, topk_raw, lse, anchor_token, B, cutoff, n_select, per_mode_kept, node_token, parent,
+                     depth, score, best_mode, n_nodes, status=None, ws=None, stream=None, modes=None):
+    """The cut-off and the tree from one search (mfd_mixture_threshold and
+    mfd_tree_build in one launch); with modes ([N] int32 on the GPU) tree n uses
+    its first modes[n] futures."""
+    N, K, L, k = topk_id.shape
+    Bp1 = B + 1
+    _want(topk_id, "topk_id", torch.int32, (N, K, L, k))
+    _want(topk_raw, "topk_raw", torch.float32, (N, K, L, k))
+    _want(lse, "lse", torch.float64, (N, K, L))
+    _want(anchor_token, "anchor_token", torch.int32, (N,))
+    _want(cutoff, "cutoff", torch.float64, (N,))
+    _want(n_select, "n_select", torch.int32, (N,))
+    _want(per_mode_kept, "per_mode_kept", torch.int32, (N, K), optional=True)
+    for name, t, dt in (("node_token", node_token, torch.int32), ("parent", parent, torch.int32),
+                        ("depth", depth, torch.int32), ("score", score, torch.float64),
+                        ("best_mode", best_mode, torch.int32)):
+        _want(t, name, dt, (N, Bp1))
+    _want(n_nodes, "n_nodes", torch.int32, (N,))
+    _want(status, "status", torch.int32, (N,), optional=True)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    common = (_ptr(topk_id), _ptr(topk_raw), _ptr(lse), _ptr(anchor_token), N, K, L, k, B)
+    outs = (_ptr(cutoff), _ptr(n_select), _ptr(per_mode_kept), _ptr(node_token), _ptr(parent), _ptr(depth),
+            _ptr(score), _ptr(best_mode), _ptr(n_nodes), _ptr(status), _ptr(ws), ws_bytes, _stream_handle(stream))
+    if modes is None:
+        _check(_lib.mfd_mixture_tree(*common, *outs), "mfd_mixture_tree")
+        return
+    _want(modes, "modes", torch.int32, (N,))
+    _check(_lib.mfd_mixture_tree_modes(*common, _ptr(modes), *outs), "mfd_mixture_tree_modes")
 
 
 def mfd_tree_mask(parent, depth, n_nodes, pos_base, mask_words, position_ids, dense_mask=None, stream=None):

@@ -119,8 +119,7 @@ class MixtureTreePath:
         """Calls 1-4 with the fused LM head: hidden states -> tree, mask, position ids."""
         self.clear_status(stream)
         self.lmhead_logsoftmax_topk(hidden, weight, stream)
-        self.mixture_threshold(stream)
-        self.tree_build(anchor, stream)
+        self.mixture_tree(anchor, stream)
         self.tree_mask(pos_base, stream)
 
     def mixture_threshold(self, stream=None):
@@ -133,6 +132,13 @@ class MixtureTreePath:
         M.mfd_tree_build_modes(b.topk_id, b.topk_raw, b.lse, b.cutoff, b.n_select, anchor, self.B, self.modes,
                                b.node_token, b.parent, b.depth, b.score, b.best_mode, b.n_nodes, b.status, b.ws,
                                stream=stream)
+
+    def mixture_tree(self, anchor, stream=None):
+        """The cut-off and the tree from one search (calls 2 and 3 in one launch)."""
+        b = self.buf
+        M.mfd_mixture_tree(b.topk_id, b.topk_raw, b.lse, anchor, self.B, b.cutoff, b.n_select, b.per_mode_kept,
+                           b.node_token, b.parent, b.depth, b.score, b.best_mode, b.n_nodes, b.status, b.ws,
+                           stream=stream, modes=self.modes)
 
     def tree_mask(self, pos_base, stream=None):
         b = self.buf
@@ -153,15 +159,20 @@ class MixtureTreePath:
             with torch.cuda.stream(stream):
                 self.buf.status.zero_()
 
-    def build(self, logits, anchor, pos_base, stream=None):
-        """Calls 1-4: logits -> tree, mask, position ids (status flags cleared first)."""
+    def build(self, logits, anchor, pos_base, stream=None, fused=True):
+        """Calls 1-4: logits -> tree, mask, position ids (status flags cleared
+        first).  The cut-off and the tree come from one launch (mfd_mixture_tree),
+        or with fused=False from the separate threshold and build calls."""
         self.clear_status(stream)
         self.logsoftmax_topk(logits, stream)
-        self.mixture_threshold(stream)
-        self.tree_build(anchor, stream)
+        if fused:
+            self.mixture_tree(anchor, stream)
+        else:
+            self.mixture_threshold(stream)
+            self.tree_build(anchor, stream)
         self.tree_mask(pos_base, stream)
 
     def step(self, logits, anchor, pos_base, target, temperature, seed, stream=None):
-        """One whole pass of the path: the five calls in order."""
+        """One whole pass of the path: logits pass, cut-off and tree, mask, walk."""
         self.build(logits, anchor, pos_base, stream)
         self.verify_walk(target, temperature, seed, stream)

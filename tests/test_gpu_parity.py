@@ -723,6 +723,11 @@ def test_threshold_capacity_flag_gives_root_only_tree():
     assert P.buf.status.item() & M.MFD_TREE_CAPACITY
     assert P.buf.n_select.item() == 0 and math.isnan(P.buf.cutoff.item())
     assert P.buf.per_mode_kept.eq(0).all()
+    Q = MixtureTreePath(1, 1, 2, 1000, 256)
+    Q.build(x.cuda(), anchor, pos, fused=False)
+    torch.cuda.synchronize()
+    assert Q.buf.status.item() & M.MFD_TREE_CAPACITY
+    assert torch.equal(Q.buf.node_token, P.buf.node_token) and torch.equal(Q.buf.n_nodes, P.buf.n_nodes)
     g = tree_rows(P, 0)
     assert g["n_nodes"] == 1 and g["node_token"][0] == 4 and g["parent"][0] == -1 and g["depth"][0] == 0
     assert np.all(g["node_token"][1:] == -1) and np.all(g["parent"][1:] == -1) and np.all(np.isneginf(g["score"][1:]))
@@ -778,3 +783,46 @@ def test_walk_more_trees_than_one_launch():
         deep += int(tau_h[n] == 2)
     say(f"[walk launches] {N} walks equal the oracle's, {deep} accepted the drafted token")
     assert deep > N // 3
+
+
+# ------------------------------------------------------------------ one search for the cut-off and the tree
+
+TREE_FIELDS = ("cutoff", "n_select", "per_mode_kept", "node_token", "parent", "depth", "score", "best_mode", "n_nodes",
+               "mask_words", "position_ids", "status")
+
+
+@pytest.mark.parametrize("name,N", [("batched", 64), ("batched_deep", 64), ("stress", 1), ("batched_modes", 64),
+                                    ("batched_subset", 16), ("tiny", 1), ("product", 1)])
+def test_fused_tree_equals_separate_calls(name, N):
+    """mfd_mixture_tree (one launch) gives the outputs of mfd_mixture_threshold
+    followed by mfd_tree_build, bit for bit."""
+    say(f"[fused tree] {name} N={N}")
+    w = synth.WORKLOADS[name]
+    b = synth.draft_batch(name, device="cuda", N=N, base_seed=11)
+    vmap = None if b.vocab_map is None else b.vocab_map.cuda()
+    modes = None if b.modes is None else b.modes.cuda()
+    out = []
+    for fused in (True, False):
+        P = MixtureTreePath(N, w.K, w.L, b.logits.shape[-1], w.B, vocab_map=vmap, V_full=w.V, modes=modes)
+        P.build(b.logits.cuda(), b.anchor.cuda(), b.pos_base.cuda(), fused=fused)
+        torch.cuda.synchronize()
+        out.append({f: getattr(P.buf, f).clone() for f in TREE_FIELDS})
+    for f in TREE_FIELDS:
+        assert torch.equal(out[0][f], out[1][f]), f
+    assert out[0]["status"].eq(0).all()
+
+
+@pytest.mark.parametrize("case", SMALL + [(12, 3, 4, 12, 25, True, 0.4)], ids=[f"s{c[0]}" for c in SMALL] + ["s12"])
+def test_fused_tree_equals_separate_calls_small(case):
+    seed, K, L, V, B, ints, neginf = case
+    x = _small_tree_case(seed, K, L, V, B, ints, neginf).cuda()
+    anchor = torch.tensor([7], dtype=torch.int32, device="cuda")
+    pos = torch.tensor([100], dtype=torch.int64, device="cuda")
+    out = []
+    for fused in (True, False):
+        P = MixtureTreePath(1, K, L, V, B)
+        P.build(x, anchor, pos, fused=fused)
+        torch.cuda.synchronize()
+        out.append({f: getattr(P.buf, f).clone() for f in TREE_FIELDS})
+    for f in TREE_FIELDS:
+        assert torch.equal(out[0][f], out[1][f]), (f, out[0][f], out[1][f])
