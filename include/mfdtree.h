@@ -115,7 +115,10 @@ const char* mfd_version(void);
 
 /* Bytes of device workspace the call `op` needs for these shapes (0 if none).
  * Arguments a call does not use are ignored.  Returns MFD_ERR_INVALID_ARG for
- * shapes outside the limits. */
+ * shapes outside the limits.  MFD_OP_VERIFY_WALK uses N, V (the target's
+ * vocabulary) and B (trees of B + 1 rows): the size includes the arrays of
+ * the walk's speculative pass (see mfd_verify_walk); with B < 0 or V < 1 it
+ * is the smaller size without them. */
 mfd_status mfd_workspace_size(mfd_op op, int N, int K, int L, int V, int B, size_t* bytes);
 
 /*
@@ -405,18 +408,23 @@ mfd_status mfd_tree_mask(const int32_t* parent, const int32_t* depth, const int3
  *             if the call gave up waiting for work to finish (a bounded wait,
  *             seconds long, that never runs out in a correct run; tau is then 0).
  *   ws        device workspace, 8-byte aligned, of at least
- *             mfd_workspace_size(MFD_OP_VERIFY_WALK) bytes (per-tree control
- *             blocks, per-round counters and slice results; set up by the call
- *             itself, so it needs no clearing).
- * Each visited row is cut into slices that any of the launch's workgroups may
- * take, so the device's resident workgroups share the open rows of all trees;
- * calls on one stream are ordered, calls that overlap must not share `ws`.
- * The workgroups wait on one another, so they are launched cooperatively
- * (all resident at once).  The HIP runtime grants cooperative launches on a
- * GPU to one process at a time: once a live process has made one, a second
- * process's call fails with MFD_ERR_DEVICE ("the operation cannot be performed
- * in the present state") and the walk does not run.  Keep the walks of a
- * GPU in one process.
+ *             mfd_workspace_size(MFD_OP_VERIFY_WALK, N, .., V, B) bytes with
+ *             B < 0 (per-tree control blocks, per-round counters and slice
+ *             results; set up by the call itself, so it needs no clearing).
+ *             With the size for the trees' B and the target's V it also
+ *             holds the speculative pass's arrays.
+ * Each visited row is cut into slices; workgroups claim the slices of open
+ * rows from counters, so the device's workgroups share the open rows of the
+ * trees and none waits for a particular other one (an ordinary launch: any
+ * number of processes may walk on one GPU).  Calls on one stream are
+ * ordered; calls that overlap must not share `ws`.
+ * Speculative pass: the token chosen at a node depends only on that node's
+ * row, T, the seed and its depth.  When the workspace holds the pass's arrays
+ * and the rows are few enough (every node's row up to 160 MiB per launch,
+ * else the rows of nodes that have a child up to 400 MiB), those rows are
+ * reduced first, in parallel over all workgroups, and each tree is walked
+ * along the chosen tokens at once; the walk proper then reads at most the
+ * last node's row.  The outputs are the same bit for bit either way.
  */
 mfd_status mfd_verify_walk(const void* target_logits, mfd_dtype dtype, int N, int Bp1, int V, int L,
                            const int32_t* node_token, const int32_t* parent, const int32_t* depth,
@@ -433,10 +441,12 @@ mfd_status mfd_verify_walk(const void* target_logits, mfd_dtype dtype, int N, in
  * until the process ends; its address on a device is looked up on the first
  * call made with that device current.  Same arguments, outputs and errors as
  * mfd_verify_walk, plus:
- *   - N is at most 1347 (the trees whose workspace fits 2 MiB); a larger N
+ *   - N is at most 1152 (the trees whose workspace fits 2 MiB); a larger N
  *     returns MFD_ERR_WORKSPACE before any launch.
  *   - The call clears what must start at zero itself; the array keeps the
  *     last call's contents otherwise.
+ *   - The speculative pass of mfd_verify_walk runs when its arrays fit in
+ *     what the walk proper leaves of the 2 MiB (same outputs either way).
  *   - Every call on one GPU uses that GPU's one array: calls that overlap on
  *     a GPU (different streams, or other threads, without ordering between
  *     them) race and give wrong results.  Calls on one stream are ordered.

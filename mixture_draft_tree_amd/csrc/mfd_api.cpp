@@ -74,7 +74,7 @@ mfd_status mfd_workspace_size(mfd_op op, int N, int K, int L, int V, int B, size
       return ok();
     case MFD_OP_VERIFY_WALK:
       if (N < 0) return fail(MFD_ERR_INVALID_ARG, "N must be >= 0 (got %d)", N);
-      *bytes = N == 0 ? 0 : mfd::walk_ws_bytes(N);
+      *bytes = N == 0 ? 0 : mfd::walk_ws_bytes_full(N, B < 0 || B > kMaxB ? 0 : B + 1, V < 1 || V > kMaxV ? 0 : V);
       return ok();
     case MFD_OP_COVERED_MASS:
       if (N < 0) return fail(MFD_ERR_INVALID_ARG, "N must be >= 0 (got %d)", N);
@@ -430,7 +430,8 @@ mfd_status mfd_verify_walk(const void* target_logits, mfd_dtype dtype, int N, in
     return fail(MFD_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws == nullptr ? (size_t)0 : ws_bytes);
   if (reinterpret_cast<uintptr_t>(ws) % 8) return fail(MFD_ERR_INVALID_ARG, "workspace must be 8-byte aligned");
   return from_hip(mfd::launch_verify_walk(target_logits, dtype == MFD_BF16, N, Bp1, V, L, node_token, parent, depth,
-                                          n_nodes, temperature, seed, tau, out_tokens, path_nodes, status, ws, stream),
+                                          n_nodes, temperature, seed, tau, out_tokens, path_nodes, status, ws, ws_bytes,
+                                          stream),
                   "mfd_verify_walk launch");
 }
 
@@ -460,7 +461,8 @@ mfd_status mfd_verify_walk_noalloc(const void* target_logits, mfd_dtype dtype, i
   mfd_status r = from_hip(mfd::walk_scratch(&ws), "mfd_verify_walk_noalloc scratch lookup");
   if (r != MFD_OK) return r;
   return from_hip(mfd::launch_verify_walk(target_logits, dtype == MFD_BF16, N, Bp1, V, L, node_token, parent, depth,
-                                          n_nodes, temperature, seed, tau, out_tokens, path_nodes, status, ws, stream),
+                                          n_nodes, temperature, seed, tau, out_tokens, path_nodes, status, ws,
+                                          mfd::walk_scratch_bytes(), stream),
                   "mfd_verify_walk_noalloc launch");
 }
 

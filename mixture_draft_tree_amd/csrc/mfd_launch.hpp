@@ -51,6 +51,9 @@ hipError_t launch_tree_mask(const int32_t* parent, const int32_t* depth, const i
                             uint8_t* dense_mask, hipStream_t stream);
 
 size_t walk_ws_bytes(int N);
+// With the speculative pass (N trees of Bp1 nodes over rows of V elements):
+// the workspace size mfd_workspace_size reports.
+size_t walk_ws_bytes_full(int N, int Bp1, long long V);
 // The walk's built-in workspace (mfd_verify_walk_noalloc): its size, and its
 // device address on the current device (looked up once per device).
 size_t walk_scratch_bytes();
@@ -70,7 +73,7 @@ hipError_t launch_chimera_count(const int32_t* node_token, const int32_t* parent
 hipError_t launch_verify_walk(const void* target, bool bf16, int N, int Bp1, long long V, int L,
                               const int32_t* node_token, const int32_t* parent, const int32_t* depth,
                               const int32_t* n_nodes, const float* temperature, const uint64_t* seed, int32_t* tau,
-                              int32_t* out_tokens, int32_t* path_nodes, int32_t* status, void* ws,
+                              int32_t* out_tokens, int32_t* path_nodes, int32_t* status, void* ws, size_t ws_bytes,
                               hipStream_t stream);
 
 

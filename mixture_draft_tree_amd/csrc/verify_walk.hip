@@ -14,15 +14,16 @@
 // T, the seed and its depth, so the only order the walk imposes is one row
 // after the other within a tree.  Every row is cut into S slices, and a round
 // is one row (or its exact re-evaluation, below) of one tree.  The launch's
-// workgroups, all resident at once (cooperative launch), form G groups of S:
-// tree n belongs to group n mod G, and workgroup s of a group always reduces
-// slice s of its trees' rows.  A workgroup serves every tree of its group, in
-// whatever order their rounds open, so one waiting tree does not idle it.
-// After its slice a workgroup publishes a top-two and counts itself in; the
-// one that completes the round merges the S results, finds the child (tree
-// nodes sit in LDS) and opens the tree's next round with one packed word, or
-// ends the tree.  Waits are polls of those words, bounded; a workgroup leaves
-// once all its trees have ended.  Only the rows on the walked path are read.
+// workgroups form groups of about S; group q serves trees q, q + groups, ...
+// and any of its workgroups claims any slice of its trees' open rounds from a
+// per-round counter, so no workgroup waits for a particular other one and the
+// kernel is an ordinary launch.  After its slice a workgroup publishes a
+// top-two and counts itself in; the one that completes the round merges the S
+// results, finds the child and opens the tree's next round with one packed
+// word, or ends the tree.  Polls for open rounds are bounded; a workgroup
+// leaves once all its group's trees have ended.  Only the rows on the walked
+// path are read (or, with the speculative pass below, every row of a small
+// batch at once).
 //
 // At T > 0 the noise is first estimated in fp32 (two v_log_f32, error below
 // kGumbelTol, see gumbel_estimate) and y = x / T + g is formed in fp64 from
@@ -83,13 +84,12 @@ constexpr int kWalkThreads = 256;
 constexpr int kWalkWaves = kWalkThreads / kWave;
 constexpr int kSlices = 64;                  // slices per row, at most
 constexpr int kMaxRounds = 2 * (32 + 1);     // two rounds per depth, L <= 32
-constexpr int kMaxServed = kWave;            // trees one workgroup serves, at most
 constexpr long long kIdleLimit = 1LL << 22;  // polls without work before giving up (seconds; never in practice)
 constexpr int kPollSleep = 2;                // s_sleep units (64 clocks each) between polls
 constexpr double kGumbelTol = 1e-4;
 constexpr float kLn2f = 0.693147180559945309f;
 constexpr int kSliceVec = 2;                 // 16-byte vectors per thread per round of loads
-constexpr int kNodesLds = 2048;              // node (parent, token) pairs of the served trees kept in LDS
+constexpr int kMaxB1 = 16384;                // rows per tree, at most (B <= 16383)
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -165,6 +165,7 @@ __host__ __device__ __forceinline__ uint32_t round_word(int r, int kind, int ste
 struct WalkArgs {
   const void* target;
   int N, Bp1, L, S, G;
+  int groups;  // walk kernel: groups of workgroups, each serving its own trees
   long long V;
   const int32_t* node_token;
   const int32_t* parent;
@@ -178,10 +179,21 @@ struct WalkArgs {
   int32_t* status;
   uint32_t* word;  // [N] round words
   double* cut;     // [N] cut-off of an exact round
+  int32_t* claim;  // [N][kMaxRounds] slices claimed per round
   int32_t* done;   // [N][kMaxRounds] slices finished per round
   double* py1;     // [N][kSlices] slice results of the open round
   double* py2;
   int32_t* pi;
+  // speculation (walk_prep_kernel / walk_spec_kernel); spec = 0: none
+  int spec;
+  int spec_rcap;         // rows the slice-result arrays hold
+  int32_t* spec_cnt;     // [N][4]: nodes with a child, all nodes (0 for an ended tree), deepest node, T > 0
+  uint16_t* spec_nodes;  // [N][Bp1]: the tree's nodes with a child, then its leaves
+  int32_t* choice;       // [N][Bp1]: token chosen at each evaluated node, -1 if not evaluated
+  int32_t* rowdone;      // [N][Bp1]: slices finished per listed row
+  int32_t* treedone;     // [N]: rows finished per tree
+  double* sy;            // [spec_rcap][S]: best exact value of each slice
+  int32_t* si;           // [spec_rcap][S]: its token
 };
 
 // Ordering between workgroups.  Everything one workgroup hands to another
@@ -214,15 +226,16 @@ __device__ __forceinline__ void st(T* p, T v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+constexpr int kWalkMaxTrees = 2048;  // trees one launch of the walk kernel handles
+
 struct WalkShared {
   Top2 w[kWalkWaves];
   Top2 g;  // merged result of a round
   int child;
-  int j, quit, last;
+  int n, slice, quit, last;
   uint32_t word;
   double cut;
-  int seen[kMaxServed];   // last round this workgroup reduced, per served tree
-  int node0[kMaxServed];  // first LDS slot of the tree's nodes, -1 if not in LDS
+  unsigned char full[kWalkMaxTrees];  // per tree: the last round (r + 1) found with every slice claimed
 };
 
 // Element value as float (bf16 or fp32 storage).
@@ -234,7 +247,7 @@ __device__ __forceinline__ float elem_at(const void* row, long long i) {
 // Calls f(i, x) for every element i of [e0, e1): scalars before and after the
 // 16-byte aligned part, then the aligned vectors kSliceVec per thread at a
 // time (all loads of a round issued before any is used).
-template <bool BF16, typename F>
+template <bool BF16, int VECS = kSliceVec, typename F>
 __device__ __forceinline__ void for_slice(const void* row, long long e0, long long e1, F f) {
   constexpr int VEC = BF16 ? 8 : 4;
   constexpr int ESZ = BF16 ? 2 : 4;
@@ -248,16 +261,16 @@ __device__ __forceinline__ void for_slice(const void* row, long long e0, long lo
   for (long long i = b + tid; i < e1; i += kWalkThreads) f(i, elem_at<BF16>(row, i));
   if (nv <= 0) return;
   const u32x4* vp = reinterpret_cast<const u32x4*>(static_cast<const char*>(row) + a * ESZ);
-  for (long long q0 = 0; q0 < nv; q0 += kSliceVec * kWalkThreads) {
-    u32x4 v[kSliceVec];
+  for (long long q0 = 0; q0 < nv; q0 += VECS * kWalkThreads) {
+    u32x4 v[VECS];
 #pragma unroll
-    for (int u = 0; u < kSliceVec; ++u) {
+    for (int u = 0; u < VECS; ++u) {
       long long q = q0 + u * kWalkThreads + tid;
       q = q < nv ? q : nv - 1;  // clamped; only q < nv is used
       v[u] = __builtin_nontemporal_load(vp + q);
     }
 #pragma unroll
-    for (int u = 0; u < kSliceVec; ++u) {
+    for (int u = 0; u < VECS; ++u) {
       const long long q = q0 + u * kWalkThreads + tid;
       if (q < nv) {
         const long long i0 = a + q * VEC;
@@ -313,20 +326,31 @@ __device__ __forceinline__ Top2 block_top2(Top2 t, WalkShared& sh) {
   return r;
 }
 
-// Opens round 0 (the root) of every tree with a valid temperature and ends
-// the others; clears the per-round counters.
-__global__ void walk_init_kernel(WalkArgs a) {
-  const int N = a.N, Lp1 = a.L + 1;
-  const int i0 = blockIdx.x * blockDim.x + threadIdx.x, stride = gridDim.x * blockDim.x;
-  for (int i = i0; i < N * kMaxRounds; i += stride) a.done[i] = 0;
-  for (int n = i0; n < N; n += stride) {
-    const float T = a.temperature[n];
+// One workgroup per tree.  Opens round 0 (the root) of a tree with a valid
+// temperature and ends the others; clears the per-round counters.  With
+// speculation on, also lists the tree's nodes (those with a child first, in
+// node order, then the leaves), marks every node's token as not yet chosen
+// and clears the speculation counters.
+__global__ void __launch_bounds__(kWalkThreads) walk_prep_kernel(WalkArgs a) {
+  __shared__ unsigned char has_child[kMaxB1];
+  __shared__ int scan[kWalkWaves];
+  const int n = blockIdx.x, tid = threadIdx.x;
+  const int Lp1 = a.L + 1, Bp1 = a.Bp1;
+  for (int i = tid; i < kMaxRounds; i += kWalkThreads) {
+    a.claim[(size_t)n * kMaxRounds + i] = 0;
+    a.done[(size_t)n * kMaxRounds + i] = 0;
+  }
+  const float T = a.temperature[n];
+  const bool bad = !(T >= 0.f) || isinf(T);
+  if (bad) {
+    for (int i = tid; i < Lp1; i += kWalkThreads) {
+      a.out_tokens[(size_t)n * Lp1 + i] = -1;
+      a.path_nodes[(size_t)n * Lp1 + i] = -1;
+    }
+  }
+  if (tid == 0) {
     a.cut[n] = 0.0;
-    if (!(T >= 0.f) || isinf(T)) {
-      for (int i = 0; i < Lp1; ++i) {
-        a.out_tokens[(size_t)n * Lp1 + i] = -1;
-        a.path_nodes[(size_t)n * Lp1 + i] = -1;
-      }
+    if (bad) {
       a.tau[n] = 0;
       if (a.status) atomicOr(&a.status[n], MFD_TREE_BAD_TEMPERATURE);
       a.word[n] = kEnded;
@@ -334,105 +358,477 @@ __global__ void walk_init_kernel(WalkArgs a) {
       a.word[n] = round_word(0, 0, 0, 0);
     }
   }
+  if (!a.spec) return;
+  int nn = a.n_nodes[n];
+  nn = nn < 1 ? 1 : (nn > Bp1 ? Bp1 : nn);
+  if (bad) nn = 0;
+  const size_t tb = (size_t)n * Bp1;
+  for (int u = tid; u < nn; u += kWalkThreads) {
+    has_child[u] = 0;
+    a.choice[tb + u] = -1;
+    a.rowdone[tb + u] = 0;
+  }
+  if (tid == 0) a.treedone[n] = 0;
+  __syncthreads();
+  for (int v = 1 + tid; v < nn; v += kWalkThreads) {
+    const int p = a.parent[tb + v];
+    if (p >= 0 && p < nn) has_child[p] = 1;
+  }
+  __syncthreads();
+  int local = 0, dmax = 0;
+  for (int u = tid; u < nn; u += kWalkThreads) {
+    local += has_child[u];
+    const int du = a.depth[tb + u];
+    dmax = du > dmax ? du : dmax;
+  }
+  const int nint = block_sum<kWalkThreads>(local, scan);
+  // the deepest node, by a max over the waves (scan[] is free again)
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) dmax = max(dmax, __shfl_xor(dmax, o, kWave));
+  if (lane_id() == 0) scan[wave_id()] = dmax;
+  __syncthreads();
+  for (int w = 0; w < kWalkWaves; ++w) dmax = max(dmax, scan[w]);
+  __syncthreads();
+  int carry = 0;
+  for (int base = 0; base < nn; base += kWalkThreads) {
+    const int u = base + tid;
+    const int h = u < nn ? has_child[u] : 0;
+    int tot;
+    const int ex = block_exclusive_scan<kWalkThreads>(h, scan, &tot);
+    if (u < nn) {
+      const int before = carry + ex;  // nodes with a child before u
+      a.spec_nodes[tb + (h ? before : nint + (u - before))] = (uint16_t)u;
+    }
+    carry += tot;
+  }
+  if (tid == 0) {
+    a.spec_cnt[4 * n] = nint;
+    a.spec_cnt[4 * n + 1] = nn;
+    a.spec_cnt[4 * n + 2] = nn > 0 ? dmax : 0;
+    a.spec_cnt[4 * n + 3] = T > 0.f ? 1 : 0;
+  }
+}
+
+// ---------------------------------------------------------------- speculation
+// The token chosen at a node depends only on the node's own row, T, the seed
+// and the node's depth, not on the path that leads there.  So when the rows
+// are few enough to read in one pass, every resident workgroup reduces them
+// in parallel before the walk: every node's row (a small batch), or the rows
+// of the nodes that have a child when those alone fit.  The tree is then
+// walked from the root along the chosen tokens at once.  What remains -- the
+// last node's row, when it is a leaf that was not evaluated -- is one round
+// of verify_walk_kernel; when neither budget holds, that kernel does all of it.
+//
+// Each slice of a row gives its exact winner in one pass.  At T = 0 that is
+// the largest logit (lowest id among equals).  At T > 0 every element gets the
+// fp32 noise estimate, whose error e(v) = |est(v) - y(v)| is below kGumbelTol
+// plus a few ulp of |y|.  Let w be the slice's exact winner and b the element
+// of the best estimate g:  est(w) >= y(w) - e(w) >= y(b) - e(w) >= g - e(b) -
+// e(w).  So w is among the elements whose estimate is within the slack
+// 2 kGumbelTol + (|g| + 1) 2^-45 of g, and evaluating just those exactly in
+// fp64 finds it; the row's winner is the best of its slices' winners.
+constexpr long long kSpecAllBytes = 160ll << 20;  // every node's row, up to this many bytes per launch
+constexpr long long kSpecIntBytes = 400ll << 20;  // else the rows of nodes with a child, up to this many
+constexpr int kFollowLds = 2048;                  // nodes of a tree the follow step copies to LDS
+constexpr int kSpecVec = 8;                       // 16-byte vectors per thread in flight in the speculative pass
+// Cost estimates behind the choice between speculation and the row-by-row
+// walk, measured on MI355X at V = 151936: a dependent round of the walk, the
+// speculative pass's fixed cost, its reading rate, and the noise cost of one
+// T > 0 element (Philox4x64-10 and the estimate) spread over the whole chip.
+constexpr double kRoundUs = 7.5;
+constexpr double kSpecFixedUs = 18.0;
+constexpr double kSpecBytesPerUs = 2.0e6;
+constexpr double kNoiseUsPerElement = 4.0e-6;
+constexpr int kSpecLaunchTrees = 4;  // the pass is only tried for launches of at most this many trees
+constexpr int kSpecMaxTrees = 64;    // trees per launch the pass can handle (its LDS prefix array)
+static_assert(kSpecLaunchTrees <= kSpecMaxTrees, "speculation prefix array too small");
+
+// (y, i) with larger y first, then lower i, over the workgroup; every thread gets it.
+struct BestYI {
+  double y;
+  int i;
+};
+
+__device__ __forceinline__ BestYI block_best(BestYI b, BestYI* wsh) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    const double y = __shfl_xor(b.y, o, kWave);
+    const int i = __shfl_xor(b.i, o, kWave);
+    if (better(y, i, b.y, b.i)) {
+      b.y = y;
+      b.i = i;
+    }
+  }
+  if (lane_id() == 0) wsh[wave_id()] = b;
+  __syncthreads();
+  BestYI r = wsh[0];
+  for (int w = 1; w < kWalkWaves; ++w)
+    if (better(wsh[w].y, wsh[w].i, r.y, r.i)) r = wsh[w];
+  __syncthreads();
+  return r;
+}
+
+// The exact winner of slice [e0, e1) of a row (see above).
+template <bool BF16>
+__device__ BestYI spec_slice(const void* row, long long e0, long long e1, double T, uint64_t sd, int d,
+                             BestYI* wsh) {
+  if (T == 0.0) {
+    BestYI b = {-INFINITY, 0x7FFFFFFF};
+    for_slice<BF16, kSpecVec>(row, e0, e1, [&](long long i, float x) {
+      if (better((double)x, (int)i, b.y, b.i)) {
+        b.y = (double)x;
+        b.i = (int)i;
+      }
+    });
+    return block_best(b, wsh);
+  }
+  const double invT = 1.0 / T;
+  // each thread: its two best estimates (value, id, logit) and the third best value
+  double e1v = -INFINITY, e2v = -INFINITY, e3v = -INFINITY;
+  int i1 = 0x7FFFFFFF, i2 = 0x7FFFFFFF;
+  float x1 = 0.f, x2 = 0.f;
+  NoiseCache nc;
+  for_slice<BF16, kSpecVec>(row, e0, e1, [&](long long i, float x) {
+    const double est = (double)x * invT + (double)gumbel_estimate(nc.word(i, sd, d));
+    if (better(est, (int)i, e1v, i1)) {
+      e3v = e2v;
+      e2v = e1v;
+      i2 = i1;
+      x2 = x1;
+      e1v = est;
+      i1 = (int)i;
+      x1 = x;
+    } else if (better(est, (int)i, e2v, i2)) {
+      e3v = e2v;
+      e2v = est;
+      i2 = (int)i;
+      x2 = x;
+    } else if (est > e3v) {
+      e3v = est;
+    }
+  });
+  BestYI g = block_best(BestYI{e1v, i1}, wsh);
+  const double lim = g.y - (2.0 * kGumbelTol + (fabs(g.y) + 1.0) * 0x1.0p-45);
+  BestYI b = {-INFINITY, 0x7FFFFFFF};
+  auto exact = [&](long long i, float x) {
+    const uint64_t w = nc.word(i, sd, d);
+    const double y = (double)x / T + gumbel_from_word(w);
+    if (better(y, (int)i, b.y, b.i)) {
+      b.y = y;
+      b.i = (int)i;
+    }
+  };
+  if (e3v >= lim) {
+    // three or more of this thread's elements are close to the slice's best
+    // (rare): go over its elements again
+    for_slice<BF16, kSpecVec>(row, e0, e1, [&](long long i, float x) {
+      if ((double)x * invT + (double)gumbel_estimate(nc.word(i, sd, d)) >= lim) exact(i, x);
+    });
+  } else {
+    if (i1 != 0x7FFFFFFF && e1v >= lim) exact(i1, x1);
+    if (i2 != 0x7FFFFFFF && e2v >= lim) exact(i2, x2);
+  }
+  return block_best(b, wsh);
 }
 
 template <bool BF16>
-__global__ void __launch_bounds__(kWalkThreads, 4) verify_walk_kernel(WalkArgs a) {
-  __shared__ WalkShared sh;
-  __shared__ int32_t lpar[kNodesLds];
-  __shared__ int32_t ltok[kNodesLds];
-  const int tid = threadIdx.x, lane = lane_id(), wid = wave_id();
-  const int N = a.N, S = a.S, G = a.G, L = a.L, Lp1 = L + 1, Bp1 = a.Bp1;
+__global__ void __launch_bounds__(kWalkThreads, 4) walk_spec_kernel(WalkArgs a) {
+  __shared__ int pre[kSpecMaxTrees + 1];
+  __shared__ int scan[kWalkWaves];
+  __shared__ BestYI wsh[kWalkWaves];
+  __shared__ int sh_row, sh_tree;  // separate flags: see the barriers
+  __shared__ int32_t fpar[kFollowLds], ftok[kFollowLds], fch[kFollowLds];
+  const int tid = threadIdx.x;
+  const int N = a.N, S = a.S, Bp1 = a.Bp1, L = a.L, Lp1 = L + 1;
   const long long V = a.V;
   const size_t esz = BF16 ? 2 : 4;
-  const int grp = blockIdx.x / S, s = blockIdx.x - grp * S;
-  // served trees: n = grp + j * G
-  const int served = grp < N ? (N - 1 - grp) / G + 1 : 0;
-  if (tid < kMaxServed) sh.seen[tid] = 0;
-  if (tid == 0) {
-    int slot = 0;
-    for (int j = 0; j < served; ++j) {
-      const int n = grp + j * G;
+  // Rows under each budget, and an estimate of each route's time.  Row by
+  // row, the walk takes one dependent round per depth of its deepest tree
+  // (trees share groups of workgroups beyond G).  Speculation reads the rows
+  // at once, pays the noise of every T > 0 row, and leaves one round for
+  // the trees that end at an unevaluated leaf.  Either route gives the same
+  // tokens; this only picks the faster one.
+  int loc_int = 0, loc_all = 0, loc_int_hot = 0, loc_all_hot = 0, loc_d = 0;
+  for (int n = tid; n < N; n += kWalkThreads) {
+    const int ni = a.spec_cnt[4 * n], na = a.spec_cnt[4 * n + 1], hot = a.spec_cnt[4 * n + 3];
+    loc_int += ni;
+    loc_all += na;
+    loc_int_hot += hot ? ni : 0;
+    loc_all_hot += hot ? na : 0;
+    loc_d = max(loc_d, a.spec_cnt[4 * n + 2]);
+  }
+  const long long tot_int = block_sum<kWalkThreads>(loc_int, scan);
+  const long long tot_all = block_sum<kWalkThreads>(loc_all, scan);
+  const long long hot_int = block_sum<kWalkThreads>(loc_int_hot, scan);
+  const long long hot_all = block_sum<kWalkThreads>(loc_all_hot, scan);
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) loc_d = max(loc_d, __shfl_xor(loc_d, o, kWave));
+  if (lane_id() == 0) scan[wave_id()] = loc_d;
+  __syncthreads();
+  int dmax = 0;
+  for (int w = 0; w < kWalkWaves; ++w) dmax = max(dmax, scan[w]);
+  __syncthreads();
+  const long long row_bytes = V * (long long)esz;
+  const double sharing = (double)(((long long)N * S + a.G - 1) / a.G);  // rounds open at once per workgroup
+  const double t_rows = (dmax + 1) * kRoundUs * sharing;
+  auto t_spec = [&](long long rows, long long hot) {
+    return kSpecFixedUs + (double)rows * row_bytes / kSpecBytesPerUs + (double)hot * V * kNoiseUsPerElement;
+  };
+  const double t_all = t_spec(tot_all, hot_all);
+  const double t_int = t_spec(tot_int, hot_int) + kRoundUs * sharing;
+  const bool ok_all = tot_all <= a.spec_rcap && tot_all * row_bytes <= kSpecAllBytes && t_all < t_rows;
+  const bool ok_int = tot_int <= a.spec_rcap && tot_int * row_bytes <= kSpecIntBytes && t_int < t_rows;
+  int which;  // 1: every node, 0: nodes with a child
+  if (ok_all && (!ok_int || t_all <= t_int)) which = 1;
+  else if (ok_int) which = 0;
+  else return;
+  // prefix of the chosen row counts over the trees
+  int carry = 0;
+  for (int base = 0; base < N; base += kWalkThreads) {
+    const int n = base + tid;
+    const int c = n < N ? a.spec_cnt[4 * n + which] : 0;
+    int tot;
+    const int ex = block_exclusive_scan<kWalkThreads>(c, scan, &tot);
+    if (n < N) pre[n] = carry + ex;
+    carry += tot;
+  }
+  if (tid == 0) pre[N] = carry;
+  __syncthreads();
+  // slices per row for this pass: about one (row, slice) item per workgroup,
+  // at most the walk's slice count (the result arrays' row stride stays S)
+  int S2 = carry > 0 ? (int)((gridDim.x + carry - 1) / carry) : 1;
+  if (S2 > S) S2 = S;
+  if (S2 < 1) S2 = 1;
+  const long long items = (long long)carry * S2;
+  for (long long it = blockIdx.x; it < items; it += gridDim.x) {
+    const int r = (int)(it / S2), s = (int)(it - (long long)r * S2);
+    int lo = 0, hi = N - 1;  // the tree of row r: the last n with pre[n] <= r
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= r) lo = mid;
+      else hi = mid - 1;
+    }
+    const int n = lo, j = r - pre[n];
+    const size_t tb = (size_t)n * Bp1;
+    const int u = a.spec_nodes[tb + j];
+    const double T = (double)a.temperature[n];
+    const void* row = static_cast<const char*>(a.target) + ((tb + u) * (size_t)V) * esz;
+    long long e0, e1;
+    slice_range<BF16>(row, V, S2, s, e0, e1);
+    const BestYI b = spec_slice<BF16>(row, e0, e1, T, a.seed[n], a.depth[tb + u], wsh);
+    if (tid == 0) {
+      st(&a.sy[(size_t)r * S + s], b.y);
+      st(&a.si[(size_t)r * S + s], b.i);
+      drain();  // the slice's result is in place before it counts as done
+      const int old = __hip_atomic_fetch_add(&a.rowdone[tb + j], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      drain();
+      sh_row = old == S2 - 1;
+    }
+    __syncthreads();
+    if (!sh_row) continue;  // uniform: read after the barrier, rewritten only after the next iteration's
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    // the row's last slice: merge the S slice winners
+    if (tid < kWave) {
+      BestYI m = {-INFINITY, 0x7FFFFFFF};
+      for (int q = tid; q < S2; q += kWave) {
+        const double y = ld(&a.sy[(size_t)r * S + q]);
+        const int i = ld(&a.si[(size_t)r * S + q]);
+        if (better(y, i, m.y, m.i)) {
+          m.y = y;
+          m.i = i;
+        }
+      }
+#pragma unroll
+      for (int o = kWave / 2; o > 0; o >>= 1) {
+        const double y = __shfl_xor(m.y, o, kWave);
+        const int i = __shfl_xor(m.i, o, kWave);
+        if (better(y, i, m.y, m.i)) {
+          m.y = y;
+          m.i = i;
+        }
+      }
+      if (tid == 0) {
+        st(&a.choice[tb + u], m.i == 0x7FFFFFFF ? 0 : m.i);
+        drain();  // the choice is in place before the row counts as done
+        const int old = __hip_atomic_fetch_add(&a.treedone[n], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        drain();
+        sh_tree = old == a.spec_cnt[4 * n + which] - 1;
+      }
+    }
+    __syncthreads();
+    if (!sh_tree) continue;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    // the tree's last row: follow the chosen tokens from the root (wave 0,
+    // with the tree's links and choices copied to LDS when they fit)
+    if (tid < kWave) {
+      const int lane = tid;
       int nn = a.n_nodes[n];
       nn = nn < 1 ? 1 : (nn > Bp1 ? Bp1 : nn);
-      sh.node0[j] = slot + nn <= kNodesLds ? slot : -1;
-      if (slot + nn <= kNodesLds) slot += nn;
+      const bool in_lds = nn <= kFollowLds;
+      if (in_lds) {
+        for (int q = lane; q < nn; q += kWave) {
+          fpar[q] = a.parent[tb + q];
+          ftok[q] = a.node_token[tb + q];
+          fch[q] = ld(&a.choice[tb + q]);
+        }
+      }
+      wave_sync();
+      int32_t* ot = a.out_tokens + (size_t)n * Lp1;
+      int32_t* pn = a.path_nodes + (size_t)n * Lp1;
+      int cur = 0, step = 0;
+      while (true) {
+        const int t = in_lds ? fch[cur] : ld(&a.choice[tb + cur]);
+        if (t < 0) {
+          // not evaluated (a leaf, when only nodes with a child were): the
+          // walk kernel reduces this row in its first round
+          if (lane == 0) st(&a.word[n], round_word(0, 0, step, cur));
+          break;
+        }
+        int child = 0x7FFFFFFF;
+        for (int q = 1 + lane; q < nn; q += kWave) {
+          const int p = in_lds ? fpar[q] : a.parent[tb + q];
+          const int tk = in_lds ? ftok[q] : a.node_token[tb + q];
+          if (p == cur && tk == t) {
+            child = q;
+            break;
+          }
+        }
+#pragma unroll
+        for (int o = kWave / 2; o > 0; o >>= 1) child = min(child, __shfl_xor(child, o, kWave));
+        if (child != 0x7FFFFFFF && step < L) {
+          if (lane == 0) {
+            ot[step] = t;
+            pn[step] = cur;
+          }
+          ++step;
+          cur = child;
+          continue;
+        }
+        for (int i = step + 1 + lane; i < Lp1; i += kWave) {
+          ot[i] = -1;
+          pn[i] = -1;
+        }
+        if (lane == 0) {
+          ot[step] = t;
+          pn[step] = cur;
+          a.tau[n] = a.depth[tb + cur] + 1;
+          st(&a.word[n], kEnded);
+        }
+        break;
+      }
     }
+    __syncthreads();
   }
-  __syncthreads();
-  for (int j = 0; j < served; ++j) {
-    const int o = sh.node0[j];
-    if (o < 0) continue;
-    const int n = grp + j * G;
-    int nn = a.n_nodes[n];
-    nn = nn < 1 ? 1 : (nn > Bp1 ? Bp1 : nn);
-    for (int q = tid; q < nn; q += kWalkThreads) {
-      lpar[o + q] = a.parent[(size_t)n * Bp1 + q];
-      ltok[o + q] = a.node_token[(size_t)n * Bp1 + q];
-    }
-  }
+}
+
+__device__ __forceinline__ uint64_t rotr64(uint64_t m, int r) { return r ? ((m >> r) | (m << (64 - r))) : m; }
+
+// The walk proper.  A round is one row of one tree (or its exact
+// re-evaluation), cut into S slices.  Workgroups claim the slices of open
+// rounds from per-round counters, whichever tree they belong to, so no
+// workgroup waits for a particular other one: the kernel needs no
+// co-residency and is launched like any other.  A workgroup that finds no
+// unclaimed slice polls again after a short sleep; it leaves once every tree
+// has ended.  The workgroup finishing a round's last slice merges the S
+// results, finds the child in the tree and opens the tree's next round (or
+// ends the tree).
+template <bool BF16>
+__global__ void __launch_bounds__(kWalkThreads, 4) verify_walk_kernel(WalkArgs a) {
+  __shared__ WalkShared sh;
+  const int tid = threadIdx.x, lane = lane_id(), wid = wave_id();
+  const int N = a.N, S = a.S, L = a.L, Lp1 = L + 1, Bp1 = a.Bp1;
+  const long long V = a.V;
+  const size_t esz = BF16 ? 2 : 4;
+  // The workgroups form a.groups groups; group q serves trees q, q + groups,
+  // q + 2 groups, ... (its own trees' rounds get its workgroups' attention),
+  // and within a group any workgroup takes any slice.
+  const int grp = (int)(blockIdx.x % a.groups);
+  const int mine_n = grp < N ? (N - 1 - grp) / a.groups + 1 : 0;  // trees of this group
+  const int nchunks = (mine_n + kWave - 1) / kWave;
+  for (int q = tid; q < mine_n; q += kWalkThreads) sh.full[q] = 0;
   long long idle = 0;
   int backoff = 1;
+  const int member = (int)(blockIdx.x / a.groups);
 
   while (true) {
     __syncthreads();  // everyone is done with the previous iteration's shared fields
-    // ------------------------------------------------ find an open round (wave 0)
+    // ------------------------------------------------ claim a slice of an open round (wave 0)
     if (wid == 0) {
-      int quit = 0, pick = -1;
-      uint32_t w = kEnded;
-      if (lane < served) w = ld(&a.word[grp + lane * G]);
-      const bool ended = w == kEnded;
-      const bool ready = !ended && w != 0u && (int)(w & 0x7Fu) > sh.seen[lane < kMaxServed ? lane : 0];
-      const uint64_t rm = __ballot(lane < served && ready);
-      if (rm != 0ull) {
-        pick = __builtin_ctzll(rm);
+      int got = -1, slice = 0, quit = 0, ended = 0;
+      uint32_t gw = 0u;
+      const int c0 = nchunks > 0 ? member % nchunks : 0, rot = member % kWave;
+      for (int k = 0; k < nchunks && got < 0; ++k) {
+        const int chunk = (c0 + k) % nchunks;
+        const int j = chunk * kWave + lane;  // the group's j-th tree
+        const int n = grp + j * a.groups;
+        const uint32_t w = j < mine_n ? ld(&a.word[n]) : kEnded;
+        ended += __popcll(__ballot(j < mine_n && w == kEnded));
+        const bool cand = j < mine_n && w != kEnded && w != 0u && (int)(w & 0x7Fu) > (int)sh.full[j < mine_n ? j : 0];
+        uint64_t m = __ballot(cand);
+        while (m != 0ull) {
+          const int l = (__builtin_ctzll(rotr64(m, rot)) + rot) & (kWave - 1);
+          int c = 0;
+          if (lane == l)
+            c = __hip_atomic_fetch_add(&a.claim[(size_t)n * kMaxRounds + (int)(w & 0x7Fu) - 1], 1, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+          c = __shfl(c, l, kWave);
+          const uint32_t wl = __shfl(w, l, kWave);
+          if (c < S) {
+            got = grp + (chunk * kWave + l) * a.groups;
+            slice = c;
+            gw = wl;
+            break;
+          }
+          if (lane == l) sh.full[j] = (unsigned char)(w & 0x7Fu);  // every slice of this round is taken
+          m &= ~(1ull << l);
+        }
+      }
+      if (got >= 0) {
         backoff = 1;
         idle = 0;
-      } else if (__ballot(lane < served && !ended) == 0ull) {
-        quit = 1;  // every served tree has ended
+      } else if (ended == mine_n) {
+        quit = 1;  // every tree of the group has ended (all its chunks were scanned)
       } else if (++idle > kIdleLimit) {
         quit = 2;
       } else {
-        // back off while nothing is ready (up to ~1 us between polls)
+        // back off while nothing is claimable (up to ~1 us between polls)
         backoff = backoff < 16 ? backoff * 2 : 16;
         for (int z = 0; z < backoff; ++z) __builtin_amdgcn_s_sleep(kPollSleep);
       }
-      w = __shfl(w, pick < 0 ? 0 : pick, kWave);
       if (lane == 0) {
         sh.quit = quit;
-        sh.j = pick;
-        sh.word = w;
+        sh.n = got;
+        sh.slice = slice;
+        sh.word = gw;
         sh.child = 0x7FFFFFFF;
-        if (pick >= 0 && ((w >> 7) & 1u)) {
+        if (got >= 0 && ((gw >> 7) & 1u)) {
           drain();  // the word was read before the cut-off it announces
-          sh.cut = ld(&a.cut[grp + pick * G]);
+          sh.cut = ld(&a.cut[got]);
         }
       }
     }
     __syncthreads();
-    const int quit = sh.quit, j = sh.j;
+    const int quit = sh.quit, n = sh.n;
     if (quit) {
       if (quit == 2 && tid == 0) {
-        // gave up waiting: flag every served tree that has not ended
-        for (int q = 0; q < served; ++q) {
-          const int n = grp + q * G;
-          if (ld(&a.word[n]) != kEnded) {
-            if (a.status) atomicOr(&a.status[n], MFD_TREE_CAPACITY);
-            a.tau[n] = 0;
+        // gave up waiting: flag every tree of the group that has not ended
+        for (int q = grp; q < N; q += a.groups) {
+          if (ld(&a.word[q]) != kEnded) {
+            if (a.status) atomicOr(&a.status[q], MFD_TREE_CAPACITY);
+            a.tau[q] = 0;
           }
         }
       }
       break;
     }
-    if (j < 0) continue;
+    if (n < 0) continue;
     const uint32_t word = sh.word;
     const int r = (int)(word & 0x7Fu) - 1, kind = (int)((word >> 7) & 1u), step = (int)((word >> 8) & 0x3Fu),
               u = (int)(word >> 14);
     const double cut = sh.cut;
-    const int n = grp + j * G;
-    if (tid == 0) sh.seen[j] = r + 1;
+    const int s = sh.slice;
 
-    // ------------------------------------------------ reduce this workgroup's slice
+    // ------------------------------------------------ reduce the claimed slice
     const size_t tb = (size_t)n * Bp1;
     const double T = (double)a.temperature[n];
     const double invT = T > 0.0 ? 1.0 / T : 0.0;
@@ -509,14 +905,8 @@ __global__ void __launch_bounds__(kWalkThreads, 4) verify_walk_kernel(WalkArgs a
     const int tstar = g.i1 == 0x7FFFFFFF ? 0 : g.i1;
     int nn = a.n_nodes[n];
     nn = nn < 1 ? 1 : (nn > Bp1 ? Bp1 : nn);
-    const int o = sh.node0[j];
-    if (o >= 0) {
-      for (int q = 1 + tid; q < nn; q += kWalkThreads)
-        if (lpar[o + q] == u && ltok[o + q] == tstar) atomicMin(&sh.child, q);
-    } else {
-      for (int q = 1 + tid; q < nn; q += kWalkThreads)
-        if (a.parent[tb + q] == u && a.node_token[tb + q] == tstar) atomicMin(&sh.child, q);
-    }
+    for (int q = 1 + tid; q < nn; q += kWalkThreads)
+      if (a.parent[tb + q] == u && a.node_token[tb + q] == tstar) atomicMin(&sh.child, q);
     __syncthreads();
     const int child = sh.child;
     int32_t* ot = a.out_tokens + (size_t)n * Lp1;
@@ -548,11 +938,34 @@ constexpr size_t round_up(size_t x) {
 }
 
 struct WalkWsLayout {
-  size_t word, cut, done, py1, py2, pi, total;
+  size_t word, cut, claim, done, py1, py2, pi, seq_total;                // the walk kernel
+  size_t spec_cnt, spec_nodes, choice, rowdone, treedone, sy, si, total;  // speculation
+  int rcap;
 };
 
-WalkWsLayout walk_ws_layout(int N) {
-  WalkWsLayout w;
+// Slices per row of V elements of esz bytes: about kSliceVec vectors per
+// thread, at most kSlices and at most `resident` workgroups.
+long long walk_slices(long long V, size_t esz, long long resident) {
+  const long long nvec = V / (long long)(16 / esz);
+  long long S = (nvec + (long long)kSliceVec * kWalkThreads - 1) / ((long long)kSliceVec * kWalkThreads);
+  if (S > kSlices) S = kSlices;
+  if (S > resident) S = resident;
+  if (S < 1) S = 1;
+  return S;
+}
+
+// Rows the speculation may reduce in one launch of N trees of Bp1 nodes over
+// rows of V elements of esz bytes.
+long long spec_rows(int N, int Bp1, long long V, size_t esz) {
+  long long r = kSpecIntBytes / (V * (long long)esz);
+  const long long all = (long long)N * Bp1;
+  return r < all ? r : all;
+}
+
+// Workspace: the walk kernel's arrays, then (Bp1 > 0) the speculation's,
+// sized for rows of V elements of either element size.
+WalkWsLayout walk_ws_layout(int N, int Bp1 = 0, long long V = 0) {
+  WalkWsLayout w = {};
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t r = o;
@@ -561,26 +974,49 @@ WalkWsLayout walk_ws_layout(int N) {
   };
   w.word = take((size_t)N * sizeof(uint32_t));
   w.cut = take((size_t)N * sizeof(double));
+  w.claim = take((size_t)N * kMaxRounds * sizeof(int32_t));
   w.done = take((size_t)N * kMaxRounds * sizeof(int32_t));
   w.py1 = take((size_t)N * kSlices * sizeof(double));
   w.py2 = take((size_t)N * kSlices * sizeof(double));
   w.pi = take((size_t)N * kSlices * sizeof(int32_t));
-  w.total = o + 128;  // room to align the base
+  w.seq_total = o + 128;  // room to align the base
+  if (Bp1 > 0 && V > 0) {
+    long long rs = 0;  // rows x slices, the larger over the two element sizes
+    for (size_t esz : {(size_t)2, (size_t)4}) {
+      const long long v = spec_rows(N, Bp1, V, esz) * walk_slices(V, esz, kSlices);
+      if (v > rs) rs = v;
+    }
+    w.rcap = (int)spec_rows(N, Bp1, V, 2);
+    w.spec_cnt = take((size_t)N * 4 * sizeof(int32_t));
+    w.spec_nodes = take((size_t)N * Bp1 * sizeof(uint16_t));
+    w.choice = take((size_t)N * Bp1 * sizeof(int32_t));
+    w.rowdone = take((size_t)N * Bp1 * sizeof(int32_t));
+    w.treedone = take((size_t)N * sizeof(int32_t));
+    w.sy = take((size_t)rs * sizeof(double));
+    w.si = take((size_t)rs * sizeof(int32_t));
+  }
+  w.total = o + 128;
   return w;
 }
 
 }  // namespace
 
-size_t walk_ws_bytes(int N) { return walk_ws_layout(N).total; }
+size_t walk_ws_bytes(int N) { return walk_ws_layout(N).seq_total; }
+
+size_t walk_ws_bytes_full(int N, int Bp1, long long V) {
+  if (V < 1 || Bp1 < 1 || Bp1 > kMaxB1) return walk_ws_bytes(N);
+  return walk_ws_layout(N, Bp1, V).total;
+}
 
 hipError_t launch_verify_walk(const void* target, bool bf16, int N, int Bp1, long long V, int L,
                               const int32_t* node_token, const int32_t* parent, const int32_t* depth,
                               const int32_t* n_nodes, const float* temperature, const uint64_t* seed, int32_t* tau,
-                              int32_t* out_tokens, int32_t* path_nodes, int32_t* status, void* ws,
+                              int32_t* out_tokens, int32_t* path_nodes, int32_t* status, void* ws, size_t ws_bytes,
                               hipStream_t stream) {
   if (N == 0) return hipSuccess;
   const void* fn = bf16 ? reinterpret_cast<const void*>(&verify_walk_kernel<true>)
                         : reinterpret_cast<const void*>(&verify_walk_kernel<false>);
+  const size_t esz = bf16 ? 2 : 4;
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -589,26 +1025,44 @@ hipError_t launch_verify_walk(const void* target, bool bf16, int N, int Bp1, lon
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kWalkThreads, 0);
   if (e != hipSuccess) return e;
   long long resident = (long long)cus * (per_cu < 1 ? 1 : per_cu);
-  // slices per row: about kSliceVec vectors per thread, at most kSlices and
-  // at most the resident workgroups
-  const long long nvec = V / (bf16 ? 8 : 4);
-  long long S = (nvec + (long long)kSliceVec * kWalkThreads - 1) / ((long long)kSliceVec * kWalkThreads);
-  if (S > kSlices) S = kSlices;
-  if (S > resident) S = resident;
-  if (S < 1) S = 1;
-  // groups: as many as fit and at most one per tree; each group serves at
-  // most kMaxServed trees, so a larger batch is walked in several launches
-  long long Gmax = resident / S;
-  if (Gmax < 1) Gmax = 1;
-  const long long per_launch = Gmax * kMaxServed;
+  const long long S = walk_slices(V, esz, resident);
+  // trees per launch (the walk kernel keeps a byte per tree in LDS)
+  const long long per_launch = kWalkMaxTrees;
 
-  const WalkWsLayout l = walk_ws_layout(N);
+  // speculation when its arrays fit the workspace (the walk gives the same
+  // result without it)
+  const WalkWsLayout lf = walk_ws_layout(N, Bp1, V);
+  const bool spec = Bp1 <= kMaxB1 && lf.total <= ws_bytes;
+  const WalkWsLayout l = spec ? lf : walk_ws_layout(N);
+  int rcap = 0;
+  if (spec) {
+    const long long rs = (long long)((l.si - l.sy) / sizeof(double));  // rows x slices the arrays hold (at least)
+    long long r = spec_rows(N, Bp1, V, esz);
+    if (r * S > rs) r = rs / S;
+    rcap = (int)r;
+  }
+  const void* sfn = bf16 ? reinterpret_cast<const void*>(&walk_spec_kernel<true>)
+                         : reinterpret_cast<const void*>(&walk_spec_kernel<false>);
+  int spec_per_cu = 0;
+  if (spec) {
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&spec_per_cu, sfn, kWalkThreads, 0);
+    if (e != hipSuccess) return e;
+  }
+  const long long spec_grid = (long long)cus * (spec_per_cu < 1 ? 1 : spec_per_cu);
+
   char* w = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(ws) + 127) & ~uintptr_t(127));
   for (long long n0 = 0; n0 < N; n0 += per_launch) {
     const int nb = (int)(N - n0 < per_launch ? N - n0 : per_launch);
-    long long G = Gmax < nb ? Gmax : nb;
-    WalkArgs a;
-    a.target = static_cast<const char*>(target) + (size_t)n0 * Bp1 * V * (bf16 ? 2 : 4);
+    // workgroups: at most one per slice that can be open at once; groups of
+    // about S workgroups, at most one per tree
+    long long G = (long long)nb * S;
+    if (G > resident) G = resident;
+    long long groups = G / S;
+    if (groups < 1) groups = 1;
+    if (groups > nb) groups = nb;
+    WalkArgs a = {};
+    a.groups = (int)groups;
+    a.target = static_cast<const char*>(target) + (size_t)n0 * Bp1 * V * esz;
     a.N = nb;
     a.Bp1 = Bp1;
     a.L = L;
@@ -627,15 +1081,34 @@ hipError_t launch_verify_walk(const void* target, bool bf16, int N, int Bp1, lon
     a.status = status ? status + n0 : nullptr;
     a.word = reinterpret_cast<uint32_t*>(w + l.word) + n0;
     a.cut = reinterpret_cast<double*>(w + l.cut) + n0;
+    a.claim = reinterpret_cast<int32_t*>(w + l.claim) + (size_t)n0 * kMaxRounds;
     a.done = reinterpret_cast<int32_t*>(w + l.done) + (size_t)n0 * kMaxRounds;
     a.py1 = reinterpret_cast<double*>(w + l.py1) + (size_t)n0 * kSlices;
     a.py2 = reinterpret_cast<double*>(w + l.py2) + (size_t)n0 * kSlices;
     a.pi = reinterpret_cast<int32_t*>(w + l.pi) + (size_t)n0 * kSlices;
-    hipLaunchKernelGGL(walk_init_kernel, dim3((nb * kMaxRounds + 255) / 256), dim3(256), 0, stream, a);
+    a.spec = (spec && nb <= kSpecLaunchTrees && rcap > 0) ? 1 : 0;
+    if (a.spec) {
+      a.spec_rcap = rcap;
+      a.spec_cnt = reinterpret_cast<int32_t*>(w + l.spec_cnt) + (size_t)n0 * 4;
+      a.spec_nodes = reinterpret_cast<uint16_t*>(w + l.spec_nodes) + (size_t)n0 * Bp1;
+      a.choice = reinterpret_cast<int32_t*>(w + l.choice) + (size_t)n0 * Bp1;
+      a.rowdone = reinterpret_cast<int32_t*>(w + l.rowdone) + (size_t)n0 * Bp1;
+      a.treedone = reinterpret_cast<int32_t*>(w + l.treedone) + n0;
+      a.sy = reinterpret_cast<double*>(w + l.sy);
+      a.si = reinterpret_cast<int32_t*>(w + l.si);
+    }
+    hipLaunchKernelGGL(walk_prep_kernel, dim3(nb), dim3(kWalkThreads), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    void* args[] = {&a};
-    e = hipLaunchCooperativeKernel(fn, dim3((unsigned)(G * S)), dim3(kWalkThreads), args, 0, stream);
+    if (a.spec) {
+      if (bf16) hipLaunchKernelGGL(walk_spec_kernel<true>, dim3((unsigned)spec_grid), dim3(kWalkThreads), 0, stream, a);
+      else hipLaunchKernelGGL(walk_spec_kernel<false>, dim3((unsigned)spec_grid), dim3(kWalkThreads), 0, stream, a);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if (bf16) hipLaunchKernelGGL(verify_walk_kernel<true>, dim3((unsigned)G), dim3(kWalkThreads), 0, stream, a);
+    else hipLaunchKernelGGL(verify_walk_kernel<false>, dim3((unsigned)G), dim3(kWalkThreads), 0, stream, a);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

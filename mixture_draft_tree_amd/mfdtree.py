@@ -145,9 +145,14 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise ValueError(f"unsupported logits dtype {t.dtype}")
 
 
-def walk_workspace(N: int, device="cuda") -> torch.Tensor:
-    """A device workspace for mfd_verify_walk on N trees."""
-    n = workspace_size(MFD_OP_VERIFY_WALK, N, 1, 1, 1, 0)
+def walk_workspace(N: int, device="cuda", Bp1: Optional[int] = None, V: Optional[int] = None) -> torch.Tensor:
+    """A device workspace for mfd_verify_walk on N trees.  With the trees' row
+    count Bp1 and the vocabulary V it also holds the speculative pass's arrays
+    (without them the walk runs row after row; the results are the same)."""
+    if Bp1 is None or V is None:
+        n = workspace_size(MFD_OP_VERIFY_WALK, N, 1, 1, 1, -1)
+    else:
+        n = workspace_size(MFD_OP_VERIFY_WALK, N, 1, 1, V, Bp1 - 1)
     return torch.empty((max(n, 8) + 7) // 8, dtype=torch.int64, device=device)
 
 
@@ -417,7 +422,7 @@ def mfd_verify_walk(target_logits, L, node_token, parent, depth, n_nodes, temper
                                 _stream_handle(stream)), "mfd_verify_walk")
 
 
-WALK_NOALLOC_MAX_TREES = 1347
+WALK_NOALLOC_MAX_TREES = 1152
 
 
 def mfd_verify_walk_noalloc(target_logits, L, node_token, parent, depth, n_nodes, temperature, seed, tau,

@@ -66,7 +66,7 @@ class MixtureTreePath:
         W = (Bp1 + 63) // 64
         ws_bytes = max(M.workspace_size(M.MFD_OP_MIXTURE_THRESHOLD, N, K, L, V, B),
                        M.workspace_size(M.MFD_OP_TREE_BUILD, N, K, L, V, B),
-                       M.workspace_size(M.MFD_OP_VERIFY_WALK, N, K, L, V, B))
+                       M.workspace_size(M.MFD_OP_VERIFY_WALK, N, K, L, self.V_full, B))  # the walk reads full rows
         e = lambda shape, dt: torch.empty(shape, dtype=dt, device=d)
         self.buf = TreeBatch(
             lse=e((N, K, L), torch.float64),

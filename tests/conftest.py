@@ -14,9 +14,8 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # The HIP runtime grants cooperative launches (the verification walk's) on
-    # a GPU to one process at a time.  The plain-C caller walks in a child
-    # process, so it runs before this process makes any GPU call of its own.
+    # The plain-C caller's GPU round runs in a child process; it is collected
+    # first so that it meets a GPU this process has not touched yet.
     first = [it for it in items if it.get_closest_marker("own_process_gpu")]
     if first:
         rest = [it for it in items if not it.get_closest_marker("own_process_gpu")]

@@ -161,8 +161,11 @@ def test_mask_and_walk_reject():
 def test_walk_noalloc_limit_and_rejects():
     """The built-in walk workspace holds 2 MiB: 1347 trees fit, 1348 do not, and
     the larger call is refused before anything touches a device."""
-    assert M.workspace_size(M.MFD_OP_VERIFY_WALK, M.WALK_NOALLOC_MAX_TREES, 1, 1, 1, 0) <= 2 << 20
-    assert M.workspace_size(M.MFD_OP_VERIFY_WALK, M.WALK_NOALLOC_MAX_TREES + 1, 1, 1, 1, 0) > 2 << 20
+    assert M.workspace_size(M.MFD_OP_VERIFY_WALK, M.WALK_NOALLOC_MAX_TREES, 1, 1, 1, -1) <= 2 << 20
+    assert M.workspace_size(M.MFD_OP_VERIFY_WALK, M.WALK_NOALLOC_MAX_TREES + 1, 1, 1, 1, -1) > 2 << 20
+    # the speculative pass's arrays come on top when the trees' B and V are given
+    assert (M.workspace_size(M.MFD_OP_VERIFY_WALK, 64, 8, 15, 151936, 256) >
+            M.workspace_size(M.MFD_OP_VERIFY_WALK, 64, 8, 15, 151936, -1))
     args = [FAKE, M.MFD_F32, M.WALK_NOALLOC_MAX_TREES + 1, 9, 16, 4] + [FAKE] * 9 + [None, None]
     assert M._lib.mfd_verify_walk_noalloc(*args) == M.MFD_ERR_WORKSPACE
     assert f"N <= {M.WALK_NOALLOC_MAX_TREES}" in M.last_error()

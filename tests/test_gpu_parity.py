@@ -320,17 +320,18 @@ def test_walk_parity_small():
         N = len(trees)
         temps = torch.tensor([0.0, 1.0, 0.5, 2.0, 0.0, 1.0], dtype=torch.float32, device="cuda")
         seeds = torch.tensor([11, 12, 13, 2 ** 62 + 5, 15, -7], dtype=torch.int64, device="cuda")
-        tau = torch.empty(N, dtype=torch.int32, device="cuda")
-        ot = torch.empty((N, L + 1), dtype=torch.int32, device="cuda")
-        pn = torch.empty((N, L + 1), dtype=torch.int32, device="cuda")
-        st = torch.zeros(N, dtype=torch.int32, device="cuda")
-        M.mfd_verify_walk(Rt.cuda(), L, tok, par, dep, nn, temps, seeds, tau, ot, pn, st, ws=M.walk_workspace(N))
-        torch.cuda.synchronize()
-        assert st.eq(0).all()
-        for n in range(N):
-            seed_u64 = int(seeds[n].item()) & ((1 << 64) - 1)
-            check_walk(trees[n], R64[n], float(temps[n].item()), seed_u64, L, tau[n].item(),
-                       ot[n].cpu().numpy(), pn[n].cpu().numpy())
+        for ws in (M.walk_workspace(N), M.walk_workspace(N, Bp1=B + 1, V=V)):  # row by row, then speculative
+            tau = torch.empty(N, dtype=torch.int32, device="cuda")
+            ot = torch.empty((N, L + 1), dtype=torch.int32, device="cuda")
+            pn = torch.empty((N, L + 1), dtype=torch.int32, device="cuda")
+            st = torch.zeros(N, dtype=torch.int32, device="cuda")
+            M.mfd_verify_walk(Rt.cuda(), L, tok, par, dep, nn, temps, seeds, tau, ot, pn, st, ws=ws)
+            torch.cuda.synchronize()
+            assert st.eq(0).all()
+            for n in range(N):
+                seed_u64 = int(seeds[n].item()) & ((1 << 64) - 1)
+                check_walk(trees[n], R64[n], float(temps[n].item()), seed_u64, L, tau[n].item(),
+                           ot[n].cpu().numpy(), pn[n].cpu().numpy())
 
 
 def test_walk_near_tie_exact():
@@ -360,17 +361,18 @@ def test_walk_near_tie_exact():
     N = len(trees)
     tt = torch.tensor(temps, dtype=torch.float32, device="cuda")
     sd_t = torch.tensor([s if s < 2 ** 63 else s - 2 ** 64 for s in seeds], dtype=torch.int64, device="cuda")
-    tau = torch.empty(N, dtype=torch.int32, device="cuda")
-    ot = torch.empty((N, L + 1), dtype=torch.int32, device="cuda")
-    pn = torch.empty((N, L + 1), dtype=torch.int32, device="cuda")
-    st = torch.zeros(N, dtype=torch.int32, device="cuda")
-    M.mfd_verify_walk(Rt.cuda(), L, tok, par, dep, nn, tt, sd_t, tau, ot, pn, st, ws=M.walk_workspace(N))
-    torch.cuda.synchronize()
-    assert st.eq(0).all()
-    for n in range(N):
-        assert check_walk(trees[n], R64[n], temps[n], seeds[n], L, tau[n].item(), ot[n].cpu().numpy(),
-                          pn[n].cpu().numpy())
-        assert int(ot[n, 0].item()) == (V - 50 if deltas[n] > 0 else 100)
+    for ws in (M.walk_workspace(N), M.walk_workspace(N, Bp1=Bp1, V=V)):  # row by row, then speculative
+        tau = torch.empty(N, dtype=torch.int32, device="cuda")
+        ot = torch.empty((N, L + 1), dtype=torch.int32, device="cuda")
+        pn = torch.empty((N, L + 1), dtype=torch.int32, device="cuda")
+        st = torch.zeros(N, dtype=torch.int32, device="cuda")
+        M.mfd_verify_walk(Rt.cuda(), L, tok, par, dep, nn, tt, sd_t, tau, ot, pn, st, ws=ws)
+        torch.cuda.synchronize()
+        assert st.eq(0).all()
+        for n in range(N):
+            assert check_walk(trees[n], R64[n], temps[n], seeds[n], L, tau[n].item(), ot[n].cpu().numpy(),
+                              pn[n].cpu().numpy())
+            assert int(ot[n, 0].item()) == (V - 50 if deltas[n] > 0 else 100)
 
 
 def test_walk_bad_temperature():
@@ -457,7 +459,8 @@ def _run_workload(name, N=None, device_gen="cpu"):
         tau = torch.empty(N, dtype=torch.int32, device="cuda")
         ot = torch.empty((N, w.L + 1), dtype=torch.int32, device="cuda")
         pn = torch.empty_like(ot)
-        M.mfd_verify_walk(Rg, w.L, tok, par, dp, nnn, temps, seeds, tau, ot, pn, ws=M.walk_workspace(N))
+        M.mfd_verify_walk(Rg, w.L, tok, par, dp, nnn, temps, seeds, tau, ot, pn,
+                          ws=M.walk_workspace(N, Bp1=Bp1, V=w.V))  # with the speculative pass's arrays
         torch.cuda.synchronize()
         del Rg
         rpath, rtag, rshape = sp.dump("target", R)
@@ -826,3 +829,83 @@ def test_fused_tree_equals_separate_calls_small(case):
         out.append({f: getattr(P.buf, f).clone() for f in TREE_FIELDS})
     for f in TREE_FIELDS:
         assert torch.equal(out[0][f], out[1][f]), (f, out[0][f], out[1][f])
+
+
+# ------------------------------------------------------------------ the walk's speculative pass
+
+SPEC_CASES = [("tiny", 1), ("product", 1), ("single", 1), ("deep", 1), ("subset", 1), ("stress", 1),
+              ("batched_deep", 2), ("batched_deep", 4), ("batched", 64), ("batched_deep", 64)]
+
+
+@pytest.mark.parametrize("name,N", SPEC_CASES, ids=[f"{c[0]}-{c[1]}" for c in SPEC_CASES])
+def test_walk_speculation_equals_row_by_row(name, N):
+    """The walk with the speculative pass's workspace gives the row-by-row
+    walk's outputs bit for bit (the pass may or may not run: its choice is a
+    cost estimate; every route must give the same tokens)."""
+    w = synth.WORKLOADS[name]
+    b = synth.draft_batch(name, device="cuda", N=N, base_seed=21)
+    vmap = None if b.vocab_map is None else b.vocab_map.cuda()
+    modes = None if b.modes is None else b.modes.cuda()
+    P = MixtureTreePath(N, w.K, w.L, b.logits.shape[-1], w.B, vocab_map=vmap, V_full=w.V, modes=modes)
+    P.build(b.logits.cuda(), b.anchor.cuda(), b.pos_base.cuda())
+    torch.cuda.synchronize()
+    R = synth.target_logits(b, P.buf.depth, P.buf.n_nodes, device="cuda", base_seed=21).contiguous()
+    outs = []
+    for ws in (M.walk_workspace(N), M.walk_workspace(N, Bp1=w.B + 1, V=w.V)):
+        tau = torch.full((N,), -9, dtype=torch.int32, device="cuda")
+        ot = torch.full((N, w.L + 1), -9, dtype=torch.int32, device="cuda")
+        pn = torch.full((N, w.L + 1), -9, dtype=torch.int32, device="cuda")
+        st = torch.zeros(N, dtype=torch.int32, device="cuda")
+        M.mfd_verify_walk(R, w.L, P.buf.node_token, P.buf.parent, P.buf.depth, P.buf.n_nodes, b.temperature.cuda(),
+                          b.seed.cuda(), tau, ot, pn, st, ws=ws)
+        torch.cuda.synchronize()
+        assert st.eq(0).all()
+        outs.append((tau.cpu(), ot.cpu(), pn.cpu()))
+    for a_, b_ in zip(*outs):
+        assert torch.equal(a_, b_)
+    say(f"[walk speculation] {name} N={N}: equal, mean tau {outs[0][0].float().mean().item():.2f}")
+
+
+@pytest.mark.parametrize("T", [0.0, 1.0])
+def test_walk_speculation_on_a_chain_tree(T):
+    """A root with 1000 leaf children and one chain of depth 15 (N = 1, V =
+    151936): the walk's rows are the chain's, so the speculative pass reduces
+    the 15 rows of nodes that have a child and the walk ends at the leaf.
+    Against the oracle walk and the row-by-row walk, with the target following
+    the chain to its end, and leaving it half way."""
+    V, L, Bp1 = 151936, 15, 1016
+    g = torch.Generator().manual_seed(99)
+    toks = torch.randperm(V, generator=g)[:Bp1 + L].tolist()
+    tok = np.full(Bp1, -1, dtype=np.int64)
+    par = np.full(Bp1, -1, dtype=np.int64)
+    dep = np.full(Bp1, -1, dtype=np.int64)
+    tok[0], dep[0] = 5, 0
+    # rows 1..15: the chain (root -> c1 -> ... -> c15), rows 16..1015: leaves under the root
+    for i in range(1, L + 1):
+        tok[i], par[i], dep[i] = toks[i], i - 1, i
+    for i in range(L + 1, Bp1):
+        tok[i], par[i], dep[i] = toks[i], 0, 1
+    tree = {"node_token": tok, "parent": par, "depth": dep, "n_nodes": Bp1}
+    for leave_at in (L, 7):
+        R = torch.randn((1, Bp1, V), generator=g)
+        for i in range(0, L):
+            if i < leave_at:
+                R[0, i, tok[i + 1]] += 12.0
+        Rb = R.to(torch.bfloat16)
+        R64 = Rb[0].double().numpy()
+        tt, pp, dd, nn = upload_tree([tree], Bp1)
+        outs = []
+        for ws in (M.walk_workspace(1), M.walk_workspace(1, Bp1=Bp1, V=V)):
+            tau = torch.empty(1, dtype=torch.int32, device="cuda")
+            ot = torch.empty((1, L + 1), dtype=torch.int32, device="cuda")
+            pn = torch.empty_like(ot)
+            st = torch.zeros(1, dtype=torch.int32, device="cuda")
+            M.mfd_verify_walk(Rb.cuda(), L, tt, pp, dd, nn, torch.tensor([T], device="cuda"),
+                              torch.tensor([31], dtype=torch.int64, device="cuda"), tau, ot, pn, st, ws=ws)
+            torch.cuda.synchronize()
+            assert st.item() == 0
+            check_walk(tree, R64, T, 31, L, tau.item(), ot[0].cpu().numpy(), pn[0].cpu().numpy())
+            outs.append((tau.cpu(), ot.cpu(), pn.cpu()))
+        for a_, b_ in zip(*outs):
+            assert torch.equal(a_, b_)
+        say(f"[walk speculation chain] T={T} leave_at={leave_at}: tau {outs[0][0].item()}")
