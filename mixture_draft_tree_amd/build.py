@@ -64,6 +64,7 @@ def build(jobs: int = 8) -> str:
     os.replace(tmp, LIB)
     build_c_smoke()
     build_hostsan(jobs)
+    build_wave_check()
     return LIB
 
 
@@ -83,6 +84,22 @@ def build_c_smoke() -> None:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"C smoke build failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+
+
+WAVE_CHECK_SRC = os.path.join(ROOT, "tests", "c", "wave_primitives.hip")
+WAVE_CHECK_BIN = os.path.join(ROOT, "tests", "c", "wave_primitives")
+
+
+def build_wave_check() -> None:
+    """The standalone GPU check of the kernels' wave-level primitives (built
+    with the library's device flags)."""
+    if not os.path.exists(WAVE_CHECK_SRC):
+        return
+    flags = [f for f in COMMON if f != "-fPIC"] + ["-I", CSRC]
+    cmd = [hipcc()] + flags + [WAVE_CHECK_SRC, "-o", WAVE_CHECK_BIN]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"wave primitive check build failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
 
 
 HOSTSAN_DIR = os.path.join(ROOT, "tests", "c", "hostsan")

@@ -296,11 +296,9 @@ __device__ __forceinline__ void wave_append(bool p, uint64_t c, uint64_t* buf, i
 __device__ __forceinline__ void pick_digit_into(Shared& S, int remaining) {
   int digit = 0, above = 0;
   wave_pick_digit(S.hist, remaining, &digit, &above);
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) {
-    digit = max(digit, __shfl_xor(digit, o, kWave));
-    above = max(above, __shfl_xor(above, o, kWave));
-  }
+  const auto mx = [](int x, int y) { return x > y ? x : y; };
+  digit = wave_allreduce(digit, mx);
+  above = wave_allreduce(above, mx);
   if (lane_id() == 0) {
     S.sh[0] = digit;
     S.sh[1] = above;
@@ -474,8 +472,7 @@ __global__ void __launch_bounds__(kThreads, 5) lsm_topk_kernel(const typename El
   }
   // Bias: the sample maximum M0 in log2 units (0 if M0 is not finite).
   uint32_t mkey = max(max(k0, k1), max(k2, k3));
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) mkey = max(mkey, (uint32_t)__shfl_xor((int)mkey, o, kWave));
+  mkey = wave_allreduce(mkey, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
   const float m0 = thr_float<BF16>(mkey);
   const float bias = isfinite(m0) ? m0 * kLog2e : 0.f;
   // Staging cut on a vector's term sum (see consume_vector); 0 stages every vector.
@@ -501,8 +498,7 @@ __global__ void __launch_bounds__(kThreads, 5) lsm_topk_kernel(const typename El
   }
 
   // ------------------------------------------------------------ log-normaliser
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, kWave);
+  s = wave_allreduce(s, [](double x, double y) { return x + y; });
   if (lane == 0) {
     S.red_s[wid] = s;
     S.cnt[wid] = sg.scnt;
@@ -528,8 +524,7 @@ __global__ void __launch_bounds__(kThreads, 5) lsm_topk_kernel(const typename El
 #pragma unroll
       for (int j = 0; j < VEC; ++j) mx = fmaxf(mx, vec_val<BF16>(v, j));
     });
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+    mx = wave_allreduce(mx, [](float x, float y) { return fmaxf(x, y); });
     __syncthreads();
     if (lane == 0) S.red_max[wid] = mx;
     __syncthreads();
@@ -549,8 +544,7 @@ __global__ void __launch_bounds__(kThreads, 5) lsm_topk_kernel(const typename El
         for (int j = 0; j < VEC; ++j) acc += valid ? term(vec_val<BF16>(v, j), b2) : 0.f;
         s2 += (double)acc;
       });
-#pragma unroll
-      for (int o = kWave / 2; o > 0; o >>= 1) s2 += __shfl_xor(s2, o, kWave);
+      s2 = wave_allreduce(s2, [](double x, double y) { return x + y; });
       if (lane == 0) S.red_s[wid] = s2;
       __syncthreads();
       double sum2 = 0.0;

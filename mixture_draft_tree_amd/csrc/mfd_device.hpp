@@ -53,22 +53,96 @@ __device__ __forceinline__ double f64_from_key(uint64_t k) {
 }
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float((b & 0xFFFFu) << 16); }
 
+// ---------------------------------------------------------------- lane exchange
+// Cross-lane moves that stay in the vector ALU instead of going through the
+// LDS crossbar (ds_bpermute): DPP quad permutes and row rotations within rows
+// of 16 lanes, and the gfx950 permlane swaps across rows and wave halves.
+// The whole wave must be active.
+
+// DPP controls (gfx9 encoding)
+constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kDppRowShr1 = 0x111;  // row_shr:n = 0x110 + n: lane i takes lane i - n of its row
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppRowRor4 = 0x124;   // row_ror:n = 0x120 + n: lane i takes lane (i - n) mod 16 of its row
+constexpr int kDppRowRor8 = 0x128;
+constexpr int kDppRowRor12 = 0x12C;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  // lanes whose source lies outside the row read 0 (the "old" operand)
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// v of lane (lane ^ s), s in {1, 2, 4, 8, 16, 32}.
+__device__ __forceinline__ uint32_t xor_lanes(uint32_t v, int s) {
+  const int lane = lane_id();
+  switch (s) {
+    case 1:
+      return dpp_u32<kDppQuadXor1>(v);
+    case 2:
+      return dpp_u32<kDppQuadXor2>(v);
+    case 4: {
+      const uint32_t below = dpp_u32<kDppRowRor4>(v), above = dpp_u32<kDppRowRor12>(v);
+      return (lane & 4) ? below : above;
+    }
+    case 8:
+      return dpp_u32<kDppRowRor8>(v);
+    case 16: {
+      // the swap hands each odd row the even row below it, and each even row the odd row above
+      const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+      return (lane & 16) ? p[0] : p[1];
+    }
+    default: {
+      const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+      return (lane & 32) ? p[0] : p[1];
+    }
+  }
+}
+__device__ __forceinline__ int xor_lanes(int v, int s) { return (int)xor_lanes((uint32_t)v, s); }
+__device__ __forceinline__ float xor_lanes(float v, int s) {
+  return __uint_as_float(xor_lanes(__float_as_uint(v), s));
+}
+__device__ __forceinline__ uint64_t xor_lanes(uint64_t v, int s) {
+  const uint32_t lo = xor_lanes((uint32_t)v, s), hi = xor_lanes((uint32_t)(v >> 32), s);
+  return ((uint64_t)hi << 32) | (uint64_t)lo;
+}
+__device__ __forceinline__ double xor_lanes(double v, int s) {
+  return __longlong_as_double((long long)xor_lanes((uint64_t)__double_as_longlong(v), s));
+}
+
 // ---------------------------------------------------------------- scans
 
+// Inclusive sum over lanes 0..lane: within each row of 16 lanes by four DPP
+// shifted adds (Hillis-Steele), then the totals of the rows below.
 __device__ __forceinline__ int wave_inclusive_scan(int x) {
-  const int lane = lane_id();
+  uint32_t u = (uint32_t)x;
+  u += dpp_u32<kDppRowShr1>(u);
+  u += dpp_u32<kDppRowShr2>(u);
+  u += dpp_u32<kDppRowShr4>(u);
+  u += dpp_u32<kDppRowShr8>(u);
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)u, 15);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)u, 31);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)u, 47);
+  const int row = lane_id() >> 4;
+  u += (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+  return (int)u;
+}
+
+// op over all 64 lanes (xor strides 32, 16, ..., 1).  The loop runs over the
+// stride's log2, a linear induction variable, so it unrolls fully and every
+// xor_lanes gets a constant stride.
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_allreduce(T x, Op op) {
 #pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
+  for (int lg = 5; lg >= 0; --lg) x = op(x, xor_lanes(x, 1 << lg));
   return x;
 }
 
 __device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
-  return x;
+  return wave_allreduce(x, [](int a, int b) { return a + b; });
 }
 
 // Exclusive scan over the block; `total` receives the block sum.  `smem` needs
@@ -120,6 +194,9 @@ __device__ __forceinline__ void block_bitonic_sort(uint64_t* a, int n) {
   }
 }
 
+// v of lane (lane ^ m) through the LDS crossbar (ds_bpermute), for a mask m
+// known only at run time: the exchanges of several registers stay in flight
+// together, where xor_lanes would branch on m for each of them.
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   const int lo = __shfl_xor((int)(uint32_t)v, m, kWave);
   const int hi = __shfl_xor((int)(uint32_t)(v >> 32), m, kWave);
@@ -128,17 +205,21 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
 
 // Sorts the 2*NT values held two per thread (thread t holds elements 2t and
 // 2t+1 in a0, a1) ascending, with the same bitonic network as
-// block_bitonic_sort.  Strides inside a wave go through lane shuffles; only the
-// strides that cross waves go through `xchg` (2*NT uint64 of LDS), two
-// barriers each.  Every thread of the block must call it.
+// block_bitonic_sort.  Strides inside a wave go through xor_lanes (constant
+// after unrolling); only the strides that cross waves go through `xchg`
+// (2*NT uint64 of LDS), two barriers each.  Every thread of the block must
+// call it.
 template <int NT>
 __device__ __forceinline__ void block_sort_pairs(uint64_t& a0, uint64_t& a1, uint64_t* xchg) {
   constexpr int P = 2 * NT;
+  constexpr int LP = __builtin_ctz(P);
   const int i0 = 2 * (int)threadIdx.x;
 #pragma unroll
-  for (int size = 2; size <= P; size <<= 1) {
+  for (int lsize = 1; lsize <= LP; ++lsize) {
+    const int size = 1 << lsize;
 #pragma unroll
-    for (int s = size >> 1; s > 0; s >>= 1) {
+    for (int ls = lsize - 1; ls >= 0; --ls) {
+      const int s = 1 << ls;
       const bool up = (i0 & size) == 0;
       if (s == 1) {
         const uint64_t lo = a0 < a1 ? a0 : a1, hi = a0 < a1 ? a1 : a0;
@@ -148,8 +229,8 @@ __device__ __forceinline__ void block_sort_pairs(uint64_t& a0, uint64_t& a1, uin
       }
       uint64_t b0, b1;
       if (s < 2 * kWave) {
-        b0 = shfl_xor_u64(a0, s >> 1);
-        b1 = shfl_xor_u64(a1, s >> 1);
+        b0 = xor_lanes(a0, s >> 1);
+        b1 = xor_lanes(a1, s >> 1);
       } else {
         xchg[i0] = a0;
         xchg[i0 + 1] = a1;
@@ -167,19 +248,22 @@ __device__ __forceinline__ void block_sort_pairs(uint64_t& a0, uint64_t& a1, uin
 }
 
 // Sorts the NT values held one per thread (thread t holds element t) ascending
-// with the bitonic network; strides inside a wave use lane shuffles, strides
+// with the bitonic network; strides inside a wave use xor_lanes, strides
 // across waves go through `xchg` (NT uint64 of LDS, two barriers each).  Every
 // thread of the block must call it.
 template <int NT>
 __device__ __forceinline__ void block_sort_single(uint64_t& a, uint64_t* xchg) {
   const int t = (int)threadIdx.x;
+  constexpr int LN = __builtin_ctz(NT);
 #pragma unroll
-  for (int size = 2; size <= NT; size <<= 1) {
+  for (int lsize = 1; lsize <= LN; ++lsize) {
+    const int size = 1 << lsize;
 #pragma unroll
-    for (int s = size >> 1; s > 0; s >>= 1) {
+    for (int ls = lsize - 1; ls >= 0; --ls) {
+      const int s = 1 << ls;
       uint64_t b;
       if (s < kWave) {
-        b = shfl_xor_u64(a, s);
+        b = xor_lanes(a, s);
       } else {
         xchg[t] = a;
         __syncthreads();
@@ -194,7 +278,8 @@ __device__ __forceinline__ void block_sort_single(uint64_t& a, uint64_t* xchg) {
 
 // block_bitonic_sort's network with each wave's segment of P keys held in
 // registers: thread (wave w, lane l) holds elements w*64E + e*64 + l,
-// e < E.  Strides below 64 are lane shuffles, strides from 64 to 64E - 1 swap
+// e < E.  Strides below 64 are lane exchanges (shfl_xor_u64: the stride is a
+// run-time value here), strides from 64 to 64E - 1 swap
 // registers within a thread, and only strides of a whole segment or more
 // go through LDS, one barrier each (plus one on either side of such a run).
 // P is a power of two: 64 <= P <= NT for E = 1, P = E * NT for E > 1.
@@ -290,10 +375,12 @@ __device__ __forceinline__ void block_sort_keys(uint64_t* a, int P) {
 __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t a) {
   const int t = lane_id();
 #pragma unroll
-  for (int size = 2; size <= kWave; size <<= 1) {
+  for (int lsize = 1; lsize <= 6; ++lsize) {
+    const int size = 1 << lsize;
 #pragma unroll
-    for (int s = size >> 1; s > 0; s >>= 1) {
-      const uint64_t b = shfl_xor_u64(a, s);
+    for (int ls = lsize - 1; ls >= 0; --ls) {
+      const int s = 1 << ls;
+      const uint64_t b = xor_lanes(a, s);
       const bool keep_max = ((t & s) == 0) == ((t & size) == 0);
       a = keep_max ? (a < b ? b : a) : (a < b ? a : b);
     }
@@ -357,12 +444,8 @@ __device__ __forceinline__ uint64_t block_kth_largest(int n, int rank, Get get, 
       int digit = 0, above = 0;
       wave_pick_digit(hist, remaining, &digit, &above);
       // exactly one lane found it; spread with a max-reduce
-      int d = digit, a = above;
-#pragma unroll
-      for (int o = kWave / 2; o > 0; o >>= 1) {
-        d = max(d, __shfl_xor(d, o, kWave));
-        a = max(a, __shfl_xor(a, o, kWave));
-      }
+      const auto mx = [](int x, int y) { return x > y ? x : y; };
+      const int d = wave_allreduce(digit, mx), a = wave_allreduce(above, mx);
       if (threadIdx.x == 0) {
         sh[0] = d;
         sh[1] = a;

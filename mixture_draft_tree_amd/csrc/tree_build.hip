@@ -230,7 +230,7 @@ __device__ __forceinline__ double kth_lower_bound(int n, int rank, Score score, 
 // `cap`) then rank themselves by direct comparison.  Falls back to the full
 // 64-bit radix select if the bucket does not fit.  Barriers inside.
 template <typename Score>
-__device__ double exact_kth(int n, int rank, Score score, Ctl& ctl, uint64_t* buf, int cap) {
+__device__ __forceinline__ double exact_kth(int n, int rank, Score score, Ctl& ctl, uint64_t* buf, int cap) {
   const int tid = threadIdx.x;
   const double lb = kth_lower_bound(n, rank, score, [](int) { return true; }, ctl);
   const uint64_t b16 = f64_key(lb) >> 48;
@@ -285,8 +285,8 @@ __device__ double exact_kth(int n, int rank, Score score, Ctl& ctl, uint64_t* bu
 // each child's score in `my_s` (lane = the child's position in that order).
 // Returns the number of children, or -1, writing nothing, if the level does
 // not fit.  Wave 0 only, no block barrier.
-__device__ int small_level(const TreeArgs& a, const Tree& t, int n, int d, int fsize, double tau,
-                           const double* norm, Ctl& ctl, uint16_t* nk, double& my_s) {
+__device__ __forceinline__ int small_level(const TreeArgs& a, const Tree& t, int n, int d, int fsize, double tau,
+                                           const double* norm, Ctl& ctl, uint16_t* nk, double& my_s) {
   const int lane = lane_id();
   const int K = a.K, L = a.L, k = a.k, Lp1 = L + 1;
   int m = 0, pnode = 0, cnt = 0;
@@ -379,8 +379,7 @@ __device__ int small_level(const TreeArgs& a, const Tree& t, int n, int d, int f
   const int nexth = after ? __builtin_ctzll(after) : C;
   int runlen = head ? nexth - lane : 0;
   int maxlen = runlen;
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) maxlen = max(maxlen, __shfl_xor(maxlen, o, kWave));
+  maxlen = wave_allreduce(maxlen, [](int x, int y) { return x > y ? x : y; });
   double best = -INFINITY;
   int mu = -1;
   for (int q = 0; q < maxlen; ++q) {
@@ -419,7 +418,7 @@ __device__ int small_level(const TreeArgs& a, const Tree& t, int n, int d, int f
 
 // Chunked exclusive scan of `val(i)` for i in [0, n) writing out[i]; returns the total.
 template <typename Val, typename Out>
-__device__ int block_scan_range(int n, Val val, Out out, int* scan_smem) {
+__device__ __forceinline__ int block_scan_range(int n, Val val, Out out, int* scan_smem) {
   int carry = 0;
   for (int base = 0; base < n; base += kNT) {
     const int i = base + (int)threadIdx.x;
@@ -436,8 +435,8 @@ __device__ int block_scan_range(int n, Val val, Out out, int* scan_smem) {
 // The search.  Returns with ctl.node_count nodes (node 0 = root) and
 // ctl.ent_count entries; ctl.fail set on capacity overflow.
 template <bool BUILD>
-__device__ void level_search(const TreeArgs& a, const Tree& t, int n, Ctl& ctl, uint64_t* keys, const double* norm,
-                             uint16_t* nk) {
+__device__ __forceinline__ void level_search(const TreeArgs& a, const Tree& t, int n, Ctl& ctl, uint64_t* keys,
+                                             const double* norm, uint16_t* nk) {
   const int K = a.K, L = a.L, k = a.k, B = a.B;
   const int tid = threadIdx.x;
   const int Lp1 = L + 1;
