@@ -45,6 +45,9 @@ constexpr int kNT = 1024;
 constexpr int kMaxSort = 16384;
 constexpr size_t kTreeLdsMax = 156 * 1024;  // LDS one workgroup may use (of 160 KB per CU)
 constexpr int kFirstQ = 64;  // depth-1 candidates per mode behind the threshold call's starting bound
+// Leading candidates of every (mode, position) row staged in LDS when they fit
+// (the searches mostly look at a row's first few candidates).
+constexpr int kPreQ = 16;
 
 // Per-tree workspace layout (offsets in bytes from the tree's base).
 struct WsLayout {
@@ -94,6 +97,8 @@ struct TreeArgs {
   int K, L, k, B;
   int sort_cap, ent_cap, node_cap, tie_cap;
   int nk_lds;  // threshold call: the nodes' 16-bit score keys are kept in LDS
+  int pre_q;   // leading candidates per row staged in LDS (0: none)
+  int pre_off; // their byte offset in LDS: raw values [K * L * pre_q], then ids
   unsigned char* ws;
   size_t ws_stride;
   int32_t* status;
@@ -136,6 +141,7 @@ struct Ctl {
   int kept[32];
   int fcount[kNT / kWave];
   int small;  // children of a level built by small_level, -1 if it did not fit
+  int up;     // a node of this level has a 16-bit score key above the threshold's
 };
 
 // Bytes of LDS before the optional node-key array: sort keys, norms, Ctl.
@@ -177,6 +183,29 @@ __device__ __forceinline__ int count_children(const float* vals, int k, double r
     const float x = vals[mid];
     const bool ok = (x != -INFINITY) && ((raw + (double)x) - norm >= tau);
     if (ok) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// count_children when the row's first q candidates (q <= k) are also in LDS
+// (pre): the search stays there unless all q of them qualify.
+__device__ __forceinline__ int count_children_pre(const float* pre, int q, const float* vals, int k, double raw,
+                                                  double norm, double tau) {
+  auto ok = [&](float x) { return (x != -INFINITY) && ((raw + (double)x) - norm >= tau); };
+  if (q > 0 && !ok(pre[q - 1])) {
+    int lo = 0, hi = q - 1;  // answer in [lo, hi]
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (ok(pre[mid])) lo = mid + 1;
+      else hi = mid;
+    }
+    return lo;
+  }
+  int lo = q, hi = k;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (ok(vals[mid])) lo = mid + 1;
     else hi = mid;
   }
   return lo;
@@ -286,7 +315,8 @@ __device__ __forceinline__ double exact_kth(int n, int rank, Score score, Ctl& c
 // Returns the number of children, or -1, writing nothing, if the level does
 // not fit.  Wave 0 only, no block barrier.
 __device__ __forceinline__ int small_level(const TreeArgs& a, const Tree& t, int n, int d, int fsize, double tau,
-                                           const double* norm, Ctl& ctl, uint16_t* nk, double& my_s) {
+                                           const double* norm, Ctl& ctl, uint16_t* nk, const float* pre_raw,
+                                           const int32_t* pre_id, double& my_s) {
   const int lane = lane_id();
   const int K = a.K, L = a.L, k = a.k, Lp1 = L + 1;
   int m = 0, pnode = 0, cnt = 0;
@@ -301,10 +331,19 @@ __device__ __forceinline__ int small_level(const TreeArgs& a, const Tree& t, int
     pnode = t.ent_node[e];
     nrm = norm[m * Lp1 + d];
     const size_t row = ((size_t)(n * K + m) * L + (d - 1)) * k;
+    if (a.pre_q >= 8) {
+      const int pr = (m * L + (d - 1)) * a.pre_q;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      v[j] = j < k ? a.topk_raw[row + j] : -INFINITY;
-      id[j] = j < k ? a.topk_id[row + j] : 0;
+      for (int j = 0; j < 8; ++j) {
+        v[j] = pre_raw[pr + j];
+        id[j] = pre_id[pr + j];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        v[j] = j < k ? a.topk_raw[row + j] : -INFINITY;
+        id[j] = j < k ? a.topk_id[row + j] : 0;
+      }
     }
     bool run = true;
 #pragma unroll
@@ -392,6 +431,8 @@ __device__ __forceinline__ int small_level(const TreeArgs& a, const Tree& t, int
     }
   }
   const int node0 = ctl.node_count, ent0 = ctl.ent_count;
+  const uint64_t kt = f64_key(tau) >> 48;
+  const bool up = __ballot(head && (f64_key(best) >> 48) > kt) != 0ull;
   if (head) {
     const int node = node0 + g;
     t.node_parent[node] = (int)(sk >> 40);
@@ -411,6 +452,7 @@ __device__ __forceinline__ int small_level(const TreeArgs& a, const Tree& t, int
   if (lane == 0) {
     ctl.node_count = node0 + G;
     ctl.ent_count = ent0 + C;
+    ctl.up = up ? 1 : 0;
   }
   my_s = sv ? ss : -INFINITY;
   return C;
@@ -436,20 +478,29 @@ __device__ __forceinline__ int block_scan_range(int n, Val val, Out out, int* sc
 // ctl.ent_count entries; ctl.fail set on capacity overflow.
 template <bool BUILD>
 __device__ __forceinline__ void level_search(const TreeArgs& a, const Tree& t, int n, Ctl& ctl, uint64_t* keys,
-                                             const double* norm, uint16_t* nk) {
+                                             const double* norm, uint16_t* nk, const float* pre_raw,
+                                             const int32_t* pre_id) {
   const int K = a.K, L = a.L, k = a.k, B = a.B;
   const int tid = threadIdx.x;
   const int Lp1 = L + 1;
 
   for (int d = 1; d <= L; ++d) {
-    if (tid == 0) ctl.level_start[d] = ctl.node_count;
+    if (tid == 0) {
+      ctl.level_start[d] = ctl.node_count;
+      ctl.up = 0;
+    }
     __syncthreads();
     const int fsize = ctl.fsize;
     if (fsize == 0 || ctl.fail) break;
     double tau = ctl.tau;
 
-    // (threshold call) raise tau to the B-th best unique node so far
+    // (threshold call) raise tau to the B-th best unique node so far.  The
+    // raise works on 16-bit score keys; if no node of this level has a key
+    // above tau's, no key above tau's is among the B best either (the older
+    // nodes above it are fewer than B after the last raise, and a bisection
+    // only lifts tau), so the bound it would find is at most tau: skipped.
     auto raise_tau = [&]() {
+      if (!ctl.up) return;
       if (nk) {
         // on the 16-bit keys in LDS: the B-th largest key among those at or
         // above tau's stands for B distinct nodes scoring at least its value
@@ -491,7 +542,7 @@ __device__ __forceinline__ void level_search(const TreeArgs& a, const Tree& t, i
       const int ent0 = ctl.ent_count;
       double my_s = -INFINITY;
       if (tid < kWave) {
-        const int cs = small_level(a, t, n, d, fsize, tau, norm, ctl, nk, my_s);
+        const int cs = small_level(a, t, n, d, fsize, tau, norm, ctl, nk, pre_raw, pre_id, my_s);
         if (tid == 0) ctl.small = cs;
       }
       __syncthreads();
@@ -516,6 +567,9 @@ __device__ __forceinline__ void level_search(const TreeArgs& a, const Tree& t, i
       const int e = t.fr[f];
       const int m = t.ent_mode[e];
       const float* vals = a.topk_raw + ((size_t)(n * K + m) * L + (d - 1)) * k;
+      if (a.pre_q)
+        return count_children_pre(pre_raw + (m * L + (d - 1)) * a.pre_q, a.pre_q, vals, k, t.ent_raw[e],
+                                  norm[m * Lp1 + d], th);
       return count_children(vals, k, t.ent_raw[e], norm[m * Lp1 + d], th);
     };
     int C;
@@ -586,8 +640,10 @@ __device__ __forceinline__ void level_search(const TreeArgs& a, const Tree& t, i
       const int m = t.ent_mode[e];
       const int j = c - t.fr_off[f];
       const size_t row = ((size_t)(n * K + m) * L + (d - 1)) * k;
-      const float x = a.topk_raw[row + j];
-      const int tok = a.topk_id[row + j];
+      const bool staged = j < a.pre_q;
+      const int pr = (m * L + (d - 1)) * a.pre_q + j;
+      const float x = staged ? pre_raw[pr] : a.topk_raw[row + j];
+      const int tok = staged ? pre_id[pr] : a.topk_id[row + j];
       const double raw = t.ent_raw[e] + (double)x;
       const double s = raw - norm[m * Lp1 + d];
       const int pnode = t.ent_node[e];
@@ -625,6 +681,7 @@ __device__ __forceinline__ void level_search(const TreeArgs& a, const Tree& t, i
         }
       }
       const int node = node0 + g;
+      if ((f64_key(best) >> 48) > (f64_key(tau) >> 48)) ctl.up = 1;
       const int c0 = (int)(keys[i] & 0x7FFFu);
       t.node_parent[node] = t.ch_pnode[c0];
       t.node_token[node] = t.ch_tok[c0];
@@ -690,6 +747,8 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
   uint16_t* nk = (kRaise && a.nk_lds)
                      ? reinterpret_cast<uint16_t*>(smem_raw + ((tree_lds_base(a.sort_cap, K, L) + 15) & ~size_t(15)))
                      : nullptr;
+  float* pre_raw = a.pre_q ? reinterpret_cast<float*>(smem_raw + a.pre_off) : nullptr;
+  int32_t* pre_id = a.pre_q ? reinterpret_cast<int32_t*>(pre_raw + (size_t)K * L * a.pre_q) : nullptr;
   const Tree t = tree_ptrs(a, n);
   // a tree built from its first K_n futures only: the inactive modes' rows
   // are never read (the strides keep the full K)
@@ -707,6 +766,13 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
   for (int q = tid; q < Kn * L; q += kNT) {
     const int m = q / L, i = q - m * L;
     norm[m * Lp1 + i + 1] = a.lse[(size_t)n * K * L + q];
+  }
+  // the rows' leading candidates (past k: -inf), loaded with the norms
+  for (int q = tid; q < Kn * L * a.pre_q; q += kNT) {
+    const int r = q / a.pre_q, j = q - r * a.pre_q;  // r = m * L + position
+    const size_t at = ((size_t)n * K * L + r) * k + j;
+    pre_raw[q] = j < k ? a.topk_raw[at] : -INFINITY;
+    pre_id[q] = j < k ? a.topk_id[at] : 0;
   }
   __syncthreads();
   for (int m = tid; m < Kn; m += kNT) {
@@ -826,7 +892,7 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
     }
   }
 
-  level_search<!kRaise>(a, t, n, ctl, keys, norm, nk);
+  level_search<!kRaise>(a, t, n, ctl, keys, norm, nk, pre_raw, pre_id);
 
   const int nc = ctl.node_count;
   const int fail = ctl.fail;
@@ -882,65 +948,72 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
     const int ge_in = block_sum<kNT>(lge, ctl.scan);
     double cstar = cutoff_in;
     int gt = gt_in;
-    if (!(gt_in < nsel && ge_in >= nsel)) {
-      cstar = exact_kth(M, nsel, [&](int i) { return t.node_S[i + 1]; }, ctl, keys, a.sort_cap);
-      lgt = 0;
-      for (int i = 1 + tid; i < nc; i += kNT) lgt += (t.node_S[i] > cstar) ? 1 : 0;
-      gt = block_sum<kNT>(lgt, ctl.scan);
-    }
-    const int need = nsel - gt;
-    // collect the ties at cstar (node ids in node_aux order via keys[] as int list)
-    int32_t* tied = reinterpret_cast<int32_t*>(keys);
-    const int T = block_scan_range(
-        M, [&](int i) { return (t.node_S[i + 1] == cstar) ? 1 : 0; },
-        [&](int i, int off, int v) {
-          if (v && off < a.tie_cap) tied[off] = i + 1;
-        },
-        ctl.scan);
-    for (int i = 1 + tid; i < nc; i += kNT) t.node_aux[i] = (t.node_S[i] > cstar) ? 1 : 0;
-    __syncthreads();
-    if (T > a.tie_cap) {
-      if (tid == 0) {
-        if (a.status) atomicOr(&a.status[n], MFD_TREE_CAPACITY);
-        ctl.fail = 1;
-      }
+    const bool exact_in = gt_in < nsel && ge_in >= nsel;
+    if (exact_in && ge_in == nsel) {
+      // exactly nsel nodes reach the cut-off: no ties to break
+      for (int i = 1 + tid; i < nc; i += kNT) t.node_aux[i] = (t.node_S[i] >= cutoff_in) ? 1 : 0;
+      __syncthreads();
     } else {
-      // token paths of the tied nodes, then rank by (best mode, tokens)
-      int32_t* paths = tied + a.tie_cap;
-      for (int q = tid; q < T; q += kNT) {
-        int node = tied[q];
-        const int dq = t.node_depth[node];
-        for (int x = 0; x < L; ++x) paths[q * L + x] = -1;
-        while (node > 0) {
-          paths[q * L + t.node_depth[node] - 1] = t.node_token[node];
-          node = t.node_parent[node];
+      if (!exact_in) {
+        cstar = exact_kth(M, nsel, [&](int i) { return t.node_S[i + 1]; }, ctl, keys, a.sort_cap);
+        lgt = 0;
+        for (int i = 1 + tid; i < nc; i += kNT) lgt += (t.node_S[i] > cstar) ? 1 : 0;
+        gt = block_sum<kNT>(lgt, ctl.scan);
+      }
+      const int need = nsel - gt;
+      // collect the ties at cstar (node ids in node_aux order via keys[] as int list)
+      int32_t* tied = reinterpret_cast<int32_t*>(keys);
+      const int T = block_scan_range(
+          M, [&](int i) { return (t.node_S[i + 1] == cstar) ? 1 : 0; },
+          [&](int i, int off, int v) {
+            if (v && off < a.tie_cap) tied[off] = i + 1;
+          },
+          ctl.scan);
+      for (int i = 1 + tid; i < nc; i += kNT) t.node_aux[i] = (t.node_S[i] > cstar) ? 1 : 0;
+      __syncthreads();
+      if (T > a.tie_cap) {
+        if (tid == 0) {
+          if (a.status) atomicOr(&a.status[n], MFD_TREE_CAPACITY);
+          ctl.fail = 1;
         }
-        (void)dq;
+      } else {
+        // token paths of the tied nodes, then rank by (best mode, tokens)
+        int32_t* paths = tied + a.tie_cap;
+        for (int q = tid; q < T; q += kNT) {
+          int node = tied[q];
+          const int dq = t.node_depth[node];
+          for (int x = 0; x < L; ++x) paths[q * L + x] = -1;
+          while (node > 0) {
+            paths[q * L + t.node_depth[node] - 1] = t.node_token[node];
+            node = t.node_parent[node];
+          }
+          (void)dq;
+        }
+        __syncthreads();
+        for (int q = tid; q < T; q += kNT) {
+          const int nq = tied[q];
+          const int mq = t.node_mu[nq], dq = t.node_depth[nq];
+          int rank = 0;
+          for (int r = 0; r < T; ++r) {
+            if (r == q) continue;
+            const int nr = tied[r];
+            const int mr = t.node_mu[nr], dr = t.node_depth[nr];
+            bool less;
+            if (mr != mq) less = mr < mq;
+            else {
+              int x = 0;
+              const int dm = dr < dq ? dr : dq;
+              while (x < dm && paths[r * L + x] == paths[q * L + x]) ++x;
+              if (x < dm) less = paths[r * L + x] < paths[q * L + x];
+              else less = dr < dq;
+            }
+            rank += less ? 1 : 0;
+          }
+          if (rank < need) t.node_aux[nq] = 1;
+        }
       }
       __syncthreads();
-      for (int q = tid; q < T; q += kNT) {
-        const int nq = tied[q];
-        const int mq = t.node_mu[nq], dq = t.node_depth[nq];
-        int rank = 0;
-        for (int r = 0; r < T; ++r) {
-          if (r == q) continue;
-          const int nr = tied[r];
-          const int mr = t.node_mu[nr], dr = t.node_depth[nr];
-          bool less;
-          if (mr != mq) less = mr < mq;
-          else {
-            int x = 0;
-            const int dm = dr < dq ? dr : dq;
-            while (x < dm && paths[r * L + x] == paths[q * L + x]) ++x;
-            if (x < dm) less = paths[r * L + x] < paths[q * L + x];
-            else less = dr < dq;
-          }
-          rank += less ? 1 : 0;
-        }
-        if (rank < need) t.node_aux[nq] = 1;
-      }
     }
-    __syncthreads();
   } else {
     for (int i = 1 + tid; i < nc; i += kNT) t.node_aux[i] = (i - 1 < nsel) ? 1 : 0;
     __syncthreads();
@@ -1040,6 +1113,12 @@ static hipError_t launch_tree(int mode, TreeArgs& a, int N, hipStream_t stream) 
   const size_t nk_end = nk_off + (size_t)c.node_cap * sizeof(uint16_t);
   a.nk_lds = (mode != kBuild && nk_end <= kTreeLdsMax) ? 1 : 0;
   if (a.nk_lds && nk_end > lds) lds = nk_end;
+  // the rows' leading candidates after that, when they fit
+  const size_t pre_off = (lds + 15) & ~size_t(15);
+  const size_t pre_end = pre_off + (size_t)a.K * a.L * kPreQ * (sizeof(float) + sizeof(int32_t));
+  a.pre_q = pre_end <= kTreeLdsMax ? kPreQ : 0;
+  a.pre_off = (int)pre_off;
+  if (a.pre_q) lds = pre_end;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   if (N == 0) return hipSuccess;

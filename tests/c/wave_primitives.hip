@@ -40,6 +40,13 @@ __global__ void sort_test(const uint64_t* in, uint64_t* out, int P) {  // 1024 t
   block_sort_keys<1024>(a, P);
   for (int i = threadIdx.x; i < P; i += 1024) out[i] = a[i];
 }
+__global__ void sort_test256(const uint64_t* in, uint64_t* out, int P) {  // 256 threads, P <= 1024 keys
+  __shared__ uint64_t a[1024];
+  for (int i = threadIdx.x; i < P; i += 256) a[i] = in[i];
+  __syncthreads();
+  block_sort_keys<256>(a, P);
+  for (int i = threadIdx.x; i < P; i += 256) out[i] = a[i];
+}
 __global__ void small_sorts(const uint64_t* in, uint64_t* out) {  // 256 threads
   __shared__ uint64_t x[512];
   const int t = threadIdx.x;
@@ -117,6 +124,21 @@ int main() {
     int b = 0;
     for (int i = 0; i < P; ++i) b += r[i] != h[i];
     printf("block_sort_keys P=%d mismatches: %d\n", P, b);
+    bad += b;
+    CK(hipFree(din)); CK(hipFree(dout));
+  }
+  for (int P : {64, 128, 256, 512, 1024}) {  // block_sort_keys with 256 threads
+    std::vector<uint64_t> h(P), r(P);
+    for (auto& v : h) v = next() % 1000;
+    uint64_t *din, *dout;
+    CK(hipMalloc(&din, P * 8)); CK(hipMalloc(&dout, P * 8));
+    CK(hipMemcpy(din, h.data(), P * 8, hipMemcpyHostToDevice));
+    hipLaunchKernelGGL(sort_test256, dim3(1), dim3(256), 0, 0, din, dout, P);
+    CK(hipMemcpy(r.data(), dout, P * 8, hipMemcpyDeviceToHost));
+    std::sort(h.begin(), h.end());
+    int b = 0;
+    for (int i = 0; i < P; ++i) b += r[i] != h[i];
+    printf("block_sort_keys<256> P=%d mismatches: %d\n", P, b);
     bad += b;
     CK(hipFree(din)); CK(hipFree(dout));
   }
