@@ -99,6 +99,10 @@ struct TreeArgs {
   int nk_lds;  // threshold call: the nodes' 16-bit score keys are kept in LDS
   int pre_q;   // leading candidates per row staged in LDS (0: none)
   int pre_off; // their byte offset in LDS: raw values [K * L * pre_q], then ids
+  int ch_lds;  // a level's children (raw sums [sort_cap], then node offsets [sort_cap]) live in LDS
+  int ch_off;  //   at this byte offset
+  int f_cap;   // frontier entries whose data an LDS cache holds (0: none)
+  int fc_off;  //   at this byte offset: raw [f_cap], offsets [f_cap], nodes [f_cap], modes [f_cap]
   unsigned char* ws;
   size_t ws_stride;
   int32_t* status;
@@ -142,6 +146,16 @@ struct Ctl {
   int fcount[kNT / kWave];
   int small;  // children of a level built by small_level, -1 if it did not fit
   int up;     // a node of this level has a 16-bit score key above the threshold's
+};
+
+// LDS cache of the current frontier's entries (mode, accumulated raw logit,
+// node) and of their child offsets, valid while the frontier has at most
+// TreeArgs::f_cap entries (every writer of a frontier fills it).
+struct FrontierCache {
+  double* raw;
+  int32_t* off;
+  uint16_t* node;
+  uint8_t* mode;
 };
 
 // Bytes of LDS before the optional node-key array: sort keys, norms, Ctl.
@@ -316,7 +330,8 @@ __device__ __forceinline__ double exact_kth(int n, int rank, Score score, Ctl& c
 // not fit.  Wave 0 only, no block barrier.
 __device__ __forceinline__ int small_level(const TreeArgs& a, const Tree& t, int n, int d, int fsize, double tau,
                                            const double* norm, Ctl& ctl, uint16_t* nk, const float* pre_raw,
-                                           const int32_t* pre_id, double& my_s) {
+                                           const int32_t* pre_id, const FrontierCache& fc, bool cached, double& my_s,
+                                           int& my_mode, double& my_raw, int& my_node) {
   const int lane = lane_id();
   const int K = a.K, L = a.L, k = a.k, Lp1 = L + 1;
   int m = 0, pnode = 0, cnt = 0;
@@ -325,10 +340,16 @@ __device__ __forceinline__ int small_level(const TreeArgs& a, const Tree& t, int
   int id[8];
   bool more = false;
   if (lane < fsize) {
-    const int e = t.fr[lane];
-    m = t.ent_mode[e];
-    raw = t.ent_raw[e];
-    pnode = t.ent_node[e];
+    if (cached) {
+      m = fc.mode[lane];
+      raw = fc.raw[lane];
+      pnode = fc.node[lane];
+    } else {
+      const int e = t.fr[lane];
+      m = t.ent_mode[e];
+      raw = t.ent_raw[e];
+      pnode = t.ent_node[e];
+    }
     nrm = norm[m * Lp1 + d];
     const size_t row = ((size_t)(n * K + m) * L + (d - 1)) * k;
     if (a.pre_q >= 8) {
@@ -455,6 +476,9 @@ __device__ __forceinline__ int small_level(const TreeArgs& a, const Tree& t, int
     ctl.up = up ? 1 : 0;
   }
   my_s = sv ? ss : -INFINITY;
+  my_mode = smode;
+  my_raw = sraw;
+  my_node = node0 + g;
   return C;
 }
 
@@ -479,7 +503,8 @@ __device__ __forceinline__ int block_scan_range(int n, Val val, Out out, int* sc
 template <bool BUILD>
 __device__ __forceinline__ void level_search(const TreeArgs& a, const Tree& t, int n, Ctl& ctl, uint64_t* keys,
                                              const double* norm, uint16_t* nk, const float* pre_raw,
-                                             const int32_t* pre_id) {
+                                             const int32_t* pre_id, double* chr, int32_t* cg,
+                                             const FrontierCache& fc) {
   const int K = a.K, L = a.L, k = a.k, B = a.B;
   const int tid = threadIdx.x;
   const int Lp1 = L + 1;
@@ -493,6 +518,13 @@ __device__ __forceinline__ void level_search(const TreeArgs& a, const Tree& t, i
     const int fsize = ctl.fsize;
     if (fsize == 0 || ctl.fail) break;
     double tau = ctl.tau;
+    // the frontier's entries are in the LDS cache (every writer fills it up
+    // to f_cap entries), else in the workspace through fr
+    const bool cached = fsize <= a.f_cap;
+    int32_t* froff = cached ? fc.off : t.fr_off;
+    auto fe_mode = [&](int f) -> int { return cached ? (int)fc.mode[f] : t.ent_mode[t.fr[f]]; };
+    auto fe_raw = [&](int f) -> double { return cached ? fc.raw[f] : t.ent_raw[t.fr[f]]; };
+    auto fe_node = [&](int f) -> int { return cached ? (int)fc.node[f] : t.ent_node[t.fr[f]]; };
 
     // (threshold call) raise tau to the B-th best unique node so far.  The
     // raise works on 16-bit score keys; if no node of this level has a key
@@ -540,9 +572,11 @@ __device__ __forceinline__ void level_search(const TreeArgs& a, const Tree& t, i
     if (fsize <= kWave) {
       // a small level: one wave builds it (or finds that it does not fit)
       const int ent0 = ctl.ent_count;
-      double my_s = -INFINITY;
+      double my_s = -INFINITY, my_raw = 0.0;
+      int my_mode = 0, my_node = 0;
       if (tid < kWave) {
-        const int cs = small_level(a, t, n, d, fsize, tau, norm, ctl, nk, pre_raw, pre_id, my_s);
+        const int cs = small_level(a, t, n, d, fsize, tau, norm, ctl, nk, pre_raw, pre_id, fc, cached, my_s, my_mode,
+                                   my_raw, my_node);
         if (tid == 0) ctl.small = cs;
       }
       __syncthreads();
@@ -554,7 +588,15 @@ __device__ __forceinline__ void level_search(const TreeArgs& a, const Tree& t, i
           const double tnext = ctl.tau;
           const bool keep = tid < Cs && my_s >= tnext;
           const uint64_t kb = __ballot(keep);
-          if (keep) t.fr[__popcll(kb & lanemask_lt())] = ent0 + tid;
+          const int pos = __popcll(kb & lanemask_lt());
+          if (keep) {
+            t.fr[pos] = ent0 + tid;
+            if (pos < a.f_cap) {
+              fc.mode[pos] = (uint8_t)my_mode;
+              fc.raw[pos] = my_raw;
+              fc.node[pos] = (uint16_t)my_node;
+            }
+          }
           if (tid == 0) ctl.fsize = __popcll(kb);
         }
         __syncthreads();
@@ -564,32 +606,29 @@ __device__ __forceinline__ void level_search(const TreeArgs& a, const Tree& t, i
 
     // 1. per frontier entry: number of children reaching tau; exclusive offsets
     auto count_at = [&](int f, double th) -> int {
-      const int e = t.fr[f];
-      const int m = t.ent_mode[e];
+      const int m = fe_mode(f);
       const float* vals = a.topk_raw + ((size_t)(n * K + m) * L + (d - 1)) * k;
       if (a.pre_q)
-        return count_children_pre(pre_raw + (m * L + (d - 1)) * a.pre_q, a.pre_q, vals, k, t.ent_raw[e],
+        return count_children_pre(pre_raw + (m * L + (d - 1)) * a.pre_q, a.pre_q, vals, k, fe_raw(f),
                                   norm[m * Lp1 + d], th);
-      return count_children(vals, k, t.ent_raw[e], norm[m * Lp1 + d], th);
+      return count_children(vals, k, fe_raw(f), norm[m * Lp1 + d], th);
     };
     int C;
     if (fsize <= kNT / kWave) {
       // a few entries (the first level): one wave per entry
       const int w = tid / kWave;
       if (w < fsize) {
-        const int e = t.fr[w];
-        const int m = t.ent_mode[e];
+        const int m = fe_mode(w);
         const float* vals = a.topk_raw + ((size_t)(n * K + m) * L + (d - 1)) * k;
-        const int cnt = wave_count_children(vals, k, t.ent_raw[e], norm[m * Lp1 + d], tau);
+        const int cnt = wave_count_children(vals, k, fe_raw(w), norm[m * Lp1 + d], tau);
         if (lane_id() == 0) ctl.fcount[w] = cnt;
       }
       __syncthreads();
       C = block_scan_range(
-          fsize, [&](int f) { return ctl.fcount[f]; }, [&](int f, int off, int) { t.fr_off[f] = off; }, ctl.scan);
+          fsize, [&](int f) { return ctl.fcount[f]; }, [&](int f, int off, int) { froff[f] = off; }, ctl.scan);
     } else {
       C = block_scan_range(
-          fsize, [&](int f) { return count_at(f, tau); }, [&](int f, int off, int) { t.fr_off[f] = off; },
-          ctl.scan);
+          fsize, [&](int f) { return count_at(f, tau); }, [&](int f, int off, int) { froff[f] = off; }, ctl.scan);
     }
 
     const bool too_big = (C > a.sort_cap) || (ctl.ent_count + C > a.ent_cap) || (ctl.node_count + C > a.node_cap);
@@ -603,10 +642,10 @@ __device__ __forceinline__ void level_search(const TreeArgs& a, const Tree& t, i
         const double th = f64_from_key(mid);
         int local = 0;
         for (int f = tid; f < fsize; f += kNT) {
-          const int node = t.ent_node[t.fr[f]];
-          if (f > 0 && t.ent_node[t.fr[f - 1]] == node) continue;  // group head only
+          const int node = fe_node(f);
+          if (f > 0 && fe_node(f - 1) == node) continue;  // group head only
           int best = 0;
-          for (int g = f; g < fsize && t.ent_node[t.fr[g]] == node; ++g) best = max(best, count_at(g, th));
+          for (int g = f; g < fsize && fe_node(g) == node; ++g) best = max(best, count_at(g, th));
           local += best;
         }
         for (int i = 1 + tid; i < ctl.node_count; i += kNT) local += (t.node_S[i] >= th) ? 1 : 0;
@@ -617,8 +656,7 @@ __device__ __forceinline__ void level_search(const TreeArgs& a, const Tree& t, i
       tau = f64_from_key(lo);
       if (tid == 0) ctl.tau = tau;
       C = block_scan_range(
-          fsize, [&](int f) { return count_at(f, tau); }, [&](int f, int off, int) { t.fr_off[f] = off; },
-          ctl.scan);
+          fsize, [&](int f) { return count_at(f, tau); }, [&](int f, int off, int) { froff[f] = off; }, ctl.scan);
     }
     if ((C > a.sort_cap) || (ctl.ent_count + C > a.ent_cap) || (ctl.node_count + C > a.node_cap)) {
       if (tid == 0) ctl.fail = 1;
@@ -627,31 +665,25 @@ __device__ __forceinline__ void level_search(const TreeArgs& a, const Tree& t, i
     }
     if (C == 0) break;
 
-    // 2. materialise children and their sort keys
+    // 2. materialise children: the accumulated raw logit (chr), and the sort
+    // key, which carries the parent node, token and mode
     for (int c = tid; c < C; c += kNT) {
-      int lo = 0, hi = fsize - 1;  // largest f with fr_off[f] <= c
+      int lo = 0, hi = fsize - 1;  // largest f with froff[f] <= c
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (t.fr_off[mid] <= c) lo = mid;
+        if (froff[mid] <= c) lo = mid;
         else hi = mid - 1;
       }
       const int f = lo;
-      const int e = t.fr[f];
-      const int m = t.ent_mode[e];
-      const int j = c - t.fr_off[f];
+      const int m = fe_mode(f);
+      const int j = c - froff[f];
       const size_t row = ((size_t)(n * K + m) * L + (d - 1)) * k;
       const bool staged = j < a.pre_q;
       const int pr = (m * L + (d - 1)) * a.pre_q + j;
       const float x = staged ? pre_raw[pr] : a.topk_raw[row + j];
       const int tok = staged ? pre_id[pr] : a.topk_id[row + j];
-      const double raw = t.ent_raw[e] + (double)x;
-      const double s = raw - norm[m * Lp1 + d];
-      const int pnode = t.ent_node[e];
-      t.ch_raw[c] = raw;
-      t.ch_s[c] = s;
-      t.ch_mode[c] = m;
-      t.ch_pnode[c] = pnode;
-      t.ch_tok[c] = tok;
+      const int pnode = fe_node(f);
+      chr[c] = fe_raw(f) + (double)x;
       keys[c] = ((uint64_t)pnode << 40) | ((uint64_t)tok << 20) | ((uint64_t)m << 15) | (uint64_t)c;
     }
     const int P = next_pow2(C);
@@ -659,44 +691,45 @@ __device__ __forceinline__ void level_search(const TreeArgs& a, const Tree& t, i
     __syncthreads();
     block_sort_keys<kNT>(keys, P);
 
-    // 3. runs of equal (parent, token) are one node
+    // 3. runs of equal (parent, token) are one node; cg[i] = the node offset
+    // of sorted entry i
     const int node0 = ctl.node_count, ent0 = ctl.ent_count;
     const int G = block_scan_range(
         C, [&](int i) { return (i == 0 || (keys[i] >> 20) != (keys[i - 1] >> 20)) ? 1 : 0; },
-        [&](int i, int off, int head) { t.grp[i] = head ? off : -1; }, ctl.scan);
-    // each run head builds its node; each member records its entry
+        [&](int i, int off, int head) { cg[i] = head ? off : off - 1; }, ctl.scan);
+    auto child_s = [&](uint64_t key) -> double {
+      const int m = (int)((key >> 15) & 31u);
+      return chr[key & 0x7FFFu] - norm[m * Lp1 + d];
+    };
+    // each entry is recorded; each run head builds its node
     for (int i = tid; i < C; i += kNT) {
-      if (t.grp[i] < 0) continue;
-      const int g = t.grp[i];
-      const uint64_t prefix = keys[i] >> 20;
+      const uint64_t key = keys[i];
+      const int m = (int)((key >> 15) & 31u);
+      const double raw = chr[key & 0x7FFFu];
+      const int node = node0 + cg[i];
+      const int e = ent0 + i;
+      t.ent_node[e] = node;
+      t.ent_mode[e] = m;
+      t.ent_raw[e] = raw;
+      t.ent_s[e] = raw - norm[m * Lp1 + d];
+      if (i > 0 && (keys[i - 1] >> 20) == (key >> 20)) continue;  // run heads only
+      const uint64_t prefix = key >> 20;
       double best = -INFINITY;
       int mu = -1;
-      int j = i;
-      for (; j < C && (keys[j] >> 20) == prefix; ++j) {
-        const int c = (int)(keys[j] & 0x7FFFu);
-        const double s = t.ch_s[c];
+      for (int j = i; j < C && (keys[j] >> 20) == prefix; ++j) {
+        const double s = child_s(keys[j]);
         if (mu < 0 || s > best) {
           best = s;
-          mu = t.ch_mode[c];
+          mu = (int)((keys[j] >> 15) & 31u);
         }
       }
-      const int node = node0 + g;
       if ((f64_key(best) >> 48) > (f64_key(tau) >> 48)) ctl.up = 1;
-      const int c0 = (int)(keys[i] & 0x7FFFu);
-      t.node_parent[node] = t.ch_pnode[c0];
-      t.node_token[node] = t.ch_tok[c0];
+      t.node_parent[node] = (int)(key >> 40);
+      t.node_token[node] = (int)((key >> 20) & 0xFFFFFu);
       t.node_depth[node] = d;
       t.node_S[node] = best;
       t.node_mu[node] = mu;
       if (nk) nk[node] = (uint16_t)(f64_key(best) >> 48);
-      for (int q = i; q < j; ++q) {
-        const int c = (int)(keys[q] & 0x7FFFu);
-        const int e = ent0 + q;
-        t.ent_node[e] = node;
-        t.ent_mode[e] = t.ch_mode[c];
-        t.ent_raw[e] = t.ch_raw[c];
-        t.ent_s[e] = t.ch_s[c];
-      }
     }
     __syncthreads();
     if (tid == 0) {
@@ -708,12 +741,20 @@ __device__ __forceinline__ void level_search(const TreeArgs& a, const Tree& t, i
     // 4. (threshold call) raise tau to the B-th best unique node so far
     if (!BUILD) raise_tau();
 
-    // 5. next frontier: this level's entries still reaching tau
+    // 5. next frontier: this level's entries still reaching tau (their data
+    // also into the LDS cache, up to f_cap of them)
     const double tnext = ctl.tau;
     const int fs = block_scan_range(
-        C, [&](int i) { return (t.ent_s[ent0 + i] >= tnext) ? 1 : 0; },
+        C, [&](int i) { return child_s(keys[i]) >= tnext ? 1 : 0; },
         [&](int i, int off, int v) {
-          if (v) t.fr[off] = ent0 + i;
+          if (!v) return;
+          t.fr[off] = ent0 + i;
+          if (off < a.f_cap) {
+            const uint64_t key = keys[i];
+            fc.mode[off] = (uint8_t)((key >> 15) & 31u);
+            fc.raw[off] = chr[key & 0x7FFFu];
+            fc.node[off] = (uint16_t)(node0 + cg[i]);
+          }
         },
         ctl.scan);
     if (tid == 0) ctl.fsize = fs;
@@ -750,6 +791,18 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
   float* pre_raw = a.pre_q ? reinterpret_cast<float*>(smem_raw + a.pre_off) : nullptr;
   int32_t* pre_id = a.pre_q ? reinterpret_cast<int32_t*>(pre_raw + (size_t)K * L * a.pre_q) : nullptr;
   const Tree t = tree_ptrs(a, n);
+  // a level's children (accumulated raw logits, node offsets): LDS when they fit
+  double* chr = a.ch_lds ? reinterpret_cast<double*>(smem_raw + a.ch_off) : t.ch_raw;
+  int32_t* cg = a.ch_lds ? reinterpret_cast<int32_t*>(smem_raw + a.ch_off + (size_t)a.sort_cap * sizeof(double))
+                         : t.grp;
+  FrontierCache fc = {};
+  if (a.f_cap) {
+    unsigned char* f0 = smem_raw + a.fc_off;
+    fc.raw = reinterpret_cast<double*>(f0);
+    fc.off = reinterpret_cast<int32_t*>(f0 + (size_t)a.f_cap * 8);
+    fc.node = reinterpret_cast<uint16_t*>(f0 + (size_t)a.f_cap * 12);
+    fc.mode = f0 + (size_t)a.f_cap * 14;
+  }
   // a tree built from its first K_n futures only: the inactive modes' rows
   // are never read (the strides keep the full K)
   int Kn = K;
@@ -802,6 +855,11 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
     t.ent_raw[m] = 0.0;
     t.ent_s[m] = 0.0;
     t.fr[m] = m;
+    if (m < a.f_cap) {
+      fc.mode[m] = (uint8_t)m;
+      fc.raw[m] = 0.0;
+      fc.node[m] = 0;
+    }
   }
   __syncthreads();
 
@@ -892,7 +950,7 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
     }
   }
 
-  level_search<!kRaise>(a, t, n, ctl, keys, norm, nk, pre_raw, pre_id);
+  level_search<!kRaise>(a, t, n, ctl, keys, norm, nk, pre_raw, pre_id, chr, cg, fc);
 
   const int nc = ctl.node_count;
   const int fail = ctl.fail;
@@ -1119,6 +1177,22 @@ static hipError_t launch_tree(int mode, TreeArgs& a, int N, hipStream_t stream) 
   a.pre_q = pre_end <= kTreeLdsMax ? kPreQ : 0;
   a.pre_off = (int)pre_off;
   if (a.pre_q) lds = pre_end;
+  // then a level's children (raw sums and node offsets, 12 bytes per key)
+  const size_t ch_off = (lds + 15) & ~size_t(15);
+  const size_t ch_end = ch_off + (size_t)c.sort_cap * (sizeof(double) + sizeof(int32_t));
+  a.ch_lds = ch_end <= kTreeLdsMax ? 1 : 0;
+  a.ch_off = (int)ch_off;
+  if (a.ch_lds) lds = ch_end;
+  // and a cache of the frontier's entries, as many as fit (15 bytes each; a
+  // frontier of more entries reads them from the workspace)
+  const size_t fc_off = (lds + 15) & ~size_t(15);
+  long long f_cap = fc_off < kTreeLdsMax ? (long long)((kTreeLdsMax - fc_off) / 15) : 0;
+  f_cap = f_cap / 64 * 64;
+  if (f_cap > c.ent_cap) f_cap = c.ent_cap;
+  if (f_cap < a.K) f_cap = 0;  // the root entries must fit
+  a.f_cap = (int)f_cap;
+  a.fc_off = (int)fc_off;
+  if (a.f_cap) lds = fc_off + (size_t)f_cap * 15;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   if (N == 0) return hipSuccess;

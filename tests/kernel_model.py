@@ -89,6 +89,8 @@ class Caps:
     tie_cap: int
     nk_lds: bool
     pre_q: int
+    ch_lds: bool   # a level's children (raw sums, node offsets) in LDS
+    f_cap: int     # frontier entries the LDS cache holds
 
 
 def tree_caps(K: int, L: int, k: int, B: int) -> Caps:
@@ -107,7 +109,19 @@ def tree_caps(K: int, L: int, k: int, B: int) -> Caps:
     pre_off = (lds + 15) & ~15
     pre_end = pre_off + K * L * PRE_Q * 8
     pre_q = PRE_Q if pre_end <= TREE_LDS_MAX else 0
-    return Caps(sort_cap, ent_cap, node_cap, tie_cap, nk_lds, pre_q)
+    if pre_q:
+        lds = pre_end
+    ch_off = (lds + 15) & ~15
+    ch_end = ch_off + sort_cap * 12
+    ch_lds = ch_end <= TREE_LDS_MAX
+    if ch_lds:
+        lds = ch_end
+    fc_off = (lds + 15) & ~15
+    f_cap = (TREE_LDS_MAX - fc_off) // 15 if fc_off < TREE_LDS_MAX else 0
+    f_cap = min(f_cap // 64 * 64, ent_cap)
+    if f_cap < K:
+        f_cap = 0
+    return Caps(sort_cap, ent_cap, node_cap, tie_cap, nk_lds, pre_q, ch_lds, f_cap)
 
 
 # ---------------------------------------------------------------- sorting networks (index arithmetic)
@@ -314,12 +328,18 @@ class TreeModel:
         self.fr_off = CheckedArray("fr_off", c.ent_cap)
         keys = CheckedArray("keys (LDS)", c.sort_cap)
         pre = CheckedArray("pre (LDS)", K * L * c.pre_q) if c.pre_q else None
+        chr_ = CheckedArray("children raw (LDS)" if c.ch_lds else "ch_raw", c.sort_cap, 0.0)
+        cg = CheckedArray("children node offsets (LDS)" if c.ch_lds else "grp", c.sort_cap)
+        self.fc = None
+        if c.f_cap:
+            self.fc = {f: CheckedArray(f"frontier cache {f} (LDS)", c.f_cap, 0) for f in ("mode", "raw", "node", "off")}
 
         node_count, ent_count, fsize = 1, K, K
         self.node_S[0] = 0.0
         for m in range(K):
             self.ent_node[m], self.ent_mode[m], self.ent_raw[m], self.ent_s[m] = 0, m, 0.0, 0.0
             self.fr[m] = m
+            self._cache_write(m, m)
         # the rows' leading candidates staged in LDS
         if pre is not None:
             for q in range(K * L * c.pre_q):
@@ -363,6 +383,7 @@ class TreeModel:
             rec = LevelRecord(d=d, fsize=fsize, path="block")
             up = False
             C = -1
+            self._cache_check(fsize)
             if fsize <= WAVE:
                 C, up, my_s = self._small_level(d, fsize, tau, node_count, ent_count, pre)
                 if C == 0:
@@ -377,6 +398,7 @@ class TreeModel:
                     kept = [ent_count - C + lane for lane in range(C) if my_s[lane] >= tau]
                     for i, e in enumerate(kept):
                         self.fr[i] = e
+                        self._cache_write(i, e)
                     fsize = len(kept)
                     rec.nodes, rec.entries = node_count, ent_count
                     res.levels.append(rec)
@@ -400,8 +422,11 @@ class TreeModel:
                 res.levels.append(rec)
                 break
             off = 0
+            cached = c.f_cap and fsize <= c.f_cap
             for f in range(fsize):
                 self.fr_off[f] = off
+                if cached:
+                    self.fc["off"][f] = off
                 off += counts[f]
             ch = []
             for cidx in range(C):
@@ -425,6 +450,7 @@ class TreeModel:
                 if pnode >= (1 << 24) or tok >= (1 << 20) or m >= 32 or cidx >= (1 << 15):
                     raise IndexError("a sort key field overflows its bits")
                 keys[cidx] = (pnode << 40) | (tok << 20) | (m << 15) | cidx
+                chr_[cidx] = raw
                 ch.append((pnode, tok, m, cidx, raw, s))
             P = next_pow2(C)
             for cidx in range(C, P):
@@ -432,6 +458,9 @@ class TreeModel:
             rec.C, rec.P = C, P
             rec.sort = check_block_sort_keys(P, c.sort_cap)
             order = sorted(range(C), key=lambda i: (ch[i][0], ch[i][1], ch[i][2], ch[i][3]))
+            unsorted = [keys[i] for i in range(C)]
+            for q_, i in enumerate(order):  # the sort, in place in LDS
+                keys[q_] = unsorted[i]
             node0, ent0 = node_count, ent_count
             g = -1
             prev = None
@@ -450,6 +479,7 @@ class TreeModel:
                     if s > self.node_S[node]:
                         self.node_S[node], self.node_mu[node] = s, m
                 e = ent0 + q_
+                cg[q_] = g
                 self.ent_node[e], self.ent_mode[e], self.ent_raw[e], self.ent_s[e] = node, m, raw, s
             for node in range(node0, node0 + g + 1):
                 if self.nk is not None:
@@ -463,6 +493,11 @@ class TreeModel:
             for i in range(C):
                 if self.ent_s[ent0 + i] >= tau:
                     self.fr[fs] = ent0 + i
+                    # the kernel reads the entry back from the sorted key and LDS
+                    key = keys[i]
+                    assert chr_[key & 0x7FFF] == self.ent_raw[ent0 + i]
+                    assert node0 + cg[i] == self.ent_node[ent0 + i]
+                    self._cache_write(fs, ent0 + i)
                     fs += 1
             fsize = fs
             rec.nodes, rec.entries = node_count, ent_count
@@ -475,6 +510,27 @@ class TreeModel:
             res.n_select = min(B, total)
             res.cutoff = sorted(res.node_S, reverse=True)[res.n_select - 1]
         return res
+
+    def _cache_write(self, pos: int, e: int):
+        """A frontier writer: entry e at frontier position pos, into the LDS cache
+        when pos < f_cap."""
+        if self.fc is not None and pos < self.caps.f_cap:
+            self.fc["mode"][pos] = self.ent_mode[e]
+            self.fc["raw"][pos] = self.ent_raw[e]
+            if not (0 <= self.ent_node[e] < 65536):
+                raise IndexError(f"node id {self.ent_node[e]} does not fit the cache's 16 bits")
+            self.fc["node"][pos] = self.ent_node[e]
+
+    def _cache_check(self, fsize: int):
+        """A level whose frontier fits the cache reads it there: it must hold
+        what the workspace path reads through fr."""
+        if self.fc is None or fsize > self.caps.f_cap:
+            return
+        for f in range(fsize):
+            e = self.fr[f]
+            assert self.fc["mode"][f] == self.ent_mode[e]
+            assert self.fc["raw"][f] == self.ent_raw[e]
+            assert self.fc["node"][f] == self.ent_node[e]
 
     def _raise(self, tau: float, node_count: int):
         """The threshold raise: the B-th largest 16-bit score key among the nodes
