@@ -8,27 +8,35 @@
 // tokens come out without the [M, V] logits ever being stored.
 //
 // Four launches on the caller's stream:
-//   1. lmh_tile_kernel<true>   (sample)  S spread V-tiles of the product; per
-//      row the maximum of every disjoint group of 4 columns goes to `samp`.
+//   1. sample  S spread vocabulary blocks of the product; per row the maximum
+//      of every disjoint group of 4 columns goes to `samp`.
 //   2. lmh_threshold_kernel    per row: thr = the k-th largest of those group
 //      maxima.  They are k distinct elements of the row, so the row's k-th
 //      largest logit is >= thr: every top-k element passes x >= thr.  Rows with
 //      fewer than k groups take thr = "everything".
-//   3. lmh_tile_kernel<false>  (main)  every tile of the product; per row and
-//      tile the partial (max, sum exp(x - max)); every logit >= thr is appended
-//      to its row's candidate list.
+//   3. main    every column of the product; per row and tile (or wave) the
+//      partial (max, sum exp(x - max)); every logit >= thr is appended to its
+//      row's candidate list.
 //   4. lmh_select_kernel       per row: lse from the partials (fp64), the exact
 //      k-th largest (logit desc, id asc) among the candidates, those k sorted.
 //
-// Tiles: 128 rows x 256 vocabulary columns per 256-thread workgroup, two
-// workgroups per CU, k in steps of 32 through double-buffered, XOR-swizzled LDS
-// (global loads two steps ahead), four waves of 64 x 128 each built
-// from v_mfma_f32_32x32x16_bf16 (fp32 accumulation).  Each product element is
-// computed from the same operands in the same k order in both tile launches,
-// so the sample and main launches see identical logits.
+// Launches 1 and 3 run one of two kernels, both on the matrix cores with fp32
+// accumulation:
+//   - up to 128 rows (one tree): lmh_skinny_kernel, one workgroup per CU, each
+//     wave streaming its own head columns through an LDS ring (below);
+//   - more rows: lmh_tile_kernel, 128 rows x 256 vocabulary columns per
+//     256-thread workgroup (128 x 128 up to 256 rows), two workgroups per CU,
+//     k in steps of 32 through double-buffered, XOR-swizzled LDS (global loads
+//     two steps ahead), four waves of 64 x 128 each built from
+//     v_mfma_f32_32x32x16_bf16.
+// Each product element is computed from the same operands in the same k order
+// in both launches of a call, so the sample and main launches see identical
+// logits.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <algorithm>
 
 #include "mfd_device.hpp"
 #include "mfd_launch.hpp"
@@ -47,6 +55,8 @@ constexpr int kLdk = kBK;  // bf16 per LDS row: 64 bytes, four 16-byte chunks, X
 // groups whether a pass serves 8 lanes over 32 banks or 16 lanes over 64.
 __device__ __forceinline__ int lds_chunk(int r, int q) { return q ^ (((r >> 1) ^ (r >> 3)) & 3); }
 constexpr int kSampleCols = 8192;  // vocabulary columns in the threshold sample
+constexpr int kCountStride = 32;   // ints between row counters: one 128-byte line per row, so
+                                   // the many adds to different rows do not meet on one line
 constexpr int kSmallM = 256;       // up to this many rows, tiles are 128 columns wide
 
 // Tile shapes.  The four waves of a workgroup split its 128 rows x BN columns
@@ -64,6 +74,7 @@ constexpr int kSelLdsCap = 8192;  // candidates a select workgroup holds in LDS
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct LmhArgs {
   const uint16_t* H;  // [M, D] bf16 bits
@@ -75,7 +86,7 @@ struct LmhArgs {
   uint32_t* thr;        // [M] candidate threshold keys
   float2* part;         // [M, wgn * T] (max, sum exp(x - max)) per tile and wave column
   uint64_t* cand;       // [M, C] candidate composites
-  int* cand_count;      // [M]
+  int* cand_count;      // [M * kCountStride]: row r's count at r * kCountStride
   int C;
   int32_t* status;      // [N] or null
   const int32_t* vocab_map;  // [V] full-vocabulary id of column v (increasing), or null
@@ -323,7 +334,7 @@ __global__ void __launch_bounds__(kNT, 2) lmh_tile_kernel(LmhArgs a) {
           total += __popcll(b & half);
         }
         int base = 0;
-        if (lr == 0 && total > 0 && grow < a.M) base = atomicAdd(&a.cand_count[grow], total);
+        if (lr == 0 && total > 0 && grow < a.M) base = atomicAdd(&a.cand_count[(size_t)grow * kCountStride], total);
         base = __shfl(base, lane & 32, kWave);
         if (grow < a.M) {
           int pos = base + before;
@@ -355,6 +366,409 @@ __global__ void __launch_bounds__(kNT, 2) lmh_tile_kernel(LmhArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Few rows (M <= 128, one tree): the head streamed once, through a per-wave
+// LDS ring filled by loads that write LDS directly.  At one tree the
+// contraction needs ~1/3 of the matrix cores' rate to keep pace with the head
+// read, so what sets the pace is how many head bytes are in flight per CU:
+// the accumulators of a wave's 128 rows x 80 columns hold 160 of its 256
+// registers, which leaves room for about one 32-deep step of head fragments
+// in registers, and a step then waits out a full memory latency.  Loads
+// straight into LDS (global_load_lds_dwordx4) hold no registers while in
+// flight.  Here:
+//   - one 512-thread workgroup per CU; each wave owns up to kSkNB blocks of 16
+//     consecutive head rows (vocabulary columns), so a launch covers the
+//     vocabulary in one round with at most one block of imbalance per wave;
+//   - each wave keeps its head fragments for the next R steps in its own LDS
+//     ring (R x blocks x 1 KB; R = 2 for the main launch, 8 for the one-block
+//     sample waves) and reads a step's fragments back as the MFMA A operand
+//     (v_mfma_f32_16x16x32_bf16: lane l holds column 16 b + l % 16, k-offset
+//     8 (l / 16) .. + 7; the load puts lane l's 16 bytes at slot + 16 l, so
+//     each lane reads back what it loaded); the packed layout makes each
+//     block's step one contiguous 1 KB run;
+//   - the hidden rows (B operand, all 128 rows) sit in a ring of eight 32-deep
+//     steps, four chunks of two: at the start of a chunk each wave loads its
+//     16 rows of the chunk three ahead, and one barrier per chunk publishes
+//     the next one.
+// The loop issues no other vector memory loads, so each wait counts exactly
+// the ring loads issued after the one it needs.
+// Accumulator element r of block (b, rb) in lane l is column 16 b + 4 (l / 16)
+// + r and row 16 rb + l % 16: a lane holds groups of 4 consecutive columns of
+// one row, and the 4 lanes l % 16 = j share row j.
+constexpr int kSkWaves = 8, kSkNT = kSkWaves * kWave;
+constexpr int kSkRows = 128, kSkRB = kSkRows / 16;
+constexpr int kSkNB = 5;      // 16-column blocks per wave (at most)
+constexpr int kSkSampleBlocks = kSampleCols / 16;
+constexpr int kSkCUs = 256;   // MI355X compute units: workgroups of one launch round
+template <int NB>
+struct SkRing {
+  static constexpr int R = NB == 1 ? 8 : 2;  // head steps in flight per wave
+  static constexpr int HS = 8;               // 32-deep steps of hidden rows in LDS: 4 chunks of 2
+  static constexpr size_t rings = (size_t)kSkWaves * R * NB * 1024 + (size_t)HS * kSkRows * 64;
+  // then per row: threshold key, this workgroup's candidate count, its base in
+  // the row's list; then per wave its staged candidate count
+  static constexpr size_t lds = rings + (3 * kSkRows + kSkWaves) * sizeof(uint32_t);
+  // after the loop the rings hold the staged candidates, a run of wave_cap
+  // per wave: composites, then (row | offset in the workgroup's run << 8)
+  static constexpr int wave_cap = (int)(rings / 12 / kSkWaves);
+};
+static_assert(SkRing<kSkNB>::lds <= 160 * 1024, "LDS of a CU");
+
+// One 16-byte-per-lane load straight into LDS (buffer_load_dwordx4 ... lds):
+// lane l reads bytes [soff + voff, + 16) of the buffer described by rsrc
+// (reads past its size return zeros) and its 16 bytes land at LDS byte
+// address lds + 16 l (lds wave-uniform, passed in M0).  Written as assembly
+// because the compiler waits for every load in flight before any LDS read
+// that follows the builtin form; the waits here are sk_vm_wait's.  The
+// instruction has no register result.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void sk_dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" : : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds)
+               : "memory");
+}
+// Raw buffer descriptor: base, no stride, `bytes` long (gfx9 word 3).
+__device__ __forceinline__ i32x4 sk_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32) & 0xFFFF);
+  r.z = __builtin_amdgcn_readfirstlane((int)bytes);
+  r.w = 0x00020000;
+  return r;
+}
+
+// Wait until at most N vector memory loads of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void sk_vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+// The same with N = (loads per step) * S + H for a wave of nb head blocks
+// (nb wave-uniform; NB or NB - 1 in a launch that spreads blocks evenly, 0
+// or other values only for tiny vocabularies, which wait for everything).
+template <int NB, int S, int H>
+__device__ __forceinline__ void sk_vm_wait_nb(int nb) {
+  if (nb == NB)
+    sk_vm_wait<NB * S + H>();
+  else if (NB > 1 && nb == NB - 1)
+    sk_vm_wait<(NB > 1 ? NB - 1 : 0) * S + H>();
+  else
+    sk_vm_wait<0>();
+}
+
+// f32_key of a logit as the matrix cores produce it (adding +0 turns -0
+// into +0; a NaN stays quiet, so its bits and key are those f32_key gives).
+__device__ __forceinline__ uint32_t sk_key(float x) {
+  const uint32_t u = __float_as_uint(x + 0.0f);
+  return u ^ ((uint32_t)((int)u >> 31) | 0x80000000u);
+}
+
+// Vocabulary block of work item i: every block in the main launch, nwork
+// spread ones in the sample launch.
+__device__ __forceinline__ int sk_vblock(bool sample, int i, int nblk, int nwork) {
+  return sample ? (int)(((long long)i * nblk) / nwork) : i;
+}
+
+template <bool SAMPLE, int NB>
+__global__ void __launch_bounds__(kSkNT, 1) lmh_skinny_kernel(LmhArgs a, int nwork, int nw_total) {
+  constexpr int R = SkRing<NB>::R, HS = SkRing<NB>::HS;
+  static_assert(HS % 2 == 0 && HS >= 4 && (HS & (HS - 1)) == 0, "whole chunks of two steps, power of two");
+  // [wave][slot][block] 1 KB head fragments, then [HS][128 rows x 4 chunks] hidden rows
+  extern __shared__ __attribute__((aligned(16))) uint4 sk_lds[];
+  const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());
+  const int gw = (int)blockIdx.x * kSkWaves + w;
+  const int D = a.D, nS = D / 32;
+  const int nblk = (a.V + 15) / 16;
+  const int b0 = (int)(((long long)gw * nwork) / nw_total);
+  const int nbc = (int)(((long long)(gw + 1) * nwork) / nw_total) - b0;  // blocks of this wave, 0..NB
+  const int lj = lane & 15, lq = lane >> 4;
+
+  // byte offset of this lane's 16 bytes of each block's head fragment at step
+  // 0 (V D and the packed size are below 2^31 elements)
+  uint32_t woff[NB];
+  int vbk[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    vbk[b] = sk_vblock(SAMPLE, min(b0 + b, nwork - 1), nblk, nwork);
+    if (a.packed) {
+      // block (vbk / 4, step) of 64 rows x 32 k is 2048 contiguous elements,
+      // row-major; this 16-row block is its (vbk % 4)-th 512
+      woff[b] = 2u * ((uint32_t)(vbk[b] >> 2) * (uint32_t)nS * 2048u + (uint32_t)(vbk[b] & 3) * 512u + (uint32_t)(4 * lj + lq) * 8u);
+    } else {
+      woff[b] = 2u * ((uint32_t)min(16 * vbk[b] + lj, a.V - 1) * (uint32_t)D + (uint32_t)(8 * lq));
+    }
+  }
+  const uint32_t wstep = a.packed ? 4096u : 64u;  // bytes per 32-deep step
+  const uint32_t wbytes = 2u * (a.packed ? (uint32_t)((a.V + 255) / 256) * 256u * (uint32_t)D : (uint32_t)a.V * (uint32_t)D);
+  const i32x4 wrs = sk_rsrc(a.W, wbytes);
+  const i32x4 hrs = sk_rsrc(a.H, 2u * (uint32_t)a.M * (uint32_t)D);
+  // hidden rows: this lane loads row 16 w + l / 4, the 16-byte chunk that the
+  // swizzle lds_chunk puts at position l % 4 of the row's 64 bytes
+  const int hr = 16 * w + (lane >> 2);
+  const uint32_t hoff = 2u * ((uint32_t)min(hr, a.M - 1) * (uint32_t)D + 8u * (uint32_t)((lane & 3) ^ lds_chunk(hr, 0)));
+
+  const uint32_t lds0 = (uint32_t)(uintptr_t)sk_lds;
+  const uint32_t ring = lds0 + (uint32_t)(w * R * NB) * 1024u;
+  const uint32_t hbase = lds0 + (uint32_t)(kSkWaves * R * NB) * 1024u;
+  const int ring_u4 = w * R * NB * 64 + lane;         // uint4 index of this lane in slot 0, block 0
+  const int hbase_u4 = kSkWaves * R * NB * 64;
+  auto wdma = [&](int g) {  // head fragments of step g into slot g mod R (g outside [0, nS): a
+                            // real step again, whose data is overwritten or never read)
+    const int gs = min(max(g, 0), nS - 1);
+    const uint32_t slot = ring + (uint32_t)((((g % R) + R) % R) * NB) * 1024u;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      if (b < nbc) sk_dma16(wrs, woff[b], (uint32_t)gs * wstep, slot + (uint32_t)b * 1024u);
+  };
+  auto hdma = [&](int g) {  // this wave's 16 hidden rows of step g into slot g mod HS (g < 0: step 0, unused)
+    sk_dma16(hrs, hoff, 64u * (uint32_t)min(max(g, 0), nS - 1),
+             hbase + (uint32_t)(g & (HS - 1)) * 8192u + (uint32_t)w * 1024u);
+  };
+
+  f32x4 acc[NB][kSkRB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int rb = 0; rb < kSkRB; ++rb) acc[b][rb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // Step g: (B) wait for head step g; (C) read it from the ring, refill the
+  // slot with step g + R; (A, even g) load the hidden rows of the chunk
+  // HS / 2 - 1 ahead (steps g + HS - 2, g + HS - 1) into the slots of the
+  // previous chunk (steps g - 2, g - 1); (D) the MFMAs of step g; (E, odd g)
+  // wait for the hidden rows of the next chunk, loaded at step g + 3 - HS,
+  // and publish them.
+  // The prologue issues the loads of steps -S0 .. -1 (S0 = max(R, HS - 2)) in
+  // that order, so every count below holds from step 0: head step s + R (for
+  // s + R < 0, step 0 again into the slot of s + R, overwritten in order
+  // later), and at even s the hidden rows of steps s + HS - 2 and s + HS - 1
+  // (negative ones: step 0 again, into slots that are refilled in order later).
+  constexpr int S0 = R > HS - 2 ? R : HS - 2;
+#pragma unroll
+  for (int s = -S0; s < 0; ++s) {
+    wdma(s + R);
+    if ((s & 1) == 0) {
+      hdma(s + HS - 2);
+      hdma(s + HS - 1);
+    }
+  }
+  // chunk 0 (loaded at step 2 - HS) is followed by HS - 3 steps' head loads
+  // and HS - 4 hidden-row loads
+  sk_vm_wait_nb<NB, HS - 3, HS - 4>(nbc);
+  uint32_t* sthr = reinterpret_cast<uint32_t*>(sk_lds + SkRing<NB>::rings / 16);
+  int* wg_cnt = reinterpret_cast<int*>(sthr + kSkRows);
+  int* wg_base = wg_cnt + kSkRows;
+  int* wv_staged = wg_base + kSkRows;
+  if (!SAMPLE && (int)threadIdx.x < kSkRows) {
+    // (this load completes before the barrier: no load of the compiler's is
+    // in flight in the loop, whose waits count only the ring loads)
+    sthr[threadIdx.x] = (int)threadIdx.x < a.M ? a.thr[threadIdx.x] : 0xFFFFFFFFu;
+    wg_cnt[threadIdx.x] = 0;
+  }
+  __syncthreads();
+
+  // (B) Loads issued after head step g's: head steps g + 1 .. g + R - 1, and
+  // two hidden-row loads for each even step in [g - R, g - 1]: R / 2 such
+  // steps for even R; (R - 1) / 2 for even g and (R + 1) / 2 for odd g when R
+  // is odd.  (E) After the next chunk's hidden rows (issued at step
+  // g + 3 - HS, even): HS - 3 steps' head loads and HS - 4 hidden-row loads.
+  // nS is even (D is a multiple of 64), so chunks are whole.
+  constexpr int kEvenH = 2 * (R % 2 == 0 ? R / 2 : (R - 1) / 2);
+  constexpr int kOddH = 2 * (R % 2 == 0 ? R / 2 : (R + 1) / 2);
+  for (int g0 = 0; g0 < nS; g0 += 2) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int g = g0 + p;
+      if (p == 0)
+        sk_vm_wait_nb<NB, R - 1, kEvenH>(nbc);
+      else
+        sk_vm_wait_nb<NB, R - 1, kOddH>(nbc);
+      const int slot_u4 = ring_u4 + (g % R) * NB * 64;
+      const int hs_u4 = hbase_u4 + (g & (HS - 1)) * 512;
+      bf16x8 wf[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) wf[b] = __builtin_bit_cast(bf16x8, sk_lds[slot_u4 + b * 64]);
+      // one-block waves have few MFMAs to hide LDS latency behind: all the
+      // step's hidden-row fragments are read before the one wait
+      bf16x8 hf1[NB == 1 ? kSkRB : 1];
+      if constexpr (NB == 1) {
+#pragma unroll
+        for (int rb = 0; rb < kSkRB; ++rb) {
+          const int r = rb * 16 + lj;
+          hf1[rb] = __builtin_bit_cast(bf16x8, sk_lds[hs_u4 + 4 * r + lds_chunk(r, lq)]);
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // ring reads done before the slot is refilled
+      __builtin_amdgcn_sched_barrier(0);
+      wdma(g + R);
+      if (p == 0) {
+        hdma(g + HS - 2);
+        hdma(g + HS - 1);
+      }
+#pragma unroll
+      for (int rb = 0; rb < kSkRB; ++rb) {
+        const int r = rb * 16 + lj;
+        const bf16x8 hf = NB == 1 ? hf1[NB == 1 ? rb : 0] : __builtin_bit_cast(bf16x8, sk_lds[hs_u4 + 4 * r + lds_chunk(r, lq)]);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[b][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[b], hf, acc[b][rb], 0, 0, 0);
+      }
+      if (p == 1) {
+        sk_vm_wait_nb<NB, HS - 3, HS - 4>(nbc);
+        __syncthreads();
+      }
+    }
+  }
+  sk_vm_wait<0>();  // no load may still write this workgroup's LDS when it ends
+
+
+  // Epilogue.  Column validity is the same for every block row: bit 4 b + r of
+  // vmask says whether column 16 vbk[b] + 4 lq + r exists (b < nbc, below V).
+  static_assert(NB * 4 <= 32, "validity bits");
+  uint32_t vmask = 0;
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (b < nbc && 16 * vbk[b] + 4 * lq + r < a.V) vmask |= 1u << (4 * b + r);
+
+  if (SAMPLE) {
+    // per row, the maximum of each group of 4 columns (0 = no column)
+#pragma unroll
+    for (int rb = 0; rb < kSkRB; ++rb) {
+      const int row = rb * 16 + lj;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        uint32_t gmax = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          gmax = max(gmax, (vmask >> (4 * b + r)) & 1u ? sk_key(acc[b][rb][r]) : 0u);
+        }
+        if (b < nbc && row < a.M) a.samp[(size_t)row * ((size_t)a.S * 4) + (size_t)(b0 + b) * 4 + lq] = gmax;
+      }
+    }
+    return;
+  }
+
+  // Main launch, per block row: the partial log-sum-exp over this wave's
+  // columns of the row, the non-finite flag, and the candidates (logits at or
+  // above the row's threshold), staged in LDS (the rings are free once every
+  // wave has drained its loads) with their offsets in the workgroup's run of
+  // the row's list.
+  constexpr int kWCap = SkRing<NB>::wave_cap;
+  constexpr int kOver = 0x40000000;  // in wg_cnt: a candidate of the row did not fit the stage
+  uint64_t* stage_c = reinterpret_cast<uint64_t*>(sk_lds);
+  uint32_t* stage_m = reinterpret_cast<uint32_t*>(stage_c + kSkWaves * kWCap);
+  int staged = 0;  // this wave's candidates so far (wave-uniform)
+  __syncthreads();
+#pragma unroll
+  for (int rb = 0; rb < kSkRB; ++rb) {
+    const int row = rb * 16 + lj;
+    const bool rok = row < a.M;
+    float mx = -INFINITY;
+    bool bad = false;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float x = acc[b][rb][r];
+        const bool v = (vmask >> (4 * b + r)) & 1u;
+        bad |= v && !__builtin_isfinite(x);
+        mx = fmaxf(mx, v ? x : -INFINITY);
+      }
+    mx = fmaxf(mx, xor_lanes(mx, 16));
+    mx = fmaxf(mx, xor_lanes(mx, 32));
+    float sm = 0.0f;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool v = (vmask >> (4 * b + r)) & 1u;
+        sm += v && mx > -INFINITY ? __expf(acc[b][rb][r] - mx) : 0.0f;
+      }
+    sm += xor_lanes(sm, 16);
+    sm += xor_lanes(sm, 32);
+    if (lq == 0 && rok) a.part[(size_t)row * nw_total + gw] = make_float2(mx, sm);
+    if (bad && rok && a.status != nullptr) atomicOr(&a.status[row / a.rows_per_tree], MFD_TREE_NONFINITE);
+
+    // candidate bits: key >= th, as a float compare where the lane's values
+    // are finite (the key order is the float order there, -0 = +0); th = 0
+    // (the sample held fewer than k groups) takes every column
+    const uint32_t th = sthr[row];
+    uint32_t pm = 0;
+    if (th == 0u) {
+      pm = 0xFFFFFFFFu;
+    } else if (!bad) {
+      const float tf = __uint_as_float(f32_from_key(th));
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pm |= acc[b][rb][r] >= tf ? 1u << (4 * b + r) : 0u;
+    } else {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pm |= sk_key(acc[b][rb][r]) >= th ? 1u << (4 * b + r) : 0u;
+    }
+    pm &= rok ? vmask : 0u;
+    // offsets: in the wave's stage run, a prefix over the wave; in the
+    // workgroup's run of the row, one LDS add per row and wave (lane group 0)
+    // plus a prefix over the row's 4 lanes (lanes l ^ 16, l ^ 32, l ^ 48 hold
+    // lane groups lq ^ 1, lq ^ 2, lq ^ 3); a candidate's place in either is
+    // then the count of candidate bits below its own
+    const int cnt = __popc(pm);
+    const int incl = wave_inclusive_scan(cnt);
+    const int wtot = __builtin_amdgcn_readlane(incl, kWave - 1);
+    if (wtot != 0) {
+      const int c16 = xor_lanes(cnt, 16), c32 = xor_lanes(cnt, 32), c48 = xor_lanes(c16, 32);
+      const int rtot = cnt + c16 + c32 + c48;
+      int roff = 0;
+      if (lq == 0 && rtot > 0) roff = atomicAdd(&wg_cnt[row], rtot) & (kOver - 1);
+      const int r16 = xor_lanes(roff, 16), r32 = xor_lanes(roff, 32), r48 = xor_lanes(r16, 32);
+      const int off = roff + r16 + r32 + r48 + ((lq ^ 1) < lq ? c16 : 0) + ((lq ^ 2) < lq ? c32 : 0) + ((lq ^ 3) < lq ? c48 : 0);
+      const int gi = staged + incl - cnt;
+      const bool fits = staged + wtot <= kWCap;  // wave-uniform
+      if (!fits && cnt > 0 && gi + cnt > kWCap) atomicOr(&wg_cnt[row], kOver);
+      const int sbase = w * kWCap;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int bit = 4 * b + r;
+          if ((pm >> bit) & 1u) {
+            const int below = __popc(pm & ((1u << bit) - 1u));
+            if (fits || gi + below < kWCap) {
+              stage_c[sbase + gi + below] = cand_composite(sk_key(acc[b][rb][r]), (uint32_t)(16 * vbk[b] + 4 * lq + r));
+              stage_m[sbase + gi + below] = (uint32_t)row | ((uint32_t)(off + below) << 8);
+            }
+          }
+        }
+      staged += wtot;
+    }
+  }
+  if (lane == 0) wv_staged[w] = min(staged, kWCap);
+
+  // one add per row and workgroup reserves the workgroup's run of the row's
+  // list (a row with unstaged candidates is pushed past the capacity, which
+  // the select kernel reports); then the stage is copied out
+  __syncthreads();
+  if ((int)threadIdx.x < kSkRows) {
+    const int n = wg_cnt[threadIdx.x];
+    int base = 0;
+    if (n != 0 && (int)threadIdx.x < a.M) {
+      int* cc = &a.cand_count[(size_t)threadIdx.x * kCountStride];
+      base = (n & kOver) ? atomicAdd(cc, a.C + 1) + a.C + 1 : atomicAdd(cc, n);
+    }
+    wg_base[threadIdx.x] = base;
+  }
+  __syncthreads();
+  for (int i = (int)threadIdx.x; i < kSkWaves * kWCap; i += kSkNT) {
+    const int sw = i / kWCap;
+    if (i - sw * kWCap >= wv_staged[sw]) continue;
+    const uint32_t m = stage_m[i];
+    const int row = (int)(m & 255u);
+    const int pos = wg_base[row] + (int)(m >> 8);
+    if (pos < a.C) a.cand[(size_t)row * a.C + pos] = stage_c[i];
+  }
+}
+
 // Per row: the candidate threshold (k-th largest group maximum, or 0 = take
 // every column when the sample holds fewer than k groups); resets the row's
 // candidate count.
@@ -380,7 +794,7 @@ __global__ void __launch_bounds__(kThrNT) lmh_threshold_kernel(LmhArgs a, int k)
   }
   if (threadIdx.x == 0) {
     a.thr[row] = thr;
-    a.cand_count[row] = 0;
+    a.cand_count[(size_t)row * kCountStride] = 0;
   }
 }
 
@@ -431,7 +845,7 @@ __global__ void __launch_bounds__(kSelNT) lmh_select_kernel(LmhArgs a, int k, do
   if (tid == 0) lse[row] = l;
 
   // 2. candidates
-  const int cnt = a.cand_count[row];
+  const int cnt = a.cand_count[(size_t)row * kCountStride];
   int32_t* oid = topk_id + (size_t)row * k;
   float* oraw = topk_raw + (size_t)row * k;
   float* olp = topk_logp ? topk_logp + (size_t)row * k : nullptr;
@@ -573,12 +987,28 @@ hipError_t launch_lmhead_pack(const void* weight, int V, int D, void* packed, hi
 
 LmhWorkspace lmhead_workspace(long long M, int V, int k) {
   LmhWorkspace w{};
-  w.small = M <= kSmallM;
-  const int BN = w.small ? TileShape<4>::BN : TileShape<2>::BN;
-  w.gpt = w.small ? TileShape<4>::GPT : TileShape<2>::GPT;
-  w.wgn = w.small ? TileShape<4>::WGN : TileShape<2>::WGN;
-  w.T = (V + BN - 1) / BN;
-  w.S = w.T < kSampleCols / BN ? w.T : kSampleCols / BN;
+  w.skinny = M <= kSkRows;
+  w.small = !w.skinny && M <= kSmallM;
+  int BN;
+  if (w.skinny) {
+    // one workgroup per CU (256 on MI355X), more when a wave would need more
+    // than kSkNB blocks; partials per row: one per wave
+    const int nblk = (V + 15) / 16;
+    const int by_cu = std::min(kSkCUs, (nblk + kSkWaves - 1) / kSkWaves);
+    const int by_nb = (nblk + kSkWaves * kSkNB - 1) / (kSkWaves * kSkNB);
+    w.nwg = std::max(by_cu, by_nb);
+    BN = 16;
+    w.gpt = 4;
+    w.wgn = 1;
+    w.T = w.nwg * kSkWaves;
+    w.S = std::min(nblk, kSkSampleBlocks);
+  } else {
+    BN = w.small ? TileShape<4>::BN : TileShape<2>::BN;
+    w.gpt = w.small ? TileShape<4>::GPT : TileShape<2>::GPT;
+    w.wgn = w.small ? TileShape<4>::WGN : TileShape<2>::WGN;
+    w.T = (V + BN - 1) / BN;
+    w.S = w.T < kSampleCols / BN ? w.T : kSampleCols / BN;
+  }
   // about k V / (S * BN) candidates per row for rows of independent logits;
   // four times that leaves room for rows of uneven spread
   const long long expect = ((long long)k * V + (long long)w.S * BN - 1) / ((long long)w.S * BN);
@@ -597,7 +1027,7 @@ LmhWorkspace lmhead_workspace(long long M, int V, int k) {
   };
   w.off_samp = take((size_t)M * w.S * w.gpt * sizeof(uint32_t));
   w.off_thr = take((size_t)M * sizeof(uint32_t));
-  w.off_count = take((size_t)M * sizeof(int));
+  w.off_count = take((size_t)M * kCountStride * sizeof(int));
   w.off_part = take((size_t)M * w.wgn * w.T * sizeof(float2));
   w.off_cand = take((size_t)M * w.C * sizeof(uint64_t));
   w.bytes = off;
@@ -632,7 +1062,21 @@ hipError_t launch_lmhead_topk(const void* hidden, const void* weight, bool packe
   const int nM = (M + kBM - 1) / kBM;
   const long long ns = (long long)nM * a.S, nm = (long long)nM * a.T;
   const long long gs = (ns + 7) / 8 * 8, gm = (nm + 7) / 8 * 8;
-  if (wsl.small) {
+  if (wsl.skinny) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lmh_skinny_kernel<true, 1>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)SkRing<1>::lds);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lmh_skinny_kernel<false, kSkNB>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)SkRing<kSkNB>::lds);
+    if (e != hipSuccess) return e;
+    const int swg = (a.S + kSkWaves - 1) / kSkWaves;
+    hipLaunchKernelGGL((lmh_skinny_kernel<true, 1>), dim3(swg), dim3(kSkNT), SkRing<1>::lds, stream, a, a.S,
+                       swg * kSkWaves);
+    hipLaunchKernelGGL(lmh_threshold_kernel, dim3(M), dim3(kThrNT), 0, stream, a, k);
+    const int nblk = (V + 15) / 16;
+    hipLaunchKernelGGL((lmh_skinny_kernel<false, kSkNB>), dim3(wsl.nwg), dim3(kSkNT), SkRing<kSkNB>::lds, stream, a,
+                       nblk, wsl.nwg * kSkWaves);
+  } else if (wsl.small) {
     hipLaunchKernelGGL((lmh_tile_kernel<true, 4>), dim3((unsigned)gs), dim3(kNT), 0, stream, a);
     hipLaunchKernelGGL(lmh_threshold_kernel, dim3(M), dim3(kThrNT), 0, stream, a, k);
     hipLaunchKernelGGL((lmh_tile_kernel<false, 4>), dim3((unsigned)gm), dim3(kNT), 0, stream, a);

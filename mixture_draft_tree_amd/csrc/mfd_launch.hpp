@@ -80,7 +80,9 @@ hipError_t launch_verify_walk(const void* target, bool bf16, int N, int Bp1, lon
 // Fused LM head + log-softmax/top-k: workspace layout (byte offsets into the
 // caller's buffer) and launcher.
 struct LmhWorkspace {
-  bool small;  // 128-column tiles (few rows) instead of 256-column ones
+  bool skinny;  // at most 128 rows: head streamed into registers, one workgroup per CU
+  int nwg;      // skinny: workgroups of the main launch
+  bool small;   // 128-column tiles (up to 256 rows) instead of 256-column ones
   int gpt;     // groups of 4 columns per tile
   int wgn;     // partials per row and tile
   int T;       // vocabulary tiles

@@ -253,7 +253,7 @@ def test_lmhead_call_rejects_before_launch():
 def test_lmhead_workspace_size():
     one = M.workspace_size(M.MFD_OP_LMHEAD_TOPK, 1, 8, 15, 151936, 256)
     many = M.workspace_size(M.MFD_OP_LMHEAD_TOPK, 64, 8, 15, 151936, 256)
-    assert 0 < one < many and many <= 70 * one   # one tree takes 128-column tiles, 64 trees 256-column ones
+    assert 0 < one < many and many <= 70 * one   # one tree takes the few-row path, 64 trees 256-column tiles
     three = M.workspace_size(M.MFD_OP_LMHEAD_TOPK, 3, 8, 15, 151936, 256)
     six = M.workspace_size(M.MFD_OP_LMHEAD_TOPK, 6, 8, 15, 151936, 256)
     assert abs(six - 2 * three) <= 5 * 256        # same tile shape: linear in the rows

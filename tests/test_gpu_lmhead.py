@@ -167,6 +167,25 @@ def test_lmhead_capacity_and_nonfinite_flags():
     assert np.max(np.abs(lse[0] - np.log(w.V))) < LSE_TOL
 
 
+def test_lmhead_flags_few_rows():
+    """The same flags on the path for at most 128 rows (one workgroup per CU,
+    head streamed through LDS rings): tree 0 all-equal logits overflow the
+    candidate list, tree 1 holds NaN logits, tree 2 stays exact."""
+    _say("lmhead flags few rows")
+    N, K, L, D, V, k = 3, 3, 5, 64, 20000, 32
+    h, w = _grid_inputs(N, K, L, D, V, seed=11)
+    h[0] = 0
+    h[1, 2, 3, 7] = float("nan")
+    lse, ids, raw, lp, st = _run(h, w, k)
+    assert st[0] == M.MFD_TREE_CAPACITY
+    assert st[1] & M.MFD_TREE_NONFINITE
+    assert st[2] == 0
+    assert np.all(ids[0] == -1) and np.all(np.isneginf(raw[0]))
+    assert np.max(np.abs(lse[0] - np.log(V))) < LSE_TOL
+    x64 = O.lmhead_logits(h[2:3].float().numpy(), w.float().numpy())
+    _check_exact(x64, k, lse[2:3], ids[2:3], raw[2:3], lp[2:3])
+
+
 def _grid_inputs(N, K, L, D, V, seed):
     g = torch.Generator().manual_seed(seed)
     h = torch.randint(-4, 5, (N, K, L, D), generator=g).to(torch.float32) * 0.25
