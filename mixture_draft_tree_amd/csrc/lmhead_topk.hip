@@ -383,9 +383,9 @@ __global__ void __launch_bounds__(kNT, 2) lmh_tile_kernel(LmhArgs a) {
 //     ring (R x blocks x 1 KB; R = 2 for the main launch, 8 for the one-block
 //     sample waves) and reads a step's fragments back as the MFMA A operand
 //     (v_mfma_f32_16x16x32_bf16: lane l holds column 16 b + l % 16, k-offset
-//     8 (l / 16) .. + 7; the load puts lane l's 16 bytes at slot + 16 l, so
-//     each lane reads back what it loaded); the packed layout makes each
-//     block's step one contiguous 1 KB run;
+//     8 (l / 16) .. + 7); the loads fill a slot with the block's 16 rows x
+//     64 bytes row-major, chunks swizzled as for the hidden rows; the packed
+//     layout makes each block's step one contiguous 1 KB run;
 //   - the hidden rows (B operand, all 128 rows) sit in a ring of eight 32-deep
 //     steps, four chunks of two: at the start of a chunk each wave loads its
 //     16 rows of the chunk three ahead, and one barrier per chunk publishes
@@ -395,24 +395,27 @@ __global__ void __launch_bounds__(kNT, 2) lmh_tile_kernel(LmhArgs a) {
 // Accumulator element r of block (b, rb) in lane l is column 16 b + 4 (l / 16)
 // + r and row 16 rb + l % 16: a lane holds groups of 4 consecutive columns of
 // one row, and the 4 lanes l % 16 = j share row j.
-constexpr int kSkWaves = 8, kSkNT = kSkWaves * kWave;
+constexpr int kSkWaves = 8;      // waves per workgroup of the main launch
+constexpr int kSkSampleWaves = 2;  // ... and of the sample launch
 constexpr int kSkRows = 128, kSkRB = kSkRows / 16;
 constexpr int kSkNB = 5;      // 16-column blocks per wave (at most)
 constexpr int kSkSampleBlocks = kSampleCols / 16;
 constexpr int kSkCUs = 256;   // MI355X compute units: workgroups of one launch round
-template <int NB>
+template <int NB, int WV>
 struct SkRing {
   static constexpr int R = NB == 1 ? 8 : 2;  // head steps in flight per wave
   static constexpr int HS = 8;               // 32-deep steps of hidden rows in LDS: 4 chunks of 2
-  static constexpr size_t rings = (size_t)kSkWaves * R * NB * 1024 + (size_t)HS * kSkRows * 64;
+  static constexpr int HD = kSkRows / 16 / WV;  // 16-row hidden loads per wave and step
+  static constexpr size_t rings = (size_t)WV * R * NB * 1024 + (size_t)HS * kSkRows * 64;
   // then per row: threshold key, this workgroup's candidate count, its base in
   // the row's list; then per wave its staged candidate count
-  static constexpr size_t lds = rings + (3 * kSkRows + kSkWaves) * sizeof(uint32_t);
+  static constexpr size_t lds = rings + (3 * kSkRows + WV) * sizeof(uint32_t);
   // after the loop the rings hold the staged candidates, a run of wave_cap
   // per wave: composites, then (row | offset in the workgroup's run << 8)
-  static constexpr int wave_cap = (int)(rings / 12 / kSkWaves);
+  static constexpr int wave_cap = (int)(rings / 12 / WV);
 };
-static_assert(SkRing<kSkNB>::lds <= 160 * 1024, "LDS of a CU");
+static_assert(SkRing<kSkNB, kSkWaves>::lds <= 160 * 1024 && SkRing<1, kSkSampleWaves>::lds <= 160 * 1024,
+              "LDS of a CU");
 
 // One 16-byte-per-lane load straight into LDS (buffer_load_dwordx4 ... lds):
 // lane l reads bytes [soff + voff, + 16) of the buffer described by rsrc
@@ -468,14 +471,15 @@ __device__ __forceinline__ int sk_vblock(bool sample, int i, int nblk, int nwork
   return sample ? (int)(((long long)i * nblk) / nwork) : i;
 }
 
-template <bool SAMPLE, int NB>
-__global__ void __launch_bounds__(kSkNT, 1) lmh_skinny_kernel(LmhArgs a, int nwork, int nw_total) {
-  constexpr int R = SkRing<NB>::R, HS = SkRing<NB>::HS;
+template <bool SAMPLE, int NB, int WV>
+__global__ void __launch_bounds__(WV * kWave, 1) lmh_skinny_kernel(LmhArgs a, int nwork, int nw_total) {
+  using Cfg = SkRing<NB, WV>;
+  constexpr int R = Cfg::R, HS = Cfg::HS, HD = Cfg::HD, NT = WV * kWave;
   static_assert(HS % 2 == 0 && HS >= 4 && (HS & (HS - 1)) == 0, "whole chunks of two steps, power of two");
   // [wave][slot][block] 1 KB head fragments, then [HS][128 rows x 4 chunks] hidden rows
   extern __shared__ __attribute__((aligned(16))) uint4 sk_lds[];
   const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(wave_id());
-  const int gw = (int)blockIdx.x * kSkWaves + w;
+  const int gw = (int)blockIdx.x * WV + w;
   const int D = a.D, nS = D / 32;
   const int nblk = (a.V + 15) / 16;
   const int b0 = (int)(((long long)gw * nwork) / nw_total);
@@ -483,7 +487,12 @@ __global__ void __launch_bounds__(kSkNT, 1) lmh_skinny_kernel(LmhArgs a, int nwo
   const int lj = lane & 15, lq = lane >> 4;
 
   // byte offset of this lane's 16 bytes of each block's head fragment at step
-  // 0 (V D and the packed size are below 2^31 elements)
+  // 0 (V D and the packed size are below 2^31 elements).  Lane l loads head
+  // row 16 vbk + l / 4, the 16-byte chunk that lds_chunk puts at position
+  // l % 4 of the row's 64 bytes, so a slot holds the 16 rows x 64 bytes
+  // row-major and swizzled like the hidden rows, and a quarter-wave of a
+  // row-major load reads 4 rows x 64 bytes
+  const int wr_ = lane >> 2, wq_ = (lane & 3) ^ lds_chunk(wr_, 0);
   uint32_t woff[NB];
   int vbk[NB];
 #pragma unroll
@@ -492,25 +501,31 @@ __global__ void __launch_bounds__(kSkNT, 1) lmh_skinny_kernel(LmhArgs a, int nwo
     if (a.packed) {
       // block (vbk / 4, step) of 64 rows x 32 k is 2048 contiguous elements,
       // row-major; this 16-row block is its (vbk % 4)-th 512
-      woff[b] = 2u * ((uint32_t)(vbk[b] >> 2) * (uint32_t)nS * 2048u + (uint32_t)(vbk[b] & 3) * 512u + (uint32_t)(4 * lj + lq) * 8u);
+      woff[b] = 2u * ((uint32_t)(vbk[b] >> 2) * (uint32_t)nS * 2048u + (uint32_t)(vbk[b] & 3) * 512u + (uint32_t)(4 * wr_ + wq_) * 8u);
     } else {
-      woff[b] = 2u * ((uint32_t)min(16 * vbk[b] + lj, a.V - 1) * (uint32_t)D + (uint32_t)(8 * lq));
+      woff[b] = 2u * ((uint32_t)min(16 * vbk[b] + wr_, a.V - 1) * (uint32_t)D + (uint32_t)(8 * wq_));
     }
   }
   const uint32_t wstep = a.packed ? 4096u : 64u;  // bytes per 32-deep step
   const uint32_t wbytes = 2u * (a.packed ? (uint32_t)((a.V + 255) / 256) * 256u * (uint32_t)D : (uint32_t)a.V * (uint32_t)D);
   const i32x4 wrs = sk_rsrc(a.W, wbytes);
   const i32x4 hrs = sk_rsrc(a.H, 2u * (uint32_t)a.M * (uint32_t)D);
-  // hidden rows: this lane loads row 16 w + l / 4, the 16-byte chunk that the
-  // swizzle lds_chunk puts at position l % 4 of the row's 64 bytes
-  const int hr = 16 * w + (lane >> 2);
-  const uint32_t hoff = 2u * ((uint32_t)min(hr, a.M - 1) * (uint32_t)D + 8u * (uint32_t)((lane & 3) ^ lds_chunk(hr, 0)));
+  // hidden rows: load j of this wave brings rows 16 (HD w + j) .. + 15, lane l
+  // row 16 (HD w + j) + l / 4, the 16-byte chunk that the swizzle lds_chunk
+  // puts at position l % 4 of the row's 64 bytes
+  uint32_t hoff[HD];
+#pragma unroll
+  for (int j = 0; j < HD; ++j) {
+    const int hr = 16 * (HD * w + j) + (lane >> 2);
+    hoff[j] = 2u * ((uint32_t)min(hr, a.M - 1) * (uint32_t)D + 8u * (uint32_t)((lane & 3) ^ lds_chunk(hr, 0)));
+  }
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)sk_lds;
   const uint32_t ring = lds0 + (uint32_t)(w * R * NB) * 1024u;
-  const uint32_t hbase = lds0 + (uint32_t)(kSkWaves * R * NB) * 1024u;
-  const int ring_u4 = w * R * NB * 64 + lane;         // uint4 index of this lane in slot 0, block 0
-  const int hbase_u4 = kSkWaves * R * NB * 64;
+  const uint32_t hbase = lds0 + (uint32_t)(WV * R * NB) * 1024u;
+  // uint4 index of this lane's A operand (column lj, k-chunk lq) in slot 0, block 0
+  const int ring_u4 = w * R * NB * 64 + 4 * lj + lds_chunk(lj, lq);
+  const int hbase_u4 = WV * R * NB * 64;
   auto wdma = [&](int g) {  // head fragments of step g into slot g mod R (g outside [0, nS): a
                             // real step again, whose data is overwritten or never read)
     const int gs = min(max(g, 0), nS - 1);
@@ -519,9 +534,11 @@ __global__ void __launch_bounds__(kSkNT, 1) lmh_skinny_kernel(LmhArgs a, int nwo
     for (int b = 0; b < NB; ++b)
       if (b < nbc) sk_dma16(wrs, woff[b], (uint32_t)gs * wstep, slot + (uint32_t)b * 1024u);
   };
-  auto hdma = [&](int g) {  // this wave's 16 hidden rows of step g into slot g mod HS (g < 0: step 0, unused)
-    sk_dma16(hrs, hoff, 64u * (uint32_t)min(max(g, 0), nS - 1),
-             hbase + (uint32_t)(g & (HS - 1)) * 8192u + (uint32_t)w * 1024u);
+  auto hdma = [&](int g) {  // this wave's hidden rows of step g into slot g mod HS (g < 0: step 0, unused)
+#pragma unroll
+    for (int j = 0; j < HD; ++j)
+      sk_dma16(hrs, hoff[j], 64u * (uint32_t)min(max(g, 0), nS - 1),
+               hbase + (uint32_t)(g & (HS - 1)) * 8192u + (uint32_t)(HD * w + j) * 1024u);
   };
 
   f32x4 acc[NB][kSkRB];
@@ -551,9 +568,9 @@ __global__ void __launch_bounds__(kSkNT, 1) lmh_skinny_kernel(LmhArgs a, int nwo
     }
   }
   // chunk 0 (loaded at step 2 - HS) is followed by HS - 3 steps' head loads
-  // and HS - 4 hidden-row loads
-  sk_vm_wait_nb<NB, HS - 3, HS - 4>(nbc);
-  uint32_t* sthr = reinterpret_cast<uint32_t*>(sk_lds + SkRing<NB>::rings / 16);
+  // and (HS - 4) HD hidden-row loads
+  sk_vm_wait_nb<NB, HS - 3, (HS - 4) * HD>(nbc);
+  uint32_t* sthr = reinterpret_cast<uint32_t*>(sk_lds + Cfg::rings / 16);
   int* wg_cnt = reinterpret_cast<int*>(sthr + kSkRows);
   int* wg_base = wg_cnt + kSkRows;
   int* wv_staged = wg_base + kSkRows;
@@ -566,13 +583,13 @@ __global__ void __launch_bounds__(kSkNT, 1) lmh_skinny_kernel(LmhArgs a, int nwo
   __syncthreads();
 
   // (B) Loads issued after head step g's: head steps g + 1 .. g + R - 1, and
-  // two hidden-row loads for each even step in [g - R, g - 1]: R / 2 such
+  // 2 HD hidden-row loads for each even step in [g - R, g - 1]: R / 2 such
   // steps for even R; (R - 1) / 2 for even g and (R + 1) / 2 for odd g when R
   // is odd.  (E) After the next chunk's hidden rows (issued at step
-  // g + 3 - HS, even): HS - 3 steps' head loads and HS - 4 hidden-row loads.
-  // nS is even (D is a multiple of 64), so chunks are whole.
-  constexpr int kEvenH = 2 * (R % 2 == 0 ? R / 2 : (R - 1) / 2);
-  constexpr int kOddH = 2 * (R % 2 == 0 ? R / 2 : (R + 1) / 2);
+  // g + 3 - HS, even): HS - 3 steps' head loads and (HS - 4) HD hidden-row
+  // loads.  nS is even (D is a multiple of 64), so chunks are whole.
+  constexpr int kEvenH = 2 * HD * (R % 2 == 0 ? R / 2 : (R - 1) / 2);
+  constexpr int kOddH = 2 * HD * (R % 2 == 0 ? R / 2 : (R + 1) / 2);
   for (int g0 = 0; g0 < nS; g0 += 2) {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
@@ -611,7 +628,7 @@ __global__ void __launch_bounds__(kSkNT, 1) lmh_skinny_kernel(LmhArgs a, int nwo
         for (int b = 0; b < NB; ++b) acc[b][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[b], hf, acc[b][rb], 0, 0, 0);
       }
       if (p == 1) {
-        sk_vm_wait_nb<NB, HS - 3, HS - 4>(nbc);
+        sk_vm_wait_nb<NB, HS - 3, (HS - 4) * HD>(nbc);
         __syncthreads();
       }
     }
@@ -652,10 +669,10 @@ __global__ void __launch_bounds__(kSkNT, 1) lmh_skinny_kernel(LmhArgs a, int nwo
   // above the row's threshold), staged in LDS (the rings are free once every
   // wave has drained its loads) with their offsets in the workgroup's run of
   // the row's list.
-  constexpr int kWCap = SkRing<NB>::wave_cap;
+  constexpr int kWCap = Cfg::wave_cap;
   constexpr int kOver = 0x40000000;  // in wg_cnt: a candidate of the row did not fit the stage
   uint64_t* stage_c = reinterpret_cast<uint64_t*>(sk_lds);
-  uint32_t* stage_m = reinterpret_cast<uint32_t*>(stage_c + kSkWaves * kWCap);
+  uint32_t* stage_m = reinterpret_cast<uint32_t*>(stage_c + WV * kWCap);
   int staged = 0;  // this wave's candidates so far (wave-uniform)
   __syncthreads();
 #pragma unroll
@@ -759,7 +776,7 @@ __global__ void __launch_bounds__(kSkNT, 1) lmh_skinny_kernel(LmhArgs a, int nwo
     wg_base[threadIdx.x] = base;
   }
   __syncthreads();
-  for (int i = (int)threadIdx.x; i < kSkWaves * kWCap; i += kSkNT) {
+  for (int i = (int)threadIdx.x; i < WV * kWCap; i += NT) {
     const int sw = i / kWCap;
     if (i - sw * kWCap >= wv_staged[sw]) continue;
     const uint32_t m = stage_m[i];
@@ -1063,19 +1080,22 @@ hipError_t launch_lmhead_topk(const void* hidden, const void* weight, bool packe
   const long long ns = (long long)nM * a.S, nm = (long long)nM * a.T;
   const long long gs = (ns + 7) / 8 * 8, gm = (nm + 7) / 8 * 8;
   if (wsl.skinny) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lmh_skinny_kernel<true, 1>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)SkRing<1>::lds);
+    auto* sk_sample = &lmh_skinny_kernel<true, 1, kSkSampleWaves>;
+    auto* sk_main = &lmh_skinny_kernel<false, kSkNB, kSkWaves>;
+    constexpr size_t lds_sample = SkRing<1, kSkSampleWaves>::lds, lds_main = SkRing<kSkNB, kSkWaves>::lds;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(sk_sample),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_sample);
     if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lmh_skinny_kernel<false, kSkNB>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)SkRing<kSkNB>::lds);
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(sk_main), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds_main);
     if (e != hipSuccess) return e;
-    const int swg = (a.S + kSkWaves - 1) / kSkWaves;
-    hipLaunchKernelGGL((lmh_skinny_kernel<true, 1>), dim3(swg), dim3(kSkNT), SkRing<1>::lds, stream, a, a.S,
-                       swg * kSkWaves);
+    const int swg = (a.S + kSkSampleWaves - 1) / kSkSampleWaves;
+    hipLaunchKernelGGL(sk_sample, dim3(swg), dim3(kSkSampleWaves * kWave), lds_sample, stream, a, a.S,
+                       swg * kSkSampleWaves);
     hipLaunchKernelGGL(lmh_threshold_kernel, dim3(M), dim3(kThrNT), 0, stream, a, k);
     const int nblk = (V + 15) / 16;
-    hipLaunchKernelGGL((lmh_skinny_kernel<false, kSkNB>), dim3(wsl.nwg), dim3(kSkNT), SkRing<kSkNB>::lds, stream, a,
-                       nblk, wsl.nwg * kSkWaves);
+    hipLaunchKernelGGL(sk_main, dim3(wsl.nwg), dim3(kSkWaves * kWave), lds_main, stream, a, nblk,
+                       wsl.nwg * kSkWaves);
   } else if (wsl.small) {
     hipLaunchKernelGGL((lmh_tile_kernel<true, 4>), dim3((unsigned)gs), dim3(kNT), 0, stream, a);
     hipLaunchKernelGGL(lmh_threshold_kernel, dim3(M), dim3(kThrNT), 0, stream, a, k);
