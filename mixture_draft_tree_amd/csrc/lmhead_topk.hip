@@ -68,7 +68,7 @@ template <int WGM>
 struct TileShape {
   static constexpr int WGN = 4 / WGM, BN = WGN * 128, IM = 4 / WGM, GPT = WGN * 32, NB = BN / 64;
 };
-constexpr int kThrNT = 256;   // threshold kernel: 2048 sample keys per row
+constexpr int kThrNT = 1024;  // threshold kernel: up to 2048 sample keys per row, two per thread
 constexpr int kSelNT = 1024;  // select kernel: thousands of candidates per row
 constexpr int kSelLdsCap = 8192;  // candidates a select workgroup holds in LDS
 
@@ -408,8 +408,9 @@ struct SkRing {
   static constexpr int HD = kSkRows / 16 / WV;  // 16-row hidden loads per wave and step
   static constexpr size_t rings = (size_t)WV * R * NB * 1024 + (size_t)HS * kSkRows * 64;
   // then per row: threshold key, this workgroup's candidate count, its base in
-  // the row's list; then per wave its staged candidate count
-  static constexpr size_t lds = rings + (3 * kSkRows + WV) * sizeof(uint32_t);
+  // the row's list; per wave its staged candidate count; per wave and row its
+  // partial (max, sum exp(x - max))
+  static constexpr size_t lds = rings + (3 * kSkRows + WV) * sizeof(uint32_t) + (size_t)WV * kSkRows * sizeof(float2);
   // after the loop the rings hold the staged candidates, a run of wave_cap
   // per wave: composites, then (row | offset in the workgroup's run << 8)
   static constexpr int wave_cap = (int)(rings / 12 / WV);
@@ -574,6 +575,7 @@ __global__ void __launch_bounds__(WV * kWave, 1) lmh_skinny_kernel(LmhArgs a, in
   int* wg_cnt = reinterpret_cast<int*>(sthr + kSkRows);
   int* wg_base = wg_cnt + kSkRows;
   int* wv_staged = wg_base + kSkRows;
+  float2* wv_part = reinterpret_cast<float2*>(wv_staged + WV);  // [WV][kSkRows]
   if (!SAMPLE && (int)threadIdx.x < kSkRows) {
     // (this load completes before the barrier: no load of the compiler's is
     // in flight in the loop, whose waits count only the ring loads)
@@ -674,36 +676,63 @@ __global__ void __launch_bounds__(WV * kWave, 1) lmh_skinny_kernel(LmhArgs a, in
   uint64_t* stage_c = reinterpret_cast<uint64_t*>(sk_lds);
   uint32_t* stage_m = reinterpret_cast<uint32_t*>(stage_c + WV * kWCap);
   int staged = 0;  // this wave's candidates so far (wave-uniform)
+  // every column of every lane exists: all waves but the last few
+  const bool all_valid = __ballot(vmask != (NB * 4 == 32 ? 0xFFFFFFFFu : (1u << (NB * 4)) - 1u)) == 0ull;
   __syncthreads();
 #pragma unroll
   for (int rb = 0; rb < kSkRB; ++rb) {
     const int row = rb * 16 + lj;
     const bool rok = row < a.M;
-    float mx = -INFINITY;
+    float mx = -INFINITY, sm = 0.0f;
     bool bad = false;
+    if (all_valid) {
+      // a NaN logit turns the sum NaN, +inf the maximum, -inf the minimum
+      float mn = INFINITY;
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float x = acc[b][rb][r];
-        const bool v = (vmask >> (4 * b + r)) & 1u;
-        bad |= v && !__builtin_isfinite(x);
-        mx = fmaxf(mx, v ? x : -INFINITY);
-      }
-    mx = fmaxf(mx, xor_lanes(mx, 16));
-    mx = fmaxf(mx, xor_lanes(mx, 32));
-    float sm = 0.0f;
+        for (int r = 0; r < 4; ++r) {
+          mx = fmaxf(mx, acc[b][rb][r]);
+          mn = fminf(mn, acc[b][rb][r]);
+        }
+      mx = fmaxf(mx, xor_lanes(mx, 16));
+      mx = fmaxf(mx, xor_lanes(mx, 32));
+      const float mxl = mx * 1.44269504088896341f;  // log2(e)
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool v = (vmask >> (4 * b + r)) & 1u;
-        sm += v && mx > -INFINITY ? __expf(acc[b][rb][r] - mx) : 0.0f;
-      }
-    sm += xor_lanes(sm, 16);
-    sm += xor_lanes(sm, 32);
-    if (lq == 0 && rok) a.part[(size_t)row * nw_total + gw] = make_float2(mx, sm);
-    if (bad && rok && a.status != nullptr) atomicOr(&a.status[row / a.rows_per_tree], MFD_TREE_NONFINITE);
+        for (int r = 0; r < 4; ++r) sm += __builtin_amdgcn_exp2f(fmaf(acc[b][rb][r], 1.44269504088896341f, -mxl));
+      sm += xor_lanes(sm, 16);
+      sm += xor_lanes(sm, 32);
+      mn = fminf(mn, xor_lanes(mn, 16));
+      mn = fminf(mn, xor_lanes(mn, 32));
+      bad = !__builtin_isfinite(sm) || !__builtin_isfinite(mx) || mn == -INFINITY;
+      if (bad && !(mx > -INFINITY)) sm = 0.0f;
+    } else {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float x = acc[b][rb][r];
+          const bool v = (vmask >> (4 * b + r)) & 1u;
+          bad |= v && !__builtin_isfinite(x);
+          mx = fmaxf(mx, v ? x : -INFINITY);
+        }
+      mx = fmaxf(mx, xor_lanes(mx, 16));
+      mx = fmaxf(mx, xor_lanes(mx, 32));
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool v = (vmask >> (4 * b + r)) & 1u;
+          sm += v && mx > -INFINITY ? __expf(acc[b][rb][r] - mx) : 0.0f;
+        }
+      sm += xor_lanes(sm, 16);
+      sm += xor_lanes(sm, 32);
+      bad = __ballot(bad) != 0ull ? (xor_lanes((int)bad, 16) | xor_lanes((int)bad, 32) | xor_lanes(xor_lanes((int)bad, 16), 32) | (int)bad) != 0 : false;
+    }
+    if (lq == 0) wv_part[w * kSkRows + row] = make_float2(mx, sm);
+    if (lq == 0 && bad && rok && a.status != nullptr) atomicOr(&a.status[row / a.rows_per_tree], MFD_TREE_NONFINITE);
 
     // candidate bits: key >= th, as a float compare where the lane's values
     // are finite (the key order is the float order there, -0 = +0); th = 0
@@ -744,19 +773,25 @@ __global__ void __launch_bounds__(WV * kWave, 1) lmh_skinny_kernel(LmhArgs a, in
       const bool fits = staged + wtot <= kWCap;  // wave-uniform
       if (!fits && cnt > 0 && gi + cnt > kWCap) atomicOr(&wg_cnt[row], kOver);
       const int sbase = w * kWCap;
+      // this lane's candidates, lowest bit first (a lane holds few: the loop
+      // runs as often as the wave's busiest lane needs)
+      uint32_t m = pm;
+      for (int j = 0; m != 0u; ++j) {
+        const int bit = __builtin_ctz(m);
+        m &= m - 1u;
+        const int bb = bit >> 2, rr = bit & 3;
+        f32x4 v = acc[0][rb];
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
+        for (int b = 1; b < NB; ++b) v = bb == b ? acc[b][rb] : v;
+        const float x = rr == 0 ? v[0] : rr == 1 ? v[1] : rr == 2 ? v[2] : v[3];
+        int vb = vbk[0];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int bit = 4 * b + r;
-          if ((pm >> bit) & 1u) {
-            const int below = __popc(pm & ((1u << bit) - 1u));
-            if (fits || gi + below < kWCap) {
-              stage_c[sbase + gi + below] = cand_composite(sk_key(acc[b][rb][r]), (uint32_t)(16 * vbk[b] + 4 * lq + r));
-              stage_m[sbase + gi + below] = (uint32_t)row | ((uint32_t)(off + below) << 8);
-            }
-          }
+        for (int b = 1; b < NB; ++b) vb = bb == b ? vbk[b] : vb;
+        if (fits || gi + j < kWCap) {
+          stage_c[sbase + gi + j] = cand_composite(sk_key(x), (uint32_t)(16 * vb + 4 * lq + rr));
+          stage_m[sbase + gi + j] = (uint32_t)row | ((uint32_t)(off + j) << 8);
         }
+      }
       staged += wtot;
     }
   }
@@ -767,6 +802,20 @@ __global__ void __launch_bounds__(WV * kWave, 1) lmh_skinny_kernel(LmhArgs a, in
   // the select kernel reports); then the stage is copied out
   __syncthreads();
   if ((int)threadIdx.x < kSkRows) {
+    // the workgroup's partial of the row: its waves' partials combined
+    const int row = (int)threadIdx.x;
+    float pm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < WV; ++i) pm = fmaxf(pm, wv_part[i * kSkRows + row].x);
+    float ps = 0.0f;
+    if (pm > -INFINITY) {
+#pragma unroll
+      for (int i = 0; i < WV; ++i) {
+        const float2 q = wv_part[i * kSkRows + row];
+        if (q.x > -INFINITY) ps += q.y * __expf(q.x - pm);
+      }
+    }
+    if (row < a.M) a.part[(size_t)row * gridDim.x + blockIdx.x] = make_float2(pm, ps);
     const int n = wg_cnt[threadIdx.x];
     int base = 0;
     if (n != 0 && (int)threadIdx.x < a.M) {
@@ -786,30 +835,91 @@ __global__ void __launch_bounds__(WV * kWave, 1) lmh_skinny_kernel(LmhArgs a, in
   }
 }
 
-// Per row: the candidate threshold (k-th largest group maximum, or 0 = take
-// every column when the sample holds fewer than k groups); resets the row's
-// candidate count.
+// Per row: the candidate threshold, or 0 = take every column when the sample
+// holds fewer than k groups; resets the row's candidate count.  The threshold
+// is the lower edge of the histogram bin that holds the k-th largest group
+// maximum, in 4096 bins over the row's range of group-maximum keys: at least
+// k of those maxima (k distinct elements of the row) lie at or above it, so
+// the row's k-th largest logit does too.  One pass over keys held in
+// registers; the bins are a 4096th of the range, so the threshold sits at
+// most that far below the k-th largest maximum.
+constexpr int kThrBins = 4096;
+static_assert(kSampleCols / 4 <= 2 * kThrNT && kThrBins == 4 * kThrNT, "keys and bins per thread");
 __global__ void __launch_bounds__(kThrNT) lmh_threshold_kernel(LmhArgs a, int k) {
-  __shared__ uint32_t hist[256];
-  __shared__ int sh[2];
-  __shared__ int red[kThrNT / kWave];
-  const int row = (int)blockIdx.x;
+  __shared__ uint32_t hist[kThrBins];
+  __shared__ uint32_t red[3][kThrNT / kWave];
+  __shared__ int found;
+  const int row = (int)blockIdx.x, tid = (int)threadIdx.x, lane = lane_id(), w = wave_id();
   const int n = a.S * a.gpt;
   const uint32_t* g = a.samp + (size_t)row * n;
+  uint32_t kv[2];
   int cnt = 0;
-  for (int i = threadIdx.x; i < n; i += kThrNT) cnt += g[i] != 0u ? 1 : 0;
-  cnt = block_sum<kThrNT>(cnt, red);
-  uint32_t thr = 0;
-  if (cnt >= k) {
-    thr = (uint32_t)block_kth_largest<kThrNT, 32>(
-        n, k,
-        [&](int i, uint64_t* key) {
-          *key = g[i];
-          return g[i] != 0u;
-        },
-        hist, sh);
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = tid + j * kThrNT;
+    kv[j] = i < n ? g[i] : 0u;  // 0: a group with no column
+    if (kv[j] != 0u) {
+      ++cnt;
+      lo = min(lo, kv[j]);
+      hi = max(hi, kv[j]);
+    }
   }
-  if (threadIdx.x == 0) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) hist[4 * tid + j] = 0u;
+  cnt = wave_allreduce(cnt, [](int x, int y) { return x + y; });
+  lo = wave_allreduce(lo, [](uint32_t x, uint32_t y) { return min(x, y); });
+  hi = wave_allreduce(hi, [](uint32_t x, uint32_t y) { return max(x, y); });
+  if (lane == 0) {
+    red[0][w] = (uint32_t)cnt;
+    red[1][w] = lo;
+    red[2][w] = hi;
+  }
+  if (tid == 0) found = 0;
+  __syncthreads();
+  cnt = 0;
+  lo = 0xFFFFFFFFu;
+  hi = 0u;
+#pragma unroll
+  for (int i = 0; i < kThrNT / kWave; ++i) {
+    cnt += (int)red[0][i];
+    lo = min(lo, red[1][i]);
+    hi = max(hi, red[2][i]);
+  }
+  uint32_t thr = 0u;
+  if (cnt >= k) {
+    const uint32_t range = hi - lo;
+    const int bits = range == 0u ? 0 : 32 - __clz((int)range);
+    const int shift = bits > 12 ? bits - 12 : 0;  // (range >> shift) < kThrBins
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (kv[j] != 0u) atomicAdd(&hist[(kv[j] - lo) >> shift], 1u);
+    __syncthreads();
+    // thread t holds bins 4095 - 4 t .. 4092 - 4 t (thread 0 the highest):
+    // a prefix over threads counts the keys in higher bins
+    uint32_t hb[4];
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      hb[j] = hist[kThrBins - 1 - 4 * tid - j];
+      c += (int)hb[j];
+    }
+    const int incl = wave_inclusive_scan(c);
+    __syncthreads();  // hist reads done; red is reused
+    if (lane == kWave - 1) red[0][w] = (uint32_t)incl;
+    __syncthreads();
+    int above = incl - c;
+    for (int i = 0; i < w; ++i) above += (int)red[0][i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int now = above + (int)hb[j];
+      if (above < k && now >= k) found = kThrBins - 1 - 4 * tid - j;  // exactly one bin
+      above = now;
+    }
+    __syncthreads();
+    thr = lo + ((uint32_t)found << shift);
+  }
+  if (tid == 0) {
     a.thr[row] = thr;
     a.cand_count[(size_t)row * kCountStride] = 0;
   }
@@ -879,8 +989,16 @@ __global__ void __launch_bounds__(kSelNT) lmh_select_kernel(LmhArgs a, int k, do
   const uint64_t* cg = a.cand + (size_t)row * a.C;
   const bool in_lds = cnt <= kSelLdsCap;
   uint64_t* sortb = lds + kSelLdsCap;
-  if (in_lds)
-    for (int i = tid; i < cnt; i += kSelNT) lds[i] = cg[i];
+  if (in_lds) {
+    // all of this thread's loads in flight at once, then the LDS writes
+    constexpr int kPer = kSelLdsCap / kSelNT;
+    uint64_t cv[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) cv[j] = tid + j * kSelNT < cnt ? cg[tid + j * kSelNT] : 0ull;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (tid + j * kSelNT < cnt) lds[tid + j * kSelNT] = cv[j];
+  }
   __syncthreads();
   const uint64_t* src = in_lds ? lds : cg;
 
@@ -945,22 +1063,58 @@ __global__ void __launch_bounds__(kSelNT) lmh_select_kernel(LmhArgs a, int k, do
           ((uint64_t)kkey << 32);
   }
 
-  // 4. gather the k composites >= kth (composites are distinct), sort, write descending
+  // 4. gather the k composites >= kth (composites are distinct), order them
+  //    descending, write.  Up to kSelNT of them: each goes straight to its
+  //    rank (the number of larger ones), counted by G threads per composite;
+  //    more: a sorting network.
   const int P = next_pow2(k);
-  for (int i = tid; i < P; i += kSelNT) sortb[i] = 0ull;
   if (tid == 0) nsel = 0;
+  if (k > kSelNT)
+    for (int i = tid; i < P; i += kSelNT) sortb[i] = 0ull;
   __syncthreads();
   for (int i = tid; i < cnt; i += kSelNT) {
     const uint64_t c = src[i];
     if (c >= kth) {
       const int slot = atomicAdd(&nsel, 1);
-      if (slot < k) sortb[P - k + slot] = c;
+      if (slot < k) sortb[(k > kSelNT ? P - k : 0) + slot] = c;
     }
   }
   __syncthreads();
-  block_sort_keys<kSelNT>(sortb, P);
+  uint64_t* sorted = sortb + P;  // descending
+  if (k <= kSelNT) {
+    const int G = min(kWave, kSelNT / P);  // threads per composite (a power of two, within a wave)
+    const int i = tid / G, part = tid % G;
+    const int per = (k + G - 1) / G;
+    int above = 0;
+    uint64_t c = 0;
+    if (i < k) {
+      c = sortb[i];
+      int j = part * per;
+      const int j1 = min(k, j + per);
+      // eight composites per batch (16-byte reads from an even index), so
+      // the reads are in flight together
+      if (j & 1) above += (j < j1 && sortb[j] > c) ? 1 : 0, ++j;
+      for (; j + 8 <= j1; j += 8) {
+        uint4 q[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) q[t] = *reinterpret_cast<const uint4*>(&sortb[j + 2 * t]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          above += (((uint64_t)q[t].y << 32) | q[t].x) > c ? 1 : 0;
+          above += (((uint64_t)q[t].w << 32) | q[t].z) > c ? 1 : 0;
+        }
+      }
+      for (; j < j1; ++j) above += sortb[j] > c ? 1 : 0;
+    }
+    for (int o = 1; o < G; o <<= 1) above += __shfl_xor(above, o, kWave);
+    if (i < k && part == 0) sorted[above] = c;
+  } else {
+    block_sort_keys<kSelNT>(sortb, P);
+    for (int j = tid; j < k; j += kSelNT) sorted[j] = sortb[P - 1 - j];
+  }
+  __syncthreads();
   for (int j = tid; j < k; j += kSelNT) {
-    const uint64_t c = sortb[P - 1 - j];
+    const uint64_t c = sorted[j];
     const uint32_t key = (uint32_t)(c >> 32);
     const float raw = __uint_as_float(f32_from_key(key));
     const int32_t col = (int32_t)(0xFFFFFFFFu - (uint32_t)c);
@@ -1017,7 +1171,7 @@ LmhWorkspace lmhead_workspace(long long M, int V, int k) {
     BN = 16;
     w.gpt = 4;
     w.wgn = 1;
-    w.T = w.nwg * kSkWaves;
+    w.T = w.nwg;  // partials per row: one per workgroup
     w.S = std::min(nblk, kSkSampleBlocks);
   } else {
     BN = w.small ? TileShape<4>::BN : TileShape<2>::BN;
@@ -1105,7 +1259,7 @@ hipError_t launch_lmhead_topk(const void* hidden, const void* weight, bool packe
     hipLaunchKernelGGL(lmh_threshold_kernel, dim3(M), dim3(kThrNT), 0, stream, a, k);
     hipLaunchKernelGGL((lmh_tile_kernel<false, 2>), dim3((unsigned)gm), dim3(kNT), 0, stream, a);
   }
-  const size_t lds = (size_t)(kSelLdsCap + next_pow2(k)) * sizeof(uint64_t);
+  const size_t lds = (size_t)(kSelLdsCap + 2 * next_pow2(k)) * sizeof(uint64_t);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lmh_select_kernel),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
