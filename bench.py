@@ -161,6 +161,8 @@ def fused_lmhead(steps: int, stream) -> dict:
             "unfused_total_ms": mm_ms + lsm_ms, "fused_over_unfused": fused_ms / (mm_ms + lsm_ms),
             "reduced_vocab_fused_ms": sub_ms, "reduced_vocab_tokens": 65536,
             "packed_head_fused_ms": packed_ms,
+            "packed_head_read_GBps": V * D * 2 / (packed_ms * 1e-3) / 1e9,
+            "packed_head_over_unfused": packed_ms / (mm_ms + lsm_ms),
         }
         del b, H, W, logits, lg, ws
         torch.cuda.empty_cache()

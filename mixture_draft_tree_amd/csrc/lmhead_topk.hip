@@ -1063,58 +1063,22 @@ __global__ void __launch_bounds__(kSelNT) lmh_select_kernel(LmhArgs a, int k, do
           ((uint64_t)kkey << 32);
   }
 
-  // 4. gather the k composites >= kth (composites are distinct), order them
-  //    descending, write.  Up to kSelNT of them: each goes straight to its
-  //    rank (the number of larger ones), counted by G threads per composite;
-  //    more: a sorting network.
+  // 4. gather the k composites >= kth (composites are distinct), sort, write descending
   const int P = next_pow2(k);
+  for (int i = tid; i < P; i += kSelNT) sortb[i] = 0ull;
   if (tid == 0) nsel = 0;
-  if (k > kSelNT)
-    for (int i = tid; i < P; i += kSelNT) sortb[i] = 0ull;
   __syncthreads();
   for (int i = tid; i < cnt; i += kSelNT) {
     const uint64_t c = src[i];
     if (c >= kth) {
       const int slot = atomicAdd(&nsel, 1);
-      if (slot < k) sortb[(k > kSelNT ? P - k : 0) + slot] = c;
+      if (slot < k) sortb[P - k + slot] = c;
     }
   }
   __syncthreads();
-  uint64_t* sorted = sortb + P;  // descending
-  if (k <= kSelNT) {
-    const int G = min(kWave, kSelNT / P);  // threads per composite (a power of two, within a wave)
-    const int i = tid / G, part = tid % G;
-    const int per = (k + G - 1) / G;
-    int above = 0;
-    uint64_t c = 0;
-    if (i < k) {
-      c = sortb[i];
-      int j = part * per;
-      const int j1 = min(k, j + per);
-      // eight composites per batch (16-byte reads from an even index), so
-      // the reads are in flight together
-      if (j & 1) above += (j < j1 && sortb[j] > c) ? 1 : 0, ++j;
-      for (; j + 8 <= j1; j += 8) {
-        uint4 q[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) q[t] = *reinterpret_cast<const uint4*>(&sortb[j + 2 * t]);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          above += (((uint64_t)q[t].y << 32) | q[t].x) > c ? 1 : 0;
-          above += (((uint64_t)q[t].w << 32) | q[t].z) > c ? 1 : 0;
-        }
-      }
-      for (; j < j1; ++j) above += sortb[j] > c ? 1 : 0;
-    }
-    for (int o = 1; o < G; o <<= 1) above += __shfl_xor(above, o, kWave);
-    if (i < k && part == 0) sorted[above] = c;
-  } else {
-    block_sort_keys<kSelNT>(sortb, P);
-    for (int j = tid; j < k; j += kSelNT) sorted[j] = sortb[P - 1 - j];
-  }
-  __syncthreads();
+  block_sort_keys<kSelNT>(sortb, P);
   for (int j = tid; j < k; j += kSelNT) {
-    const uint64_t c = sorted[j];
+    const uint64_t c = sortb[P - 1 - j];
     const uint32_t key = (uint32_t)(c >> 32);
     const float raw = __uint_as_float(f32_from_key(key));
     const int32_t col = (int32_t)(0xFFFFFFFFu - (uint32_t)c);
@@ -1259,7 +1223,7 @@ hipError_t launch_lmhead_topk(const void* hidden, const void* weight, bool packe
     hipLaunchKernelGGL(lmh_threshold_kernel, dim3(M), dim3(kThrNT), 0, stream, a, k);
     hipLaunchKernelGGL((lmh_tile_kernel<false, 2>), dim3((unsigned)gm), dim3(kNT), 0, stream, a);
   }
-  const size_t lds = (size_t)(kSelLdsCap + 2 * next_pow2(k)) * sizeof(uint64_t);
+  const size_t lds = (size_t)(kSelLdsCap + next_pow2(k)) * sizeof(uint64_t);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&lmh_select_kernel),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
