@@ -901,7 +901,48 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
     // disagree.  Scores use the search's own expression.
     const int q = k < kFirstQ ? k : kFirstQ;
     const int np = Kn * q;
-    if (np >= B) {
+    // the distinct tokens: an LDS hash table in the (free) sort area, slot h
+    // holding a token and the ordered key of its best pooled score (a NaN
+    // score takes the largest key, so the token's best is NaN, as below)
+    int H = 1;
+    while (H * 2 * 12 <= a.sort_cap * 8) H *= 2;  // 12 bytes per slot
+    if (np >= B && H >= 2 * np) {
+      uint64_t* hkey = keys;
+      uint32_t* htok = reinterpret_cast<uint32_t*>(keys + H);
+      constexpr uint32_t kEmpty = 0xFFFFFFFFu;
+      for (int c = tid; c < H; c += kNT) {
+        hkey[c] = 0ull;
+        htok[c] = kEmpty;
+      }
+      __syncthreads();
+      for (int c = tid; c < np; c += kNT) {
+        const int m = c / q, j = c - m * q;
+        const size_t at = ((size_t)(n * K + m) * L) * k + j;
+        const int tok = a.topk_id[at];
+        const float x = a.topk_raw[at];
+        if (tok < 0 || x == -INFINITY) continue;  // no candidate: its score is -inf
+        const double sc = (0.0 + (double)x) - norm[m * Lp1 + 1];
+        // Fibonacci hashing, linear probing; H > np slots, so a probe ends
+        uint32_t h = ((uint32_t)tok * 0x9E3779B1u) & (uint32_t)(H - 1);
+        while (true) {
+          const uint32_t prev = atomicCAS(&htok[h], kEmpty, (uint32_t)tok);
+          if (prev == kEmpty || prev == (uint32_t)tok) break;
+          h = (h + 1u) & (uint32_t)(H - 1);
+        }
+        atomicMax(reinterpret_cast<unsigned long long*>(&hkey[h]), (unsigned long long)(sc != sc ? ~0ull : f64_key(sc)));
+      }
+      __syncthreads();
+      const double t0 = ctl.tau;
+      auto best = [&](int i) { return htok[i] == kEmpty ? (double)NAN : f64_from_key(hkey[i]); };
+      int local = 0;
+      for (int i = tid; i < H; i += kNT) local += best(i) >= t0 ? 1 : 0;
+      const int alive = block_sum<kNT>(local, ctl.scan);
+      if (alive >= B) {
+        const double nb = kth_lower_bound(H, B, best, [&](int i) { return best(i) >= t0; }, ctl);
+        if (tid == 0 && nb > t0) ctl.tau = nb;
+      }
+      __syncthreads();
+    } else if (np >= B) {
       // keys[0, P) are sorted; the pooled scores wait in keys[P, 2P)
       // (2P <= sort_cap: sort_cap >= 2 K k, or 16384)
       const int P = next_pow2(np);

@@ -357,12 +357,38 @@ class TreeModel:
         if B > 0:
             q = min(k, FIRST_Q)
             npool = K * q
+            # distinct tokens by an LDS hash table in the sort area (12 bytes
+            # per slot, at most half full), else by a sort of the pooled keys
+            H = 1
+            while H * 2 * 12 <= c.sort_cap * 8:
+                H *= 2
+            if npool >= B and H >= 2 * npool:
+                hkey = CheckedArray("pool hash keys", c.sort_cap)          # slots [0, H) as 8-byte words
+                htok = CheckedArray("pool hash tokens", 2 * c.sort_cap)    # 4-byte words from byte 8 H
+                for h in range(H):
+                    hkey[h] = 0
+                    htok[2 * H + h] = -1
+                for m in range(K):
+                    for j in range(q):
+                        t = int(self.id[m, 0, j])
+                        if t < 0 or float(self.raw[m, 0, j]) == -math.inf:
+                            continue
+                        h = (t * 0x9E3779B1) & 0xFFFFFFFF & (H - 1)
+                        for _ in range(H):
+                            if htok[2 * H + h] in (-1, t):
+                                htok[2 * H + h] = t
+                                break
+                            h = (h + 1) & (H - 1)
+                        else:
+                            raise IndexError("pooled bound: hash table full")
+                res.pooled_P = H
             if npool >= B:
                 P = next_pow2(npool)
-                if 2 * P > c.sort_cap:
-                    raise IndexError(f"pooled bound: 2P={2 * P} keys past the sort buffer {c.sort_cap}")
-                res.pooled_P = P
-                check_block_sort_keys(P, c.sort_cap)
+                if not (H >= 2 * npool):
+                    if 2 * P > c.sort_cap:
+                        raise IndexError(f"pooled bound: 2P={2 * P} keys past the sort buffer {c.sort_cap}")
+                    res.pooled_P = P
+                    check_block_sort_keys(P, c.sort_cap)
                 best = {}
                 for m in range(K):
                     for j in range(q):
