@@ -129,7 +129,8 @@ mfd_status mfd_workspace_size(mfd_op op, int N, int K, int L, int V, int B, size
  *   logits    device [N, K, L, V], bf16 (MFD_BF16) or fp32 (MFD_F32), read once.
  *             Row r = (n, K, L) flattened; must be aligned to the element size.
  *   lse       device [N, K, L] fp64 out: log sum_v exp(logits[r, v]); -inf for
- *             a row of only -inf.
+ *             a row of only -inf.  Never below the row's largest logit (as the
+ *             exact value never is), so no log-probability is positive.
  *   topk_id   device [N, K, L, k] int32 out: token ids by logit descending,
  *             equal logits by id ascending (-0.0 and +0.0 are equal).
  *   topk_raw  device [N, K, L, k] fp32 out: the logit of each listed token,
@@ -170,7 +171,9 @@ mfd_status mfd_logsoftmax_topk_mapped(const void* logits, mfd_dtype dtype, int N
  * one cut-off shared by every mode; step 3: every prefix is scored by its best
  * mode).  A prefix t = (t_1..t_d), 1 <= d <= L, scores
  *     s_k(t) = (sum_{i<=d} raw_k(i, t_i)) - (sum_{i<=d} lse[k, i])
- * under mode k (both sums fp64, accumulated from i = 1 upward), and
+ * under mode k (both sums fp64, accumulated from i = 1 upward; an lse below
+ * its row's first listed logit is taken as that logit, so that a prefix
+ * never outscores its parent), and
  * S(t) = max_k s_k(t).  A mode scores only prefixes whose every token is among
  * its k listed candidates at that position (with k = min(B, V) this changes
  * nothing among the B best); -inf candidates never count.  Prefixes are

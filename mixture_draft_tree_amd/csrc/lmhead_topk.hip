@@ -968,7 +968,12 @@ __global__ void __launch_bounds__(kSelNT) lmh_select_kernel(LmhArgs a, int k, do
   double tot = 0.0;
 #pragma unroll
   for (int i = 0; i < kSelNT / kWave; ++i) tot += redd[i];
-  const double l = mx > -INFINITY ? (double)mx + log(tot) : -INFINITY;
+  // the row maximum's own term is about 1, but exp2-domain rounding can leave
+  // the sum just under it; the normaliser is kept at or above the maximum
+  // (a NaN sum stays NaN)
+  double lg = log(tot);
+  lg = lg < 0.0 ? 0.0 : lg;
+  const double l = mx > -INFINITY ? (double)mx + lg : -INFINITY;
   if (tid == 0) lse[row] = l;
 
   // 2. candidates

@@ -553,10 +553,7 @@ __global__ void __launch_bounds__(kThreads, 5) lsm_topk_kernel(const typename El
       lse = (double)b2 * kLn2 + log(sum2);
     }
   }
-  if (tid == 0) {
-    lse_out[row] = lse;
-    if (status && (isnan(lse) || lse == INFINITY)) atomicOr(&status[row / rows_per_tree], 1);
-  }
+  if (tid == 0 && status && (isnan(lse) || lse == INFINITY)) atomicOr(&status[row / rows_per_tree], 1);
 
   // ------------------------------------------------------------ exact top-k
   uint64_t* sb = sortbuf;  // where the survivors end up
@@ -768,6 +765,18 @@ __global__ void __launch_bounds__(kThreads, 5) lsm_topk_kernel(const typename El
     __syncthreads();
   }
 
+  // The log-normaliser is stored once the row maximum (the largest survivor)
+  // is known: exp2-domain rounding can leave it a little under the maximum,
+  // and it is raised to it there (a NaN stays NaN), so that no
+  // log-probability comes out positive.
+  auto settle_lse = [&](bool mine, float top) {
+    if (mine) S.red_max[0] = top;
+    __syncthreads();
+    const double t = (double)S.red_max[0];
+    if (lse < t) lse = t;
+    if (tid == 0) lse_out[row] = lse;
+  };
+
   // sort the survivors (descending composite = key descending, token ascending)
   const int ns = S.nsurv;
   const int P = next_pow2(ns < k ? k : ns);
@@ -775,6 +784,7 @@ __global__ void __launch_bounds__(kThreads, 5) lsm_topk_kernel(const typename El
     uint64_t a0 = tid < ns ? sb[tid] : 0ull;
     __syncthreads();
     block_sort_single<kThreads>(a0, sb);
+    settle_lse(tid == kThreads - 1, E::val_of_key((uint32_t)(a0 >> 32)));
     const int j = kThreads - 1 - tid;
     if (j < k) {
       const uint32_t key = (uint32_t)(a0 >> 32);
@@ -792,6 +802,7 @@ __global__ void __launch_bounds__(kThreads, 5) lsm_topk_kernel(const typename El
     uint64_t a1 = 2 * tid + 1 < ns ? sb[2 * tid + 1] : 0ull;
     __syncthreads();
     block_sort_pairs<kThreads>(a0, a1, sb);
+    settle_lse(tid == kThreads - 1, E::val_of_key((uint32_t)(a1 >> 32)));
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int j = 2 * kThreads - 1 - (2 * tid + e);
@@ -811,6 +822,7 @@ __global__ void __launch_bounds__(kThreads, 5) lsm_topk_kernel(const typename El
   for (int i = ns + tid; i < P; i += kThreads) sb[i] = 0ull;
   __syncthreads();
   block_bitonic_sort<kThreads>(sb, P);
+  settle_lse(tid == 0, E::val_of_key((uint32_t)(sb[P - 1] >> 32)));
   for (int j = tid; j < k; j += kThreads) {
     const uint64_t c = sb[P - 1 - j];
     const uint32_t key = (uint32_t)(c >> 32);

@@ -535,8 +535,40 @@ __device__ __forceinline__ void level_search(const TreeArgs& a, const Tree& t, i
       if (!ctl.up) return;
       if (nk) {
         // on the 16-bit keys in LDS: the B-th largest key among those at or
-        // above tau's stands for B distinct nodes scoring at least its value
+        // above tau's stands for B distinct nodes scoring at least its value.
+        // One pass first: a histogram of key - kt (255 and above share the
+        // top bin), which also counts the keys at or above kt; keys of the
+        // scores in play span far fewer than 255 values above tau's, so the
+        // B-th largest is found there unless it falls in the top bin.
         const uint32_t kt = (uint32_t)(f64_key(tau) >> 48);
+        for (int i = tid; i < 256; i += kNT) ctl.hist[i] = 0u;
+        __syncthreads();
+        for (int i = 1 + tid; i < ctl.node_count; i += kNT) {
+          const uint32_t kk = nk[i];
+          if (kk >= kt) atomicAdd(&ctl.hist[min(kk - kt, 255u)], 1u);
+        }
+        __syncthreads();
+        if (tid < kWave) {
+          int tot = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) tot += (int)ctl.hist[4 * tid + j];
+          tot = wave_allreduce(tot, [](int x, int y) { return x + y; });
+          int digit = -1, above = 0;
+          if (tot >= B && B > 0) wave_pick_digit(ctl.hist, B, &digit, &above);
+          digit = wave_allreduce(digit, [](int x, int y) { return x > y ? x : y; });
+          if (tid == 0) ctl.sh[0] = tot >= B && B > 0 ? digit : -1;
+        }
+        __syncthreads();
+        const int dg = ctl.sh[0];
+        __syncthreads();
+        if (dg < 0) return;  // fewer than B keys at or above tau's
+        if (dg < 255) {
+          const double nt = f64_from_key((uint64_t)(kt + (uint32_t)dg) << 48);
+          if (nt > tau) tau = nt;
+          if (tid == 0) ctl.tau = tau;
+          __syncthreads();
+          return;
+        }
         int local = 0;
         for (int i = 1 + tid; i < ctl.node_count; i += kNT) local += nk[i] >= kt ? 1 : 0;
         const int alive = block_sum<kNT>(local, ctl.scan);
@@ -815,10 +847,15 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
   }
 
   // norm[m][d] = sum_{i<d} lse[m][i], fp64, from i = 0 upward (all Kn*L
-  // values loaded at once, then one running sum per mode)
+  // values loaded at once, then one running sum per mode).  A row's
+  // normaliser is taken no lower than its top logit: the true one never is,
+  // and a positive log-probability from rounding would let a child outscore
+  // its parent (the comparison keeps a NaN normaliser NaN).
   for (int q = tid; q < Kn * L; q += kNT) {
     const int m = q / L, i = q - m * L;
-    norm[m * Lp1 + i + 1] = a.lse[(size_t)n * K * L + q];
+    const double l = a.lse[(size_t)n * K * L + q];
+    const double top = (double)a.topk_raw[((size_t)n * K * L + q) * k];
+    norm[m * Lp1 + i + 1] = l < top ? top : l;
   }
   // the rows' leading candidates (past k: -inf), loaded with the norms
   for (int q = tid; q < Kn * L * a.pre_q; q += kNT) {

@@ -275,6 +275,8 @@ class SearchResult:
     cutoff: float = math.inf
     n_select: int = 0
     pooled_P: int = 0
+    window_hits: int = 0
+    window_misses: int = 0
     node_S: list = field(default_factory=list)
 
 
@@ -293,7 +295,8 @@ class TreeModel:
         for m in range(self.K):
             acc = 0.0
             for i in range(self.L):
-                acc = acc + float(lse[m, i])
+                # the kernel's normaliser: lse, but never below the row's top logit
+                acc = acc + max(float(lse[m, i]), float(self.raw[m, i, 0]))
                 self.norm[m, i + 1] = acc
 
     # the per-entry child count: leading candidates of the row reaching tau
@@ -320,6 +323,8 @@ class TreeModel:
         self.node_S = CheckedArray("node_S", c.node_cap, 0.0)
         self.node_mu = CheckedArray("node_mu", c.node_cap)
         self.nk = CheckedArray("nk (LDS)", c.node_cap) if c.nk_lds else None
+        self.window_hits = 0
+        self.window_misses = 0
         self.ent_node = CheckedArray("ent_node", c.ent_cap)
         self.ent_mode = CheckedArray("ent_mode", c.ent_cap)
         self.ent_raw = CheckedArray("ent_raw", c.ent_cap, 0.0)
@@ -530,6 +535,7 @@ class TreeModel:
             res.levels.append(rec)
 
         res.node_count, res.ent_count = node_count, ent_count
+        res.window_hits, res.window_misses = self.window_hits, self.window_misses
         res.node_S = [self.node_S[i] for i in range(1, node_count)]
         total = node_count - 1
         if not res.fail and B > 0 and total > 0:
@@ -565,6 +571,24 @@ class TreeModel:
         if self.nk is not None:
             kt = key16(tau)
             alive = [self.nk[i] for i in range(1, node_count) if self.nk[i] >= kt]
+            # the one-pass window: bins of key - kt, 255 and above in the top one
+            hist = CheckedArray("raise window (LDS)", 256)
+            for i in range(256):
+                hist[i] = 0
+            for kk in alive:
+                hist[min(kk - kt, 255)] = hist[min(kk - kt, 255)] + 1
+            assert sum(hist[i] for i in range(256)) == len(alive)
+            if len(alive) >= B and B > 0:
+                cum, dg = 0, -1
+                for b in range(255, -1, -1):
+                    cum += hist[b]
+                    if cum >= B:
+                        dg = b
+                        break
+                self.window_hits += int(dg < 255)
+                self.window_misses += int(dg == 255)
+                if dg < 255:
+                    assert kt + dg == sorted(alive, reverse=True)[B - 1]
         else:
             alive = [key16(self.node_S[i]) for i in range(1, node_count) if self.node_S[i] >= tau]
         if len(alive) >= B and B > 0:

@@ -25,6 +25,22 @@ LSE_TOL = 1e-5        # row log-normalisers: absolute tolerance
 BAND = 1e-4           # cut-off band inside which cross-mode order is not decided exactly
 
 
+def peaked_logits(seed: int, K: int, L: int, V: int, gap: float) -> np.ndarray:
+    """Logits [K, L, V] (fp32 values) in which token 5 leads every row by about
+    `gap`: the chain of token 5 scores far above every other prefix, so with a
+    small B the B best nodes lie many binades above the running threshold."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((K, L, V)).astype(np.float32)
+    x[:, :, 5] += np.float32(gap)
+    return x
+
+
+# seed, K, L, V, B, gap: peaked trees whose threshold raise finds the B-th
+# best node more than 255 16-bit score keys above the running threshold
+PEAKED = [(31, 2, 10, 64, 3, 20.0), (32, 3, 8, 200, 4, 20.0), (33, 1, 12, 100, 5, 20.0),
+          (35, 2, 10, 64, 3, 30.0)]
+
+
 def oracle_rows(x64: np.ndarray, k: int):
     """Oracle lse [..] and ranked ids [.., k] for rows of x64 [..., V]."""
     lse = O.lse_rows(x64)

@@ -14,6 +14,7 @@ import pytest
 import torch
 
 import oracle as O
+from parity_checks import PEAKED, peaked_logits
 from mixture_draft_tree_amd import synth
 from mixture_draft_tree_amd import mfdtree as M
 from mixture_draft_tree_amd.pipeline import MixtureTreePath
@@ -237,6 +238,26 @@ def test_tree_shared_modes(case):
     assert P.buf.status.item() == 0
     r = compare_tree(x[0].double().numpy(), B, 3, tree_rows(P, 0))
     say(f"[tree shared modes] seed={seed} exact={r['exact']} n_nodes={tree_rows(P, 0)['n_nodes']}")
+
+
+@pytest.mark.parametrize("case", PEAKED, ids=[f"p{c[0]}" for c in PEAKED])
+def test_tree_peaked_rows(case):
+    """One token leads every row by a wide gap: the B best prefixes score many
+    binades above the running threshold, so the threshold's raise takes its
+    radix passes rather than the one-pass window."""
+    seed, K, L, V, B, gap = case
+    say(f"[tree peaked] seed={seed} K={K} L={L} V={V} B={B} gap={gap}")
+    x = torch.from_numpy(peaked_logits(seed, K, L, V, gap))[None]
+    P = MixtureTreePath(1, K, L, V, B, with_logp=True)
+    anchor = torch.tensor([2], dtype=torch.int32, device="cuda")
+    pos = torch.tensor([0], dtype=torch.int64, device="cuda")
+    P.build(x.cuda(), anchor, pos)
+    torch.cuda.synchronize()
+    assert P.buf.status.item() == 0
+    # the normaliser of a row never falls below its top logit
+    assert bool((P.buf.lse.cpu() >= P.buf.topk_raw[..., 0].double().cpu()).all())
+    r = compare_tree(x[0].double().numpy(), B, 2, tree_rows(P, 0))
+    say(f"[tree peaked] seed={seed} exact={r['exact']} n_nodes={tree_rows(P, 0)['n_nodes']}")
 
 
 def test_modes_small_batch():

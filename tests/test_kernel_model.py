@@ -15,7 +15,7 @@ import oracle as O
 from mixture_draft_tree_amd import synth
 
 import kernel_model as KM
-from parity_checks import run_pool
+from parity_checks import PEAKED, peaked_logits, run_pool
 
 
 @pytest.mark.parametrize("nt", [1024, 256])
@@ -94,7 +94,7 @@ def _tree_job(job):
     res = KM.TreeModel(ids, raw, lse, w.B).run()
     return {
         "fail": res.fail, "n_select": res.n_select, "nodes": res.node_count, "entries": res.ent_count,
-        "pooled_P": res.pooled_P,
+        "pooled_P": res.pooled_P, "window": (res.window_hits, res.window_misses),
         "levels": [(r.d, r.path, r.fsize, r.C, r.P, r.sort, r.bisected, r.raised) for r in res.levels],
     }
 
@@ -114,7 +114,9 @@ def _summary(results):
             "raises": raised, "sorts": dict(sorted(Ps.items())),
             "max_nodes": int(max(r["nodes"] for r in results)),
             "max_entries": int(max(r["entries"] for r in results)),
-            "max_C": int(max((lv[3] for r in results for lv in r["levels"]), default=0))}
+            "max_C": int(max((lv[3] for r in results for lv in r["levels"]), default=0)),
+            "window_hits": sum(r["window"][0] for r in results),
+            "window_misses": sum(r["window"][1] for r in results)}
 
 
 def _oracle_job(job):
@@ -169,7 +171,7 @@ def _sweep_job(job):
     ids, raw, lse = KM.row_lists(x, min(B, V))
     res = KM.TreeModel(ids, raw, lse, B).run()
     return {"fail": res.fail, "n_select": res.n_select, "nodes": res.node_count, "entries": res.ent_count,
-            "pooled_P": res.pooled_P,
+            "pooled_P": res.pooled_P, "window": (res.window_hits, res.window_misses),
             "levels": [(r.d, r.path, r.fsize, r.C, r.P, r.sort, r.bisected, r.raised) for r in res.levels]}
 
 
@@ -181,3 +183,15 @@ def test_sweep_level_sizes_stay_in_bounds():
     print(f"[kernel model] sweep: {s}")
     assert not any(r["fail"] for r in results)
     assert any(k.startswith("regs") for k in s["sorts"])
+
+
+@pytest.mark.parametrize("case", PEAKED, ids=[f"p{c[0]}" for c in PEAKED])
+def test_peaked_trees_reach_the_wide_raise(case):
+    """On the peaked cases some raise finds its B-th best key beyond the
+    one-pass window (key - tau's key >= 255) and takes the radix passes; the
+    model's cut-off is still the oracle's."""
+    seed, K, L, V, B, gap = case
+    x = peaked_logits(seed, K, L, V, gap).astype(np.float64)
+    res, sel = _model_vs_oracle(x, B)
+    assert not res.fail and res.window_misses > 0
+    assert res.n_select == sel.n_select and abs(res.cutoff - sel.cutoff) <= 1e-12
