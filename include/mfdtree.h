@@ -115,10 +115,10 @@ const char* mfd_version(void);
 
 /* Bytes of device workspace the call `op` needs for these shapes (0 if none).
  * Arguments a call does not use are ignored.  Returns MFD_ERR_INVALID_ARG for
- * shapes outside the limits.  MFD_OP_VERIFY_WALK uses N, V (the target's
- * vocabulary) and B (trees of B + 1 rows): the size includes the arrays of
- * the walk's speculative pass (see mfd_verify_walk); with B < 0 or V < 1 it
- * is the smaller size without them. */
+ * shapes outside the limits.  MFD_OP_VERIFY_WALK uses N, L (outside [1, 32]:
+ * sized for L = 32), V (the target's vocabulary) and B (trees of B + 1 rows):
+ * the size includes the arrays of the walk's speculative pass (see
+ * mfd_verify_walk); with B < 0 or V < 1 it is the smaller size without them. */
 mfd_status mfd_workspace_size(mfd_op op, int N, int K, int L, int V, int B, size_t* bytes);
 
 /*
@@ -411,16 +411,19 @@ mfd_status mfd_tree_mask(const int32_t* parent, const int32_t* depth, const int3
  *             if the call gave up waiting for work to finish (a bounded wait,
  *             seconds long, that never runs out in a correct run; tau is then 0).
  *   ws        device workspace, 8-byte aligned, of at least
- *             mfd_workspace_size(MFD_OP_VERIFY_WALK, N, .., V, B) bytes with
- *             B < 0 (per-tree control blocks, per-round counters and slice
- *             results; set up by the call itself, so it needs no clearing).
- *             With the size for the trees' B and the target's V it also
- *             holds the speculative pass's arrays.
- * Each visited row is cut into slices; workgroups claim the slices of open
- * rows from counters, so the device's workgroups share the open rows of the
- * trees and none waits for a particular other one (an ordinary launch: any
- * number of processes may walk on one GPU).  Calls on one stream are
- * ordered; calls that overlap must not share `ws`.
+ *             mfd_workspace_size(MFD_OP_VERIFY_WALK, N, .., L, V, B) bytes
+ *             with B < 0 (per tree: its first round, and a result slot and
+ *             flag per round and slice; set up by the call itself, so it
+ *             needs no clearing).  With the size for the trees' B and the
+ *             target's V it also holds the speculative pass's arrays.
+ * Each visited row is cut into slices, one per workgroup of the tree's
+ * group; each slice's result goes to a slot of its own round, and every
+ * workgroup of the group merges the round from the slots itself.  A
+ * workgroup that sees no progress for a while computes a missing slice
+ * (results are the same whoever computes them), so none depends on another
+ * being resident (an ordinary launch: any number of processes may walk on
+ * one GPU).  Calls on one stream are ordered; calls that overlap must not
+ * share `ws`.
  * Speculative pass: the token chosen at a node depends only on that node's
  * row, T, the seed and its depth.  When the workspace holds the pass's arrays
  * and the rows are few enough (every node's row up to 160 MiB per launch,
@@ -440,16 +443,18 @@ mfd_status mfd_verify_walk(const void* target_logits, mfd_dtype dtype, int N, in
  * allocate device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc.  The call itself allocates nothing (no
  * hipMalloc, hipFree or allocating library routine).  The walk's workspace
- * is a built-in 2 MiB device array of the library, one copy per GPU, held
+ * is a built-in 16 MiB device array of the library, one copy per GPU, held
  * until the process ends; its address on a device is looked up on the first
  * call made with that device current.  Same arguments, outputs and errors as
  * mfd_verify_walk, plus:
- *   - N is at most 1152 (the trees whose workspace fits 2 MiB); a larger N
- *     returns MFD_ERR_WORKSPACE before any launch.
+ *   - N is at most the number of trees whose walk workspace
+ *     (mfd_workspace_size(MFD_OP_VERIFY_WALK, N, 0, L, 0, -1)) fits 16 MiB:
+ *     511 at L = 15, 248 at L = 32; a larger N returns MFD_ERR_WORKSPACE
+ *     before any launch.
  *   - The call clears what must start at zero itself; the array keeps the
  *     last call's contents otherwise.
  *   - The speculative pass of mfd_verify_walk runs when its arrays fit in
- *     what the walk proper leaves of the 2 MiB (same outputs either way).
+ *     what the walk proper leaves of the 16 MiB (same outputs either way).
  *   - Every call on one GPU uses that GPU's one array: calls that overlap on
  *     a GPU (different streams, or other threads, without ordering between
  *     them) race and give wrong results.  Calls on one stream are ordered.

@@ -74,7 +74,10 @@ mfd_status mfd_workspace_size(mfd_op op, int N, int K, int L, int V, int B, size
       return ok();
     case MFD_OP_VERIFY_WALK:
       if (N < 0) return fail(MFD_ERR_INVALID_ARG, "N must be >= 0 (got %d)", N);
-      *bytes = N == 0 ? 0 : mfd::walk_ws_bytes_full(N, B < 0 || B > kMaxB ? 0 : B + 1, V < 1 || V > kMaxV ? 0 : V);
+      // L outside [1, kMaxL] sizes for the longest walk
+      *bytes = N == 0 ? 0
+                      : mfd::walk_ws_bytes_full(N, L < 1 || L > kMaxL ? kMaxL : L, B < 0 || B > kMaxB ? 0 : B + 1,
+                                                V < 1 || V > kMaxV ? 0 : V);
       return ok();
     case MFD_OP_COVERED_MASS:
       if (N < 0) return fail(MFD_ERR_INVALID_ARG, "N must be >= 0 (got %d)", N);
@@ -425,7 +428,7 @@ mfd_status mfd_verify_walk(const void* target_logits, mfd_dtype dtype, int N, in
   mfd_status s = verify_walk_checks(target_logits, dtype, N, Bp1, V, L, node_token, parent, depth, n_nodes,
                                     temperature, seed, tau, out_tokens, path_nodes);
   if (s != MFD_OK || N == 0) return s == MFD_OK ? ok() : s;
-  const size_t need = mfd::walk_ws_bytes(N);
+  const size_t need = mfd::walk_ws_bytes(N, L);
   if (ws == nullptr || ws_bytes < need)
     return fail(MFD_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws == nullptr ? (size_t)0 : ws_bytes);
   if (reinterpret_cast<uintptr_t>(ws) % 8) return fail(MFD_ERR_INVALID_ARG, "workspace must be 8-byte aligned");
@@ -435,11 +438,11 @@ mfd_status mfd_verify_walk(const void* target_logits, mfd_dtype dtype, int N, in
                   "mfd_verify_walk launch");
 }
 
-static int walk_noalloc_max_trees() {
+static int walk_noalloc_max_trees(int L) {
   int lo = 0, hi = 1 << 20;  // the largest N whose workspace fits the built-in scratch
   while (lo < hi) {
     const int mid = lo + (hi - lo + 1) / 2;
-    if (mfd::walk_ws_bytes(mid) <= mfd::walk_scratch_bytes()) lo = mid;
+    if (mfd::walk_ws_bytes(mid, L) <= mfd::walk_scratch_bytes()) lo = mid;
     else hi = mid - 1;
   }
   return lo;
@@ -453,10 +456,10 @@ mfd_status mfd_verify_walk_noalloc(const void* target_logits, mfd_dtype dtype, i
   mfd_status s = verify_walk_checks(target_logits, dtype, N, Bp1, V, L, node_token, parent, depth, n_nodes,
                                     temperature, seed, tau, out_tokens, path_nodes);
   if (s != MFD_OK || N == 0) return s == MFD_OK ? ok() : s;
-  const size_t need = mfd::walk_ws_bytes(N);
+  const size_t need = mfd::walk_ws_bytes(N, L);
   if (need > mfd::walk_scratch_bytes())
     return fail(MFD_ERR_WORKSPACE, "N = %d trees need %zu bytes of walk workspace; the built-in one holds %zu (N <= %d)",
-                N, need, mfd::walk_scratch_bytes(), walk_noalloc_max_trees());
+                N, need, mfd::walk_scratch_bytes(), walk_noalloc_max_trees(L));
   void* ws = nullptr;
   mfd_status r = from_hip(mfd::walk_scratch(&ws), "mfd_verify_walk_noalloc scratch lookup");
   if (r != MFD_OK) return r;

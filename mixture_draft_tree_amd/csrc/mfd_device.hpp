@@ -507,26 +507,28 @@ __device__ __forceinline__ uint64_t block_kth_largest(int n, int rank, Get get, 
   return prefix;
 }
 
-// ---------------------------------------------------------------- Philox4x64-10
+// ---------------------------------------------------------------- Philox4x32-10
 // Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3",
-// SC'11: two 64x64->128 multiplies per round, key bumped by Weyl constants.
+// SC'11: per round, two 32x32->64 products of counter words 0 and 2 with the
+// round constants; the key is bumped by Weyl constants between rounds.  Each
+// product is one v_mad_u64_u32; with a wave-uniform key the key schedule
+// stays on the scalar unit.
 struct Philox4 {
-  uint64_t v[4];
+  uint32_t v[4];
 };
 
-__device__ __forceinline__ Philox4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3, uint64_t k0,
-                                                 uint64_t k1) {
-  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
-  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                                 uint32_t k1) {
+  constexpr uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+  constexpr uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint64_t lo0 = M0 * c0, hi0 = __umul64hi(M0, c0);
-    const uint64_t lo1 = M1 * c2, hi1 = __umul64hi(M1, c2);
-    const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    const uint64_t p0 = (uint64_t)M0 * c0, p1 = (uint64_t)M1 * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
     c0 = n0;
-    c1 = lo1;
     c2 = n2;
-    c3 = lo0;
     k0 += W0;
     k1 += W1;
   }
@@ -538,9 +540,9 @@ __device__ __forceinline__ Philox4 philox4x64_10(uint64_t c0, uint64_t c1, uint6
   return out;
 }
 
-// Standard Gumbel noise from one 64-bit word: U = ((w >> 12) + 1/2) 2^-52.
-__device__ __forceinline__ double gumbel_from_word(uint64_t w) {
-  const double u = ((double)(w >> 12) + 0.5) * 0x1.0p-52;
+// Standard Gumbel noise from one 32-bit word: U = (w + 1/2) 2^-32, in fp64.
+__device__ __forceinline__ double gumbel_from_word(uint32_t w) {
+  const double u = ((double)w + 0.5) * 0x1.0p-32;
   return -log(-log(u));
 }
 

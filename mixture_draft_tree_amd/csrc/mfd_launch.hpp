@@ -50,10 +50,10 @@ hipError_t launch_tree_mask(const int32_t* parent, const int32_t* depth, const i
                             const int64_t* pos_base, int N, int Bp1, uint64_t* mask_words, int64_t* position_ids,
                             uint8_t* dense_mask, hipStream_t stream);
 
-size_t walk_ws_bytes(int N);
+size_t walk_ws_bytes(int N, int L);
 // With the speculative pass (N trees of Bp1 nodes over rows of V elements):
 // the workspace size mfd_workspace_size reports.
-size_t walk_ws_bytes_full(int N, int Bp1, long long V);
+size_t walk_ws_bytes_full(int N, int L, int Bp1, long long V);
 // The walk's built-in workspace (mfd_verify_walk_noalloc): its size, and its
 // device address on the current device (looked up once per device).
 size_t walk_scratch_bytes();

@@ -7,32 +7,26 @@
 // page, Figure 2: six drafted tokens plus the bonus).  At T = 0 the token is
 // the argmax; at T > 0 it is a Gumbel-max sample, which draws exactly from
 // softmax(R / T), so decoding stays lossless (model card summary).  The noise
-// is counter-based (Philox4x64-10) and keyed by (seed, depth, token), so a
-// given seed samples the same tokens whatever the tree's shape.
+// is counter-based (Philox4x32-10, one 32-bit word per token) and keyed by
+// (seed, depth, token), so a given seed samples the same tokens whatever the
+// tree's shape.
 //
 // Work layout: the token chosen at a node depends only on that node's row,
 // T, the seed and its depth, so the only order the walk imposes is one row
 // after the other within a tree.  Every row is cut into S slices, and a round
-// is one row (or its exact re-evaluation, below) of one tree.  The launch's
-// workgroups form groups of about S; group q serves trees q, q + groups, ...
-// and any of its workgroups claims any slice of its trees' open rounds from a
-// per-round counter, so no workgroup waits for a particular other one and the
-// kernel is an ordinary launch.  After its slice a workgroup publishes a
-// top-two and counts itself in; the one that completes the round merges the S
-// results, finds the child and opens the tree's next round with one packed
-// word, or ends the tree.  Polls for open rounds are bounded; a workgroup
-// leaves once all its group's trees have ended.  Only the rows on the walked
-// path are read (or, with the speculative pass below, every row of a small
-// batch at once).
+// is one row (or its exact re-evaluation, below) of one tree; the hand-off
+// between the workgroups of a tree is described at verify_walk_kernel.  Only
+// the rows on the walked path are read (or, with the speculative pass below,
+// every row of a small batch at once).
 //
-// At T > 0 the noise is first estimated in fp32 (two v_log_f32, error below
-// kGumbelTol, see gumbel_estimate) and y = x / T + g is formed in fp64 from
-// it, so every estimate lies within kGumbelTol (plus a few ulp of |y|) of the
-// exact y.  Each round keeps the best estimate and the second best value.
-// When they are further apart than twice that the best one is the exact
-// winner; otherwise a second round evaluates the exact fp64 noise for every
-// element whose estimate comes that close to the best, and takes the exact
-// maximum.
+// At T > 0 the first pass over a row works in fp32: the noise estimate
+// (two v_log_f32, error below 2e-5, see gumbel_estimate) and
+// est = fma(x, fp32(1 / T), g), which lies within est_err(y) of the exact
+// y = x / T + g (fp64).  Each round keeps the best estimate and the second
+// best value.  When they are further apart than est_slack the best one is the
+// exact winner; otherwise a second round evaluates the exact fp64 noise for
+// every element whose estimate comes that close to the best, and takes the
+// exact maximum.
 #include <math.h>
 
 #include <mutex>
@@ -47,7 +41,7 @@ namespace mfd {
 // uses this name as an address: it is a host-side stand-in, and a kernel
 // handed it would fault.  The device address comes from hipGetSymbolAddress,
 // once per device, below.
-constexpr size_t kWalkScratchBytes = size_t(2) << 20;
+constexpr size_t kWalkScratchBytes = size_t(16) << 20;
 static __device__ __align__(256) unsigned char scratch[kWalkScratchBytes];
 
 namespace {
@@ -82,10 +76,17 @@ namespace {
 
 constexpr int kWalkThreads = 256;
 constexpr int kWalkWaves = kWalkThreads / kWave;
-constexpr int kSlices = 64;                  // slices per row, at most
-constexpr int kMaxRounds = 2 * (32 + 1);     // two rounds per depth, L <= 32
-constexpr long long kIdleLimit = 1LL << 22;  // polls without work before giving up (seconds; never in practice)
-constexpr int kPollSleep = 2;                // s_sleep units (64 clocks each) between polls
+constexpr int kSlices = 64;                  // slices per row, at most (one lane each in the merge)
+constexpr int kTreesPerGroup = 2;            // trees one group of workgroups serves at most
+constexpr int kNodeLds = 512;                // nodes of a tree whose links a workgroup keeps in LDS
+constexpr int kWalkVec = 2;                  // 16-byte vectors per thread in flight in the walk's slices (T > 0)
+constexpr int kWalkVec0 = 8;                 // the same at T = 0 (a slice is then one round of loads)
+// Waits, in s_memrealtime ticks (100 MHz): a workgroup that has seen no
+// progress for kHelpTicks computes a missing slice itself; one that has seen
+// none for kGiveUpTicks flags its trees and leaves (never in practice).
+constexpr uint64_t kHelpTicks = 5000;            // 50 us
+constexpr uint64_t kGiveUpTicks = 200000000ull;  // 2 s
+constexpr int kPollSleep = 1;                    // s_sleep units (64 clocks each) between polls, doubled up to 8x
 constexpr double kGumbelTol = 1e-4;
 constexpr float kLn2f = 0.693147180559945309f;
 constexpr int kSliceVec = 2;                 // 16-byte vectors per thread per round of loads
@@ -93,7 +94,7 @@ constexpr int kMaxB1 = 16384;                // rows per tree, at most (B <= 163
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ uint64_t lane_word(const Philox4& r, int l) {
+__device__ __forceinline__ uint32_t lane_word(const Philox4& r, int l) {
   return l == 0 ? r.v[0] : (l == 1 ? r.v[1] : (l == 2 ? r.v[2] : r.v[3]));
 }
 
@@ -102,25 +103,63 @@ __device__ __forceinline__ bool better(double y, int i, double by, int bi) {
   return (y > by) || (y == by && i < bi);
 }
 
-// fp32 estimate of the noise g = -ln(-ln U), U = ((w >> 12) + 0.5) 2^-52.
+// fp32 estimate of the noise g = -ln(-ln U), U = (w + 0.5) 2^-32.
 // With t = -ln U:
-//  * 1 - U < 2^-8 (m = 2^52 - (w >> 12) < 2^44): u = 1 - U = (m - 0.5) 2^-52
-//    is formed with relative error <= 2^-23 and t ~ u (1 + u / 2), whose
+//  * 1 - U < 2^-8 (m = 2^32 - w <= 2^24): u = 1 - U = (m - 0.5) 2^-32 is
+//    formed with relative error <= 2^-24, and t ~ u (1 + u / 2), whose
 //    truncation error is below u^2 / 3 <= 2^-16 / 3 relative;
-//  * otherwise U is formed with relative error <= 2^-23, which moves ln U by
-//    at most 2^-23, i.e. by at most 2^-23 / |ln U| <= 2^-15 relative to t
-//    (|ln U| >= 2^-8 here); v_log_f32 adds a few ulp of |log2 U| <= 53.
+//  * otherwise U is formed with relative error <= 2^-24, which moves ln U by
+//    at most 2^-24, i.e. by at most 2^-24 / |ln U| <= 2^-16 relative to t
+//    (|ln U| >= 2^-8 here); v_log_f32 adds about an ulp of its result.
 // A relative error e of t moves g by about e, and the final v_log_f32 and
-// scaling add at most ~1e-5, so |estimate - g| < 5e-5 < kGumbelTol.
-__device__ __forceinline__ float gumbel_estimate(uint64_t w) {
-  const uint64_t hi = w >> 12;
-  const uint64_t m = (1ull << 52) - hi;  // in [1, 2^52]
-  const float u = ((float)m - 0.5f) * 0x1.0p-52f;
-  const float U = ((float)hi + 0.5f) * 0x1.0p-52f;
+// scaling add about 1e-6, so |estimate - g| < 2e-5.
+__device__ __forceinline__ float gumbel_estimate(uint32_t w) {
+  const uint32_t m = 0u - w;  // 2^32 - w where it is used (w >= 0xFF000000)
+  const float u = ((float)m - 0.5f) * 0x1.0p-32f;
+  const float U = ((float)w + 0.5f) * 0x1.0p-32f;
   const float t_small = u * (1.f + 0.5f * u);
   const float t_big = -__builtin_amdgcn_logf(U) * kLn2f;
-  const float t = m < (1ull << 44) ? t_small : t_big;
+  const float t = w >= 0xFF000000u ? t_small : t_big;
   return -__builtin_amdgcn_logf(t) * kLn2f;
+}
+
+// est = fma(x, fp32(1 / T), estimate) against the exact y = x / T + g: the
+// noise estimate is off by < 2e-5, fp32(1 / T) by 2^-24 relative (an error of
+// |x / T| 2^-24 <= (|y| + 23) 2^-24, as |g| < 23 for 32-bit U), and the fma
+// rounds by 2^-24 |est|; so |est - y| <= 3e-5 + |y| 2^-22 =: est_err(y).
+// Two elements whose estimates are further apart than est_err of both are in
+// the same order exactly; est_slack bounds est_err(a) + est_err(b) for values
+// near the given ones, with room to spare.
+__device__ __forceinline__ double est_slack(double y1, double y2) {
+  return 2.0 * kGumbelTol + (fabs(y1) + fabs(y2) + 2.0) * 0x1.0p-20;
+}
+
+// A value the whole wave holds alike, moved to scalar registers (so that,
+// e.g., the Philox key schedule runs on the scalar unit).
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ uint64_t uni(uint64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ double uni(double x) { return __longlong_as_double((long long)uni((uint64_t)__double_as_longlong(x))); }
+
+// Best (value, index) and the second best value seen, per thread, in fp32
+// (the estimates and the T = 0 logits).
+struct Top2f {
+  float y1;
+  int i1;
+  float y2;
+};
+
+__device__ __forceinline__ void top2f_add(Top2f& t, float y, int i) {
+  if ((y > t.y1) || (y == t.y1 && i < t.i1)) {
+    t.y2 = t.y1;
+    t.y1 = y;
+    t.i1 = i;
+  } else if (y > t.y2) {
+    t.y2 = y;
+  }
 }
 
 // Best (value, index) and the second best value seen.
@@ -165,7 +204,7 @@ __host__ __device__ __forceinline__ uint32_t round_word(int r, int kind, int ste
 struct WalkArgs {
   const void* target;
   int N, Bp1, L, S, G;
-  int groups;  // walk kernel: groups of workgroups, each serving its own trees
+  int groups;  // walk kernel: groups of S workgroups, each serving its own trees
   long long V;
   const int32_t* node_token;
   const int32_t* parent;
@@ -178,12 +217,8 @@ struct WalkArgs {
   int32_t* path_nodes;
   int32_t* status;
   uint32_t* word;  // [N] round words
-  double* cut;     // [N] cut-off of an exact round
-  int32_t* claim;  // [N][kMaxRounds] slices claimed per round
-  int32_t* done;   // [N][kMaxRounds] slices finished per round
-  double* py1;     // [N][kSlices] slice results of the open round
-  double* py2;
-  int32_t* pi;
+  int R;           // rounds a tree may take: two per depth, 2 (L + 1)
+  uint64_t* slot;  // [N][R][S][2]: each slice's result of each round (slot_pack)
   // speculation (walk_prep_kernel / walk_spec_kernel); spec = 0: none
   int spec;
   int spec_rcap;         // rows the slice-result arrays hold
@@ -226,16 +261,54 @@ __device__ __forceinline__ void st(T* p, T v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-constexpr int kWalkMaxTrees = 2048;  // trees one launch of the walk kernel handles
+// A slice's result as two 64-bit words, each written and read as one atomic
+// access and each carrying a check pattern, so a reader that finds both
+// patterns has the whole result with no ordering between the two stores
+// (the prep pass zeroes the slots).  Word A: the high 32 bits of the value,
+// the best index (20 bits; 0xFFFFF for none) and a 12-bit pattern; word B:
+// the low 32 bits and a 32-bit pattern.  The value is the best fp32 estimate
+// or logit (high) with the second best one (low) after a first pass, and the
+// exact fp64 winner's value (high and low halves) after an exact pass.
+constexpr uint64_t kSlotTagA = 0x5A5u;
+constexpr uint64_t kSlotTagB = 0x5A5A5A5Au;
+constexpr int kNoIndex20 = 0xFFFFF;
+
+__device__ __forceinline__ void slot_pack(uint32_t hi, uint32_t lo, int i1, uint64_t& A, uint64_t& B) {
+  const uint32_t i20 = (i1 < 0 || i1 >= kNoIndex20) ? (uint32_t)kNoIndex20 : (uint32_t)i1;
+  A = ((uint64_t)hi << 32) | ((uint64_t)i20 << 12) | kSlotTagA;
+  B = ((uint64_t)lo << 32) | kSlotTagB;
+}
+
+__device__ __forceinline__ bool slot_ok(uint64_t A, uint64_t B) {
+  return (A & 0xFFFu) == kSlotTagA && (B & 0xFFFFFFFFu) == kSlotTagB;
+}
+
+// A tree's walk as one workgroup of its group sees it: every workgroup of
+// the group merges every round itself, so all of them step through the same
+// states.
+struct WalkState {
+  int r;           // current round
+  int kind;        // 1: the exact re-evaluation of the previous round's row
+  int step;        // moves from the root so far (the output position)
+  int u;           // current node
+  int ended;
+  int mine;        // this workgroup's own slice of round r is done
+  int d;           // depth of u (keys the noise)
+  int nn;          // nodes of the tree
+  uint64_t miss;   // slices of round r without a result at the last poll
+  double cut;      // exact round: estimates below this cannot win
+  double T;        // the tree's temperature
+  uint64_t sd;     // and seed
+};
 
 struct WalkShared {
   Top2 w[kWalkWaves];
-  Top2 g;  // merged result of a round
-  int child;
-  int n, slice, quit, last;
-  uint32_t word;
-  double cut;
-  unsigned char full[kWalkMaxTrees];  // per tree: the last round (r + 1) found with every slice claimed
+  WalkState ts[kTreesPerGroup];
+  int complete[kTreesPerGroup];
+  int action, help_j, help_s;
+  int32_t npar[kTreesPerGroup][kNodeLds];
+  int32_t ntok[kTreesPerGroup][kNodeLds];
+  int32_t ndep[kTreesPerGroup][kNodeLds];
 };
 
 // Element value as float (bf16 or fp32 storage).
@@ -304,10 +377,10 @@ __device__ __forceinline__ void slice_range(const void* row, long long V, int S,
 struct NoiseCache {
   long long blk = -1;
   Philox4 r;
-  __device__ __forceinline__ uint64_t word(long long i, uint64_t seed, int d) {
+  __device__ __forceinline__ uint32_t word(long long i, uint64_t seed, int d) {
     const long long bk = i >> 2;
     if (bk != blk) {
-      r = philox4x64_10((uint64_t)bk, (uint64_t)d, 0, 0, seed, 0);
+      r = philox4x32_10((uint32_t)bk, (uint32_t)d, 0, 0, (uint32_t)seed, (uint32_t)(seed >> 32));
       blk = bk;
     }
     return lane_word(r, (int)(i & 3));
@@ -315,14 +388,14 @@ struct NoiseCache {
 };
 
 // Block-wide Top2 of the per-thread values (barriers inside); every thread gets it.
-__device__ __forceinline__ Top2 block_top2(Top2 t, WalkShared& sh) {
+__device__ __forceinline__ Top2 block_top2(Top2 t, Top2* wsh) {
 #pragma unroll
   for (int o = kWave / 2; o > 0; o >>= 1) top2_merge(t, top2_shfl_xor(t, o));
-  if (lane_id() == 0) sh.w[wave_id()] = t;
+  if (lane_id() == 0) wsh[wave_id()] = t;
   __syncthreads();
-  Top2 r = sh.w[0];
-  for (int w = 1; w < kWalkWaves; ++w) top2_merge(r, sh.w[w]);
-  __syncthreads();  // sh.w may be reused
+  Top2 r = wsh[0];
+  for (int w = 1; w < kWalkWaves; ++w) top2_merge(r, wsh[w]);
+  __syncthreads();  // wsh may be reused
   return r;
 }
 
@@ -336,10 +409,7 @@ __global__ void __launch_bounds__(kWalkThreads) walk_prep_kernel(WalkArgs a) {
   __shared__ int scan[kWalkWaves];
   const int n = blockIdx.x, tid = threadIdx.x;
   const int Lp1 = a.L + 1, Bp1 = a.Bp1;
-  for (int i = tid; i < kMaxRounds; i += kWalkThreads) {
-    a.claim[(size_t)n * kMaxRounds + i] = 0;
-    a.done[(size_t)n * kMaxRounds + i] = 0;
-  }
+  for (int i = tid; i < 2 * a.R * a.S; i += kWalkThreads) a.slot[(size_t)n * 2 * a.R * a.S + i] = 0;
   const float T = a.temperature[n];
   const bool bad = !(T >= 0.f) || isinf(T);
   if (bad) {
@@ -349,7 +419,6 @@ __global__ void __launch_bounds__(kWalkThreads) walk_prep_kernel(WalkArgs a) {
     }
   }
   if (tid == 0) {
-    a.cut[n] = 0.0;
     if (bad) {
       a.tau[n] = 0;
       if (a.status) atomicOr(&a.status[n], MFD_TREE_BAD_TEMPERATURE);
@@ -421,12 +490,12 @@ __global__ void __launch_bounds__(kWalkThreads) walk_prep_kernel(WalkArgs a) {
 //
 // Each slice of a row gives its exact winner in one pass.  At T = 0 that is
 // the largest logit (lowest id among equals).  At T > 0 every element gets the
-// fp32 noise estimate, whose error e(v) = |est(v) - y(v)| is below kGumbelTol
-// plus a few ulp of |y|.  Let w be the slice's exact winner and b the element
-// of the best estimate g:  est(w) >= y(w) - e(w) >= y(b) - e(w) >= g - e(b) -
-// e(w).  So w is among the elements whose estimate is within the slack
-// 2 kGumbelTol + (|g| + 1) 2^-45 of g, and evaluating just those exactly in
-// fp64 finds it; the row's winner is the best of its slices' winners.
+// fp32 estimate est(v), within e(v) = est_err(y(v)) of the exact y(v).  Let w
+// be the slice's exact winner and b the element of the best estimate g:
+// est(w) >= y(w) - e(w) >= y(b) - e(w) >= g - e(b) - e(w).  So w is among the
+// elements whose estimate is within est_slack(g, g) of g, and evaluating just
+// those exactly in fp64 finds it; the row's winner is the best of its slices'
+// winners.
 constexpr long long kSpecAllBytes = 160ll << 20;  // every node's row, up to this many bytes per launch
 constexpr long long kSpecIntBytes = 400ll << 20;  // else the rows of nodes with a child, up to this many
 constexpr int kFollowLds = 2048;                  // nodes of a tree the follow step copies to LDS
@@ -482,15 +551,15 @@ __device__ BestYI spec_slice(const void* row, long long e0, long long e1, double
     });
     return block_best(b, wsh);
   }
-  const double invT = 1.0 / T;
+  const float invTf = (float)(1.0 / T);
   // each thread: its two best estimates (value, id, logit) and the third best value
-  double e1v = -INFINITY, e2v = -INFINITY, e3v = -INFINITY;
+  float e1v = -INFINITY, e2v = -INFINITY, e3v = -INFINITY;
   int i1 = 0x7FFFFFFF, i2 = 0x7FFFFFFF;
   float x1 = 0.f, x2 = 0.f;
   NoiseCache nc;
   for_slice<BF16, kSpecVec>(row, e0, e1, [&](long long i, float x) {
-    const double est = (double)x * invT + (double)gumbel_estimate(nc.word(i, sd, d));
-    if (better(est, (int)i, e1v, i1)) {
+    const float est = fmaf(x, invTf, gumbel_estimate(nc.word(i, sd, d)));
+    if (est > e1v || (est == e1v && (int)i < i1)) {
       e3v = e2v;
       e2v = e1v;
       i2 = i1;
@@ -498,7 +567,7 @@ __device__ BestYI spec_slice(const void* row, long long e0, long long e1, double
       e1v = est;
       i1 = (int)i;
       x1 = x;
-    } else if (better(est, (int)i, e2v, i2)) {
+    } else if (est > e2v || (est == e2v && (int)i < i2)) {
       e3v = e2v;
       e2v = est;
       i2 = (int)i;
@@ -507,11 +576,11 @@ __device__ BestYI spec_slice(const void* row, long long e0, long long e1, double
       e3v = est;
     }
   });
-  BestYI g = block_best(BestYI{e1v, i1}, wsh);
-  const double lim = g.y - (2.0 * kGumbelTol + (fabs(g.y) + 1.0) * 0x1.0p-45);
+  BestYI g = block_best(BestYI{(double)e1v, i1}, wsh);
+  const double lim = g.y - est_slack(g.y, g.y);
   BestYI b = {-INFINITY, 0x7FFFFFFF};
   auto exact = [&](long long i, float x) {
-    const uint64_t w = nc.word(i, sd, d);
+    const uint32_t w = nc.word(i, sd, d);
     const double y = (double)x / T + gumbel_from_word(w);
     if (better(y, (int)i, b.y, b.i)) {
       b.y = y;
@@ -522,11 +591,11 @@ __device__ BestYI spec_slice(const void* row, long long e0, long long e1, double
     // three or more of this thread's elements are close to the slice's best
     // (rare): go over its elements again
     for_slice<BF16, kSpecVec>(row, e0, e1, [&](long long i, float x) {
-      if ((double)x * invT + (double)gumbel_estimate(nc.word(i, sd, d)) >= lim) exact(i, x);
+      if ((double)fmaf(x, invTf, gumbel_estimate(nc.word(i, sd, d))) >= lim) exact(i, x);
     });
   } else {
-    if (i1 != 0x7FFFFFFF && e1v >= lim) exact(i1, x1);
-    if (i2 != 0x7FFFFFFF && e2v >= lim) exact(i2, x2);
+    if (i1 != 0x7FFFFFFF && (double)e1v >= lim) exact(i1, x1);
+    if (i2 != 0x7FFFFFFF && (double)e2v >= lim) exact(i2, x2);
   }
   return block_best(b, wsh);
 }
@@ -724,210 +793,276 @@ __global__ void __launch_bounds__(kWalkThreads, 4) walk_spec_kernel(WalkArgs a) 
 __device__ __forceinline__ uint64_t rotr64(uint64_t m, int r) { return r ? ((m >> r) | (m << (64 - r))) : m; }
 
 // The walk proper.  A round is one row of one tree (or its exact
-// re-evaluation), cut into S slices.  Workgroups claim the slices of open
-// rounds from per-round counters, whichever tree they belong to, so no
-// workgroup waits for a particular other one: the kernel needs no
-// co-residency and is launched like any other.  A workgroup that finds no
-// unclaimed slice polls again after a short sleep; it leaves once every tree
-// has ended.  The workgroup finishing a round's last slice merges the S
-// results, finds the child in the tree and opens the tree's next round (or
-// ends the tree).
+// re-evaluation), cut into S slices.  The launch's workgroups form groups of
+// S; group q serves trees q, q + groups, ... (at most kTreesPerGroup).
+// Workgroup m of a group reduces slice m of each round of its trees and
+// stores the result in that round's own slot (two self-checking words, see
+// slot_pack).  Every workgroup of the group polls the round's S slots and,
+// once all hold a result, merges them itself in one fixed order, so each one
+// finds the same winner and the same child and goes on to the next round
+// with no further hand-off: per round, one store per slice and one poll per
+// reader, and no read-modify-write.
+//
+// No workgroup relies on another being resident.  A result depends only on
+// its tree, round and slice, and every round has slots of its own, so a slot
+// written twice holds the same bits either time: a workgroup that has seen
+// no progress for kHelpTicks computes a slice that is still missing, and one
+// that fell behind merges the rounds it missed from their slots.  A
+// workgroup leaves once its trees have ended (or, after kGiveUpTicks without
+// progress, flags them).
 template <bool BF16>
 __global__ void __launch_bounds__(kWalkThreads, 4) verify_walk_kernel(WalkArgs a) {
   __shared__ WalkShared sh;
   const int tid = threadIdx.x, lane = lane_id(), wid = wave_id();
-  const int N = a.N, S = a.S, L = a.L, Lp1 = L + 1, Bp1 = a.Bp1;
+  const int N = a.N, S = a.S, L = a.L, Lp1 = L + 1, Bp1 = a.Bp1, R = a.R;
   const long long V = a.V;
   const size_t esz = BF16 ? 2 : 4;
-  // The workgroups form a.groups groups; group q serves trees q, q + groups,
-  // q + 2 groups, ... (its own trees' rounds get its workgroups' attention),
-  // and within a group any workgroup takes any slice.
-  const int grp = (int)(blockIdx.x % a.groups);
-  const int mine_n = grp < N ? (N - 1 - grp) / a.groups + 1 : 0;  // trees of this group
-  const int nchunks = (mine_n + kWave - 1) / kWave;
-  for (int q = tid; q < mine_n; q += kWalkThreads) sh.full[q] = 0;
-  long long idle = 0;
-  int backoff = 1;
-  const int member = (int)(blockIdx.x / a.groups);
+  // consecutive workgroups serve one tree: the device deals workgroups to
+  // its XCDs in turn, so each tree's slices spread over all of them (and each
+  // XCD gets slices of every tree) rather than landing on one
+  const int grp = (int)(blockIdx.x / S);
+  const int member = (int)(blockIdx.x % S);                    // own slice
 
-  while (true) {
-    __syncthreads();  // everyone is done with the previous iteration's shared fields
-    // ------------------------------------------------ claim a slice of an open round (wave 0)
-    if (wid == 0) {
-      int got = -1, slice = 0, quit = 0, ended = 0;
-      uint32_t gw = 0u;
-      const int c0 = nchunks > 0 ? member % nchunks : 0, rot = member % kWave;
-      for (int k = 0; k < nchunks && got < 0; ++k) {
-        const int chunk = (c0 + k) % nchunks;
-        const int j = chunk * kWave + lane;  // the group's j-th tree
-        const int n = grp + j * a.groups;
-        const uint32_t w = j < mine_n ? ld(&a.word[n]) : kEnded;
-        ended += __popcll(__ballot(j < mine_n && w == kEnded));
-        const bool cand = j < mine_n && w != kEnded && w != 0u && (int)(w & 0x7Fu) > (int)sh.full[j < mine_n ? j : 0];
-        uint64_t m = __ballot(cand);
-        while (m != 0ull) {
-          const int l = (__builtin_ctzll(rotr64(m, rot)) + rot) & (kWave - 1);
-          int c = 0;
-          if (lane == l)
-            c = __hip_atomic_fetch_add(&a.claim[(size_t)n * kMaxRounds + (int)(w & 0x7Fu) - 1], 1, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-          c = __shfl(c, l, kWave);
-          const uint32_t wl = __shfl(w, l, kWave);
-          if (c < S) {
-            got = grp + (chunk * kWave + l) * a.groups;
-            slice = c;
-            gw = wl;
-            break;
-          }
-          if (lane == l) sh.full[j] = (unsigned char)(w & 0x7Fu);  // every slice of this round is taken
-          m &= ~(1ull << l);
-        }
-      }
-      if (got >= 0) {
-        backoff = 1;
-        idle = 0;
-      } else if (ended == mine_n) {
-        quit = 1;  // every tree of the group has ended (all its chunks were scanned)
-      } else if (++idle > kIdleLimit) {
-        quit = 2;
-      } else {
-        // back off while nothing is claimable (up to ~1 us between polls)
-        backoff = backoff < 16 ? backoff * 2 : 16;
-        for (int z = 0; z < backoff; ++z) __builtin_amdgcn_s_sleep(kPollSleep);
-      }
-      if (lane == 0) {
-        sh.quit = quit;
-        sh.n = got;
-        sh.slice = slice;
-        sh.word = gw;
-        sh.child = 0x7FFFFFFF;
-        if (got >= 0 && ((gw >> 7) & 1u)) {
-          drain();  // the word was read before the cut-off it announces
-          sh.cut = ld(&a.cut[got]);
-        }
-      }
-    }
-    __syncthreads();
-    const int quit = sh.quit, n = sh.n;
-    if (quit) {
-      if (quit == 2 && tid == 0) {
-        // gave up waiting: flag every tree of the group that has not ended
-        for (int q = grp; q < N; q += a.groups) {
-          if (ld(&a.word[q]) != kEnded) {
-            if (a.status) atomicOr(&a.status[q], MFD_TREE_CAPACITY);
-            a.tau[q] = 0;
-          }
-        }
-      }
-      break;
-    }
-    if (n < 0) continue;
-    const uint32_t word = sh.word;
-    const int r = (int)(word & 0x7Fu) - 1, kind = (int)((word >> 7) & 1u), step = (int)((word >> 8) & 0x3Fu),
-              u = (int)(word >> 14);
-    const double cut = sh.cut;
-    const int s = sh.slice;
+  const int nt = grp < N ? (N - 1 - grp) / a.groups + 1 : 0;  // trees of the group
 
-    // ------------------------------------------------ reduce the claimed slice
+  // each tree's first round (set by the prep or the speculative pass) and,
+  // when they fit, its links and depths
+  for (int j = 0; j < nt; ++j) {
+    const int n = grp + j * a.groups;
     const size_t tb = (size_t)n * Bp1;
-    const double T = (double)a.temperature[n];
-    const double invT = T > 0.0 ? 1.0 / T : 0.0;
-    const uint64_t sd = a.seed[n];
-    const int d = a.depth[tb + u];
-    const void* row = static_cast<const char*>(a.target) + ((tb + u) * (size_t)V) * esz;
-    long long e0, e1;
-    slice_range<BF16>(row, V, S, s, e0, e1);
-    Top2 t = {-INFINITY, 0x7FFFFFFF, -INFINITY};
-    NoiseCache nc;
-    if (T == 0.0) {
-      for_slice<BF16>(row, e0, e1, [&](long long i, float x) { top2_add(t, (double)x, (int)i); });
-    } else if (kind == 0) {
-      for_slice<BF16>(row, e0, e1, [&](long long i, float x) {
-        const float g = gumbel_estimate(nc.word(i, sd, d));
-        top2_add(t, (double)x * invT + (double)g, (int)i);
-      });
-    } else {
-      // exact fp64 noise for every element whose estimate comes within the
-      // slack of the best estimate
-      for_slice<BF16>(row, e0, e1, [&](long long i, float x) {
-        const uint64_t w = nc.word(i, sd, d);
-        if ((double)x * invT + (double)gumbel_estimate(w) >= cut)
-          top2_add(t, (double)x / T + gumbel_from_word(w), (int)i);
-      });
-    }
-    const Top2 mine = block_top2(t, sh);
-    double* py1 = a.py1 + (size_t)n * kSlices;
-    double* py2 = a.py2 + (size_t)n * kSlices;
-    int32_t* pi = a.pi + (size_t)n * kSlices;
-    int32_t* done = a.done + (size_t)n * kMaxRounds + r;
-    if (tid == 0) {
-      st(&py1[s], mine.y1);
-      st(&py2[s], mine.y2);
-      st(&pi[s], mine.i1);
-      drain();  // the result is in place before the slice counts as done
-      const int old = __hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      drain();  // the count is in before the merge below reads the other slices' results
-      sh.last = old == S - 1;
-    }
-    __syncthreads();
-    if (!sh.last) continue;
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-
-    // ------------------------------------------------ finish the round
-    if (wid == 0) {
-      // every slice stored its result before counting itself done, and the
-      // count has reached S: the S results are in place
-      Top2 g = {-INFINITY, 0x7FFFFFFF, -INFINITY};
-      for (int q = lane; q < S; q += kWave) {
-        Top2 o;
-        o.y1 = ld(&py1[q]);
-        o.y2 = ld(&py2[q]);
-        o.i1 = ld(&pi[q]);
-        top2_merge(g, o);
-      }
-#pragma unroll
-      for (int o = kWave / 2; o > 0; o >>= 1) top2_merge(g, top2_shfl_xor(g, o));
-      if (lane == 0) sh.g = g;
-    }
-    __syncthreads();
-    const Top2 g = sh.g;
-    // the estimates also carry the rounding of x / T (a few ulp of |y|)
-    const double slack = 2.0 * kGumbelTol + (fabs(g.y1) + fabs(g.y2)) * 0x1.0p-48;
-    if (T != 0.0 && kind == 0 && !(g.y1 - g.y2 > slack) && r + 1 < kMaxRounds) {
-      // too close to call from the estimates: the same row once more, exactly
-      if (tid == 0) {
-        st(&a.cut[n], g.y1 - slack);
-        drain();
-        st(&a.word[n], round_word(r + 1, 1, step, u));
-      }
-      continue;
-    }
-    const int tstar = g.i1 == 0x7FFFFFFF ? 0 : g.i1;
     int nn = a.n_nodes[n];
     nn = nn < 1 ? 1 : (nn > Bp1 ? Bp1 : nn);
-    for (int q = 1 + tid; q < nn; q += kWalkThreads)
-      if (a.parent[tb + q] == u && a.node_token[tb + q] == tstar) atomicMin(&sh.child, q);
-    __syncthreads();
-    const int child = sh.child;
-    int32_t* ot = a.out_tokens + (size_t)n * Lp1;
-    int32_t* pn = a.path_nodes + (size_t)n * Lp1;
-    if (child != 0x7FFFFFFF && step < L && r + 1 < kMaxRounds) {
-      if (tid == 0) {
-        ot[step] = tstar;
-        pn[step] = u;
-        st(&a.word[n], round_word(r + 1, 0, step + 1, child));
+    if (nn <= kNodeLds)
+      for (int q = tid; q < nn; q += kWalkThreads) {
+        sh.npar[j][q] = a.parent[tb + q];
+        sh.ntok[j][q] = a.node_token[tb + q];
+        sh.ndep[j][q] = a.depth[tb + q];
       }
+    if (tid == 0) {
+      const uint32_t w = a.word[n];
+      WalkState& t = sh.ts[j];
+      t.r = 0;
+      t.kind = 0;
+      t.ended = w == kEnded ? 1 : 0;
+      t.step = (int)((w >> 8) & 0x3Fu);
+      t.u = t.ended ? 0 : (int)(w >> 14);
+      t.d = a.depth[tb + t.u];
+      t.nn = nn;
+      t.mine = 0;
+      t.miss = 0;
+      t.cut = 0.0;
+      t.T = (double)a.temperature[n];
+      t.sd = a.seed[n];
+    }
+  }
+
+  // Reduce slice s of the current round of tree j (state t) and publish it.
+  // (The state's fields are read from LDS where they are used, into scalar
+  // registers, so that no copy of it stays live across the row's loop.)
+  auto do_slice = [&](int j, int s) {
+    const WalkState& t = sh.ts[j];
+    const int n = uni(grp + j * a.groups);
+    const size_t tb = (size_t)n * Bp1;
+    const double T = uni(t.T);
+    const uint64_t sd = uni(t.sd);
+    const int d = uni(t.d);
+    const int r = uni(t.r);
+    const void* row = static_cast<const char*>(a.target) + ((tb + uni(t.u)) * (size_t)V) * esz;
+    long long e0, e1;
+    slice_range<BF16>(row, V, S, uni(s), e0, e1);
+    Top2 acc = {-INFINITY, 0x7FFFFFFF, -INFINITY};
+    NoiseCache nc;
+    const bool exact_pass = T != 0.0 && uni(t.kind) != 0;
+    if (!exact_pass) {
+      // the logits (T = 0) or the fp32 estimates, per thread in fp32
+      Top2f f = {-INFINITY, 0x7FFFFFFF, -INFINITY};
+      if (T == 0.0) {
+        for_slice<BF16, kWalkVec0>(row, e0, e1, [&](long long i, float x) { top2f_add(f, x, (int)i); });
+      } else {
+        const float invTf = (float)(1.0 / T);
+        for_slice<BF16, kWalkVec>(row, e0, e1, [&](long long i, float x) {
+          top2f_add(f, fmaf(x, invTf, gumbel_estimate(nc.word(i, sd, d))), (int)i);
+        });
+      }
+      acc = {(double)f.y1, f.i1, (double)f.y2};
     } else {
-      for (int i = step + 1 + tid; i < Lp1; i += kWalkThreads) {
-        ot[i] = -1;
-        pn[i] = -1;
+      // exact fp64 noise for every element whose estimate comes within the
+      // slack of the previous round's best estimate
+      const float invTf = (float)(1.0 / T);
+      const double cut = uni(t.cut);
+      for_slice<BF16, kWalkVec>(row, e0, e1, [&](long long i, float x) {
+        const uint32_t w = nc.word(i, sd, d);
+        if ((double)fmaf(x, invTf, gumbel_estimate(w)) >= cut)
+          top2_add(acc, (double)x / T + gumbel_from_word(w), (int)i);
+      });
+    }
+    const Top2 m = block_top2(acc, sh.w);
+    if (tid == 0) {
+      const size_t slot = ((size_t)n * R + r) * S + uni(s);
+      uint64_t A, B;
+      if (exact_pass) {
+        const uint64_t y = (uint64_t)__double_as_longlong(m.y1);
+        slot_pack((uint32_t)(y >> 32), (uint32_t)y, m.i1, A, B);
+      } else {  // fp32 values, held exactly in the doubles
+        slot_pack(__float_as_uint((float)m.y1), __float_as_uint((float)m.y2), m.i1, A, B);
       }
-      if (tid == 0) {
-        ot[step] = tstar;
-        pn[step] = u;
-        a.tau[n] = d + 1;
-        st(&a.word[n], kEnded);
+      st(&a.slot[2 * slot], A);
+      st(&a.slot[2 * slot + 1], B);
+    }
+  };
+
+  uint64_t last_progress = 0;  // thread 0's clock decides; 0: read it at the next idle pass
+  int backoff = 1;
+  while (true) {
+    __syncthreads();  // the previous pass's shared fields have been read
+    bool progress = false;
+    int alive = 0;
+    for (int j = 0; j < nt; ++j) {
+      if (uni(sh.ts[j].ended)) continue;
+      ++alive;
+      const int n = grp + j * a.groups;
+      if (!uni(sh.ts[j].mine)) {
+        do_slice(j, member);
+        if (tid == 0) sh.ts[j].mine = 1;
+        progress = true;
       }
+      // poll the round's slots; once all hold a result, merge and step (wave 0)
+      if (wid == 0) {
+        WalkState& t = sh.ts[j];
+        const size_t base = ((size_t)n * R + uni(t.r)) * S;
+        uint64_t A = 0, B = 0;
+        if (lane < S) {
+          A = ld(&a.slot[2 * (base + lane)]);
+          B = ld(&a.slot[2 * (base + lane) + 1]);
+        }
+        const uint64_t have = __ballot(lane >= S || slot_ok(A, B));
+        const int complete = have == ~0ull;
+        if (complete) {
+          Top2 g = {-INFINITY, 0x7FFFFFFF, -INFINITY};
+          if (lane < S) {
+            const uint32_t hi = (uint32_t)(A >> 32), lo = (uint32_t)(B >> 32);
+            const int i20 = (int)((A >> 12) & 0xFFFFFu);
+            g.i1 = i20 == kNoIndex20 ? 0x7FFFFFFF : i20;
+            if (uni(t.T) != 0.0 && uni(t.kind) != 0) {
+              g.y1 = __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+            } else {
+              g.y1 = (double)__uint_as_float(hi);
+              g.y2 = (double)__uint_as_float(lo);
+            }
+          }
+#pragma unroll
+          for (int o = kWave / 2; o > 0; o >>= 1) top2_merge(g, top2_shfl_xor(g, o));
+          // every lane holds the merged result; lane 0 updates the state
+          const int r = uni(t.r), step = uni(t.step), u = uni(t.u);
+          const double slack = est_slack(g.y1, g.y2);
+          wave_sync();  // every lane has read the state before lane 0 rewrites it
+          if (uni(t.T) != 0.0 && uni(t.kind) == 0 && !(g.y1 - g.y2 > slack) && r + 1 < R) {
+            // too close to call from the estimates: the same row once more, exactly
+            if (lane == 0) {
+              t.r = r + 1;
+              t.kind = 1;
+              t.cut = g.y1 - slack;
+              t.mine = 0;
+              t.miss = 0;
+            }
+          } else {
+            const int tstar = g.i1 == 0x7FFFFFFF ? 0 : g.i1;
+            const size_t tb = (size_t)n * Bp1;
+            const int nn = uni(t.nn);
+            const bool cached = nn <= kNodeLds;
+            int child = 0x7FFFFFFF;
+            for (int q = 1 + lane; q < nn; q += kWave) {
+              const int p = cached ? sh.npar[j][q] : a.parent[tb + q];
+              const int tk = cached ? sh.ntok[j][q] : a.node_token[tb + q];
+              if (p == u && tk == tstar && q < child) child = q;
+            }
+#pragma unroll
+            for (int o = kWave / 2; o > 0; o >>= 1) child = min(child, __shfl_xor(child, o, kWave));
+            int32_t* ot = a.out_tokens + (size_t)n * Lp1;
+            int32_t* pn = a.path_nodes + (size_t)n * Lp1;
+            if (lane == 0) {
+              ot[step] = tstar;
+              pn[step] = u;
+            }
+            if (child != 0x7FFFFFFF && step < L && r + 1 < R) {
+              const int dc = cached ? sh.ndep[j][child] : a.depth[tb + child];
+              if (lane == 0) {
+                t.r = r + 1;
+                t.kind = 0;
+                t.step = step + 1;
+                t.u = child;
+                t.d = dc;
+                t.mine = 0;
+                t.miss = 0;
+              }
+            } else {
+              for (int i = step + 1 + lane; i < Lp1; i += kWave) {
+                ot[i] = -1;
+                pn[i] = -1;
+              }
+              const int dd = uni(t.d);
+              if (lane == 0) {
+                a.tau[n] = dd + 1;
+                t.ended = 1;
+              }
+            }
+          }
+        } else if (lane == 0) {
+          t.miss = ~have;
+        }
+        if (lane == 0) sh.complete[j] = complete;
+      }
+      __syncthreads();
+      if (sh.complete[j]) progress = true;
+    }
+    if (alive == 0) break;
+    // nothing moved: wait, help with a missing slice, or give up (thread 0
+    // decides for the workgroup)
+    if (tid == 0) {
+      int act = 0, hj = -1, hs = 0;
+      // (the clock is read on idle passes only: a read takes a while)
+      const uint64_t now = progress ? 0 : __builtin_amdgcn_s_memrealtime();
+      if (progress || last_progress == 0) {
+        last_progress = now;
+      } else if (now - last_progress > kGiveUpTicks) {
+        act = 2;
+      } else if (now - last_progress > kHelpTicks) {
+        for (int j = 0; j < nt && hj < 0; ++j)
+          if (!sh.ts[j].ended && sh.ts[j].miss != 0ull) {
+            hj = j;
+            // the first missing slice at or after this workgroup's own
+            const uint64_t m = sh.ts[j].miss;
+            hs = (__builtin_ctzll(rotr64(m, member & (kWave - 1))) + member) & (kWave - 1);
+          }
+        if (hj >= 0) {
+          act = 1;
+          last_progress = now;
+        }
+      }
+      sh.action = act;
+      sh.help_j = hj;
+      sh.help_s = hs;
+    }
+    __syncthreads();
+    const int act = sh.action;
+    if (act == 2) {
+      if (tid == 0)
+        for (int j = 0; j < nt; ++j)
+          if (!sh.ts[j].ended) {
+            const int n = grp + j * a.groups;
+            if (a.status) atomicOr(&a.status[n], MFD_TREE_CAPACITY);
+            a.tau[n] = 0;
+          }
+      break;
+    }
+    if (act == 1) {
+      do_slice(uni(sh.help_j), uni(sh.help_s));
+      backoff = 1;
+    } else if (!progress) {
+      backoff = backoff < 8 ? backoff * 2 : 8;
+      for (int z = 0; z < backoff; ++z) __builtin_amdgcn_s_sleep(kPollSleep);
+    } else {
+      backoff = 1;
     }
   }
 }
@@ -938,21 +1073,25 @@ constexpr size_t round_up(size_t x) {
 }
 
 struct WalkWsLayout {
-  size_t word, cut, claim, done, py1, py2, pi, seq_total;                // the walk kernel
+  size_t word, slot, seq_total;                                           // the walk kernel
   size_t spec_cnt, spec_nodes, choice, rowdone, treedone, sy, si, total;  // speculation
   int rcap;
 };
 
-// Slices per row of V elements of esz bytes: about kSliceVec vectors per
-// thread, at most kSlices and at most `resident` workgroups.
-long long walk_slices(long long V, size_t esz, long long resident) {
+// Slices per row of V elements of esz bytes: at least one 16-byte vector per
+// thread, at most kSlices and at most `cap`.
+long long walk_slices(long long V, size_t esz, long long cap) {
   const long long nvec = V / (long long)(16 / esz);
-  long long S = (nvec + (long long)kSliceVec * kWalkThreads - 1) / ((long long)kSliceVec * kWalkThreads);
+  long long S = (nvec + kWalkThreads - 1) / kWalkThreads;
   if (S > kSlices) S = kSlices;
-  if (S > resident) S = resident;
+  if (S > cap) S = cap;
   if (S < 1) S = 1;
   return S;
 }
+
+// Rounds a tree's walk may take: the root's row and one per move, each at
+// most twice (the estimate, then the exact re-evaluation).
+int walk_rounds(int L) { return 2 * (L + 1); }
 
 // Rows the speculation may reduce in one launch of N trees of Bp1 nodes over
 // rows of V elements of esz bytes.
@@ -964,7 +1103,7 @@ long long spec_rows(int N, int Bp1, long long V, size_t esz) {
 
 // Workspace: the walk kernel's arrays, then (Bp1 > 0) the speculation's,
 // sized for rows of V elements of either element size.
-WalkWsLayout walk_ws_layout(int N, int Bp1 = 0, long long V = 0) {
+WalkWsLayout walk_ws_layout(int N, int L, int Bp1 = 0, long long V = 0) {
   WalkWsLayout w = {};
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -972,13 +1111,10 @@ WalkWsLayout walk_ws_layout(int N, int Bp1 = 0, long long V = 0) {
     o = round_up<128>(o + bytes);
     return r;
   };
+  // per tree, round and slice: a result slot of two 64-bit words
+  const size_t slots = (size_t)N * walk_rounds(L) * kSlices;
   w.word = take((size_t)N * sizeof(uint32_t));
-  w.cut = take((size_t)N * sizeof(double));
-  w.claim = take((size_t)N * kMaxRounds * sizeof(int32_t));
-  w.done = take((size_t)N * kMaxRounds * sizeof(int32_t));
-  w.py1 = take((size_t)N * kSlices * sizeof(double));
-  w.py2 = take((size_t)N * kSlices * sizeof(double));
-  w.pi = take((size_t)N * kSlices * sizeof(int32_t));
+  w.slot = take(slots * 2 * sizeof(uint64_t));
   w.seq_total = o + 128;  // room to align the base
   if (Bp1 > 0 && V > 0) {
     long long rs = 0;  // rows x slices, the larger over the two element sizes
@@ -1001,11 +1137,11 @@ WalkWsLayout walk_ws_layout(int N, int Bp1 = 0, long long V = 0) {
 
 }  // namespace
 
-size_t walk_ws_bytes(int N) { return walk_ws_layout(N).seq_total; }
+size_t walk_ws_bytes(int N, int L) { return walk_ws_layout(N, L).seq_total; }
 
-size_t walk_ws_bytes_full(int N, int Bp1, long long V) {
-  if (V < 1 || Bp1 < 1 || Bp1 > kMaxB1) return walk_ws_bytes(N);
-  return walk_ws_layout(N, Bp1, V).total;
+size_t walk_ws_bytes_full(int N, int L, int Bp1, long long V) {
+  if (V < 1 || Bp1 < 1 || Bp1 > kMaxB1) return walk_ws_bytes(N, L);
+  return walk_ws_layout(N, L, Bp1, V).total;
 }
 
 hipError_t launch_verify_walk(const void* target, bool bf16, int N, int Bp1, long long V, int L,
@@ -1024,23 +1160,17 @@ hipError_t launch_verify_walk(const void* target, bool bf16, int N, int Bp1, lon
   if (e != hipSuccess) return e;
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kWalkThreads, 0);
   if (e != hipSuccess) return e;
-  long long resident = (long long)cus * (per_cu < 1 ? 1 : per_cu);
-  const long long S = walk_slices(V, esz, resident);
-  // trees per launch (the walk kernel keeps a byte per tree in LDS)
-  const long long per_launch = kWalkMaxTrees;
+  const long long resident = (long long)cus * (per_cu < 1 ? 1 : per_cu);
+  // trees per launch: one slice per row and kTreesPerGroup trees per group
+  const long long per_launch = resident * kTreesPerGroup;
+  const int R = walk_rounds(L);
 
   // speculation when its arrays fit the workspace (the walk gives the same
   // result without it)
-  const WalkWsLayout lf = walk_ws_layout(N, Bp1, V);
+  const WalkWsLayout lf = walk_ws_layout(N, L, Bp1, V);
   const bool spec = Bp1 <= kMaxB1 && lf.total <= ws_bytes;
-  const WalkWsLayout l = spec ? lf : walk_ws_layout(N);
-  int rcap = 0;
-  if (spec) {
-    const long long rs = (long long)((l.si - l.sy) / sizeof(double));  // rows x slices the arrays hold (at least)
-    long long r = spec_rows(N, Bp1, V, esz);
-    if (r * S > rs) r = rs / S;
-    rcap = (int)r;
-  }
+  const WalkWsLayout l = spec ? lf : walk_ws_layout(N, L);
+  const long long Smax = walk_slices(V, esz, kSlices);  // the slice-result arrays' row stride bound
   const void* sfn = bf16 ? reinterpret_cast<const void*>(&walk_spec_kernel<true>)
                          : reinterpret_cast<const void*>(&walk_spec_kernel<false>);
   int spec_per_cu = 0;
@@ -1053,13 +1183,16 @@ hipError_t launch_verify_walk(const void* target, bool bf16, int N, int Bp1, lon
   char* w = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(ws) + 127) & ~uintptr_t(127));
   for (long long n0 = 0; n0 < N; n0 += per_launch) {
     const int nb = (int)(N - n0 < per_launch ? N - n0 : per_launch);
-    // workgroups: at most one per slice that can be open at once; groups of
-    // about S workgroups, at most one per tree
-    long long G = (long long)nb * S;
-    if (G > resident) G = resident;
-    long long groups = G / S;
-    if (groups < 1) groups = 1;
+    // S slices per row, as many as the resident workgroups allow for one
+    // group per tree; groups of S workgroups, each serving at most
+    // kTreesPerGroup trees
+    long long S = resident / nb;
+    if (S > Smax) S = Smax;
+    if (S < 1) S = 1;
+    long long groups = resident / S;
     if (groups > nb) groups = nb;
+    if ((nb + groups - 1) / groups > kTreesPerGroup) return hipErrorInvalidConfiguration;  // (cannot happen)
+    const long long G = groups * S;
     WalkArgs a = {};
     a.groups = (int)groups;
     a.target = static_cast<const char*>(target) + (size_t)n0 * Bp1 * V * esz;
@@ -1068,6 +1201,7 @@ hipError_t launch_verify_walk(const void* target, bool bf16, int N, int Bp1, lon
     a.L = L;
     a.S = (int)S;
     a.G = (int)G;
+    a.R = R;
     a.V = V;
     a.node_token = node_token + (size_t)n0 * Bp1;
     a.parent = parent + (size_t)n0 * Bp1;
@@ -1080,12 +1214,16 @@ hipError_t launch_verify_walk(const void* target, bool bf16, int N, int Bp1, lon
     a.path_nodes = path_nodes + (size_t)n0 * (L + 1);
     a.status = status ? status + n0 : nullptr;
     a.word = reinterpret_cast<uint32_t*>(w + l.word) + n0;
-    a.cut = reinterpret_cast<double*>(w + l.cut) + n0;
-    a.claim = reinterpret_cast<int32_t*>(w + l.claim) + (size_t)n0 * kMaxRounds;
-    a.done = reinterpret_cast<int32_t*>(w + l.done) + (size_t)n0 * kMaxRounds;
-    a.py1 = reinterpret_cast<double*>(w + l.py1) + (size_t)n0 * kSlices;
-    a.py2 = reinterpret_cast<double*>(w + l.py2) + (size_t)n0 * kSlices;
-    a.pi = reinterpret_cast<int32_t*>(w + l.pi) + (size_t)n0 * kSlices;
+    // the slot arrays are cleared by each launch's prep pass and indexed
+    // from the launch's first tree with row stride S <= kSlices
+    a.slot = reinterpret_cast<uint64_t*>(w + l.slot);
+    int rcap = 0;
+    if (spec) {
+      const long long rs = (long long)((l.si - l.sy) / sizeof(double));  // rows x slices the arrays hold (at least)
+      long long r = spec_rows(nb, Bp1, V, esz);
+      if (r * Smax > rs) r = rs / Smax;
+      rcap = (int)r;
+    }
     a.spec = (spec && nb <= kSpecLaunchTrees && rcap > 0) ? 1 : 0;
     if (a.spec) {
       a.spec_rcap = rcap;

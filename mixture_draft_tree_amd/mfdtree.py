@@ -145,14 +145,16 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise ValueError(f"unsupported logits dtype {t.dtype}")
 
 
-def walk_workspace(N: int, device="cuda", Bp1: Optional[int] = None, V: Optional[int] = None) -> torch.Tensor:
-    """A device workspace for mfd_verify_walk on N trees.  With the trees' row
-    count Bp1 and the vocabulary V it also holds the speculative pass's arrays
-    (without them the walk runs row after row; the results are the same)."""
+def walk_workspace(N: int, device="cuda", Bp1: Optional[int] = None, V: Optional[int] = None,
+                   L: int = 32) -> torch.Tensor:
+    """A device workspace for mfd_verify_walk on N trees of draft length up to L.
+    With the trees' row count Bp1 and the vocabulary V it also holds the
+    speculative pass's arrays (without them the walk runs row after row; the
+    results are the same)."""
     if Bp1 is None or V is None:
-        n = workspace_size(MFD_OP_VERIFY_WALK, N, 1, 1, 1, -1)
+        n = workspace_size(MFD_OP_VERIFY_WALK, N, 1, L, 1, -1)
     else:
-        n = workspace_size(MFD_OP_VERIFY_WALK, N, 1, 1, V, Bp1 - 1)
+        n = workspace_size(MFD_OP_VERIFY_WALK, N, 1, L, V, Bp1 - 1)
     return torch.empty((max(n, 8) + 7) // 8, dtype=torch.int64, device=device)
 
 
@@ -422,13 +424,26 @@ def mfd_verify_walk(target_logits, L, node_token, parent, depth, n_nodes, temper
                                 _stream_handle(stream)), "mfd_verify_walk")
 
 
-WALK_NOALLOC_MAX_TREES = 1152
+WALK_NOALLOC_BYTES = 16 << 20  # the library's built-in walk workspace
+
+
+def walk_noalloc_max_trees(L: int) -> int:
+    """The most trees mfd_verify_walk_noalloc takes at draft length L: those
+    whose walk workspace fits the built-in WALK_NOALLOC_BYTES."""
+    lo, hi = 0, 1 << 20
+    while lo < hi:
+        mid = (lo + hi + 1) // 2
+        if workspace_size(MFD_OP_VERIFY_WALK, mid, 1, L, 1, -1) <= WALK_NOALLOC_BYTES:
+            lo = mid
+        else:
+            hi = mid - 1
+    return lo
 
 
 def mfd_verify_walk_noalloc(target_logits, L, node_token, parent, depth, n_nodes, temperature, seed, tau,
                             out_tokens, path_nodes, status=None, stream=None):
     """mfd_verify_walk on the library's built-in workspace (no workspace argument,
-    no allocation); at most WALK_NOALLOC_MAX_TREES trees, calls on one GPU must not overlap."""
+    no allocation); at most walk_noalloc_max_trees(L) trees, calls on one GPU must not overlap."""
     if target_logits.dim() != 3 or not target_logits.is_contiguous() or target_logits.device.type != "cuda":
         raise ValueError("target_logits must be a contiguous [N, B+1, V] GPU tensor")
     N, Bp1, V = target_logits.shape

@@ -25,8 +25,8 @@ Readings where the pages are silent (each listed in the design notes):
     token ids lexicographically with a proper prefix before its extensions.
     Rank order within a row: higher logit first, then lower token id.
   * Node layout: root first, then nodes by (depth, token sequence).
-  * Sampling at T > 0 is Gumbel-max with Philox4x64-10 noise keyed by
-    (seed, 0), counter (v div 4, depth, 0, 0), lane v mod 4.
+  * Sampling at T > 0 is Gumbel-max with Philox4x32-10 noise keyed by the
+    seed's two 32-bit halves, counter (v div 4, depth, 0, 0), word v mod 4.
   * -inf logits are allowed and never selected.
 """
 
@@ -43,7 +43,7 @@ __all__ = [
     "lse_rows", "rank_order", "prefix_norms", "lmhead_logits", "lmhead_abs_bound", "MixtureSelection",
     "mixture_select_heap", "mixture_select_bruteforce", "ddtree_product_select",
     "mode_scores", "union_at_cutoff", "canonical_tree", "tree_mask",
-    "pack_mask_words", "philox4x64_10", "gumbel_noise", "verify_walk",
+    "pack_mask_words", "philox4x32_10", "gumbel_noise", "verify_walk",
     "covered_mass", "chimera_nodes", "band_is_exact", "build_tree",
     "PHILOX_M0", "PHILOX_M1", "PHILOX_W0", "PHILOX_W1",
 ]
@@ -508,63 +508,53 @@ def pack_mask_words(dense: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
-# Counter-based noise: Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11)
+# Counter-based noise: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11)
 # ---------------------------------------------------------------------------
 
-PHILOX_M0 = 0xD2E7470EE14C6C93
-PHILOX_M1 = 0xCA5A826395121157
-PHILOX_W0 = 0x9E3779B97F4A7C15
-PHILOX_W1 = 0xBB67AE8584CAA73B
+PHILOX_M0 = 0xD2511F53
+PHILOX_M1 = 0xCD9E8D57
+PHILOX_W0 = 0x9E3779B9
+PHILOX_W1 = 0xBB67AE85
 _M32 = np.uint64(0xFFFFFFFF)
 
 
-def _mulhilo(a: int, b: np.ndarray):
-    """(high, low) 64-bit halves of the 128-bit product a * b, elementwise."""
-    a = np.uint64(a)
-    a_lo, a_hi = a & _M32, a >> np.uint64(32)
-    b_lo, b_hi = b & _M32, b >> np.uint64(32)
-    ll = a_lo * b_lo
-    lh = a_lo * b_hi
-    hl = a_hi * b_lo
-    hh = a_hi * b_hi
-    mid = (ll >> np.uint64(32)) + (lh & _M32) + (hl & _M32)
-    lo = (ll & _M32) | (mid << np.uint64(32))
-    hi = hh + (lh >> np.uint64(32)) + (hl >> np.uint64(32)) + (mid >> np.uint64(32))
-    return hi, lo
+def philox4x32_10(ctr, key):
+    """Philox4x32 with 10 rounds.  ctr: four arrays (or ints) of 32-bit words;
+    key: two 32-bit ints.  Returns the four output words as uint64 arrays.
 
-
-def philox4x64_10(ctr, key):
-    """Philox4x64 with 10 rounds.  ctr: four uint64 arrays (or ints); key: two ints.
-
-    Each round multiplies counter words 0 and 2 by the two round constants,
-    swaps halves and mixes in the key; the key is bumped by the two Weyl
-    constants between rounds.
+    Each round forms the 64-bit products of counter words 0 and 2 with the two
+    round constants; the new words are (hi of the second product ^ word 1 ^
+    key 0, its low half, hi of the first product ^ word 3 ^ key 1, its low
+    half).  The key is bumped by the two Weyl constants between rounds.
     """
     with np.errstate(over="ignore"):
-        x0, x1, x2, x3 = (np.asarray(c, dtype=np.uint64) for c in ctr)
-        k0, k1 = int(key[0]) & ((1 << 64) - 1), int(key[1]) & ((1 << 64) - 1)
+        x0, x1, x2, x3 = (np.asarray(c, dtype=np.uint64) & _M32 for c in ctr)
+        k0, k1 = int(key[0]) & 0xFFFFFFFF, int(key[1]) & 0xFFFFFFFF
         for r in range(10):
-            hi0, lo0 = _mulhilo(PHILOX_M0, x0)
-            hi1, lo1 = _mulhilo(PHILOX_M1, x2)
-            x0, x1, x2, x3 = hi1 ^ x1 ^ np.uint64(k0), lo1, hi0 ^ x3 ^ np.uint64(k1), lo0
-            k0 = (k0 + PHILOX_W0) & ((1 << 64) - 1)
-            k1 = (k1 + PHILOX_W1) & ((1 << 64) - 1)
+            p0 = np.uint64(PHILOX_M0) * x0  # < 2^64: exact in uint64
+            p1 = np.uint64(PHILOX_M1) * x2
+            x0, x1, x2, x3 = ((p1 >> np.uint64(32)) ^ x1 ^ np.uint64(k0), p1 & _M32,
+                              (p0 >> np.uint64(32)) ^ x3 ^ np.uint64(k1), p0 & _M32)
+            k0 = (k0 + PHILOX_W0) & 0xFFFFFFFF
+            k1 = (k1 + PHILOX_W1) & 0xFFFFFFFF
     return x0, x1, x2, x3
 
 
 def gumbel_noise(seed: int, depth: int, V: int) -> np.ndarray:
     """Standard Gumbel noise g_v for v in [0, V) at one walk depth, fp64.
 
-    w_v = Philox4x64-10(counter = (v div 4, depth, 0, 0), key = (seed, 0)) lane v mod 4;
-    U_v = ((w_v >> 12) + 1/2) * 2^-52, strictly inside (0, 1);  g_v = -log(-log U_v).
+    w_v = word (v mod 4) of Philox4x32-10(counter = (v div 4, depth, 0, 0),
+          key = (seed mod 2^32, seed div 2^32));
+    U_v = (w_v + 1/2) * 2^-32, strictly inside (0, 1);  g_v = -log(-log U_v).
     """
     v = np.arange(V, dtype=np.uint64)
     q = v >> np.uint64(2)
     z = np.zeros_like(q)
-    outs = philox4x64_10((q, np.full_like(q, depth), z, z), (seed, 0))
+    seed = int(seed) & ((1 << 64) - 1)
+    outs = philox4x32_10((q, np.full_like(q, depth), z, z), (seed & 0xFFFFFFFF, seed >> 32))
     lane = (v & np.uint64(3)).astype(np.int64)
     w = np.choose(lane, outs)
-    U = ((w >> np.uint64(12)).astype(np.float64) + 0.5) * 2.0 ** -52
+    U = (w.astype(np.float64) + 0.5) * 2.0 ** -32
     return -np.log(-np.log(U))
 
 

@@ -157,10 +157,11 @@ static int cpu_checks(void) {
   expect(mfd_verify_walk(fake, MFD_F32, 1, 9, 16, 4, fake, fake, fake, fake, fake, fake, fake, fake, fake, NULL, odd,
                          1 << 20, 0) == MFD_ERR_INVALID_ARG,
          "walk: misaligned workspace rejected");
-  expect(mfd_verify_walk_noalloc(fake, MFD_F32, 1153, 9, 16, 4, fake, fake, fake, fake, fake, fake, fake, fake, fake,
+  /* at L = 4 the built-in 16 MiB holds the walk workspace of 1637 trees */
+  expect(mfd_verify_walk_noalloc(fake, MFD_F32, 1638, 9, 16, 4, fake, fake, fake, fake, fake, fake, fake, fake, fake,
                                  NULL, 0) == MFD_ERR_WORKSPACE &&
-             strstr(mfd_last_error(), "N <= 1152") != NULL,
-         "walk without workspace: 1153 trees rejected with the limit");
+             strstr(mfd_last_error(), "N <= 1637") != NULL,
+         "walk without workspace: 1638 trees rejected with the limit");
   expect(mfd_verify_walk_noalloc(NULL, MFD_F32, 0, 9, 16, 4, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL,
                                  NULL, 0) == MFD_OK,
          "walk without workspace: N = 0 is a no-op");

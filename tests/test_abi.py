@@ -159,16 +159,20 @@ def test_mask_and_walk_reject():
 
 
 def test_walk_noalloc_limit_and_rejects():
-    """The built-in walk workspace holds 2 MiB: 1347 trees fit, 1348 do not, and
-    the larger call is refused before anything touches a device."""
-    assert M.workspace_size(M.MFD_OP_VERIFY_WALK, M.WALK_NOALLOC_MAX_TREES, 1, 1, 1, -1) <= 2 << 20
-    assert M.workspace_size(M.MFD_OP_VERIFY_WALK, M.WALK_NOALLOC_MAX_TREES + 1, 1, 1, 1, -1) > 2 << 20
+    """The built-in walk workspace holds 16 MiB: the trees whose workspace fits
+    are accepted, one more is refused before anything touches a device, and
+    fewer trees fit at a longer draft length (a tree keeps slots per round)."""
+    cap = M.walk_noalloc_max_trees(4)
+    assert M.workspace_size(M.MFD_OP_VERIFY_WALK, cap, 1, 4, 1, -1) <= 16 << 20
+    assert M.workspace_size(M.MFD_OP_VERIFY_WALK, cap + 1, 1, 4, 1, -1) > 16 << 20
+    assert M.walk_noalloc_max_trees(32) < M.walk_noalloc_max_trees(15) < cap
+    assert M.walk_noalloc_max_trees(15) >= 64  # a batch of 64 trees of 15 tokens fits
     # the speculative pass's arrays come on top when the trees' B and V are given
     assert (M.workspace_size(M.MFD_OP_VERIFY_WALK, 64, 8, 15, 151936, 256) >
             M.workspace_size(M.MFD_OP_VERIFY_WALK, 64, 8, 15, 151936, -1))
-    args = [FAKE, M.MFD_F32, M.WALK_NOALLOC_MAX_TREES + 1, 9, 16, 4] + [FAKE] * 9 + [None, None]
+    args = [FAKE, M.MFD_F32, cap + 1, 9, 16, 4] + [FAKE] * 9 + [None, None]
     assert M._lib.mfd_verify_walk_noalloc(*args) == M.MFD_ERR_WORKSPACE
-    assert f"N <= {M.WALK_NOALLOC_MAX_TREES}" in M.last_error()
+    assert f"N <= {cap}" in M.last_error()
     bad = list(args)
     bad[1] = 5
     assert M._lib.mfd_verify_walk_noalloc(*bad) == M.MFD_ERR_DTYPE

@@ -375,16 +375,43 @@ def test_canonical_layout_and_mask():
 
 # ---------------------------------------------------------------- RNG
 
-def test_philox_matches_numpy():
+# Known-answer vectors of Philox4x32-10 published with the generator (the
+# Random123 distribution of Salmon et al., SC'11): counter, key -> output.
+PHILOX4X32_KAT = [
+    ((0x00000000, 0x00000000, 0x00000000, 0x00000000), (0x00000000, 0x00000000),
+     (0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8)),
+    ((0xFFFFFFFF, 0xFFFFFFFF, 0xFFFFFFFF, 0xFFFFFFFF), (0xFFFFFFFF, 0xFFFFFFFF),
+     (0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD)),
+    ((0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344), (0xA4093822, 0x299F31D0),
+     (0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1)),
+]
+
+
+@pytest.mark.parametrize("ctr,key,want", PHILOX4X32_KAT)
+def test_philox_known_answers(ctr, key, want):
+    assert tuple(int(np.asarray(w)) for w in O.philox4x32_10(ctr, key)) == want
+
+
+def test_philox_vectorised_equals_one_at_a_time():
+    """The array form gives each counter's block as the scalar form does."""
     rng = np.random.default_rng(10)
-    for _ in range(20):
-        key = [int(v) for v in rng.integers(0, 2 ** 63, size=2)]
-        ctr = [int(v) for v in rng.integers(1, 2 ** 63, size=4)]
-        ours = [int(np.asarray(w)) for w in O.philox4x64_10(ctr, key)]
-        npc = np.array(ctr, dtype=np.uint64)
-        npc[0] -= np.uint64(1)  # numpy bumps the counter before each block
-        g = np.random.Philox(key=np.array(key, dtype=np.uint64), counter=npc)
-        assert ours == [int(v) for v in g.random_raw(4)]
+    ctr = [rng.integers(0, 2 ** 32, size=50, dtype=np.uint64) for _ in range(4)]
+    key = [int(v) for v in rng.integers(0, 2 ** 32, size=2)]
+    outs = O.philox4x32_10(ctr, key)
+    for i in range(50):
+        one = O.philox4x32_10([int(c[i]) for c in ctr], key)
+        assert [int(o[i]) for o in outs] == [int(np.asarray(o)) for o in one]
+
+
+def test_gumbel_noise_words():
+    """Noise of token v at depth d comes from word v mod 4 of the block with
+    counter (v div 4, d, 0, 0) and the seed's two halves as the key."""
+    seed, d = 0x0123456789ABCDEF, 5
+    g = O.gumbel_noise(seed, d, 12)
+    for v in range(12):
+        w = int(np.asarray(O.philox4x32_10((v // 4, d, 0, 0), (seed & 0xFFFFFFFF, seed >> 32))[v % 4]))
+        # numpy's and math's log may differ in the last bit
+        assert math.isclose(g[v], -math.log(-math.log((w + 0.5) * 2.0 ** -32)), rel_tol=1e-14, abs_tol=1e-15)
 
 
 def test_gumbel_moments():

@@ -67,7 +67,7 @@ def test_walk_noalloc_equals_workspace_walk(first, second):
 
 
 def test_walk_noalloc_rejects_more_trees_than_it_holds():
-    N = M.WALK_NOALLOC_MAX_TREES + 1
+    N = M.walk_noalloc_max_trees(1) + 1
     R = torch.zeros((N, 2, 8), dtype=torch.float32, device="cuda")
     z = lambda *s: torch.zeros(s, dtype=torch.int32, device="cuda")
     with pytest.raises(M.MfdError) as e:
