@@ -320,8 +320,24 @@ __device__ __forceinline__ float elem_at(const void* row, long long i) {
 // Calls f(i, x) for every element i of [e0, e1): scalars before and after the
 // 16-byte aligned part, then the aligned vectors kSliceVec per thread at a
 // time (all loads of a round issued before any is used).
-template <bool BF16, int VECS = kSliceVec, typename F>
-__device__ __forceinline__ void for_slice(const void* row, long long e0, long long e1, F f) {
+// Philox block of element i (four words per counter), cached across calls.
+struct NoiseCache {
+  long long blk = -1;
+  Philox4 r;
+  __device__ __forceinline__ uint32_t word(long long i, uint64_t seed, int d) {
+    const long long bk = i >> 2;
+    if (bk != blk) {
+      r = philox4x32_10((uint32_t)bk, (uint32_t)d, 0, 0, (uint32_t)seed, (uint32_t)(seed >> 32));
+      blk = bk;
+    }
+    return lane_word(r, (int)(i & 3));
+  }
+};
+
+// As for_slice, but each aligned vector goes to fv(i0, x) whole (x[j] is
+// element i0 + j), the scalars to f(i, x).
+template <bool BF16, int VECS, typename F, typename FV>
+__device__ __forceinline__ void for_slice_vec(const void* row, long long e0, long long e1, F f, FV fv) {
   constexpr int VEC = BF16 ? 8 : 4;
   constexpr int ESZ = BF16 ? 2 : 4;
   const int tid = threadIdx.x;
@@ -346,16 +362,51 @@ __device__ __forceinline__ void for_slice(const void* row, long long e0, long lo
     for (int u = 0; u < VECS; ++u) {
       const long long q = q0 + u * kWalkThreads + tid;
       if (q < nv) {
-        const long long i0 = a + q * VEC;
+        float x[VEC];
 #pragma unroll
         for (int j = 0; j < VEC; ++j) {
           const uint32_t w = v[u][BF16 ? (j >> 1) : j];
-          const float x = BF16 ? __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16)) : __uint_as_float(w);
-          f(i0 + j, x);
+          x[j] = BF16 ? __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16)) : __uint_as_float(w);
         }
+        fv(a + q * VEC, x);
       }
     }
   }
+}
+
+template <bool BF16, int VECS = kSliceVec, typename F>
+__device__ __forceinline__ void for_slice(const void* row, long long e0, long long e1, F f) {
+  constexpr int VEC = BF16 ? 8 : 4;
+  for_slice_vec<BF16, VECS>(row, e0, e1, f, [&](long long i0, const float (&x)[VEC]) {
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) f(i0 + j, x[j]);
+  });
+}
+
+// The fp32 first pass at T > 0 over [e0, e1): est = fma(x, invTf, noise
+// estimate) into the per-thread top two.  A vector whose first element starts
+// a Philox block (every vector, when the row's aligned part does) takes its
+// blocks whole, with no per-element bookkeeping.
+template <bool BF16, int VECS>
+__device__ __forceinline__ void slice_estimates(const void* row, long long e0, long long e1, uint64_t sd, int d,
+                                                float invTf, Top2f& f) {
+  constexpr int VEC = BF16 ? 8 : 4;
+  NoiseCache nc;
+  const uint32_t k0 = (uint32_t)sd, k1 = (uint32_t)(sd >> 32);
+  auto one = [&](long long i, float x) { top2f_add(f, fmaf(x, invTf, gumbel_estimate(nc.word(i, sd, d))), (int)i); };
+  for_slice_vec<BF16, VECS>(row, e0, e1, one, [&](long long i0, const float (&x)[VEC]) {
+    if ((i0 & 3) == 0) {
+#pragma unroll
+      for (int b = 0; b < VEC / 4; ++b) {
+        const Philox4 r = philox4x32_10((uint32_t)(i0 >> 2) + b, (uint32_t)d, 0, 0, k0, k1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) top2f_add(f, fmaf(x[4 * b + j], invTf, gumbel_estimate(r.v[j])), (int)i0 + 4 * b + j);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) one(i0 + j, x[j]);
+    }
+  });
 }
 
 // Element range [e0, e1) of slice s of S of a row: the row's aligned vectors
@@ -373,19 +424,6 @@ __device__ __forceinline__ void slice_range(const void* row, long long V, int S,
   e1 = s == S - 1 ? V : a + (nv * (s + 1) / S) * VEC;
 }
 
-// Philox block of element i (four words per counter), cached across calls.
-struct NoiseCache {
-  long long blk = -1;
-  Philox4 r;
-  __device__ __forceinline__ uint32_t word(long long i, uint64_t seed, int d) {
-    const long long bk = i >> 2;
-    if (bk != blk) {
-      r = philox4x32_10((uint32_t)bk, (uint32_t)d, 0, 0, (uint32_t)seed, (uint32_t)(seed >> 32));
-      blk = bk;
-    }
-    return lane_word(r, (int)(i & 3));
-  }
-};
 
 // Block-wide Top2 of the per-thread values (barriers inside); every thread gets it.
 __device__ __forceinline__ Top2 block_top2(Top2 t, Top2* wsh) {
@@ -879,10 +917,7 @@ __global__ void __launch_bounds__(kWalkThreads, 4) verify_walk_kernel(WalkArgs a
       if (T == 0.0) {
         for_slice<BF16, kWalkVec0>(row, e0, e1, [&](long long i, float x) { top2f_add(f, x, (int)i); });
       } else {
-        const float invTf = (float)(1.0 / T);
-        for_slice<BF16, kWalkVec>(row, e0, e1, [&](long long i, float x) {
-          top2f_add(f, fmaf(x, invTf, gumbel_estimate(nc.word(i, sd, d))), (int)i);
-        });
+        slice_estimates<BF16, kWalkVec>(row, e0, e1, sd, d, (float)(1.0 / T), f);
       }
       acc = {(double)f.y1, f.i1, (double)f.y2};
     } else {
