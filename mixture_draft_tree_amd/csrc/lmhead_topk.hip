@@ -428,7 +428,7 @@ static_assert(SkRing<kSkNB, kSkWaves>::lds <= 160 * 1024 && SkRing<1, kSkSampleW
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void sk_dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" : : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds)
-               : "memory");
+               : "memory", "m0");
 }
 // Raw buffer descriptor: base, no stride, `bytes` long (gfx9 word 3).
 __device__ __forceinline__ i32x4 sk_rsrc(const void* base, uint32_t bytes) {
