@@ -218,11 +218,14 @@ struct WalkArgs {
   int32_t* status;
   uint32_t* word;  // [N] round words
   int R;           // rounds a tree may take: two per depth, 2 (L + 1)
+  int esz;         // bytes per target element
   uint64_t* slot;  // [N][R][S][2]: each slice's result of each round (slot_pack)
   // speculation (walk_prep_kernel / walk_spec_kernel); spec = 0: none
   int spec;
   int spec_rcap;         // rows the slice-result arrays hold
-  int32_t* spec_cnt;     // [N][4]: nodes with a child, all nodes (0 for an ended tree), deepest node, T > 0
+  int32_t* spec_cnt;     // [N][4]: nodes with a child, all nodes (0 for an ended tree), expected rounds x16, T > 0
+  int32_t* spec_go;      // [1]: the pass's route decided by the prep pass (one tree): 0 none, 1 nodes with a
+                         // child, 2 every node; -1: decided by the pass itself
   uint16_t* spec_nodes;  // [N][Bp1]: the tree's nodes with a child, then its leaves
   int32_t* choice;       // [N][Bp1]: token chosen at each evaluated node, -1 if not evaluated
   int32_t* rowdone;      // [N][Bp1]: slices finished per listed row
@@ -437,6 +440,8 @@ __device__ __forceinline__ Top2 block_top2(Top2 t, Top2* wsh) {
   return r;
 }
 
+__device__ int spec_route(const WalkArgs& a, int N, int* scan);
+
 // One workgroup per tree.  Opens round 0 (the root) of a tree with a valid
 // temperature and ends the others; clears the per-round counters.  With
 // speculation on, also lists the tree's nodes (those with a child first, in
@@ -482,13 +487,15 @@ __global__ void __launch_bounds__(kWalkThreads) walk_prep_kernel(WalkArgs a) {
     if (p >= 0 && p < nn) has_child[p] = 1;
   }
   __syncthreads();
-  int local = 0, dmax = 0;
+  int local = 0, dmax = 0, dsum = 0;
   for (int u = tid; u < nn; u += kWalkThreads) {
     local += has_child[u];
     const int du = a.depth[tb + u];
     dmax = du > dmax ? du : dmax;
+    dsum += du;
   }
   const int nint = block_sum<kWalkThreads>(local, scan);
+  const int dtot = block_sum<kWalkThreads>(dsum, scan);
   // the deepest node, by a max over the waves (scan[] is free again)
 #pragma unroll
   for (int o = kWave / 2; o > 0; o >>= 1) dmax = max(dmax, __shfl_xor(dmax, o, kWave));
@@ -496,6 +503,27 @@ __global__ void __launch_bounds__(kWalkThreads) walk_prep_kernel(WalkArgs a) {
   __syncthreads();
   for (int w = 0; w < kWalkWaves; ++w) dmax = max(dmax, scan[w]);
   __syncthreads();
+  if (tid == 0) {
+    a.spec_cnt[4 * n] = nint;
+    a.spec_cnt[4 * n + 1] = nn;
+    // rounds the row-by-row walk is expected to take, x16: one more than
+    // the mean of the nodes' mean depth and the deepest depth (the walk stops
+    // at the first token the tree lacks, usually well short of its deepest
+    // node in a bushy tree, near it in a chain)
+    a.spec_cnt[4 * n + 2] = nn > 1 ? 16 + (int)((8ll * dtot) / (nn - 1)) + 8 * dmax : (nn > 0 ? 16 : 0);
+    a.spec_cnt[4 * n + 3] = T > 0.f ? 1 : 0;
+  }
+  // one tree: this workgroup has every count the route needs, so it decides
+  // here, the speculative pass's workgroups just read the answer, and the
+  // node lists are only made when the pass runs
+  if (a.N == 1) {
+    __syncthreads();  // the counts above are in place
+    const int route = spec_route(a, 1, scan);
+    if (tid == 0) a.spec_go[0] = route + 2;
+    if (route < 0) return;
+  } else if (n == 0 && tid == 0) {
+    a.spec_go[0] = 0;
+  }
   int carry = 0;
   for (int base = 0; base < nn; base += kWalkThreads) {
     const int u = base + tid;
@@ -507,12 +535,6 @@ __global__ void __launch_bounds__(kWalkThreads) walk_prep_kernel(WalkArgs a) {
       a.spec_nodes[tb + (h ? before : nint + (u - before))] = (uint16_t)u;
     }
     carry += tot;
-  }
-  if (tid == 0) {
-    a.spec_cnt[4 * n] = nint;
-    a.spec_cnt[4 * n + 1] = nn;
-    a.spec_cnt[4 * n + 2] = nn > 0 ? dmax : 0;
-    a.spec_cnt[4 * n + 3] = T > 0.f ? 1 : 0;
   }
 }
 
@@ -539,13 +561,17 @@ constexpr long long kSpecIntBytes = 400ll << 20;  // else the rows of nodes with
 constexpr int kFollowLds = 2048;                  // nodes of a tree the follow step copies to LDS
 constexpr int kSpecVec = 8;                       // 16-byte vectors per thread in flight in the speculative pass
 // Cost estimates behind the choice between speculation and the row-by-row
-// walk, measured on MI355X at V = 151936: a dependent round of the walk, the
-// speculative pass's fixed cost, its reading rate, and the noise cost of one
-// T > 0 element (Philox4x64-10 and the estimate) spread over the whole chip.
-constexpr double kRoundUs = 7.5;
-constexpr double kSpecFixedUs = 18.0;
+// walk, measured on MI355X at V = 151936 (one tree, graph replays): a
+// dependent round of the walk (8 us: 27.8 us for a 2-round walk, 108 us for
+// 12 rounds), the speculative pass's fixed cost over the row-by-row walk's
+// (its launch and hand-offs; 34.4 against 27.8 us on a 2-round tree whose
+// interior rows take ~2 us to read), its reading rate, and the noise cost of
+// one T > 0 element (Philox4x32-10 and the estimate, ~1000 G elements/s)
+// spread over the whole chip.
+constexpr double kRoundUs = 8.0;
+constexpr double kSpecFixedUs = 25.0;
 constexpr double kSpecBytesPerUs = 2.0e6;
-constexpr double kNoiseUsPerElement = 4.0e-6;
+constexpr double kNoiseUsPerElement = 1.0e-6;
 constexpr int kSpecLaunchTrees = 4;  // the pass is only tried for launches of at most this many trees
 constexpr int kSpecMaxTrees = 64;    // trees per launch the pass can handle (its LDS prefix array)
 static_assert(kSpecLaunchTrees <= kSpecMaxTrees, "speculation prefix array too small");
@@ -638,23 +664,20 @@ __device__ BestYI spec_slice(const void* row, long long e0, long long e1, double
   return block_best(b, wsh);
 }
 
-template <bool BF16>
-__global__ void __launch_bounds__(kWalkThreads, 4) walk_spec_kernel(WalkArgs a) {
-  __shared__ int pre[kSpecMaxTrees + 1];
-  __shared__ int scan[kWalkWaves];
-  __shared__ BestYI wsh[kWalkWaves];
-  __shared__ int sh_row, sh_tree;  // separate flags: see the barriers
-  __shared__ int32_t fpar[kFollowLds], ftok[kFollowLds], fch[kFollowLds];
+// The speculative pass's route for the launch's N trees (their counts in
+// spec_cnt): 1 every node's row, 0 the rows of the nodes with a child, -1 no
+// pass.  Rows under each budget, and an estimate of each route's time.  Row
+// by row, the walk takes one dependent round per move of its longest walk,
+// estimated per tree by the prep pass (trees share groups of workgroups
+// beyond G).  Speculation reads the rows at once, pays the noise of every
+// T > 0 row, and leaves one round for the trees that end at an unevaluated
+// leaf.  Either route gives the same tokens; this only picks the faster one.
+// Every thread of the block calls it (barriers inside); all get the result.
+__device__ int spec_route(const WalkArgs& a, int N, int* scan) {
   const int tid = threadIdx.x;
-  const int N = a.N, S = a.S, Bp1 = a.Bp1, L = a.L, Lp1 = L + 1;
+  const int S = a.S;
   const long long V = a.V;
-  const size_t esz = BF16 ? 2 : 4;
-  // Rows under each budget, and an estimate of each route's time.  Row by
-  // row, the walk takes one dependent round per depth of its deepest tree
-  // (trees share groups of workgroups beyond G).  Speculation reads the rows
-  // at once, pays the noise of every T > 0 row, and leaves one round for
-  // the trees that end at an unevaluated leaf.  Either route gives the same
-  // tokens; this only picks the faster one.
+  const size_t esz = (size_t)a.esz;
   int loc_int = 0, loc_all = 0, loc_int_hot = 0, loc_all_hot = 0, loc_d = 0;
   for (int n = tid; n < N; n += kWalkThreads) {
     const int ni = a.spec_cnt[4 * n], na = a.spec_cnt[4 * n + 1], hot = a.spec_cnt[4 * n + 3];
@@ -677,7 +700,7 @@ __global__ void __launch_bounds__(kWalkThreads, 4) walk_spec_kernel(WalkArgs a) 
   __syncthreads();
   const long long row_bytes = V * (long long)esz;
   const double sharing = (double)(((long long)N * S + a.G - 1) / a.G);  // rounds open at once per workgroup
-  const double t_rows = (dmax + 1) * kRoundUs * sharing;
+  const double t_rows = (dmax / 16.0) * kRoundUs * sharing;  // dmax: the largest expected rounds x16
   auto t_spec = [&](long long rows, long long hot) {
     return kSpecFixedUs + (double)rows * row_bytes / kSpecBytesPerUs + (double)hot * V * kNoiseUsPerElement;
   };
@@ -685,10 +708,27 @@ __global__ void __launch_bounds__(kWalkThreads, 4) walk_spec_kernel(WalkArgs a) 
   const double t_int = t_spec(tot_int, hot_int) + kRoundUs * sharing;
   const bool ok_all = tot_all <= a.spec_rcap && tot_all * row_bytes <= kSpecAllBytes && t_all < t_rows;
   const bool ok_int = tot_int <= a.spec_rcap && tot_int * row_bytes <= kSpecIntBytes && t_int < t_rows;
-  int which;  // 1: every node, 0: nodes with a child
-  if (ok_all && (!ok_int || t_all <= t_int)) which = 1;
-  else if (ok_int) which = 0;
-  else return;
+  if (ok_all && (!ok_int || t_all <= t_int)) return 1;
+  if (ok_int) return 0;
+  return -1;
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(kWalkThreads, 4) walk_spec_kernel(WalkArgs a) {
+  __shared__ int pre[kSpecMaxTrees + 1];
+  __shared__ int scan[kWalkWaves];
+  __shared__ BestYI wsh[kWalkWaves];
+  __shared__ int sh_row, sh_tree;  // separate flags: see the barriers
+  __shared__ int32_t fpar[kFollowLds], ftok[kFollowLds], fch[kFollowLds];
+  const int tid = threadIdx.x;
+  const int N = a.N, S = a.S, Bp1 = a.Bp1, L = a.L, Lp1 = L + 1;
+  const long long V = a.V;
+  const size_t esz = BF16 ? 2 : 4;
+  // the route: decided by the prep pass for one tree (a previous launch;
+  // spec_go = route + 2), else here
+  const int go = a.spec_go[0];
+  const int which = go > 0 ? go - 2 : spec_route(a, N, scan);
+  if (which < 0) return;
   // prefix of the chosen row counts over the trees
   int carry = 0;
   for (int base = 0; base < N; base += kWalkThreads) {
@@ -1109,7 +1149,7 @@ constexpr size_t round_up(size_t x) {
 
 struct WalkWsLayout {
   size_t word, slot, seq_total;                                           // the walk kernel
-  size_t spec_cnt, spec_nodes, choice, rowdone, treedone, sy, si, total;  // speculation
+  size_t spec_cnt, spec_go, spec_nodes, choice, rowdone, treedone, sy, si, total;  // speculation
   int rcap;
 };
 
@@ -1159,6 +1199,7 @@ WalkWsLayout walk_ws_layout(int N, int L, int Bp1 = 0, long long V = 0) {
     }
     w.rcap = (int)spec_rows(N, Bp1, V, 2);
     w.spec_cnt = take((size_t)N * 4 * sizeof(int32_t));
+    w.spec_go = take(sizeof(int32_t));
     w.spec_nodes = take((size_t)N * Bp1 * sizeof(uint16_t));
     w.choice = take((size_t)N * Bp1 * sizeof(int32_t));
     w.rowdone = take((size_t)N * Bp1 * sizeof(int32_t));
@@ -1237,6 +1278,7 @@ hipError_t launch_verify_walk(const void* target, bool bf16, int N, int Bp1, lon
     a.S = (int)S;
     a.G = (int)G;
     a.R = R;
+    a.esz = (int)esz;
     a.V = V;
     a.node_token = node_token + (size_t)n0 * Bp1;
     a.parent = parent + (size_t)n0 * Bp1;
@@ -1263,6 +1305,7 @@ hipError_t launch_verify_walk(const void* target, bool bf16, int N, int Bp1, lon
     if (a.spec) {
       a.spec_rcap = rcap;
       a.spec_cnt = reinterpret_cast<int32_t*>(w + l.spec_cnt) + (size_t)n0 * 4;
+      a.spec_go = reinterpret_cast<int32_t*>(w + l.spec_go);
       a.spec_nodes = reinterpret_cast<uint16_t*>(w + l.spec_nodes) + (size_t)n0 * Bp1;
       a.choice = reinterpret_cast<int32_t*>(w + l.choice) + (size_t)n0 * Bp1;
       a.rowdone = reinterpret_cast<int32_t*>(w + l.rowdone) + (size_t)n0 * Bp1;
