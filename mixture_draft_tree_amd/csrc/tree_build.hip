@@ -267,6 +267,42 @@ __device__ __forceinline__ double kth_lower_bound(int n, int rank, Score score, 
   return f64_from_key(kb << 48);
 }
 
+// The rank-th largest 16-bit score key among the items scoring at least t0,
+// as a lower bound of their rank-th best score; -inf when fewer than rank
+// items reach t0.  Their keys are at least t0's key kt, and the scores in
+// play span far fewer than 255 keys above it (16 per binade), so one pass
+// histograms key - kt (255 and above share the top bin), counting the items
+// as it goes, and the two radix passes of kth_lower_bound run only when the
+// rank-th key falls in the top bin.  Barriers inside.
+template <typename Score>
+__device__ __forceinline__ double kth_lower_bound_above(int n, int rank, Score score, double t0, Ctl& ctl) {
+  const int tid = threadIdx.x;
+  const uint32_t kt = (uint32_t)(f64_key(t0) >> 48);
+  for (int i = tid; i < 256; i += kNT) ctl.hist[i] = 0u;
+  __syncthreads();
+  for (int i = tid; i < n; i += kNT) {
+    const double sc = score(i);
+    if (sc >= t0) atomicAdd(&ctl.hist[min((uint32_t)(f64_key(sc) >> 48) - kt, 255u)], 1u);
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    int tot = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tot += (int)ctl.hist[4 * tid + j];
+    tot = wave_allreduce(tot, [](int x, int y) { return x + y; });
+    int digit = -1, above = 0;
+    if (tot >= rank && rank > 0) wave_pick_digit(ctl.hist, rank, &digit, &above);
+    digit = wave_allreduce(digit, [](int x, int y) { return x > y ? x : y; });
+    if (tid == 0) ctl.sh[0] = tot >= rank && rank > 0 ? digit : -1;
+  }
+  __syncthreads();
+  const int dg = ctl.sh[0];
+  __syncthreads();
+  if (dg < 0) return -INFINITY;
+  if (dg < 255) return f64_from_key((uint64_t)(kt + (uint32_t)dg) << 48);
+  return kth_lower_bound(n, rank, score, [&](int i) { return score(i) >= t0; }, ctl);
+}
+
 // The exact rank-th largest (rank >= 1, at most n) of the doubles score(i),
 // i in [0, n).  The 16-bit lower bound first fixes the bucket of keys that
 // holds the answer; the members of that bucket (listed in `buf`, capacity
@@ -585,19 +621,13 @@ __device__ __forceinline__ void level_search(const TreeArgs& a, const Tree& t, i
         __syncthreads();
         return;
       }
-      int local = 0;
-      for (int i = 1 + tid; i < ctl.node_count; i += kNT) local += (t.node_S[i] >= tau) ? 1 : 0;
-      const int alive = block_sum<kNT>(local, ctl.scan);
-      if (alive >= B && B > 0) {
-        // any lower bound of the B-th best node score is a valid threshold;
-        // a 16-bit one takes two radix passes instead of eight
-        const double tcur = tau;
-        const double nt = kth_lower_bound(
-            ctl.node_count - 1, B, [&](int i) { return t.node_S[i + 1]; },
-            [&](int i) { return t.node_S[i + 1] >= tcur; }, ctl);
-        if (nt > tau) tau = nt;
-        if (tid == 0) ctl.tau = tau;
-      }
+      // any lower bound of the B-th best node score is a valid threshold;
+      // a 16-bit one (-inf when fewer than B nodes reach tau)
+      const double tcur = tau;
+      const double nt =
+          kth_lower_bound_above(ctl.node_count - 1, B, [&](int i) { return t.node_S[i + 1]; }, tcur, ctl);
+      if (nt > tau) tau = nt;
+      if (tid == 0) ctl.tau = tau;
       __syncthreads();
     };
 
@@ -971,13 +1001,8 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
       __syncthreads();
       const double t0 = ctl.tau;
       auto best = [&](int i) { return htok[i] == kEmpty ? (double)NAN : f64_from_key(hkey[i]); };
-      int local = 0;
-      for (int i = tid; i < H; i += kNT) local += best(i) >= t0 ? 1 : 0;
-      const int alive = block_sum<kNT>(local, ctl.scan);
-      if (alive >= B) {
-        const double nb = kth_lower_bound(H, B, best, [&](int i) { return best(i) >= t0; }, ctl);
-        if (tid == 0 && nb > t0) ctl.tau = nb;
-      }
+      const double nb = kth_lower_bound_above(H, B, best, t0, ctl);  // -inf: fewer than B reach t0
+      if (tid == 0 && nb > t0) ctl.tau = nb;
       __syncthreads();
     } else if (np >= B) {
       // keys[0, P) are sorted; the pooled scores wait in keys[P, 2P)
@@ -1016,14 +1041,8 @@ __global__ void __launch_bounds__(kNT) tree_kernel(TreeArgs a) {
       }
       __syncthreads();
       const double t0 = ctl.tau;
-      int local = 0;
-      for (int i = tid; i < np; i += kNT) local += t.ch_s[i] >= t0 ? 1 : 0;
-      const int alive = block_sum<kNT>(local, ctl.scan);
-      if (alive >= B) {
-        const double nb = kth_lower_bound(
-            np, B, [&](int i) { return t.ch_s[i]; }, [&](int i) { return t.ch_s[i] >= t0; }, ctl);
-        if (tid == 0 && nb > t0) ctl.tau = nb;
-      }
+      const double nb = kth_lower_bound_above(np, B, [&](int i) { return t.ch_s[i]; }, t0, ctl);
+      if (tid == 0 && nb > t0) ctl.tau = nb;
       __syncthreads();
     }
   }
