@@ -308,6 +308,8 @@ struct WalkShared {
   Top2 w[kWalkWaves];
   WalkState ts[kTreesPerGroup];
   int complete[kTreesPerGroup];
+  int tree[kTreesPerGroup];  // the group's trees (launch-local indices)
+  int scan[kWalkWaves];
   int action, help_j, help_s;
   int32_t npar[kTreesPerGroup][kNodeLds];
   int32_t ntok[kTreesPerGroup][kNodeLds];
@@ -903,10 +905,49 @@ __global__ void __launch_bounds__(kWalkThreads, 4) verify_walk_kernel(WalkArgs a
 
   const int nt = grp < N ? (N - 1 - grp) / a.groups + 1 : 0;  // trees of the group
 
+  // The group's trees: position p of the launch's trees, those sampled at
+  // T > 0 first and then the rest, each kind in index order, goes to group
+  // p % groups.  A sampled row costs several times a greedy one (the noise of
+  // every element), so where groups serve two trees this pairs sampled trees
+  // with greedy ones rather than giving some groups two sampled rows per
+  // round while the groups of two greedy trees wait between theirs.  Results
+  // do not depend on which group serves a tree.
+  {
+    const auto sampled = [&](int i) {
+      const float T = a.temperature[i];
+      return T > 0.f && !isinf(T);
+    };
+    const int c = (N + kWalkThreads - 1) / kWalkThreads;
+    const int i0 = min(tid * c, N), i1 = min(i0 + c, N);
+    int h = 0;
+    for (int i = i0; i < i1; ++i) h += sampled(i) ? 1 : 0;
+    int nsampled = 0;
+    const int hb = block_exclusive_scan<kWalkThreads>(h, sh.scan, &nsampled);
+    for (int j = 0; j < nt; ++j) {
+      const int p = grp + j * a.groups;
+      const bool want = p < nsampled;
+      const int k = want ? p : p - nsampled;               // rank among the trees of its kind
+      const int before = want ? hb : i0 - hb;              // trees of that kind before this thread's range
+      const int here = want ? h : (i1 - i0) - h;
+      if (k >= before && k < before + here) {
+        int seen = before;
+        for (int i = i0; i < i1; ++i)
+          if (sampled(i) == want) {
+            if (seen == k) {
+              sh.tree[j] = i;
+              break;
+            }
+            ++seen;
+          }
+      }
+    }
+    __syncthreads();
+  }
+
   // each tree's first round (set by the prep or the speculative pass) and,
   // when they fit, its links and depths
   for (int j = 0; j < nt; ++j) {
-    const int n = grp + j * a.groups;
+    const int n = sh.tree[j];
     const size_t tb = (size_t)n * Bp1;
     int nn = a.n_nodes[n];
     nn = nn < 1 ? 1 : (nn > Bp1 ? Bp1 : nn);
@@ -939,7 +980,7 @@ __global__ void __launch_bounds__(kWalkThreads, 4) verify_walk_kernel(WalkArgs a
   // registers, so that no copy of it stays live across the row's loop.)
   auto do_slice = [&](int j, int s) {
     const WalkState& t = sh.ts[j];
-    const int n = uni(grp + j * a.groups);
+    const int n = uni(sh.tree[j]);
     const size_t tb = (size_t)n * Bp1;
     const double T = uni(t.T);
     const uint64_t sd = uni(t.sd);
@@ -995,7 +1036,7 @@ __global__ void __launch_bounds__(kWalkThreads, 4) verify_walk_kernel(WalkArgs a
     for (int j = 0; j < nt; ++j) {
       if (uni(sh.ts[j].ended)) continue;
       ++alive;
-      const int n = grp + j * a.groups;
+      const int n = sh.tree[j];
       if (!uni(sh.ts[j].mine)) {
         do_slice(j, member);
         if (tid == 0) sh.ts[j].mine = 1;
@@ -1124,7 +1165,7 @@ __global__ void __launch_bounds__(kWalkThreads, 4) verify_walk_kernel(WalkArgs a
       if (tid == 0)
         for (int j = 0; j < nt; ++j)
           if (!sh.ts[j].ended) {
-            const int n = grp + j * a.groups;
+            const int n = sh.tree[j];
             if (a.status) atomicOr(&a.status[n], MFD_TREE_CAPACITY);
             a.tau[n] = 0;
           }
