@@ -152,14 +152,14 @@ struct Top2f {
   float y2;
 };
 
+// (selects, not branches: a branch per element splits the slice loops into
+// one basic block per element; a NaN y changes nothing)
 __device__ __forceinline__ void top2f_add(Top2f& t, float y, int i) {
-  if ((y > t.y1) || (y == t.y1 && i < t.i1)) {
-    t.y2 = t.y1;
-    t.y1 = y;
-    t.i1 = i;
-  } else if (y > t.y2) {
-    t.y2 = y;
-  }
+  const bool take = (y > t.y1) | ((y == t.y1) & (i < t.i1));
+  const float y2 = take ? t.y1 : (y > t.y2 ? y : t.y2);
+  t.y1 = take ? y : t.y1;
+  t.i1 = take ? i : t.i1;
+  t.y2 = y2;
 }
 
 // Best (value, index) and the second best value seen.
@@ -978,7 +978,7 @@ __global__ void __launch_bounds__(kWalkThreads, 4) verify_walk_kernel(WalkArgs a
   // Reduce slice s of the current round of tree j (state t) and publish it.
   // (The state's fields are read from LDS where they are used, into scalar
   // registers, so that no copy of it stays live across the row's loop.)
-  auto do_slice = [&](int j, int s) {
+  auto do_slice = [&](int j, int s) __attribute__((always_inline)) {
     const WalkState& t = sh.ts[j];
     const int n = uni(sh.tree[j]);
     const size_t tb = (size_t)n * Bp1;
