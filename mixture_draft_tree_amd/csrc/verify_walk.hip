@@ -944,19 +944,12 @@ __global__ void __launch_bounds__(kWalkThreads, 4) verify_walk_kernel(WalkArgs a
     __syncthreads();
   }
 
-  // each tree's first round (set by the prep or the speculative pass) and,
-  // when they fit, its links and depths
+  // each tree's first round (set by the prep or the speculative pass)
   for (int j = 0; j < nt; ++j) {
     const int n = sh.tree[j];
     const size_t tb = (size_t)n * Bp1;
     int nn = a.n_nodes[n];
     nn = nn < 1 ? 1 : (nn > Bp1 ? Bp1 : nn);
-    if (nn <= kNodeLds)
-      for (int q = tid; q < nn; q += kWalkThreads) {
-        sh.npar[j][q] = a.parent[tb + q];
-        sh.ntok[j][q] = a.node_token[tb + q];
-        sh.ndep[j][q] = a.depth[tb + q];
-      }
     if (tid == 0) {
       const uint32_t w = a.word[n];
       WalkState& t = sh.ts[j];
@@ -1029,9 +1022,33 @@ __global__ void __launch_bounds__(kWalkThreads, 4) verify_walk_kernel(WalkArgs a
 
   uint64_t last_progress = 0;  // thread 0's clock decides; 0: read it at the next idle pass
   int backoff = 1;
+  bool links = false;
   while (true) {
     __syncthreads();  // the previous pass's shared fields have been read
     bool progress = false;
+    if (!links) {
+      // the first round's own slices, then the trees' links and depths (when
+      // they fit): the first merge is their first reader, so their loads
+      // wait behind the slices instead of delaying them
+      for (int j = 0; j < nt; ++j)
+        if (!uni(sh.ts[j].ended) && !uni(sh.ts[j].mine)) {
+          do_slice(j, member);
+          if (tid == 0) sh.ts[j].mine = 1;
+          progress = true;
+        }
+      for (int j = 0; j < nt; ++j) {
+        const int nn = uni(sh.ts[j].nn);
+        const size_t tb = (size_t)uni(sh.tree[j]) * Bp1;
+        if (nn <= kNodeLds)
+          for (int q = tid; q < nn; q += kWalkThreads) {
+            sh.npar[j][q] = a.parent[tb + q];
+            sh.ntok[j][q] = a.node_token[tb + q];
+            sh.ndep[j][q] = a.depth[tb + q];
+          }
+      }
+      links = true;
+      __syncthreads();
+    }
     int alive = 0;
     for (int j = 0; j < nt; ++j) {
       if (uni(sh.ts[j].ended)) continue;
