@@ -765,10 +765,13 @@ def test_threshold_capacity_flag_gives_root_only_tree():
 
 
 def test_walk_more_trees_than_one_launch():
-    """1100 one- and two-node trees over rows of 262144 bf16 logits: 64 slices
-    per row, at most 16 groups of 64 trees resident, so the walk needs two
-    launches.  Every tree against the oracle walk."""
-    N, V, L, Bp1 = 1100, 262144, 1, 2
+    """2700 one- and two-node trees over rows of 65536 bf16 logits.  A launch
+    takes at most two trees per resident workgroup (2048 or 2560 on this
+    device), so the walk needs two launches, and in the first one every
+    group of one workgroup serves two trees: one in five sampled at T = 1,
+    the rest greedy, which exercises the sampled-first pairing of trees to
+    groups.  Every tree against the oracle walk."""
+    N, V, L, Bp1 = 2700, 65536, 1, 2
     say(f"[walk launches] N={N} V={V}")
     g = torch.Generator().manual_seed(77)
     child = torch.randint(0, V, (N,), generator=g)
@@ -787,7 +790,7 @@ def test_walk_more_trees_than_one_launch():
     idx = torch.arange(N, device="cuda")
     R[idx[boost], 0, child.cuda()[boost]] += 6.0
     R = R.to(torch.bfloat16)
-    temps = torch.where(torch.arange(N) % 100 == 7, 1.0, 0.0).to(torch.float32).cuda()
+    temps = torch.where(torch.arange(N) % 5 == 2, 1.0, 0.0).to(torch.float32).cuda()
     seeds = (torch.arange(N, dtype=torch.int64) * 7919 + 1).cuda()
     tau = torch.empty(N, dtype=torch.int32, device="cuda")
     ot = torch.empty((N, L + 1), dtype=torch.int32, device="cuda")
