@@ -392,10 +392,13 @@ mfd_status mfd_tree_mask(const int32_t* parent, const int32_t* depth, const int3
  * From the root u = 0: the target's token at u is t* = argmax_v R[u, v] at
  * T = 0 (equal logits to the lower id), or at T > 0 the Gumbel-max sample
  *     t* = argmax_v ( fp64(R[u, v]) / fp64(T) + g_v ),  g_v = -log(-log(U_v)),
- *     U_v = ((w_v >> 12) + 1/2) * 2^-52,
- *     w_v = lane (v mod 4) of Philox4x64-10(counter = (v div 4, depth(u), 0, 0),
- *                                           key = (seed[n], 0))
- * (Salmon et al., "Parallel random numbers: as easy as 1, 2, 3", SC'11).
+ *     U_v = (w_v + 1/2) * 2^-32,
+ *     w_v = word (v mod 4) of Philox4x32-10(counter = (v div 4, depth(u), 0, 0),
+ *                                           key = (seed[n] mod 2^32, seed[n] div 2^32))
+ * (Salmon et al., "Parallel random numbers: as easy as 1, 2, 3", SC'11).  The
+ * kernel ranks fp32 estimates of these values first and evaluates the exact
+ * fp64 ones only for elements within the estimates' error bound of the best,
+ * so the winner is that of the fp64 values.
  * If u has a child with token t*, the walk moves there and repeats; else it
  * stops with tau = depth(u) + 1.
  *
