@@ -372,6 +372,8 @@ def single_tree_latency(seed, steps, stream, name="single"):
     assert int(status.abs().sum()) == 0, f"per-tree status flags set ({name}): {status.tolist()}"
     stages = {nm: statistics.mean(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps))
               for i, nm in enumerate(STAGES)}
+    stages["median"] = {nm: statistics.median(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps))
+                        for i, nm in enumerate(STAGES)}
     stages["separate_threshold_and_build"] = separate_tree_calls_ms(P, anchor, min(steps, 20), stream)
     g = capture_step(P, logits, anchor, pos, R, temps, seeds)
     graph_ms, _ = graph_steps(g, steps, 3, stream)
@@ -455,6 +457,11 @@ def timed_workload(name, seed, steps, warmup, stream, diagnostics=False):
     total_ms, ev = run_steps(P, logits, anchor, pos, R, temps, seeds, steps, warmup, stream)
     stage = {nm: statistics.mean(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps))
              for i, nm in enumerate(STAGES)}
+    # eager stage times include any host delay in enqueueing the stage's launch;
+    # the medians are robust to such single outliers, the means are what the
+    # roofline uses (average launch duration)
+    stage["median"] = {nm: statistics.median(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps))
+                       for i, nm in enumerate(STAGES)}
     per_step = sorted(ev[s][0].elapsed_time(ev[s][len(STAGES)]) for s in range(steps))
     q = lambda f: per_step[min(len(per_step) - 1, int(f * len(per_step)))]
     stage["step_ms_percentiles"] = {"p10": q(0.1), "p50": statistics.median(per_step), "p90": q(0.9)}
